@@ -1,0 +1,161 @@
+"""fp64 CPU oracle for the Kimi Delta Attention forward operator.
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product path
+(``kimi_delta_attention_amd``) never imports it, and this package imports
+nothing from the product; they share only the seeded input arrays.
+
+Two independent formulations live here:
+
+* :func:`recurrent` -- the C token loop in ``kda_oracle.c`` (decay, old value,
+  corrected write, read-out), fp64, parallel over (sequence, head, column block).
+  Sources: "Kimi Delta Attention 完全拆解", section "一次 KDA 前向究竟发生了什么"
+  (decode sequence) and section "KDA 的核心"; "Kimi K3模型架构详解" section 3.2.
+* :func:`recurrent_matrix` -- a small numpy restatement that builds each step's
+  explicit transition matrix in the diagonal-plus-low-rank form
+  Diag(alpha) - (beta k)(k * alpha)^T ("从线性注意力到 KDA", section "公式 (1) 的图解";
+  "Kimi Delta Attention 完全拆解", section "KDA 为什么比一般 DPLR 更容易做成快 Kernel")
+  and applies S <- M S + beta k v^T.  It is for tiny inputs only.
+
+Parity status: pinned (see the CPU tests) by linear-attention brute force, the
+exact-overwrite property, the beta = 0 closed form, the erase-free two-token
+expansion, the gradient-step derivation, the state-size arithmetic, the
+chunk form and two-segment composition; the general random case has no printed
+values on the pages.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+
+MODES = {"kda": 0, "erase_off": 1, "erase_then_decay": 2}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compiles ``kda_oracle.c`` with gcc into ``libkda_oracle.so`` (in place)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+             "-o", tmp, _SRC, "-lm", "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.kda_oracle_forward.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, P, P,
+                                           ctypes.c_int, ctypes.c_int]
+        lib.kda_oracle_forward.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    """Exact upcast to a C-contiguous fp64 numpy array (torch tensors accepted)."""
+    if hasattr(x, "detach"):  # torch tensor: go through fp64 on CPU (exact for bf16/fp32)
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def recurrent(q, k, v, alpha, beta, cu_seqlens=None, initial_state=None, mode: str = "kda",
+              nthreads: int | None = None):
+    """Token-by-token fp64 recurrence.
+
+    Shapes follow the operator's statement: dense ``q, k, alpha`` are
+    ``[B, T, H, Dk]``, ``v`` is ``[B, T, H, Dv]``, ``beta`` is ``[B, T, H]``,
+    and the state is ``[B, H, Dk, Dv]``.  With ``cu_seqlens`` (``[N+1]``) the
+    inputs are packed ``[1, NTOK, H, .]`` and the state is ``[N, H, Dk, Dv]``.
+
+    Returns ``(o, final_state)`` as fp64 numpy arrays, ``o`` shaped like ``v``.
+    """
+    q, k, v, alpha, beta = (_f64(x) for x in (q, k, v, alpha, beta))
+    if q.ndim != 4:
+        raise ValueError("q must be [B, T, H, Dk]")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or alpha.shape != q.shape or v.shape != (B, T, H, Dv) \
+            or beta.shape != (B, T, H):
+        raise ValueError("inconsistent shapes")
+    if cu_seqlens is None:
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        if B != 1:
+            raise ValueError("packed inputs must have B == 1")
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64))
+        if cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+            raise ValueError("cu_seqlens must start at 0, end at T and be non-decreasing")
+    n_seq = len(cu) - 1
+    s_init = None
+    if initial_state is not None:
+        s_init = _f64(initial_state)
+        if s_init.shape != (n_seq, H, Dk, Dv):
+            raise ValueError("initial_state must be [N, H, Dk, Dv]")
+    o = np.zeros((B, T, H, Dv), dtype=np.float64)
+    s_final = np.zeros((n_seq, H, Dk, Dv), dtype=np.float64)
+    rc = _load().kda_oracle_forward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu), n_seq, H, Dk, Dv,
+        _ptr(s_init) if s_init is not None else None, _ptr(o), _ptr(s_final),
+        MODES[mode], int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_forward failed with code {rc}")
+    return o, s_final
+
+
+def recurrent_matrix(q, k, v, alpha, beta, initial_state=None):
+    """Explicit-transition restatement for tiny dense inputs (pure numpy, fp64).
+
+    For each (b, h) and t: M_t = Diag(alpha_t) - (beta_t k_t)(k_t * alpha_t)^T,
+    S_t = M_t S_{t-1} + beta_t k_t v_t^T, o_t = S_t^T q_t.
+    """
+    q, k, v, alpha, beta = (_f64(x) for x in (q, k, v, alpha, beta))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    o = np.zeros((B, T, H, Dv))
+    sf = np.zeros((B, H, Dk, Dv))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((Dk, Dv)) if initial_state is None else _f64(initial_state)[b, h].copy()
+            for t in range(T):
+                kt, at, bt = k[b, t, h], alpha[b, t, h], beta[b, t, h]
+                M = np.diag(at) - np.outer(bt * kt, kt * at)
+                S = M @ S + bt * np.outer(kt, v[b, t, h])
+                o[b, t, h] = S.T @ q[b, t, h]
+            sf[b, h] = S
+    return o, sf
+
+
+def rel_l2(x, ref) -> float:
+    """||x - ref||_2 / ||ref||_2 over the whole tensor, in fp64."""
+    x = _f64(x)
+    ref = _f64(ref)
+    den = np.linalg.norm(ref.ravel())
+    num = np.linalg.norm((x - ref).ravel())
+    return float(num / den) if den > 0 else float(num)

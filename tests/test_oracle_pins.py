@@ -1,0 +1,315 @@
+"""Pins of the fp64 CPU oracle against what the pages and the mathematics fix.
+
+Each test names the passage it follows.  None of them re-types the oracle's own
+loop: they use brute force, closed forms, invariants, finite differences or an
+independent formulation (explicit transition matrices, the chunk form).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(rng, B, T, H, Dk, Dv, unit_k=True, alpha_lo=0.3, beta=None):
+    q = rng.standard_normal((B, T, H, Dk))
+    k = rng.standard_normal((B, T, H, Dk))
+    if unit_k:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, Dv))
+    a = rng.uniform(alpha_lo, 1.0, (B, T, H, Dk))
+    b = rng.uniform(0.05, 0.95, (B, T, H)) if beta is None else np.full((B, T, H), beta)
+    return q, k, v, a, b
+
+
+def test_linear_attention_bruteforce():
+    """alpha = 1, no erase, beta = 1 is linear attention: o_t = sum_{i<=t} (q_t.k_i) v_i.
+    "Kimi K3 的 KDA" section 2; "Kimi Delta Attention 完全拆解", section
+    "线性注意力是一张矩阵形式的关联表"."""
+    rng = np.random.default_rng(1)
+    B, T, H, Dk, Dv = 2, 48, 2, 8, 6
+    q, k, v, _, _ = _rand(rng, B, T, H, Dk, Dv, unit_k=False)
+    a = np.ones((B, T, H, Dk))
+    b = np.ones((B, T, H))
+    o, S = oracle.recurrent(q, k, v, a, b, mode="erase_off")
+    ref = np.zeros_like(o)
+    for bb in range(B):
+        for h in range(H):
+            for t in range(T):
+                for i in range(t + 1):
+                    ref[bb, t, h] += np.dot(q[bb, t, h], k[bb, i, h]) * v[bb, i, h]
+    assert np.max(np.abs(o - ref)) < 1e-12 * max(1.0, np.max(np.abs(ref)))
+    # state is the sum of outer products k_i v_i^T
+    Sref = np.einsum("bthk,bthv->bhkv", k, v)
+    assert np.max(np.abs(S - Sref)) < 1e-12 * np.max(np.abs(Sref))
+
+
+def test_exact_overwrite_unit_key():
+    """Unit-norm k, beta = 1, alpha = 1: after each step S_t^T k_t = v_t exactly
+    ("从线性注意力到 KDA", section "一步在线学习": the regression minimum;
+    "Kimi Delta Attention 完全拆解", section "Delta Rule 先计算写入误差").
+    Read-out with q_t = k_t returns S_t^T k_t, so o_t must equal v_t."""
+    rng = np.random.default_rng(2)
+    B, T, H, Dk, Dv = 1, 40, 3, 16, 12
+    _, k, v, _, _ = _rand(rng, B, T, H, Dk, Dv)
+    s0 = rng.standard_normal((B, H, Dk, Dv))
+    o, S = oracle.recurrent(k, k, v, np.ones_like(k), np.ones((B, T, H)), initial_state=s0)
+    assert np.max(np.abs(o - v)) < 1e-13 * 10
+    last = np.einsum("bhkv,bhk->bhv", S, k[:, -1])
+    assert np.max(np.abs(last - v[:, -1])) < 1e-12
+
+
+def test_beta_zero_pure_decay_closed_form():
+    """beta = 0 only forgets: S_t = Diag(prod_{r<=t} alpha_r) S_0 and
+    o_t = S_0^T (Gamma_t * q_t) ("Kimi Delta Attention 完全拆解", section "KDA 的核心",
+    degenerate cases)."""
+    rng = np.random.default_rng(3)
+    B, T, H, Dk, Dv = 2, 30, 2, 8, 5
+    q, k, v, a, _ = _rand(rng, B, T, H, Dk, Dv, alpha_lo=0.8)
+    s0 = rng.standard_normal((B, H, Dk, Dv))
+    o, S = oracle.recurrent(q, k, v, a, np.zeros((B, T, H)), initial_state=s0)
+    gamma = np.cumprod(a, axis=1)  # [B,T,H,Dk]
+    Sref = gamma[:, -1, :, :, None] * s0
+    oref = np.einsum("bhkv,bthk->bthv", s0, gamma * q)
+    assert np.max(np.abs(S - Sref)) < 1e-13
+    assert np.max(np.abs(o - oref)) < 1e-13
+
+
+def test_two_token_erase_free_expansion():
+    """Erase-free, scalar alpha, two tokens: S_2 = a2 a1 S_in + a2 k1 v1^T + k2 v2^T
+    ("Kimi K3 的 KDA", section 5, the two-token example)."""
+    rng = np.random.default_rng(4)
+    Dk, Dv = 5, 4
+    k = rng.standard_normal((1, 2, 1, Dk))
+    v = rng.standard_normal((1, 2, 1, Dv))
+    q = rng.standard_normal((1, 2, 1, Dk))
+    a1, a2 = 0.7, 0.4
+    a = np.stack([np.full(Dk, a1), np.full(Dk, a2)])[None, :, None, :]
+    s_in = rng.standard_normal((1, 1, Dk, Dv))
+    _, S = oracle.recurrent(q, k, v, a, np.ones((1, 2, 1)), initial_state=s_in, mode="erase_off")
+    ref = a2 * a1 * s_in[0, 0] + a2 * np.outer(k[0, 0, 0], v[0, 0, 0]) + np.outer(k[0, 1, 0], v[0, 1, 0])
+    assert np.max(np.abs(S[0, 0] - ref)) < 1e-14
+
+
+def test_one_gradient_step_on_decayed_state():
+    """S_t = Sbar - beta grad L(Sbar), L(S) = 1/2 ||S^T k - v||^2, Sbar = Diag(alpha) S_{t-1}
+    ("Kimi Delta Attention 完全拆解", section "Delta Rule"; "从线性注意力到 KDA", section
+    "一步在线学习", decay before erase).  The gradient is taken by central finite
+    differences, which are exact up to rounding for a quadratic loss."""
+    rng = np.random.default_rng(5)
+    Dk, Dv = 6, 4
+    s0 = rng.standard_normal((1, 1, Dk, Dv))
+    q, k, v, a, b = _rand(rng, 1, 1, 1, Dk, Dv)
+    sbar = a[0, 0, 0][:, None] * s0[0, 0]
+    kk, vv = k[0, 0, 0], v[0, 0, 0]
+
+    def loss(S):
+        r = S.T @ kk - vv
+        return 0.5 * float(r @ r)
+
+    grad = np.zeros_like(sbar)
+    h = 1e-3
+    for i in range(Dk):
+        for j in range(Dv):
+            E = np.zeros_like(sbar)
+            E[i, j] = h
+            grad[i, j] = (loss(sbar + E) - loss(sbar - E)) / (2 * h)
+    ref = sbar - b[0, 0, 0] * grad
+    o, S = oracle.recurrent(q, k, v, a, b, initial_state=s0)
+    assert np.max(np.abs(S[0, 0] - ref)) < 1e-9
+    assert np.max(np.abs(o[0, 0, 0] - ref.T @ q[0, 0, 0])) < 1e-9
+
+
+def test_matches_explicit_dplr_transition():
+    """The loop equals S_t = (Diag(alpha) - (beta k)(k*alpha)^T) S_{t-1} + beta k v^T with
+    explicit matrices ("从线性注意力到 KDA", section "公式 (1) 的图解", DPLR form;
+    "Kimi Delta Attention 完全拆解", section on DPLR)."""
+    rng = np.random.default_rng(6)
+    B, T, H, Dk, Dv = 2, 37, 2, 12, 10
+    q, k, v, a, b = _rand(rng, B, T, H, Dk, Dv)
+    s0 = rng.standard_normal((B, H, Dk, Dv))
+    o1, S1 = oracle.recurrent(q, k, v, a, b, initial_state=s0)
+    o2, S2 = oracle.recurrent_matrix(q, k, v, a, b, initial_state=s0)
+    assert np.max(np.abs(o1 - o2)) < 1e-12
+    assert np.max(np.abs(S1 - S2)) < 1e-12
+    # and the DPLR matrix is the product (I - beta k k^T) Diag(alpha)
+    kk, aa, bb = k[0, 0, 0], a[0, 0, 0], b[0, 0, 0]
+    M1 = (np.eye(Dk) - bb * np.outer(kk, kk)) @ np.diag(aa)
+    M2 = np.diag(aa) - np.outer(bb * kk, kk * aa)
+    assert np.max(np.abs(M1 - M2)) < 1e-15
+
+
+def test_degenerate_gdn_and_deltanet():
+    """Equal channels give the scalar-gate GDN form alpha (I - beta k k^T) S + beta k v^T;
+    alpha = 1 gives DeltaNet S - beta k (S^T k - v)^T ("Kimi Delta Attention 完全拆解",
+    sections "Gated DeltaNet 仍只有一个遗忘旋钮" and "Delta Rule")."""
+    rng = np.random.default_rng(7)
+    B, T, H, Dk, Dv = 1, 20, 1, 8, 6
+    q, k, v, _, b = _rand(rng, B, T, H, Dk, Dv)
+    s0 = rng.standard_normal((B, H, Dk, Dv))
+    sc = rng.uniform(0.5, 1.0, (B, T, H))
+    a = np.repeat(sc[..., None], Dk, axis=-1)
+    _, S = oracle.recurrent(q, k, v, a, b, initial_state=s0)
+    Sg = s0[0, 0].copy()
+    for t in range(T):
+        kt = k[0, t, 0]
+        Sg = sc[0, t, 0] * (np.eye(Dk) - b[0, t, 0] * np.outer(kt, kt)) @ Sg \
+            + b[0, t, 0] * np.outer(kt, v[0, t, 0])
+    assert np.max(np.abs(S[0, 0] - Sg)) < 1e-12
+    _, S = oracle.recurrent(q, k, v, np.ones_like(q), b, initial_state=s0)
+    Sd = s0[0, 0].copy()
+    for t in range(T):
+        kt = k[0, t, 0]
+        Sd = Sd - b[0, t, 0] * np.outer(kt, Sd.T @ kt - v[0, t, 0])
+    assert np.max(np.abs(S[0, 0] - Sd)) < 1e-12
+
+
+def _chunk_form(q, k, v, a, b, s0, C):
+    """fp64 chunk form of the recurrence, written from its derivation: inside a chunk
+    with entry state S, G = cumsum(log alpha); A_rj = beta_r sum_c k_rc k_jc e^{G_rc-G_jc}
+    (j < r); T = (I + A)^-1; W = T Diag(beta)(e^G * K); U = T Diag(beta) V; P = U - W S;
+    O = (e^G * Q) S + tril_incl(Mqk) P; S' = Diag(e^{G_C}) S + (e^{G_C - G} * K)^T P.
+    ("Kimi Delta Attention 完全拆解", section "chunk 内并行、chunk 间递推";
+    "Kimi K3 的 KDA" section 5)."""
+    T_, Dk = q.shape
+    S = s0.copy()
+    o = np.zeros((T_, v.shape[1]))
+    for c0 in range(0, T_, C):
+        Q, K, V, Al, Bt = q[c0:c0 + C], k[c0:c0 + C], v[c0:c0 + C], a[c0:c0 + C], b[c0:c0 + C]
+        n = Q.shape[0]
+        G = np.cumsum(np.log(Al), axis=0)
+        D = np.exp(G[:, None, :] - G[None, :, :])           # [r, j, c] = e^{G_rc - G_jc}
+        A = Bt[:, None] * np.einsum("rc,jc,rjc->rj", K, K, D)
+        A = np.tril(A, -1)
+        Mqk = np.tril(np.einsum("rc,jc,rjc->rj", Q, K, D))
+        Tm = np.linalg.inv(np.eye(n) + A)
+        W = Tm @ (Bt[:, None] * np.exp(G) * K)
+        U = Tm @ (Bt[:, None] * V)
+        P = U - W @ S
+        o[c0:c0 + n] = (np.exp(G) * Q) @ S + Mqk @ P
+        Kt = np.exp(G[-1][None, :] - G) * K
+        S = np.exp(G[-1])[:, None] * S + Kt.T @ P
+    return o, S
+
+
+def test_chunk_form_matches_recurrence():
+    """The chunk form (with a ragged last chunk) reproduces the token loop in fp64."""
+    rng = np.random.default_rng(8)
+    B, T, H, Dk, Dv = 1, 83, 2, 16, 12
+    q, k, v, a, b = _rand(rng, B, T, H, Dk, Dv, alpha_lo=0.5)
+    s0 = rng.standard_normal((B, H, Dk, Dv))
+    o, S = oracle.recurrent(q, k, v, a, b, initial_state=s0)
+    for h in range(H):
+        oc, Sc = _chunk_form(q[0, :, h], k[0, :, h], v[0, :, h], a[0, :, h], b[0, :, h],
+                             s0[0, h], C=16)
+        assert np.max(np.abs(oc - o[0, :, h])) < 1e-11
+        assert np.max(np.abs(Sc - S[0, h])) < 1e-11
+
+
+def test_decay_then_erase_order_matters():
+    """Erase-then-decay is a different operator; the implemented order is decay first
+    ("从线性注意力到 KDA", section "术语坑", last item; "Kimi Delta Attention 完全拆解",
+    section "KDA 的核心": the order cannot be swapped)."""
+    rng = np.random.default_rng(9)
+    q, k, v, a, b = _rand(rng, 1, 64, 2, 16, 16, alpha_lo=0.2)
+    o1, S1 = oracle.recurrent(q, k, v, a, b)
+    o2, S2 = oracle.recurrent(q, k, v, a, b, mode="erase_then_decay")
+    assert oracle.rel_l2(o2, o1) > 1e-3
+    assert oracle.rel_l2(S2, S1) > 1e-3
+
+
+def test_state_norm_bound():
+    """For unit k and beta in [0, 1], I - beta k k^T has eigenvalues in [1 - beta, 1]
+    ("从线性注意力到 KDA", section "参数化", L2 normalisation), and Diag(alpha) with
+    alpha <= 1 does not expand, so ||S_t||_F <= ||S_{t-1}||_F + beta_t ||v_t|| and, with
+    v = 0, ||S_t||_F never grows.  Checked step by step through the state hand-off."""
+    rng = np.random.default_rng(10)
+    T, Dk, Dv = 50, 16, 8
+    q, k, v, a, b = _rand(rng, 1, T, 1, Dk, Dv, alpha_lo=0.5)
+    for vv in (v, np.zeros_like(v)):
+        S = rng.standard_normal((1, 1, Dk, Dv))
+        for t in range(T):
+            _, S2 = oracle.recurrent(q[:, t:t + 1], k[:, t:t + 1], vv[:, t:t + 1],
+                                     a[:, t:t + 1], b[:, t:t + 1], initial_state=S)
+            n0, n1 = np.linalg.norm(S), np.linalg.norm(S2)
+            assert n1 <= n0 + b[0, t, 0] * np.linalg.norm(vv[0, t, 0]) + 1e-12
+            S = S2
+
+
+def test_two_segments_equal_whole():
+    """Two segments with the state handed over equal the whole sequence
+    ("Kimi Delta Attention 完全拆解", section "数值路径必须以 recurrent 版本为基准校验")."""
+    rng = np.random.default_rng(11)
+    q, k, v, a, b = _rand(rng, 1, 90, 2, 16, 12)
+    s0 = rng.standard_normal((1, 2, 16, 12))
+    o, S = oracle.recurrent(q, k, v, a, b, initial_state=s0)
+    cut = 37
+    o1, S1 = oracle.recurrent(q[:, :cut], k[:, :cut], v[:, :cut], a[:, :cut], b[:, :cut],
+                              initial_state=s0)
+    o2, S2 = oracle.recurrent(q[:, cut:], k[:, cut:], v[:, cut:], a[:, cut:], b[:, cut:],
+                              initial_state=S1)
+    assert np.max(np.abs(np.concatenate([o1, o2], axis=1) - o)) < 1e-13
+    assert np.max(np.abs(S2 - S)) < 1e-13
+
+
+def test_packed_batch_isolation():
+    """A packed batch gives each sequence exactly its solo result (same section:
+    variable-length batches must not depend on their neighbours)."""
+    rng = np.random.default_rng(12)
+    lens = [5, 1, 17, 0, 9]
+    q, k, v, a, b = _rand(rng, 1, sum(lens), 2, 8, 8)
+    s0 = rng.standard_normal((len(lens), 2, 8, 8))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    o, S = oracle.recurrent(q, k, v, a, b, cu_seqlens=cu, initial_state=s0)
+    for i, L in enumerate(lens):
+        sl = slice(cu[i], cu[i + 1])
+        oi, Si = oracle.recurrent(q[:, sl], k[:, sl], v[:, sl], a[:, sl], b[:, sl],
+                                  initial_state=s0[i:i + 1])
+        assert np.array_equal(oi, o[:, sl])
+        assert np.array_equal(Si, S[i:i + 1])
+
+
+def test_thread_count_does_not_change_results():
+    rng = np.random.default_rng(13)
+    q, k, v, a, b = _rand(rng, 2, 33, 3, 16, 40)
+    r1 = oracle.recurrent(q, k, v, a, b, nthreads=1)
+    r2 = oracle.recurrent(q, k, v, a, b, nthreads=7)
+    assert np.array_equal(r1[0], r2[0]) and np.array_equal(r1[1], r2[1])
+
+
+def test_state_size_is_t_independent_and_matches_pages():
+    """69 x 96 x 128 x 128 x 2 B = 217,055,232 B, independent of T ("Kimi K3 混合线性注意力");
+    32 x 128 x 128 x 2 B = 1 MiB per layer ("Kimi Delta Attention 完全拆解", section
+    "缓存从 O(T) 变成 O(1)"); about 1.68M numbers per layer with the conv cache
+    ("从线性注意力到 KDA", section "每层的状态有多大")."""
+    g = json.load(open(os.path.join(GOLDEN, "state_size.json")))
+    rng = np.random.default_rng(14)
+    H, D = 96, 128
+    sizes = []
+    for T in (1, 3):
+        q, k, v, a, b = _rand(rng, 1, T, H, D, D)
+        _, S = oracle.recurrent(q, k, v, a, b)
+        sizes.append(S[0].size)
+    assert sizes[0] == sizes[1] == H * D * D
+    k3 = g["k3_session"]
+    assert k3["layers"] * sizes[0] * k3["bytes_per_value"] == k3["total_bytes"]
+    h32 = g["h32_layer"]
+    assert h32["heads"] * h32["dk"] * h32["dv"] * h32["bytes_per_value"] == h32["total_bytes"]
+    approx = g["k3_layer_numbers_approx"]
+    # matrix state plus the last 3 projected inputs of q, k and v (kernel size 4)
+    n = H * D * D + 3 * 3 * H * D
+    assert round(n / 1e6, 2) == approx["approx_numbers_millions"]
+
+
+def test_bad_arguments_rejected():
+    rng = np.random.default_rng(15)
+    q, k, v, a, b = _rand(rng, 1, 4, 1, 4, 4)
+    with pytest.raises(ValueError):
+        oracle.recurrent(q, k, v[:, :3], a, b)
+    with pytest.raises(ValueError):
+        oracle.recurrent(q, k, v, a, b, cu_seqlens=[0, 3, 2, 4])
