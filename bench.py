@@ -1,0 +1,173 @@
+"""KDA forward benchmark on one MI355X.
+
+One step = one chunked prefill (every step of the chunk form) of a K3-shaped
+layer: B=1, H=96, T=8192, d_k=d_v=128, bf16 q/k/v, fp32 alpha/beta/state,
+fp32 output, inputs resident in HBM.  The line also carries the decode step's
+state bandwidth (64 sessions x 96 heads x 128x128 fp32 state, updated in place),
+the prefill kernel's roofline position, and the fp64 CPU oracle timed on this
+host on the same prefill workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def prefill_bytes(B, T, H, Dk, Dv):
+    """Algorithmic HBM bytes of one prefill launch: bf16 q, k, v; fp32 alpha,
+    beta and o, per token-head; fp32 initial and final state per sequence-head."""
+    per_token_head = 2 * Dk + 2 * Dk + 2 * Dv + 4 * Dk + 4 + 4 * Dv
+    return B * T * H * per_token_head + 2 * B * H * Dk * Dv * 4
+
+
+def prefill_flops(B, T, H, d, C=64):
+    """The chunk kernel's FLOP count per head, 6 T d^2 + 3 T C d + T C^2
+    ("Kimi Delta Attention 完全拆解", section "Prefill 仍是线性复杂度")."""
+    return B * H * (6 * T * d * d + 3 * T * C * d + T * C * C)
+
+
+def decode_bytes(B, H, Dk, Dv):
+    state = 2 * B * H * Dk * Dv * 4
+    other = B * H * (2 * Dk + 2 * Dk + 2 * Dv + 4 * Dk + 4 + 4 * Dv)
+    return state, other
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--decode-steps", type=int, default=50)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "the operator is not sharded across GPUs", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kimi_delta_attention_amd as kda
+    from kimi_delta_attention_amd import synth
+
+    d = torch.device("cuda:0")
+    w = synth.WORKLOADS["k3_prefill_8k"]
+    B, T, H, D = w["B"], w["T"], w["H"], w["D"]
+    print(f"bench: generating k3_prefill_8k inputs B={B} T={T} H={H} d={D}", file=sys.stderr,
+          flush=True)
+    inp = synth.make_dense(B, T, H, D, D, seed=w["seed"], state_std=w["state_std"], device=d)
+    o = torch.empty(B, T, H, D, dtype=torch.float32, device=d)
+    fs = torch.empty(B, H, D, D, dtype=torch.float32, device=d)
+
+    def step():
+        kda.prefill_chunked(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
+                            initial_state=inp.state, final_state=fs, o=o)
+
+    # plain device copy of known size: calibrates HBM byte counters under rocprofv3
+    calib = torch.empty(64 << 20, dtype=torch.float32, device=d)  # 256 MiB
+    calib2 = torch.empty_like(calib)
+    calib2.copy_(calib)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(d)  # the library launches on this stream
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]  # ms per launch
+    total_ms = ev[0].elapsed_time(ev[-1])
+    ms_step = total_ms / args.steps
+    avg_launch_ms = sum(per) / len(per)
+    tokens_s = B * T * args.steps / (total_ms / 1e3)
+    nbytes = prefill_bytes(B, T, H, D, D)
+    gbs = nbytes / (avg_launch_ms / 1e3) / 1e9
+    tflops = prefill_flops(B, T, H, D) / (avg_launch_ms / 1e3) / 1e12
+    print(f"bench: prefill {ms_step:.3f} ms/step, {gbs:.0f} GB/s algorithmic, "
+          f"{tflops:.1f} TFLOP/s (pages' count), wall {wall:.2f}s", file=sys.stderr, flush=True)
+
+    # decode step (state read + write once per step)
+    wd = synth.WORKLOADS["decode_b64"]
+    dec = synth.make_dense(wd["B"], 1, wd["H"], wd["D"], wd["D"], seed=wd["seed"],
+                           state_std=wd["state_std"], device=d)
+    dq, dk, dv, da, db = (x[:, 0].contiguous() for x in (dec.q, dec.k, dec.v, dec.alpha, dec.beta))
+    st = dec.state
+    od = torch.empty(wd["B"], wd["H"], wd["D"], dtype=torch.float32, device=d)
+    for _ in range(5):
+        kda.decode_step(dq, dk, dv, da, db, st, o=od)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.decode_steps):
+        kda.decode_step(dq, dk, dv, da, db, st, o=od)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / args.decode_steps
+    sbytes, obytes = decode_bytes(wd["B"], wd["H"], wd["D"], wd["D"])
+    dec_state_gbs = sbytes / (dec_ms / 1e3) / 1e9
+    dec_total_gbs = (sbytes + obytes) / (dec_ms / 1e3) / 1e9
+    print(f"bench: decode {dec_ms * 1e3:.1f} us/step, state {dec_state_gbs:.0f} GB/s",
+          file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        nth = oracle.default_threads()
+        print(f"bench: cpu oracle on the full prefill workload, {nth} threads", file=sys.stderr,
+              flush=True)
+        host = [x.cpu() for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.state)]
+        tc = time.perf_counter()
+        oracle.recurrent(*host[:5], initial_state=host[5], nthreads=nth)
+        ct = time.perf_counter() - tc
+        cpu = {"value": B * T / ct, "unit": "tokens/s", "cores": nth, "kind": "oracle",
+               "sample": f"the whole workload (B={B}, T={T}, H={H}, d={D}), one pass, "
+                         f"fp64 token loop, {ct:.2f} s"}
+
+    line = {
+        "metric": "KDA prefill tokens/s (H=96,d=128) + decode-step state GB/s vs HBM peak",
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "k3_prefill_8k", "B": B, "T": T, "H": H, "d_k": D, "d_v": D,
+                   "chunk": 64, "qkv": "bf16", "alpha_beta_state": "fp32", "o": "fp32"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "prefill_kernel<128,64,bf16->fp32>",
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_ms": avg_launch_ms,
+                     "mfma_frac_pages_flops": tflops / BF16_PEAK_TFLOPS},
+        "decode": {"workload": "decode_b64", "B": wd["B"], "H": wd["H"], "d": wd["D"],
+                   "us_per_step": dec_ms * 1e3, "state_gbs": dec_state_gbs,
+                   "total_gbs": dec_total_gbs, "frac_hbm": dec_total_gbs / HBM_PEAK_GBS},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward operator.
+ *
+ * The operator, per (sequence, head), with S in R^{Dk x Dv} (rows = key
+ * channels, columns = value channels):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t                      (read-out from the UPDATED state)
+ *
+ * alpha_t in (0,1]^Dk decays each key channel (row) of the state first; the
+ * delta-rule erase and the write then act on the decayed state.  Sources:
+ * "Kimi Delta Attention 完全拆解" (pinghaoyang.com.cn), section "KDA 的核心：让遗忘从
+ * 一个标量细化为逐通道向量"; "Kimi K3模型架构详解" (gentlecold.top), section 3.2
+ * "KDA的递推式"; "从线性注意力到 KDA" (blog.javazero.top), sections "一步在线学习" and
+ * "衰减为什么要按行做".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller, dense and
+ *    row-major in the shapes given, aligned to their element size; state
+ *    pointers (initial_state, final_state, state) 16-byte aligned.  The library never
+ *    allocates device memory and keeps no state besides cached device
+ *    properties.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls enqueue work asynchronously on it; a kernel fault surfaces at the
+ *    caller's next synchronisation.
+ *  - Argument errors are detected on the host and returned BEFORE anything is
+ *    launched (KDA_ERR_INVALID_ARGUMENT / KDA_ERR_UNSUPPORTED);
+ *    kda_last_error_message() then gives the detail (thread-local).  A failed
+ *    launch returns KDA_ERR_HIP.  No exception or abort crosses the ABI.
+ *  - Supported shapes: Dk, Dv in {64, 128}; chunk == 64.  q/k/v dtype KDA_BF16
+ *    or KDA_F32 (all three the same); alpha, beta and the state are fp32; the
+ *    output o is KDA_F32 or KDA_BF16.
+ *  - Documented, not checked: alpha in (0, 1] and, for the chunked paths, the
+ *    per-channel product of alpha over any 16-token tile aligned to a 64-token
+ *    chunk boundary is at least 1e-35 (true whenever log alpha >= -5 per token,
+ *    the bounded gate of "Kimi K3 的 KDA" section 6 / "Kimi K3模型架构详解" section
+ *    3.4); finite beta; monotone cu_seqlens; o does not alias any input.
+ *  - Results are deterministic (no floating-point atomics): the same call on
+ *    the same inputs gives bitwise-identical results, and a sequence of a
+ *    packed batch gives bitwise the result it gives when run alone.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad alignment      */
+    KDA_ERR_UNSUPPORTED = 2,      /* valid but not built (head dim, chunk, dtype) */
+    KDA_ERR_HIP = 3               /* the HIP runtime reported an error            */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/*
+ * kda_prefill_chunked -- dense prefill over B sequences of T tokens each.
+ * The chunkwise form of the recurrence: inside each 64-token chunk the
+ * cumulative decay, the strictly lower-triangular beta-weighted decayed k k^T
+ * matrix A, its unit-triangular inverse (I + A)^{-1} (the UT transform), the
+ * intra-chunk q.k matrix and the pseudo-values U - W S are formed, and the state
+ * is handed from chunk to chunk ("Kimi Delta Attention 完全拆解", section
+ * "chunk 内并行、chunk 间递推"; "Kimi K3 的 KDA" section 5; "Kimi K3模型架构详解"
+ * section 3.5).  Equal to the token recurrence up to rounding.
+ *
+ *   q, k          [B, T, H, Dk]  qkv_dtype
+ *   v             [B, T, H, Dv]  qkv_dtype
+ *   alpha         [B, T, H, Dk]  fp32, per-key-channel decay
+ *   beta          [B, T, H]      fp32, write strength
+ *   initial_state [B, H, Dk, Dv] fp32, or NULL for zeros
+ *   final_state   [B, H, Dk, Dv] fp32, or NULL to skip; may equal initial_state
+ *                 (updated in place)
+ *   o             [B, T, H, Dv]  o_dtype
+ *   chunk         must be 64
+ *   workspace     unused by this version (kda_prefill_workspace_size returns 0);
+ *                 may be NULL
+ * T == 0 or B == 0 is allowed (then only final_state = initial_state is written).
+ */
+kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                               const float* alpha, const float* beta,
+                               const float* initial_state, float* final_state,
+                               void* o, kda_dtype o_dtype,
+                               int B, int T, int H, int Dk, int Dv, int chunk,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_prefill_varlen -- packed variable-length prefill.  N sequences are
+ * concatenated along the token axis (B = 1); sequence i occupies tokens
+ * cu_seqlens[i] .. cu_seqlens[i+1]-1, has its own initial state and final state,
+ * and its chunks start at its own first token (the last chunk may be partial).
+ * A sequence's results do not depend on its neighbours ("Kimi Delta Attention
+ * 完全拆解", section "数值路径必须以 recurrent 版本为基准校验").
+ *
+ *   q, k, alpha   [1, total_tokens, H, Dk];  v, o [1, total_tokens, H, Dv]
+ *   beta          [1, total_tokens, H]
+ *   cu_seqlens    DEVICE int32 [N + 1], cu_seqlens[0] = 0,
+ *                 cu_seqlens[N] = total_tokens, non-decreasing (read on the
+ *                 device; not checked)
+ *   initial_state [N, H, Dk, Dv] or NULL;  final_state [N, H, Dk, Dv] or NULL
+ * Other arguments as for kda_prefill_chunked.
+ */
+kda_status kda_prefill_varlen(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                              const float* alpha, const float* beta,
+                              const int32_t* cu_seqlens, int N, int total_tokens,
+                              const float* initial_state, float* final_state,
+                              void* o, kda_dtype o_dtype,
+                              int H, int Dk, int Dv, int chunk,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_decode_step -- one token for each of B sessions, the fused recurrent
+ * form: decay the state, read the decayed state's answer for k, write the
+ * corrected value along k, read out with q ("Kimi Delta Attention 完全拆解",
+ * section "一次 KDA 前向究竟发生了什么", the decode sequence; section "Prefill 与
+ * decode 必须走不同 Kernel").  The state is read once and written once.
+ *
+ *   q, k   [B, H, Dk] qkv_dtype;  v [B, H, Dv] qkv_dtype
+ *   alpha  [B, H, Dk] fp32;       beta [B, H] fp32
+ *   state  [B, H, Dk, Dv] fp32, updated IN PLACE
+ *   o      [B, H, Dv] o_dtype
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                           const float* alpha, const float* beta, float* state,
+                           void* o, kda_dtype o_dtype, int B, int H, int Dk, int Dv,
+                           void* stream);
+
+/*
+ * kda_prefill_workspace_size -- device scratch bytes the prefill entry points
+ * need for these sizes.  Independent of T by design (the state is fixed-size,
+ * "Kimi K3 混合线性注意力": the per-session state does not grow with length).
+ * Returns 0 in this version.  Returns (size_t)-1 for invalid sizes.
+ */
+size_t kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv, int chunk);
+
+/* Static string naming a status code. */
+const char* kda_status_string(kda_status s);
+
+/* Thread-local detail of the last error returned on this thread ("" if none). */
+const char* kda_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

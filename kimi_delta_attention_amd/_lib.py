@@ -1,0 +1,185 @@
+"""ctypes binding of libkda.so (the C ABI in include/kda.h).
+
+Argument marshalling only: tensors are passed as device pointers with their
+sizes, on torch's current HIP stream; every step of the operator runs in the
+library's HIP kernels.  There is no fallback: if the library is missing or
+cannot be loaded, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+_STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_HIP"}
+
+EXPORTED = ("kda_prefill_chunked", "kda_prefill_varlen", "kda_decode_step",
+            "kda_prefill_workspace_size", "kda_status_string", "kda_last_error_message")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads libkda.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                           "python kimi_delta_attention_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.kda_prefill_chunked.argtypes = [P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P]
+    lib.kda_prefill_chunked.restype = I
+    lib.kda_prefill_varlen.argtypes = [P, P, P, I, P, P, P, I, I, P, P, P, I, I, I, I, I, P, Z, P]
+    lib.kda_prefill_varlen.restype = I
+    lib.kda_decode_step.argtypes = [P, P, P, I, P, P, P, P, I, I, I, I, I, P]
+    lib.kda_decode_step.restype = I
+    lib.kda_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.kda_prefill_workspace_size.restype = Z
+    lib.kda_status_string.argtypes = [I]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_error_message.argtypes = []
+    lib.kda_last_error_message.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load().kda_last_error_message().decode()
+        raise KdaError(status, msg)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def workspace_size(B: int, T: int, H: int, Dk: int, Dv: int, chunk: int = 64) -> int:
+    return int(load().kda_prefill_workspace_size(B, T, H, Dk, Dv, chunk))
+
+
+def prefill_chunked(q, k, v, alpha, beta, initial_state=None, out_dtype=torch.float32,
+                    final_state: bool | torch.Tensor = True, o: torch.Tensor | None = None):
+    """Dense chunked prefill.  q, k, alpha [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H];
+    initial_state [B,H,Dk,Dv] fp32 or None.  Returns (o, final_state)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(alpha, "alpha", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    if k.shape != q.shape or alpha.shape != q.shape or v.shape != (B, T, H, Dv) \
+            or beta.shape != (B, T, H):
+        raise ValueError("inconsistent shapes")
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev)
+        if initial_state.shape != (B, H, Dk, Dv):
+            raise ValueError("initial_state must be [B, H, Dk, Dv]")
+    if o is None:
+        o = torch.empty(B, T, H, Dv, dtype=out_dtype, device=dev)
+    else:
+        _need(o, "o", None, dev)
+    if isinstance(final_state, torch.Tensor):
+        fs = final_state
+        _need(fs, "final_state", torch.float32, dev)
+    elif final_state:
+        fs = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev)
+    else:
+        fs = None
+    _check(load().kda_prefill_chunked(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(alpha), _ptr(beta), _ptr(initial_state),
+        _ptr(fs), _ptr(o), _dt(o), B, T, H, Dk, Dv, 64, None, 0, _stream(dev)))
+    return o, fs
+
+
+def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None,
+                   out_dtype=torch.float32, final_state: bool | torch.Tensor = True,
+                   o: torch.Tensor | None = None):
+    """Packed prefill.  q, k, alpha [1,NTOK,H,Dk]; v [1,NTOK,H,Dv]; beta [1,NTOK,H];
+    cu_seqlens int32 [N+1] on the device; states [N,H,Dk,Dv].  Returns (o, final_state)."""
+    _, NT, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    if q.shape[0] != 1:
+        raise ValueError("packed inputs have B == 1")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(alpha, "alpha", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    N = cu_seqlens.numel() - 1
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev)
+        if initial_state.shape != (N, H, Dk, Dv):
+            raise ValueError("initial_state must be [N, H, Dk, Dv]")
+    if o is None:
+        o = torch.empty(1, NT, H, Dv, dtype=out_dtype, device=dev)
+    if isinstance(final_state, torch.Tensor):
+        fs = final_state
+    elif final_state:
+        fs = torch.empty(N, H, Dk, Dv, dtype=torch.float32, device=dev)
+    else:
+        fs = None
+    _check(load().kda_prefill_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), N, NT,
+        _ptr(initial_state), _ptr(fs), _ptr(o), _dt(o), H, Dk, Dv, 64, None, 0, _stream(dev)))
+    return o, fs
+
+
+def decode_step(q, k, v, alpha, beta, state, out_dtype=torch.float32,
+                o: torch.Tensor | None = None):
+    """One token per session.  q, k, alpha [B,H,Dk]; v [B,H,Dv]; beta [B,H];
+    state [B,H,Dk,Dv] fp32 updated in place.  Returns o [B,H,Dv]."""
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(alpha, "alpha", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    _need(state, "state", torch.float32, dev)
+    if state.shape != (B, H, Dk, Dv) or beta.shape != (B, H) or alpha.shape != q.shape:
+        raise ValueError("inconsistent shapes")
+    if o is None:
+        o = torch.empty(B, H, Dv, dtype=out_dtype, device=dev)
+    _check(load().kda_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o),
+        _dt(o), B, H, Dk, Dv, _stream(dev)))
+    return o

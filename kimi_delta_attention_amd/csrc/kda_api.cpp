@@ -1,0 +1,160 @@
+// kda_api.cpp -- the C ABI declared in include/kda.h: argument validation on the
+// host (before any HIP call), dispatch to the kernels, status strings.
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+kda_status fail(kda_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kda_status fail(kda_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+kda_status ok() {
+  g_msg[0] = '\0';
+  return KDA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kda_status check_common(const void* q, const void* k, const void* v, kda_dtype qkv,
+                        const float* alpha, const float* beta, const void* o, kda_dtype od,
+                        int H, int Dk, int Dv) {
+  if (!q || !k || !v || !alpha || !beta || !o)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, alpha, beta and o must be non-null");
+  if (qkv != KDA_F32 && qkv != KDA_BF16) return fail(KDA_ERR_INVALID_ARGUMENT, "bad qkv_dtype");
+  if (od != KDA_F32 && od != KDA_BF16) return fail(KDA_ERR_INVALID_ARGUMENT, "bad o_dtype");
+  if (H <= 0 || Dk <= 0 || Dv <= 0)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "H, Dk and Dv must be positive");
+  // token tensors are read and written element by element: natural alignment suffices
+  const uintptr_t m_in = qkv == KDA_BF16 ? 1u : 3u, m_out = od == KDA_BF16 ? 1u : 3u;
+  if (((uintptr_t)q & m_in) || ((uintptr_t)k & m_in) || ((uintptr_t)v & m_in) ||
+      ((uintptr_t)alpha & 3u) || ((uintptr_t)beta & 3u) || ((uintptr_t)o & m_out))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "tensor pointers must be aligned to their element size");
+  return KDA_OK;
+}
+
+kda_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return ok();
+  return fail(KDA_ERR_HIP, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+const char* kda_last_error_message(void) { return g_msg; }
+
+size_t kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv, int chunk) {
+  if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || chunk != 64) return (size_t)-1;
+  return 0;
+}
+
+static kda_status prefill_common(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                                 const float* alpha, const float* beta,
+                                 const int32_t* cu_seqlens, int n_seq, int T,
+                                 const float* initial_state, float* final_state, void* o,
+                                 kda_dtype o_dtype, int H, int Dk, int Dv, int chunk,
+                                 void* stream) {
+  if (n_seq < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative batch or length");
+  if (n_seq == 0) return ok();
+  if (T > 0 || cu_seqlens) {
+    kda_status s = check_common(q, k, v, qkv_dtype, alpha, beta, o, o_dtype, H, Dk, Dv);
+    if (s != KDA_OK) return s;
+  } else if (H <= 0 || Dk <= 0 || Dv <= 0) {
+    // T == 0: no token tensor is read; the kernel only hands the state through
+    return fail(KDA_ERR_INVALID_ARGUMENT, "H, Dk and Dv must be positive");
+  }
+  if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk must be 64 (got %d)", chunk);
+  if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "state pointers must be 16-byte aligned");
+  if (!kda::prefill_supported(qkv_dtype == KDA_BF16, Dk, Dv))
+    return fail(KDA_ERR_UNSUPPORTED,
+                "unsupported head dims Dk=%d Dv=%d for %s inputs (bf16: Dk,Dv in {64,128}; "
+                "fp32: Dk=64, Dv in {64,128})",
+                Dk, Dv, qkv_dtype == KDA_BF16 ? "bf16" : "fp32");
+  // token offsets are 64-bit in the kernels; the head / row counts must fit int32
+  if ((long long)n_seq * H * (Dv / 64) > 0x7fffffffLL)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "too many (sequence, head) work items");
+  if (T == 0 && !cu_seqlens && !final_state) return ok();
+  kda::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+  a.initial_state = initial_state; a.final_state = final_state; a.o = o;
+  a.qkv_bf16 = qkv_dtype == KDA_BF16; a.o_bf16 = o_dtype == KDA_BF16;
+  a.cu_seqlens = cu_seqlens; a.n_seq = n_seq; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv;
+  a.stream = stream;
+  return hip_status(kda::launch_prefill(a));
+}
+
+kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                               const float* alpha, const float* beta,
+                               const float* initial_state, float* final_state, void* o,
+                               kda_dtype o_dtype, int B, int T, int H, int Dk, int Dv, int chunk,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (B < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B and T must be >= 0");
+  return prefill_common(q, k, v, qkv_dtype, alpha, beta, nullptr, B, T, initial_state,
+                        final_state, o, o_dtype, H, Dk, Dv, chunk, stream);
+}
+
+kda_status kda_prefill_varlen(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                              const float* alpha, const float* beta, const int32_t* cu_seqlens,
+                              int N, int total_tokens, const float* initial_state,
+                              float* final_state, void* o, kda_dtype o_dtype, int H, int Dk,
+                              int Dv, int chunk, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (N < 0 || total_tokens < 0)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "N and total_tokens must be >= 0");
+  if (N > 0 && !cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens must be non-null");
+  if (N > 0 && ((uintptr_t)cu_seqlens & 3u))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
+  return prefill_common(q, k, v, qkv_dtype, alpha, beta, cu_seqlens, N, total_tokens,
+                        initial_state, final_state, o, o_dtype, H, Dk, Dv, chunk, stream);
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                           const float* alpha, const float* beta, float* state, void* o,
+                           kda_dtype o_dtype, int B, int H, int Dk, int Dv, void* stream) {
+  if (B < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B must be >= 0");
+  if (B == 0) return ok();
+  kda_status s = check_common(q, k, v, qkv_dtype, alpha, beta, o, o_dtype, H, Dk, Dv);
+  if (s != KDA_OK) return s;
+  if (!state) return fail(KDA_ERR_INVALID_ARGUMENT, "state must be non-null");
+  if (!aligned16(state)) return fail(KDA_ERR_INVALID_ARGUMENT, "state must be 16-byte aligned");
+  if (!((Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128)))
+    return fail(KDA_ERR_UNSUPPORTED, "Dk and Dv must be 64 or 128 (got %d, %d)", Dk, Dv);
+  if ((long long)B * H > 0x7fffffffLL) return fail(KDA_ERR_INVALID_ARGUMENT, "B*H too large");
+  kda::DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state = state; a.o = o;
+  a.qkv_bf16 = qkv_dtype == KDA_BF16; a.o_bf16 = o_dtype == KDA_BF16;
+  a.B = B; a.H = H; a.Dk = Dk; a.Dv = Dv; a.stream = stream;
+  return hip_status(kda::launch_decode(a));
+}
+
+}  // extern "C"

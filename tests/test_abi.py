@@ -1,0 +1,108 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad arguments before launching anything.  None of
+these calls reaches the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import kimi_delta_attention_amd as kda
+from kimi_delta_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+F32, BF16 = 0, 1
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+FAKE = 0x10000  # an aligned non-null address; never dereferenced by these calls
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kda.load()
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    for n in names:
+        assert getattr(lib, n) is not None
+        assert re.search(rf"\bT {n}$", out, flags=re.M), n
+
+
+def test_status_strings():
+    lib = kda.load()
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(1) == b"KDA_ERR_INVALID_ARGUMENT"
+    assert lib.kda_status_string(2) == b"KDA_ERR_UNSUPPORTED"
+    assert lib.kda_status_string(3) == b"KDA_ERR_HIP"
+
+
+def test_workspace_size_is_t_independent():
+    """The state is fixed-size; scratch must not grow with the sequence length."""
+    sizes = {kda.workspace_size(1, T, 96, 128, 128) for T in (1, 256, 8192, 1 << 20)}
+    assert len(sizes) == 1
+    assert kda.workspace_size(1, 256, 96, 128, 128, chunk=32) == ctypes.c_size_t(-1).value
+
+
+def _prefill(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, qd=BF16, alpha=FAKE, beta=FAKE, s0=None, s1=None, o=FAKE,
+             od=F32, B=1, T=128, H=2, Dk=128, Dv=128, chunk=64)
+    a.update(over)
+    lib = kda.load()
+    return lib.kda_prefill_chunked(a["q"], a["k"], a["v"], a["qd"], a["alpha"], a["beta"],
+                                   a["s0"], a["s1"], a["o"], a["od"], a["B"], a["T"], a["H"],
+                                   a["Dk"], a["Dv"], a["chunk"], None, 0, None)
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(q=None), INVALID),
+    (dict(beta=None), INVALID),
+    (dict(o=FAKE + 2), INVALID),
+    (dict(q=FAKE + 1), INVALID),
+    (dict(s0=FAKE + 8), INVALID),
+    (dict(H=0), INVALID),
+    (dict(T=-1), INVALID),
+    (dict(qd=7), INVALID),
+    (dict(chunk=32), UNSUPPORTED),
+    (dict(Dk=96), UNSUPPORTED),
+    (dict(Dv=256), UNSUPPORTED),
+    (dict(qd=F32, Dk=128), UNSUPPORTED),
+    (dict(B=0), OK),
+])
+def test_prefill_argument_validation(over, expect):
+    assert _prefill(**over) == expect
+    if expect != OK:
+        assert len(kda.load().kda_last_error_message()) > 0
+
+
+def test_varlen_and_decode_validation():
+    lib = kda.load()
+    # varlen: missing cu_seqlens
+    assert lib.kda_prefill_varlen(FAKE, FAKE, FAKE, BF16, FAKE, FAKE, None, 4, 100, None, None,
+                                  FAKE, F32, 2, 128, 128, 64, None, 0, None) == INVALID
+    # varlen: N == 0 is a no-op
+    assert lib.kda_prefill_varlen(None, None, None, BF16, None, None, None, 0, 0, None, None,
+                                  None, F32, 2, 128, 128, 64, None, 0, None) == OK
+    # decode: missing state, bad head dim, misaligned input, empty batch
+    assert lib.kda_decode_step(FAKE, FAKE, FAKE, BF16, FAKE, FAKE, None, FAKE, F32, 4, 2, 128,
+                               128, None) == INVALID
+    assert lib.kda_decode_step(FAKE, FAKE, FAKE, BF16, FAKE, FAKE, FAKE, FAKE, F32, 4, 2, 96,
+                               128, None) == UNSUPPORTED
+    assert lib.kda_decode_step(FAKE + 1, FAKE, FAKE, BF16, FAKE, FAKE, FAKE, FAKE, F32, 4, 2, 128,
+                               128, None) == INVALID
+    assert lib.kda_decode_step(None, None, None, BF16, None, None, None, None, F32, 0, 2, 128,
+                               128, None) == OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(ValueError):
+        kda.prefill_chunked(q, q, q, q, torch.zeros(1, 4, 1))

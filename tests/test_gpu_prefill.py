@@ -1,0 +1,205 @@
+"""Chunked and packed prefill on the GPU against the fp64 oracle and against the
+GPU decode step replayed token by token."""
+import numpy as np
+import pytest
+import torch
+
+import kimi_delta_attention_amd as kda
+import oracle
+from kimi_delta_attention_amd import synth
+from tests._common import TOL_BF16, TOL_BF16_OUT, TOL_F32, dev, oracle_heads, rel, to
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, d, out_dtype=torch.float32):
+    return kda.prefill_chunked(to(inp.q, d), to(inp.k, d), to(inp.v, d), to(inp.alpha, d),
+                               to(inp.beta, d), initial_state=to(inp.state, d),
+                               out_dtype=out_dtype)
+
+
+def test_tiny_fp32_full():
+    """fp32 workload: B=1, H=2, T=256, d=64, zero initial state; tolerance 1e-5."""
+    d = dev()
+    w = synth.WORKLOADS["tiny_fp32"]
+    inp = synth.make_dense(w["B"], w["T"], w["H"], w["D"], w["D"], seed=w["seed"],
+                           qkv_dtype=w["qkv_dtype"], shift=w["shift"], state_std=None)
+    o_ref, s_ref = oracle.recurrent(inp.q, inp.k, inp.v, inp.alpha, inp.beta)
+    o, s = _run(inp, d)
+    torch.cuda.synchronize()
+    assert rel(o.cpu(), o_ref) <= TOL_F32
+    assert rel(s.cpu(), s_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("B,T,H,Dk,Dv", [
+    (2, 200, 3, 128, 128),   # several chunks and a ragged tail
+    (1, 77, 2, 64, 64),
+    (1, 130, 2, 128, 64),
+    (1, 65, 1, 64, 128),
+    (1, 1, 2, 128, 128),
+    (1, 64, 2, 128, 128),
+    (1, 63, 2, 128, 128),
+])
+def test_small_bf16_against_oracle(B, T, H, Dk, Dv):
+    d = dev()
+    inp = synth.make_dense(B, T, H, Dk, Dv, seed=100 + T + Dk, state_std=0.02)
+    o_ref, s_ref = oracle.recurrent(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
+                                    initial_state=inp.state)
+    o, s = _run(inp, d)
+    torch.cuda.synchronize()
+    assert rel(o.cpu(), o_ref) <= TOL_BF16
+    assert rel(s.cpu(), s_ref) <= TOL_BF16
+
+
+def test_fp32_inputs_dv128_and_bf16_output():
+    d = dev()
+    inp = synth.make_dense(1, 150, 2, 64, 128, seed=31, qkv_dtype=torch.float32, shift=0.0,
+                           state_std=0.02)
+    o_ref, s_ref = oracle.recurrent(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
+                                    initial_state=inp.state)
+    o, s = _run(inp, d)
+    assert rel(o.cpu(), o_ref) <= TOL_F32 and rel(s.cpu(), s_ref) <= TOL_F32
+    o, s = _run(inp, d, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert rel(o.float().cpu(), o_ref) <= TOL_BF16_OUT
+
+
+@pytest.mark.parametrize("kind", ["slow_decay", "alpha_one", "bounded_gate"])
+def test_decay_regimes(kind):
+    """Slow decay (mean alpha ~0.97), alpha = 1 (DeltaNet) and the bounded gate
+    g = -5 sigmoid(z) of "Kimi K3 的 KDA" section 6: the state carry dominates."""
+    d = dev()
+    if kind == "slow_decay":
+        inp = synth.make_dense(1, 1024, 4, 128, 128, seed=41, shift=-4.0)
+    elif kind == "alpha_one":
+        inp = synth.make_dense(1, 1024, 4, 128, 128, seed=42, alpha_one=True)
+    else:
+        inp = synth.make_dense(1, 1024, 4, 128, 128, seed=43)
+        g = torch.Generator().manual_seed(44)
+        z = torch.randn(inp.alpha.shape, generator=g, dtype=torch.float64)
+        inp.alpha = torch.exp(-5.0 * torch.sigmoid(z)).float()
+    o_ref, s_ref = oracle.recurrent(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
+                                    initial_state=inp.state)
+    o, s = _run(inp, d)
+    torch.cuda.synchronize()
+    assert rel(o.cpu(), o_ref) <= TOL_BF16
+    assert rel(s.cpu(), s_ref) <= TOL_BF16
+
+
+def test_zero_length_hands_state_through():
+    d = dev()
+    s0 = synth.make_state(2, 3, 128, 128, seed=5).to(d)
+    e = torch.empty(2, 0, 3, 128, dtype=torch.bfloat16, device=d)
+    a = torch.empty(2, 0, 3, 128, dtype=torch.float32, device=d)
+    o, s = kda.prefill_chunked(e, e, e, a, torch.empty(2, 0, 3, device=d), initial_state=s0)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 3, 128) and torch.equal(s, s0)
+
+
+def test_two_segments_equal_whole():
+    """Prefill in two calls with the state handed over matches one call."""
+    d = dev()
+    inp = synth.make_dense(1, 300, 2, 128, 128, seed=51)
+    o, s = _run(inp, d)
+    cut = 130
+    o1, s1 = kda.prefill_chunked(*(x[:, :cut].contiguous().to(d) for x in
+                                   (inp.q, inp.k, inp.v, inp.alpha, inp.beta)),
+                                 initial_state=inp.state.to(d))
+    o2, s2 = kda.prefill_chunked(*(x[:, cut:].contiguous().to(d) for x in
+                                   (inp.q, inp.k, inp.v, inp.alpha, inp.beta)),
+                                 initial_state=s1)
+    torch.cuda.synchronize()
+    assert rel(torch.cat([o1, o2], 1).cpu(), o.cpu()) <= TOL_BF16
+    assert rel(s2.cpu(), s.cpu()) <= TOL_BF16
+
+
+def _k3_8k(d):
+    w = synth.WORKLOADS["k3_prefill_8k"]
+    return synth.make_dense(w["B"], w["T"], w["H"], w["D"], w["D"], seed=w["seed"],
+                            state_std=w["state_std"], device=d)
+
+
+def test_k3_prefill_8k_sampled_heads():
+    """K3-shaped layer (B=1, H=96, T=8192, d=128) at full size; the oracle runs on
+    8 heads spread over the head axis (all tokens)."""
+    d = dev()
+    inp = _k3_8k(d)
+    o, s = _run(inp, d)
+    torch.cuda.synchronize()
+    heads = [0, 13, 27, 40, 53, 66, 81, 95]
+    o_ref, s_ref = oracle_heads(inp, heads)
+    assert rel(o[:, :, heads].cpu(), o_ref) <= TOL_BF16
+    assert rel(s[:, heads].cpu(), s_ref) <= TOL_BF16
+    # determinism: a second launch is bitwise identical
+    o2, s2 = _run(inp, d)
+    assert torch.equal(o, o2) and torch.equal(s, s2)
+
+
+def test_k3_prefill_8k_matches_decode_replay():
+    """All 96 heads: chunked prefill vs the GPU decode step replayed token by token."""
+    d = dev()
+    inp = _k3_8k(d)
+    o, s = _run(inp, d)
+    state = inp.state.clone()
+    T = inp.q.shape[1]
+    orep = torch.empty_like(o)
+    for t in range(T):
+        kda.decode_step(inp.q[:, t], inp.k[:, t], inp.v[:, t], inp.alpha[:, t], inp.beta[:, t],
+                        state, o=orep[:, t])
+    torch.cuda.synchronize()
+    assert rel(o.cpu(), orep.cpu()) <= TOL_BF16
+    assert rel(s.cpu(), state.cpu()) <= TOL_BF16
+
+
+def _varlen_case(lengths, H, D, seed, d):
+    return synth.make_varlen(lengths, H, D, D, seed=seed, device=d)
+
+
+def _run_varlen(inp, d):
+    return kda.prefill_varlen(inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.cu_seqlens,
+                              initial_state=inp.state)
+
+
+def test_varlen_edges_and_isolation():
+    """Empty, 1-token, chunk-boundary and ragged sequences in one packed batch; each
+    sequence must equal the oracle and, bitwise, its own solo run."""
+    d = dev()
+    lengths = [0, 1, 63, 64, 65, 200, 7]
+    inp = _varlen_case(lengths, 3, 128, seed=61, d=d)
+    o, s = _run_varlen(inp, d)
+    torch.cuda.synchronize()
+    cu = inp.cu_seqlens.cpu().numpy()
+    o_ref, s_ref = oracle.recurrent(inp.q.cpu(), inp.k.cpu(), inp.v.cpu(), inp.alpha.cpu(),
+                                    inp.beta.cpu(), cu_seqlens=cu, initial_state=inp.state.cpu())
+    assert rel(o.cpu(), o_ref) <= TOL_BF16
+    assert rel(s.cpu(), s_ref) <= TOL_BF16
+    for i in range(len(lengths)):
+        sl = slice(int(cu[i]), int(cu[i + 1]))
+        oi, si = kda.prefill_chunked(*(x[:, sl].contiguous() for x in
+                                       (inp.q, inp.k, inp.v, inp.alpha, inp.beta)),
+                                     initial_state=inp.state[i:i + 1].contiguous())
+        assert torch.equal(oi, o[:, sl]) and torch.equal(si, s[i:i + 1])
+
+
+def test_varlen_16_sequences_sampled():
+    """Packed workload: 16 sequences, lengths uniform in [1024, 16384] from the seed,
+    H=96, d=128, per-sequence initial / final state.  The oracle runs on 2 heads of
+    every sequence; 3 sequences are also compared bitwise with solo runs."""
+    d = dev()
+    w = synth.WORKLOADS["varlen_16"]
+    lengths = synth.varlen_lengths(w["N"], w["lo"], w["hi"], seed=w["seed"])
+    inp = _varlen_case(lengths, w["H"], w["D"], seed=w["seed"], d=d)
+    o, s = _run_varlen(inp, d)
+    torch.cuda.synchronize()
+    cu = inp.cu_seqlens.cpu().numpy()
+    heads = [7, 88]
+    o_ref, s_ref = oracle_heads(inp, heads, cu=cu)
+    assert rel(o[:, :, heads].cpu(), o_ref) <= TOL_BF16
+    assert rel(s[:, heads].cpu(), s_ref) <= TOL_BF16
+    order = np.argsort(lengths)
+    for i in (int(order[0]), int(order[len(order) // 2]), int(order[-1])):
+        sl = slice(int(cu[i]), int(cu[i + 1]))
+        oi, si = kda.prefill_chunked(*(x[:, sl].contiguous() for x in
+                                       (inp.q, inp.k, inp.v, inp.alpha, inp.beta)),
+                                     initial_state=inp.state[i:i + 1].contiguous())
+        assert torch.equal(oi, o[:, sl]) and torch.equal(si, s[i:i + 1])
