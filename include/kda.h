@@ -18,7 +18,8 @@
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller, dense and
  *    row-major in the shapes given, aligned to their element size; state
- *    pointers (initial_state, final_state, state) 16-byte aligned.  The library never
+ *    pointers (initial_state, final_state, state) and, for the bf16 prefill
+ *    entry points, q, k, v and alpha 16-byte aligned.  The library never
  *    allocates device memory and keeps no state besides cached device
  *    properties.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).

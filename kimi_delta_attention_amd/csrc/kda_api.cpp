@@ -89,6 +89,10 @@ static kda_status prefill_common(const void* q, const void* k, const void* v, kd
     return fail(KDA_ERR_INVALID_ARGUMENT, "H, Dk and Dv must be positive");
   }
   if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk must be 64 (got %d)", chunk);
+  // the bf16 kernel reads q, k, v and alpha with 8- and 16-byte vector loads
+  if (qkv_dtype == KDA_BF16 && (T > 0 || cu_seqlens) &&
+      (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "bf16 prefill needs 16-byte aligned q, k, v and alpha");
   if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
     return fail(KDA_ERR_INVALID_ARGUMENT, "state pointers must be 16-byte aligned");
   if (!kda::prefill_supported(qkv_dtype == KDA_BF16, Dk, Dv))

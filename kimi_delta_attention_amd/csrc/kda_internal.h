@@ -31,7 +31,8 @@ struct PrefillArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
-hipError_t launch_prefill(const PrefillArgs& a);
+hipError_t launch_prefill(const PrefillArgs& a);      // dispatch (kda_prefill.hip)
+hipError_t launch_prefill_f32(const PrefillArgs& a);  // fp32 inputs (kda_prefill_f32.hip)
 bool prefill_supported(bool qkv_bf16, int Dk, int Dv);
 
 }  // namespace kda

@@ -1,161 +1,189 @@
-// kda_prefill.hip -- chunked KDA prefill for gfx950 (dense and packed varlen).
+// kda_prefill.hip -- chunked KDA prefill for bf16 inputs on gfx950 (dense and
+// packed varlen), plus the dispatch of both prefill kernels.
 //
-// The chunk form of the recurrence S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1}
-// + b_t k_t v_t^T, o_t = S_t^T q_t ("Kimi Delta Attention 完全拆解", section
-// "chunk 内并行、chunk 间递推"; "Kimi K3 的 KDA" section 5; "Kimi K3模型架构详解"
-// sections 3.4-3.5).  For a 64-token chunk with entry state S and in-chunk
-// cumulative decay Gamma_r = prod_{s<=r} a_s (per key channel):
+// Chunk form of S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,
+// o_t = S_t^T q_t ("Kimi Delta Attention 完全拆解", section "chunk 内并行、chunk 间
+// 递推"; "Kimi K3 的 KDA" section 5; "Kimi K3模型架构详解" sections 3.4-3.5).  For a
+// 64-token chunk with entry state S and in-chunk cumulative decay
+// Gamma_r = prod_{s<=r} a_s (per key channel):
 //
-//   A_rj  = b_r sum_c k_rc k_jc Gamma_rc / Gamma_jc           (j < r)
-//   T     = (I + A)^{-1}                                       (UT transform)
-//   W     = T Diag(b) (Gamma * K),   U = T Diag(b) V
-//   P     = U - W S                                            (pseudo-values)
-//   Mqk_rj = sum_c q_rc k_jc Gamma_rc / Gamma_jc              (j <= r)
-//   O     = (Gamma * Q) S + Mqk P
-//   S'    = Diag(Gamma_C) S + Ktil^T P,  Ktil_j = (Gamma_C / Gamma_j) * k_j
+//   A_rj   = b_r sum_c k_rc k_jc Gamma_rc / Gamma_jc      (j < r)
+//   T      = (I + A)^{-1}                                  (UT transform)
+//   W      = T Diag(b) (Gamma * K),   U = T Diag(b) V
+//   P      = U - W S                                       (per-token corrections)
+//   Mqk_rj = sum_c q_rc k_jc Gamma_rc / Gamma_jc          (j <= r)
+//   O      = (Gamma * Q) S + Mqk P
+//   S'     = Diag(Gamma_C) S + Ktil^T P,   Ktil_j = (Gamma_C / Gamma_j) * k_j
 //
-// (P's rows are the per-token corrections u_r = b_r (v_r - Sbar_r^T k_r).)
-// The decay ratios inside A and Mqk are split over 16-token tiles: with
-// P_r = product of a from the start of r's tile up to r, a pair (r in tile m,
-// j in tile n) uses left factor P_r (<= 1) and right factor (E_n / P_j) times
-// the whole-tile decays E_i of the tiles strictly between (all <= 1), and the
-// diagonal tile uses 1 / P_j, bounded by the decay of one 16-token tile (the
-// tiling the bounded gate of "Kimi K3 的 KDA" section 6 is made for).
+// Decay ratios inside A and Mqk are factored over 16-token tiles: with P_r the
+// product of a from the start of r's tile up to r and E_n the whole-tile
+// product, a pair (r in tile m, j in tile n < m) uses P_r and
+// (E_n / P_j) * prod_{n<i<m} E_i, both <= 1; the diagonal tile uses P_r and
+// 1 / P_j, bounded by one tile's decay (the tiling the bounded gate of
+// "Kimi K3 的 KDA" section 6 is made for).
 //
-// One workgroup (4 waves) owns (sequence, head, 64-wide value slice) and walks
-// the chunks in order; the state slice lives in MFMA accumulators for the
-// whole sequence.  Products run on bf16 MFMA 16x16x32; products whose accuracy
-// matters are done in split bf16 (hi*hi + hi*lo + lo*hi), see Pol below.  The
-// fp32-input / Dk = 64 path uses fp32 MFMA 16x16x4 throughout.
+// Work decomposition.  One workgroup (4 waves) owns (sequence, head, 64-wide
+// value slice) and walks the chunks in order; the state slice stays in MFMA
+// accumulators for the whole sequence.  Wave w owns token tile w (tokens
+// 16w..16w+15) of every chunk: lane l holds token 16w + l%16 and, per 32-channel
+// block kb, the 8 channels 32kb + 4g + {0..3} and 32kb + 16 + 4g + {0..3}
+// (g = l/16).  That set is exactly the k range an MFMA 16x16x32 output tile of a
+// transposed product delivers to a lane, so outputs chain into the next
+// product's operands in registers: (Gamma*K)^T T^T gives W in the operand layout
+// of W S, and Mqk^T tiles give the operand of Mqk P.  Products contracted over
+// the token axis read row-major [token][channel] LDS tiles through the gfx950
+// transpose read (ds_read_b64_tr_b16).  The within-tile decay products are a
+// 16-lane DPP scan.
+//
+// Precision: bf16 MFMA with split-bf16 operands (x = hi + lo, product
+// hi*hi + hi*lo + lo*hi) everywhere except A (single pass); U and (Gamma*Q) S
+// split only the side that is not exact in bf16.
 #include "kda_common.h"
 #include "kda_internal.h"
 
 namespace kda {
+namespace {
 
-constexpr int CH = 64;   // chunk length
-constexpr int NTH = 256; // threads per workgroup
+constexpr int CH = 64;    // chunk
+constexpr int NTH = 256;  // 4 waves
+constexpr int BV = 64;    // value slice per workgroup
 
-// LDS layout.  Arrays are MFMA operands stored k-contiguous ([M][K] for A
-// operands, [N][K] for B operands); a split array is its hi part followed by
-// its lo part.  Arrays of different phases share space; the static_asserts
-// check that arrays alive at the same time do not overlap.
-template <int DK, int BV, bool F32OPS>
-struct Layout {
-  static constexpr int ES = F32OPS ? 4 : 2;
-  static constexpr bool LO = !F32OPS;
-  static constexpr int ldK = DK + 8;   // rows indexed by token, DK channels
-  static constexpr int ldC = CH + 8;   // rows of 64 tokens
-  static constexpr int ldA = CH + 4;   // fp32 A and T
-  static constexpr int sz(int rows, int ld, bool lo) { return rows * ld * ES * (lo ? 2 : 1); }
-  static constexpr int KL = sz(CH, ldK, false);
-  static constexpr int QL = sz(CH, ldK, LO);
-  static constexpr int RT = sz(160, ldK, LO);
-  static constexpr int VT = sz(BV, ldC, false);
-  static constexpr int AF = CH * ldA * 4;
-  static constexpr int TF = CH * ldA * 4;
-  static constexpr int MQ = sz(CH, ldC, LO);
-  static constexpr int WO = sz(CH, ldK, LO);
-  static constexpr int TB = sz(CH, ldC, LO);
-  static constexpr int GK = sz(DK, ldC, LO);
-  static constexpr int QT = sz(CH, ldK, false);
-  static constexpr int KT = sz(DK, ldC, LO);
-  static constexpr int ST = sz(BV, ldK, LO);
-  static constexpr int PT = sz(BV, ldC, LO);
-  // serial phase: MQ | WO | QT | KT | ST | PT
-  static constexpr int oMQ = 0, oWO = oMQ + MQ, oQT = oWO + WO, oKT = oQT + QT, oST = oKT + KT,
-                       oPT = oST + ST, endSerial = oPT + PT;
-  // A / Mqk phase: KL | QL | RT ; V is parked in the P region
-  static constexpr int oKL = 0, oQL = oKL + KL, oRT = oQL + QL, endA = oRT + RT;
-  static constexpr int oVT = oPT;
-  // triangular solve: T in the W region, A in the S region
-  static constexpr int oTF = oWO, oAF = oST;
-  // W / U phase: TB | GK from the Q region on
-  static constexpr int oTB = oQT, oGK = oTB + TB;
-  // fixed tail: per-tile decays E[4][DK], chunk decay gC[DK], beta[64]
-  static constexpr int oES = endSerial > oVT + VT ? endSerial : oVT + VT;
-  static constexpr int oGC = oES + 4 * DK * 4;
-  static constexpr int oBS = oGC + DK * 4;
-  static constexpr int total = oBS + CH * 4;
-  static_assert(endA <= oVT, "phase-A operands overlap V");
-  static_assert(TF <= WO && AF <= ST, "A/T placement");
-  static_assert(oTB >= oTF + TF, "TB overlaps T");
-  static_assert(oGK + GK <= oVT, "W-phase operands overlap V");
-  static_assert(total <= 163840, "LDS budget (160 KiB)");
-};
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
+typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
 
-// Precision policy per product (bf16 path).  A is single-pass; U splits only
-// the T side because V is exact in bf16; (Gamma*Q) S splits only S; every other
-// product splits both operands.
-struct Pol {
-  static constexpr int A = P_SINGLE, M = P_SPLIT_AB, W = P_SPLIT_AB, U = P_SPLIT_A,
-                       WS = P_SPLIT_AB, QS = P_SPLIT_B, MP = P_SPLIT_AB, KP = P_SPLIT_AB;
-};
-
-template <typename TIn>
-__device__ __forceinline__ float ldf(const TIn* p, size_t i);
-template <>
-__device__ __forceinline__ float ldf<float>(const float* p, size_t i) { return p[i]; }
-template <>
-__device__ __forceinline__ float ldf<bf16>(const bf16* p, size_t i) { return (float)p[i]; }
-
-// Pairs of 16-token tiles (row tile, column tile) of A / Mqk computed by each
-// wave; n < 0 marks an upper block the wave zeroes in Mqk instead.
-__device__ __forceinline__ void pair_of(int w, int p, int& mm, int& n) {
-  const int tab[4][3][2] = {{{0, 0}, {3, 0}, {3, 1}},
-                            {{1, 0}, {1, 1}, {3, 2}},
-                            {{2, 0}, {2, 1}, {0, -1}},
-                            {{2, 2}, {3, 3}, {2, -3}}};
-  mm = tab[w][p][0];
-  n = tab[w][p][1];
+// Operand fragment (16 columns m0.., 8 k values per lane) of a row-major
+// [k][m] LDS tile: lane l gets column m0 + l%16 at rows ra..ra+3 and rb..rb+3
+// (ra, rb chosen per 16-lane group).  Two transpose reads, each of which
+// gives lane i of a 16-lane group element i%4 of the 8-byte words read by
+// lanes i/4, i/4+4, i/4+8, i/4+12 of that group.
+__device__ __forceinline__ bf16x8 frag_tr(const bf16* X, int ld, int m0, int ra, int rb) {
+  const int j = threadIdx.x & 15;
+  const bf16* pa = X + (ra + (j >> 2)) * ld + m0 + 4 * (j & 3);
+  const bf16* pb = X + (rb + (j >> 2)) * ld + m0 + 4 * (j & 3);
+  const short4v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)pa);
+  const short4v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)pb);
+  const short8v s = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, s);
 }
 
-template <int DK, int BV, bool F32OPS, typename TIn, typename TOut>
-__global__ __launch_bounds__(NTH) void prefill_kernel(
-    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+// 16 contiguous bytes of a k-contiguous LDS row.
+__device__ __forceinline__ bf16x8 frag_ld(const bf16* X, int ld, int row, int k0) {
+  return *reinterpret_cast<const bf16x8*>(X + row * ld + k0 + 8 * ((threadIdx.x & 63) >> 4));
+}
+
+template <int D>
+__device__ __forceinline__ float row_shr_or_one(float x) {
+  // lane i of each 16-lane row gets lane i-D's value; lanes i < D keep 1.0
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      __builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, x), 0x110 + D, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bf16 h = (bf16)x[e];
+    hi[e] = h;
+    lo[e] = (bf16)(x[e] - (float)h);
+  }
+}
+
+__device__ __forceinline__ float bfv(unsigned int packed, int half) {
+  return __builtin_bit_cast(float, half ? (packed & 0xffff0000u) : (packed << 16));
+}
+
+__device__ __forceinline__ void st_bf16x4(bf16* p, const float* x) {
+  // 4 values -> one 8-byte LDS store
+  short4v s;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s[e] = __builtin_bit_cast(short, (bf16)x[e]);
+  *reinterpret_cast<short4v*>(p) = s;
+}
+
+__device__ __forceinline__ void st_split4(bf16* hi, int lo_off, const float* x) {
+  short4v sh, sl;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16 h = (bf16)x[e];
+    sh[e] = __builtin_bit_cast(short, h);
+    sl[e] = __builtin_bit_cast(short, (bf16)(x[e] - (float)h));
+  }
+  *reinterpret_cast<short4v*>(hi) = sh;
+  *reinterpret_cast<short4v*>(hi + lo_off) = sl;
+}
+
+__device__ __forceinline__ floatx4 mma_ab(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
+                                          const bf16x8& bl, floatx4 c) {
+  c = mfma_bf16(ah, bh, c);
+  c = mfma_bf16(ah, bl, c);
+  c = mfma_bf16(al, bh, c);
+  return c;
+}
+
+// LDS plan (bytes).  R0 is reused phase by phase:
+//   A / Mqk:       RT (right operands of every row tile, position order)
+//   solve / W, U:  AF, TF (fp32), TB (T Diag(b), split), VS (V slice)
+//   serial:        ST (state, split), PT (P, split)
+// GK ((Gamma*K), split) and KT (Ktil, split) are [token][channel] tiles that
+// live from operand build to their last product; ES / GC / BS are small.
+template <int DK>
+struct Plan {
+  static constexpr int ldR = DK + 8, ldG = DK + 8, ldA = CH + 4, ldT = CH + 8, ldV = BV + 8,
+                       ldS = DK + 8, ldP = CH + 8;
+  static constexpr int RT = 160 * ldR * 2 * 2;
+  static constexpr int AF = CH * ldA * 4, TF = CH * ldA * 4, TB = CH * ldT * 2 * 2,
+                       VS = CH * ldV * 2;
+  static constexpr int ST = BV * ldS * 2 * 2, PT = BV * ldP * 2 * 2;
+  static constexpr int oRT = 0, oAF = 0, oTF = AF, oTB = AF + TF, oVS = AF + TF + TB,
+                       oST = 0, oPT = ST;
+  static constexpr int r0a = RT, r0b = AF + TF + TB + VS, r0c = ST + PT;
+  static constexpr int R0 = r0a > r0b ? (r0a > r0c ? r0a : r0c) : (r0b > r0c ? r0b : r0c);
+  static constexpr int GK = CH * ldG * 2 * 2, KT = CH * ldG * 2 * 2;
+  static constexpr int oGK = R0, oKT = oGK + GK, oES = oKT + KT, oGC = oES + 4 * DK * 4,
+                       oBS = oGC + DK * 4, total = oBS + CH * 4;
+  static_assert(total <= 163840, "LDS budget (160 KiB)");
+  static_assert((oGK | oKT | oES | oGC | oBS | oTF | oTB | oVS | oPT) % 16 == 0, "alignment");
+};
+
+template <int DK, typename TOut>
+__global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* __restrict__ s_init, float* __restrict__ s_final, TOut* __restrict__ o,
     const int32_t* __restrict__ cu_seqlens, int n_seq, int T, int H, int DV) {
-  using L = Layout<DK, BV, F32OPS>;
-  using Ld = Lds<F32OPS>;
-  using E = typename Ld::T;
-  constexpr int NSEG = DK / 64;        // (tile, channel) segments per thread
-  constexpr int TPC = NTH / DK;        // tiles covered by one pass of the threads
-  constexpr int RPW = DK / 4;          // state rows per wave
-  constexpr int RTW = RPW / 16;        // state row tiles per wave
-  constexpr int NCT = BV / 16;         // value column tiles
-  constexpr int NKB = DK / 32;         // k-blocks over the key axis
-  constexpr int ldK = L::ldK, ldC = L::ldC, ldA = L::ldA;
-  constexpr int loQL = CH * ldK, loRT = 160 * ldK, loMQ = CH * ldC, loWO = CH * ldK,
-                loTB = CH * ldC, loGK = DK * ldC, loKT = DK * ldC, loST = BV * ldK,
-                loPT = BV * ldC;
+  using L = Plan<DK>;
+  constexpr int NKB = DK / 32;   // 32-channel blocks
+  constexpr int NCHT = DK / 16;  // 16-channel tiles
+  constexpr int RPW = DK / 4;    // state rows per wave
+  constexpr int RTW = RPW / 16;  // state row tiles per wave
+  constexpr int NCT = BV / 16;   // value tiles
+  constexpr int ldR = L::ldR, ldG = L::ldG, ldA = L::ldA, ldT = L::ldT, ldV = L::ldV,
+                ldS = L::ldS, ldP = L::ldP;
+  constexpr int loR = 160 * ldR, loG = CH * ldG, loT = CH * ldT, loS = BV * ldS, loP = BV * ldP;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  E* KL = reinterpret_cast<E*>(smem + L::oKL);
-  E* QL = reinterpret_cast<E*>(smem + L::oQL);
-  E* RT = reinterpret_cast<E*>(smem + L::oRT);
-  E* VT = reinterpret_cast<E*>(smem + L::oVT);
+  bf16* RT = reinterpret_cast<bf16*>(smem + L::oRT);
   float* AF = reinterpret_cast<float*>(smem + L::oAF);
   float* TF = reinterpret_cast<float*>(smem + L::oTF);
-  E* MQ = reinterpret_cast<E*>(smem + L::oMQ);
-  E* WO = reinterpret_cast<E*>(smem + L::oWO);
-  E* TB = reinterpret_cast<E*>(smem + L::oTB);
-  E* GK = reinterpret_cast<E*>(smem + L::oGK);
-  E* QT = reinterpret_cast<E*>(smem + L::oQT);
-  E* KT = reinterpret_cast<E*>(smem + L::oKT);
-  E* ST = reinterpret_cast<E*>(smem + L::oST);
-  E* PT = reinterpret_cast<E*>(smem + L::oPT);
-  float* ESd = reinterpret_cast<float*>(smem + L::oES);  // [4][DK]
-  float* GC = reinterpret_cast<float*>(smem + L::oGC);   // [DK]
-  float* BS = reinterpret_cast<float*>(smem + L::oBS);   // [64]
+  bf16* TB = reinterpret_cast<bf16*>(smem + L::oTB);
+  bf16* VS = reinterpret_cast<bf16*>(smem + L::oVS);
+  bf16* ST = reinterpret_cast<bf16*>(smem + L::oST);
+  bf16* PT = reinterpret_cast<bf16*>(smem + L::oPT);
+  bf16* GK = reinterpret_cast<bf16*>(smem + L::oGK);
+  bf16* KT = reinterpret_cast<bf16*>(smem + L::oKT);
+  float* ES = reinterpret_cast<float*>(smem + L::oES);  // [4][DK] tile decays
+  float* GC = reinterpret_cast<float*>(smem + L::oGC);  // [DK] chunk decay
+  float* BS = reinterpret_cast<float*>(smem + L::oBS);  // [64] beta
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
-  const int l16 = lane & 15;
-  const int g4 = lane >> 4;
+  const int tr = lane & 15;  // token within the wave's tile / MFMA row-col index
+  const int g = lane >> 4;   // k group of the MFMA layouts
 
-  // ---- work item: (sequence, head, value slice); the slices of one head are
-  // placed on the same XCD (block ids are dealt round-robin over 8 XCDs).
+  // ---- work item (sequence, head, value slice); slices of a head share an XCD
   const int nsl = DV / BV;
   const int total = n_seq * H * nsl;
   int wid = blockIdx.x;
@@ -173,7 +201,7 @@ __global__ __launch_bounds__(NTH) void prefill_kernel(
   }
   const int vcol0 = sl * BV;
 
-  // ---- state slice in accumulators: wave w owns key rows [w*RPW, (w+1)*RPW)
+  // state slice: wave w owns key rows [w*RPW, (w+1)*RPW), natural channel order
   floatx4 Sacc[RTW][NCT];
   {
     const float* si = s_init ? s_init + ((size_t)seq * H + h) * DK * DV : nullptr;
@@ -183,148 +211,209 @@ __global__ __launch_bounds__(NTH) void prefill_kernel(
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = w * RPW + rt * 16 + 4 * g4 + i;
-          const int col = vcol0 + ct * 16 + l16;
-          Sacc[rt][ct][i] = si ? si[(size_t)row * DV + col] : 0.f;
+          const int row = w * RPW + rt * 16 + 4 * g + i;
+          Sacc[rt][ct][i] = si ? si[(size_t)row * DV + vcol0 + ct * 16 + tr] : 0.f;
         }
   }
 
-  const int ch = tid % DK;
+  const int r = 16 * w + tr;  // this lane's token within the chunk
   for (long long c0 = 0; c0 < len; c0 += CH) {
     const int nv = (int)(len - c0 < CH ? len - c0 : CH);
     const long long tok0 = start + c0;
-    __syncthreads();  // previous chunk's serial phase is done with LDS
+    const bool ok = r < nv;
+    const size_t th = (size_t)(tok0 + r) * H + h;
+    __syncthreads();  // the previous chunk is done with LDS
 
-    // ---- load: k, q, alpha for this thread's (tile, channel) segments;
-    // P = running product of alpha from the tile start.
-    TIn kf[NSEG][16], qf[NSEG][16];  // exact input values (bf16 stays bf16)
-    float Pf[NSEG][16];
+    // ---- loads: this lane's token, its 8 channels of each 32-channel block
+    uint2v kraw[NKB][2], qraw[NKB][2];
+    floatx4 araw[NKB][2];
+    uint4v vraw[2];
+    float bt = 0.f;
 #pragma unroll
-    for (int s = 0; s < NSEG; ++s) {
-      const int m = tid / DK + s * TPC;
-      float run = 1.f;
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = 16 * m + j;
-        const bool ok = r < nv;
-        const size_t off = ((size_t)(tok0 + r) * H + h) * DK + ch;
-        kf[s][j] = ok ? k[off] : (TIn)0.f;
-        qf[s][j] = ok ? q[off] : (TIn)0.f;
-        const float a = ok ? alpha[off] : 1.f;
-        run = (j == 0) ? a : run * a;
-        Pf[s][j] = run;
+      for (int hf = 0; hf < 2; ++hf) {
+        const int c = 32 * kb + 16 * hf + 4 * g;
+        if (ok) {
+          kraw[kb][hf] = *reinterpret_cast<const uint2v*>(k + th * DK + c);
+          qraw[kb][hf] = *reinterpret_cast<const uint2v*>(q + th * DK + c);
+          araw[kb][hf] = *reinterpret_cast<const floatx4*>(alpha + th * DK + c);
+        } else {
+          kraw[kb][hf] = uint2v{0u, 0u};
+          qraw[kb][hf] = uint2v{0u, 0u};
+          araw[kb][hf] = floatx4{1.f, 1.f, 1.f, 1.f};
+        }
       }
-      ESd[m * DK + ch] = run;
-    }
-    if (tid < CH) BS[tid] = tid < nv ? beta[(size_t)(tok0 + tid) * H + h] : 0.f;
-    {
-      // V slice, transposed to [value][token] (B operand of U = T Diag(b) V)
-      const int vv = tid & 63;
-#pragma unroll 4
-      for (int i = 0; i < CH / 4; ++i) {
-        const int r = (tid >> 6) + 4 * i;
-        const float x = (r < nv && vv < BV)
-                            ? ldf(v, ((size_t)(tok0 + r) * H + h) * DV + vcol0 + vv) : 0.f;
-        if (vv < BV) Ld::store_hi(VT, vv * ldC + r, x);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      vraw[hf] = ok ? *reinterpret_cast<const uint4v*>(v + th * DV + vcol0 + 16 * g + 8 * hf)
+                    : uint4v{0u, 0u, 0u, 0u};
+    if (ok) bt = beta[th];
+
+    // ---- within-tile decay products P (inclusive scan over the 16 tokens)
+    float Pv[NKB][8];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = araw[kb][e >> 2][e & 3];
+        x *= row_shr_or_one<1>(x);
+        x *= row_shr_or_one<2>(x);
+        x *= row_shr_or_one<4>(x);
+        x *= row_shr_or_one<8>(x);
+        Pv[kb][e] = x;
       }
+    if (tr == 15) {  // whole-tile decay E_w
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          *reinterpret_cast<floatx4*>(ES + w * DK + 32 * kb + 16 * hf + 4 * g) =
+              floatx4{Pv[kb][4 * hf], Pv[kb][4 * hf + 1], Pv[kb][4 * hf + 2], Pv[kb][4 * hf + 3]};
     }
+    if (g == 0) BS[r] = bt;
     __syncthreads();
 
-    // ---- build the A / Mqk operands
-    float pre[NSEG], post[NSEG], Em[NSEG];
-    float Et[4];
+    // ---- operands.  Registers: KL = k*P (A's left factor), QL = q*P (split),
+    // QT = q*Gamma (operand of (Gamma*Q) S).  LDS: RT rows of this tile for the
+    // row tiles mm >= w, GK = k*Gamma and KT = k*Gamma_C/Gamma (split).
+    bf16x8 kl[NKB], qlh[NKB], qll[NKB], qt[NKB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Et[i] = ESd[i * DK + ch];
-    if (tid < DK) GC[ch] = Et[0] * Et[1] * Et[2] * Et[3];
+    for (int kb = 0; kb < NKB; ++kb) {
+      float Ei[4][8];
 #pragma unroll
-    for (int s = 0; s < NSEG; ++s) {
-      const int m = tid / DK + s * TPC;
-      float p = 1.f, po = 1.f;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i < m) p *= Et[i];
-        if (i > m) po *= Et[i];
+        for (int hf = 0; hf < 2; ++hf) {
+          const floatx4 e4 = *reinterpret_cast<const floatx4*>(ES + i * DK + 32 * kb + 16 * hf + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Ei[i][4 * hf + e] = e4[e];
+        }
+      float kk[8], qq[8], pre[8], post[8], Ew[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kk[e] = bfv(kraw[kb][e >> 2][(e & 3) >> 1], e & 1);
+        qq[e] = bfv(qraw[kb][e >> 2][(e & 3) >> 1], e & 1);
+        float p = 1.f, po = 1.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i < w) p *= Ei[i][e];
+          if (i > w) po *= Ei[i][e];
+        }
+        pre[e] = p;
+        post[e] = po;
+        Ew[e] = w == 0 ? Ei[0][e] : w == 1 ? Ei[1][e] : w == 2 ? Ei[2][e] : Ei[3][e];
       }
-      pre[s] = p;
-      post[s] = po;
-      Em[s] = Et[m];
+      float x[8], y[8];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = 16 * m + j;
-        const float ip = 1.f / Pf[s][j];
-        const float kv = (float)kf[s][j];
-        Ld::store_hi(KL, r * ldK + ch, kv * Pf[s][j]);
-        Ld::store(QL, r * ldK + ch, loQL, (float)qf[s][j] * Pf[s][j]);
-        // right operand rows for row tiles mm >= m
-        const float kd = kv * ip;                         // diagonal tile
-        float ke = kv * (Em[s] * ip);                     // decayed to the end of tile m
+      for (int e = 0; e < 8; ++e) {
+        x[e] = kk[e] * Pv[kb][e];
+        kl[kb][e] = (bf16)x[e];
+        y[e] = qq[e] * Pv[kb][e];
+      }
+      split8(y, qlh[kb], qll[kb]);
+      float gk[8], kt[8];
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm) {
-          if (mm < m) continue;
-          const int base = 8 * mm * (mm + 1);            // 16 * mm(mm+1)/2
-          const float val = (mm == m) ? kd : ke;
-          Ld::store(RT, (base + r) * ldK + ch, loRT, val);
-          if (mm > m) ke *= Et[mm];
+      for (int e = 0; e < 8; ++e) {
+        const float gam = pre[e] * Pv[kb][e];
+        qt[kb][e] = (bf16)(qq[e] * gam);
+        gk[e] = kk[e] * gam;
+        kt[e] = kk[e] * ((Ew[e] * __builtin_amdgcn_rcpf(Pv[kb][e])) * post[e]);
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        st_split4(GK + r * ldG + 32 * kb + 16 * hf + 4 * g, loG, gk + 4 * hf);
+        st_split4(KT + r * ldG + 32 * kb + 16 * hf + 4 * g, loG, kt + 4 * hf);
+      }
+      if (w == 0 && tr == 0) {
+        float gc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gc[e] = Ei[0][e] * Ei[1][e] * Ei[2][e] * Ei[3][e];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          *reinterpret_cast<floatx4*>(GC + 32 * kb + 16 * hf + 4 * g) =
+              floatx4{gc[4 * hf], gc[4 * hf + 1], gc[4 * hf + 2], gc[4 * hf + 3]};
+      }
+      // right operands: diagonal tile k/P, then k*(E_w/P) decayed through the
+      // whole tiles between w and mm
+      float rd[8], re[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ip = __builtin_amdgcn_rcpf(Pv[kb][e]);
+        rd[e] = kk[e] * ip;
+        re[e] = kk[e] * (Ew[e] * ip);
+      }
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        if (mm < w) continue;
+        const int row = 8 * mm * (mm + 1) + r;  // 16 * mm(mm+1)/2 rows precede row tile mm
+        bf16x8 hi, lo;
+        split8(mm == w ? rd : re, hi, lo);
+        *reinterpret_cast<bf16x8*>(RT + row * ldR + 32 * kb + 8 * g) = hi;
+        *reinterpret_cast<bf16x8*>(RT + row * ldR + 32 * kb + 8 * g + loR) = lo;
+        if (mm > w) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) re[e] *= Ei[mm][e];
         }
       }
     }
     __syncthreads();
 
-    // ---- A and Mqk: 16x16 tile pairs, K = DK
-    floatx4 accA[3], accM[3];
+    // ---- A^T and Mqk^T tiles (j in tile n, r in tile w), n = 0..w
+    floatx4 accA[4], accM[4];
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      accA[p] = floatx4{0.f, 0.f, 0.f, 0.f};
-      accM[p] = floatx4{0.f, 0.f, 0.f, 0.f};
-      int mm, n;
-      pair_of(w, p, mm, n);
-      if (n < 0) continue;
-      const int base = 8 * mm * (mm + 1);
+    for (int n = 0; n < 4; ++n) {
+      accA[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+      accM[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (n > w) continue;
+      const int row = 8 * w * (w + 1) + 16 * n + tr;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const auto ak = Ld::load(KL, ldK, 16 * mm + l16, 32 * kb, 0, false);
-        const auto aq = Ld::load(QL, ldK, 16 * mm + l16, 32 * kb, loQL, wants_lo_a(Pol::M));
-        const auto b = Ld::load(RT, ldK, base + 16 * n + l16, 32 * kb, loRT, true);
-        accA[p] = mma<Pol::A>(ak, b, accA[p]);
-        accM[p] = mma<Pol::M>(aq, b, accM[p]);
+        const bf16x8 ah = frag_ld(RT, ldR, row, 32 * kb);
+        const bf16x8 al = frag_ld(RT + loR, ldR, row, 32 * kb);
+        accA[n] = mfma_bf16(ah, kl[kb], accA[n]);
+        accM[n] = mma_ab(ah, al, qlh[kb], qll[kb], accM[n]);
       }
     }
-    __syncthreads();
+    __syncthreads();  // RT reads done; AF overwrites it
+    // A (row r, beta_r, strictly lower) to LDS; Mqk^T into operand fragments of
+    // Mqk P (token k-slots in the 8g/4-swizzled order, masked j <= r)
+    bf16x8 mqh[2], mql[2];
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      int mm, n;
-      pair_of(w, p, mm, n);
-      if (n < 0) {  // zero an upper block of Mqk that the output product reads
-        const int nn = -n;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Ld::store(MQ, (16 * mm + 4 * g4 + i) * ldC + 16 * nn + l16, loMQ, 0.f);
-        continue;
-      }
+    for (int n = 0; n < 4; ++n) {
+      float a4[4], m4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * mm + 4 * g4 + i, j = 16 * n + l16;
-        AF[r * ldA + j] = (j < r) ? BS[r] * accA[p][i] : 0.f;
-        Ld::store(MQ, r * ldC + j, loMQ, (j <= r) ? accM[p][i] : 0.f);
+        const int j = 16 * n + 4 * g + i;
+        a4[i] = (n <= w && j < r) ? bt * accA[n][i] : 0.f;
+        m4[i] = (n <= w && j <= r) ? accM[n][i] : 0.f;
+      }
+      if (n <= w) *reinterpret_cast<floatx4*>(AF + r * ldA + 16 * n + 4 * g) =
+          floatx4{a4[0], a4[1], a4[2], a4[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16 hh = (bf16)m4[i];
+        mqh[n >> 1][4 * (n & 1) + i] = hh;
+        mql[n >> 1][4 * (n & 1) + i] = (bf16)(m4[i] - (float)hh);
       }
     }
     __syncthreads();
 
     // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by substitution (fp32) ...
-    if (lane < 16) {
-      const int c = lane, b0 = 16 * w;
+    if (tr == lane) {  // lanes 0..15: column tr of block w
+      const int b0 = 16 * w;
       float t[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) t[i] = (i == c) ? 1.f : 0.f;
+      for (int i = 0; i < 16; ++i) t[i] = (i == tr) ? 1.f : 0.f;
 #pragma unroll
       for (int jj = 0; jj < 15; ++jj)
 #pragma unroll
         for (int i = jj + 1; i < 16; ++i) t[i] -= AF[(b0 + i) * ldA + b0 + jj] * t[jj];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) TF[(b0 + i) * ldA + b0 + c] = t[i];
+      for (int i = 0; i < 16; ++i) TF[(b0 + i) * ldA + b0 + tr] = t[i];
     }
     __syncthreads();
-    // ... then blocks below the diagonal, by distance d from it:
-    // T_mn = -T_mm sum_{j=n}^{m-1} A_mj T_jn  (fp32 MFMA 16x16x4)
+    // ... then below the diagonal by distance d: T_mn = -T_mm sum_{j=n}^{m-1} A_mj T_jn
 #pragma unroll
     for (int d = 1; d < 4; ++d) {
       const int m = w, n = w - d;
@@ -333,127 +422,143 @@ __global__ __launch_bounds__(NTH) void prefill_kernel(
         for (int j = n; j < m; ++j)
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            const float a = AF[(16 * m + l16) * ldA + 16 * j + 4 * g4 + s];
-            const float b = TF[(16 * j + 4 * g4 + s) * ldA + 16 * n + l16];
+            const float a = AF[(16 * m + tr) * ldA + 16 * j + 4 * g + s];
+            const float b = TF[(16 * j + 4 * g + s) * ldA + 16 * n + tr];
             X = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, X, 0, 0, 0);
           }
         floatx4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const float a = TF[(16 * m + l16) * ldA + 16 * m + 4 * g4 + s];
+          const float a = TF[(16 * m + tr) * ldA + 16 * m + 4 * g + s];
           Y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, X[s], Y, 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) TF[(16 * m + 4 * g4 + i) * ldA + 16 * n + l16] = -Y[i];
+        for (int i = 0; i < 4; ++i) TF[(16 * m + 4 * g + i) * ldA + 16 * n + tr] = -Y[i];
       }
       __syncthreads();
     }
 
-    // ---- TB = T Diag(b) (A operand of W and U) and (Gamma * K) as B operand
-    for (int idx = tid; idx < CH * CH; idx += NTH) {
-      const int r = idx >> 6, j = idx & 63;
-      Ld::store(TB, r * ldC + j, loTB, (j <= r) ? TF[r * ldA + j] * BS[j] : 0.f);
+    // ---- TB = T Diag(beta) (split, [r][j]) and the V slice ([token][value])
+#pragma unroll
+    for (int it = 0; it < CH * CH / 4 / NTH; ++it) {
+      const int idx = tid + NTH * it;
+      const int rr = idx >> 4, j0 = 4 * (idx & 15);
+      const floatx4 t4 = *reinterpret_cast<const floatx4*>(TF + rr * ldA + j0);
+      const floatx4 b4 = *reinterpret_cast<const floatx4*>(BS + j0);
+      float x4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x4[e] = (j0 + e <= rr) ? t4[e] * b4[e] : 0.f;
+      st_split4(TB + rr * ldT + j0, loT, x4);
     }
 #pragma unroll
-    for (int s = 0; s < NSEG; ++s) {
-      const int m = tid / DK + s * TPC;
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        Ld::store(GK, ch * ldC + 16 * m + j, loGK, (float)kf[s][j] * (pre[s] * Pf[s][j]));
-    }
+    for (int hf = 0; hf < 2; ++hf)
+      *reinterpret_cast<uint4v*>(VS + r * ldV + 16 * g + 8 * hf) = vraw[hf];
     __syncthreads();
 
-    // ---- W = TB (Gamma*K)  [64 x DK] and U = TB V [64 x BV]; wave w: row tile w
+    // ---- W^T = (Gamma*K)^T (T Diag b)^T for this wave's tokens (all channels),
+    // kept as the split operand of W S; U = T Diag(b) V
+    bf16x8 wh[NKB], wl[NKB];
     floatx4 accU[NCT];
     {
-      floatx4 accW[DK / 16];
+      bf16x8 tbh[2], tbl[2];
 #pragma unroll
-      for (int ct = 0; ct < DK / 16; ++ct) accW[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 2; ++kb) {
+        tbh[kb] = frag_ld(TB, ldT, r, 32 * kb);
+        tbl[kb] = frag_ld(TB + loT, ldT, r, 32 * kb);
+      }
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) accU[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-      for (int kb = 0; kb <= (w >> 1); ++kb) {
-        const auto a = Ld::load(TB, ldC, 16 * w + l16, 32 * kb, loTB, true);
+      for (int ct = 0; ct < NCHT; ++ct) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ct = 0; ct < DK / 16; ++ct) {
-          const auto b = Ld::load(GK, ldC, 16 * ct + l16, 32 * kb, loGK, wants_lo_b(Pol::W));
-          accW[ct] = mma<Pol::W>(a, b, accW[ct]);
+        for (int kb = 0; kb < 2; ++kb) {
+          if (kb > (w >> 1)) continue;
+          const bf16x8 ah = frag_tr(GK, ldG, 16 * ct, 32 * kb + 8 * g, 32 * kb + 8 * g + 4);
+          const bf16x8 al = frag_tr(GK + loG, ldG, 16 * ct, 32 * kb + 8 * g, 32 * kb + 8 * g + 4);
+          acc = mma_ab(ah, al, tbh[kb], tbl[kb], acc);
         }
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          const auto b = Ld::load(VT, ldC, 16 * ct + l16, 32 * kb, 0, false);
-          accU[ct] = mma<Pol::U>(a, b, accU[ct]);
+        for (int i = 0; i < 4; ++i) {
+          const bf16 hh = (bf16)acc[i];
+          wh[ct >> 1][4 * (ct & 1) + i] = hh;
+          wl[ct >> 1][4 * (ct & 1) + i] = (bf16)(acc[i] - (float)hh);
         }
       }
-      __syncthreads();  // TB / GK / V reads done before the regions are reused
-#pragma unroll
-      for (int ct = 0; ct < DK / 16; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          Ld::store(WO, (16 * w + 4 * g4 + i) * ldK + 16 * ct + l16, loWO, accW[ct][i]);
-    }
-
-    // ---- (Gamma * Q) and Ktil^T operands, and the state as B operand
-#pragma unroll
-    for (int s = 0; s < NSEG; ++s) {
-      const int m = tid / DK + s * TPC;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = 16 * m + j;
-        Ld::store_hi(QT, r * ldK + ch, (float)qf[s][j] * (pre[s] * Pf[s][j]));
-        Ld::store(KT, ch * ldC + r, loKT, (float)kf[s][j] * ((Em[s] / Pf[s][j]) * post[s]));
-      }
-    }
-#pragma unroll
-    for (int rt = 0; rt < RTW; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          Ld::store(ST, (16 * ct + l16) * ldK + w * RPW + rt * 16 + 4 * g4 + i, loST, Sacc[rt][ct][i]);
-    __syncthreads();
-
-    // ---- serial part.  P = U - W S and O = (Gamma*Q) S  (wave w: token tile w)
-    floatx4 accO[NCT];
-    {
-      floatx4 accWS[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        accWS[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+        accU[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if (kb > (w >> 1)) continue;
+          const bf16x8 b = frag_tr(VS, ldV, 16 * ct, 32 * kb + 8 * g, 32 * kb + 8 * g + 4);
+          accU[ct] = mfma_bf16(tbh[kb], b, accU[ct]);
+          accU[ct] = mfma_bf16(tbl[kb], b, accU[ct]);
+        }
+      }
+    }
+    __syncthreads();  // TB / VS / TF reads done; ST and PT overwrite them
+
+    // ---- state to LDS as the B operand of W S and (Gamma*Q) S: [value][channel
+    // position], position 32kb + 8g + 4h + i holds channel 32kb + 16h + 4g + i
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int c0r = w * RPW + rt * 16;
+      const int pos = 32 * (c0r >> 5) + 8 * g + 4 * ((c0r >> 4) & 1);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        float x4[4] = {Sacc[rt][ct][0], Sacc[rt][ct][1], Sacc[rt][ct][2], Sacc[rt][ct][3]};
+        st_split4(ST + (16 * ct + tr) * ldS + pos, loS, x4);
+      }
+    }
+    __syncthreads();
+
+    // ---- P = U - W S and O = (Gamma*Q) S for this wave's 16 tokens
+    floatx4 accO[NCT];
+    {
+      floatx4 accW[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        accW[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
         accO[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const auto aw = Ld::load(WO, ldK, 16 * w + l16, 32 * kb, loWO, true);
-        const auto aq = Ld::load(QT, ldK, 16 * w + l16, 32 * kb, 0, false);
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-          const auto b = Ld::load(ST, ldK, 16 * ct + l16, 32 * kb, loST, true);
-          accWS[ct] = mma<Pol::WS>(aw, b, accWS[ct]);
-          accO[ct] = mma<Pol::QS>(aq, b, accO[ct]);
+          const bf16x8 bh = frag_ld(ST, ldS, 16 * ct + tr, 32 * kb);
+          const bf16x8 bl = frag_ld(ST + loS, ldS, 16 * ct + tr, 32 * kb);
+          accW[ct] = mma_ab(wh[kb], wl[kb], bh, bl, accW[ct]);
+          accO[ct] = mfma_bf16(qt[kb], bh, accO[ct]);
+          accO[ct] = mfma_bf16(qt[kb], bl, accO[ct]);
         }
+      // P to LDS as [value][token position]; token 32kb + 16h + 4g + i sits at
+      // position 32kb + 8g + 4h + i (the order of the Mqk^T operand)
+      const int pos = 32 * (w >> 1) + 8 * g + 4 * (w & 1);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        float x4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x4[i] = accU[ct][i] - accW[ct][i];
+        st_split4(PT + (16 * ct + tr) * ldP + pos, loP, x4);
       }
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          Ld::store(PT, (16 * ct + l16) * ldC + 16 * w + 4 * g4 + i, loPT, accU[ct][i] - accWS[ct][i]);
     }
     __syncthreads();
 
-    // ---- O += Mqk P, store o
-    for (int kb = 0; kb <= (w >> 1); ++kb) {
-      const auto a = Ld::load(MQ, ldC, 16 * w + l16, 32 * kb, loMQ, true);
+    // ---- O += Mqk P; store o
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb > (w >> 1)) continue;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const auto b = Ld::load(PT, ldC, 16 * ct + l16, 32 * kb, loPT, true);
-        accO[ct] = mma<Pol::MP>(a, b, accO[ct]);
+        const bf16x8 bh = frag_ld(PT, ldP, 16 * ct + tr, 32 * kb);
+        const bf16x8 bl = frag_ld(PT + loP, ldP, 16 * ct + tr, 32 * kb);
+        accO[ct] = mma_ab(mqh[kb], mql[kb], bh, bl, accO[ct]);
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + 4 * g4 + i;
-      if (r < nv) {
-        TOut* orow = o + ((size_t)(tok0 + r) * H + h) * DV + vcol0 + l16;
+      const int rr = 16 * w + 4 * g + i;
+      if (rr < nv) {
+        TOut* orow = o + ((size_t)(tok0 + rr) * H + h) * DV + vcol0 + tr;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) orow[16 * ct] = (TOut)accO[ct][i];
       }
@@ -461,25 +566,30 @@ __global__ __launch_bounds__(NTH) void prefill_kernel(
 
     // ---- S = Diag(Gamma_C) S + Ktil^T P
     {
-      decltype(Ld::load(PT, ldC, 0, 0, loPT, true)) bp[2][NCT];
+      bf16x8 bph[2][NCT], bpl[2][NCT];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) bp[kb][ct] = Ld::load(PT, ldC, 16 * ct + l16, 32 * kb, loPT, true);
+        for (int ct = 0; ct < NCT; ++ct) {
+          bph[kb][ct] = frag_ld(PT, ldP, 16 * ct + tr, 32 * kb);
+          bpl[kb][ct] = frag_ld(PT + loP, ldP, 16 * ct + tr, 32 * kb);
+        }
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt) {
-        float gc[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gc[i] = GC[w * RPW + rt * 16 + 4 * g4 + i];
+        const int c0r = w * RPW + rt * 16;
+        const floatx4 gc = *reinterpret_cast<const floatx4*>(GC + c0r + 4 * g);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
           for (int i = 0; i < 4; ++i) Sacc[rt][ct][i] *= gc[i];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const auto a = Ld::load(KT, ldC, w * RPW + rt * 16 + l16, 32 * kb, loKT, true);
+          // Ktil^T rows c0r.., token k-slots in the same order as P's positions
+          const bf16x8 ah = frag_tr(KT, ldG, c0r, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g);
+          const bf16x8 al = frag_tr(KT + loG, ldG, c0r, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g);
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) Sacc[rt][ct] = mma<Pol::KP>(a, bp[kb][ct], Sacc[rt][ct]);
+          for (int ct = 0; ct < NCT; ++ct)
+            Sacc[rt][ct] = mma_ab(ah, al, bph[kb][ct], bpl[kb][ct], Sacc[rt][ct]);
         }
       }
     }
@@ -493,19 +603,17 @@ __global__ __launch_bounds__(NTH) void prefill_kernel(
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = w * RPW + rt * 16 + 4 * g4 + i;
-          const int col = vcol0 + ct * 16 + l16;
-          sf[(size_t)row * DV + col] = Sacc[rt][ct][i];
+          const int row = w * RPW + rt * 16 + 4 * g + i;
+          sf[(size_t)row * DV + vcol0 + ct * 16 + tr] = Sacc[rt][ct][i];
         }
   }
 }
 
-template <int DK, bool F32OPS, typename TIn, typename TOut>
-static hipError_t launch_t(const PrefillArgs& a) {
-  constexpr int BV = 64;
-  using L = Layout<DK, BV, F32OPS>;
-  auto kern = prefill_kernel<DK, BV, F32OPS, TIn, TOut>;
-  static bool attr_set = false;  // per instantiation; benign if raced (idempotent)
+template <int DK, typename TOut>
+hipError_t launch_bf16(const PrefillArgs& a) {
+  using L = Plan<DK>;
+  auto kern = prefill_bf16_kernel<DK, TOut>;
+  static bool attr_set = false;  // per instantiation; idempotent if raced
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, L::total);
@@ -514,25 +622,24 @@ static hipError_t launch_t(const PrefillArgs& a) {
   }
   const int grid = a.n_seq * a.H * (a.Dv / BV);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH), L::total, (hipStream_t)a.stream,
-                     (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.alpha, a.beta,
+                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.alpha, a.beta,
                      a.initial_state, a.final_state, (TOut*)a.o, a.cu_seqlens, a.n_seq, a.T, a.H,
                      a.Dv);
   return hipGetLastError();
 }
 
+}  // namespace
+
 bool prefill_supported(bool qkv_bf16, int Dk, int Dv) {
   if (!(Dv == 64 || Dv == 128)) return false;
   if (qkv_bf16) return Dk == 64 || Dk == 128;
-  return Dk == 64;  // fp32 inputs: fp32 MFMA path, Dk = 64
+  return Dk == 64;  // fp32 inputs: the fp32-MFMA kernel, Dk = 64
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {
-  if (a.qkv_bf16) {
-    if (a.Dk == 128)
-      return a.o_bf16 ? launch_t<128, false, bf16, bf16>(a) : launch_t<128, false, bf16, float>(a);
-    return a.o_bf16 ? launch_t<64, false, bf16, bf16>(a) : launch_t<64, false, bf16, float>(a);
-  }
-  return a.o_bf16 ? launch_t<64, true, float, bf16>(a) : launch_t<64, true, float, float>(a);
+  if (!a.qkv_bf16) return launch_prefill_f32(a);
+  if (a.Dk == 128) return a.o_bf16 ? launch_bf16<128, bf16>(a) : launch_bf16<128, float>(a);
+  return a.o_bf16 ? launch_bf16<64, bf16>(a) : launch_bf16<64, float>(a);
 }
 
 }  // namespace kda

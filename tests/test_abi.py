@@ -66,6 +66,7 @@ def _prefill(**over):
     (dict(beta=None), INVALID),
     (dict(o=FAKE + 2), INVALID),
     (dict(q=FAKE + 1), INVALID),
+    (dict(alpha=FAKE + 8), INVALID),
     (dict(s0=FAKE + 8), INVALID),
     (dict(H=0), INVALID),
     (dict(T=-1), INVALID),
