@@ -178,7 +178,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
   float* BS = reinterpret_cast<float*>(smem + L::oBS);  // [64] beta
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
   const int lane = tid & 63;
   const int tr = lane & 15;  // token within the wave's tile / MFMA row-col index
   const int g = lane >> 4;   // k group of the MFMA layouts
@@ -217,38 +217,63 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
   }
 
   const int r = 16 * w + tr;  // this lane's token within the chunk
-  for (long long c0 = 0; c0 < len; c0 += CH) {
-    const int nv = (int)(len - c0 < CH ? len - c0 : CH);
-    const long long tok0 = start + c0;
-    const bool ok = r < nv;
-    const size_t th = (size_t)(tok0 + r) * H + h;
-    __syncthreads();  // the previous chunk is done with LDS
 
-    // ---- loads: this lane's token, its 8 channels of each 32-channel block
-    uint2v kraw[NKB][2], qraw[NKB][2];
-    floatx4 araw[NKB][2];
-    uint4v vraw[2];
-    float bt = 0.f;
+  // Global loads of one chunk for this lane's token: k, q, alpha (its 8
+  // channels of every 32-channel block), 16 values of the V slice and beta.
+  // The next chunk's loads are issued before the current chunk is processed,
+  // so their latency hides behind a whole chunk of work.
+  struct ChunkIn {
+    uint2v k[NKB][2], q[NKB][2];
+    floatx4 a[NKB][2];
+    uint4v v[2];
+    float b;
+  };
+  // part 0: k, 1: q, 2: alpha, 3: v and beta.  The parts of the next chunk are
+  // issued at four points of the current one, a few instructions at a time, so
+  // the vector-memory queue never fills and blocks instruction issue.
+  auto load_part = [&](long long cc, ChunkIn& in, int part) {
+    const int nvc = (int)(len - cc < CH ? len - cc : CH);
+    const bool okc = r < nvc;
+    const size_t thc = (size_t)(start + cc + r) * H + h;
+    if (part == 3) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        in.v[hf] = okc ? *reinterpret_cast<const uint4v*>(v + thc * DV + vcol0 + 16 * g + 8 * hf)
+                       : uint4v{0u, 0u, 0u, 0u};
+      in.b = okc ? beta[thc] : 0.f;
+      return;
+    }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int c = 32 * kb + 16 * hf + 4 * g;
-        if (ok) {
-          kraw[kb][hf] = *reinterpret_cast<const uint2v*>(k + th * DK + c);
-          qraw[kb][hf] = *reinterpret_cast<const uint2v*>(q + th * DK + c);
-          araw[kb][hf] = *reinterpret_cast<const floatx4*>(alpha + th * DK + c);
-        } else {
-          kraw[kb][hf] = uint2v{0u, 0u};
-          qraw[kb][hf] = uint2v{0u, 0u};
-          araw[kb][hf] = floatx4{1.f, 1.f, 1.f, 1.f};
-        }
+        if (part == 0) in.k[kb][hf] = okc ? *reinterpret_cast<const uint2v*>(k + thc * DK + c)
+                                          : uint2v{0u, 0u};
+        if (part == 1) in.q[kb][hf] = okc ? *reinterpret_cast<const uint2v*>(q + thc * DK + c)
+                                          : uint2v{0u, 0u};
+        if (part == 2) in.a[kb][hf] = okc ? *reinterpret_cast<const floatx4*>(alpha + thc * DK + c)
+                                          : floatx4{1.f, 1.f, 1.f, 1.f};
       }
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-      vraw[hf] = ok ? *reinterpret_cast<const uint4v*>(v + th * DV + vcol0 + 16 * g + 8 * hf)
-                    : uint4v{0u, 0u, 0u, 0u};
-    if (ok) bt = beta[th];
+  };
+  ChunkIn nxt;
+  if (len > 0)
+    for (int part = 0; part < 4; ++part) load_part(0, nxt, part);
+
+  for (long long c0 = 0; c0 < len; c0 += CH) {
+    const int nv = (int)(len - c0 < CH ? len - c0 : CH);
+    const long long tok0 = start + c0;
+    __syncthreads();  // the previous chunk is done with LDS
+
+    // ---- loads: take the prefetched chunk, start fetching the next one
+    const ChunkIn cur = nxt;
+    const bool more = c0 + CH < len;
+    if (more) load_part(c0 + CH, nxt, 0);
+    const auto& kraw = cur.k;
+    const auto& qraw = cur.q;
+    const auto& araw = cur.a;
+    const auto& vraw = cur.v;
+    const float bt = cur.b;
 
     // ---- within-tile decay products P (inclusive scan over the 16 tokens)
     float Pv[NKB][8];
@@ -280,29 +305,35 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     bf16x8 kl[NKB], qlh[NKB], qll[NKB], qt[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      float Ei[4][8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
+      // whole-tile decays of this lane's channels: E_w, the product over the
+      // tiles before w (pre) and after w (post); w is uniform, so these are
+      // scalar-controlled loops over LDS reads
+      auto ld_e = [&](int i, float* out) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const floatx4 e4 = *reinterpret_cast<const floatx4*>(ES + i * DK + 32 * kb + 16 * hf + 4 * g);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) Ei[i][4 * hf + e] = e4[e];
+          for (int e = 0; e < 4; ++e) out[4 * hf + e] = e4[e];
         }
-      float kk[8], qq[8], pre[8], post[8], Ew[8];
+      };
+      float kk[8], qq[8], pre[8], post[8], Ew[8], tmp[8];
+      ld_e(w, Ew);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
+        pre[e] = 1.f;
+        post[e] = 1.f;
         kk[e] = bfv(kraw[kb][e >> 2][(e & 3) >> 1], e & 1);
         qq[e] = bfv(qraw[kb][e >> 2][(e & 3) >> 1], e & 1);
-        float p = 1.f, po = 1.f;
+      }
+      for (int i = 0; i < w; ++i) {
+        ld_e(i, tmp);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (i < w) p *= Ei[i][e];
-          if (i > w) po *= Ei[i][e];
-        }
-        pre[e] = p;
-        post[e] = po;
-        Ew[e] = w == 0 ? Ei[0][e] : w == 1 ? Ei[1][e] : w == 2 ? Ei[2][e] : Ei[3][e];
+        for (int e = 0; e < 8; ++e) pre[e] *= tmp[e];
+      }
+      for (int i = w + 1; i < 4; ++i) {
+        ld_e(i, tmp);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) post[e] *= tmp[e];
       }
       float x[8], y[8];
 #pragma unroll
@@ -328,7 +359,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       if (w == 0 && tr == 0) {
         float gc[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) gc[e] = Ei[0][e] * Ei[1][e] * Ei[2][e] * Ei[3][e];
+        for (int e = 0; e < 8; ++e) gc[e] = Ew[e] * post[e];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
           *reinterpret_cast<floatx4*>(GC + 32 * kb + 16 * hf + 4 * g) =
@@ -343,21 +374,28 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
         rd[e] = kk[e] * ip;
         re[e] = kk[e] * (Ew[e] * ip);
       }
-#pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        if (mm < w) continue;
-        const int row = 8 * mm * (mm + 1) + r;  // 16 * mm(mm+1)/2 rows precede row tile mm
+      {
+        const int row = 8 * w * (w + 1) + r;  // 16 * w(w+1)/2 rows precede row tile w
         bf16x8 hi, lo;
-        split8(mm == w ? rd : re, hi, lo);
+        split8(rd, hi, lo);
         *reinterpret_cast<bf16x8*>(RT + row * ldR + 32 * kb + 8 * g) = hi;
         *reinterpret_cast<bf16x8*>(RT + row * ldR + 32 * kb + 8 * g + loR) = lo;
-        if (mm > w) {
+      }
+      for (int mm = w + 1; mm < 4; ++mm) {
+        const int row = 8 * mm * (mm + 1) + r;
+        bf16x8 hi, lo;
+        split8(re, hi, lo);
+        *reinterpret_cast<bf16x8*>(RT + row * ldR + 32 * kb + 8 * g) = hi;
+        *reinterpret_cast<bf16x8*>(RT + row * ldR + 32 * kb + 8 * g + loR) = lo;
+        if (mm < 3) {
+          ld_e(mm, tmp);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) re[e] *= Ei[mm][e];
+          for (int e = 0; e < 8; ++e) re[e] *= tmp[e];
         }
       }
     }
     __syncthreads();
+    if (more) load_part(c0 + CH, nxt, 1);
 
     // ---- A^T and Mqk^T tiles (j in tile n, r in tile w), n = 0..w
     floatx4 accA[4], accM[4];
@@ -398,6 +436,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       }
     }
     __syncthreads();
+    if (more) load_part(c0 + CH, nxt, 2);
 
     // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by substitution (fp32) ...
     if (tr == lane) {  // lanes 0..15: column tr of block w
@@ -437,6 +476,8 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       }
       __syncthreads();
     }
+
+    if (more) load_part(c0 + CH, nxt, 3);
 
     // ---- TB = T Diag(beta) (split, [r][j]) and the V slice ([token][value])
 #pragma unroll
