@@ -44,6 +44,32 @@ def decode_bytes(B, H, Dk, Dv):
     return state, other
 
 
+def measured_traffic(summary: str, sources: list[str]):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when the kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if kv.get("source_sha256") != h.hexdigest():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+PREFILL_SOURCES = ["kimi_delta_attention_amd/csrc/kda_prefill.hip",
+                   "kimi_delta_attention_amd/csrc/kda_common.h"]
+DECODE_SOURCES = ["kimi_delta_attention_amd/csrc/kda_decode.hip",
+                  "kimi_delta_attention_amd/csrc/kda_common.h"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,14 +182,23 @@ def main():
         "config": {"workload": "k3_prefill_8k", "B": B, "T": T, "H": H, "d_k": D, "d_v": D,
                    "chunk": 64, "qkv": "bf16", "alpha_beta_state": "fp32", "o": "fp32"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "prefill_kernel<128,64,bf16->fp32>",
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("prefill_bf16_kernel__k3_prefill_8k__hbm_counters.txt",
+                                                 PREFILL_SOURCES),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-calibrated)",
+                     "kernel": "prefill_bf16_kernel<Dk=128, fp32 out>",
                      "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_ms": avg_launch_ms,
                      "mfma_frac_pages_flops": tflops / BF16_PEAK_TFLOPS},
         "decode": {"workload": "decode_b64", "B": wd["B"], "H": wd["H"], "d": wd["D"],
                    "us_per_step": dec_ms * 1e3, "state_gbs": dec_state_gbs,
-                   "total_gbs": dec_total_gbs, "frac_hbm": dec_total_gbs / HBM_PEAK_GBS},
+                   "total_gbs": dec_total_gbs,
+                   "roofline": {"bound": "hbm", "achieved": dec_total_gbs, "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": dec_total_gbs / HBM_PEAK_GBS,
+                                "traffic": measured_traffic(
+                                    "decode_step_kernel__decode_b64__hbm_counters.txt",
+                                    DECODE_SOURCES)}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -1,0 +1,73 @@
+"""Long-context prefill: B=1, H=96, T=1,048,576, d=128 (inputs about 176 GB,
+generated on the device).  The oracle runs on 4 seeded heads over the whole
+length; all 96 heads are compared with the GPU decode step replayed token by
+token.  Takes about a minute or two; run it alone with
+`pytest -m gpu tests/test_gpu_long.py`."""
+import random
+import sys
+import time
+
+import pytest
+import torch
+
+import kimi_delta_attention_amd as kda
+import oracle
+from kimi_delta_attention_amd import synth
+from tests._common import TOL_BF16, dev, oracle_heads, rel
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _log(msg):
+    print(f"[long_1m] {msg}", file=sys.stderr, flush=True)
+
+
+def test_long_1m():
+    d = dev()
+    w = synth.WORKLOADS["long_1m"]
+    free, _ = torch.cuda.mem_get_info(d)
+    if free < 200e9:
+        pytest.skip(f"needs ~200 GB of device memory, {free / 1e9:.0f} GB free")
+    t0 = time.time()
+    inp = synth.make_dense(w["B"], w["T"], w["H"], w["D"], w["D"], seed=w["seed"],
+                           state_std=w["state_std"], device=d)
+    torch.cuda.synchronize()
+    _log(f"inputs generated in {time.time() - t0:.1f}s")
+    o, s = kda.prefill_chunked(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
+                               initial_state=inp.state)
+    torch.cuda.synchronize()
+    _log("chunked prefill done")
+
+    # oracle on 4 heads drawn from the seed, whole length
+    heads = sorted(random.Random(w["seed"]).sample(range(w["H"]), 4))
+    t1 = time.time()
+    o_ref, s_ref = oracle_heads(inp, heads)
+    _log(f"oracle on heads {heads} in {time.time() - t1:.1f}s")
+    e_o = rel(o[:, :, heads].cpu(), o_ref)
+    e_s = rel(s[:, heads].cpu(), s_ref)
+    _log(f"oracle rel-L2 o={e_o:.3e} S={e_s:.3e}")
+    del o_ref, s_ref
+    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
+
+    # all heads: GPU decode replay, compared block by block
+    T = inp.q.shape[1]
+    state = inp.state.clone()
+    blk = 4096
+    orep = torch.empty(blk, w["H"], w["D"], dtype=torch.float32, device=d)
+    num = torch.zeros((), dtype=torch.float64, device=d)
+    den = torch.zeros((), dtype=torch.float64, device=d)
+    t2 = time.time()
+    for b0 in range(0, T, blk):
+        for t in range(b0, min(T, b0 + blk)):
+            kda.decode_step(inp.q[:, t], inp.k[:, t], inp.v[:, t], inp.alpha[:, t],
+                            inp.beta[:, t], state, o=orep[t - b0:t - b0 + 1])
+        n = min(T, b0 + blk) - b0
+        ref = o[0, b0:b0 + n].double()
+        num += (orep[:n].double() - ref).square().sum()
+        den += ref.square().sum()
+        if (b0 // blk) % 32 == 0:
+            _log(f"replay {b0 + n}/{T} tokens, {time.time() - t2:.0f}s")
+    e_rep = (num / den).sqrt().item()
+    e_rep_s = rel(s.cpu(), state.cpu())
+    _log(f"replay rel-L2 o={e_rep:.3e} S={e_rep_s:.3e}")
+    assert e_rep <= TOL_BF16 and e_rep_s <= TOL_BF16
