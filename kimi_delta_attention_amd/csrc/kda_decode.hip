@@ -12,7 +12,8 @@
 // Mapping: one workgroup (4 waves) per (session, head) tile of Dk x Dv fp32.
 // Wave w owns the value columns [w*Dv/4, (w+1)*Dv/4); a lane holds float4
 // column groups of a set of rows, so every global access is a 16-byte vector
-// and a wave touches whole 64..128-byte row segments.  The column sums over
+// and a wave touches whole 64..128-byte row segments; the state write uses
+// non-temporal stores.  The column sums over
 // the key axis are finished with cross-lane xor shuffles inside the wave (no
 // LDS, no barrier).
 #include "kda_common.h"
@@ -84,9 +85,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 #pragma unroll
   for (int j = 0; j < 4; ++j) u[j] = b * (ld_in(v + (size_t)tile * DV, col + j) - old[j]);
 
+  // streaming (non-temporal) stores: the state is written once and not re-read
+  // by this launch; on gfx950 this write path sustains close to HBM peak where
+  // ordinary stores of the same pattern stall on the cache write-back path
 #pragma unroll
   for (int i = 0; i < NP; ++i)
-    *reinterpret_cast<floatx4*>(S + (size_t)(ro + RPP * i) * DV + col) = s[i] + kr[i] * u;
+    __builtin_nontemporal_store(s[i] + kr[i] * u,
+                                reinterpret_cast<floatx4*>(S + (size_t)(ro + RPP * i) * DV + col));
 
   if (ro == 0) {
     TOut* ot = o + (size_t)tile * DV + col;

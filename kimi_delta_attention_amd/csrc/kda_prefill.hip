@@ -601,7 +601,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       if (rr < nv) {
         TOut* orow = o + ((size_t)(tok0 + rr) * H + h) * DV + vcol0 + tr;
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) orow[16 * ct] = (TOut)accO[ct][i];
+        for (int ct = 0; ct < NCT; ++ct) __builtin_nontemporal_store((TOut)accO[ct][i], orow + 16 * ct);
       }
     }
 
