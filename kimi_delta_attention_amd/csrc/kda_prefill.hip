@@ -22,18 +22,23 @@
 // 1 / P_j, bounded by one tile's decay (the tiling the bounded gate of
 // "Kimi K3 的 KDA" section 6 is made for).
 //
-// Work decomposition.  One workgroup (4 waves) owns (sequence, head, 64-wide
-// value slice) and walks the chunks in order; the state slice stays in MFMA
-// accumulators for the whole sequence.  Wave w owns token tile w (tokens
-// 16w..16w+15) of every chunk: lane l holds token 16w + l%16 and, per 32-channel
-// block kb, the 8 channels 32kb + 4g + {0..3} and 32kb + 16 + 4g + {0..3}
-// (g = l/16).  That set is exactly the k range an MFMA 16x16x32 output tile of a
-// transposed product delivers to a lane, so outputs chain into the next
-// product's operands in registers: (Gamma*K)^T T^T gives W in the operand layout
-// of W S, and Mqk^T tiles give the operand of Mqk P.  Products contracted over
-// the token axis read row-major [token][channel] LDS tiles through the gfx950
-// transpose read (ds_read_b64_tr_b16).  The within-tile decay products are a
-// 16-lane DPP scan.
+// Work decomposition.  One workgroup (8 waves, two per SIMD) owns (sequence,
+// head, 64-wide value slice) and walks the chunks in order; the state slice
+// stays in MFMA accumulators for the whole sequence.  Token tile w (tokens
+// 16w..16w+15 of the chunk) belongs to a pair of waves: during operand build
+// and the A / Mqk products each wave of the pair takes one half of the key
+// channels (the halves are summed through LDS), afterwards each takes one
+// 32-column half of the value slice.  A lane holds token 16w + l%16 and, per
+// 32-channel block kb, the 8 channels 32kb + 4g + {0..3} and
+// 32kb + 16 + 4g + {0..3} (g = l/16).  That set is exactly the k range an MFMA
+// 16x16x32 output tile of a transposed product delivers to a lane, so outputs
+// chain into the next product's operands in registers: (Gamma*K)^T T^T gives W
+// in the operand layout of W S, and Mqk^T tiles give the operand of Mqk P.
+// Products contracted over the token axis read row-major [token][channel] LDS
+// tiles through the gfx950 transpose read (ds_read_b64_tr_b16).  The
+// within-tile decay products are a 16-lane DPP scan; T comes from a blockwise
+// solve on fp32 MFMA whose diagonal 16x16 blocks use the nilpotent product
+// (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8).
 //
 // Precision: bf16 MFMA with split-bf16 operands (x = hi + lo, product
 // hi*hi + hi*lo + lo*hi) everywhere except A (single pass); U and (Gamma*Q) S
@@ -45,7 +50,7 @@ namespace kda {
 namespace {
 
 constexpr int CH = 64;    // chunk
-constexpr int NTH = 256;  // 4 waves
+constexpr int NTH = 512;  // 8 waves
 constexpr int BV = 64;    // value slice per workgroup
 
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -123,28 +128,35 @@ __device__ __forceinline__ floatx4 mma_ab(const bf16x8& ah, const bf16x8& al, co
 }
 
 // LDS plan (bytes).  R0 is reused phase by phase:
-//   A / Mqk:       RT (right operands of every row tile, position order)
-//   solve / W, U:  AF, TF (fp32), TB (T Diag(b), split), VS (V slice)
-//   serial:        ST (state, split), PT (P, split)
-// GK ((Gamma*K), split) and KT (Ktil, split) are [token][channel] tiles that
+//   A / Mqk:      RT (right operands of every row tile, position order)
+//   partials:     AF, AF2 (the two channel halves of beta*A), MQ0, MQ1 (of Mqk), TF
+//   solve:        AF, AF2, TF, and the per-wave scratch SCR in the MQ0 region
+//   T*b, V:       TB (T Diag(b), split) and VS (V slice) over MQ0 / MQ1
+//   serial:       ST (state, split), PT (P, split), KT (Ktil, split)
+// GK ((Gamma*K), split, [token][channel]) and QT ((Gamma*Q), [token][position])
 // live from operand build to their last product; ES / GC / BS are small.
 template <int DK>
 struct Plan {
-  static constexpr int ldR = DK + 8, ldG = DK + 8, ldA = CH + 4, ldT = CH + 8, ldV = BV + 8,
-                       ldS = DK + 8, ldP = CH + 8;
+  static constexpr int ldR = DK + 8, ldG = DK + 8, ldQ = DK + 8, ldA = CH + 4, ldT = CH + 8,
+                       ldV = BV + 8, ldS = DK + 8, ldP = CH + 8;
   static constexpr int RT = 160 * ldR * 2 * 2;
-  static constexpr int AF = CH * ldA * 4, TF = CH * ldA * 4, TB = CH * ldT * 2 * 2,
-                       VS = CH * ldV * 2;
-  static constexpr int ST = BV * ldS * 2 * 2, PT = BV * ldP * 2 * 2;
-  static constexpr int oRT = 0, oAF = 0, oTF = AF, oTB = AF + TF, oVS = AF + TF + TB,
-                       oST = 0, oPT = ST;
-  static constexpr int r0a = RT, r0b = AF + TF + TB + VS, r0c = ST + PT;
-  static constexpr int R0 = r0a > r0b ? (r0a > r0c ? r0a : r0c) : (r0b > r0c ? r0b : r0c);
-  static constexpr int GK = CH * ldG * 2 * 2, KT = CH * ldG * 2 * 2;
-  static constexpr int oGK = R0, oKT = oGK + GK, oES = oKT + KT, oGC = oES + 4 * DK * 4,
+  static constexpr int AF = CH * ldA * 4, TB = CH * ldT * 2 * 2, VS = CH * ldV * 2;
+  static constexpr int ST = BV * ldS * 2 * 2, PT = BV * ldP * 2 * 2, KT = CH * ldG * 2 * 2;
+  static constexpr int oRT = 0;
+  static constexpr int oAF = 0, oAF2 = AF, oTF = 2 * AF, oMQ0 = 3 * AF, oMQ1 = 4 * AF,
+                       oSCR = 3 * AF, oTB = 3 * AF, oVS = 3 * AF + TB, endB = oVS + VS;
+  static constexpr int oST = 0, oPT = ST, oKT = ST + PT, endC = ST + PT + KT;
+  static constexpr int m1 = RT > 5 * AF ? RT : 5 * AF;
+  static constexpr int m2 = endB > endC ? endB : endC;
+  static constexpr int R0 = m1 > m2 ? m1 : m2;
+  static constexpr int GK = CH * ldG * 2 * 2, QT = CH * ldQ * 2;
+  static constexpr int oGK = R0, oQT = oGK + GK, oES = oQT + QT, oGC = oES + 4 * DK * 4,
                        oBS = oGC + DK * 4, total = oBS + CH * 4;
   static_assert(total <= 163840, "LDS budget (160 KiB)");
-  static_assert((oGK | oKT | oES | oGC | oBS | oTF | oTB | oVS | oPT) % 16 == 0, "alignment");
+  static_assert(4 * 2048 <= AF, "T-solve scratch fits in the MQ0 region");
+  static_assert(oTB >= oTF + AF, "TB is built from TF and must not overlap it");
+  static_assert((oGK | oQT | oES | oGC | oBS | oTF | oTB | oVS | oPT | oKT | oAF2 | oMQ1) % 16 == 0,
+                "alignment");
 };
 
 template <int DK, typename TOut>
@@ -155,35 +167,46 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     const int32_t* __restrict__ cu_seqlens, int n_seq, int T, int H, int DV) {
   using L = Plan<DK>;
   constexpr int NKB = DK / 32;   // 32-channel blocks
+  constexpr int NKH = NKB / 2;   // blocks of one channel half
   constexpr int NCHT = DK / 16;  // 16-channel tiles
-  constexpr int RPW = DK / 4;    // state rows per wave
+  constexpr int RPW = DK / 4;    // state rows per token-tile wave pair
   constexpr int RTW = RPW / 16;  // state row tiles per wave
-  constexpr int NCT = BV / 16;   // value tiles
-  constexpr int ldR = L::ldR, ldG = L::ldG, ldA = L::ldA, ldT = L::ldT, ldV = L::ldV,
-                ldS = L::ldS, ldP = L::ldP;
+  constexpr int NCH = BV / 32;   // value tiles per wave (its 32-column half)
+  constexpr int ldR = L::ldR, ldG = L::ldG, ldQ = L::ldQ, ldA = L::ldA, ldT = L::ldT,
+                ldV = L::ldV, ldS = L::ldS, ldP = L::ldP;
   constexpr int loR = 160 * ldR, loG = CH * ldG, loT = CH * ldT, loS = BV * ldS, loP = BV * ldP;
 
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* RT = reinterpret_cast<bf16*>(smem + L::oRT);
   float* AF = reinterpret_cast<float*>(smem + L::oAF);
+  float* AF2 = reinterpret_cast<float*>(smem + L::oAF2);
   float* TF = reinterpret_cast<float*>(smem + L::oTF);
+  float* MQ0 = reinterpret_cast<float*>(smem + L::oMQ0);
+  float* MQ1 = reinterpret_cast<float*>(smem + L::oMQ1);
+  float* SCR = reinterpret_cast<float*>(smem + L::oSCR);
   bf16* TB = reinterpret_cast<bf16*>(smem + L::oTB);
   bf16* VS = reinterpret_cast<bf16*>(smem + L::oVS);
   bf16* ST = reinterpret_cast<bf16*>(smem + L::oST);
   bf16* PT = reinterpret_cast<bf16*>(smem + L::oPT);
-  bf16* GK = reinterpret_cast<bf16*>(smem + L::oGK);
   bf16* KT = reinterpret_cast<bf16*>(smem + L::oKT);
+  bf16* GK = reinterpret_cast<bf16*>(smem + L::oGK);
+  bf16* QT = reinterpret_cast<bf16*>(smem + L::oQT);
   float* ES = reinterpret_cast<float*>(smem + L::oES);  // [4][DK] tile decays
   float* GC = reinterpret_cast<float*>(smem + L::oGC);  // [DK] chunk decay
   float* BS = reinterpret_cast<float*>(smem + L::oBS);  // [64] beta
 
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
+  // Eight waves: wave pair (w, hh) with hh = 0, 1 shares token tile w.  Waves
+  // are dealt to the 4 SIMDs round-robin, so pairing tile s with tile 3 - s
+  // on one SIMD evens out the per-tile work (low tiles build more decay
+  // variants, high tiles compute more A / Mqk pairs).
+  const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = w8 >> 2;                       // channel half (prep) / value half (serial)
+  const int w = hh ? 3 - (w8 & 3) : (w8 & 3);   // token tile
   const int lane = tid & 63;
-  const int tr = lane & 15;  // token within the wave's tile / MFMA row-col index
-  const int g = lane >> 4;   // k group of the MFMA layouts
+  const int tr = lane & 15;
+  const int g = lane >> 4;
 
-  // ---- work item (sequence, head, value slice); slices of a head share an XCD
   const int nsl = DV / BV;
   const int total = n_seq * H * nsl;
   int wid = blockIdx.x;
@@ -200,59 +223,54 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     len = T;
   }
   const int vcol0 = sl * BV;
+  const int vh0 = 32 * hh;  // this wave's value columns within the slice
 
-  // state slice: wave w owns key rows [w*RPW, (w+1)*RPW), natural channel order
-  floatx4 Sacc[RTW][NCT];
+  // state: wave (w, hh) owns key rows [w*RPW, (w+1)*RPW) x value columns vh0..vh0+31
+  floatx4 Sacc[RTW][NCH];
   {
     const float* si = s_init ? s_init + ((size_t)seq * H + h) * DK * DV : nullptr;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+      for (int c = 0; c < NCH; ++c)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = w * RPW + rt * 16 + 4 * g + i;
-          Sacc[rt][ct][i] = si ? si[(size_t)row * DV + vcol0 + ct * 16 + tr] : 0.f;
+          Sacc[rt][c][i] = si ? si[(size_t)row * DV + vcol0 + vh0 + c * 16 + tr] : 0.f;
         }
   }
 
   const int r = 16 * w + tr;  // this lane's token within the chunk
 
-  // Global loads of one chunk for this lane's token: k, q, alpha (its 8
-  // channels of every 32-channel block), 16 values of the V slice and beta.
-  // The next chunk's loads are issued before the current chunk is processed,
-  // so their latency hides behind a whole chunk of work.
+  // Global loads of one chunk for this lane's token and channel half (k, q,
+  // alpha), 8 values of the V slice and beta; issued for the next chunk at four
+  // points of the current one so the vector-memory queue never blocks issue.
   struct ChunkIn {
-    uint2v k[NKB][2], q[NKB][2];
-    floatx4 a[NKB][2];
-    uint4v v[2];
+    uint2v k[NKH][2], q[NKH][2];
+    floatx4 a[NKH][2];
+    uint4v v;
     float b;
   };
-  // part 0: k, 1: q, 2: alpha, 3: v and beta.  The parts of the next chunk are
-  // issued at four points of the current one, a few instructions at a time, so
-  // the vector-memory queue never fills and blocks instruction issue.
   auto load_part = [&](long long cc, ChunkIn& in, int part) {
     const int nvc = (int)(len - cc < CH ? len - cc : CH);
     const bool okc = r < nvc;
     const size_t thc = (size_t)(start + cc + r) * H + h;
     if (part == 3) {
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        in.v[hf] = okc ? *reinterpret_cast<const uint4v*>(v + thc * DV + vcol0 + 16 * g + 8 * hf)
-                       : uint4v{0u, 0u, 0u, 0u};
+      in.v = okc ? *reinterpret_cast<const uint4v*>(v + thc * DV + vcol0 + vh0 + 8 * g)
+                 : uint4v{0u, 0u, 0u, 0u};
       in.b = okc ? beta[thc] : 0.f;
       return;
     }
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kk = 0; kk < NKH; ++kk)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int c = 32 * kb + 16 * hf + 4 * g;
-        if (part == 0) in.k[kb][hf] = okc ? *reinterpret_cast<const uint2v*>(k + thc * DK + c)
+        const int c = 32 * (NKH * hh + kk) + 16 * hf + 4 * g;
+        if (part == 0) in.k[kk][hf] = okc ? *reinterpret_cast<const uint2v*>(k + thc * DK + c)
                                           : uint2v{0u, 0u};
-        if (part == 1) in.q[kb][hf] = okc ? *reinterpret_cast<const uint2v*>(q + thc * DK + c)
+        if (part == 1) in.q[kk][hf] = okc ? *reinterpret_cast<const uint2v*>(q + thc * DK + c)
                                           : uint2v{0u, 0u};
-        if (part == 2) in.a[kb][hf] = okc ? *reinterpret_cast<const floatx4*>(alpha + thc * DK + c)
+        if (part == 2) in.a[kk][hf] = okc ? *reinterpret_cast<const floatx4*>(alpha + thc * DK + c)
                                           : floatx4{1.f, 1.f, 1.f, 1.f};
       }
   };
@@ -269,45 +287,40 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     const ChunkIn cur = nxt;
     const bool more = c0 + CH < len;
     if (more) load_part(c0 + CH, nxt, 0);
-    const auto& kraw = cur.k;
-    const auto& qraw = cur.q;
-    const auto& araw = cur.a;
-    const auto& vraw = cur.v;
     const float bt = cur.b;
 
     // ---- within-tile decay products P (inclusive scan over the 16 tokens)
-    float Pv[NKB][8];
+    float Pv[NKH][8];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kk = 0; kk < NKH; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float x = araw[kb][e >> 2][e & 3];
+        float x = cur.a[kk][e >> 2][e & 3];
         x *= row_shr_or_one<1>(x);
         x *= row_shr_or_one<2>(x);
         x *= row_shr_or_one<4>(x);
         x *= row_shr_or_one<8>(x);
-        Pv[kb][e] = x;
+        Pv[kk][e] = x;
       }
-    if (tr == 15) {  // whole-tile decay E_w
+    if (tr == 15) {  // whole-tile decay E_w of this wave's channels
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int kk = 0; kk < NKH; ++kk)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
-          *reinterpret_cast<floatx4*>(ES + w * DK + 32 * kb + 16 * hf + 4 * g) =
-              floatx4{Pv[kb][4 * hf], Pv[kb][4 * hf + 1], Pv[kb][4 * hf + 2], Pv[kb][4 * hf + 3]};
+          *reinterpret_cast<floatx4*>(ES + w * DK + 32 * (NKH * hh + kk) + 16 * hf + 4 * g) =
+              floatx4{Pv[kk][4 * hf], Pv[kk][4 * hf + 1], Pv[kk][4 * hf + 2], Pv[kk][4 * hf + 3]};
     }
-    if (g == 0) BS[r] = bt;
+    if (g == 0 && hh == 0) BS[r] = bt;
     __syncthreads();
 
-    // ---- operands.  Registers: KL = k*P (A's left factor), QL = q*P (split),
-    // QT = q*Gamma (operand of (Gamma*Q) S).  LDS: RT rows of this tile for the
-    // row tiles mm >= w, GK = k*Gamma and KT = k*Gamma_C/Gamma (split).
-    bf16x8 kl[NKB], qlh[NKB], qll[NKB], qt[NKB];
+    // ---- operands for this wave's channels.  Registers: KL = k*P and QL = q*P
+    // (split), the B operands of A^T and Mqk^T; Ktil (split) until it is stored.
+    // LDS: RT rows of this tile for row tiles mm >= w, GK = k*Gamma (split,
+    // [token][channel]), QT = q*Gamma ([token][position]).
+    bf16x8 kl[NKH], qlh[NKH], qll[NKH], kth[NKH], ktl[NKH];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      // whole-tile decays of this lane's channels: E_w, the product over the
-      // tiles before w (pre) and after w (post); w is uniform, so these are
-      // scalar-controlled loops over LDS reads
+    for (int kk = 0; kk < NKH; ++kk) {
+      const int kb = NKH * hh + kk;
       auto ld_e = [&](int i, float* out) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -316,14 +329,14 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
           for (int e = 0; e < 4; ++e) out[4 * hf + e] = e4[e];
         }
       };
-      float kk[8], qq[8], pre[8], post[8], Ew[8], tmp[8];
+      float kk8[8], qq[8], pre[8], post[8], Ew[8], tmp[8];
       ld_e(w, Ew);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         pre[e] = 1.f;
         post[e] = 1.f;
-        kk[e] = bfv(kraw[kb][e >> 2][(e & 3) >> 1], e & 1);
-        qq[e] = bfv(qraw[kb][e >> 2][(e & 3) >> 1], e & 1);
+        kk8[e] = bfv(cur.k[kk][e >> 2][(e & 3) >> 1], e & 1);
+        qq[e] = bfv(cur.q[kk][e >> 2][(e & 3) >> 1], e & 1);
       }
       for (int i = 0; i < w; ++i) {
         ld_e(i, tmp);
@@ -335,27 +348,26 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) post[e] *= tmp[e];
       }
-      float x[8], y[8];
+      float y[8], gk[8], kt[8], rd[8], re[8];
+      bf16x8 qt8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        x[e] = kk[e] * Pv[kb][e];
-        kl[kb][e] = (bf16)x[e];
-        y[e] = qq[e] * Pv[kb][e];
+        kl[kk][e] = (bf16)(kk8[e] * Pv[kk][e]);
+        y[e] = qq[e] * Pv[kk][e];
+        const float gam = pre[e] * Pv[kk][e];
+        qt8[e] = (bf16)(qq[e] * gam);
+        gk[e] = kk8[e] * gam;
+        const float ip = __builtin_amdgcn_rcpf(Pv[kk][e]);
+        kt[e] = kk8[e] * ((Ew[e] * ip) * post[e]);
+        rd[e] = kk8[e] * ip;
+        re[e] = kk8[e] * (Ew[e] * ip);
       }
-      split8(y, qlh[kb], qll[kb]);
-      float gk[8], kt[8];
+      split8(y, qlh[kk], qll[kk]);
+      split8(kt, kth[kk], ktl[kk]);
+      *reinterpret_cast<bf16x8*>(QT + r * ldQ + 32 * kb + 8 * g) = qt8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float gam = pre[e] * Pv[kb][e];
-        qt[kb][e] = (bf16)(qq[e] * gam);
-        gk[e] = kk[e] * gam;
-        kt[e] = kk[e] * ((Ew[e] * __builtin_amdgcn_rcpf(Pv[kb][e])) * post[e]);
-      }
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
+      for (int hf = 0; hf < 2; ++hf)
         st_split4(GK + r * ldG + 32 * kb + 16 * hf + 4 * g, loG, gk + 4 * hf);
-        st_split4(KT + r * ldG + 32 * kb + 16 * hf + 4 * g, loG, kt + 4 * hf);
-      }
       if (w == 0 && tr == 0) {
         float gc[8];
 #pragma unroll
@@ -364,15 +376,6 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
         for (int hf = 0; hf < 2; ++hf)
           *reinterpret_cast<floatx4*>(GC + 32 * kb + 16 * hf + 4 * g) =
               floatx4{gc[4 * hf], gc[4 * hf + 1], gc[4 * hf + 2], gc[4 * hf + 3]};
-      }
-      // right operands: diagonal tile k/P, then k*(E_w/P) decayed through the
-      // whole tiles between w and mm
-      float rd[8], re[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float ip = __builtin_amdgcn_rcpf(Pv[kb][e]);
-        rd[e] = kk[e] * ip;
-        re[e] = kk[e] * (Ew[e] * ip);
       }
       {
         const int row = 8 * w * (w + 1) + r;  // 16 * w(w+1)/2 rows precede row tile w
@@ -397,7 +400,8 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     __syncthreads();
     if (more) load_part(c0 + CH, nxt, 1);
 
-    // ---- A^T and Mqk^T tiles (j in tile n, r in tile w), n = 0..w
+    // ---- A^T and Mqk^T tiles (j in tile n, r in tile w), n = 0..w, over this
+    // wave's channel half; the two halves are summed through LDS
     floatx4 accA[4], accM[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
@@ -406,75 +410,114 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       if (n > w) continue;
       const int row = 8 * w * (w + 1) + 16 * n + tr;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+      for (int kk = 0; kk < NKH; ++kk) {
+        const int kb = NKH * hh + kk;
         const bf16x8 ah = frag_ld(RT, ldR, row, 32 * kb);
         const bf16x8 al = frag_ld(RT + loR, ldR, row, 32 * kb);
-        accA[n] = mfma_bf16(ah, kl[kb], accA[n]);
-        accM[n] = mma_ab(ah, al, qlh[kb], qll[kb], accM[n]);
+        accA[n] = mfma_bf16(ah, kl[kk], accA[n]);
+        accM[n] = mma_ab(ah, al, qlh[kk], qll[kk], accM[n]);
       }
     }
-    __syncthreads();  // RT reads done; AF overwrites it
-    // A (row r, beta_r, strictly lower) to LDS; Mqk^T into operand fragments of
-    // Mqk P (token k-slots in the 8g/4-swizzled order, masked j <= r)
-    bf16x8 mqh[2], mql[2];
+    __syncthreads();  // RT reads done; the partials overwrite it
+    {
+      float* AFh = hh ? AF2 : AF;
+      float* MQh = hh ? MQ1 : MQ0;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      float a4[4], m4[4];
+      for (int n = 0; n < 4; ++n) {
+        if (n > w) continue;
+        float a4[4], m4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 16 * n + 4 * g + i;
-        a4[i] = (n <= w && j < r) ? bt * accA[n][i] : 0.f;
-        m4[i] = (n <= w && j <= r) ? accM[n][i] : 0.f;
-      }
-      if (n <= w) *reinterpret_cast<floatx4*>(AF + r * ldA + 16 * n + 4 * g) =
-          floatx4{a4[0], a4[1], a4[2], a4[3]};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16 hh = (bf16)m4[i];
-        mqh[n >> 1][4 * (n & 1) + i] = hh;
-        mql[n >> 1][4 * (n & 1) + i] = (bf16)(m4[i] - (float)hh);
+        for (int i = 0; i < 4; ++i) {
+          const int j = 16 * n + 4 * g + i;
+          a4[i] = (j < r) ? bt * accA[n][i] : 0.f;
+          m4[i] = (j <= r) ? accM[n][i] : 0.f;
+        }
+        *reinterpret_cast<floatx4*>(AFh + r * ldA + 16 * n + 4 * g) = floatx4{a4[0], a4[1], a4[2], a4[3]};
+        *reinterpret_cast<floatx4*>(MQh + r * ldA + 16 * n + 4 * g) = floatx4{m4[0], m4[1], m4[2], m4[3]};
       }
     }
     __syncthreads();
     if (more) load_part(c0 + CH, nxt, 2);
-
-    // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by substitution (fp32) ...
-    if (tr == lane) {  // lanes 0..15: column tr of block w
-      const int b0 = 16 * w;
-      float t[16];
+    // Mqk^T into operand fragments of Mqk P (token k-slots in the swizzled order)
+    bf16x8 mqh[2], mql[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) t[i] = (i == tr) ? 1.f : 0.f;
+    for (int n = 0; n < 4; ++n) {
+      floatx4 m4 = {0.f, 0.f, 0.f, 0.f};
+      if (n <= w)
+        m4 = *reinterpret_cast<const floatx4*>(MQ0 + r * ldA + 16 * n + 4 * g) +
+             *reinterpret_cast<const floatx4*>(MQ1 + r * ldA + 16 * n + 4 * g);
 #pragma unroll
-      for (int jj = 0; jj < 15; ++jj)
-#pragma unroll
-        for (int i = jj + 1; i < 16; ++i) t[i] -= AF[(b0 + i) * ldA + b0 + jj] * t[jj];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) TF[(b0 + i) * ldA + b0 + tr] = t[i];
+      for (int i = 0; i < 4; ++i) {
+        const bf16 hv = (bf16)m4[i];
+        mqh[n >> 1][4 * (n & 1) + i] = hv;
+        mql[n >> 1][4 * (n & 1) + i] = (bf16)(m4[i] - (float)hv);
+      }
     }
-    __syncthreads();
-    // ... then below the diagonal by distance d: T_mn = -T_mm sum_{j=n}^{m-1} A_mj T_jn
+    __syncthreads();  // MQ0 / MQ1 reads done; the solve's scratch reuses them
+
+    // ---- T = (I + A)^{-1} (A = AF + AF2), blockwise over 16x16 tiles on fp32
+    // MFMA 16x16x4 by waves 0..3.  Every product is (LDS matrix, row-major, read
+    // 16 bytes per lane as the A operand) x (register matrix in the accumulator
+    // layout, which is the B operand layout): lane l supplies k = 4g + s in MFMA s.
+    {
+      auto arow = [&](const float* M, int ld) -> floatx4 {
+        return *reinterpret_cast<const floatx4*>(M + tr * ld + 4 * g);
+      };
+      auto mm16 = [&](const floatx4& a, const floatx4& x) -> floatx4 {
+        floatx4 yv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int d = 1; d < 4; ++d) {
-      const int m = w, n = w - d;
-      if (n >= 0) {
-        floatx4 X = {0.f, 0.f, 0.f, 0.f};
-        for (int j = n; j < m; ++j)
+        for (int s = 0; s < 4; ++s) yv = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], x[s], yv, 0, 0, 0);
+        return yv;
+      };
+      if (hh == 0) {
+        // diagonal block of tile w: N = A_ww strictly lower, N^16 = 0, so
+        // (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8)
+        const int b0 = 16 * w;
+        float* S2 = SCR + w * 512;
+        float* S4 = S2 + 256;
+        floatx4 nB;
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const float a = AF[(16 * m + tr) * ldA + 16 * j + 4 * g + s];
-            const float b = TF[(16 * j + 4 * g + s) * ldA + 16 * n + tr];
-            X = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, X, 0, 0, 0);
-          }
-        floatx4 Y = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 4; ++i)
+          nB[i] = AF[(b0 + 4 * g + i) * ldA + b0 + tr] + AF2[(b0 + 4 * g + i) * ldA + b0 + tr];
+        const floatx4 aN = arow(AF + b0 * ldA + b0, ldA) + arow(AF2 + b0 * ldA + b0, ldA);
+        const floatx4 n2 = mm16(aN, nB);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const float a = TF[(16 * m + tr) * ldA + 16 * m + 4 * g + s];
-          Y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, X[s], Y, 0, 0, 0);
-        }
+        for (int i = 0; i < 4; ++i) S2[(4 * g + i) * 16 + tr] = n2[i];
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const floatx4 a2 = arow(S2, 16);
+        const floatx4 n4 = mm16(a2, n2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) TF[(16 * m + 4 * g + i) * ldA + 16 * n + tr] = -Y[i];
+        for (int i = 0; i < 4; ++i) S4[(4 * g + i) * 16 + tr] = n4[i];
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const floatx4 a4 = arow(S4, 16);
+        floatx4 X = mm16(a4, n4);  // N^8
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[i] += (4 * g + i == tr) ? 1.f : 0.f;
+        X += mm16(a4, X);
+        X += mm16(a2, X);
+        X -= mm16(aN, X);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) TF[(b0 + 4 * g + i) * ldA + b0 + tr] = X[i];
       }
       __syncthreads();
+      // below the diagonal by distance d: T_mn = -T_mm sum_{j=n}^{m-1} A_mj T_jn
+#pragma unroll
+      for (int d = 1; d < 4; ++d) {
+        const int m = w, n = w - d;
+        if (hh == 0 && n >= 0) {
+          floatx4 Xs = {0.f, 0.f, 0.f, 0.f};
+          for (int j = n; j < m; ++j) {
+            floatx4 tB;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tB[i] = TF[(16 * j + 4 * g + i) * ldA + 16 * n + tr];
+            Xs += mm16(arow(AF + 16 * m * ldA + 16 * j, ldA) + arow(AF2 + 16 * m * ldA + 16 * j, ldA), tB);
+          }
+          const floatx4 Y = mm16(arow(TF + 16 * m * ldA + 16 * m, ldA), Xs);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) TF[(16 * m + 4 * g + i) * ldA + 16 * n + tr] = -Y[i];
+        }
+        __syncthreads();
+      }
     }
 
     if (more) load_part(c0 + CH, nxt, 3);
@@ -491,15 +534,14 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       for (int e = 0; e < 4; ++e) x4[e] = (j0 + e <= rr) ? t4[e] * b4[e] : 0.f;
       st_split4(TB + rr * ldT + j0, loT, x4);
     }
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-      *reinterpret_cast<uint4v*>(VS + r * ldV + 16 * g + 8 * hf) = vraw[hf];
+    *reinterpret_cast<uint4v*>(VS + r * ldV + vh0 + 8 * g) = cur.v;
     __syncthreads();
 
-    // ---- W^T = (Gamma*K)^T (T Diag b)^T for this wave's tokens (all channels),
-    // kept as the split operand of W S; U = T Diag(b) V
+    // ---- W^T = (Gamma*K)^T (T Diag b)^T for this tile's tokens (all channels,
+    // computed by both waves of the pair), kept as the split operand of W S;
+    // U = T Diag(b) V for this wave's 32 value columns
     bf16x8 wh[NKB], wl[NKB];
-    floatx4 accU[NCT];
+    floatx4 accU[NCH];
     {
       bf16x8 tbh[2], tbl[2];
 #pragma unroll
@@ -519,67 +561,84 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bf16 hh = (bf16)acc[i];
-          wh[ct >> 1][4 * (ct & 1) + i] = hh;
-          wl[ct >> 1][4 * (ct & 1) + i] = (bf16)(acc[i] - (float)hh);
+          const bf16 hv = (bf16)acc[i];
+          wh[ct >> 1][4 * (ct & 1) + i] = hv;
+          wl[ct >> 1][4 * (ct & 1) + i] = (bf16)(acc[i] - (float)hv);
         }
       }
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        accU[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < NCH; ++c) {
+        accU[c] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (kb > (w >> 1)) continue;
-          const bf16x8 b = frag_tr(VS, ldV, 16 * ct, 32 * kb + 8 * g, 32 * kb + 8 * g + 4);
-          accU[ct] = mfma_bf16(tbh[kb], b, accU[ct]);
-          accU[ct] = mfma_bf16(tbl[kb], b, accU[ct]);
+          const bf16x8 b = frag_tr(VS, ldV, vh0 + 16 * c, 32 * kb + 8 * g, 32 * kb + 8 * g + 4);
+          accU[c] = mfma_bf16(tbh[kb], b, accU[c]);
+          accU[c] = mfma_bf16(tbl[kb], b, accU[c]);
         }
       }
     }
-    __syncthreads();  // TB / VS / TF reads done; ST and PT overwrite them
+    __syncthreads();  // TB / VS / GK reads done; ST, PT and KT overwrite the region
 
-    // ---- state to LDS as the B operand of W S and (Gamma*Q) S: [value][channel
-    // position], position 32kb + 8g + 4h + i holds channel 32kb + 16h + 4g + i
+    // ---- Ktil ([token][channel], split) and the state as the B operand of W S
+    // and (Gamma*Q) S: [value][channel position], position 32kb + 8g + 4h + i
+    // holds channel 32kb + 16h + 4g + i
+#pragma unroll
+    for (int kk = 0; kk < NKH; ++kk) {
+      const int kb = NKH * hh + kk;
+      // whole 32-bit words (element pairs) of the packed registers
+      const uint4v uh = __builtin_bit_cast(uint4v, kth[kk]);
+      const uint4v ul = __builtin_bit_cast(uint4v, ktl[kk]);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        *reinterpret_cast<uint2v*>(KT + r * ldG + 32 * kb + 16 * hf + 4 * g) =
+            uint2v{uh[2 * hf], uh[2 * hf + 1]};
+        *reinterpret_cast<uint2v*>(KT + r * ldG + 32 * kb + 16 * hf + 4 * g + loG) =
+            uint2v{ul[2 * hf], ul[2 * hf + 1]};
+      }
+    }
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
       const int c0r = w * RPW + rt * 16;
       const int pos = 32 * (c0r >> 5) + 8 * g + 4 * ((c0r >> 4) & 1);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        float x4[4] = {Sacc[rt][ct][0], Sacc[rt][ct][1], Sacc[rt][ct][2], Sacc[rt][ct][3]};
-        st_split4(ST + (16 * ct + tr) * ldS + pos, loS, x4);
+      for (int c = 0; c < NCH; ++c) {
+        float x4[4] = {Sacc[rt][c][0], Sacc[rt][c][1], Sacc[rt][c][2], Sacc[rt][c][3]};
+        st_split4(ST + (vh0 + 16 * c + tr) * ldS + pos, loS, x4);
       }
     }
     __syncthreads();
 
-    // ---- P = U - W S and O = (Gamma*Q) S for this wave's 16 tokens
-    floatx4 accO[NCT];
+    // ---- P = U - W S and O = (Gamma*Q) S for this tile's tokens, this wave's columns
+    floatx4 accO[NCH];
     {
-      floatx4 accW[NCT];
+      floatx4 accW[NCH];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        accW[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-        accO[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < NCH; ++c) {
+        accW[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+        accO[c] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 aq = frag_ld(QT, ldQ, r, 32 * kb);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          const bf16x8 bh = frag_ld(ST, ldS, 16 * ct + tr, 32 * kb);
-          const bf16x8 bl = frag_ld(ST + loS, ldS, 16 * ct + tr, 32 * kb);
-          accW[ct] = mma_ab(wh[kb], wl[kb], bh, bl, accW[ct]);
-          accO[ct] = mfma_bf16(qt[kb], bh, accO[ct]);
-          accO[ct] = mfma_bf16(qt[kb], bl, accO[ct]);
+        for (int c = 0; c < NCH; ++c) {
+          const bf16x8 bh = frag_ld(ST, ldS, vh0 + 16 * c + tr, 32 * kb);
+          const bf16x8 bl = frag_ld(ST + loS, ldS, vh0 + 16 * c + tr, 32 * kb);
+          accW[c] = mma_ab(wh[kb], wl[kb], bh, bl, accW[c]);
+          accO[c] = mfma_bf16(aq, bh, accO[c]);
+          accO[c] = mfma_bf16(aq, bl, accO[c]);
         }
+      }
       // P to LDS as [value][token position]; token 32kb + 16h + 4g + i sits at
       // position 32kb + 8g + 4h + i (the order of the Mqk^T operand)
       const int pos = 32 * (w >> 1) + 8 * g + 4 * (w & 1);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
+      for (int c = 0; c < NCH; ++c) {
         float x4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x4[i] = accU[ct][i] - accW[ct][i];
-        st_split4(PT + (16 * ct + tr) * ldP + pos, loP, x4);
+        for (int i = 0; i < 4; ++i) x4[i] = accU[c][i] - accW[c][i];
+        st_split4(PT + (vh0 + 16 * c + tr) * ldP + pos, loP, x4);
       }
     }
     __syncthreads();
@@ -589,48 +648,48 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     for (int kb = 0; kb < 2; ++kb) {
       if (kb > (w >> 1)) continue;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const bf16x8 bh = frag_ld(PT, ldP, 16 * ct + tr, 32 * kb);
-        const bf16x8 bl = frag_ld(PT + loP, ldP, 16 * ct + tr, 32 * kb);
-        accO[ct] = mma_ab(mqh[kb], mql[kb], bh, bl, accO[ct]);
+      for (int c = 0; c < NCH; ++c) {
+        const bf16x8 bh = frag_ld(PT, ldP, vh0 + 16 * c + tr, 32 * kb);
+        const bf16x8 bl = frag_ld(PT + loP, ldP, vh0 + 16 * c + tr, 32 * kb);
+        accO[c] = mma_ab(mqh[kb], mql[kb], bh, bl, accO[c]);
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = 16 * w + 4 * g + i;
       if (rr < nv) {
-        TOut* orow = o + ((size_t)(tok0 + rr) * H + h) * DV + vcol0 + tr;
+        TOut* orow = o + ((size_t)(tok0 + rr) * H + h) * DV + vcol0 + vh0 + tr;
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) __builtin_nontemporal_store((TOut)accO[ct][i], orow + 16 * ct);
+        for (int c = 0; c < NCH; ++c) __builtin_nontemporal_store((TOut)accO[c][i], orow + 16 * c);
       }
     }
 
     // ---- S = Diag(Gamma_C) S + Ktil^T P
     {
-      bf16x8 bph[2][NCT], bpl[2][NCT];
+      bf16x8 bph[2][NCH], bpl[2][NCH];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          bph[kb][ct] = frag_ld(PT, ldP, 16 * ct + tr, 32 * kb);
-          bpl[kb][ct] = frag_ld(PT + loP, ldP, 16 * ct + tr, 32 * kb);
+        for (int c = 0; c < NCH; ++c) {
+          bph[kb][c] = frag_ld(PT, ldP, vh0 + 16 * c + tr, 32 * kb);
+          bpl[kb][c] = frag_ld(PT + loP, ldP, vh0 + 16 * c + tr, 32 * kb);
         }
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt) {
         const int c0r = w * RPW + rt * 16;
         const floatx4 gc = *reinterpret_cast<const floatx4*>(GC + c0r + 4 * g);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
+        for (int c = 0; c < NCH; ++c)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Sacc[rt][ct][i] *= gc[i];
+          for (int i = 0; i < 4; ++i) Sacc[rt][c][i] *= gc[i];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           // Ktil^T rows c0r.., token k-slots in the same order as P's positions
           const bf16x8 ah = frag_tr(KT, ldG, c0r, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g);
           const bf16x8 al = frag_tr(KT + loG, ldG, c0r, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g);
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct)
-            Sacc[rt][ct] = mma_ab(ah, al, bph[kb][ct], bpl[kb][ct], Sacc[rt][ct]);
+          for (int c = 0; c < NCH; ++c)
+            Sacc[rt][c] = mma_ab(ah, al, bph[kb][c], bpl[kb][c], Sacc[rt][c]);
         }
       }
     }
@@ -641,11 +700,11 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+      for (int c = 0; c < NCH; ++c)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = w * RPW + rt * 16 + 4 * g + i;
-          sf[(size_t)row * DV + vcol0 + ct * 16 + tr] = Sacc[rt][ct][i];
+          sf[(size_t)row * DV + vcol0 + vh0 + c * 16 + tr] = Sacc[rt][c][i];
         }
   }
 }
