@@ -60,12 +60,11 @@ typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
 typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
 
 // Operand fragment (16 columns m0.., 8 k values per lane) of a row-major
-// [k][m] LDS tile: lane l gets column m0 + l%16 at rows ra..ra+3 and rb..rb+3
-// (ra, rb chosen per 16-lane group).  Two transpose reads, each of which
+// [k][m] LDS tile: lane l (j = l%16) gets column m0 + j at rows ra..ra+3 and
+// rb..rb+3 (ra, rb chosen per 16-lane group).  Two transpose reads, each of which
 // gives lane i of a 16-lane group element i%4 of the 8-byte words read by
 // lanes i/4, i/4+4, i/4+8, i/4+12 of that group.
-__device__ __forceinline__ bf16x8 frag_tr(const bf16* X, int ld, int m0, int ra, int rb) {
-  const int j = threadIdx.x & 15;
+__device__ __forceinline__ bf16x8 frag_tr(const bf16* X, int ld, int m0, int ra, int rb, int j) {
   const bf16* pa = X + (ra + (j >> 2)) * ld + m0 + 4 * (j & 3);
   const bf16* pb = X + (rb + (j >> 2)) * ld + m0 + 4 * (j & 3);
   const short4v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)pa);
@@ -74,16 +73,38 @@ __device__ __forceinline__ bf16x8 frag_tr(const bf16* X, int ld, int m0, int ra,
   return __builtin_bit_cast(bf16x8, s);
 }
 
-// 16 contiguous bytes of a k-contiguous LDS row.
-__device__ __forceinline__ bf16x8 frag_ld(const bf16* X, int ld, int row, int k0) {
-  return *reinterpret_cast<const bf16x8*>(X + row * ld + k0 + 8 * ((threadIdx.x & 63) >> 4));
+// 16 contiguous bytes of a k-contiguous LDS row (g = lane / 16).
+__device__ __forceinline__ bf16x8 frag_ld(const bf16* X, int ld, int row, int k0, int g) {
+  return *reinterpret_cast<const bf16x8*>(X + row * ld + k0 + 8 * g);
 }
 
-template <int D>
-__device__ __forceinline__ float row_shr_or_one(float x) {
-  // lane i of each 16-lane row gets lane i-D's value; lanes i < D keep 1.0
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-      __builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, x), 0x110 + D, 0xF, 0xF, false));
+// Inclusive product scan over the 16 lanes of each DPP row, for N values per
+// lane: lane i of a row ends with x_0 * ... * x_i.  Each step is one
+// v_mul_f32_dpp with row_shr:D and bound_ctrl off, which leaves lanes i < D
+// unwritten (they keep x_i).  A step reads values written N instructions
+// earlier, so only the first needs the 2 wait states of a VALU write -> DPP
+// read.
+template <int N>
+__device__ __forceinline__ void row_scan_mul(float* x) {
+  static_assert(N == 8 || N == 16, "scan width");
+#define KDA_SCAN_STEP(D, i) "v_mul_f32_dpp %" #i ", %" #i ", %" #i " row_shr:" #D " row_mask:0xf bank_mask:0xf\n"
+#define KDA_SCAN8(D) KDA_SCAN_STEP(D, 0) KDA_SCAN_STEP(D, 1) KDA_SCAN_STEP(D, 2) KDA_SCAN_STEP(D, 3) \
+  KDA_SCAN_STEP(D, 4) KDA_SCAN_STEP(D, 5) KDA_SCAN_STEP(D, 6) KDA_SCAN_STEP(D, 7)
+#define KDA_SCAN16(D) KDA_SCAN8(D) KDA_SCAN_STEP(D, 8) KDA_SCAN_STEP(D, 9) KDA_SCAN_STEP(D, 10) \
+  KDA_SCAN_STEP(D, 11) KDA_SCAN_STEP(D, 12) KDA_SCAN_STEP(D, 13) KDA_SCAN_STEP(D, 14) KDA_SCAN_STEP(D, 15)
+  if constexpr (N == 8) {
+    __asm__("s_nop 1\n" KDA_SCAN8(1) KDA_SCAN8(2) KDA_SCAN8(4) KDA_SCAN8(8)
+            : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+              "+v"(x[7]));
+  } else {
+    __asm__("s_nop 1\n" KDA_SCAN16(1) KDA_SCAN16(2) KDA_SCAN16(4) KDA_SCAN16(8)
+            : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+              "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]),
+              "+v"(x[13]), "+v"(x[14]), "+v"(x[15]));
+  }
+#undef KDA_SCAN16
+#undef KDA_SCAN8
+#undef KDA_SCAN_STEP
 }
 
 __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
@@ -117,6 +138,19 @@ __device__ __forceinline__ void st_split4(bf16* hi, int lo_off, const float* x) 
   }
   *reinterpret_cast<short4v*>(hi) = sh;
   *reinterpret_cast<short4v*>(hi + lo_off) = sl;
+}
+
+// x = hi + lo for 4 values, each part packed two bf16 per 32-bit word.
+__device__ __forceinline__ void split4_pack(const float* x, uint2v& hi, uint2v& lo) {
+  unsigned int h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16 hv = (bf16)x[e];
+    h[e] = __builtin_bit_cast(unsigned short, hv);
+    l[e] = __builtin_bit_cast(unsigned short, (bf16)(x[e] - (float)hv));
+  }
+  hi = uint2v{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  lo = uint2v{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
 }
 
 __device__ __forceinline__ floatx4 mma_ab(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
@@ -243,8 +277,11 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
   const int r = 16 * w + tr;  // this lane's token within the chunk
 
   // Global loads of one chunk for this lane's token and channel half (k, q,
-  // alpha), 8 values of the V slice and beta; issued for the next chunk at four
-  // points of the current one so the vector-memory queue never blocks issue.
+  // alpha), 8 values of the V slice and beta.  One register set: each part is
+  // refetched for the next chunk right after its last use in the current one
+  // (alpha after the scan, k and q after the operand build, v and beta after
+  // the V slice is staged), so no copies are needed and the loads have most of
+  // a chunk to arrive.
   struct ChunkIn {
     uint2v k[NKH][2], q[NKH][2];
     floatx4 a[NKH][2];
@@ -274,34 +311,36 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
                                           : floatx4{1.f, 1.f, 1.f, 1.f};
       }
   };
-  ChunkIn nxt;
+  ChunkIn in;
   if (len > 0)
-    for (int part = 0; part < 4; ++part) load_part(0, nxt, part);
+    for (int part = 0; part < 4; ++part) load_part(0, in, part);
 
   for (long long c0 = 0; c0 < len; c0 += CH) {
+    // Lane indices, re-derived each chunk behind an empty asm so that the
+    // compiler recomputes the many per-lane LDS addresses inside the loop
+    // instead of keeping them all live across it (which exhausts the 256
+    // registers a wave has at two waves per SIMD).
+    int lane_x = lane;
+    // __asm__ volatile("" : "+v"(lane_x));
+    const int tr = lane_x & 15;
+    const int g = lane_x >> 4;
+    const int r = 16 * w + tr;
+    const int tid = 64 * w8 + lane_x;
     const int nv = (int)(len - c0 < CH ? len - c0 : CH);
     const long long tok0 = start + c0;
     __syncthreads();  // the previous chunk is done with LDS
 
-    // ---- loads: take the prefetched chunk, start fetching the next one
-    const ChunkIn cur = nxt;
     const bool more = c0 + CH < len;
-    if (more) load_part(c0 + CH, nxt, 0);
-    const float bt = cur.b;
+    const float bt = in.b;
 
     // ---- within-tile decay products P (inclusive scan over the 16 tokens)
     float Pv[NKH][8];
 #pragma unroll
     for (int kk = 0; kk < NKH; ++kk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x = cur.a[kk][e >> 2][e & 3];
-        x *= row_shr_or_one<1>(x);
-        x *= row_shr_or_one<2>(x);
-        x *= row_shr_or_one<4>(x);
-        x *= row_shr_or_one<8>(x);
-        Pv[kk][e] = x;
-      }
+      for (int e = 0; e < 8; ++e) Pv[kk][e] = in.a[kk][e >> 2][e & 3];
+    row_scan_mul<8 * NKH>(&Pv[0][0]);
+    if (more) load_part(c0 + CH, in, 2);
     if (tr == 15) {  // whole-tile decay E_w of this wave's channels
 #pragma unroll
       for (int kk = 0; kk < NKH; ++kk)
@@ -335,8 +374,8 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       for (int e = 0; e < 8; ++e) {
         pre[e] = 1.f;
         post[e] = 1.f;
-        kk8[e] = bfv(cur.k[kk][e >> 2][(e & 3) >> 1], e & 1);
-        qq[e] = bfv(cur.q[kk][e >> 2][(e & 3) >> 1], e & 1);
+        kk8[e] = bfv(in.k[kk][e >> 2][(e & 3) >> 1], e & 1);
+        qq[e] = bfv(in.q[kk][e >> 2][(e & 3) >> 1], e & 1);
       }
       for (int i = 0; i < w; ++i) {
         ld_e(i, tmp);
@@ -398,7 +437,10 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       }
     }
     __syncthreads();
-    if (more) load_part(c0 + CH, nxt, 1);
+    if (more) {
+      load_part(c0 + CH, in, 0);
+      load_part(c0 + CH, in, 1);
+    }
 
     // ---- A^T and Mqk^T tiles (j in tile n, r in tile w), n = 0..w, over this
     // wave's channel half; the two halves are summed through LDS
@@ -412,8 +454,8 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
 #pragma unroll
       for (int kk = 0; kk < NKH; ++kk) {
         const int kb = NKH * hh + kk;
-        const bf16x8 ah = frag_ld(RT, ldR, row, 32 * kb);
-        const bf16x8 al = frag_ld(RT + loR, ldR, row, 32 * kb);
+        const bf16x8 ah = frag_ld(RT, ldR, row, 32 * kb, g);
+        const bf16x8 al = frag_ld(RT + loR, ldR, row, 32 * kb, g);
         accA[n] = mfma_bf16(ah, kl[kk], accA[n]);
         accM[n] = mma_ab(ah, al, qlh[kk], qll[kk], accM[n]);
       }
@@ -437,7 +479,6 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       }
     }
     __syncthreads();
-    if (more) load_part(c0 + CH, nxt, 2);
     // Mqk^T into operand fragments of Mqk P (token k-slots in the swizzled order)
     bf16x8 mqh[2], mql[2];
 #pragma unroll
@@ -520,8 +561,6 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       }
     }
 
-    if (more) load_part(c0 + CH, nxt, 3);
-
     // ---- TB = T Diag(beta) (split, [r][j]) and the V slice ([token][value])
 #pragma unroll
     for (int it = 0; it < CH * CH / 4 / NTH; ++it) {
@@ -534,7 +573,8 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       for (int e = 0; e < 4; ++e) x4[e] = (j0 + e <= rr) ? t4[e] * b4[e] : 0.f;
       st_split4(TB + rr * ldT + j0, loT, x4);
     }
-    *reinterpret_cast<uint4v*>(VS + r * ldV + vh0 + 8 * g) = cur.v;
+    *reinterpret_cast<uint4v*>(VS + r * ldV + vh0 + 8 * g) = in.v;
+    if (more) load_part(c0 + CH, in, 3);
     __syncthreads();
 
     // ---- W^T = (Gamma*K)^T (T Diag b)^T for this tile's tokens (all channels,
@@ -546,8 +586,8 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       bf16x8 tbh[2], tbl[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        tbh[kb] = frag_ld(TB, ldT, r, 32 * kb);
-        tbl[kb] = frag_ld(TB + loT, ldT, r, 32 * kb);
+        tbh[kb] = frag_ld(TB, ldT, r, 32 * kb, g);
+        tbl[kb] = frag_ld(TB + loT, ldT, r, 32 * kb, g);
       }
 #pragma unroll
       for (int ct = 0; ct < NCHT; ++ct) {
@@ -555,8 +595,8 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (kb > (w >> 1)) continue;
-          const bf16x8 ah = frag_tr(GK, ldG, 16 * ct, 32 * kb + 8 * g, 32 * kb + 8 * g + 4);
-          const bf16x8 al = frag_tr(GK + loG, ldG, 16 * ct, 32 * kb + 8 * g, 32 * kb + 8 * g + 4);
+          const bf16x8 ah = frag_tr(GK, ldG, 16 * ct, 32 * kb + 8 * g, 32 * kb + 8 * g + 4, tr);
+          const bf16x8 al = frag_tr(GK + loG, ldG, 16 * ct, 32 * kb + 8 * g, 32 * kb + 8 * g + 4, tr);
           acc = mma_ab(ah, al, tbh[kb], tbl[kb], acc);
         }
 #pragma unroll
@@ -572,7 +612,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (kb > (w >> 1)) continue;
-          const bf16x8 b = frag_tr(VS, ldV, vh0 + 16 * c, 32 * kb + 8 * g, 32 * kb + 8 * g + 4);
+          const bf16x8 b = frag_tr(VS, ldV, vh0 + 16 * c, 32 * kb + 8 * g, 32 * kb + 8 * g + 4, tr);
           accU[c] = mfma_bf16(tbh[kb], b, accU[c]);
           accU[c] = mfma_bf16(tbl[kb], b, accU[c]);
         }
@@ -620,11 +660,11 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 aq = frag_ld(QT, ldQ, r, 32 * kb);
+        const bf16x8 aq = frag_ld(QT, ldQ, r, 32 * kb, g);
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          const bf16x8 bh = frag_ld(ST, ldS, vh0 + 16 * c + tr, 32 * kb);
-          const bf16x8 bl = frag_ld(ST + loS, ldS, vh0 + 16 * c + tr, 32 * kb);
+          const bf16x8 bh = frag_ld(ST, ldS, vh0 + 16 * c + tr, 32 * kb, g);
+          const bf16x8 bl = frag_ld(ST + loS, ldS, vh0 + 16 * c + tr, 32 * kb, g);
           accW[c] = mma_ab(wh[kb], wl[kb], bh, bl, accW[c]);
           accO[c] = mfma_bf16(aq, bh, accO[c]);
           accO[c] = mfma_bf16(aq, bl, accO[c]);
@@ -649,8 +689,8 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       if (kb > (w >> 1)) continue;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const bf16x8 bh = frag_ld(PT, ldP, vh0 + 16 * c + tr, 32 * kb);
-        const bf16x8 bl = frag_ld(PT + loP, ldP, vh0 + 16 * c + tr, 32 * kb);
+        const bf16x8 bh = frag_ld(PT, ldP, vh0 + 16 * c + tr, 32 * kb, g);
+        const bf16x8 bl = frag_ld(PT + loP, ldP, vh0 + 16 * c + tr, 32 * kb, g);
         accO[c] = mma_ab(mqh[kb], mql[kb], bh, bl, accO[c]);
       }
     }
@@ -671,8 +711,8 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          bph[kb][c] = frag_ld(PT, ldP, vh0 + 16 * c + tr, 32 * kb);
-          bpl[kb][c] = frag_ld(PT + loP, ldP, vh0 + 16 * c + tr, 32 * kb);
+          bph[kb][c] = frag_ld(PT, ldP, vh0 + 16 * c + tr, 32 * kb, g);
+          bpl[kb][c] = frag_ld(PT + loP, ldP, vh0 + 16 * c + tr, 32 * kb, g);
         }
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt) {
@@ -685,8 +725,8 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           // Ktil^T rows c0r.., token k-slots in the same order as P's positions
-          const bf16x8 ah = frag_tr(KT, ldG, c0r, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g);
-          const bf16x8 al = frag_tr(KT + loG, ldG, c0r, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g);
+          const bf16x8 ah = frag_tr(KT, ldG, c0r, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g, tr);
+          const bf16x8 al = frag_tr(KT + loG, ldG, c0r, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g, tr);
 #pragma unroll
           for (int c = 0; c < NCH; ++c)
             Sacc[rt][c] = mma_ab(ah, al, bph[kb][c], bpl[kb][c], Sacc[rt][c]);
