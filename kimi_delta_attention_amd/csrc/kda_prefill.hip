@@ -321,7 +321,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     // instead of keeping them all live across it (which exhausts the 256
     // registers a wave has at two waves per SIMD).
     int lane_x = lane;
-    // __asm__ volatile("" : "+v"(lane_x));
+    __asm__ volatile("" : "+v"(lane_x));
     const int tr = lane_x & 15;
     const int g = lane_x >> 4;
     const int r = 16 * w + tr;
