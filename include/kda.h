@@ -19,9 +19,9 @@
  *  - All tensor pointers are DEVICE pointers owned by the caller, dense and
  *    row-major in the shapes given, aligned to their element size; state
  *    pointers (initial_state, final_state, state) and, for the bf16 prefill
- *    entry points, q, k, v and alpha 16-byte aligned.  The library never
- *    allocates device memory and keeps no state besides cached device
- *    properties.
+ *    entry points, q, k, v and alpha 16-byte aligned; a prefill workspace
+ *    256-byte aligned.  The library never allocates device memory and keeps
+ *    no state besides cached device properties.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Calls enqueue work asynchronously on it; a kernel fault surfaces at the
  *    caller's next synchronisation.
@@ -39,7 +39,26 @@
  *    3.4); finite beta; monotone cu_seqlens; o does not alias any input.
  *  - Results are deterministic (no floating-point atomics): the same call on
  *    the same inputs gives bitwise-identical results, and a sequence of a
- *    packed batch gives bitwise the result it gives when run alone.
+ *    packed batch gives bitwise the result it gives when run alone.  Both
+ *    prefill schedules (below) compute the same products in the same order and
+ *    give bitwise-identical results.
+ *
+ * Prefill schedules (bf16 inputs)
+ * -------------------------------
+ * The chunk form splits every 64-token chunk into work that does not depend on
+ * the entry state (decays, A and its UT inverse, W, U, the intra-chunk q.k
+ * matrix) and a short state-dependent remainder ("Kimi Delta Attention 完全拆解",
+ * section "chunk 内并行、chunk 间递推").  Fused: one kernel, one workgroup per
+ * (sequence, head, 64-wide value slice) walks its chunks and does both.
+ * Two-pass: a first kernel does the state-independent work once per
+ * (chunk, head) over the whole device and leaves per-chunk operands in the
+ * caller's workspace; a second kernel runs the recurrence over chunks.  The
+ * two-pass schedule runs when the call passes a workspace of at least
+ * kda_prefill_workspace_size / kda_prefill_varlen_workspace_size bytes (a
+ * non-zero value); otherwise the fused kernel runs.  The workspace grows with
+ * the number of chunks (about 128.5 KiB per (chunk, head) at Dk = Dv = 128);
+ * its contents on return are unspecified.  kda_prefill_two_pass_preferred
+ * says which schedule is expected to be faster on the current device.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -79,8 +98,10 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *                 (updated in place)
  *   o             [B, T, H, Dv]  o_dtype
  *   chunk         must be 64
- *   workspace     unused by this version (kda_prefill_workspace_size returns 0);
- *                 may be NULL
+ *   workspace     NULL (fused schedule) or device scratch of workspace_bytes
+ *                 bytes, 256-byte aligned, not aliasing any tensor; with at
+ *                 least kda_prefill_workspace_size(B, T, H, Dk, Dv, chunk)
+ *                 bytes (bf16 inputs) the two-pass schedule runs
  * T == 0 or B == 0 is allowed (then only final_state = initial_state is written).
  */
 kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
@@ -104,6 +125,8 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_
  *                 cu_seqlens[N] = total_tokens, non-decreasing (read on the
  *                 device; not checked)
  *   initial_state [N, H, Dk, Dv] or NULL;  final_state [N, H, Dk, Dv] or NULL
+ *   workspace     as for kda_prefill_chunked, sized by
+ *                 kda_prefill_varlen_workspace_size(N, total_tokens, ...)
  * Other arguments as for kda_prefill_chunked.
  */
 kda_status kda_prefill_varlen(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
@@ -132,12 +155,34 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
                            void* stream);
 
 /*
- * kda_prefill_workspace_size -- device scratch bytes the prefill entry points
- * need for these sizes.  Independent of T by design (the state is fixed-size,
- * "Kimi K3 混合线性注意力": the per-session state does not grow with length).
- * Returns 0 in this version.  Returns (size_t)-1 for invalid sizes.
+ * kda_prefill_workspace_size -- workspace bytes that enable the two-pass
+ * schedule of kda_prefill_chunked for these sizes: B * ceil(T / 64) * H
+ * per-chunk operand blocks.  0 when the schedule does not exist for the shape
+ * (head dims outside {64, 128}, or more than 2^31 - 1 blocks).  (size_t)-1 for
+ * invalid sizes.  Only bf16 inputs use it.
  */
 size_t kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv, int chunk);
+
+/*
+ * kda_prefill_varlen_workspace_size -- as above for kda_prefill_varlen with N
+ * packed sequences of total_tokens tokens in all: a chunk table of N + 1
+ * int32 plus (ceil(total_tokens / 64) + N) * H operand blocks, enough for any
+ * split of the tokens into N sequences.
+ */
+size_t kda_prefill_varlen_workspace_size(int N, int total_tokens, int H, int Dk, int Dv,
+                                         int chunk);
+
+/*
+ * kda_prefill_two_pass_preferred -- 1 if the two-pass schedule is expected to
+ * be faster than the fused kernel on the current device for n_seq sequences of
+ * total_tokens tokens in all, else 0.  The fused kernel fills the device with
+ * n_seq * H * Dv / 64 workgroups and repeats the state-independent work for
+ * each 64-wide value slice; the two-pass schedule wins when that grid is below
+ * about twice the compute-unit count and the sequences are at least 4 chunks
+ * long on average.
+ */
+int kda_prefill_two_pass_preferred(kda_dtype qkv_dtype, int n_seq, int total_tokens, int H, int Dk,
+                                   int Dv);
 
 /* Static string naming a status code. */
 const char* kda_status_string(kda_status s);

@@ -19,7 +19,10 @@ KDA_F32, KDA_BF16 = 0, 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_HIP"}
 
 EXPORTED = ("kda_prefill_chunked", "kda_prefill_varlen", "kda_decode_step",
-            "kda_prefill_workspace_size", "kda_status_string", "kda_last_error_message")
+            "kda_prefill_workspace_size", "kda_prefill_varlen_workspace_size",
+            "kda_prefill_two_pass_preferred", "kda_status_string", "kda_last_error_message")
+
+SCHEDULES = ("auto", "fused", "two_pass")
 
 
 class KdaError(RuntimeError):
@@ -49,6 +52,10 @@ def load() -> ctypes.CDLL:
     lib.kda_decode_step.restype = I
     lib.kda_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.kda_prefill_workspace_size.restype = Z
+    lib.kda_prefill_varlen_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.kda_prefill_varlen_workspace_size.restype = Z
+    lib.kda_prefill_two_pass_preferred.argtypes = [I, I, I, I, I, I]
+    lib.kda_prefill_two_pass_preferred.restype = I
     lib.kda_status_string.argtypes = [I]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error_message.argtypes = []
@@ -94,10 +101,44 @@ def workspace_size(B: int, T: int, H: int, Dk: int, Dv: int, chunk: int = 64) ->
     return int(load().kda_prefill_workspace_size(B, T, H, Dk, Dv, chunk))
 
 
+def varlen_workspace_size(N: int, total_tokens: int, H: int, Dk: int, Dv: int,
+                          chunk: int = 64) -> int:
+    return int(load().kda_prefill_varlen_workspace_size(N, total_tokens, H, Dk, Dv, chunk))
+
+
+def _workspace(schedule, workspace, dtype, n_seq, tokens, size, dev):
+    """The workspace argument for the requested schedule: None (fused) or a
+    uint8 device tensor of at least `size` bytes (two-pass).  'auto' asks the
+    library which schedule it expects to be faster."""
+    if schedule not in SCHEDULES:
+        raise ValueError(f"schedule must be one of {SCHEDULES}")
+    if schedule == "fused":
+        return None
+    H, Dk, Dv = size[2], size[3], size[4]
+    if schedule == "auto" and not load().kda_prefill_two_pass_preferred(
+            _DT[dtype], n_seq, tokens, H, Dk, Dv):
+        return None
+    need = size[0]
+    if need == 0:  # nothing to split (no tokens) or no two-pass kernel for the shape
+        return None
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
+        return workspace
+    return torch.empty(need, dtype=torch.uint8, device=dev)
+
+
+_DT = {torch.bfloat16: KDA_BF16, torch.float32: KDA_F32}
+
+
 def prefill_chunked(q, k, v, alpha, beta, initial_state=None, out_dtype=torch.float32,
-                    final_state: bool | torch.Tensor = True, o: torch.Tensor | None = None):
+                    final_state: bool | torch.Tensor = True, o: torch.Tensor | None = None,
+                    schedule: str = "auto", workspace: torch.Tensor | None = None):
     """Dense chunked prefill.  q, k, alpha [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H];
-    initial_state [B,H,Dk,Dv] fp32 or None.  Returns (o, final_state)."""
+    initial_state [B,H,Dk,Dv] fp32 or None.  schedule: 'auto', 'fused' or
+    'two_pass' (the latter with `workspace`, a uint8 device buffer, or one
+    allocated here).  Returns (o, final_state)."""
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     dev = q.device
@@ -123,17 +164,22 @@ def prefill_chunked(q, k, v, alpha, beta, initial_state=None, out_dtype=torch.fl
         fs = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev)
     else:
         fs = None
+    ws = _workspace(schedule, workspace, q.dtype, B, B * T,
+                    (workspace_size(B, T, H, Dk, Dv), B, H, Dk, Dv), dev)
     _check(load().kda_prefill_chunked(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(alpha), _ptr(beta), _ptr(initial_state),
-        _ptr(fs), _ptr(o), _dt(o), B, T, H, Dk, Dv, 64, None, 0, _stream(dev)))
+        _ptr(fs), _ptr(o), _dt(o), B, T, H, Dk, Dv, 64, _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(dev)))
     return o, fs
 
 
 def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None,
                    out_dtype=torch.float32, final_state: bool | torch.Tensor = True,
-                   o: torch.Tensor | None = None):
+                   o: torch.Tensor | None = None, schedule: str = "auto",
+                   workspace: torch.Tensor | None = None):
     """Packed prefill.  q, k, alpha [1,NTOK,H,Dk]; v [1,NTOK,H,Dv]; beta [1,NTOK,H];
-    cu_seqlens int32 [N+1] on the device; states [N,H,Dk,Dv].  Returns (o, final_state)."""
+    cu_seqlens int32 [N+1] on the device; states [N,H,Dk,Dv].  schedule and
+    workspace as for prefill_chunked.  Returns (o, final_state)."""
     _, NT, H, Dk = q.shape
     Dv = v.shape[-1]
     dev = q.device
@@ -157,9 +203,12 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None,
         fs = torch.empty(N, H, Dk, Dv, dtype=torch.float32, device=dev)
     else:
         fs = None
+    ws = _workspace(schedule, workspace, q.dtype, N, NT,
+                    (varlen_workspace_size(N, NT, H, Dk, Dv), N, H, Dk, Dv), dev)
     _check(load().kda_prefill_varlen(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), N, NT,
-        _ptr(initial_state), _ptr(fs), _ptr(o), _dt(o), H, Dk, Dv, 64, None, 0, _stream(dev)))
+        _ptr(initial_state), _ptr(fs), _ptr(o), _dt(o), H, Dk, Dv, 64, _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(dev)))
     return o, fs
 
 

@@ -70,7 +70,19 @@ const char* kda_last_error_message(void) { return g_msg; }
 
 size_t kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv, int chunk) {
   if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || chunk != 64) return (size_t)-1;
-  return 0;
+  return kda::prefill_two_pass_bytes(false, B, T, H, Dk, Dv);
+}
+
+size_t kda_prefill_varlen_workspace_size(int N, int total_tokens, int H, int Dk, int Dv,
+                                         int chunk) {
+  if (N < 0 || total_tokens < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || chunk != 64) return (size_t)-1;
+  return kda::prefill_two_pass_bytes(true, N, total_tokens, H, Dk, Dv);
+}
+
+int kda_prefill_two_pass_preferred(kda_dtype qkv_dtype, int n_seq, int total_tokens, int H, int Dk,
+                                   int Dv) {
+  if (qkv_dtype != KDA_BF16) return 0;
+  return kda::prefill_two_pass_preferred(n_seq, total_tokens, H, Dk, Dv) ? 1 : 0;
 }
 
 static kda_status prefill_common(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
@@ -78,7 +90,7 @@ static kda_status prefill_common(const void* q, const void* k, const void* v, kd
                                  const int32_t* cu_seqlens, int n_seq, int T,
                                  const float* initial_state, float* final_state, void* o,
                                  kda_dtype o_dtype, int H, int Dk, int Dv, int chunk,
-                                 void* stream) {
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   if (n_seq < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative batch or length");
   if (n_seq == 0) return ok();
   if (T > 0 || cu_seqlens) {
@@ -104,11 +116,14 @@ static kda_status prefill_common(const void* q, const void* k, const void* v, kd
   if ((long long)n_seq * H * (Dv / 64) > 0x7fffffffLL)
     return fail(KDA_ERR_INVALID_ARGUMENT, "too many (sequence, head) work items");
   if (T == 0 && !cu_seqlens && !final_state) return ok();
+  if (workspace && ((uintptr_t)workspace & 255u))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   kda::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
   a.initial_state = initial_state; a.final_state = final_state; a.o = o;
   a.qkv_bf16 = qkv_dtype == KDA_BF16; a.o_bf16 = o_dtype == KDA_BF16;
   a.cu_seqlens = cu_seqlens; a.n_seq = n_seq; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv;
+  a.workspace = workspace; a.workspace_bytes = workspace ? workspace_bytes : 0;
   a.stream = stream;
   return hip_status(kda::launch_prefill(a));
 }
@@ -118,11 +133,10 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_
                                const float* initial_state, float* final_state, void* o,
                                kda_dtype o_dtype, int B, int T, int H, int Dk, int Dv, int chunk,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (B < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B and T must be >= 0");
   return prefill_common(q, k, v, qkv_dtype, alpha, beta, nullptr, B, T, initial_state,
-                        final_state, o, o_dtype, H, Dk, Dv, chunk, stream);
+                        final_state, o, o_dtype, H, Dk, Dv, chunk, workspace, workspace_bytes,
+                        stream);
 }
 
 kda_status kda_prefill_varlen(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
@@ -131,15 +145,14 @@ kda_status kda_prefill_varlen(const void* q, const void* k, const void* v, kda_d
                               float* final_state, void* o, kda_dtype o_dtype, int H, int Dk,
                               int Dv, int chunk, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (N < 0 || total_tokens < 0)
     return fail(KDA_ERR_INVALID_ARGUMENT, "N and total_tokens must be >= 0");
   if (N > 0 && !cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens must be non-null");
   if (N > 0 && ((uintptr_t)cu_seqlens & 3u))
     return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
   return prefill_common(q, k, v, qkv_dtype, alpha, beta, cu_seqlens, N, total_tokens,
-                        initial_state, final_state, o, o_dtype, H, Dk, Dv, chunk, stream);
+                        initial_state, final_state, o, o_dtype, H, Dk, Dv, chunk, workspace,
+                        workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,

@@ -1,0 +1,166 @@
+// kda_frag.h -- register-fragment helpers of the gfx950 bf16 chunk kernels
+// (prefill pass 1 / fused prefill in kda_prefill.hip, the state pass in
+// kda_prefill_state.hip) and the layout of the per-chunk operand images that
+// pass 1 writes and the state pass reads.
+#pragma once
+#include "kda_common.h"
+
+namespace kda {
+namespace frag {
+
+constexpr int CH = 64;    // chunk
+constexpr int BV = 64;    // value slice per workgroup
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
+typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
+
+// Operand fragment (16 columns m0.., 8 k values per lane) of a row-major
+// [k][m] LDS tile: lane l (j = l%16) gets column m0 + j at rows ra..ra+3 and
+// rb..rb+3 (ra, rb chosen per 16-lane group).  Two transpose reads, each of which
+// gives lane i of a 16-lane group element i%4 of the 8-byte words read by
+// lanes i/4, i/4+4, i/4+8, i/4+12 of that group.
+__device__ __forceinline__ bf16x8 frag_tr(const bf16* X, int ld, int m0, int ra, int rb, int j) {
+  const bf16* pa = X + (ra + (j >> 2)) * ld + m0 + 4 * (j & 3);
+  const bf16* pb = X + (rb + (j >> 2)) * ld + m0 + 4 * (j & 3);
+  const short4v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)pa);
+  const short4v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)pb);
+  const short8v s = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, s);
+}
+
+// 16 contiguous bytes of a k-contiguous LDS row (g = lane / 16).
+__device__ __forceinline__ bf16x8 frag_ld(const bf16* X, int ld, int row, int k0, int g) {
+  return *reinterpret_cast<const bf16x8*>(X + row * ld + k0 + 8 * g);
+}
+
+// Inclusive product scan over the 16 lanes of each DPP row, for N values per
+// lane: lane i of a row ends with x_0 * ... * x_i.  Each step is one
+// v_mul_f32_dpp with row_shr:D and bound_ctrl off, which leaves lanes i < D
+// unwritten (they keep x_i).  A step reads values written N instructions
+// earlier, so only the first needs the 2 wait states of a VALU write -> DPP
+// read.
+template <int N>
+__device__ __forceinline__ void row_scan_mul(float* x) {
+  static_assert(N == 8 || N == 16, "scan width");
+#define KDA_SCAN_STEP(D, i) "v_mul_f32_dpp %" #i ", %" #i ", %" #i " row_shr:" #D " row_mask:0xf bank_mask:0xf\n"
+#define KDA_SCAN8(D) KDA_SCAN_STEP(D, 0) KDA_SCAN_STEP(D, 1) KDA_SCAN_STEP(D, 2) KDA_SCAN_STEP(D, 3) \
+  KDA_SCAN_STEP(D, 4) KDA_SCAN_STEP(D, 5) KDA_SCAN_STEP(D, 6) KDA_SCAN_STEP(D, 7)
+#define KDA_SCAN16(D) KDA_SCAN8(D) KDA_SCAN_STEP(D, 8) KDA_SCAN_STEP(D, 9) KDA_SCAN_STEP(D, 10) \
+  KDA_SCAN_STEP(D, 11) KDA_SCAN_STEP(D, 12) KDA_SCAN_STEP(D, 13) KDA_SCAN_STEP(D, 14) KDA_SCAN_STEP(D, 15)
+  if constexpr (N == 8) {
+    __asm__("s_nop 1\n" KDA_SCAN8(1) KDA_SCAN8(2) KDA_SCAN8(4) KDA_SCAN8(8)
+            : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+              "+v"(x[7]));
+  } else {
+    __asm__("s_nop 1\n" KDA_SCAN16(1) KDA_SCAN16(2) KDA_SCAN16(4) KDA_SCAN16(8)
+            : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+              "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]),
+              "+v"(x[13]), "+v"(x[14]), "+v"(x[15]));
+  }
+#undef KDA_SCAN16
+#undef KDA_SCAN8
+#undef KDA_SCAN_STEP
+}
+
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bf16 h = (bf16)x[e];
+    hi[e] = h;
+    lo[e] = (bf16)(x[e] - (float)h);
+  }
+}
+
+__device__ __forceinline__ float bfv(unsigned int packed, int half) {
+  return __builtin_bit_cast(float, half ? (packed & 0xffff0000u) : (packed << 16));
+}
+
+__device__ __forceinline__ void st_bf16x4(bf16* p, const float* x) {
+  // 4 values -> one 8-byte LDS store
+  short4v s;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s[e] = __builtin_bit_cast(short, (bf16)x[e]);
+  *reinterpret_cast<short4v*>(p) = s;
+}
+
+__device__ __forceinline__ void st_split4(bf16* hi, int lo_off, const float* x) {
+  short4v sh, sl;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16 h = (bf16)x[e];
+    sh[e] = __builtin_bit_cast(short, h);
+    sl[e] = __builtin_bit_cast(short, (bf16)(x[e] - (float)h));
+  }
+  *reinterpret_cast<short4v*>(hi) = sh;
+  *reinterpret_cast<short4v*>(hi + lo_off) = sl;
+}
+
+// x = hi + lo for 4 values, each part packed two bf16 per 32-bit word.
+__device__ __forceinline__ void split4_pack(const float* x, uint2v& hi, uint2v& lo) {
+  unsigned int h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16 hv = (bf16)x[e];
+    h[e] = __builtin_bit_cast(unsigned short, hv);
+    l[e] = __builtin_bit_cast(unsigned short, (bf16)(x[e] - (float)hv));
+  }
+  hi = uint2v{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  lo = uint2v{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+}
+
+__device__ __forceinline__ floatx4 mma_ab(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
+                                          const bf16x8& bl, floatx4 c) {
+  c = mfma_bf16(ah, bh, c);
+  c = mfma_bf16(ah, bl, c);
+  c = mfma_bf16(al, bh, c);
+  return c;
+}
+
+// Per-chunk operand images written by the first pass of the two-pass prefill
+// and read by the state pass.  Every image is a sequence of 1 KiB frames; a
+// frame is one 16-byte register fragment per lane (lane l at byte 16 l), so a
+// wave moves a frame with one fully coalesced 16-byte load or store per lane.
+// Frames (w = token tile of the chunk, kb = 32-wide k block):
+//   W  [w][kb < DK/32][hi, lo]   A operand of W S (row = token, k = channel
+//                                position 32kb + 8g + 4h + i <-> channel
+//                                32kb + 16h + 4g + i)
+//   Q  [w][kb < DK/32]           A operand of (Gamma*Q) S, same positions
+//   M  [w][kb < 2][hi, lo]       A operand of Mqk P (k = token position)
+//   K  [rt < DK/16][kb < 2][hi, lo]  A operand of Ktil^T P for state rows
+//                                16rt..16rt+15 (k = token position)
+//   U  [w][vt < DV/16]           U tile (tokens 16w.., values 16vt..) in the
+//                                accumulator layout, fp32
+// followed by Gamma_C (DK floats).
+template <int DK, int DV>
+struct Images {
+  static constexpr int NKB = DK / 32, NCHT = DK / 16, NVT = DV / 16;
+  static constexpr int W = 0;
+  static constexpr int Q = W + 4 * NKB * 2;
+  static constexpr int M = Q + 4 * NKB;
+  static constexpr int K = M + 4 * 2 * 2;
+  static constexpr int U = K + NCHT * 2 * 2;
+  static constexpr int frames = U + 4 * NVT;
+  static constexpr size_t g_off = (size_t)frames * 1024;
+  static constexpr size_t bytes = (g_off + DK * 4 + 255) / 256 * 256;
+  static __device__ __forceinline__ int w_frame(int w, int kb, int part) { return W + (w * NKB + kb) * 2 + part; }
+  static __device__ __forceinline__ int q_frame(int w, int kb) { return Q + w * NKB + kb; }
+  static __device__ __forceinline__ int m_frame(int w, int kb, int part) { return M + (w * 2 + kb) * 2 + part; }
+  static __device__ __forceinline__ int k_frame(int rt, int kb, int part) { return K + (rt * 2 + kb) * 2 + part; }
+  static __device__ __forceinline__ int u_frame(int w, int vt) { return U + w * NVT + vt; }
+};
+
+// 16-byte fragment of frame f of an image at `base`, lane `lane`.
+template <typename T>
+__device__ __forceinline__ T* frame_ptr(unsigned char* base, int f, int lane) {
+  return reinterpret_cast<T*>(base + (size_t)f * 1024 + 16 * lane);
+}
+template <typename T>
+__device__ __forceinline__ const T* frame_ptr(const unsigned char* base, int f, int lane) {
+  return reinterpret_cast<const T*>(base + (size_t)f * 1024 + 16 * lane);
+}
+
+}  // namespace frag
+}  // namespace kda

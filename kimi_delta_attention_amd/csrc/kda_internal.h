@@ -27,6 +27,10 @@ struct PrefillArgs {
   // or n_seq packed sequences delimited by the device array cu_seqlens.
   const int32_t* cu_seqlens;
   int n_seq, T, H, Dk, Dv;
+  // Optional device scratch; with at least prefill_two_pass_bytes(...) bytes
+  // the two-pass schedule runs, otherwise the fused kernel.
+  void* workspace;
+  size_t workspace_bytes;
   void* stream;
 };
 
@@ -34,5 +38,18 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);      // dispatch (kda_prefill.hip)
 hipError_t launch_prefill_f32(const PrefillArgs& a);  // fp32 inputs (kda_prefill_f32.hip)
 bool prefill_supported(bool qkv_bf16, int Dk, int Dv);
+
+// Two-pass bf16 prefill.  `tokens` is T per sequence (dense) or the packed
+// total (varlen).  Workspace bytes it needs (0 if unavailable for the shape),
+// and whether it is expected to beat the fused kernel on the current device.
+size_t prefill_two_pass_bytes(bool varlen, int n_seq, long long tokens, int H, int Dk, int Dv);
+bool prefill_two_pass_preferred(int n_seq, long long tokens, int H, int Dk, int Dv);
+// (kda_prefill_state.hip) operand-image bytes per (chunk, head); the state
+// pass; the chunk table of packed sequences (clamped to `cap` chunks).
+size_t prefill_image_bytes(int Dk, int Dv);
+hipError_t launch_prefill_state(const PrefillArgs& a, const unsigned char* img,
+                                const int32_t* chunk_off);
+hipError_t launch_chunk_table(const int32_t* cu_seqlens, int n_seq, int cap, int32_t* chunk_off,
+                              void* stream);
 
 }  // namespace kda

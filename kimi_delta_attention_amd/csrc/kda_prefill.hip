@@ -44,122 +44,15 @@
 // hi*hi + hi*lo + lo*hi) everywhere except A (single pass); U and (Gamma*Q) S
 // split only the side that is not exact in bf16.
 #include "kda_common.h"
+#include "kda_frag.h"
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
 
-constexpr int CH = 64;    // chunk
 constexpr int NTH = 512;  // 8 waves
-constexpr int BV = 64;    // value slice per workgroup
 
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef short short8v __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) short4v lds_short4v;
-typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
-typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
-
-// Operand fragment (16 columns m0.., 8 k values per lane) of a row-major
-// [k][m] LDS tile: lane l (j = l%16) gets column m0 + j at rows ra..ra+3 and
-// rb..rb+3 (ra, rb chosen per 16-lane group).  Two transpose reads, each of which
-// gives lane i of a 16-lane group element i%4 of the 8-byte words read by
-// lanes i/4, i/4+4, i/4+8, i/4+12 of that group.
-__device__ __forceinline__ bf16x8 frag_tr(const bf16* X, int ld, int m0, int ra, int rb, int j) {
-  const bf16* pa = X + (ra + (j >> 2)) * ld + m0 + 4 * (j & 3);
-  const bf16* pb = X + (rb + (j >> 2)) * ld + m0 + 4 * (j & 3);
-  const short4v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)pa);
-  const short4v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)pb);
-  const short8v s = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, s);
-}
-
-// 16 contiguous bytes of a k-contiguous LDS row (g = lane / 16).
-__device__ __forceinline__ bf16x8 frag_ld(const bf16* X, int ld, int row, int k0, int g) {
-  return *reinterpret_cast<const bf16x8*>(X + row * ld + k0 + 8 * g);
-}
-
-// Inclusive product scan over the 16 lanes of each DPP row, for N values per
-// lane: lane i of a row ends with x_0 * ... * x_i.  Each step is one
-// v_mul_f32_dpp with row_shr:D and bound_ctrl off, which leaves lanes i < D
-// unwritten (they keep x_i).  A step reads values written N instructions
-// earlier, so only the first needs the 2 wait states of a VALU write -> DPP
-// read.
-template <int N>
-__device__ __forceinline__ void row_scan_mul(float* x) {
-  static_assert(N == 8 || N == 16, "scan width");
-#define KDA_SCAN_STEP(D, i) "v_mul_f32_dpp %" #i ", %" #i ", %" #i " row_shr:" #D " row_mask:0xf bank_mask:0xf\n"
-#define KDA_SCAN8(D) KDA_SCAN_STEP(D, 0) KDA_SCAN_STEP(D, 1) KDA_SCAN_STEP(D, 2) KDA_SCAN_STEP(D, 3) \
-  KDA_SCAN_STEP(D, 4) KDA_SCAN_STEP(D, 5) KDA_SCAN_STEP(D, 6) KDA_SCAN_STEP(D, 7)
-#define KDA_SCAN16(D) KDA_SCAN8(D) KDA_SCAN_STEP(D, 8) KDA_SCAN_STEP(D, 9) KDA_SCAN_STEP(D, 10) \
-  KDA_SCAN_STEP(D, 11) KDA_SCAN_STEP(D, 12) KDA_SCAN_STEP(D, 13) KDA_SCAN_STEP(D, 14) KDA_SCAN_STEP(D, 15)
-  if constexpr (N == 8) {
-    __asm__("s_nop 1\n" KDA_SCAN8(1) KDA_SCAN8(2) KDA_SCAN8(4) KDA_SCAN8(8)
-            : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
-              "+v"(x[7]));
-  } else {
-    __asm__("s_nop 1\n" KDA_SCAN16(1) KDA_SCAN16(2) KDA_SCAN16(4) KDA_SCAN16(8)
-            : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
-              "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]),
-              "+v"(x[13]), "+v"(x[14]), "+v"(x[15]));
-  }
-#undef KDA_SCAN16
-#undef KDA_SCAN8
-#undef KDA_SCAN_STEP
-}
-
-__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const bf16 h = (bf16)x[e];
-    hi[e] = h;
-    lo[e] = (bf16)(x[e] - (float)h);
-  }
-}
-
-__device__ __forceinline__ float bfv(unsigned int packed, int half) {
-  return __builtin_bit_cast(float, half ? (packed & 0xffff0000u) : (packed << 16));
-}
-
-__device__ __forceinline__ void st_bf16x4(bf16* p, const float* x) {
-  // 4 values -> one 8-byte LDS store
-  short4v s;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) s[e] = __builtin_bit_cast(short, (bf16)x[e]);
-  *reinterpret_cast<short4v*>(p) = s;
-}
-
-__device__ __forceinline__ void st_split4(bf16* hi, int lo_off, const float* x) {
-  short4v sh, sl;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const bf16 h = (bf16)x[e];
-    sh[e] = __builtin_bit_cast(short, h);
-    sl[e] = __builtin_bit_cast(short, (bf16)(x[e] - (float)h));
-  }
-  *reinterpret_cast<short4v*>(hi) = sh;
-  *reinterpret_cast<short4v*>(hi + lo_off) = sl;
-}
-
-// x = hi + lo for 4 values, each part packed two bf16 per 32-bit word.
-__device__ __forceinline__ void split4_pack(const float* x, uint2v& hi, uint2v& lo) {
-  unsigned int h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const bf16 hv = (bf16)x[e];
-    h[e] = __builtin_bit_cast(unsigned short, hv);
-    l[e] = __builtin_bit_cast(unsigned short, (bf16)(x[e] - (float)hv));
-  }
-  hi = uint2v{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-  lo = uint2v{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
-}
-
-__device__ __forceinline__ floatx4 mma_ab(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
-                                          const bf16x8& bl, floatx4 c) {
-  c = mfma_bf16(ah, bh, c);
-  c = mfma_bf16(ah, bl, c);
-  c = mfma_bf16(al, bh, c);
-  return c;
-}
+using namespace frag;
 
 // LDS plan (bytes).  R0 is reused phase by phase:
 //   A / Mqk:      RT (right operands of every row tile, position order)
@@ -168,11 +61,13 @@ __device__ __forceinline__ floatx4 mma_ab(const bf16x8& ah, const bf16x8& al, co
 //   T*b, V:       TB (T Diag(b), split) and VS (V slice) over MQ0 / MQ1
 //   serial:       ST (state, split), PT (P, split), KT (Ktil, split)
 // GK ((Gamma*K), split, [token][channel]) and QT ((Gamma*Q), [token][position])
-// live from operand build to their last product; ES / GC / BS are small.
-template <int DK>
+// live from operand build to their last product; ES / GC / BS are small.  VW is
+// the width of the staged V block (the 64-wide slice, or all of Dv when the
+// kernel runs as the first pass of the two-pass schedule).
+template <int DK, int VW>
 struct Plan {
   static constexpr int ldR = DK + 8, ldG = DK + 8, ldQ = DK + 8, ldA = CH + 4, ldT = CH + 8,
-                       ldV = BV + 8, ldS = DK + 8, ldP = CH + 8;
+                       ldV = VW + 8, ldS = DK + 8, ldP = CH + 8;
   static constexpr int RT = 160 * ldR * 2 * 2;
   static constexpr int AF = CH * ldA * 4, TB = CH * ldT * 2 * 2, VS = CH * ldV * 2;
   static constexpr int ST = BV * ldS * 2 * 2, PT = BV * ldP * 2 * 2, KT = CH * ldG * 2 * 2;
@@ -193,19 +88,31 @@ struct Plan {
                 "alignment");
 };
 
-template <int DK, typename TOut>
+// PREP_DV == 0: the fused kernel (one workgroup per (sequence, head, value
+// slice), state carried across chunks).  PREP_DV == Dv: the first pass of the
+// two-pass schedule; a persistent grid walks (chunk, head) items, computes
+// everything that does not depend on the state and writes it as operand images
+// (Images<DK, Dv>) for the state pass.
+template <int DK, typename TOut, int PREP_DV>
 __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* __restrict__ s_init, float* __restrict__ s_final, TOut* __restrict__ o,
-    const int32_t* __restrict__ cu_seqlens, int n_seq, int T, int H, int DV) {
-  using L = Plan<DK>;
+    const int32_t* __restrict__ cu_seqlens, int n_seq, int T, int H, int DV_,
+    unsigned char* __restrict__ img, const int32_t* __restrict__ chunk_off, int n_items) {
+  constexpr bool PREP = PREP_DV != 0;
+  using L = Plan<DK, PREP ? PREP_DV : BV>;
+  using IM = Images<DK, PREP ? PREP_DV : 64>;
+  const int DV = PREP ? PREP_DV : DV_;
   constexpr int NKB = DK / 32;   // 32-channel blocks
   constexpr int NKH = NKB / 2;   // blocks of one channel half
   constexpr int NCHT = DK / 16;  // 16-channel tiles
   constexpr int RPW = DK / 4;    // state rows per token-tile wave pair
   constexpr int RTW = RPW / 16;  // state row tiles per wave
   constexpr int NCH = BV / 32;   // value tiles per wave (its 32-column half)
+  constexpr int NVL = PREP ? (PREP_DV / 64 > 0 ? PREP_DV / 64 : 1) : 1;  // 16-byte v loads per lane
+  constexpr int NCTW = PREP ? NCHT / 2 : NCHT;  // W^T channel tiles per wave
+  constexpr int NUT = PREP ? PREP_DV / 32 : NCH;  // U tiles per wave
   constexpr int ldR = L::ldR, ldG = L::ldG, ldQ = L::ldQ, ldA = L::ldA, ldT = L::ldT,
                 ldV = L::ldV, ldS = L::ldS, ldP = L::ldP;
   constexpr int loR = 160 * ldR, loG = CH * ldG, loT = CH * ldT, loS = BV * ldS, loP = BV * ldP;
@@ -242,26 +149,29 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
   const int g = lane >> 4;
 
   const int nsl = DV / BV;
-  const int total = n_seq * H * nsl;
-  int wid = blockIdx.x;
-  if ((total & 7) == 0) wid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int sl = wid % nsl;
-  const int h = (wid / nsl) % H;
-  const int seq = wid / (nsl * H);
-  long long start, len;
-  if (cu_seqlens) {
-    start = cu_seqlens[seq];
-    len = (long long)cu_seqlens[seq + 1] - start;
-  } else {
-    start = (long long)seq * T;
-    len = T;
+  int sl = 0, h = 0, seq = 0;
+  long long start = 0, len = 0;
+  if constexpr (!PREP) {
+    const int total = n_seq * H * nsl;
+    int wid = blockIdx.x;
+    if ((total & 7) == 0) wid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+    sl = wid % nsl;
+    h = (wid / nsl) % H;
+    seq = wid / (nsl * H);
+    if (cu_seqlens) {
+      start = cu_seqlens[seq];
+      len = (long long)cu_seqlens[seq + 1] - start;
+    } else {
+      start = (long long)seq * T;
+      len = T;
+    }
   }
   const int vcol0 = sl * BV;
   const int vh0 = 32 * hh;  // this wave's value columns within the slice
 
   // state: wave (w, hh) owns key rows [w*RPW, (w+1)*RPW) x value columns vh0..vh0+31
   floatx4 Sacc[RTW][NCH];
-  {
+  if constexpr (!PREP) {
     const float* si = s_init ? s_init + ((size_t)seq * H + h) * DK * DV : nullptr;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
@@ -274,6 +184,43 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
         }
   }
 
+  // One chunk of one head: first token (global index), valid tokens, head,
+  // and (first pass) the item index.
+  struct Desc {
+    long long tok0;
+    int nv, hd, item;
+    long long c0;
+  };
+  if constexpr (PREP) {
+    if (n_items < 0) n_items = chunk_off[n_seq] * H;  // packed sequences: count on the device
+  }
+  auto item_desc = [&](int it, Desc& d) {
+    const int ci = it / H;
+    d.hd = it - ci * H;
+    d.item = it;
+    long long st, ln, cc;
+    if (chunk_off) {
+      int lo = 0, hi = n_seq - 1;  // last sequence whose first chunk is <= ci
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (chunk_off[mid] <= ci) lo = mid;
+        else hi = mid - 1;
+      }
+      st = cu_seqlens[lo];
+      ln = (long long)cu_seqlens[lo + 1] - st;
+      cc = (long long)(ci - chunk_off[lo]) * CH;
+    } else {
+      const int nch = (T + CH - 1) / CH;
+      const int sq = ci / nch;
+      st = (long long)sq * T;
+      ln = T;
+      cc = (long long)(ci - sq * nch) * CH;
+    }
+    d.tok0 = st + cc;
+    d.nv = (int)(ln - cc < CH ? ln - cc : CH);
+    d.c0 = cc;
+  };
+
   const int r = 16 * w + tr;  // this lane's token within the chunk
 
   // Global loads of one chunk for this lane's token and channel half (k, q,
@@ -285,16 +232,19 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
   struct ChunkIn {
     uint2v k[NKH][2], q[NKH][2];
     floatx4 a[NKH][2];
-    uint4v v;
+    uint4v v[NVL];
     float b;
   };
-  auto load_part = [&](long long cc, ChunkIn& in, int part) {
-    const int nvc = (int)(len - cc < CH ? len - cc : CH);
-    const bool okc = r < nvc;
-    const size_t thc = (size_t)(start + cc + r) * H + h;
+  // V columns this lane stages: 8 of the slice, or (first pass) Dv/8 of all Dv
+  const int vld0 = PREP ? (DV / 2) * hh + (DV / 8) * g : vcol0 + vh0 + 8 * g;
+  auto load_part = [&](const Desc& d, ChunkIn& in, int part) {
+    const bool okc = r < d.nv;
+    const size_t thc = (size_t)(d.tok0 + r) * H + d.hd;
     if (part == 3) {
-      in.v = okc ? *reinterpret_cast<const uint4v*>(v + thc * DV + vcol0 + vh0 + 8 * g)
-                 : uint4v{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < NVL; ++j)
+        in.v[j] = okc ? *reinterpret_cast<const uint4v*>(v + thc * DV + vld0 + 8 * j)
+                      : uint4v{0u, 0u, 0u, 0u};
       in.b = okc ? beta[thc] : 0.f;
       return;
     }
@@ -311,11 +261,32 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
                                           : floatx4{1.f, 1.f, 1.f, 1.f};
       }
   };
+  Desc cur;
+  bool have;
+  if constexpr (PREP) {
+    have = (int)blockIdx.x < n_items;
+    cur = Desc{0, 0, 0, 0, 0};
+    if (have) item_desc(blockIdx.x, cur);
+  } else {
+    have = len > 0;
+    cur = Desc{start, (int)(len < CH ? len : CH), h, 0, 0};
+  }
   ChunkIn in;
-  if (len > 0)
-    for (int part = 0; part < 4; ++part) load_part(0, in, part);
+  if (have)
+    for (int part = 0; part < 4; ++part) load_part(cur, in, part);
 
-  for (long long c0 = 0; c0 < len; c0 += CH) {
+  while (have) {
+    Desc nxt = cur;
+    bool more;
+    if constexpr (PREP) {
+      const int ni = cur.item + (int)gridDim.x;
+      more = ni < n_items;
+      if (more) item_desc(ni, nxt);
+    } else {
+      const long long c1 = cur.c0 + CH;
+      more = c1 < len;
+      nxt = Desc{start + c1, (int)(len - c1 < CH ? len - c1 : CH), h, 0, c1};
+    }
     // Lane indices, re-derived each chunk behind an empty asm so that the
     // compiler recomputes the many per-lane LDS addresses inside the loop
     // instead of keeping them all live across it (which exhausts the 256
@@ -326,11 +297,11 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     const int g = lane_x >> 4;
     const int r = 16 * w + tr;
     const int tid = 64 * w8 + lane_x;
-    const int nv = (int)(len - c0 < CH ? len - c0 : CH);
-    const long long tok0 = start + c0;
+    const int nv = cur.nv;
+    const long long tok0 = cur.tok0;
+    unsigned char* im = PREP ? img + (size_t)cur.item * IM::bytes : nullptr;
     __syncthreads();  // the previous chunk is done with LDS
 
-    const bool more = c0 + CH < len;
     const float bt = in.b;
 
     // ---- within-tile decay products P (inclusive scan over the 16 tokens)
@@ -340,7 +311,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) Pv[kk][e] = in.a[kk][e >> 2][e & 3];
     row_scan_mul<8 * NKH>(&Pv[0][0]);
-    if (more) load_part(c0 + CH, in, 2);
+    if (more) load_part(nxt, in, 2);
     if (tr == 15) {  // whole-tile decay E_w of this wave's channels
 #pragma unroll
       for (int kk = 0; kk < NKH; ++kk)
@@ -438,8 +409,11 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     }
     __syncthreads();
     if (more) {
-      load_part(c0 + CH, in, 0);
-      load_part(c0 + CH, in, 1);
+      load_part(nxt, in, 0);
+      load_part(nxt, in, 1);
+    }
+    if constexpr (PREP) {
+      if (tid < DK) reinterpret_cast<float*>(im + IM::g_off)[tid] = GC[tid];
     }
 
     // ---- A^T and Mqk^T tiles (j in tile n, r in tile w), n = 0..w, over this
@@ -458,6 +432,13 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
         const bf16x8 al = frag_ld(RT + loR, ldR, row, 32 * kb, g);
         accA[n] = mfma_bf16(ah, kl[kk], accA[n]);
         accM[n] = mma_ab(ah, al, qlh[kk], qll[kk], accM[n]);
+      }
+    }
+    if constexpr (PREP) {  // (Gamma*Q) operand of this tile, this wave's channel half
+#pragma unroll
+      for (int kk = 0; kk < NKH; ++kk) {
+        const int kb = NKH * hh + kk;
+        *frame_ptr<bf16x8>(im, IM::q_frame(w, kb), lane_x) = frag_ld(QT, ldQ, r, 32 * kb, g);
       }
     }
     __syncthreads();  // RT reads done; the partials overwrite it
@@ -492,6 +473,15 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
         const bf16 hv = (bf16)m4[i];
         mqh[n >> 1][4 * (n & 1) + i] = hv;
         mql[n >> 1][4 * (n & 1) + i] = (bf16)(m4[i] - (float)hv);
+      }
+    }
+    if constexpr (PREP) {
+      if (hh == 0) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          *frame_ptr<bf16x8>(im, IM::m_frame(w, kb, 0), lane_x) = mqh[kb];
+          *frame_ptr<bf16x8>(im, IM::m_frame(w, kb, 1), lane_x) = mql[kb];
+        }
       }
     }
     __syncthreads();  // MQ0 / MQ1 reads done; the solve's scratch reuses them
@@ -573,15 +563,19 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       for (int e = 0; e < 4; ++e) x4[e] = (j0 + e <= rr) ? t4[e] * b4[e] : 0.f;
       st_split4(TB + rr * ldT + j0, loT, x4);
     }
-    *reinterpret_cast<uint4v*>(VS + r * ldV + vh0 + 8 * g) = in.v;
-    if (more) load_part(c0 + CH, in, 3);
+#pragma unroll
+    for (int j = 0; j < NVL; ++j)
+      *reinterpret_cast<uint4v*>(VS + r * ldV + (PREP ? vld0 : vh0 + 8 * g) + 8 * j) = in.v[j];
+    if (more) load_part(nxt, in, 3);
     __syncthreads();
 
-    // ---- W^T = (Gamma*K)^T (T Diag b)^T for this tile's tokens (all channels,
-    // computed by both waves of the pair), kept as the split operand of W S;
-    // U = T Diag(b) V for this wave's 32 value columns
-    bf16x8 wh[NKB], wl[NKB];
-    floatx4 accU[NCH];
+    // ---- W^T = (Gamma*K)^T (T Diag b)^T for this tile's tokens, kept as the
+    // split operand of W S: all channels, computed by both waves of the pair
+    // (fused) or one channel half per wave (first pass).  U = T Diag(b) V for
+    // this wave's 32 value columns (fused) or half of all Dv (first pass).
+    const int ct0 = PREP ? NCTW * hh : 0;
+    bf16x8 wh[NCTW / 2], wl[NCTW / 2];
+    floatx4 accU[NUT];
     {
       bf16x8 tbh[2], tbl[2];
 #pragma unroll
@@ -590,7 +584,8 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
         tbl[kb] = frag_ld(TB + loT, ldT, r, 32 * kb, g);
       }
 #pragma unroll
-      for (int ct = 0; ct < NCHT; ++ct) {
+      for (int ctl = 0; ctl < NCTW; ++ctl) {
+        const int ct = ct0 + ctl;
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -602,23 +597,63 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bf16 hv = (bf16)acc[i];
-          wh[ct >> 1][4 * (ct & 1) + i] = hv;
-          wl[ct >> 1][4 * (ct & 1) + i] = (bf16)(acc[i] - (float)hv);
+          wh[ctl >> 1][4 * (ctl & 1) + i] = hv;
+          wl[ctl >> 1][4 * (ctl & 1) + i] = (bf16)(acc[i] - (float)hv);
         }
       }
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
+      for (int c = 0; c < NUT; ++c) {
+        const int vc = PREP ? 16 * (NUT * hh + c) : vh0 + 16 * c;
         accU[c] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (kb > (w >> 1)) continue;
-          const bf16x8 b = frag_tr(VS, ldV, vh0 + 16 * c, 32 * kb + 8 * g, 32 * kb + 8 * g + 4, tr);
+          const bf16x8 b = frag_tr(VS, ldV, vc, 32 * kb + 8 * g, 32 * kb + 8 * g + 4, tr);
           accU[c] = mfma_bf16(tbh[kb], b, accU[c]);
           accU[c] = mfma_bf16(tbl[kb], b, accU[c]);
         }
       }
     }
     __syncthreads();  // TB / VS / GK reads done; ST, PT and KT overwrite the region
+
+    if constexpr (PREP) {
+      // W and U images of this tile; Ktil through LDS into the A operands of
+      // Ktil^T P, one 16-row state tile per wave
+#pragma unroll
+      for (int kbl = 0; kbl < NCTW / 2; ++kbl) {
+        *frame_ptr<bf16x8>(im, IM::w_frame(w, NKH * hh + kbl, 0), lane_x) = wh[kbl];
+        *frame_ptr<bf16x8>(im, IM::w_frame(w, NKH * hh + kbl, 1), lane_x) = wl[kbl];
+      }
+#pragma unroll
+      for (int c = 0; c < NUT; ++c)
+        *frame_ptr<floatx4>(im, IM::u_frame(w, NUT * hh + c), lane_x) = accU[c];
+#pragma unroll
+      for (int kk = 0; kk < NKH; ++kk) {
+        const int kb = NKH * hh + kk;
+        const uint4v uh = __builtin_bit_cast(uint4v, kth[kk]);
+        const uint4v ul = __builtin_bit_cast(uint4v, ktl[kk]);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          *reinterpret_cast<uint2v*>(KT + r * ldG + 32 * kb + 16 * hf + 4 * g) =
+              uint2v{uh[2 * hf], uh[2 * hf + 1]};
+          *reinterpret_cast<uint2v*>(KT + r * ldG + 32 * kb + 16 * hf + 4 * g + loG) =
+              uint2v{ul[2 * hf], ul[2 * hf + 1]};
+        }
+      }
+      __syncthreads();
+      if (w8 < NCHT) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          *frame_ptr<bf16x8>(im, IM::k_frame(w8, kb, 0), lane_x) =
+              frag_tr(KT, ldG, 16 * w8, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g, tr);
+          *frame_ptr<bf16x8>(im, IM::k_frame(w8, kb, 1), lane_x) =
+              frag_tr(KT + loG, ldG, 16 * w8, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g, tr);
+        }
+      }
+      cur = nxt;
+      have = more;
+      continue;
+    }
 
     // ---- Ktil ([token][channel], split) and the state as the B operand of W S
     // and (Gamma*Q) S: [value][channel position], position 32kb + 8g + 4h + i
@@ -733,9 +768,11 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
         }
       }
     }
+    cur = nxt;
+    have = more;
   }
 
-  if (s_final) {
+  if (!PREP && s_final) {
     float* sf = s_final + ((size_t)seq * H + h) * DK * DV;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
@@ -749,24 +786,61 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
   }
 }
 
+template <typename K>
+hipError_t set_lds(K kern, int bytes) {
+  return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
 template <int DK, typename TOut>
-hipError_t launch_bf16(const PrefillArgs& a) {
-  using L = Plan<DK>;
-  auto kern = prefill_bf16_kernel<DK, TOut>;
+hipError_t launch_fused(const PrefillArgs& a) {
+  using L = Plan<DK, BV>;
+  auto kern = prefill_bf16_kernel<DK, TOut, 0>;
   static bool attr_set = false;  // per instantiation; idempotent if raced
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::total);
-    if (e != hipSuccess) return e;
+    if (hipError_t e = set_lds(kern, L::total); e != hipSuccess) return e;
     attr_set = true;
   }
   const int grid = a.n_seq * a.H * (a.Dv / BV);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH), L::total, (hipStream_t)a.stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.alpha, a.beta,
                      a.initial_state, a.final_state, (TOut*)a.o, a.cu_seqlens, a.n_seq, a.T, a.H,
-                     a.Dv);
+                     a.Dv, (unsigned char*)nullptr, (const int32_t*)nullptr, 0);
   return hipGetLastError();
 }
+
+// First pass: a persistent grid of at most one workgroup per compute unit walks
+// the (chunk, head) items; n_items < 0 means "count them on the device" (packed).
+template <int DK, int DV>
+hipError_t launch_first_pass(const PrefillArgs& a, unsigned char* img, const int32_t* chunk_off,
+                             int n_items, int grid) {
+  using L = Plan<DK, DV>;
+  auto kern = prefill_bf16_kernel<DK, float, DV>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipError_t e = set_lds(kern, L::total); e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH), L::total, (hipStream_t)a.stream,
+                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.alpha, a.beta,
+                     (const float*)nullptr, (float*)nullptr, (float*)nullptr, a.cu_seqlens,
+                     a.n_seq, a.T, a.H, DV, img, chunk_off, n_items);
+  return hipGetLastError();
+}
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+size_t table_bytes(int n_seq) { return ((size_t)(n_seq + 1) * 4 + 255) / 256 * 256; }
 
 }  // namespace
 
@@ -776,10 +850,59 @@ bool prefill_supported(bool qkv_bf16, int Dk, int Dv) {
   return Dk == 64;  // fp32 inputs: the fp32-MFMA kernel, Dk = 64
 }
 
+size_t prefill_two_pass_bytes(bool varlen, int n_seq, long long tokens, int H, int Dk, int Dv) {
+  if (n_seq <= 0 || tokens < 0 || H <= 0 || !prefill_supported(true, Dk, Dv)) return 0;
+  const long long chunks = varlen ? (tokens + CH - 1) / CH + n_seq
+                                  : (long long)n_seq * ((tokens + CH - 1) / CH);
+  if (chunks * H > 0x7fffffffLL) return 0;
+  return (varlen ? table_bytes(n_seq) : 0) + (size_t)chunks * H * prefill_image_bytes(Dk, Dv);
+}
+
+bool prefill_two_pass_preferred(int n_seq, long long tokens, int H, int Dk, int Dv) {
+  if (n_seq <= 0 || H <= 0 || !prefill_supported(true, Dk, Dv)) return false;
+  // The fused kernel runs one workgroup per (sequence, head, 64-wide value
+  // slice) and repeats the state-independent work once per slice; the two-pass
+  // schedule does that work once per (chunk, head) on every compute unit.  It
+  // pays off when the fused grid leaves the device under-filled and the
+  // sequences are several chunks long.
+  const long long grid = (long long)n_seq * H * (Dv / BV);
+  return grid < 2LL * device_cus() && tokens / n_seq >= 4 * CH;
+}
+
 hipError_t launch_prefill(const PrefillArgs& a) {
   if (!a.qkv_bf16) return launch_prefill_f32(a);
-  if (a.Dk == 128) return a.o_bf16 ? launch_bf16<128, bf16>(a) : launch_bf16<128, float>(a);
-  return a.o_bf16 ? launch_bf16<64, bf16>(a) : launch_bf16<64, float>(a);
+  const bool varlen = a.cu_seqlens != nullptr;
+  const long long tokens = a.T;  // per sequence (dense) or in total (packed)
+  const size_t need = prefill_two_pass_bytes(varlen, a.n_seq, tokens, a.H, a.Dk, a.Dv);
+  if (need == 0 || !a.workspace || a.workspace_bytes < need || tokens == 0) {
+    if (a.Dk == 128) return a.o_bf16 ? launch_fused<128, bf16>(a) : launch_fused<128, float>(a);
+    return a.o_bf16 ? launch_fused<64, bf16>(a) : launch_fused<64, float>(a);
+  }
+  unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+  int32_t* chunk_off = nullptr;
+  unsigned char* img = ws;
+  int n_items = -1;
+  if (varlen) {
+    chunk_off = reinterpret_cast<int32_t*>(ws);
+    img = ws + table_bytes(a.n_seq);
+    const int cap = (int)((tokens + CH - 1) / CH + a.n_seq);
+    if (hipError_t e = launch_chunk_table(a.cu_seqlens, a.n_seq, cap, chunk_off, a.stream);
+        e != hipSuccess)
+      return e;
+  } else {
+    n_items = (int)((long long)a.n_seq * ((a.T + CH - 1) / CH) * a.H);
+  }
+  int grid = device_cus();
+  if (n_items >= 0 && n_items < grid) grid = n_items;
+  hipError_t e;
+  if (a.Dk == 128)
+    e = a.Dv == 128 ? launch_first_pass<128, 128>(a, img, chunk_off, n_items, grid)
+                    : launch_first_pass<128, 64>(a, img, chunk_off, n_items, grid);
+  else
+    e = a.Dv == 128 ? launch_first_pass<64, 128>(a, img, chunk_off, n_items, grid)
+                    : launch_first_pass<64, 64>(a, img, chunk_off, n_items, grid);
+  if (e != hipSuccess) return e;
+  return launch_prefill_state(a, img, chunk_off);
 }
 
 }  // namespace kda

@@ -44,21 +44,41 @@ def test_status_strings():
     assert lib.kda_status_string(3) == b"KDA_ERR_HIP"
 
 
-def test_workspace_size_is_t_independent():
-    """The state is fixed-size; scratch must not grow with the sequence length."""
-    sizes = {kda.workspace_size(1, T, 96, 128, 128) for T in (1, 256, 8192, 1 << 20)}
-    assert len(sizes) == 1
+def test_workspace_sizes():
+    """Two-pass workspace: one operand block per (chunk, head), a block holding
+    the frames of W, (Gamma*Q), Mqk, Ktil^T and U plus Gamma_C, rounded to 256 B;
+    packed calls add a chunk table and budget one partial chunk per sequence."""
+    frames = {(128, 128): 4 * 4 * 2 + 4 * 4 + 16 + 8 * 4 + 4 * 8,
+              (64, 64): 4 * 2 * 2 + 4 * 2 + 16 + 4 * 4 + 4 * 4}
+    for (dk, dv), f in frames.items():
+        blk = -(-(f * 1024 + dk * 4) // 256) * 256
+        for B, T, H in ((1, 1, 1), (1, 8192, 96), (3, 200, 2)):
+            assert kda.workspace_size(B, T, H, dk, dv) == B * -(-T // 64) * H * blk
+        n, tot, h = 16, 129161, 96
+        table = -(-(n + 1) * 4 // 256) * 256
+        assert _lib.varlen_workspace_size(n, tot, h, dk, dv) == table + (-(-tot // 64) + n) * h * blk
     assert kda.workspace_size(1, 256, 96, 128, 128, chunk=32) == ctypes.c_size_t(-1).value
+    assert kda.workspace_size(1, 256, 96, 96, 128) == 0          # no two-pass kernel for Dk = 96
+    assert kda.workspace_size(0, 256, 96, 128, 128) == 0         # nothing to do
+
+
+def test_two_pass_preference():
+    lib = kda.load()
+    # under-filled device, long sequences: two-pass; many short sequences: fused
+    assert lib.kda_prefill_two_pass_preferred(BF16, 1, 8192, 96, 128, 128) == 1
+    assert lib.kda_prefill_two_pass_preferred(BF16, 64, 64 * 1024, 96, 128, 128) == 0
+    assert lib.kda_prefill_two_pass_preferred(BF16, 1, 128, 96, 128, 128) == 0
+    assert lib.kda_prefill_two_pass_preferred(F32, 1, 8192, 2, 64, 64) == 0
 
 
 def _prefill(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, qd=BF16, alpha=FAKE, beta=FAKE, s0=None, s1=None, o=FAKE,
-             od=F32, B=1, T=128, H=2, Dk=128, Dv=128, chunk=64)
+             od=F32, B=1, T=128, H=2, Dk=128, Dv=128, chunk=64, ws=None, wsb=0)
     a.update(over)
     lib = kda.load()
     return lib.kda_prefill_chunked(a["q"], a["k"], a["v"], a["qd"], a["alpha"], a["beta"],
                                    a["s0"], a["s1"], a["o"], a["od"], a["B"], a["T"], a["H"],
-                                   a["Dk"], a["Dv"], a["chunk"], None, 0, None)
+                                   a["Dk"], a["Dv"], a["chunk"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("over,expect", [
@@ -76,6 +96,7 @@ def _prefill(**over):
     (dict(Dv=256), UNSUPPORTED),
     (dict(qd=F32, Dk=128), UNSUPPORTED),
     (dict(B=0), OK),
+    (dict(ws=FAKE + 64, wsb=1 << 30), INVALID),
 ])
 def test_prefill_argument_validation(over, expect):
     assert _prefill(**over) == expect

@@ -1,5 +1,7 @@
 """Chunked and packed prefill on the GPU against the fp64 oracle and against the
-GPU decode step replayed token by token."""
+GPU decode step replayed token by token.  bf16 cases run under both prefill
+schedules (the fused kernel and the two-pass first pass + state pass), which must
+also agree with each other bitwise."""
 import numpy as np
 import pytest
 import torch
@@ -12,10 +14,19 @@ from tests._common import TOL_BF16, TOL_BF16_OUT, TOL_F32, dev, oracle_heads, re
 pytestmark = pytest.mark.gpu
 
 
-def _run(inp, d, out_dtype=torch.float32):
+SCHEDULES = ["fused", "two_pass"]
+
+
+def _run(inp, d, out_dtype=torch.float32, schedule="auto"):
     return kda.prefill_chunked(to(inp.q, d), to(inp.k, d), to(inp.v, d), to(inp.alpha, d),
                                to(inp.beta, d), initial_state=to(inp.state, d),
-                               out_dtype=out_dtype)
+                               out_dtype=out_dtype, schedule=schedule)
+
+
+def _solo(inp, i, sl, schedule):
+    return kda.prefill_chunked(*(x[:, sl].contiguous() for x in
+                                 (inp.q, inp.k, inp.v, inp.alpha, inp.beta)),
+                               initial_state=inp.state[i:i + 1].contiguous(), schedule=schedule)
 
 
 def test_tiny_fp32_full():
@@ -40,12 +51,13 @@ def test_tiny_fp32_full():
     (1, 64, 2, 128, 128),
     (1, 63, 2, 128, 128),
 ])
-def test_small_bf16_against_oracle(B, T, H, Dk, Dv):
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_small_bf16_against_oracle(B, T, H, Dk, Dv, schedule):
     d = dev()
     inp = synth.make_dense(B, T, H, Dk, Dv, seed=100 + T + Dk, state_std=0.02)
     o_ref, s_ref = oracle.recurrent(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
                                     initial_state=inp.state)
-    o, s = _run(inp, d)
+    o, s = _run(inp, d, schedule=schedule)
     torch.cuda.synchronize()
     assert rel(o.cpu(), o_ref) <= TOL_BF16
     assert rel(s.cpu(), s_ref) <= TOL_BF16
@@ -64,8 +76,9 @@ def test_fp32_inputs_dv128_and_bf16_output():
     assert rel(o.float().cpu(), o_ref) <= TOL_BF16_OUT
 
 
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("kind", ["slow_decay", "alpha_one", "bounded_gate"])
-def test_decay_regimes(kind):
+def test_decay_regimes(kind, schedule):
     """Slow decay (mean alpha ~0.97), alpha = 1 (DeltaNet) and the bounded gate
     g = -5 sigmoid(z) of "Kimi K3 的 KDA" section 6: the state carry dominates."""
     d = dev()
@@ -80,34 +93,37 @@ def test_decay_regimes(kind):
         inp.alpha = torch.exp(-5.0 * torch.sigmoid(z)).float()
     o_ref, s_ref = oracle.recurrent(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
                                     initial_state=inp.state)
-    o, s = _run(inp, d)
+    o, s = _run(inp, d, schedule=schedule)
     torch.cuda.synchronize()
     assert rel(o.cpu(), o_ref) <= TOL_BF16
     assert rel(s.cpu(), s_ref) <= TOL_BF16
 
 
-def test_zero_length_hands_state_through():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_zero_length_hands_state_through(schedule):
     d = dev()
     s0 = synth.make_state(2, 3, 128, 128, seed=5).to(d)
     e = torch.empty(2, 0, 3, 128, dtype=torch.bfloat16, device=d)
     a = torch.empty(2, 0, 3, 128, dtype=torch.float32, device=d)
-    o, s = kda.prefill_chunked(e, e, e, a, torch.empty(2, 0, 3, device=d), initial_state=s0)
+    o, s = kda.prefill_chunked(e, e, e, a, torch.empty(2, 0, 3, device=d), initial_state=s0,
+                               schedule="fused" if schedule == "fused" else "auto")
     torch.cuda.synchronize()
     assert o.shape == (2, 0, 3, 128) and torch.equal(s, s0)
 
 
-def test_two_segments_equal_whole():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_two_segments_equal_whole(schedule):
     """Prefill in two calls with the state handed over matches one call."""
     d = dev()
     inp = synth.make_dense(1, 300, 2, 128, 128, seed=51)
-    o, s = _run(inp, d)
+    o, s = _run(inp, d, schedule=schedule)
     cut = 130
     o1, s1 = kda.prefill_chunked(*(x[:, :cut].contiguous().to(d) for x in
                                    (inp.q, inp.k, inp.v, inp.alpha, inp.beta)),
-                                 initial_state=inp.state.to(d))
+                                 initial_state=inp.state.to(d), schedule=schedule)
     o2, s2 = kda.prefill_chunked(*(x[:, cut:].contiguous().to(d) for x in
                                    (inp.q, inp.k, inp.v, inp.alpha, inp.beta)),
-                                 initial_state=s1)
+                                 initial_state=s1, schedule=schedule)
     torch.cuda.synchronize()
     assert rel(torch.cat([o1, o2], 1).cpu(), o.cpu()) <= TOL_BF16
     assert rel(s2.cpu(), s.cpu()) <= TOL_BF16
@@ -119,24 +135,29 @@ def _k3_8k(d):
                             state_std=w["state_std"], device=d)
 
 
-def test_k3_prefill_8k_sampled_heads():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_k3_prefill_8k_sampled_heads(schedule):
     """K3-shaped layer (B=1, H=96, T=8192, d=128) at full size; the oracle runs on
     8 heads spread over the head axis (all tokens)."""
     d = dev()
     inp = _k3_8k(d)
-    o, s = _run(inp, d)
+    o, s = _run(inp, d, schedule=schedule)
     torch.cuda.synchronize()
     heads = [0, 13, 27, 40, 53, 66, 81, 95]
     o_ref, s_ref = oracle_heads(inp, heads)
     assert rel(o[:, :, heads].cpu(), o_ref) <= TOL_BF16
     assert rel(s[:, heads].cpu(), s_ref) <= TOL_BF16
-    # determinism: a second launch is bitwise identical
-    o2, s2 = _run(inp, d)
+    # determinism: a second launch is bitwise identical, and so is the other schedule
+    o2, s2 = _run(inp, d, schedule=schedule)
     assert torch.equal(o, o2) and torch.equal(s, s2)
+    other = SCHEDULES[1 - SCHEDULES.index(schedule)]
+    o3, s3 = _run(inp, d, schedule=other)
+    assert torch.equal(o, o3) and torch.equal(s, s3)
 
 
 def test_k3_prefill_8k_matches_decode_replay():
-    """All 96 heads: chunked prefill vs the GPU decode step replayed token by token."""
+    """All 96 heads: chunked prefill (the schedule the library picks for this
+    shape) vs the GPU decode step replayed token by token."""
     d = dev()
     inp = _k3_8k(d)
     o, s = _run(inp, d)
@@ -155,18 +176,19 @@ def _varlen_case(lengths, H, D, seed, d):
     return synth.make_varlen(lengths, H, D, D, seed=seed, device=d)
 
 
-def _run_varlen(inp, d):
+def _run_varlen(inp, d, schedule="auto"):
     return kda.prefill_varlen(inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.cu_seqlens,
-                              initial_state=inp.state)
+                              initial_state=inp.state, schedule=schedule)
 
 
-def test_varlen_edges_and_isolation():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_varlen_edges_and_isolation(schedule):
     """Empty, 1-token, chunk-boundary and ragged sequences in one packed batch; each
     sequence must equal the oracle and, bitwise, its own solo run."""
     d = dev()
     lengths = [0, 1, 63, 64, 65, 200, 7]
     inp = _varlen_case(lengths, 3, 128, seed=61, d=d)
-    o, s = _run_varlen(inp, d)
+    o, s = _run_varlen(inp, d, schedule)
     torch.cuda.synchronize()
     cu = inp.cu_seqlens.cpu().numpy()
     o_ref, s_ref = oracle.recurrent(inp.q.cpu(), inp.k.cpu(), inp.v.cpu(), inp.alpha.cpu(),
@@ -175,13 +197,12 @@ def test_varlen_edges_and_isolation():
     assert rel(s.cpu(), s_ref) <= TOL_BF16
     for i in range(len(lengths)):
         sl = slice(int(cu[i]), int(cu[i + 1]))
-        oi, si = kda.prefill_chunked(*(x[:, sl].contiguous() for x in
-                                       (inp.q, inp.k, inp.v, inp.alpha, inp.beta)),
-                                     initial_state=inp.state[i:i + 1].contiguous())
+        oi, si = _solo(inp, i, sl, schedule)
         assert torch.equal(oi, o[:, sl]) and torch.equal(si, s[i:i + 1])
 
 
-def test_varlen_16_sequences_sampled():
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_varlen_16_sequences_sampled(schedule):
     """Packed workload: 16 sequences, lengths uniform in [1024, 16384] from the seed,
     H=96, d=128, per-sequence initial / final state.  The oracle runs on 2 heads of
     every sequence; 3 sequences are also compared bitwise with solo runs."""
@@ -189,7 +210,7 @@ def test_varlen_16_sequences_sampled():
     w = synth.WORKLOADS["varlen_16"]
     lengths = synth.varlen_lengths(w["N"], w["lo"], w["hi"], seed=w["seed"])
     inp = _varlen_case(lengths, w["H"], w["D"], seed=w["seed"], d=d)
-    o, s = _run_varlen(inp, d)
+    o, s = _run_varlen(inp, d, schedule)
     torch.cuda.synchronize()
     cu = inp.cu_seqlens.cpu().numpy()
     heads = [7, 88]
@@ -199,7 +220,50 @@ def test_varlen_16_sequences_sampled():
     order = np.argsort(lengths)
     for i in (int(order[0]), int(order[len(order) // 2]), int(order[-1])):
         sl = slice(int(cu[i]), int(cu[i + 1]))
-        oi, si = kda.prefill_chunked(*(x[:, sl].contiguous() for x in
-                                       (inp.q, inp.k, inp.v, inp.alpha, inp.beta)),
-                                     initial_state=inp.state[i:i + 1].contiguous())
+        oi, si = _solo(inp, i, sl, schedule)
         assert torch.equal(oi, o[:, sl]) and torch.equal(si, s[i:i + 1])
+
+
+@pytest.mark.parametrize("B,T,H,Dk,Dv", [
+    (2, 200, 3, 128, 128), (1, 77, 2, 64, 64), (1, 130, 2, 128, 64), (1, 300, 1, 64, 128),
+])
+def test_schedules_agree_bitwise(B, T, H, Dk, Dv):
+    """The two schedules compute the same products in the same order."""
+    d = dev()
+    inp = synth.make_dense(B, T, H, Dk, Dv, seed=300 + T, state_std=0.02)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        o1, s1 = _run(inp, d, out_dtype, schedule="fused")
+        o2, s2 = _run(inp, d, out_dtype, schedule="two_pass")
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    lengths = [130, 1, 0, 64, 257]
+    vin = _varlen_case(lengths, 2, 128, seed=71, d=d)
+    o1, s1 = _run_varlen(vin, d, "fused")
+    o2, s2 = _run_varlen(vin, d, "two_pass")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_two_pass_workspace_reuse_and_capacity():
+    """A caller-owned workspace serves consecutive calls of different sizes, and
+    the packed bound holds when every sequence ends in a partial chunk."""
+    d = dev()
+    big = kda.workspace_size(1, 1024, 4, 128, 128)
+    ws = torch.empty(big, dtype=torch.uint8, device=d)
+    for T in (1024, 70):
+        inp = synth.make_dense(1, T, 4, 128, 128, seed=400 + T, state_std=0.02)
+        o1, s1 = _run(inp, d, schedule="fused")
+        o2, s2 = kda.prefill_chunked(inp.q.to(d), inp.k.to(d), inp.v.to(d), inp.alpha.to(d),
+                                     inp.beta.to(d), initial_state=inp.state.to(d),
+                                     schedule="two_pass", workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    lengths = [65] * 9 + [1] * 5
+    vin = _varlen_case(lengths, 2, 64, seed=72, d=d)
+    need = kda._lib.varlen_workspace_size(len(lengths), sum(lengths), 2, 64, 64)
+    ws = torch.empty(need, dtype=torch.uint8, device=d)
+    o1, s1 = _run_varlen(vin, d, "fused")
+    o2, s2 = kda.prefill_varlen(vin.q, vin.k, vin.v, vin.alpha, vin.beta, vin.cu_seqlens,
+                                initial_state=vin.state, schedule="two_pass", workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
