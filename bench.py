@@ -2,10 +2,14 @@
 
 One step = one chunked prefill (every step of the chunk form) of a K3-shaped
 layer: B=1, H=96, T=8192, d_k=d_v=128, bf16 q/k/v, fp32 alpha/beta/state,
-fp32 output, inputs resident in HBM.  The line also carries the decode step's
-state bandwidth (64 sessions x 96 heads x 128x128 fp32 state, updated in place),
-the prefill kernel's roofline position, and the fp64 CPU oracle timed on this
-host on the same prefill workload.
+fp32 output, inputs resident in HBM, in the schedule the library prefers for
+the shape (two-pass: a first pass over all (chunk, head) items, then the
+state pass; one kda_prefill_chunked call, two kernel launches, workspace
+allocated once outside the timed region).  The line also carries the fused
+single-kernel schedule's time on the same step, the decode step's state
+bandwidth (64 sessions x 96 heads x 128x128 fp32 state, updated in place), the
+step's roofline position, and the fp64 CPU oracle timed on this host on the
+same prefill workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 """
@@ -65,6 +69,8 @@ def measured_traffic(summary: str, sources: list[str]):
 
 
 PREFILL_SOURCES = ["kimi_delta_attention_amd/csrc/kda_prefill.hip",
+                   "kimi_delta_attention_amd/csrc/kda_prefill_state.hip",
+                   "kimi_delta_attention_amd/csrc/kda_frag.h",
                    "kimi_delta_attention_amd/csrc/kda_common.h"]
 DECODE_SOURCES = ["kimi_delta_attention_amd/csrc/kda_decode.hip",
                   "kimi_delta_attention_amd/csrc/kda_common.h"]
@@ -96,10 +102,16 @@ def main():
     inp = synth.make_dense(B, T, H, D, D, seed=w["seed"], state_std=w["state_std"], device=d)
     o = torch.empty(B, T, H, D, dtype=torch.float32, device=d)
     fs = torch.empty(B, H, D, D, dtype=torch.float32, device=d)
+    lib = kda.load()
+    two_pass = bool(lib.kda_prefill_two_pass_preferred(1, B, B * T, H, D, D))
+    schedule = "two_pass" if two_pass else "fused"
+    ws = (torch.empty(kda.workspace_size(B, T, H, D, D), dtype=torch.uint8, device=d)
+          if two_pass else None)
 
-    def step():
+    def step(sched=schedule):
         kda.prefill_chunked(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
-                            initial_state=inp.state, final_state=fs, o=o)
+                            initial_state=inp.state, final_state=fs, o=o, schedule=sched,
+                            workspace=ws if sched == "two_pass" else None)
 
     # plain device copy of known size: calibrates HBM byte counters under rocprofv3
     calib = torch.empty(64 << 20, dtype=torch.float32, device=d)  # 256 MiB
@@ -126,8 +138,24 @@ def main():
     nbytes = prefill_bytes(B, T, H, D, D)
     gbs = nbytes / (avg_launch_ms / 1e3) / 1e9
     tflops = prefill_flops(B, T, H, D) / (avg_launch_ms / 1e3) / 1e12
-    print(f"bench: prefill {ms_step:.3f} ms/step, {gbs:.0f} GB/s algorithmic, "
+    print(f"bench: prefill ({schedule}) {ms_step:.3f} ms/step, {gbs:.0f} GB/s algorithmic, "
           f"{tflops:.1f} TFLOP/s (pages' count), wall {wall:.2f}s", file=sys.stderr, flush=True)
+
+    # the other schedule on the same step, for context (not the headline value)
+    other = "fused" if two_pass else None
+    other_ms = None
+    if other:
+        for _ in range(2):
+            step(other)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step(other)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        other_ms = e0.elapsed_time(e1) / args.steps
+        print(f"bench: prefill ({other}) {other_ms:.3f} ms/step", file=sys.stderr, flush=True)
 
     # decode step (state read + write once per step)
     wd = synth.WORKLOADS["decode_b64"]
@@ -180,17 +208,22 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "k3_prefill_8k", "B": B, "T": T, "H": H, "d_k": D, "d_v": D,
-                   "chunk": 64, "qkv": "bf16", "alpha_beta_state": "fp32", "o": "fp32"},
+                   "chunk": 64, "qkv": "bf16", "alpha_beta_state": "fp32", "o": "fp32",
+                   "schedule": schedule},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("prefill_bf16_kernel__k3_prefill_8k__hbm_counters.txt",
+                     "traffic": measured_traffic(f"prefill_{schedule}__k3_prefill_8k__hbm_counters.txt",
                                                  PREFILL_SOURCES),
-                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
-                                     "copy-calibrated)",
-                     "kernel": "prefill_bf16_kernel<Dk=128, fp32 out>",
+                     "traffic_unit": "HBM bytes per kda_prefill_chunked call (rocprofv3 "
+                                     "FETCH_SIZE + WRITE_SIZE of its kernels, copy-calibrated)",
+                     "kernel": ("kda_prefill_chunked, two-pass: prefill_bf16_kernel<128, PREP_DV=128> "
+                                "+ prefill_state_kernel<128, 128>" if two_pass else
+                                "kda_prefill_chunked, fused: prefill_bf16_kernel<128, fp32 out>"),
                      "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_ms": avg_launch_ms,
                      "mfma_frac_pages_flops": tflops / BF16_PEAK_TFLOPS},
+        "prefill_other_schedule": ({"schedule": other, "ms_per_step": other_ms,
+                                    "tokens_per_s": B * T / (other_ms / 1e3)} if other else None),
         "decode": {"workload": "decode_b64", "B": wd["B"], "H": wd["H"], "d": wd["D"],
                    "us_per_step": dec_ms * 1e3, "state_gbs": dec_state_gbs,
                    "total_gbs": dec_total_gbs,

@@ -179,7 +179,8 @@ size_t kda_prefill_varlen_workspace_size(int N, int total_tokens, int H, int Dk,
  * n_seq * H * Dv / 64 workgroups and repeats the state-independent work for
  * each 64-wide value slice; the two-pass schedule wins when that grid is below
  * about twice the compute-unit count and the sequences are at least 4 chunks
- * long on average.
+ * long on average.  It is preferred only while its workspace is at most 1/16
+ * of device memory and 16 GiB.
  */
 int kda_prefill_two_pass_preferred(kda_dtype qkv_dtype, int n_seq, int total_tokens, int H, int Dk,
                                    int Dv);

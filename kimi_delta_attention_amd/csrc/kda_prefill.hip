@@ -684,14 +684,18 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     }
     __syncthreads();
 
-    // ---- P = U - W S and O = (Gamma*Q) S for this tile's tokens, this wave's columns
+    // ---- P = U - W S and O = (Gamma*Q) S for this tile's tokens, this wave's
+    // columns; each product is accumulated as two chains, the low and the high
+    // channel half, added at the end (the order the state pass uses)
     floatx4 accO[NCH];
     {
-      floatx4 accW[NCH];
+      floatx4 accW[NCH], accW2[NCH], accO2[NCH];
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         accW[c] = floatx4{0.f, 0.f, 0.f, 0.f};
         accO[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+        accW2[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+        accO2[c] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -700,10 +704,17 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
         for (int c = 0; c < NCH; ++c) {
           const bf16x8 bh = frag_ld(ST, ldS, vh0 + 16 * c + tr, 32 * kb, g);
           const bf16x8 bl = frag_ld(ST + loS, ldS, vh0 + 16 * c + tr, 32 * kb, g);
-          accW[c] = mma_ab(wh[kb], wl[kb], bh, bl, accW[c]);
-          accO[c] = mfma_bf16(aq, bh, accO[c]);
-          accO[c] = mfma_bf16(aq, bl, accO[c]);
+          floatx4& aw = kb < NKH ? accW[c] : accW2[c];
+          floatx4& ao = kb < NKH ? accO[c] : accO2[c];
+          aw = mma_ab(wh[kb], wl[kb], bh, bl, aw);
+          ao = mfma_bf16(aq, bh, ao);
+          ao = mfma_bf16(aq, bl, ao);
         }
+      }
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        accW[c] = accW[c] + accW2[c];
+        accO[c] = accO[c] + accO2[c];
       }
       // P to LDS as [value][token position]; token 32kb + 16h + 4g + i sits at
       // position 32kb + 8g + 4h + i (the order of the Mqk^T operand)
@@ -858,15 +869,32 @@ size_t prefill_two_pass_bytes(bool varlen, int n_seq, long long tokens, int H, i
   return (varlen ? table_bytes(n_seq) : 0) + (size_t)chunks * H * prefill_image_bytes(Dk, Dv);
 }
 
+size_t device_mem() {
+  static size_t mem[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (mem[dev] == 0) {
+    size_t b = 0;
+    if (hipDeviceTotalMem(&b, dev) != hipSuccess) b = 0;
+    mem[dev] = b;
+  }
+  return mem[dev];
+}
+
 bool prefill_two_pass_preferred(int n_seq, long long tokens, int H, int Dk, int Dv) {
   if (n_seq <= 0 || H <= 0 || !prefill_supported(true, Dk, Dv)) return false;
   // The fused kernel runs one workgroup per (sequence, head, 64-wide value
   // slice) and repeats the state-independent work once per slice; the two-pass
   // schedule does that work once per (chunk, head) on every compute unit.  It
   // pays off when the fused grid leaves the device under-filled and the
-  // sequences are several chunks long.
+  // sequences are several chunks long, and is chosen only while its workspace
+  // stays within 1/16 of device memory (and 16 GiB).
   const long long grid = (long long)n_seq * H * (Dv / BV);
-  return grid < 2LL * device_cus() && tokens / n_seq >= 4 * CH;
+  if (!(grid < 2LL * device_cus() && tokens / n_seq >= 4 * CH)) return false;
+  const size_t need = prefill_two_pass_bytes(true, n_seq, tokens, H, Dk, Dv);
+  size_t cap = device_mem() / 16;
+  if (cap == 0 || cap > (size_t(16) << 30)) cap = size_t(16) << 30;
+  return need > 0 && need <= cap;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {

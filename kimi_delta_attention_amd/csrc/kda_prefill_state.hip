@@ -10,13 +10,19 @@
 //
 // This kernel runs that part.  One workgroup owns (sequence, head, 64-wide
 // value slice) and walks the chunks in order with the state slice in MFMA
-// accumulators, exactly as the fused kernel does, but its per-chunk operands
-// arrive as register images (Images<DK, DV>) that are fetched with coalesced
-// 16-byte loads one chunk ahead.  Eight waves: wave (w, hh) takes token tile w
-// (tokens 16w..16w+15) and value half hh for P and O, and state rows
-// [w*DK/4, (w+1)*DK/4) x the same value half for the update.  The products and
-// their order are those of the fused kernel, so both schedules give bitwise
-// the same results.
+// accumulators; its per-chunk operands arrive as register images
+// (Images<DK, DV>) fetched with coalesced 16-byte loads.  Eight waves; wave
+// (w, hh) fetches only operands no other wave of the workgroup fetches (the
+// per-compute-unit load path, not HBM, limits this pass):
+//   W S and (Gamma*Q) S   token tile w, all 64 values, channel half hh; the
+//                         two halves are added through LDS, each wave keeping
+//                         the sum for its value half hh
+//   P, Mqk P, o           token tile w, value half hh
+//   state update          Dk = 128: state rows 16(2w + hh).., all 64 values;
+//                         Dk = 64: rows 16w.., value half hh
+// The fused kernel computes the same products with the same accumulation
+// order (the two channel halves as separate chains, low half first), so both
+// schedules give bitwise the same results.
 #include "kda_common.h"
 #include "kda_frag.h"
 #include "kda_internal.h"
@@ -32,7 +38,10 @@ template <int DK>
 struct StatePlan {
   static constexpr int ldS = DK + 8, ldP = CH + 8;
   static constexpr int ST = BV * ldS * 2 * 2, PT = BV * ldP * 2 * 2;
-  static constexpr int oST = 0, oPT = ST, total = ST + PT;
+  // partial sums handed between the two waves of a tile: [w][from hh][tile j][W, O] frames
+  static constexpr int XC = 4 * 2 * 2 * 2 * 1024;
+  static constexpr int oST = 0, oPT = ST, oXC = ST + PT, total = ST + PT + XC;
+  static_assert(total <= 163840, "LDS budget");
 };
 
 template <int DK, int DV, typename TOut>
@@ -43,15 +52,16 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
   using L = StatePlan<DK>;
   using IM = Images<DK, DV>;
   constexpr int NKB = DK / 32;
-  constexpr int RPW = DK / 4;
-  constexpr int RTW = RPW / 16;
-  constexpr int NCH = BV / 32;
+  constexpr int NKH = NKB / 2;                   // 32-channel blocks per channel half
+  constexpr int NVT = BV / 16;                   // value tiles of the slice
+  constexpr int KVT = DK == 128 ? NVT : NVT / 2;  // value tiles of this wave's state rows
   constexpr int ldS = L::ldS, ldP = L::ldP;
   constexpr int loS = BV * ldS, loP = BV * ldP;
 
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* ST = reinterpret_cast<bf16*>(smem + L::oST);
   bf16* PT = reinterpret_cast<bf16*>(smem + L::oPT);
+  unsigned char* XC = smem + L::oXC;
 
   const int tid = threadIdx.x;
   const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -81,137 +91,151 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     ci0 = seq * ((T + CH - 1) / CH);
   }
   const int vcol0 = sl * BV;
-  const int vh0 = 32 * hh;
-  const int vt0 = (vcol0 + vh0) / 16;  // first U tile of this wave
+  const int vh0 = 32 * hh;             // value half of P and o
+  const int vt0 = (vcol0 + vh0) / 16;  // its first U tile
+  // state rows and value tiles of the update
+  const int srt = DK == 128 ? 2 * w + hh : w;  // 16-row tile
+  const int sv0 = DK == 128 ? 0 : 2 * hh;      // first value tile (within the slice)
 
-  floatx4 Sacc[RTW][NCH];
+  floatx4 Sacc[KVT];
   {
     const int tr = lane & 15, g = lane >> 4;
     const float* si = s_init ? s_init + ((size_t)seq * H + h) * DK * DV : nullptr;
 #pragma unroll
-    for (int rt = 0; rt < RTW; ++rt)
+    for (int j = 0; j < KVT; ++j)
 #pragma unroll
-      for (int c = 0; c < NCH; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = w * RPW + rt * 16 + 4 * g + i;
-          Sacc[rt][c][i] = si ? si[(size_t)row * DV + vcol0 + vh0 + c * 16 + tr] : 0.f;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * srt + 4 * g + i;
+        Sacc[j][i] = si ? si[(size_t)row * DV + vcol0 + 16 * (sv0 + j) + tr] : 0.f;
+      }
   }
 
-  // Operands of one chunk, loaded one chunk ahead into a single register set:
-  // the W, (Gamma*Q) and U parts right after W S and (Gamma*Q) S have used
-  // them, the Mqk, Ktil and Gamma_C parts after the state update.
-  struct Ops {
-    bf16x8 wh[NKB], wl[NKB], qf[NKB], mh[2], ml[2], kh[RTW][2], kl[RTW][2];
-    floatx4 u[NCH], gc[RTW];
+  // Operands of one chunk.  OpsA (W and Gamma*Q of this wave's channel half,
+  // U of its value half; needed first) is fetched one chunk ahead into a second
+  // register set; OpsB (Mqk of tile w, Ktil of the state rows, Gamma_C; needed
+  // last) at the start of its own chunk.  Every fetch is unconditional (the
+  // last chunk refetches itself) so that the waits the compiler places for
+  // OpsB never have to cover the OpsA fetch issued after it.
+  struct OpsA {
+    bf16x8 wh[NKH], wl[NKH], qf[NKH];
+    floatx4 u[2];
+  };
+  struct OpsB {
+    bf16x8 mh[2], ml[2], kh[2], kl[2];
+    floatx4 gc;
   };
   auto item_base = [&](int c) -> const unsigned char* {
     return img + ((size_t)(ci0 + c) * H + h) * IM::bytes;
   };
-  auto load_a = [&](int c, Ops& op) {
+  auto load_a = [&](int c, OpsA& op) {
     const unsigned char* b = item_base(c);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      op.wh[kb] = *frame_ptr<bf16x8>(b, IM::w_frame(w, kb, 0), lane);
-      op.wl[kb] = *frame_ptr<bf16x8>(b, IM::w_frame(w, kb, 1), lane);
-      op.qf[kb] = *frame_ptr<bf16x8>(b, IM::q_frame(w, kb), lane);
+    for (int kk = 0; kk < NKH; ++kk) {
+      op.wh[kk] = *frame_ptr<bf16x8>(b, IM::w_frame(w, NKH * hh + kk, 0), lane);
+      op.wl[kk] = *frame_ptr<bf16x8>(b, IM::w_frame(w, NKH * hh + kk, 1), lane);
+      op.qf[kk] = *frame_ptr<bf16x8>(b, IM::q_frame(w, NKH * hh + kk), lane);
     }
 #pragma unroll
-    for (int c2 = 0; c2 < NCH; ++c2) op.u[c2] = *frame_ptr<floatx4>(b, IM::u_frame(w, vt0 + c2), lane);
+    for (int j = 0; j < 2; ++j) op.u[j] = *frame_ptr<floatx4>(b, IM::u_frame(w, vt0 + j), lane);
   };
-  auto load_b = [&](int c, Ops& op) {
+  auto load_b = [&](int c, OpsB& op) {
     const unsigned char* b = item_base(c);
-    const int g = lane >> 4;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       op.mh[kb] = *frame_ptr<bf16x8>(b, IM::m_frame(w, kb, 0), lane);
       op.ml[kb] = *frame_ptr<bf16x8>(b, IM::m_frame(w, kb, 1), lane);
+      op.kh[kb] = *frame_ptr<bf16x8>(b, IM::k_frame(srt, kb, 0), lane);
+      op.kl[kb] = *frame_ptr<bf16x8>(b, IM::k_frame(srt, kb, 1), lane);
     }
-#pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        op.kh[rt][kb] = *frame_ptr<bf16x8>(b, IM::k_frame(RTW * w + rt, kb, 0), lane);
-        op.kl[rt][kb] = *frame_ptr<bf16x8>(b, IM::k_frame(RTW * w + rt, kb, 1), lane);
-      }
-      op.gc[rt] = *reinterpret_cast<const floatx4*>(b + IM::g_off +
-                                                    4 * (w * RPW + rt * 16 + 4 * g));
-    }
+    op.gc = *reinterpret_cast<const floatx4*>(b + IM::g_off + 4 * (16 * srt + 4 * (lane >> 4)));
+  };
+  // partial-sum frames: [w][from hh][tile j][W, O]
+  auto xc = [&](int from, int j, int part, int ln) {
+    return reinterpret_cast<floatx4*>(XC + ((((w * 2 + from) * 2 + j) * 2 + part) * 1024) + 16 * ln);
   };
 
   const int nch = (int)((len + CH - 1) / CH);
-  Ops op;
-  if (nch > 0) {
-    load_a(0, op);
-    load_b(0, op);
-  }
+  OpsA op;
+  if (nch > 0) load_a(0, op);
   for (int c = 0; c < nch; ++c) {
+    OpsB ob;
+    load_b(c, ob);
     int lane_x = lane;
     __asm__ volatile("" : "+v"(lane_x));
     const int tr = lane_x & 15;
     const int g = lane_x >> 4;
     const long long tok0 = start + (long long)c * CH;
     const int nv = (int)(len - (long long)c * CH < CH ? len - (long long)c * CH : CH);
-    const bool more = c + 1 < nch;
 
     // ---- the state as the B operand of W S and (Gamma*Q) S: [value][channel
     // position], position 32kb + 8g + 4h + i holds channel 32kb + 16h + 4g + i
-#pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
-      const int c0r = w * RPW + rt * 16;
+    {
+      const int c0r = 16 * srt;
       const int pos = 32 * (c0r >> 5) + 8 * g + 4 * ((c0r >> 4) & 1);
 #pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) {
-        float x4[4] = {Sacc[rt][cc][0], Sacc[rt][cc][1], Sacc[rt][cc][2], Sacc[rt][cc][3]};
-        st_split4(ST + (vh0 + 16 * cc + tr) * ldS + pos, loS, x4);
+      for (int j = 0; j < KVT; ++j) {
+        float x4[4] = {Sacc[j][0], Sacc[j][1], Sacc[j][2], Sacc[j][3]};
+        st_split4(ST + (16 * (sv0 + j) + tr) * ldS + pos, loS, x4);
       }
     }
     __syncthreads();
+    OpsA nx;
+    load_a(c + 1 < nch ? c + 1 : c, nx);
 
-    // ---- P = U - W S and O = (Gamma*Q) S for tile w, this wave's columns
-    floatx4 accO[NCH];
-    {
-      floatx4 accW[NCH];
+    // ---- W S and (Gamma*Q) S over this wave's channel half, all 64 values
+    floatx4 accW[NVT], accO[NVT];
 #pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) {
-        accW[cc] = floatx4{0.f, 0.f, 0.f, 0.f};
-        accO[cc] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int vt = 0; vt < NVT; ++vt) {
+      accW[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      accO[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKH; ++kk) {
+      const int kb = NKH * hh + kk;
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) {
+        const bf16x8 bh = frag_ld(ST, ldS, 16 * vt + tr, 32 * kb, g);
+        const bf16x8 bl = frag_ld(ST + loS, ldS, 16 * vt + tr, 32 * kb, g);
+        accW[vt] = mma_ab(op.wh[kk], op.wl[kk], bh, bl, accW[vt]);
+        accO[vt] = mfma_bf16(op.qf[kk], bh, accO[vt]);
+        accO[vt] = mfma_bf16(op.qf[kk], bl, accO[vt]);
       }
+    }
+    // hand the partner's value half over, take its partial sums for ours
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+    for (int j = 0; j < 2; ++j) {
+      *xc(hh, j, 0, lane_x) = accW[2 * (1 - hh) + j];
+      *xc(hh, j, 1, lane_x) = accO[2 * (1 - hh) + j];
+    }
+    __syncthreads();
+    floatx4 accP[2];
 #pragma unroll
-        for (int cc = 0; cc < NCH; ++cc) {
-          const bf16x8 bh = frag_ld(ST, ldS, vh0 + 16 * cc + tr, 32 * kb, g);
-          const bf16x8 bl = frag_ld(ST + loS, ldS, vh0 + 16 * cc + tr, 32 * kb, g);
-          accW[cc] = mma_ab(op.wh[kb], op.wl[kb], bh, bl, accW[cc]);
-          accO[cc] = mfma_bf16(op.qf[kb], bh, accO[cc]);
-          accO[cc] = mfma_bf16(op.qf[kb], bl, accO[cc]);
-        }
-      }
-      float pv[NCH][4];
+    for (int j = 0; j < 2; ++j) {
+      const floatx4 pw = *xc(1 - hh, j, 0, lane_x), po = *xc(1 - hh, j, 1, lane_x);
+      const floatx4 mw = accW[2 * hh + j], mo = accO[2 * hh + j];
+      const floatx4 wsum = hh ? pw + mw : mw + pw;  // low channel half first
+      accP[j] = hh ? po + mo : mo + po;             // (Gamma*Q) S, then Mqk P below
+      float pv[4];
 #pragma unroll
-      for (int cc = 0; cc < NCH; ++cc)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pv[cc][i] = op.u[cc][i] - accW[cc][i];
-      if (more) load_a(c + 1, op);
+      for (int i = 0; i < 4; ++i) pv[i] = op.u[j][i] - wsum[i];
       // P to LDS as [value][token position]; token 32kb + 16h + 4g + i sits at
       // position 32kb + 8g + 4h + i (the order of the Mqk^T operand)
       const int pos = 32 * (w >> 1) + 8 * g + 4 * (w & 1);
-#pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) st_split4(PT + (vh0 + 16 * cc + tr) * ldP + pos, loP, pv[cc]);
+      st_split4(PT + (vh0 + 16 * j + tr) * ldP + pos, loP, pv);
     }
+    op = nx;
     __syncthreads();
 
-    // ---- O += Mqk P; store o
+    // ---- O += Mqk P; store o.  Both token blocks for every tile: the Mqk
+    // frames of blocks after the tile are zero, and a branch here would let the
+    // compiler move their fetch next to this use.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      if (kb > (w >> 1)) continue;
 #pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) {
-        const bf16x8 bh = frag_ld(PT, ldP, vh0 + 16 * cc + tr, 32 * kb, g);
-        const bf16x8 bl = frag_ld(PT + loP, ldP, vh0 + 16 * cc + tr, 32 * kb, g);
-        accO[cc] = mma_ab(op.mh[kb], op.ml[kb], bh, bl, accO[cc]);
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 bh = frag_ld(PT, ldP, vh0 + 16 * j + tr, 32 * kb, g);
+        const bf16x8 bl = frag_ld(PT + loP, ldP, vh0 + 16 * j + tr, 32 * kb, g);
+        accP[j] = mma_ab(ob.mh[kb], ob.ml[kb], bh, bl, accP[j]);
       }
     }
 #pragma unroll
@@ -220,49 +244,35 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       if (rr < nv) {
         TOut* orow = o + ((size_t)(tok0 + rr) * H + h) * DV + vcol0 + vh0 + tr;
 #pragma unroll
-        for (int cc = 0; cc < NCH; ++cc) __builtin_nontemporal_store((TOut)accO[cc][i], orow + 16 * cc);
+        for (int j = 0; j < 2; ++j) __builtin_nontemporal_store((TOut)accP[j][i], orow + 16 * j);
       }
     }
 
     // ---- S = Diag(Gamma_C) S + Ktil^T P
-    {
-      bf16x8 bph[2][NCH], bpl[2][NCH];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int j = 0; j < KVT; ++j) {
 #pragma unroll
-        for (int cc = 0; cc < NCH; ++cc) {
-          bph[kb][cc] = frag_ld(PT, ldP, vh0 + 16 * cc + tr, 32 * kb, g);
-          bpl[kb][cc] = frag_ld(PT + loP, ldP, vh0 + 16 * cc + tr, 32 * kb, g);
-        }
+      for (int i = 0; i < 4; ++i) Sacc[j][i] *= ob.gc[i];
 #pragma unroll
-      for (int rt = 0; rt < RTW; ++rt) {
-#pragma unroll
-        for (int cc = 0; cc < NCH; ++cc)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) Sacc[rt][cc][i] *= op.gc[rt][i];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int cc = 0; cc < NCH; ++cc)
-            Sacc[rt][cc] = mma_ab(op.kh[rt][kb], op.kl[rt][kb], bph[kb][cc], bpl[kb][cc], Sacc[rt][cc]);
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 bh = frag_ld(PT, ldP, 16 * (sv0 + j) + tr, 32 * kb, g);
+        const bf16x8 bl = frag_ld(PT + loP, ldP, 16 * (sv0 + j) + tr, 32 * kb, g);
+        Sacc[j] = mma_ab(ob.kh[kb], ob.kl[kb], bh, bl, Sacc[j]);
       }
     }
-    if (more) load_b(c + 1, op);
-    __syncthreads();  // PT and ST reads done before the next chunk overwrites them
+    __syncthreads();  // PT, ST and the partial sums are read before the next chunk rewrites them
   }
 
   if (s_final) {
     const int tr = lane & 15, g = lane >> 4;
     float* sf = s_final + ((size_t)seq * H + h) * DK * DV;
 #pragma unroll
-    for (int rt = 0; rt < RTW; ++rt)
+    for (int j = 0; j < KVT; ++j)
 #pragma unroll
-      for (int cc = 0; cc < NCH; ++cc)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = w * RPW + rt * 16 + 4 * g + i;
-          sf[(size_t)row * DV + vcol0 + vh0 + cc * 16 + tr] = Sacc[rt][cc][i];
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * srt + 4 * g + i;
+        sf[(size_t)row * DV + vcol0 + 16 * (sv0 + j) + tr] = Sacc[j][i];
+      }
   }
 }
 
@@ -306,6 +316,13 @@ template <int DK, int DV, typename TOut>
 hipError_t launch_state_t(const PrefillArgs& a, const unsigned char* img, const int32_t* chunk_off) {
   using L = StatePlan<DK>;
   auto kern = prefill_state_kernel<DK, DV, TOut>;
+  static bool attr_set = false;  // per instantiation; idempotent if raced
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::total);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   const int grid = a.n_seq * a.H * (DV / BV);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH_S), L::total, (hipStream_t)a.stream, img, chunk_off,
                      a.cu_seqlens, a.initial_state, a.final_state, (TOut*)a.o, a.n_seq, a.T, a.H);
