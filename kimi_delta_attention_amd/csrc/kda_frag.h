@@ -162,5 +162,12 @@ __device__ __forceinline__ const T* frame_ptr(const unsigned char* base, int f, 
   return reinterpret_cast<const T*>(base + (size_t)f * 1024 + 16 * lane);
 }
 
+// Streaming store of one fragment into an image: written once, read by the
+// next kernel, so it bypasses the caches (non-temporal).
+template <typename T>
+__device__ __forceinline__ void put_frame(unsigned char* base, int f, int lane, const T& v) {
+  __builtin_nontemporal_store(v, frame_ptr<T>(base, f, lane));
+}
+
 }  // namespace frag
 }  // namespace kda

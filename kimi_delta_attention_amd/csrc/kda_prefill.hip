@@ -42,7 +42,9 @@
 //
 // Precision: bf16 MFMA with split-bf16 operands (x = hi + lo, product
 // hi*hi + hi*lo + lo*hi) everywhere except A (single pass); U and (Gamma*Q) S
-// split only the side that is not exact in bf16.
+// split only the side that is not exact in bf16, W only the T Diag(b) side
+// (an emulation of every per-product choice against the fp64 recurrence, over
+// the gate regimes of the tests, set this policy).
 #include "kda_common.h"
 #include "kda_frag.h"
 #include "kda_internal.h"
@@ -60,7 +62,7 @@ using namespace frag;
 //   solve:        AF, AF2, TF, and the per-wave scratch SCR in the MQ0 region
 //   T*b, V:       TB (T Diag(b), split) and VS (V slice) over MQ0 / MQ1
 //   serial:       ST (state, split), PT (P, split), KT (Ktil, split)
-// GK ((Gamma*K), split, [token][channel]) and QT ((Gamma*Q), [token][position])
+// GK ((Gamma*K), bf16, [token][channel]) and QT ((Gamma*Q), [token][position])
 // live from operand build to their last product; ES / GC / BS are small.  VW is
 // the width of the staged V block (the 64-wide slice, or all of Dv when the
 // kernel runs as the first pass of the two-pass schedule).
@@ -78,7 +80,7 @@ struct Plan {
   static constexpr int m1 = RT > 5 * AF ? RT : 5 * AF;
   static constexpr int m2 = endB > endC ? endB : endC;
   static constexpr int R0 = m1 > m2 ? m1 : m2;
-  static constexpr int GK = CH * ldG * 2 * 2, QT = CH * ldQ * 2;
+  static constexpr int GK = CH * ldG * 2, QT = CH * ldQ * 2;
   static constexpr int oGK = R0, oQT = oGK + GK, oES = oQT + QT, oGC = oES + 4 * DK * 4,
                        oBS = oGC + DK * 4, total = oBS + CH * 4;
   static_assert(total <= 163840, "LDS budget (160 KiB)");
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
 
     // ---- operands for this wave's channels.  Registers: KL = k*P and QL = q*P
     // (split), the B operands of A^T and Mqk^T; Ktil (split) until it is stored.
-    // LDS: RT rows of this tile for row tiles mm >= w, GK = k*Gamma (split,
+    // LDS: RT rows of this tile for row tiles mm >= w, GK = k*Gamma (bf16,
     // [token][channel]), QT = q*Gamma ([token][position]).
     bf16x8 kl[NKH], qlh[NKH], qll[NKH], kth[NKH], ktl[NKH];
 #pragma unroll
@@ -374,10 +376,13 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       }
       split8(y, qlh[kk], qll[kk]);
       split8(kt, kth[kk], ktl[kk]);
-      *reinterpret_cast<bf16x8*>(QT + r * ldQ + 32 * kb + 8 * g) = qt8;
+      // (Gamma*Q) at operand positions 32kb + 8g.. of token r: the first pass
+      // writes it as this lane's fragment of the image, the fused kernel stages it
+      if constexpr (PREP) put_frame(im, IM::q_frame(w, kb), lane_x, qt8);
+      else *reinterpret_cast<bf16x8*>(QT + r * ldQ + 32 * kb + 8 * g) = qt8;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
-        st_split4(GK + r * ldG + 32 * kb + 16 * hf + 4 * g, loG, gk + 4 * hf);
+        st_bf16x4(GK + r * ldG + 32 * kb + 16 * hf + 4 * g, gk + 4 * hf);
       if (w == 0 && tr == 0) {
         float gc[8];
 #pragma unroll
@@ -413,7 +418,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       load_part(nxt, in, 1);
     }
     if constexpr (PREP) {
-      if (tid < DK) reinterpret_cast<float*>(im + IM::g_off)[tid] = GC[tid];
+      if (tid < DK) __builtin_nontemporal_store(GC[tid], reinterpret_cast<float*>(im + IM::g_off) + tid);
     }
 
     // ---- A^T and Mqk^T tiles (j in tile n, r in tile w), n = 0..w, over this
@@ -432,13 +437,6 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
         const bf16x8 al = frag_ld(RT + loR, ldR, row, 32 * kb, g);
         accA[n] = mfma_bf16(ah, kl[kk], accA[n]);
         accM[n] = mma_ab(ah, al, qlh[kk], qll[kk], accM[n]);
-      }
-    }
-    if constexpr (PREP) {  // (Gamma*Q) operand of this tile, this wave's channel half
-#pragma unroll
-      for (int kk = 0; kk < NKH; ++kk) {
-        const int kb = NKH * hh + kk;
-        *frame_ptr<bf16x8>(im, IM::q_frame(w, kb), lane_x) = frag_ld(QT, ldQ, r, 32 * kb, g);
       }
     }
     __syncthreads();  // RT reads done; the partials overwrite it
@@ -479,8 +477,8 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       if (hh == 0) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          *frame_ptr<bf16x8>(im, IM::m_frame(w, kb, 0), lane_x) = mqh[kb];
-          *frame_ptr<bf16x8>(im, IM::m_frame(w, kb, 1), lane_x) = mql[kb];
+          put_frame(im, IM::m_frame(w, kb, 0), lane_x, mqh[kb]);
+          put_frame(im, IM::m_frame(w, kb, 1), lane_x, mql[kb]);
         }
       }
     }
@@ -590,9 +588,11 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (kb > (w >> 1)) continue;
+          // split T Diag(b) only: (Gamma*K) single-rounded is within the error
+          // budget of this product, the T side is not
           const bf16x8 ah = frag_tr(GK, ldG, 16 * ct, 32 * kb + 8 * g, 32 * kb + 8 * g + 4, tr);
-          const bf16x8 al = frag_tr(GK + loG, ldG, 16 * ct, 32 * kb + 8 * g, 32 * kb + 8 * g + 4, tr);
-          acc = mma_ab(ah, al, tbh[kb], tbl[kb], acc);
+          acc = mfma_bf16(ah, tbh[kb], acc);
+          acc = mfma_bf16(ah, tbl[kb], acc);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -621,12 +621,12 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       // Ktil^T P, one 16-row state tile per wave
 #pragma unroll
       for (int kbl = 0; kbl < NCTW / 2; ++kbl) {
-        *frame_ptr<bf16x8>(im, IM::w_frame(w, NKH * hh + kbl, 0), lane_x) = wh[kbl];
-        *frame_ptr<bf16x8>(im, IM::w_frame(w, NKH * hh + kbl, 1), lane_x) = wl[kbl];
+        put_frame(im, IM::w_frame(w, NKH * hh + kbl, 0), lane_x, wh[kbl]);
+        put_frame(im, IM::w_frame(w, NKH * hh + kbl, 1), lane_x, wl[kbl]);
       }
 #pragma unroll
       for (int c = 0; c < NUT; ++c)
-        *frame_ptr<floatx4>(im, IM::u_frame(w, NUT * hh + c), lane_x) = accU[c];
+        put_frame(im, IM::u_frame(w, NUT * hh + c), lane_x, accU[c]);
 #pragma unroll
       for (int kk = 0; kk < NKH; ++kk) {
         const int kb = NKH * hh + kk;
@@ -644,10 +644,10 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       if (w8 < NCHT) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          *frame_ptr<bf16x8>(im, IM::k_frame(w8, kb, 0), lane_x) =
-              frag_tr(KT, ldG, 16 * w8, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g, tr);
-          *frame_ptr<bf16x8>(im, IM::k_frame(w8, kb, 1), lane_x) =
-              frag_tr(KT + loG, ldG, 16 * w8, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g, tr);
+          put_frame(im, IM::k_frame(w8, kb, 0), lane_x,
+                    frag_tr(KT, ldG, 16 * w8, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g, tr));
+          put_frame(im, IM::k_frame(w8, kb, 1), lane_x,
+                    frag_tr(KT + loG, ldG, 16 * w8, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g, tr));
         }
       }
       cur = nxt;

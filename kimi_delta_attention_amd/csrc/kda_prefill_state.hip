@@ -110,12 +110,12 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       }
   }
 
-  // Operands of one chunk.  OpsA (W and Gamma*Q of this wave's channel half,
-  // U of its value half; needed first) is fetched one chunk ahead into a second
-  // register set; OpsB (Mqk of tile w, Ktil of the state rows, Gamma_C; needed
-  // last) at the start of its own chunk.  Every fetch is unconditional (the
-  // last chunk refetches itself) so that the waits the compiler places for
-  // OpsB never have to cover the OpsA fetch issued after it.
+  // Operands of one chunk: OpsA (W and Gamma*Q of this wave's channel half, U
+  // of its value half; needed first) and OpsB (Mqk of tile w, Ktil of the state
+  // rows, Gamma_C; needed last).  Both are fetched one chunk ahead into second
+  // register sets, OpsB at the start of a chunk and OpsA after its first
+  // barrier.  Every fetch is unconditional (the last chunk refetches itself) so
+  // that the compiler's waits for one group never have to cover the other.
   struct OpsA {
     bf16x8 wh[NKH], wl[NKH], qf[NKH];
     floatx4 u[2];
@@ -156,10 +156,14 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
 
   const int nch = (int)((len + CH - 1) / CH);
   OpsA op;
-  if (nch > 0) load_a(0, op);
+  OpsB ob;
+  if (nch > 0) {
+    load_a(0, op);
+    load_b(0, ob);
+  }
   for (int c = 0; c < nch; ++c) {
-    OpsB ob;
-    load_b(c, ob);
+    OpsB nb;
+    load_b(c + 1 < nch ? c + 1 : c, nb);
     int lane_x = lane;
     __asm__ volatile("" : "+v"(lane_x));
     const int tr = lane_x & 15;
@@ -260,6 +264,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
         Sacc[j] = mma_ab(ob.kh[kb], ob.kl[kb], bh, bl, Sacc[j]);
       }
     }
+    ob = nb;
     __syncthreads();  // PT, ST and the partial sums are read before the next chunk rewrites them
   }
 
