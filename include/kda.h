@@ -50,15 +50,18 @@
  * matrix) and a short state-dependent remainder ("Kimi Delta Attention 完全拆解",
  * section "chunk 内并行、chunk 间递推").  Fused: one kernel, one workgroup per
  * (sequence, head, 64-wide value slice) walks its chunks and does both.
- * Two-pass: a first kernel does the state-independent work once per
- * (chunk, head) over the whole device and leaves per-chunk operands in the
- * caller's workspace; a second kernel runs the recurrence over chunks.  The
- * two-pass schedule runs when the call passes a workspace of at least
+ * Two-pass: the packed token axis is cut into windows of 4096 tokens; for each
+ * window a first kernel does the state-independent work of the chunks starting
+ * in it, once per (chunk, head) over the whole device, and leaves per-chunk
+ * operands in the caller's workspace, and a second kernel runs the recurrence
+ * over those chunks, carrying the state from window to window.  The two-pass
+ * schedule runs when the call passes a workspace of at least
  * kda_prefill_workspace_size / kda_prefill_varlen_workspace_size bytes (a
- * non-zero value); otherwise the fused kernel runs.  The workspace grows with
- * the number of chunks (about 128.5 KiB per (chunk, head) at Dk = Dv = 128);
- * its contents on return are unspecified.  kda_prefill_two_pass_preferred
- * says which schedule is expected to be faster on the current device.
+ * non-zero value); otherwise the fused kernel runs.  Like the state, the
+ * workspace does not grow with the sequence length (about 8.2 MiB per head for
+ * one sequence at Dk = Dv = 128); its contents on return are unspecified.
+ * kda_prefill_two_pass_preferred says which schedule is expected to be faster
+ * on the current device.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -156,18 +159,20 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
 
 /*
  * kda_prefill_workspace_size -- workspace bytes that enable the two-pass
- * schedule of kda_prefill_chunked for these sizes: B * ceil(T / 64) * H
- * per-chunk operand blocks.  0 when the schedule does not exist for the shape
- * (head dims outside {64, 128}, or more than 2^31 - 1 blocks).  (size_t)-1 for
- * invalid sizes.  Only bf16 inputs use it.
+ * schedule of kda_prefill_chunked for these sizes, independent of T (the state
+ * is fixed-size, "Kimi K3 混合线性注意力": the per-session state does not grow
+ * with length): a chunk table of B + 1 int32, one carried state per
+ * (sequence, head) and the operand blocks of one window, (64 + B) * H of them
+ * (131,584 B each at Dk = Dv = 128).  0 when the schedule does not exist for
+ * the shape (head dims outside {64, 128}, or B <= 0).  (size_t)-1 for invalid
+ * sizes.  Only bf16 inputs use it.
  */
 size_t kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv, int chunk);
 
 /*
  * kda_prefill_varlen_workspace_size -- as above for kda_prefill_varlen with N
- * packed sequences of total_tokens tokens in all: a chunk table of N + 1
- * int32 plus (ceil(total_tokens / 64) + N) * H operand blocks, enough for any
- * split of the tokens into N sequences.
+ * packed sequences (any total_tokens, any split of them): the same layout
+ * with B = N.
  */
 size_t kda_prefill_varlen_workspace_size(int N, int total_tokens, int H, int Dk, int Dv,
                                          int chunk);
@@ -179,8 +184,8 @@ size_t kda_prefill_varlen_workspace_size(int N, int total_tokens, int H, int Dk,
  * n_seq * H * Dv / 64 workgroups and repeats the state-independent work for
  * each 64-wide value slice; the two-pass schedule wins when that grid is below
  * about twice the compute-unit count and the sequences are at least 4 chunks
- * long on average.  It is preferred only while its workspace is at most 1/16
- * of device memory and 16 GiB.
+ * long on average, and only while its workspace is at most 1/16 of device
+ * memory and 16 GiB.
  */
 int kda_prefill_two_pass_preferred(kda_dtype qkv_dtype, int n_seq, int total_tokens, int H, int Dk,
                                    int Dv);

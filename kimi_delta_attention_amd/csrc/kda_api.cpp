@@ -70,13 +70,13 @@ const char* kda_last_error_message(void) { return g_msg; }
 
 size_t kda_prefill_workspace_size(int B, int T, int H, int Dk, int Dv, int chunk) {
   if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || chunk != 64) return (size_t)-1;
-  return kda::prefill_two_pass_bytes(false, B, T, H, Dk, Dv);
+  return kda::prefill_two_pass_bytes(B, H, Dk, Dv);
 }
 
 size_t kda_prefill_varlen_workspace_size(int N, int total_tokens, int H, int Dk, int Dv,
                                          int chunk) {
   if (N < 0 || total_tokens < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || chunk != 64) return (size_t)-1;
-  return kda::prefill_two_pass_bytes(true, N, total_tokens, H, Dk, Dv);
+  return kda::prefill_two_pass_bytes(N, H, Dk, Dv);
 }
 
 int kda_prefill_two_pass_preferred(kda_dtype qkv_dtype, int n_seq, int total_tokens, int H, int Dk,

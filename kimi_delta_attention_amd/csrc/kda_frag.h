@@ -162,6 +162,34 @@ __device__ __forceinline__ const T* frame_ptr(const unsigned char* base, int f, 
   return reinterpret_cast<const T*>(base + (size_t)f * 1024 + 16 * lane);
 }
 
+// Number of 64-token chunks, over all sequences in order, that start before
+// packed token `tok`.  Dense: n_seq sequences of T tokens back to back (cu
+// NULL).  Packed: sequence s spans tokens cu[s]..cu[s+1]-1 and its chunks are
+// numbered from off[s] (the chunk table).  Chunk starts increase with the chunk
+// index, so the chunks starting in [a, b) are chunks_before(a)..chunks_before(b)-1.
+__device__ __forceinline__ int chunks_before(long long tok, const int32_t* cu, const int32_t* off,
+                                             int n_seq, int T) {
+  if (tok <= 0 || n_seq <= 0) return 0;
+  if (!cu) {
+    const int nch = (T + CH - 1) / CH;
+    const long long s = tok / T;
+    if (s >= n_seq) return n_seq * nch;
+    const long long c = (tok - s * T + CH - 1) / CH;
+    return (int)s * nch + (int)(c < nch ? c : nch);
+  }
+  if (tok >= cu[n_seq]) return off[n_seq];
+  int lo = 0, hi = n_seq - 1;  // last sequence starting at or before tok
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= tok) lo = mid;
+    else hi = mid - 1;
+  }
+  const int nch = off[lo + 1] - off[lo];
+  long long c = (tok - cu[lo] + CH - 1) / CH;
+  if (c < 0) c = 0;
+  return off[lo] + (int)(c < nch ? c : nch);
+}
+
 // Streaming store of one fragment into an image: written once, read by the
 // next kernel, so it bypasses the caches (non-temporal).
 template <typename T>

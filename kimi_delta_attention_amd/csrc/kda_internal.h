@@ -39,16 +39,19 @@ hipError_t launch_prefill(const PrefillArgs& a);      // dispatch (kda_prefill.h
 hipError_t launch_prefill_f32(const PrefillArgs& a);  // fp32 inputs (kda_prefill_f32.hip)
 bool prefill_supported(bool qkv_bf16, int Dk, int Dv);
 
-// Two-pass bf16 prefill.  `tokens` is T per sequence (dense) or the packed
-// total (varlen).  Workspace bytes it needs (0 if unavailable for the shape),
-// and whether it is expected to beat the fused kernel on the current device.
-size_t prefill_two_pass_bytes(bool varlen, int n_seq, long long tokens, int H, int Dk, int Dv);
+// Two-pass bf16 prefill.  Workspace bytes it needs (0 if unavailable for the
+// shape; independent of the sequence length), and whether it is expected to
+// beat the fused kernel on the current device (`tokens`: packed total).
+size_t prefill_two_pass_bytes(int n_seq, int H, int Dk, int Dv);
 bool prefill_two_pass_preferred(int n_seq, long long tokens, int H, int Dk, int Dv);
 // (kda_prefill_state.hip) operand-image bytes per (chunk, head); the state
-// pass; the chunk table of packed sequences (clamped to `cap` chunks).
+// pass over one window of packed tokens [tok_lo, tok_hi) (state read from the
+// initial state for a sequence's first chunk, else from `carry`, and written
+// to `carry`); the chunk table of packed sequences (clamped to `cap` chunks).
 size_t prefill_image_bytes(int Dk, int Dv);
 hipError_t launch_prefill_state(const PrefillArgs& a, const unsigned char* img,
-                                const int32_t* chunk_off);
+                                const int32_t* chunk_off, float* carry, long long tok_lo,
+                                long long tok_hi, int cap);
 hipError_t launch_chunk_table(const int32_t* cu_seqlens, int n_seq, int cap, int32_t* chunk_off,
                               void* stream);
 

@@ -53,6 +53,7 @@ namespace kda {
 namespace {
 
 constexpr int NTH = 512;  // 8 waves
+constexpr int WIN_CHUNKS = 64;  // two-pass window: 64 chunks of packed tokens
 
 using namespace frag;
 
@@ -92,16 +93,19 @@ struct Plan {
 
 // PREP_DV == 0: the fused kernel (one workgroup per (sequence, head, value
 // slice), state carried across chunks).  PREP_DV == Dv: the first pass of the
-// two-pass schedule; a persistent grid walks (chunk, head) items, computes
-// everything that does not depend on the state and writes it as operand images
-// (Images<DK, Dv>) for the state pass.
+// two-pass schedule for one window of packed tokens [tok_lo, tok_hi); a
+// persistent grid walks the (chunk, head) items of the chunks starting in the
+// window (at most `cap` chunks are stored), computes everything that does not
+// depend on the state and writes it as operand images (Images<DK, Dv>),
+// window-relative item (chunk - first chunk of the window) * H + head.
 template <int DK, typename TOut, int PREP_DV>
 __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* __restrict__ s_init, float* __restrict__ s_final, TOut* __restrict__ o,
     const int32_t* __restrict__ cu_seqlens, int n_seq, int T, int H, int DV_,
-    unsigned char* __restrict__ img, const int32_t* __restrict__ chunk_off, int n_items) {
+    unsigned char* __restrict__ img, const int32_t* __restrict__ chunk_off, long long tok_lo,
+    long long tok_hi, int cap) {
   constexpr bool PREP = PREP_DV != 0;
   using L = Plan<DK, PREP ? PREP_DV : BV>;
   using IM = Images<DK, PREP ? PREP_DV : 64>;
@@ -193,12 +197,16 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     int nv, hd, item;
     long long c0;
   };
+  int ci_lo = 0, n_items = 0;
   if constexpr (PREP) {
-    if (n_items < 0) n_items = chunk_off[n_seq] * H;  // packed sequences: count on the device
+    ci_lo = chunks_before(tok_lo, cu_seqlens, chunk_off, n_seq, T);
+    int nc = chunks_before(tok_hi, cu_seqlens, chunk_off, n_seq, T) - ci_lo;
+    if (nc > cap) nc = cap;  // reached only if cu_seqlens is not monotone
+    n_items = nc > 0 ? nc * H : 0;
   }
   auto item_desc = [&](int it, Desc& d) {
-    const int ci = it / H;
-    d.hd = it - ci * H;
+    const int ci = ci_lo + it / H;
+    d.hd = it - (ci - ci_lo) * H;
     d.item = it;
     long long st, ln, cc;
     if (chunk_off) {
@@ -815,15 +823,15 @@ hipError_t launch_fused(const PrefillArgs& a) {
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH), L::total, (hipStream_t)a.stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.alpha, a.beta,
                      a.initial_state, a.final_state, (TOut*)a.o, a.cu_seqlens, a.n_seq, a.T, a.H,
-                     a.Dv, (unsigned char*)nullptr, (const int32_t*)nullptr, 0);
+                     a.Dv, (unsigned char*)nullptr, (const int32_t*)nullptr, 0LL, 0LL, 0);
   return hipGetLastError();
 }
 
-// First pass: a persistent grid of at most one workgroup per compute unit walks
-// the (chunk, head) items; n_items < 0 means "count them on the device" (packed).
+// First pass over one window: a persistent grid of at most one workgroup per
+// compute unit walks the window's (chunk, head) items.
 template <int DK, int DV>
 hipError_t launch_first_pass(const PrefillArgs& a, unsigned char* img, const int32_t* chunk_off,
-                             int n_items, int grid) {
+                             long long tok_lo, long long tok_hi, int cap, int grid) {
   using L = Plan<DK, DV>;
   auto kern = prefill_bf16_kernel<DK, float, DV>;
   static bool attr_set = false;
@@ -834,7 +842,7 @@ hipError_t launch_first_pass(const PrefillArgs& a, unsigned char* img, const int
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH), L::total, (hipStream_t)a.stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.alpha, a.beta,
                      (const float*)nullptr, (float*)nullptr, (float*)nullptr, a.cu_seqlens,
-                     a.n_seq, a.T, a.H, DV, img, chunk_off, n_items);
+                     a.n_seq, a.T, a.H, DV, img, chunk_off, tok_lo, tok_hi, cap);
   return hipGetLastError();
 }
 
@@ -852,6 +860,9 @@ int device_cus() {
 }
 
 size_t table_bytes(int n_seq) { return ((size_t)(n_seq + 1) * 4 + 255) / 256 * 256; }
+size_t carry_bytes(int n_seq, int H, int Dk, int Dv) {
+  return ((size_t)n_seq * H * Dk * Dv * 4 + 255) / 256 * 256;
+}
 
 }  // namespace
 
@@ -861,12 +872,17 @@ bool prefill_supported(bool qkv_bf16, int Dk, int Dv) {
   return Dk == 64;  // fp32 inputs: the fp32-MFMA kernel, Dk = 64
 }
 
-size_t prefill_two_pass_bytes(bool varlen, int n_seq, long long tokens, int H, int Dk, int Dv) {
-  if (n_seq <= 0 || tokens < 0 || H <= 0 || !prefill_supported(true, Dk, Dv)) return 0;
-  const long long chunks = varlen ? (tokens + CH - 1) / CH + n_seq
-                                  : (long long)n_seq * ((tokens + CH - 1) / CH);
-  if (chunks * H > 0x7fffffffLL) return 0;
-  return (varlen ? table_bytes(n_seq) : 0) + (size_t)chunks * H * prefill_image_bytes(Dk, Dv);
+// Workspace of the two-pass schedule: the chunk table (packed calls), a state
+// carried from window to window when the caller passes no final_state, and the
+// operand blocks of one window -- at most WIN_CHUNKS + n_seq chunks start in a
+// window of WIN_CHUNKS * 64 packed tokens (one partial chunk per sequence).
+// Independent of the sequence length.
+size_t prefill_two_pass_bytes(int n_seq, int H, int Dk, int Dv) {
+  if (n_seq <= 0 || H <= 0 || !prefill_supported(true, Dk, Dv)) return 0;
+  const long long items = (long long)(WIN_CHUNKS + n_seq) * H;
+  if (items > 0x7fffffffLL) return 0;
+  return table_bytes(n_seq) + carry_bytes(n_seq, H, Dk, Dv) +
+         (size_t)items * prefill_image_bytes(Dk, Dv);
 }
 
 size_t device_mem() {
@@ -891,7 +907,7 @@ bool prefill_two_pass_preferred(int n_seq, long long tokens, int H, int Dk, int 
   // stays within 1/16 of device memory (and 16 GiB).
   const long long grid = (long long)n_seq * H * (Dv / BV);
   if (!(grid < 2LL * device_cus() && tokens / n_seq >= 4 * CH)) return false;
-  const size_t need = prefill_two_pass_bytes(true, n_seq, tokens, H, Dk, Dv);
+  const size_t need = prefill_two_pass_bytes(n_seq, H, Dk, Dv);
   size_t cap = device_mem() / 16;
   if (cap == 0 || cap > (size_t(16) << 30)) cap = size_t(16) << 30;
   return need > 0 && need <= cap;
@@ -900,37 +916,43 @@ bool prefill_two_pass_preferred(int n_seq, long long tokens, int H, int Dk, int 
 hipError_t launch_prefill(const PrefillArgs& a) {
   if (!a.qkv_bf16) return launch_prefill_f32(a);
   const bool varlen = a.cu_seqlens != nullptr;
-  const long long tokens = a.T;  // per sequence (dense) or in total (packed)
-  const size_t need = prefill_two_pass_bytes(varlen, a.n_seq, tokens, a.H, a.Dk, a.Dv);
-  if (need == 0 || !a.workspace || a.workspace_bytes < need || tokens == 0) {
+  // packed tokens in all (dense: n_seq sequences of T tokens back to back)
+  const long long total = varlen ? (long long)a.T : (long long)a.n_seq * a.T;
+  const size_t need = prefill_two_pass_bytes(a.n_seq, a.H, a.Dk, a.Dv);
+  if (need == 0 || !a.workspace || a.workspace_bytes < need || total == 0) {
     if (a.Dk == 128) return a.o_bf16 ? launch_fused<128, bf16>(a) : launch_fused<128, float>(a);
     return a.o_bf16 ? launch_fused<64, bf16>(a) : launch_fused<64, float>(a);
   }
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  int32_t* chunk_off = nullptr;
-  unsigned char* img = ws;
-  int n_items = -1;
+  int32_t* chunk_off = varlen ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  float* scratch = reinterpret_cast<float*>(ws + table_bytes(a.n_seq));
+  unsigned char* img = ws + table_bytes(a.n_seq) + carry_bytes(a.n_seq, a.H, a.Dk, a.Dv);
+  float* carry = a.final_state ? a.final_state : scratch;
+  const int cap = WIN_CHUNKS + a.n_seq;
   if (varlen) {
-    chunk_off = reinterpret_cast<int32_t*>(ws);
-    img = ws + table_bytes(a.n_seq);
-    const int cap = (int)((tokens + CH - 1) / CH + a.n_seq);
-    if (hipError_t e = launch_chunk_table(a.cu_seqlens, a.n_seq, cap, chunk_off, a.stream);
+    const long long all = (total + CH - 1) / CH + a.n_seq;
+    if (hipError_t e = launch_chunk_table(a.cu_seqlens, a.n_seq,
+                                          (int)(all < 0x7fffffffLL ? all : 0x7fffffffLL),
+                                          chunk_off, a.stream);
         e != hipSuccess)
       return e;
-  } else {
-    n_items = (int)((long long)a.n_seq * ((a.T + CH - 1) / CH) * a.H);
   }
   int grid = device_cus();
-  if (n_items >= 0 && n_items < grid) grid = n_items;
-  hipError_t e;
-  if (a.Dk == 128)
-    e = a.Dv == 128 ? launch_first_pass<128, 128>(a, img, chunk_off, n_items, grid)
-                    : launch_first_pass<128, 64>(a, img, chunk_off, n_items, grid);
-  else
-    e = a.Dv == 128 ? launch_first_pass<64, 128>(a, img, chunk_off, n_items, grid)
-                    : launch_first_pass<64, 64>(a, img, chunk_off, n_items, grid);
-  if (e != hipSuccess) return e;
-  return launch_prefill_state(a, img, chunk_off);
+  if ((long long)cap * a.H < grid) grid = cap * a.H;
+  const long long win = (long long)WIN_CHUNKS * CH;
+  for (long long t0 = 0; t0 < total; t0 += win) {
+    hipError_t e;
+    if (a.Dk == 128)
+      e = a.Dv == 128 ? launch_first_pass<128, 128>(a, img, chunk_off, t0, t0 + win, cap, grid)
+                      : launch_first_pass<128, 64>(a, img, chunk_off, t0, t0 + win, cap, grid);
+    else
+      e = a.Dv == 128 ? launch_first_pass<64, 128>(a, img, chunk_off, t0, t0 + win, cap, grid)
+                      : launch_first_pass<64, 64>(a, img, chunk_off, t0, t0 + win, cap, grid);
+    if (e != hipSuccess) return e;
+    e = launch_prefill_state(a, img, chunk_off, carry, t0, t0 + win, cap);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace kda

@@ -8,9 +8,12 @@
 //
 //   P  = U - W S,   O = (Gamma*Q) S + Mqk P,   S' = Diag(Gamma_C) S + Ktil^T P
 //
-// This kernel runs that part.  One workgroup owns (sequence, head, 64-wide
-// value slice) and walks the chunks in order with the state slice in MFMA
-// accumulators; its per-chunk operands arrive as register images
+// This kernel runs that part for one window of packed tokens (the chunks that
+// start in it).  One workgroup owns (sequence, head, 64-wide value slice) and
+// walks its chunks of the window in order with the state slice in MFMA
+// accumulators, entering from the initial state (at the sequence's first chunk)
+// or from the carry buffer, and leaving the state in the carry buffer (the
+// caller's final state or workspace); its per-chunk operands arrive as register images
 // (Images<DK, DV>) fetched with coalesced 16-byte loads.  Eight waves; wave
 // (w, hh) fetches only operands no other wave of the workgroup fetches (the
 // per-compute-unit load path, not HBM, limits this pass):
@@ -47,8 +50,8 @@ struct StatePlan {
 template <int DK, int DV, typename TOut>
 __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     const unsigned char* __restrict__ img, const int32_t* __restrict__ chunk_off,
-    const int32_t* __restrict__ cu_seqlens, const float* __restrict__ s_init,
-    float* __restrict__ s_final, TOut* __restrict__ o, int n_seq, int T, int H) {
+    const int32_t* __restrict__ cu_seqlens, const float* s_init, float* carry,
+    TOut* __restrict__ o, int n_seq, int T, int H, long long tok_lo, long long tok_hi, int cap) {
   using L = StatePlan<DK>;
   using IM = Images<DK, DV>;
   constexpr int NKB = DK / 32;
@@ -77,19 +80,32 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
   const int h = (wid / nsl) % H;
   const int seq = wid / (nsl * H);
   long long start, len;
-  int ci0;  // global index of the sequence's first chunk
+  int ci0, nch_seq;  // global index of the sequence's first chunk, its chunk count
   if (cu_seqlens) {
     start = cu_seqlens[seq];
     len = (long long)cu_seqlens[seq + 1] - start;
     ci0 = chunk_off[seq];
-    // the table's chunk count (equal to ceil(len / 64) for monotone offsets)
-    const long long tab = (long long)(chunk_off[seq + 1] - ci0) * CH;
-    if (len > tab) len = tab;
+    nch_seq = chunk_off[seq + 1] - ci0;  // ceil(len / 64) for monotone offsets
   } else {
     start = (long long)seq * T;
     len = T;
-    ci0 = seq * ((T + CH - 1) / CH);
+    nch_seq = (T + CH - 1) / CH;
+    ci0 = seq * nch_seq;
   }
+  if (len > (long long)nch_seq * CH) len = (long long)nch_seq * CH;
+  // this window's chunks of the sequence, [c_lo, c_hi); item slot of chunk c
+  // is ci0 + c - ci_lo, below cap
+  const int ci_lo = chunks_before(tok_lo, cu_seqlens, chunk_off, n_seq, T);
+  auto first_from = [&](long long tok) {
+    long long c = (tok - start + CH - 1) / CH;
+    if (c < 0) c = 0;
+    return (int)(c < nch_seq ? c : nch_seq);
+  };
+  int c_lo = first_from(tok_lo), c_hi = first_from(tok_hi);
+  if (c_lo < ci_lo - ci0) c_lo = ci_lo - ci0;          // reached only for
+  if (c_hi > cap + ci_lo - ci0) c_hi = cap + ci_lo - ci0;  // non-monotone cu_seqlens
+  // an empty sequence hands its initial state through in the first window
+  if (!(c_lo < c_hi || (nch_seq == 0 && tok_lo == 0))) return;
   const int vcol0 = sl * BV;
   const int vh0 = 32 * hh;             // value half of P and o
   const int vt0 = (vcol0 + vh0) / 16;  // its first U tile
@@ -100,7 +116,8 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
   floatx4 Sacc[KVT];
   {
     const int tr = lane & 15, g = lane >> 4;
-    const float* si = s_init ? s_init + ((size_t)seq * H + h) * DK * DV : nullptr;
+    const float* src = c_lo == 0 ? s_init : carry;
+    const float* si = src ? src + ((size_t)seq * H + h) * DK * DV : nullptr;
 #pragma unroll
     for (int j = 0; j < KVT; ++j)
 #pragma unroll
@@ -125,7 +142,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     floatx4 gc;
   };
   auto item_base = [&](int c) -> const unsigned char* {
-    return img + ((size_t)(ci0 + c) * H + h) * IM::bytes;
+    return img + ((size_t)(ci0 + c - ci_lo) * H + h) * IM::bytes;
   };
   auto load_a = [&](int c, OpsA& op) {
     const unsigned char* b = item_base(c);
@@ -154,16 +171,15 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     return reinterpret_cast<floatx4*>(XC + ((((w * 2 + from) * 2 + j) * 2 + part) * 1024) + 16 * ln);
   };
 
-  const int nch = (int)((len + CH - 1) / CH);
   OpsA op;
   OpsB ob;
-  if (nch > 0) {
-    load_a(0, op);
-    load_b(0, ob);
+  if (c_lo < c_hi) {
+    load_a(c_lo, op);
+    load_b(c_lo, ob);
   }
-  for (int c = 0; c < nch; ++c) {
+  for (int c = c_lo; c < c_hi; ++c) {
     OpsB nb;
-    load_b(c + 1 < nch ? c + 1 : c, nb);
+    load_b(c + 1 < c_hi ? c + 1 : c, nb);
     int lane_x = lane;
     __asm__ volatile("" : "+v"(lane_x));
     const int tr = lane_x & 15;
@@ -184,7 +200,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     }
     __syncthreads();
     OpsA nx;
-    load_a(c + 1 < nch ? c + 1 : c, nx);
+    load_a(c + 1 < c_hi ? c + 1 : c, nx);
 
     // ---- W S and (Gamma*Q) S over this wave's channel half, all 64 values
     floatx4 accW[NVT], accO[NVT];
@@ -268,9 +284,9 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     __syncthreads();  // PT, ST and the partial sums are read before the next chunk rewrites them
   }
 
-  if (s_final) {
+  {
     const int tr = lane & 15, g = lane >> 4;
-    float* sf = s_final + ((size_t)seq * H + h) * DK * DV;
+    float* sf = carry + ((size_t)seq * H + h) * DK * DV;
 #pragma unroll
     for (int j = 0; j < KVT; ++j)
 #pragma unroll
@@ -318,7 +334,8 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restr
 }
 
 template <int DK, int DV, typename TOut>
-hipError_t launch_state_t(const PrefillArgs& a, const unsigned char* img, const int32_t* chunk_off) {
+hipError_t launch_state_t(const PrefillArgs& a, const unsigned char* img, const int32_t* chunk_off,
+                          float* carry, long long tok_lo, long long tok_hi, int cap) {
   using L = StatePlan<DK>;
   auto kern = prefill_state_kernel<DK, DV, TOut>;
   static bool attr_set = false;  // per instantiation; idempotent if raced
@@ -330,26 +347,29 @@ hipError_t launch_state_t(const PrefillArgs& a, const unsigned char* img, const 
   }
   const int grid = a.n_seq * a.H * (DV / BV);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH_S), L::total, (hipStream_t)a.stream, img, chunk_off,
-                     a.cu_seqlens, a.initial_state, a.final_state, (TOut*)a.o, a.n_seq, a.T, a.H);
+                     a.cu_seqlens, a.initial_state, carry, (TOut*)a.o, a.n_seq, a.T, a.H, tok_lo,
+                     tok_hi, cap);
   return hipGetLastError();
 }
 
 template <int DK, int DV>
-hipError_t launch_state_d(const PrefillArgs& a, const unsigned char* img, const int32_t* chunk_off) {
-  return a.o_bf16 ? launch_state_t<DK, DV, bf16>(a, img, chunk_off)
-                  : launch_state_t<DK, DV, float>(a, img, chunk_off);
+hipError_t launch_state_d(const PrefillArgs& a, const unsigned char* img, const int32_t* chunk_off,
+                          float* carry, long long tok_lo, long long tok_hi, int cap) {
+  return a.o_bf16 ? launch_state_t<DK, DV, bf16>(a, img, chunk_off, carry, tok_lo, tok_hi, cap)
+                  : launch_state_t<DK, DV, float>(a, img, chunk_off, carry, tok_lo, tok_hi, cap);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_state(const PrefillArgs& a, const unsigned char* img,
-                                const int32_t* chunk_off) {
+                                const int32_t* chunk_off, float* carry, long long tok_lo,
+                                long long tok_hi, int cap) {
   if (a.Dk == 128) {
-    return a.Dv == 128 ? launch_state_d<128, 128>(a, img, chunk_off)
-                       : launch_state_d<128, 64>(a, img, chunk_off);
+    return a.Dv == 128 ? launch_state_d<128, 128>(a, img, chunk_off, carry, tok_lo, tok_hi, cap)
+                       : launch_state_d<128, 64>(a, img, chunk_off, carry, tok_lo, tok_hi, cap);
   }
-  return a.Dv == 128 ? launch_state_d<64, 128>(a, img, chunk_off)
-                     : launch_state_d<64, 64>(a, img, chunk_off);
+  return a.Dv == 128 ? launch_state_d<64, 128>(a, img, chunk_off, carry, tok_lo, tok_hi, cap)
+                     : launch_state_d<64, 64>(a, img, chunk_off, carry, tok_lo, tok_hi, cap);
 }
 
 hipError_t launch_chunk_table(const int32_t* cu_seqlens, int n_seq, int cap, int32_t* chunk_off,

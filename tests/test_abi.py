@@ -45,18 +45,21 @@ def test_status_strings():
 
 
 def test_workspace_sizes():
-    """Two-pass workspace: one operand block per (chunk, head), a block holding
-    the frames of W, (Gamma*Q), Mqk, Ktil^T and U plus Gamma_C, rounded to 256 B;
-    packed calls add a chunk table and budget one partial chunk per sequence."""
+    """Two-pass workspace: a chunk table (B + 1 int32), one carried fp32 state per
+    (sequence, head), and the operand blocks of one 4096-token window, (64 + B) * H
+    of them; each block holds the frames of W, (Gamma*Q), Mqk, Ktil^T and U plus
+    Gamma_C, rounded to 256 B.  Like the state, it does not depend on T."""
     frames = {(128, 128): 4 * 4 * 2 + 4 * 4 + 16 + 8 * 4 + 4 * 8,
               (64, 64): 4 * 2 * 2 + 4 * 2 + 16 + 4 * 4 + 4 * 4}
+    up = lambda x: -(-x // 256) * 256
     for (dk, dv), f in frames.items():
-        blk = -(-(f * 1024 + dk * 4) // 256) * 256
-        for B, T, H in ((1, 1, 1), (1, 8192, 96), (3, 200, 2)):
-            assert kda.workspace_size(B, T, H, dk, dv) == B * -(-T // 64) * H * blk
-        n, tot, h = 16, 129161, 96
-        table = -(-(n + 1) * 4 // 256) * 256
-        assert _lib.varlen_workspace_size(n, tot, h, dk, dv) == table + (-(-tot // 64) + n) * h * blk
+        blk = up(f * 1024 + dk * 4)
+        for B, H in ((1, 1), (1, 96), (3, 2), (16, 96)):
+            want = up((B + 1) * 4) + up(B * H * dk * dv * 4) + (64 + B) * H * blk
+            sizes = {kda.workspace_size(B, T, H, dk, dv) for T in (1, 256, 8192, 1 << 20)}
+            assert sizes == {want}
+            assert {_lib.varlen_workspace_size(B, tot, H, dk, dv) for tot in (B, 129161, 1 << 30)} \
+                == {want}
     assert kda.workspace_size(1, 256, 96, 128, 128, chunk=32) == ctypes.c_size_t(-1).value
     assert kda.workspace_size(1, 256, 96, 96, 128) == 0          # no two-pass kernel for Dk = 96
     assert kda.workspace_size(0, 256, 96, 128, 128) == 0         # nothing to do

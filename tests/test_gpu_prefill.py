@@ -245,12 +245,12 @@ def test_schedules_agree_bitwise(B, T, H, Dk, Dv):
 
 
 def test_two_pass_workspace_reuse_and_capacity():
-    """A caller-owned workspace serves consecutive calls of different sizes, and
-    the packed bound holds when every sequence ends in a partial chunk."""
+    """One caller-owned workspace (its size does not depend on T) serves calls of
+    different lengths, and the packed layout holds when every sequence ends in a
+    partial chunk."""
     d = dev()
-    big = kda.workspace_size(1, 1024, 4, 128, 128)
-    ws = torch.empty(big, dtype=torch.uint8, device=d)
-    for T in (1024, 70):
+    ws = torch.empty(kda.workspace_size(1, 64, 4, 128, 128), dtype=torch.uint8, device=d)
+    for T in (1024, 70, 9000):
         inp = synth.make_dense(1, T, 4, 128, 128, seed=400 + T, state_std=0.02)
         o1, s1 = _run(inp, d, schedule="fused")
         o2, s2 = kda.prefill_chunked(inp.q.to(d), inp.k.to(d), inp.v.to(d), inp.alpha.to(d),
@@ -267,3 +267,37 @@ def test_two_pass_workspace_reuse_and_capacity():
                                 initial_state=vin.state, schedule="two_pass", workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_two_pass_windows():
+    """Several 4096-token windows: dense sequences longer than a window, packed
+    sequences that start, end or lie entirely inside later windows (and empty
+    ones among them), state handed over in place or not returned at all.  The
+    two-pass result equals the fused kernel bitwise and the oracle within 2e-3."""
+    d = dev()
+    inp = synth.make_dense(2, 5000, 2, 128, 128, seed=501, state_std=0.02)
+    o_ref, s_ref = oracle.recurrent(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
+                                    initial_state=inp.state)
+    o1, s1 = _run(inp, d, schedule="fused")
+    o2, s2 = _run(inp, d, schedule="two_pass")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert rel(o2.cpu(), o_ref) <= TOL_BF16 and rel(s2.cpu(), s_ref) <= TOL_BF16
+    # final state written over the initial state, and no final state at all
+    st = inp.state.to(d).clone()
+    g = [x.to(d) for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta)]
+    o3, _ = kda.prefill_chunked(*g, initial_state=st, final_state=st, schedule="two_pass")
+    o4, none = kda.prefill_chunked(*g, initial_state=inp.state.to(d), final_state=False,
+                                   schedule="two_pass")
+    torch.cuda.synchronize()
+    assert none is None and torch.equal(st, s1) and torch.equal(o3, o1) and torch.equal(o4, o1)
+    lengths = [3000, 0, 2500, 64, 4096, 1, 0, 5000, 130]
+    vin = _varlen_case(lengths, 2, 64, seed=73, d=d)
+    cu = vin.cu_seqlens.cpu().numpy()
+    o_ref, s_ref = oracle.recurrent(vin.q.cpu(), vin.k.cpu(), vin.v.cpu(), vin.alpha.cpu(),
+                                    vin.beta.cpu(), cu_seqlens=cu, initial_state=vin.state.cpu())
+    o1, s1 = _run_varlen(vin, d, "fused")
+    o2, s2 = _run_varlen(vin, d, "two_pass")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert rel(o2.cpu(), o_ref) <= TOL_BF16 and rel(s2.cpu(), s_ref) <= TOL_BF16
