@@ -65,7 +65,7 @@ def measured_traffic(summary: str, sources: list[str]):
         h.update(open(os.path.join(ROOT, f), "rb").read())
     if kv.get("source_sha256") != h.hexdigest():
         return None
-    return float(kv["traffic_bytes_per_launch"])
+    return float(kv["traffic_bytes_per_launch"].split()[0])
 
 
 PREFILL_SOURCES = ["kimi_delta_attention_amd/csrc/kda_prefill.hip",
