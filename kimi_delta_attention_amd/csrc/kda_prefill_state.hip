@@ -13,19 +13,27 @@
 // walks its chunks of the window in order with the state slice in MFMA
 // accumulators, entering from the initial state (at the sequence's first chunk)
 // or from the carry buffer, and leaving the state in the carry buffer (the
-// caller's final state or workspace); its per-chunk operands arrive as register images
-// (Images<DK, DV>) fetched with coalesced 16-byte loads.  Eight waves; wave
-// (w, hh) fetches only operands no other wave of the workgroup fetches (the
-// per-compute-unit load path, not HBM, limits this pass):
-//   W S and (Gamma*Q) S   token tile w, all 64 values, channel half hh; the
-//                         two halves are added through LDS, each wave keeping
-//                         the sum for its value half hh
-//   P, Mqk P, o           token tile w, value half hh
-//   state update          Dk = 128: state rows 16(2w + hh).., all 64 values;
-//                         Dk = 64: rows 16w.., value half hh
-// The fused kernel computes the same products with the same accumulation
-// order (the two channel halves as separate chains, low half first), so both
-// schedules give bitwise the same results.
+// caller's final state or workspace); its per-chunk operands arrive as register
+// images (Images<DK, DV>) fetched with coalesced 16-byte loads, one chunk ahead.
+//
+// Eight waves in two roles, one wave of each role per SIMD.  Token tile w
+// (tokens 16w..16w+15 of the chunk) has a chain wave (waves 0..3), which
+// computes W S and P = U - W S for the tile's 16 tokens, and an output wave
+// (waves 4..7), which computes (Gamma*Q) S and Mqk P and stores o.  Both update
+// a share of the state: Dk = 128, state rows 16(2w + role).., all 64 values;
+// Dk = 64, rows 16w.., value tiles 2 role, 2 role + 1.  Per chunk:
+//   1. every wave writes its state tiles to LDS as the split B operand of
+//      W S and (Gamma*Q) S                                        -- barrier
+//   2. chain: W S (two channel-half chains), P, P to LDS (split);
+//      output: (Gamma*Q) S (two channel-half chains)               -- barrier
+//   3. chain: S = Diag(Gamma_C) S + Ktil^T P on its tiles;
+//      output: o = (Gamma*Q) S + Mqk P, stored; the same state update
+// so the state's dependency chain (W S -> P -> Ktil^T P) shares each SIMD's
+// matrix pipe with independent output work and a chunk costs two barriers.
+// Every wave fetches only the operand frames it uses, and no frame is fetched
+// twice in a workgroup.  The fused kernel computes the same products with the
+// same accumulation order (the two channel halves as separate chains, low half
+// first), so both schedules give bitwise the same results.
 #include "kda_common.h"
 #include "kda_frag.h"
 #include "kda_internal.h"
@@ -40,12 +48,63 @@ constexpr int NTH_S = 512;
 template <int DK>
 struct StatePlan {
   static constexpr int ldS = DK + 8, ldP = CH + 8;
-  static constexpr int ST = BV * ldS * 2 * 2, PT = BV * ldP * 2 * 2;
-  // partial sums handed between the two waves of a tile: [w][from hh][tile j][W, O] frames
-  static constexpr int XC = 4 * 2 * 2 * 2 * 1024;
-  static constexpr int oST = 0, oPT = ST, oXC = ST + PT, total = ST + PT + XC;
+  // o staging of each output wave: 16 rows x 64 values fp32, row stride 80
+  // floats (16-lane groups of the 16-byte accesses hit distinct banks)
+  static constexpr int ldO = BV + 16;
+  static constexpr int ST = BV * ldS * 2 * 2, PT = BV * ldP * 2 * 2, OS = 4 * 16 * ldO * 4;
+  static constexpr int oST = 0, oPT = ST, oOS = ST + PT, total = ST + PT + OS;
   static_assert(total <= 163840, "LDS budget");
+  static_assert(oOS % 16 == 0, "alignment");
 };
+
+// Lane quad transpose: lane b of each group of four lanes holds x[i] = element
+// (i, b) of a 4x4 block and receives element (b, i).  Two exchange steps, over
+// lane bit 0 / element bit 0 and then lane bit 1 / element bit 1, each a DPP
+// quad permutation and a per-lane select.
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ floatx4 quad_transpose(const floatx4& x, int b) {
+  floatx4 z, y;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float t = quad_perm<0xB1>(x[i ^ 1]);  // lanes [1, 0, 3, 2]
+    z[i] = ((b ^ i) & 1) ? t : x[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float t = quad_perm<0x4E>(z[i ^ 2]);  // lanes [2, 3, 0, 1]
+    y[i] = ((b ^ i) & 2) ? t : z[i];
+  }
+  return y;
+}
+
+// Four consecutive o values of one row through a buffer descriptor: a store
+// whose byte offset lies beyond the descriptor's range is dropped by the
+// hardware, which masks the rows past the end of a partial chunk without a
+// branch (non-temporal: o is written once).
+template <typename TOut>
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t rs, int off, const floatx4& y);
+template <>
+__device__ __forceinline__ void store4<float>(__amdgpu_buffer_rsrc_t rs, int off, const floatx4& y) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4v, y), rs, off, 0, 2);
+}
+template <>
+__device__ __forceinline__ void store4<bf16>(__amdgpu_buffer_rsrc_t rs, int off, const floatx4& y) {
+  uint2v u;
+  u[0] = (unsigned)__builtin_bit_cast(unsigned short, (bf16)y[0]) |
+         ((unsigned)__builtin_bit_cast(unsigned short, (bf16)y[1]) << 16);
+  u[1] = (unsigned)__builtin_bit_cast(unsigned short, (bf16)y[2]) |
+         ((unsigned)__builtin_bit_cast(unsigned short, (bf16)y[3]) << 16);
+  __builtin_amdgcn_raw_buffer_store_b64(u, rs, off, 0, 2);
+}
+
+// Waits for every outstanding vector memory access of the wave.  Placed after
+// the fetch in front of a chunk loop, so that the loop is entered with nothing
+// in flight but what the loop body itself issues (the wait counts the compiler
+// derives for the loop then hold on every iteration).
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int DK, int DV, typename TOut>
 __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
@@ -58,18 +117,18 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
   constexpr int NKH = NKB / 2;                   // 32-channel blocks per channel half
   constexpr int NVT = BV / 16;                   // value tiles of the slice
   constexpr int KVT = DK == 128 ? NVT : NVT / 2;  // value tiles of this wave's state rows
-  constexpr int ldS = L::ldS, ldP = L::ldP;
+  constexpr int ldS = L::ldS, ldP = L::ldP, ldO = L::ldO;
   constexpr int loS = BV * ldS, loP = BV * ldP;
 
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* ST = reinterpret_cast<bf16*>(smem + L::oST);
   bf16* PT = reinterpret_cast<bf16*>(smem + L::oPT);
-  unsigned char* XC = smem + L::oXC;
+  float* OS = reinterpret_cast<float*>(smem + L::oOS);
 
   const int tid = threadIdx.x;
   const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hh = w8 >> 2;
-  const int w = w8 & 3;
+  const int role = w8 >> 2;  // 0: chain wave, 1: output wave
+  const int w = w8 & 3;      // token tile
   const int lane = tid & 63;
 
   constexpr int nsl = DV / BV;
@@ -107,11 +166,10 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
   // an empty sequence hands its initial state through in the first window
   if (!(c_lo < c_hi || (nch_seq == 0 && tok_lo == 0))) return;
   const int vcol0 = sl * BV;
-  const int vh0 = 32 * hh;             // value half of P and o
-  const int vt0 = (vcol0 + vh0) / 16;  // its first U tile
-  // state rows and value tiles of the update
-  const int srt = DK == 128 ? 2 * w + hh : w;  // 16-row tile
-  const int sv0 = DK == 128 ? 0 : 2 * hh;      // first value tile (within the slice)
+  const int vt0 = vcol0 / 16;  // first U tile of the slice
+  // state tiles of this wave
+  const int srt = DK == 128 ? 2 * w + role : w;  // 16-row tile
+  const int sv0 = DK == 128 ? 0 : 2 * role;      // first value tile (within the slice)
 
   floatx4 Sacc[KVT];
   {
@@ -127,161 +185,228 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       }
   }
 
-  // Operands of one chunk: OpsA (W and Gamma*Q of this wave's channel half, U
-  // of its value half; needed first) and OpsB (Mqk of tile w, Ktil of the state
-  // rows, Gamma_C; needed last).  Both are fetched one chunk ahead into second
-  // register sets, OpsB at the start of a chunk and OpsA after its first
-  // barrier.  Every fetch is unconditional (the last chunk refetches itself) so
-  // that the compiler's waits for one group never have to cover the other.
-  struct OpsA {
-    bf16x8 wh[NKH], wl[NKH], qf[NKH];
-    floatx4 u[2];
-  };
-  struct OpsB {
-    bf16x8 mh[2], ml[2], kh[2], kl[2];
-    floatx4 gc;
-  };
   auto item_base = [&](int c) -> const unsigned char* {
     return img + ((size_t)(ci0 + c - ci_lo) * H + h) * IM::bytes;
   };
-  auto load_a = [&](int c, OpsA& op) {
-    const unsigned char* b = item_base(c);
-#pragma unroll
-    for (int kk = 0; kk < NKH; ++kk) {
-      op.wh[kk] = *frame_ptr<bf16x8>(b, IM::w_frame(w, NKH * hh + kk, 0), lane);
-      op.wl[kk] = *frame_ptr<bf16x8>(b, IM::w_frame(w, NKH * hh + kk, 1), lane);
-      op.qf[kk] = *frame_ptr<bf16x8>(b, IM::q_frame(w, NKH * hh + kk), lane);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) op.u[j] = *frame_ptr<floatx4>(b, IM::u_frame(w, vt0 + j), lane);
-  };
-  auto load_b = [&](int c, OpsB& op) {
-    const unsigned char* b = item_base(c);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      op.mh[kb] = *frame_ptr<bf16x8>(b, IM::m_frame(w, kb, 0), lane);
-      op.ml[kb] = *frame_ptr<bf16x8>(b, IM::m_frame(w, kb, 1), lane);
-      op.kh[kb] = *frame_ptr<bf16x8>(b, IM::k_frame(srt, kb, 0), lane);
-      op.kl[kb] = *frame_ptr<bf16x8>(b, IM::k_frame(srt, kb, 1), lane);
-    }
-    op.gc = *reinterpret_cast<const floatx4*>(b + IM::g_off + 4 * (16 * srt + 4 * (lane >> 4)));
-  };
-  // partial-sum frames: [w][from hh][tile j][W, O]
-  auto xc = [&](int from, int j, int part, int ln) {
-    return reinterpret_cast<floatx4*>(XC + ((((w * 2 + from) * 2 + j) * 2 + part) * 1024) + 16 * ln);
-  };
-
-  OpsA op;
-  OpsB ob;
-  if (c_lo < c_hi) {
-    load_a(c_lo, op);
-    load_b(c_lo, ob);
-  }
-  for (int c = c_lo; c < c_hi; ++c) {
-    OpsB nb;
-    load_b(c + 1 < c_hi ? c + 1 : c, nb);
-    int lane_x = lane;
-    __asm__ volatile("" : "+v"(lane_x));
-    const int tr = lane_x & 15;
-    const int g = lane_x >> 4;
-    const long long tok0 = start + (long long)c * CH;
-    const int nv = (int)(len - (long long)c * CH < CH ? len - (long long)c * CH : CH);
-
-    // ---- the state as the B operand of W S and (Gamma*Q) S: [value][channel
-    // position], position 32kb + 8g + 4h + i holds channel 32kb + 16h + 4g + i
-    {
-      const int c0r = 16 * srt;
-      const int pos = 32 * (c0r >> 5) + 8 * g + 4 * ((c0r >> 4) & 1);
-#pragma unroll
-      for (int j = 0; j < KVT; ++j) {
-        float x4[4] = {Sacc[j][0], Sacc[j][1], Sacc[j][2], Sacc[j][3]};
-        st_split4(ST + (16 * (sv0 + j) + tr) * ldS + pos, loS, x4);
-      }
-    }
-    __syncthreads();
-    OpsA nx;
-    load_a(c + 1 < c_hi ? c + 1 : c, nx);
-
-    // ---- W S and (Gamma*Q) S over this wave's channel half, all 64 values
-    floatx4 accW[NVT], accO[NVT];
-#pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) {
-      accW[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      accO[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int kk = 0; kk < NKH; ++kk) {
-      const int kb = NKH * hh + kk;
-#pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) {
-        const bf16x8 bh = frag_ld(ST, ldS, 16 * vt + tr, 32 * kb, g);
-        const bf16x8 bl = frag_ld(ST + loS, ldS, 16 * vt + tr, 32 * kb, g);
-        accW[vt] = mma_ab(op.wh[kk], op.wl[kk], bh, bl, accW[vt]);
-        accO[vt] = mfma_bf16(op.qf[kk], bh, accO[vt]);
-        accO[vt] = mfma_bf16(op.qf[kk], bl, accO[vt]);
-      }
-    }
-    // hand the partner's value half over, take its partial sums for ours
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      *xc(hh, j, 0, lane_x) = accW[2 * (1 - hh) + j];
-      *xc(hh, j, 1, lane_x) = accO[2 * (1 - hh) + j];
-    }
-    __syncthreads();
-    floatx4 accP[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const floatx4 pw = *xc(1 - hh, j, 0, lane_x), po = *xc(1 - hh, j, 1, lane_x);
-      const floatx4 mw = accW[2 * hh + j], mo = accO[2 * hh + j];
-      const floatx4 wsum = hh ? pw + mw : mw + pw;  // low channel half first
-      accP[j] = hh ? po + mo : mo + po;             // (Gamma*Q) S, then Mqk P below
-      float pv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pv[i] = op.u[j][i] - wsum[i];
-      // P to LDS as [value][token position]; token 32kb + 16h + 4g + i sits at
-      // position 32kb + 8g + 4h + i (the order of the Mqk^T operand)
-      const int pos = 32 * (w >> 1) + 8 * g + 4 * (w & 1);
-      st_split4(PT + (vh0 + 16 * j + tr) * ldP + pos, loP, pv);
-    }
-    op = nx;
-    __syncthreads();
-
-    // ---- O += Mqk P; store o.  Both token blocks for every tile: the Mqk
-    // frames of blocks after the tile are zero, and a branch here would let the
-    // compiler move their fetch next to this use.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8 bh = frag_ld(PT, ldP, vh0 + 16 * j + tr, 32 * kb, g);
-        const bf16x8 bl = frag_ld(PT + loP, ldP, vh0 + 16 * j + tr, 32 * kb, g);
-        accP[j] = mma_ab(ob.mh[kb], ob.ml[kb], bh, bl, accP[j]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 16 * w + 4 * g + i;
-      if (rr < nv) {
-        TOut* orow = o + ((size_t)(tok0 + rr) * H + h) * DV + vcol0 + vh0 + tr;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) __builtin_nontemporal_store((TOut)accP[j][i], orow + 16 * j);
-      }
-    }
-
-    // ---- S = Diag(Gamma_C) S + Ktil^T P
+  // the state as the B operand of W S and (Gamma*Q) S: [value][channel
+  // position], position 32kb + 8g + 4h + i holds channel 32kb + 16h + 4g + i
+  auto put_state = [&](int g, int tr) {
+    const int c0r = 16 * srt;
+    const int pos = 32 * (c0r >> 5) + 8 * g + 4 * ((c0r >> 4) & 1);
 #pragma unroll
     for (int j = 0; j < KVT; ++j) {
+      float x4[4] = {Sacc[j][0], Sacc[j][1], Sacc[j][2], Sacc[j][3]};
+      st_split4(ST + (16 * (sv0 + j) + tr) * ldS + pos, loS, x4);
+    }
+  };
+  // the fetch index of the chunk after c: the last chunk fetches itself again,
+  // so that every fetch is unconditional
+  auto next_of = [&](int c) { return c + 1 < c_hi ? c + 1 : c; };
+
+  if (role == 0) {
+    // ---- chain waves
+    struct Ops {
+      bf16x8 wh[NKB], wl[NKB];
+      floatx4 u[NVT];
+      bf16x8 kh[2], kl[2];
+      floatx4 gc;
+    };
+    // the operands of W S (fetched during the W S of the chunk before) and
+    // the rest (fetched during its state update)
+    auto fetch_w = [&](int c, Ops& op) {
+      const unsigned char* b = item_base(c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Sacc[j][i] *= ob.gc[i];
+      for (int kb = 0; kb < NKB; ++kb) {
+        op.wh[kb] = *frame_ptr<bf16x8>(b, IM::w_frame(w, kb, 0), lane);
+        op.wl[kb] = *frame_ptr<bf16x8>(b, IM::w_frame(w, kb, 1), lane);
+      }
+    };
+    auto fetch_r = [&](int c, Ops& op) {
+      const unsigned char* b = item_base(c);
+      op.gc = *reinterpret_cast<const floatx4*>(b + IM::g_off + 4 * (16 * srt + 4 * (lane >> 4)));
+#pragma unroll
+      for (int j = 0; j < NVT; ++j) op.u[j] = *frame_ptr<floatx4>(b, IM::u_frame(w, vt0 + j), lane);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 bh = frag_ld(PT, ldP, 16 * (sv0 + j) + tr, 32 * kb, g);
-        const bf16x8 bl = frag_ld(PT + loP, ldP, 16 * (sv0 + j) + tr, 32 * kb, g);
-        Sacc[j] = mma_ab(ob.kh[kb], ob.kl[kb], bh, bl, Sacc[j]);
+        op.kh[kb] = *frame_ptr<bf16x8>(b, IM::k_frame(srt, kb, 0), lane);
+        op.kl[kb] = *frame_ptr<bf16x8>(b, IM::k_frame(srt, kb, 1), lane);
+      }
+    };
+    auto chunk = [&](int c, const Ops& op, Ops& nx) {
+      int lane_x = lane;
+      __asm__ volatile("" : "+v"(lane_x));
+      const int tr = lane_x & 15;
+      const int g = lane_x >> 4;
+      put_state(g, tr);
+      __syncthreads();
+      fetch_w(next_of(c), nx);
+      // ---- W S over both channel halves (separate chains, low half first)
+      // and P = U - W S, to LDS as [value][token position]: token
+      // 32kb + 16h + 4g + i sits at position 32kb + 8g + 4h + i (the order of
+      // the Mqk^T operand)
+      floatx4 a0[NVT], a1[NVT];
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) {
+        a0[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        a1[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) {
+          const bf16x8 bh = frag_ld(ST, ldS, 16 * vt + tr, 32 * kb, g);
+          const bf16x8 bl = frag_ld(ST + loS, ldS, 16 * vt + tr, 32 * kb, g);
+          floatx4& acc = kb < NKH ? a0[vt] : a1[vt];
+          acc = mma_ab(op.wh[kb], op.wl[kb], bh, bl, acc);
+        }
+      const int pos = 32 * (w >> 1) + 8 * g + 4 * (w & 1);
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) {
+        const floatx4 ws = a0[vt] + a1[vt];
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[i] = op.u[vt][i] - ws[i];
+        st_split4(PT + (16 * vt + tr) * ldP + pos, loP, pv);
+      }
+      __syncthreads();
+      fetch_r(next_of(c), nx);
+      // ---- S = Diag(Gamma_C) S + Ktil^T P on this wave's tiles
+#pragma unroll
+      for (int j = 0; j < KVT; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Sacc[j][i] *= op.gc[i];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 bh = frag_ld(PT, ldP, 16 * (sv0 + j) + tr, 32 * kb, g);
+          const bf16x8 bl = frag_ld(PT + loP, ldP, 16 * (sv0 + j) + tr, 32 * kb, g);
+          Sacc[j] = mma_ab(op.kh[kb], op.kl[kb], bh, bl, Sacc[j]);
+        }
+      }
+    };
+    if (c_lo < c_hi) {
+      Ops X, Y;
+      fetch_w(c_lo, X);
+      fetch_r(c_lo, X);
+      wait_vm0();
+      for (int c = c_lo; c < c_hi; c += 2) {
+        chunk(c, X, Y);
+        if (c + 1 >= c_hi) break;
+        chunk(c + 1, Y, X);
       }
     }
-    ob = nb;
-    __syncthreads();  // PT, ST and the partial sums are read before the next chunk rewrites them
+  } else {
+    // ---- output waves
+    constexpr int OSV = DK == 128 ? 0 : NVT / 2;  // first value tile of the state update
+    struct Ops {
+      bf16x8 qf[NKB];
+      bf16x8 mh[2], ml[2];
+      bf16x8 kh[2], kl[2];
+      floatx4 gc;
+    };
+    // (Gamma*Q) and Mqk frames (fetched during the (Gamma*Q) S of the chunk
+    // before) and the state-update operands (fetched during its update)
+    auto fetch_w = [&](int c, Ops& op) {
+      const unsigned char* b = item_base(c);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) op.qf[kb] = *frame_ptr<bf16x8>(b, IM::q_frame(w, kb), lane);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        op.mh[kb] = *frame_ptr<bf16x8>(b, IM::m_frame(w, kb, 0), lane);
+        op.ml[kb] = *frame_ptr<bf16x8>(b, IM::m_frame(w, kb, 1), lane);
+      }
+    };
+    auto fetch_r = [&](int c, Ops& op) {
+      const unsigned char* b = item_base(c);
+      op.gc = *reinterpret_cast<const floatx4*>(b + IM::g_off + 4 * (16 * srt + 4 * (lane >> 4)));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        op.kh[kb] = *frame_ptr<bf16x8>(b, IM::k_frame(srt, kb, 0), lane);
+        op.kl[kb] = *frame_ptr<bf16x8>(b, IM::k_frame(srt, kb, 1), lane);
+      }
+    };
+    auto chunk = [&](int c, const Ops& op, Ops& nx) {
+      int lane_x = lane;
+      __asm__ volatile("" : "+v"(lane_x));
+      const int tr = lane_x & 15;
+      const int g = lane_x >> 4;
+      const long long tok0 = start + (long long)c * CH;
+      const int nv = (int)(len - (long long)c * CH < CH ? len - (long long)c * CH : CH);
+      put_state(g, tr);
+      __syncthreads();
+      fetch_w(next_of(c), nx);
+      // ---- (Gamma*Q) S over both channel halves (separate chains, low half first)
+      floatx4 a0[NVT], a1[NVT];
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) {
+        a0[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        a1[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) {
+          const bf16x8 bh = frag_ld(ST, ldS, 16 * vt + tr, 32 * kb, g);
+          const bf16x8 bl = frag_ld(ST + loS, ldS, 16 * vt + tr, 32 * kb, g);
+          floatx4& acc = kb < NKH ? a0[vt] : a1[vt];
+          acc = mfma_bf16(op.qf[kb], bh, acc);
+          acc = mfma_bf16(op.qf[kb], bl, acc);
+        }
+      floatx4 ov[NVT];
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) ov[vt] = a0[vt] + a1[vt];
+      __syncthreads();
+      fetch_r(next_of(c), nx);
+      // ---- O += Mqk P and the state update of this wave's tiles, from the same
+      // P fragments.  Both token blocks for every tile: the Mqk frames of blocks
+      // after the tile are zero.
+#pragma unroll
+      for (int j = 0; j < KVT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Sacc[j][i] *= op.gc[i];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) {
+          const bf16x8 bh = frag_ld(PT, ldP, 16 * vt + tr, 32 * kb, g);
+          const bf16x8 bl = frag_ld(PT + loP, ldP, 16 * vt + tr, 32 * kb, g);
+          ov[vt] = mma_ab(op.mh[kb], op.ml[kb], bh, bl, ov[vt]);
+          if (vt >= OSV && vt < OSV + KVT)
+            Sacc[vt - OSV] = mma_ab(op.kh[kb], op.kl[kb], bh, bl, Sacc[vt - OSV]);
+        }
+      // o of the tile through this wave's LDS staging area: a quad transpose
+      // gives each lane four consecutive values of row 4g + (tr & 3), stored
+      // as one 16-byte word; read back, each store instruction covers four
+      // whole rows of the slice.  The descriptor spans the chunk's nv rows.
+      {
+        float* os = OS + w * 16 * ldO;
+        const int b = tr & 3;
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt)
+          *reinterpret_cast<floatx4*>(os + (4 * g + b) * ldO + 16 * vt + 4 * (tr >> 2)) =
+              quad_transpose(ov[vt], b);
+        const size_t rowel = (size_t)H * DV;  // elements from one token to the next
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            o + ((size_t)tok0 * H + h) * DV + vcol0, 0, (int)((size_t)nv * rowel * sizeof(TOut)),
+            0x00020000);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int row = 4 * q4 + (lane_x >> 4);
+          const floatx4 y = *reinterpret_cast<const floatx4*>(os + row * ldO + 4 * (lane_x & 15));
+          store4<TOut>(rs, (int)(((size_t)(16 * w + row) * rowel + 4 * (lane_x & 15)) * sizeof(TOut)), y);
+        }
+      }
+    };
+    if (c_lo < c_hi) {
+      Ops X, Y;
+      fetch_w(c_lo, X);
+      fetch_r(c_lo, X);
+      wait_vm0();
+      for (int c = c_lo; c < c_hi; c += 2) {
+        chunk(c, X, Y);
+        if (c + 1 >= c_hi) break;
+        chunk(c + 1, Y, X);
+      }
+    }
   }
 
   {
