@@ -69,6 +69,7 @@ def measured_traffic(summary: str, sources: list[str]):
 
 
 PREFILL_SOURCES = ["kimi_delta_attention_amd/csrc/kda_prefill.hip",
+                   "kimi_delta_attention_amd/csrc/kda_prefill_prep.hip",
                    "kimi_delta_attention_amd/csrc/kda_prefill_state.hip",
                    "kimi_delta_attention_amd/csrc/kda_frag.h",
                    "kimi_delta_attention_amd/csrc/kda_common.h"]
@@ -216,7 +217,7 @@ def main():
                                                  PREFILL_SOURCES),
                      "traffic_unit": "HBM bytes per kda_prefill_chunked call (rocprofv3 "
                                      "FETCH_SIZE + WRITE_SIZE of its kernels, copy-calibrated)",
-                     "kernel": ("kda_prefill_chunked, two-pass: prefill_bf16_kernel<128, PREP_DV=128> "
+                     "kernel": ("kda_prefill_chunked, two-pass: prefill_prep_kernel<128, 128> "
                                 "+ prefill_state_kernel<128, 128>" if two_pass else
                                 "kda_prefill_chunked, fused: prefill_bf16_kernel<128, fp32 out>"),
                      "algorithmic_bytes_per_launch": nbytes,

@@ -54,5 +54,12 @@ hipError_t launch_prefill_state(const PrefillArgs& a, const unsigned char* img,
                                 long long tok_hi, int cap);
 hipError_t launch_chunk_table(const int32_t* cu_seqlens, int n_seq, int cap, int32_t* chunk_off,
                               void* stream);
+// (kda_prefill_prep.hip) the first pass over one window: operand images of the
+// (chunk, head) items of the chunks starting in [tok_lo, tok_hi) (at most `cap`
+// chunks), item (chunk - first chunk of the window) * H + head, on a persistent
+// grid of `grid` workgroups (prefill_prep_per_cu() of them fit a compute unit).
+int prefill_prep_per_cu();
+hipError_t launch_prefill_prep(const PrefillArgs& a, unsigned char* img, const int32_t* chunk_off,
+                               long long tok_lo, long long tok_hi, int cap, int grid);
 
 }  // namespace kda

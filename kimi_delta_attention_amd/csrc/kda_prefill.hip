@@ -49,6 +49,12 @@
 #include "kda_frag.h"
 #include "kda_internal.h"
 
+// Every product is rounded on its own (no fused multiply-add contraction):
+// the fused kernel and the two-pass kernels evaluate the same expressions in
+// different code shapes, and only uncontracted arithmetic gives them bitwise
+// the same results whatever the compiler's scheduling.
+#pragma clang fp contract(off)
+
 namespace kda {
 namespace {
 
@@ -937,17 +943,11 @@ hipError_t launch_prefill(const PrefillArgs& a) {
         e != hipSuccess)
       return e;
   }
-  int grid = device_cus();
+  int grid = device_cus() * prefill_prep_per_cu();
   if ((long long)cap * a.H < grid) grid = cap * a.H;
   const long long win = (long long)WIN_CHUNKS * CH;
   for (long long t0 = 0; t0 < total; t0 += win) {
-    hipError_t e;
-    if (a.Dk == 128)
-      e = a.Dv == 128 ? launch_first_pass<128, 128>(a, img, chunk_off, t0, t0 + win, cap, grid)
-                      : launch_first_pass<128, 64>(a, img, chunk_off, t0, t0 + win, cap, grid);
-    else
-      e = a.Dv == 128 ? launch_first_pass<64, 128>(a, img, chunk_off, t0, t0 + win, cap, grid)
-                      : launch_first_pass<64, 64>(a, img, chunk_off, t0, t0 + win, cap, grid);
+    hipError_t e = launch_prefill_prep(a, img, chunk_off, t0, t0 + win, cap, grid);
     if (e != hipSuccess) return e;
     e = launch_prefill_state(a, img, chunk_off, carry, t0, t0 + win, cap);
     if (e != hipSuccess) return e;

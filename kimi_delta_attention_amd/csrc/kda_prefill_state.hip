@@ -38,6 +38,12 @@
 #include "kda_frag.h"
 #include "kda_internal.h"
 
+// Every product is rounded on its own (no fused multiply-add contraction):
+// the fused kernel and the two-pass kernels evaluate the same expressions in
+// different code shapes, and only uncontracted arithmetic gives them bitwise
+// the same results whatever the compiler's scheduling.
+#pragma clang fp contract(off)
+
 namespace kda {
 namespace {
 
