@@ -71,8 +71,7 @@ using namespace frag;
 //   serial:       ST (state, split), PT (P, split), KT (Ktil, split)
 // GK ((Gamma*K), bf16, [token][channel]) and QT ((Gamma*Q), [token][position])
 // live from operand build to their last product; ES / GC / BS are small.  VW is
-// the width of the staged V block (the 64-wide slice, or all of Dv when the
-// kernel runs as the first pass of the two-pass schedule).
+// the width of the staged V block (the 64-wide value slice).
 template <int DK, int VW>
 struct Plan {
   static constexpr int ldR = DK + 8, ldG = DK + 8, ldQ = DK + 8, ldA = CH + 4, ldT = CH + 8,
@@ -97,34 +96,21 @@ struct Plan {
                 "alignment");
 };
 
-// PREP_DV == 0: the fused kernel (one workgroup per (sequence, head, value
-// slice), state carried across chunks).  PREP_DV == Dv: the first pass of the
-// two-pass schedule for one window of packed tokens [tok_lo, tok_hi); a
-// persistent grid walks the (chunk, head) items of the chunks starting in the
-// window (at most `cap` chunks are stored), computes everything that does not
-// depend on the state and writes it as operand images (Images<DK, Dv>),
-// window-relative item (chunk - first chunk of the window) * H + head.
-template <int DK, typename TOut, int PREP_DV>
+// One workgroup per (sequence, head, 64-wide value slice), state carried
+// across the sequence's chunks.
+template <int DK, typename TOut>
 __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* __restrict__ s_init, float* __restrict__ s_final, TOut* __restrict__ o,
-    const int32_t* __restrict__ cu_seqlens, int n_seq, int T, int H, int DV_,
-    unsigned char* __restrict__ img, const int32_t* __restrict__ chunk_off, long long tok_lo,
-    long long tok_hi, int cap) {
-  constexpr bool PREP = PREP_DV != 0;
-  using L = Plan<DK, PREP ? PREP_DV : BV>;
-  using IM = Images<DK, PREP ? PREP_DV : 64>;
-  const int DV = PREP ? PREP_DV : DV_;
+    const int32_t* __restrict__ cu_seqlens, int n_seq, int T, int H, int DV) {
+  using L = Plan<DK, BV>;
   constexpr int NKB = DK / 32;   // 32-channel blocks
   constexpr int NKH = NKB / 2;   // blocks of one channel half
   constexpr int NCHT = DK / 16;  // 16-channel tiles
   constexpr int RPW = DK / 4;    // state rows per token-tile wave pair
   constexpr int RTW = RPW / 16;  // state row tiles per wave
   constexpr int NCH = BV / 32;   // value tiles per wave (its 32-column half)
-  constexpr int NVL = PREP ? (PREP_DV / 64 > 0 ? PREP_DV / 64 : 1) : 1;  // 16-byte v loads per lane
-  constexpr int NCTW = PREP ? NCHT / 2 : NCHT;  // W^T channel tiles per wave
-  constexpr int NUT = PREP ? PREP_DV / 32 : NCH;  // U tiles per wave
   constexpr int ldR = L::ldR, ldG = L::ldG, ldQ = L::ldQ, ldA = L::ldA, ldT = L::ldT,
                 ldV = L::ldV, ldS = L::ldS, ldP = L::ldP;
   constexpr int loR = 160 * ldR, loG = CH * ldG, loT = CH * ldT, loS = BV * ldS, loP = BV * ldP;
@@ -161,9 +147,9 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
   const int g = lane >> 4;
 
   const int nsl = DV / BV;
-  int sl = 0, h = 0, seq = 0;
-  long long start = 0, len = 0;
-  if constexpr (!PREP) {
+  int sl, h, seq;
+  long long start, len;
+  {
     const int total = n_seq * H * nsl;
     int wid = blockIdx.x;
     if ((total & 7) == 0) wid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
@@ -183,7 +169,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
 
   // state: wave (w, hh) owns key rows [w*RPW, (w+1)*RPW) x value columns vh0..vh0+31
   floatx4 Sacc[RTW][NCH];
-  if constexpr (!PREP) {
+  {
     const float* si = s_init ? s_init + ((size_t)seq * H + h) * DK * DV : nullptr;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
@@ -196,45 +182,12 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
         }
   }
 
-  // One chunk of one head: first token (global index), valid tokens, head,
-  // and (first pass) the item index.
+  // One chunk: first token (global index), valid tokens, head, offset in the
+  // sequence.
   struct Desc {
     long long tok0;
-    int nv, hd, item;
+    int nv, hd;
     long long c0;
-  };
-  int ci_lo = 0, n_items = 0;
-  if constexpr (PREP) {
-    ci_lo = chunks_before(tok_lo, cu_seqlens, chunk_off, n_seq, T);
-    int nc = chunks_before(tok_hi, cu_seqlens, chunk_off, n_seq, T) - ci_lo;
-    if (nc > cap) nc = cap;  // reached only if cu_seqlens is not monotone
-    n_items = nc > 0 ? nc * H : 0;
-  }
-  auto item_desc = [&](int it, Desc& d) {
-    const int ci = ci_lo + it / H;
-    d.hd = it - (ci - ci_lo) * H;
-    d.item = it;
-    long long st, ln, cc;
-    if (chunk_off) {
-      int lo = 0, hi = n_seq - 1;  // last sequence whose first chunk is <= ci
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (chunk_off[mid] <= ci) lo = mid;
-        else hi = mid - 1;
-      }
-      st = cu_seqlens[lo];
-      ln = (long long)cu_seqlens[lo + 1] - st;
-      cc = (long long)(ci - chunk_off[lo]) * CH;
-    } else {
-      const int nch = (T + CH - 1) / CH;
-      const int sq = ci / nch;
-      st = (long long)sq * T;
-      ln = T;
-      cc = (long long)(ci - sq * nch) * CH;
-    }
-    d.tok0 = st + cc;
-    d.nv = (int)(ln - cc < CH ? ln - cc : CH);
-    d.c0 = cc;
   };
 
   const int r = 16 * w + tr;  // this lane's token within the chunk
@@ -248,19 +201,16 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
   struct ChunkIn {
     uint2v k[NKH][2], q[NKH][2];
     floatx4 a[NKH][2];
-    uint4v v[NVL];
+    uint4v v;
     float b;
   };
-  // V columns this lane stages: 8 of the slice, or (first pass) Dv/8 of all Dv
-  const int vld0 = PREP ? (DV / 2) * hh + (DV / 8) * g : vcol0 + vh0 + 8 * g;
+  // V columns this lane stages: 8 of the slice
+  const int vld0 = vcol0 + vh0 + 8 * g;
   auto load_part = [&](const Desc& d, ChunkIn& in, int part) {
     const bool okc = r < d.nv;
     const size_t thc = (size_t)(d.tok0 + r) * H + d.hd;
     if (part == 3) {
-#pragma unroll
-      for (int j = 0; j < NVL; ++j)
-        in.v[j] = okc ? *reinterpret_cast<const uint4v*>(v + thc * DV + vld0 + 8 * j)
-                      : uint4v{0u, 0u, 0u, 0u};
+      in.v = okc ? *reinterpret_cast<const uint4v*>(v + thc * DV + vld0) : uint4v{0u, 0u, 0u, 0u};
       in.b = okc ? beta[thc] : 0.f;
       return;
     }
@@ -277,32 +227,16 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
                                           : floatx4{1.f, 1.f, 1.f, 1.f};
       }
   };
-  Desc cur;
-  bool have;
-  if constexpr (PREP) {
-    have = (int)blockIdx.x < n_items;
-    cur = Desc{0, 0, 0, 0, 0};
-    if (have) item_desc(blockIdx.x, cur);
-  } else {
-    have = len > 0;
-    cur = Desc{start, (int)(len < CH ? len : CH), h, 0, 0};
-  }
+  Desc cur = Desc{start, (int)(len < CH ? len : CH), h, 0};
+  bool have = len > 0;
   ChunkIn in;
   if (have)
     for (int part = 0; part < 4; ++part) load_part(cur, in, part);
 
   while (have) {
-    Desc nxt = cur;
-    bool more;
-    if constexpr (PREP) {
-      const int ni = cur.item + (int)gridDim.x;
-      more = ni < n_items;
-      if (more) item_desc(ni, nxt);
-    } else {
-      const long long c1 = cur.c0 + CH;
-      more = c1 < len;
-      nxt = Desc{start + c1, (int)(len - c1 < CH ? len - c1 : CH), h, 0, c1};
-    }
+    const long long c1 = cur.c0 + CH;
+    const bool more = c1 < len;
+    const Desc nxt = Desc{start + c1, (int)(len - c1 < CH ? len - c1 : CH), h, c1};
     // Lane indices, re-derived each chunk behind an empty asm so that the
     // compiler recomputes the many per-lane LDS addresses inside the loop
     // instead of keeping them all live across it (which exhausts the 256
@@ -315,7 +249,6 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     const int tid = 64 * w8 + lane_x;
     const int nv = cur.nv;
     const long long tok0 = cur.tok0;
-    unsigned char* im = PREP ? img + (size_t)cur.item * IM::bytes : nullptr;
     __syncthreads();  // the previous chunk is done with LDS
 
     const float bt = in.b;
@@ -390,10 +323,8 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       }
       split8(y, qlh[kk], qll[kk]);
       split8(kt, kth[kk], ktl[kk]);
-      // (Gamma*Q) at operand positions 32kb + 8g.. of token r: the first pass
-      // writes it as this lane's fragment of the image, the fused kernel stages it
-      if constexpr (PREP) put_frame(im, IM::q_frame(w, kb), lane_x, qt8);
-      else *reinterpret_cast<bf16x8*>(QT + r * ldQ + 32 * kb + 8 * g) = qt8;
+      // (Gamma*Q) at operand positions 32kb + 8g.. of token r
+      *reinterpret_cast<bf16x8*>(QT + r * ldQ + 32 * kb + 8 * g) = qt8;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
         st_bf16x4(GK + r * ldG + 32 * kb + 16 * hf + 4 * g, gk + 4 * hf);
@@ -430,9 +361,6 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     if (more) {
       load_part(nxt, in, 0);
       load_part(nxt, in, 1);
-    }
-    if constexpr (PREP) {
-      if (tid < DK) __builtin_nontemporal_store(GC[tid], reinterpret_cast<float*>(im + IM::g_off) + tid);
     }
 
     // ---- A^T and Mqk^T tiles (j in tile n, r in tile w), n = 0..w, over this
@@ -485,15 +413,6 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
         const bf16 hv = (bf16)m4[i];
         mqh[n >> 1][4 * (n & 1) + i] = hv;
         mql[n >> 1][4 * (n & 1) + i] = (bf16)(m4[i] - (float)hv);
-      }
-    }
-    if constexpr (PREP) {
-      if (hh == 0) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          put_frame(im, IM::m_frame(w, kb, 0), lane_x, mqh[kb]);
-          put_frame(im, IM::m_frame(w, kb, 1), lane_x, mql[kb]);
-        }
       }
     }
     __syncthreads();  // MQ0 / MQ1 reads done; the solve's scratch reuses them
@@ -575,19 +494,15 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       for (int e = 0; e < 4; ++e) x4[e] = (j0 + e <= rr) ? t4[e] * b4[e] : 0.f;
       st_split4(TB + rr * ldT + j0, loT, x4);
     }
-#pragma unroll
-    for (int j = 0; j < NVL; ++j)
-      *reinterpret_cast<uint4v*>(VS + r * ldV + (PREP ? vld0 : vh0 + 8 * g) + 8 * j) = in.v[j];
+    *reinterpret_cast<uint4v*>(VS + r * ldV + vh0 + 8 * g) = in.v;
     if (more) load_part(nxt, in, 3);
     __syncthreads();
 
     // ---- W^T = (Gamma*K)^T (T Diag b)^T for this tile's tokens, kept as the
-    // split operand of W S: all channels, computed by both waves of the pair
-    // (fused) or one channel half per wave (first pass).  U = T Diag(b) V for
-    // this wave's 32 value columns (fused) or half of all Dv (first pass).
-    const int ct0 = PREP ? NCTW * hh : 0;
-    bf16x8 wh[NCTW / 2], wl[NCTW / 2];
-    floatx4 accU[NUT];
+    // split operand of W S: all channels, computed by both waves of the pair.
+    // U = T Diag(b) V for this wave's 32 value columns.
+    bf16x8 wh[NCHT / 2], wl[NCHT / 2];
+    floatx4 accU[NCH];
     {
       bf16x8 tbh[2], tbl[2];
 #pragma unroll
@@ -596,8 +511,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
         tbl[kb] = frag_ld(TB + loT, ldT, r, 32 * kb, g);
       }
 #pragma unroll
-      for (int ctl = 0; ctl < NCTW; ++ctl) {
-        const int ct = ct0 + ctl;
+      for (int ct = 0; ct < NCHT; ++ct) {
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -611,13 +525,13 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bf16 hv = (bf16)acc[i];
-          wh[ctl >> 1][4 * (ctl & 1) + i] = hv;
-          wl[ctl >> 1][4 * (ctl & 1) + i] = (bf16)(acc[i] - (float)hv);
+          wh[ct >> 1][4 * (ct & 1) + i] = hv;
+          wl[ct >> 1][4 * (ct & 1) + i] = (bf16)(acc[i] - (float)hv);
         }
       }
 #pragma unroll
-      for (int c = 0; c < NUT; ++c) {
-        const int vc = PREP ? 16 * (NUT * hh + c) : vh0 + 16 * c;
+      for (int c = 0; c < NCH; ++c) {
+        const int vc = vh0 + 16 * c;
         accU[c] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -629,45 +543,6 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       }
     }
     __syncthreads();  // TB / VS / GK reads done; ST, PT and KT overwrite the region
-
-    if constexpr (PREP) {
-      // W and U images of this tile; Ktil through LDS into the A operands of
-      // Ktil^T P, one 16-row state tile per wave
-#pragma unroll
-      for (int kbl = 0; kbl < NCTW / 2; ++kbl) {
-        put_frame(im, IM::w_frame(w, NKH * hh + kbl, 0), lane_x, wh[kbl]);
-        put_frame(im, IM::w_frame(w, NKH * hh + kbl, 1), lane_x, wl[kbl]);
-      }
-#pragma unroll
-      for (int c = 0; c < NUT; ++c)
-        put_frame(im, IM::u_frame(w, NUT * hh + c), lane_x, accU[c]);
-#pragma unroll
-      for (int kk = 0; kk < NKH; ++kk) {
-        const int kb = NKH * hh + kk;
-        const uint4v uh = __builtin_bit_cast(uint4v, kth[kk]);
-        const uint4v ul = __builtin_bit_cast(uint4v, ktl[kk]);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          *reinterpret_cast<uint2v*>(KT + r * ldG + 32 * kb + 16 * hf + 4 * g) =
-              uint2v{uh[2 * hf], uh[2 * hf + 1]};
-          *reinterpret_cast<uint2v*>(KT + r * ldG + 32 * kb + 16 * hf + 4 * g + loG) =
-              uint2v{ul[2 * hf], ul[2 * hf + 1]};
-        }
-      }
-      __syncthreads();
-      if (w8 < NCHT) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          put_frame(im, IM::k_frame(w8, kb, 0), lane_x,
-                    frag_tr(KT, ldG, 16 * w8, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g, tr));
-          put_frame(im, IM::k_frame(w8, kb, 1), lane_x,
-                    frag_tr(KT + loG, ldG, 16 * w8, 32 * kb + 4 * g, 32 * kb + 16 + 4 * g, tr));
-        }
-      }
-      cur = nxt;
-      have = more;
-      continue;
-    }
 
     // ---- Ktil ([token][channel], split) and the state as the B operand of W S
     // and (Gamma*Q) S: [value][channel position], position 32kb + 8g + 4h + i
@@ -797,7 +672,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     have = more;
   }
 
-  if (!PREP && s_final) {
+  if (s_final) {
     float* sf = s_final + ((size_t)seq * H + h) * DK * DV;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
@@ -819,7 +694,7 @@ hipError_t set_lds(K kern, int bytes) {
 template <int DK, typename TOut>
 hipError_t launch_fused(const PrefillArgs& a) {
   using L = Plan<DK, BV>;
-  auto kern = prefill_bf16_kernel<DK, TOut, 0>;
+  auto kern = prefill_bf16_kernel<DK, TOut>;
   static bool attr_set = false;  // per instantiation; idempotent if raced
   if (!attr_set) {
     if (hipError_t e = set_lds(kern, L::total); e != hipSuccess) return e;
@@ -829,26 +704,7 @@ hipError_t launch_fused(const PrefillArgs& a) {
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH), L::total, (hipStream_t)a.stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.alpha, a.beta,
                      a.initial_state, a.final_state, (TOut*)a.o, a.cu_seqlens, a.n_seq, a.T, a.H,
-                     a.Dv, (unsigned char*)nullptr, (const int32_t*)nullptr, 0LL, 0LL, 0);
-  return hipGetLastError();
-}
-
-// First pass over one window: a persistent grid of at most one workgroup per
-// compute unit walks the window's (chunk, head) items.
-template <int DK, int DV>
-hipError_t launch_first_pass(const PrefillArgs& a, unsigned char* img, const int32_t* chunk_off,
-                             long long tok_lo, long long tok_hi, int cap, int grid) {
-  using L = Plan<DK, DV>;
-  auto kern = prefill_bf16_kernel<DK, float, DV>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipError_t e = set_lds(kern, L::total); e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH), L::total, (hipStream_t)a.stream,
-                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.alpha, a.beta,
-                     (const float*)nullptr, (float*)nullptr, (float*)nullptr, a.cu_seqlens,
-                     a.n_seq, a.T, a.H, DV, img, chunk_off, tok_lo, tok_hi, cap);
+                     a.Dv);
   return hipGetLastError();
 }
 

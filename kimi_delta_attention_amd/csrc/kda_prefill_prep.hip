@@ -371,8 +371,10 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
           mql[n >> 1][4 * (n & 1) + i] = (bf16)(m4[i] - (float)hv);
         }
       }
+      // (the frames of key blocks after the tile, all zero, are not written)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        if (kb > (w >> 1)) continue;
         put_frame(im, IM::m_frame(w, kb, 0), lane_x, mqh[kb]);
         put_frame(im, IM::m_frame(w, kb, 1), lane_x, mql[kb]);
       }

@@ -317,8 +317,12 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       for (int kb = 0; kb < NKB; ++kb) op.qf[kb] = *frame_ptr<bf16x8>(b, IM::q_frame(w, kb), lane);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        op.mh[kb] = *frame_ptr<bf16x8>(b, IM::m_frame(w, kb, 0), lane);
-        op.ml[kb] = *frame_ptr<bf16x8>(b, IM::m_frame(w, kb, 1), lane);
+        // key block 1 of tiles 0 and 1 lies after the tile: its frames are
+        // zero and not stored; block 0 is fetched again in their place (the
+        // fetch stays unconditional) and zeroed when used
+        const int kbm = kb > (w >> 1) ? 0 : kb;
+        op.mh[kb] = *frame_ptr<bf16x8>(b, IM::m_frame(w, kbm, 0), lane);
+        op.ml[kb] = *frame_ptr<bf16x8>(b, IM::m_frame(w, kbm, 1), lane);
       }
     };
     auto fetch_r = [&](int c, Ops& op) {
@@ -362,9 +366,13 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       for (int vt = 0; vt < NVT; ++vt) ov[vt] = a0[vt] + a1[vt];
       __syncthreads();
       fetch_r(next_of(c), nx);
-      // ---- O += Mqk P and the state update of this wave's tiles, from the same
-      // P fragments.  Both token blocks for every tile: the Mqk frames of blocks
-      // after the tile are zero.
+      // ---- O += Mqk P and the state update of this wave's tiles, from the
+      // same P fragments (the Mqk block after the tile enters as zeros)
+      bf16x8 mh1 = op.mh[1], ml1 = op.ml[1];
+      if (w < 2) {
+        mh1 = bf16x8{};
+        ml1 = bf16x8{};
+      }
 #pragma unroll
       for (int j = 0; j < KVT; ++j)
 #pragma unroll
@@ -375,7 +383,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
         for (int vt = 0; vt < NVT; ++vt) {
           const bf16x8 bh = frag_ld(PT, ldP, 16 * vt + tr, 32 * kb, g);
           const bf16x8 bl = frag_ld(PT + loP, ldP, 16 * vt + tr, 32 * kb, g);
-          ov[vt] = mma_ab(op.mh[kb], op.ml[kb], bh, bl, ov[vt]);
+          ov[vt] = mma_ab(kb ? mh1 : op.mh[0], kb ? ml1 : op.ml[0], bh, bl, ov[vt]);
           if (vt >= OSV && vt < OSV + KVT)
             Sacc[vt - OSV] = mma_ab(op.kh[kb], op.kl[kb], bh, bl, Sacc[vt - OSV]);
         }
