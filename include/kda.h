@@ -83,6 +83,50 @@ typedef enum {
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
 /*
+ * The decay gate, for the *_gated entry points.  The recurrence always uses a
+ * per-key-channel alpha_t in (0, 1]^Dk; the gate hands it over in one of the
+ * parametrizations the pages describe, and the kernels form alpha (in fp32) as
+ * they load it:
+ *
+ *   KDA_GATE_ALPHA    gate [.., H, Dk] fp32 = alpha itself (what the plain
+ *                     entry points take)
+ *   KDA_GATE_LOG      gate [.., H, Dk] fp32 = g = log alpha <= 0, alpha = exp(g):
+ *                     the gate kept in log space ("Kimi Delta Attention 完全拆解",
+ *                     section "KDA 的核心：让遗忘从一个标量细化为逐通道向量")
+ *   KDA_GATE_BOUNDED  gate [.., H, Dk] fp32 = logits z, a_log [H] fp32 = A;
+ *                     g = g_min * Sigmoid(exp(A_h) z), alpha = exp(g): K3's
+ *                     lower-bounded gate with g_min = -5 on the pages ("Kimi K3 的
+ *                     KDA" section 6; "Kimi K3模型架构详解" section 3.4).  g_min must
+ *                     lie in [-5, 0): every token then decays by at most e^-5,
+ *                     which keeps the 16-token tile factors of the chunked paths
+ *                     in fp32 range
+ *   KDA_GATE_SCALAR   gate [.., H] fp32 = one alpha per token and head, applied
+ *                     to every key channel: gated DeltaNet, the vector gate with
+ *                     equal components (same section of "Kimi Delta Attention
+ *                     完全拆解")
+ *   KDA_GATE_NONE     no decay, alpha = 1: DeltaNet; `gate` is ignored
+ *
+ * ".." stands for the leading token dimensions of the entry point: [B, T] for
+ * the dense prefill, [1, total_tokens] for the packed prefill, [B] for decode.
+ * Pointers are device pointers aligned like alpha (16 bytes for the bf16
+ * prefill paths with a per-channel gate, 4 bytes otherwise).
+ */
+typedef enum {
+    KDA_GATE_ALPHA = 0,
+    KDA_GATE_LOG = 1,
+    KDA_GATE_BOUNDED = 2,
+    KDA_GATE_SCALAR = 3,
+    KDA_GATE_NONE = 4
+} kda_gate_kind;
+
+typedef struct {
+    kda_gate_kind kind;
+    const float* gate;   /* per kind above; may be NULL for KDA_GATE_NONE        */
+    const float* a_log;  /* [H] per-head log scale A, KDA_GATE_BOUNDED only      */
+    float g_min;         /* KDA_GATE_BOUNDED only, in [-5, 0)                   */
+} kda_gate;
+
+/*
  * kda_prefill_chunked -- dense prefill over B sequences of T tokens each.
  * The chunkwise form of the recurrence: inside each 64-token chunk the
  * cumulative decay, the strictly lower-triangular beta-weighted decayed k k^T
@@ -156,6 +200,35 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
                            const float* alpha, const float* beta, float* state,
                            void* o, kda_dtype o_dtype, int B, int H, int Dk, int Dv,
                            void* stream);
+
+/*
+ * kda_prefill_chunked_gated, kda_prefill_varlen_gated, kda_decode_step_gated --
+ * the same operations with the decay given as a kda_gate (`gate` a HOST
+ * pointer to the descriptor, read during the call; the tensors it names are
+ * device tensors) instead of an alpha tensor.  The plain entry points are
+ * these with {KDA_GATE_ALPHA, alpha}.  An unknown kind, a NULL gate tensor (for
+ * a kind that reads one), a NULL a_log or a g_min outside [-5, 0) for
+ * KDA_GATE_BOUNDED return KDA_ERR_INVALID_ARGUMENT.
+ */
+kda_status kda_prefill_chunked_gated(const void* q, const void* k, const void* v,
+                                     kda_dtype qkv_dtype, const kda_gate* gate,
+                                     const float* beta, const float* initial_state,
+                                     float* final_state, void* o, kda_dtype o_dtype,
+                                     int B, int T, int H, int Dk, int Dv, int chunk,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+kda_status kda_prefill_varlen_gated(const void* q, const void* k, const void* v,
+                                    kda_dtype qkv_dtype, const kda_gate* gate,
+                                    const float* beta, const int32_t* cu_seqlens, int N,
+                                    int total_tokens, const float* initial_state,
+                                    float* final_state, void* o, kda_dtype o_dtype,
+                                    int H, int Dk, int Dv, int chunk,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+kda_status kda_decode_step_gated(const void* q, const void* k, const void* v,
+                                 kda_dtype qkv_dtype, const kda_gate* gate, const float* beta,
+                                 float* state, void* o, kda_dtype o_dtype, int B, int H, int Dk,
+                                 int Dv, void* stream);
 
 /*
  * kda_prefill_workspace_size -- workspace bytes that enable the two-pass

@@ -19,10 +19,19 @@ KDA_F32, KDA_BF16 = 0, 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_HIP"}
 
 EXPORTED = ("kda_prefill_chunked", "kda_prefill_varlen", "kda_decode_step",
+            "kda_prefill_chunked_gated", "kda_prefill_varlen_gated", "kda_decode_step_gated",
             "kda_prefill_workspace_size", "kda_prefill_varlen_workspace_size",
             "kda_prefill_two_pass_preferred", "kda_status_string", "kda_last_error_message")
 
 SCHEDULES = ("auto", "fused", "two_pass")
+
+# kda_gate_kind: how the decay tensor passed as `alpha` is read (include/kda.h)
+GATES = {"alpha": 0, "log": 1, "bounded": 2, "scalar": 3, "none": 4}
+
+
+class _Gate(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int), ("gate", ctypes.c_void_p),
+                ("a_log", ctypes.c_void_p), ("g_min", ctypes.c_float)]
 
 
 class KdaError(RuntimeError):
@@ -50,6 +59,15 @@ def load() -> ctypes.CDLL:
     lib.kda_prefill_varlen.restype = I
     lib.kda_decode_step.argtypes = [P, P, P, I, P, P, P, P, I, I, I, I, I, P]
     lib.kda_decode_step.restype = I
+    G = ctypes.POINTER(_Gate)
+    lib.kda_prefill_chunked_gated.argtypes = [P, P, P, I, G, P, P, P, P, I, I, I, I, I, I, I, P,
+                                              Z, P]
+    lib.kda_prefill_chunked_gated.restype = I
+    lib.kda_prefill_varlen_gated.argtypes = [P, P, P, I, G, P, P, I, I, P, P, P, I, I, I, I, I,
+                                             P, Z, P]
+    lib.kda_prefill_varlen_gated.restype = I
+    lib.kda_decode_step_gated.argtypes = [P, P, P, I, G, P, P, P, I, I, I, I, I, P]
+    lib.kda_decode_step_gated.restype = I
     lib.kda_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.kda_prefill_workspace_size.restype = Z
     lib.kda_prefill_varlen_workspace_size.argtypes = [I, I, I, I, I, I]
@@ -97,6 +115,32 @@ def _need(t: torch.Tensor, name: str, dtype=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _gate(kind: str, alpha, a_log, g_min: float, lead: tuple, H: int, Dk: int, dev):
+    """Checks the decay tensor against its gate kind and returns the kda_gate
+    descriptor.  Per-channel kinds take [*lead, H, Dk], 'scalar' [*lead, H],
+    'none' no tensor; 'bounded' also takes a_log [H]."""
+    if kind not in GATES:
+        raise ValueError(f"gate must be one of {tuple(GATES)}")
+    if kind == "none":
+        if alpha is not None:
+            raise ValueError("gate 'none' takes no decay tensor (pass alpha=None)")
+        return _Gate(GATES[kind], None, None, 0.0)
+    _need(alpha, "alpha", torch.float32, dev)
+    want = (*lead, H) if kind == "scalar" else (*lead, H, Dk)
+    if tuple(alpha.shape) != want:
+        raise ValueError(f"gate '{kind}' expects a decay tensor of shape {want}, "
+                         f"got {tuple(alpha.shape)}")
+    al = None
+    if kind == "bounded":
+        if a_log is None:
+            raise ValueError("gate 'bounded' needs a_log [H]")
+        _need(a_log, "a_log", torch.float32, dev)
+        if tuple(a_log.shape) != (H,):
+            raise ValueError("a_log must be [H]")
+        al = a_log.data_ptr()
+    return _Gate(GATES[kind], alpha.data_ptr(), al, float(g_min))
+
+
 def workspace_size(B: int, T: int, H: int, Dk: int, Dv: int, chunk: int = 64) -> int:
     return int(load().kda_prefill_workspace_size(B, T, H, Dk, Dv, chunk))
 
@@ -134,20 +178,24 @@ _DT = {torch.bfloat16: KDA_BF16, torch.float32: KDA_F32}
 
 def prefill_chunked(q, k, v, alpha, beta, initial_state=None, out_dtype=torch.float32,
                     final_state: bool | torch.Tensor = True, o: torch.Tensor | None = None,
-                    schedule: str = "auto", workspace: torch.Tensor | None = None):
+                    schedule: str = "auto", workspace: torch.Tensor | None = None,
+                    gate: str = "alpha", a_log: torch.Tensor | None = None,
+                    g_min: float = -5.0):
     """Dense chunked prefill.  q, k, alpha [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H];
     initial_state [B,H,Dk,Dv] fp32 or None.  schedule: 'auto', 'fused' or
     'two_pass' (the latter with `workspace`, a uint8 device buffer, or one
-    allocated here).  Returns (o, final_state)."""
+    allocated here).  gate: how `alpha` is read -- 'alpha' (the decay itself),
+    'log' (log alpha), 'bounded' (logits z with a_log [H] and g_min), 'scalar'
+    (one alpha per token and head, [B,T,H]) or 'none' (alpha = 1, pass None).
+    Returns (o, final_state)."""
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, q.dtype, dev)
-    _need(alpha, "alpha", torch.float32, dev)
+    g = _gate(gate, alpha, a_log, g_min, (B, T), H, Dk, dev)
     _need(beta, "beta", torch.float32, dev)
-    if k.shape != q.shape or alpha.shape != q.shape or v.shape != (B, T, H, Dv) \
-            or beta.shape != (B, T, H):
+    if k.shape != q.shape or v.shape != (B, T, H, Dv) or beta.shape != (B, T, H):
         raise ValueError("inconsistent shapes")
     if initial_state is not None:
         _need(initial_state, "initial_state", torch.float32, dev)
@@ -166,8 +214,8 @@ def prefill_chunked(q, k, v, alpha, beta, initial_state=None, out_dtype=torch.fl
         fs = None
     ws = _workspace(schedule, workspace, q.dtype, B, B * T,
                     (workspace_size(B, T, H, Dk, Dv), B, H, Dk, Dv), dev)
-    _check(load().kda_prefill_chunked(
-        _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(alpha), _ptr(beta), _ptr(initial_state),
+    _check(load().kda_prefill_chunked_gated(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), ctypes.byref(g), _ptr(beta), _ptr(initial_state),
         _ptr(fs), _ptr(o), _dt(o), B, T, H, Dk, Dv, 64, _ptr(ws),
         0 if ws is None else ws.numel(), _stream(dev)))
     return o, fs
@@ -176,10 +224,12 @@ def prefill_chunked(q, k, v, alpha, beta, initial_state=None, out_dtype=torch.fl
 def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None,
                    out_dtype=torch.float32, final_state: bool | torch.Tensor = True,
                    o: torch.Tensor | None = None, schedule: str = "auto",
-                   workspace: torch.Tensor | None = None):
+                   workspace: torch.Tensor | None = None, gate: str = "alpha",
+                   a_log: torch.Tensor | None = None, g_min: float = -5.0):
     """Packed prefill.  q, k, alpha [1,NTOK,H,Dk]; v [1,NTOK,H,Dv]; beta [1,NTOK,H];
-    cu_seqlens int32 [N+1] on the device; states [N,H,Dk,Dv].  schedule and
-    workspace as for prefill_chunked.  Returns (o, final_state)."""
+    cu_seqlens int32 [N+1] on the device; states [N,H,Dk,Dv].  schedule,
+    workspace and the gate arguments as for prefill_chunked.  Returns
+    (o, final_state)."""
     _, NT, H, Dk = q.shape
     Dv = v.shape[-1]
     dev = q.device
@@ -187,7 +237,7 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None,
         raise ValueError("packed inputs have B == 1")
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, q.dtype, dev)
-    _need(alpha, "alpha", torch.float32, dev)
+    g = _gate(gate, alpha, a_log, g_min, (1, NT), H, Dk, dev)
     _need(beta, "beta", torch.float32, dev)
     _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
     N = cu_seqlens.numel() - 1
@@ -205,30 +255,32 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None,
         fs = None
     ws = _workspace(schedule, workspace, q.dtype, N, NT,
                     (varlen_workspace_size(N, NT, H, Dk, Dv), N, H, Dk, Dv), dev)
-    _check(load().kda_prefill_varlen(
-        _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), N, NT,
+    _check(load().kda_prefill_varlen_gated(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), ctypes.byref(g), _ptr(beta), _ptr(cu_seqlens), N, NT,
         _ptr(initial_state), _ptr(fs), _ptr(o), _dt(o), H, Dk, Dv, 64, _ptr(ws),
         0 if ws is None else ws.numel(), _stream(dev)))
     return o, fs
 
 
 def decode_step(q, k, v, alpha, beta, state, out_dtype=torch.float32,
-                o: torch.Tensor | None = None):
+                o: torch.Tensor | None = None, gate: str = "alpha",
+                a_log: torch.Tensor | None = None, g_min: float = -5.0):
     """One token per session.  q, k, alpha [B,H,Dk]; v [B,H,Dv]; beta [B,H];
-    state [B,H,Dk,Dv] fp32 updated in place.  Returns o [B,H,Dv]."""
+    state [B,H,Dk,Dv] fp32 updated in place; the gate arguments as for
+    prefill_chunked ('scalar' takes alpha [B,H]).  Returns o [B,H,Dv]."""
     B, H, Dk = q.shape
     Dv = v.shape[-1]
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, q.dtype, dev)
-    _need(alpha, "alpha", torch.float32, dev)
+    g = _gate(gate, alpha, a_log, g_min, (B,), H, Dk, dev)
     _need(beta, "beta", torch.float32, dev)
     _need(state, "state", torch.float32, dev)
-    if state.shape != (B, H, Dk, Dv) or beta.shape != (B, H) or alpha.shape != q.shape:
+    if state.shape != (B, H, Dk, Dv) or beta.shape != (B, H):
         raise ValueError("inconsistent shapes")
     if o is None:
         o = torch.empty(B, H, Dv, dtype=out_dtype, device=dev)
-    _check(load().kda_decode_step(
-        _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o),
+    _check(load().kda_decode_step_gated(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), ctypes.byref(g), _ptr(beta), _ptr(state), _ptr(o),
         _dt(o), B, H, Dk, Dv, _stream(dev)))
     return o

@@ -31,10 +31,9 @@ kda_status ok() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 kda_status check_common(const void* q, const void* k, const void* v, kda_dtype qkv,
-                        const float* alpha, const float* beta, const void* o, kda_dtype od,
-                        int H, int Dk, int Dv) {
-  if (!q || !k || !v || !alpha || !beta || !o)
-    return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, alpha, beta and o must be non-null");
+                        const float* beta, const void* o, kda_dtype od, int H, int Dk, int Dv) {
+  if (!q || !k || !v || !beta || !o)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, beta and o must be non-null");
   if (qkv != KDA_F32 && qkv != KDA_BF16) return fail(KDA_ERR_INVALID_ARGUMENT, "bad qkv_dtype");
   if (od != KDA_F32 && od != KDA_BF16) return fail(KDA_ERR_INVALID_ARGUMENT, "bad o_dtype");
   if (H <= 0 || Dk <= 0 || Dv <= 0)
@@ -42,8 +41,37 @@ kda_status check_common(const void* q, const void* k, const void* v, kda_dtype q
   // token tensors are read and written element by element: natural alignment suffices
   const uintptr_t m_in = qkv == KDA_BF16 ? 1u : 3u, m_out = od == KDA_BF16 ? 1u : 3u;
   if (((uintptr_t)q & m_in) || ((uintptr_t)k & m_in) || ((uintptr_t)v & m_in) ||
-      ((uintptr_t)alpha & 3u) || ((uintptr_t)beta & 3u) || ((uintptr_t)o & m_out))
+      ((uintptr_t)beta & 3u) || ((uintptr_t)o & m_out))
     return fail(KDA_ERR_INVALID_ARGUMENT, "tensor pointers must be aligned to their element size");
+  return KDA_OK;
+}
+
+// The gate descriptor: kind, tensors, bound.  `vec16`: the caller's kernels read
+// a per-channel gate with 16-byte loads.
+kda_status check_gate(const kda_gate* g, bool vec16, kda::Gate* out) {
+  if (!g) return fail(KDA_ERR_INVALID_ARGUMENT, "gate descriptor must be non-null");
+  if (g->kind < KDA_GATE_ALPHA || g->kind > KDA_GATE_NONE)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "unknown gate kind %d", (int)g->kind);
+  const bool per_channel = g->kind == KDA_GATE_ALPHA || g->kind == KDA_GATE_LOG ||
+                           g->kind == KDA_GATE_BOUNDED;
+  if (g->kind != KDA_GATE_NONE) {
+    if (!g->gate) return fail(KDA_ERR_INVALID_ARGUMENT, "gate tensor (alpha) must be non-null");
+    const uintptr_t m = (vec16 && per_channel) ? 15u : 3u;
+    if ((uintptr_t)g->gate & m)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "gate tensor (alpha) must be %d-byte aligned",
+                  (int)m + 1);
+  }
+  if (g->kind == KDA_GATE_BOUNDED) {
+    if (!g->a_log || ((uintptr_t)g->a_log & 3u))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "bounded gate needs a non-null, aligned a_log");
+    if (!(g->g_min >= -5.f && g->g_min < 0.f))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "bounded gate g_min must lie in [-5, 0) (got %g)",
+                  (double)g->g_min);
+  }
+  out->kind = (int)g->kind;
+  out->g = g->kind == KDA_GATE_NONE ? nullptr : g->gate;
+  out->a_log = g->kind == KDA_GATE_BOUNDED ? g->a_log : nullptr;
+  out->g_min = g->kind == KDA_GATE_BOUNDED ? g->g_min : 0.f;
   return KDA_OK;
 }
 
@@ -86,24 +114,28 @@ int kda_prefill_two_pass_preferred(kda_dtype qkv_dtype, int n_seq, int total_tok
 }
 
 static kda_status prefill_common(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
-                                 const float* alpha, const float* beta,
+                                 const kda_gate* gate, const float* beta,
                                  const int32_t* cu_seqlens, int n_seq, int T,
                                  const float* initial_state, float* final_state, void* o,
                                  kda_dtype o_dtype, int H, int Dk, int Dv, int chunk,
                                  void* workspace, size_t workspace_bytes, void* stream) {
   if (n_seq < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative batch or length");
   if (n_seq == 0) return ok();
+  kda::Gate g = {KDA_GATE_NONE, nullptr, nullptr, 0.f};
   if (T > 0 || cu_seqlens) {
-    kda_status s = check_common(q, k, v, qkv_dtype, alpha, beta, o, o_dtype, H, Dk, Dv);
+    kda_status s = check_common(q, k, v, qkv_dtype, beta, o, o_dtype, H, Dk, Dv);
+    if (s != KDA_OK) return s;
+    s = check_gate(gate, qkv_dtype == KDA_BF16, &g);
     if (s != KDA_OK) return s;
   } else if (H <= 0 || Dk <= 0 || Dv <= 0) {
     // T == 0: no token tensor is read; the kernel only hands the state through
     return fail(KDA_ERR_INVALID_ARGUMENT, "H, Dk and Dv must be positive");
   }
   if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk must be 64 (got %d)", chunk);
-  // the bf16 kernel reads q, k, v and alpha with 8- and 16-byte vector loads
+  // the bf16 kernels read q, k, v (and a per-channel gate, checked above) with
+  // 8- and 16-byte vector loads
   if (qkv_dtype == KDA_BF16 && (T > 0 || cu_seqlens) &&
-      (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha)))
+      (!aligned16(q) || !aligned16(k) || !aligned16(v)))
     return fail(KDA_ERR_INVALID_ARGUMENT, "bf16 prefill needs 16-byte aligned q, k, v and alpha");
   if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
     return fail(KDA_ERR_INVALID_ARGUMENT, "state pointers must be 16-byte aligned");
@@ -119,7 +151,7 @@ static kda_status prefill_common(const void* q, const void* k, const void* v, kd
   if (workspace && ((uintptr_t)workspace & 255u))
     return fail(KDA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   kda::PrefillArgs a;
-  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+  a.q = q; a.k = k; a.v = v; a.gate = g; a.beta = beta;
   a.initial_state = initial_state; a.final_state = final_state; a.o = o;
   a.qkv_bf16 = qkv_dtype == KDA_BF16; a.o_bf16 = o_dtype == KDA_BF16;
   a.cu_seqlens = cu_seqlens; a.n_seq = n_seq; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv;
@@ -128,15 +160,43 @@ static kda_status prefill_common(const void* q, const void* k, const void* v, kd
   return hip_status(kda::launch_prefill(a));
 }
 
+kda_status kda_prefill_chunked_gated(const void* q, const void* k, const void* v,
+                                     kda_dtype qkv_dtype, const kda_gate* gate,
+                                     const float* beta, const float* initial_state,
+                                     float* final_state, void* o, kda_dtype o_dtype, int B, int T,
+                                     int H, int Dk, int Dv, int chunk, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (B < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B and T must be >= 0");
+  return prefill_common(q, k, v, qkv_dtype, gate, beta, nullptr, B, T, initial_state,
+                        final_state, o, o_dtype, H, Dk, Dv, chunk, workspace, workspace_bytes,
+                        stream);
+}
+
 kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
                                const float* alpha, const float* beta,
                                const float* initial_state, float* final_state, void* o,
                                kda_dtype o_dtype, int B, int T, int H, int Dk, int Dv, int chunk,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  if (B < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B and T must be >= 0");
-  return prefill_common(q, k, v, qkv_dtype, alpha, beta, nullptr, B, T, initial_state,
-                        final_state, o, o_dtype, H, Dk, Dv, chunk, workspace, workspace_bytes,
-                        stream);
+  const kda_gate g = {KDA_GATE_ALPHA, alpha, nullptr, 0.f};
+  return kda_prefill_chunked_gated(q, k, v, qkv_dtype, &g, beta, initial_state, final_state, o,
+                                   o_dtype, B, T, H, Dk, Dv, chunk, workspace, workspace_bytes,
+                                   stream);
+}
+
+kda_status kda_prefill_varlen_gated(const void* q, const void* k, const void* v,
+                                    kda_dtype qkv_dtype, const kda_gate* gate, const float* beta,
+                                    const int32_t* cu_seqlens, int N, int total_tokens,
+                                    const float* initial_state, float* final_state, void* o,
+                                    kda_dtype o_dtype, int H, int Dk, int Dv, int chunk,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (N < 0 || total_tokens < 0)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "N and total_tokens must be >= 0");
+  if (N > 0 && !cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens must be non-null");
+  if (N > 0 && ((uintptr_t)cu_seqlens & 3u))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
+  return prefill_common(q, k, v, qkv_dtype, gate, beta, cu_seqlens, N, total_tokens,
+                        initial_state, final_state, o, o_dtype, H, Dk, Dv, chunk, workspace,
+                        workspace_bytes, stream);
 }
 
 kda_status kda_prefill_varlen(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
@@ -145,22 +205,21 @@ kda_status kda_prefill_varlen(const void* q, const void* k, const void* v, kda_d
                               float* final_state, void* o, kda_dtype o_dtype, int H, int Dk,
                               int Dv, int chunk, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  if (N < 0 || total_tokens < 0)
-    return fail(KDA_ERR_INVALID_ARGUMENT, "N and total_tokens must be >= 0");
-  if (N > 0 && !cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens must be non-null");
-  if (N > 0 && ((uintptr_t)cu_seqlens & 3u))
-    return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
-  return prefill_common(q, k, v, qkv_dtype, alpha, beta, cu_seqlens, N, total_tokens,
-                        initial_state, final_state, o, o_dtype, H, Dk, Dv, chunk, workspace,
-                        workspace_bytes, stream);
+  const kda_gate g = {KDA_GATE_ALPHA, alpha, nullptr, 0.f};
+  return kda_prefill_varlen_gated(q, k, v, qkv_dtype, &g, beta, cu_seqlens, N, total_tokens,
+                                  initial_state, final_state, o, o_dtype, H, Dk, Dv, chunk,
+                                  workspace, workspace_bytes, stream);
 }
 
-kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
-                           const float* alpha, const float* beta, float* state, void* o,
-                           kda_dtype o_dtype, int B, int H, int Dk, int Dv, void* stream) {
+kda_status kda_decode_step_gated(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                                 const kda_gate* gate, const float* beta, float* state, void* o,
+                                 kda_dtype o_dtype, int B, int H, int Dk, int Dv, void* stream) {
   if (B < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B must be >= 0");
   if (B == 0) return ok();
-  kda_status s = check_common(q, k, v, qkv_dtype, alpha, beta, o, o_dtype, H, Dk, Dv);
+  kda_status s = check_common(q, k, v, qkv_dtype, beta, o, o_dtype, H, Dk, Dv);
+  if (s != KDA_OK) return s;
+  kda::Gate g;
+  s = check_gate(gate, false, &g);
   if (s != KDA_OK) return s;
   if (!state) return fail(KDA_ERR_INVALID_ARGUMENT, "state must be non-null");
   if (!aligned16(state)) return fail(KDA_ERR_INVALID_ARGUMENT, "state must be 16-byte aligned");
@@ -168,10 +227,18 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
     return fail(KDA_ERR_UNSUPPORTED, "Dk and Dv must be 64 or 128 (got %d, %d)", Dk, Dv);
   if ((long long)B * H > 0x7fffffffLL) return fail(KDA_ERR_INVALID_ARGUMENT, "B*H too large");
   kda::DecodeArgs a;
-  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.state = state; a.o = o;
+  a.q = q; a.k = k; a.v = v; a.gate = g; a.beta = beta; a.state = state; a.o = o;
   a.qkv_bf16 = qkv_dtype == KDA_BF16; a.o_bf16 = o_dtype == KDA_BF16;
   a.B = B; a.H = H; a.Dk = Dk; a.Dv = Dv; a.stream = stream;
   return hip_status(kda::launch_decode(a));
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                           const float* alpha, const float* beta, float* state, void* o,
+                           kda_dtype o_dtype, int B, int H, int Dk, int Dv, void* stream) {
+  const kda_gate g = {KDA_GATE_ALPHA, alpha, nullptr, 0.f};
+  return kda_decode_step_gated(q, k, v, qkv_dtype, &g, beta, state, o, o_dtype, B, H, Dk, Dv,
+                               stream);
 }
 
 }  // extern "C"

@@ -43,6 +43,148 @@ __device__ __forceinline__ floatx4 mfma_f32x8(const floatx8& a, const floatx8& b
   return c;
 }
 
+// The decay gate of the recurrence, in one of the parametrizations the pages
+// describe; every kernel turns it into the per-key-channel alpha in (0, 1] as it
+// loads it.  `row` indexes a (token, head) row of the [.., H, Dk] gate tensors
+// (the [.., H] tensor for GATE_SCALAR), `h` the head.
+//   GATE_ALPHA    alpha itself
+//   GATE_LOG      g = log alpha, alpha = exp(g) (the gate kept in log space,
+//                 "Kimi Delta Attention 完全拆解", section "KDA 的核心")
+//   GATE_BOUNDED  logits z and a per-head log scale A: g = g_min Sigmoid(exp(A_h) z),
+//                 alpha = exp(g) (K3's lower-bounded gate, "Kimi K3 的 KDA" section
+//                 6, g_min = -5)
+//   GATE_SCALAR   one alpha per token and head for every channel (gated DeltaNet)
+//   GATE_NONE     alpha = 1 (DeltaNet)
+enum GateKind { GATE_ALPHA = 0, GATE_LOG = 1, GATE_BOUNDED = 2, GATE_SCALAR = 3, GATE_NONE = 4 };
+
+struct Gate {
+  int kind;
+  const float* g;      // [rows, Dk], or [rows] for GATE_SCALAR; unused for GATE_NONE
+  const float* a_log;  // [H], GATE_BOUNDED
+  float g_min;         // GATE_BOUNDED
+};
+
+__device__ __forceinline__ float gate_bounded(float z, float scale, float g_min) {
+  return expf(g_min * (1.f / (1.f + expf(-scale * z))));
+}
+
+// The same two gates on the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32,
+// about 1 ulp each): e^x = 2^(x log2 e).  For the arguments a gate produces
+// (|x| <= 5 log2 e in the outer exponential of the bounded gate) the rounding of
+// x log2 e adds under 1e-6 relative error to alpha.  The bf16 prefill kernels
+// use these (both schedules the same ones); a logit of -inf still gives alpha 1.
+constexpr float kLog2e = 1.44269504088896341f;
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float gate_bounded_hw(float z, float scale, float g_min) {
+  return exp_hw(g_min * __builtin_amdgcn_rcpf(1.f + exp_hw(-scale * z)));
+}
+
+// alpha of key channels c..c+3 (c a multiple of 4, 16-byte aligned rows), the
+// bf16 first pass's form (hardware exponentials, like gate_finish_blocks)
+__device__ __forceinline__ floatx4 gate_alpha4(const Gate& G, size_t row, int Dk, int c, int h) {
+  switch (G.kind) {
+    case GATE_LOG: {
+      const floatx4 x = *reinterpret_cast<const floatx4*>(G.g + row * Dk + c);
+      return floatx4{exp_hw(x[0]), exp_hw(x[1]), exp_hw(x[2]), exp_hw(x[3])};
+    }
+    case GATE_BOUNDED: {
+      const floatx4 x = *reinterpret_cast<const floatx4*>(G.g + row * Dk + c);
+      const float sc = expf(G.a_log[h]);
+      return floatx4{gate_bounded_hw(x[0], sc, G.g_min), gate_bounded_hw(x[1], sc, G.g_min),
+                     gate_bounded_hw(x[2], sc, G.g_min), gate_bounded_hw(x[3], sc, G.g_min)};
+    }
+    case GATE_SCALAR: {
+      const float a = G.g[row];
+      return floatx4{a, a, a, a};
+    }
+    case GATE_NONE:
+      return floatx4{1.f, 1.f, 1.f, 1.f};
+    default:
+      return *reinterpret_cast<const floatx4*>(G.g + row * Dk + c);
+  }
+}
+
+// alpha of one key channel c
+__device__ __forceinline__ float gate_alpha1(const Gate& G, size_t row, int Dk, int c, int h) {
+  switch (G.kind) {
+    case GATE_LOG: return expf(G.g[row * Dk + c]);
+    case GATE_BOUNDED: return gate_bounded(G.g[row * Dk + c], expf(G.a_log[h]), G.g_min);
+    case GATE_SCALAR: return G.g[row];
+    case GATE_NONE: return 1.f;
+    default: return G.g[row * Dk + c];
+  }
+}
+
+// alpha of the N key channels c0, c0 + STRIDE, ... of one row, for a gate kind
+// fixed at compile time (one straight-line loop per kind)
+template <int KIND, int N, int STRIDE>
+__device__ __forceinline__ void gate_alpha_rows(const Gate& G, size_t row, int Dk, int c0, int h,
+                                                float (&a)[N]) {
+  const float* g = G.g + row * Dk + c0;
+  if constexpr (KIND == GATE_LOG) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) a[i] = expf(g[STRIDE * i]);
+  } else if constexpr (KIND == GATE_BOUNDED) {
+    const float sc = expf(G.a_log[h]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) a[i] = gate_bounded(g[STRIDE * i], sc, G.g_min);
+  } else if constexpr (KIND == GATE_SCALAR) {
+    const float x = G.g[row];
+#pragma unroll
+    for (int i = 0; i < N; ++i) a[i] = x;
+  } else if constexpr (KIND == GATE_NONE) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) a[i] = 1.f;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) a[i] = g[STRIDE * i];
+  }
+}
+
+// Gate values of the key channels c0 + 32 kb + 16 hf + {0..3} (kb < NB, hf < 2)
+// of one row (c0 a multiple of 4, 16-byte aligned rows), as stored, for a gate
+// kind fixed at compile time: a prefetch issues the loads only, and
+// gate_finish_blocks turns them into alpha where they are used.  A row with !ok
+// reads nothing and gets the stored value whose alpha is 1 (1 for alpha, 0 for
+// log alpha, a logit of -inf for the bounded gate).
+template <int KIND, int NB>
+__device__ __forceinline__ void gate_load_blocks(const Gate& G, bool ok, size_t row, int Dk,
+                                                 int c0, floatx4 (&a)[NB][2]) {
+  if constexpr (KIND == GATE_SCALAR || KIND == GATE_NONE) {
+    float x = 1.f;
+    if constexpr (KIND == GATE_SCALAR) x = ok ? G.g[row] : 1.f;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) a[kb][hf] = floatx4{x, x, x, x};
+  } else {
+    constexpr float f = KIND == GATE_LOG ? 0.f : KIND == GATE_BOUNDED ? -INFINITY : 1.f;
+    const float* g = G.g + row * Dk + c0;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        a[kb][hf] = ok ? *reinterpret_cast<const floatx4*>(g + 32 * kb + 16 * hf)
+                       : floatx4{f, f, f, f};
+  }
+}
+
+// alpha from the values gate_load_blocks gave, in place; `sc` = exp(A_h) of the
+// row's head for the bounded gate
+template <int KIND, int NB>
+__device__ __forceinline__ void gate_finish_blocks(const Gate& G, float sc, floatx4 (&a)[NB][2]) {
+  if constexpr (KIND == GATE_LOG || KIND == GATE_BOUNDED) {
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a[kb][hf][i] = KIND == GATE_LOG ? exp_hw(a[kb][hf][i])
+                                          : gate_bounded_hw(a[kb][hf][i], sc, G.g_min);
+  }
+}
+
 // Operand fragment for one 16x32 (A) or 32x16 (B) k-block.
 template <bool F32> struct Frag;
 template <> struct Frag<false> { bf16x8 hi, lo; };

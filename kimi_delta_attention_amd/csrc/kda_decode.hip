@@ -28,11 +28,11 @@ __device__ __forceinline__ float ld_in<float>(const float* p, size_t i) { return
 template <>
 __device__ __forceinline__ float ld_in<bf16>(const bf16* p, size_t i) { return (float)p[i]; }
 
-template <int DK, int DV, typename TIn, typename TOut>
+template <int DK, int DV, typename TIn, typename TOut, int KIND>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta, float* __restrict__ state,
-    TOut* __restrict__ o) {
+    Gate gate, const float* __restrict__ beta, float* __restrict__ state, TOut* __restrict__ o,
+    int H) {
   constexpr int CW = DV / 4;       // value columns per wave
   constexpr int LPR = CW / 4;      // lanes sharing one row (float4 each)
   constexpr int RPP = 64 / LPR;    // rows covered per pass
@@ -49,20 +49,36 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   float* S = state + (size_t)tile * DK * DV;
   const TIn* qt = q + (size_t)tile * DK;
   const TIn* kt = k + (size_t)tile * DK;
-  const float* at = alpha + (size_t)tile * DK;
 
   floatx4 s[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i)
     s[i] = *reinterpret_cast<const floatx4*>(S + (size_t)(ro + RPP * i) * DV + col);
 
-  float kr[NP], qr[NP];
+  float kr[NP], qr[NP], al[NP];
+  if constexpr (KIND == GATE_BOUNDED) {
+    // the LPR lanes that hold the same rows each evaluate NP / LPR of the gates
+    // (two exponentials each) and read the others' across the group
+    constexpr int PER = NP / LPR;
+    static_assert(PER * LPR == NP, "rows per lane split");
+    float mine[PER];
+    const float sc = expf(gate.a_log[tile % H]);
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      mine[j] = gate_bounded(gate.g[(size_t)tile * DK + ro + RPP * (PER * cg + j)], sc,
+                             gate.g_min);
+    const int base = lane - cg;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) al[i] = __shfl(mine[i % PER], base + i / PER, 64);
+  } else {
+    gate_alpha_rows<KIND, NP, RPP>(gate, tile, DK, ro, 0, al);
+  }
   floatx4 old = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
   float qk = 0.f;
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int r = ro + RPP * i;
-    const float a = at[r];
+    const float a = al[i];
     kr[i] = ld_in(kt, r);
     qr[i] = ld_in(qt, r);
     s[i] *= a;                     // Sbar = Diag(alpha) S
@@ -100,12 +116,24 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   }
 }
 
+template <int DK, int DV, typename TIn, typename TOut, int KIND>
+static hipError_t launch_decode_k(const DecodeArgs& a) {
+  hipLaunchKernelGGL((decode_step_kernel<DK, DV, TIn, TOut, KIND>), dim3(a.B * a.H), dim3(256), 0,
+                     (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
+                     a.gate, a.beta, a.state, (TOut*)a.o, a.H);
+  return hipGetLastError();
+}
+
+// one instantiation per gate kind: the per-row decay is a straight-line loop
 template <int DK, int DV, typename TIn, typename TOut>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
-  hipLaunchKernelGGL((decode_step_kernel<DK, DV, TIn, TOut>), dim3(a.B * a.H), dim3(256), 0,
-                     (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                     a.alpha, a.beta, a.state, (TOut*)a.o);
-  return hipGetLastError();
+  switch (a.gate.kind) {
+    case GATE_LOG: return launch_decode_k<DK, DV, TIn, TOut, GATE_LOG>(a);
+    case GATE_BOUNDED: return launch_decode_k<DK, DV, TIn, TOut, GATE_BOUNDED>(a);
+    case GATE_SCALAR: return launch_decode_k<DK, DV, TIn, TOut, GATE_SCALAR>(a);
+    case GATE_NONE: return launch_decode_k<DK, DV, TIn, TOut, GATE_NONE>(a);
+    default: return launch_decode_k<DK, DV, TIn, TOut, GATE_ALPHA>(a);
+  }
 }
 
 template <int DK, int DV>

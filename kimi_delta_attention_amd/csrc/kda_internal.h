@@ -4,11 +4,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kda_common.h"
+
 namespace kda {
 
 struct DecodeArgs {
   const void *q, *k, *v;
-  const float *alpha, *beta;
+  Gate gate;
+  const float* beta;
   float* state;
   void* o;
   bool qkv_bf16, o_bf16;
@@ -18,7 +21,8 @@ struct DecodeArgs {
 
 struct PrefillArgs {
   const void *q, *k, *v;
-  const float *alpha, *beta;
+  Gate gate;
+  const float* beta;
   const float* initial_state;
   float* final_state;
   void* o;

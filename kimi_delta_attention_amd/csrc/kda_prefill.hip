@@ -98,10 +98,10 @@ struct Plan {
 
 // One workgroup per (sequence, head, 64-wide value slice), state carried
 // across the sequence's chunks.
-template <int DK, typename TOut>
+template <int DK, typename TOut, int KIND>
 __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta,
+    Gate gate, const float* __restrict__ beta,
     const float* __restrict__ s_init, float* __restrict__ s_final, TOut* __restrict__ o,
     const int32_t* __restrict__ cu_seqlens, int n_seq, int T, int H, int DV) {
   using L = Plan<DK, BV>;
@@ -166,6 +166,8 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
   }
   const int vcol0 = sl * BV;
   const int vh0 = 32 * hh;  // this wave's value columns within the slice
+  // per-head logit scale exp(A_h) of the bounded gate
+  const float gsc = KIND == GATE_BOUNDED ? expf(gate.a_log[h]) : 1.f;
 
   // state: wave (w, hh) owns key rows [w*RPW, (w+1)*RPW) x value columns vh0..vh0+31
   floatx4 Sacc[RTW][NCH];
@@ -214,6 +216,10 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       in.b = okc ? beta[thc] : 0.f;
       return;
     }
+    if (part == 2) {
+      gate_load_blocks<KIND, NKH>(gate, okc, thc, DK, 32 * NKH * hh + 4 * g, in.a);
+      return;
+    }
 #pragma unroll
     for (int kk = 0; kk < NKH; ++kk)
 #pragma unroll
@@ -223,15 +229,15 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
                                           : uint2v{0u, 0u};
         if (part == 1) in.q[kk][hf] = okc ? *reinterpret_cast<const uint2v*>(q + thc * DK + c)
                                           : uint2v{0u, 0u};
-        if (part == 2) in.a[kk][hf] = okc ? *reinterpret_cast<const floatx4*>(alpha + thc * DK + c)
-                                          : floatx4{1.f, 1.f, 1.f, 1.f};
       }
   };
   Desc cur = Desc{start, (int)(len < CH ? len : CH), h, 0};
   bool have = len > 0;
   ChunkIn in;
-  if (have)
+  if (have) {
     for (int part = 0; part < 4; ++part) load_part(cur, in, part);
+    gate_finish_blocks<KIND, NKH>(gate, gsc, in.a);
+  }
 
   while (have) {
     const long long c1 = cur.c0 + CH;
@@ -494,6 +500,9 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       for (int e = 0; e < 4; ++e) x4[e] = (j0 + e <= rr) ? t4[e] * b4[e] : 0.f;
       st_split4(TB + rr * ldT + j0, loT, x4);
     }
+    // the next chunk's gate values (fetched after the scan; only k and q were
+    // fetched after them) become alpha here, off the scan's dependency chain
+    if (more) gate_finish_blocks<KIND, NKH>(gate, gsc, in.a);
     *reinterpret_cast<uint4v*>(VS + r * ldV + vh0 + 8 * g) = in.v;
     if (more) load_part(nxt, in, 3);
     __syncthreads();
@@ -691,10 +700,12 @@ hipError_t set_lds(K kern, int bytes) {
   return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <int DK, typename TOut>
-hipError_t launch_fused(const PrefillArgs& a) {
+// one instantiation per gate kind: the alpha path carries no gate code, and the
+// transforms of the other kinds run where their values are used
+template <int DK, typename TOut, int KIND>
+hipError_t launch_fused_k(const PrefillArgs& a) {
   using L = Plan<DK, BV>;
-  auto kern = prefill_bf16_kernel<DK, TOut>;
+  auto kern = prefill_bf16_kernel<DK, TOut, KIND>;
   static bool attr_set = false;  // per instantiation; idempotent if raced
   if (!attr_set) {
     if (hipError_t e = set_lds(kern, L::total); e != hipSuccess) return e;
@@ -702,10 +713,21 @@ hipError_t launch_fused(const PrefillArgs& a) {
   }
   const int grid = a.n_seq * a.H * (a.Dv / BV);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH), L::total, (hipStream_t)a.stream,
-                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.alpha, a.beta,
+                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.gate, a.beta,
                      a.initial_state, a.final_state, (TOut*)a.o, a.cu_seqlens, a.n_seq, a.T, a.H,
                      a.Dv);
   return hipGetLastError();
+}
+
+template <int DK, typename TOut>
+hipError_t launch_fused(const PrefillArgs& a) {
+  switch (a.gate.kind) {
+    case GATE_LOG: return launch_fused_k<DK, TOut, GATE_LOG>(a);
+    case GATE_BOUNDED: return launch_fused_k<DK, TOut, GATE_BOUNDED>(a);
+    case GATE_SCALAR: return launch_fused_k<DK, TOut, GATE_SCALAR>(a);
+    case GATE_NONE: return launch_fused_k<DK, TOut, GATE_NONE>(a);
+    default: return launch_fused_k<DK, TOut, GATE_ALPHA>(a);
+  }
 }
 
 int device_cus() {

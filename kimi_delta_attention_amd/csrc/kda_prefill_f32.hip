@@ -114,7 +114,7 @@ __device__ __forceinline__ void pair_of(int w, int p, int& mm, int& n) {
 template <int DK, int BV, bool F32OPS, typename TIn, typename TOut>
 __global__ __launch_bounds__(NTH) void prefill_f32_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta,
+    Gate gate, const float* __restrict__ beta,
     const float* __restrict__ s_init, float* __restrict__ s_final, TOut* __restrict__ o,
     const int32_t* __restrict__ cu_seqlens, int n_seq, int T, int H, int DV) {
   using L = Layout<DK, BV, F32OPS>;
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(NTH) void prefill_f32_kernel(
         const size_t off = ((size_t)(tok0 + r) * H + h) * DK + ch;
         kf[s][j] = ok ? k[off] : (TIn)0.f;
         qf[s][j] = ok ? q[off] : (TIn)0.f;
-        const float a = ok ? alpha[off] : 1.f;
+        const float a = ok ? gate_alpha1(gate, (size_t)(tok0 + r) * H + h, DK, ch, h) : 1.f;
         run = (j == 0) ? a : run * a;
         Pf[s][j] = run;
       }
@@ -516,7 +516,7 @@ static hipError_t launch_t(const PrefillArgs& a) {
   }
   const int grid = a.n_seq * a.H * (a.Dv / BV);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH), L::total, (hipStream_t)a.stream,
-                     (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.alpha, a.beta,
+                     (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.gate, a.beta,
                      a.initial_state, a.final_state, (TOut*)a.o, a.cu_seqlens, a.n_seq, a.T, a.H,
                      a.Dv);
   return hipGetLastError();

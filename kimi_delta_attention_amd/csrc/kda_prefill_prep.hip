@@ -89,7 +89,7 @@ __device__ __forceinline__ float scaled_sum(float b, float x, float y) { return 
 template <int DK, int DV>
 __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta,
+    Gate gate, const float* __restrict__ beta,
     const int32_t* __restrict__ cu_seqlens, int n_seq, int T, int H, unsigned char* __restrict__ img,
     const int32_t* __restrict__ chunk_off, long long tok_lo, long long tok_hi, int cap) {
   using L = PrepPlan<DK, DV>;
@@ -173,8 +173,7 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
         const int c = 32 * kb + 16 * hf + 4 * gl;
         kin[kb][hf] = okc ? *reinterpret_cast<const uint2v*>(k + thc * DK + c) : uint2v{0u, 0u};
         qin[kb][hf] = okc ? *reinterpret_cast<const uint2v*>(q + thc * DK + c) : uint2v{0u, 0u};
-        const floatx4 a4 = okc ? *reinterpret_cast<const floatx4*>(alpha + thc * DK + c)
-                               : floatx4{1.f, 1.f, 1.f, 1.f};
+        const floatx4 a4 = okc ? gate_alpha4(gate, thc, DK, c, d.hd) : floatx4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) Pv[kb][4 * hf + i] = a4[i];
       }
@@ -548,7 +547,7 @@ hipError_t launch_t(const PrefillArgs& a, unsigned char* img, const int32_t* chu
     attr_set = true;
   }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH_P), L::total, (hipStream_t)a.stream, (const bf16*)a.q,
-                     (const bf16*)a.k, (const bf16*)a.v, a.alpha, a.beta, a.cu_seqlens, a.n_seq, a.T, a.H,
+                     (const bf16*)a.k, (const bf16*)a.v, a.gate, a.beta, a.cu_seqlens, a.n_seq, a.T, a.H,
                      img, chunk_off, tok_lo, tok_hi, cap);
   return hipGetLastError();
 }

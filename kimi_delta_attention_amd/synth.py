@@ -17,6 +17,10 @@ Distributions (the workload recipe):
   stress input (mean alpha about 0.97); ``alpha_one=True`` gives alpha = 1.
 * beta = sigmoid(N(0, 1)) in fp64, stored fp32.
 * initial state ~ N(0, state_std^2) fp32 when requested.
+* decay in another gate parametrization (``make_gate``): 'log' stores
+  -softplus(z + shift) (the same decays, in log space); 'bounded' stores the
+  logits z ~ N(0, 1) with a per-head log scale A ~ U(-1, 1); 'scalar' stores
+  exp(-softplus(z + shift)) with one z per (token, head); 'none' stores nothing.
 
 Token tensors are drawn in fixed blocks of ``BLOCK`` tokens, each from its own
 generator seeded with (seed, block index), so a long input never needs an fp64
@@ -132,6 +136,29 @@ def make_varlen(lengths: list[int], H: int, Dk: int, Dv: int, *, seed: int,
     return KdaInputs(torch.cat(qs)[None], torch.cat(ks)[None], torch.cat(vs)[None],
                      torch.cat(as_)[None], torch.cat(bs)[None], st,
                      torch.tensor(cu, dtype=torch.int32, device=device))
+
+
+def make_gate(kind: str, lead: tuple, H: int, Dk: int, *, seed: int, shift: float = 1.0,
+              device="cpu"):
+    """Seeded decay tensor for a gate parametrization (see the module docstring):
+    returns (gate, a_log) -- gate [*lead, H, Dk] fp32 ([*lead, H] for 'scalar',
+    None for 'none'), a_log [H] fp32 for 'bounded', else None."""
+    g = _gen(device, seed * 1_000_033 + 17)
+    lead = tuple(lead)
+    if kind == "none":
+        return None, None
+    if kind == "scalar":
+        z = torch.randn(*lead, H, generator=g, device=device, dtype=torch.float64)
+        return torch.exp(-_softplus64(z + shift)).to(torch.float32), None
+    z = torch.randn(*lead, H, Dk, generator=g, device=device, dtype=torch.float64)
+    if kind == "alpha":
+        return torch.exp(-_softplus64(z + shift)).to(torch.float32), None
+    if kind == "log":
+        return (-_softplus64(z + shift)).to(torch.float32), None
+    if kind == "bounded":
+        a_log = torch.rand(H, generator=g, device=device, dtype=torch.float64) * 2.0 - 1.0
+        return z.to(torch.float32), a_log.to(torch.float32)
+    raise ValueError(f"unknown gate kind {kind!r}")
 
 
 # The workloads, named by what they are.

@@ -152,6 +152,57 @@ def recurrent_matrix(q, k, v, alpha, beta, initial_state=None):
     return o, sf
 
 
+GATES = ("alpha", "log", "bounded", "scalar", "none")
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    """Logistic function in fp64, evaluated without overflow for either sign."""
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    e = np.exp(x[~pos])
+    out[~pos] = e / (1.0 + e)
+    return out
+
+
+def gate_alpha(kind: str, gate, shape, a_log=None, g_min: float = -5.0) -> np.ndarray:
+    """Per-key-channel decay alpha in fp64, shape ``shape`` = [..., H, Dk], from
+    one of the gate parametrizations the pages describe (the values handed to the
+    GPU, upcast exactly):
+
+    * ``alpha``   -- alpha itself, [..., H, Dk].
+    * ``log``     -- g = log alpha, [..., H, Dk]; alpha = exp(g).  The FLA code
+      keeps the gate in log space ("Kimi Delta Attention 完全拆解", section
+      "KDA 的核心：让遗忘从一个标量细化为逐通道向量").
+    * ``bounded`` -- K3's lower-bounded gate: logits z [..., H, Dk] and a per-head
+      log scale A (``a_log`` [H]); g = g_min * Sigmoid(exp(A_h) z), alpha = exp(g),
+      g_min = -5 on the pages ("Kimi K3 的 KDA" section 6; "Kimi K3模型架构详解"
+      section 3.4).
+    * ``scalar``  -- one alpha per token and head, [..., H], the same for every
+      key channel: the gated DeltaNet case of a vector gate with equal
+      components ("Kimi Delta Attention 完全拆解", section "KDA 的核心").
+    * ``none``    -- alpha = 1: DeltaNet (same section).
+    """
+    shape = tuple(shape)
+    if kind == "alpha":
+        a = _f64(gate)
+    elif kind == "log":
+        a = np.exp(_f64(gate))
+    elif kind == "bounded":
+        z = _f64(gate)
+        scale = np.exp(_f64(a_log))  # [H]
+        a = np.exp(float(g_min) * _sigmoid(scale[:, None] * z))
+    elif kind == "scalar":
+        a = np.repeat(_f64(gate)[..., None], shape[-1], axis=-1)
+    elif kind == "none":
+        a = np.ones(shape, dtype=np.float64)
+    else:
+        raise ValueError(f"unknown gate kind {kind!r}")
+    if a.shape != shape:
+        raise ValueError(f"gate {kind!r} gives shape {a.shape}, expected {shape}")
+    return np.ascontiguousarray(a)
+
+
 def rel_l2(x, ref) -> float:
     """||x - ref||_2 / ||ref||_2 over the whole tensor, in fp64."""
     x = _f64(x)

@@ -86,6 +86,19 @@ def main():
         row(f"{kind} (B1 H8 T4096 d128)", 2e-3, oracle.rel_l2(o.cpu(), ro),
             oracle.rel_l2(s.cpu(), rs), "oracle, all heads (stress input)")
 
+    for kind in ("log", "bounded", "scalar", "none"):
+        inp = synth.make_dense(1, 4096, 8, 128, 128, seed=78, device=d)
+        gate, a_log = synth.make_gate(kind, (1, 4096), 8, 128, seed=79, device=d)
+        o, s = kda.prefill_chunked(inp.q, inp.k, inp.v, gate, inp.beta, initial_state=inp.state,
+                                   gate=kind, a_log=a_log)
+        torch.cuda.synchronize()
+        alpha = oracle.gate_alpha(kind, None if gate is None else gate.cpu().numpy(), inp.q.shape,
+                                  a_log=None if a_log is None else a_log.cpu().numpy())
+        ro, rs = oracle.recurrent(inp.q.cpu(), inp.k.cpu(), inp.v.cpu(), alpha, inp.beta.cpu(),
+                                  initial_state=inp.state.cpu())
+        row(f"gate '{kind}' (B1 H8 T4096 d128)", 2e-3, oracle.rel_l2(o.cpu(), ro),
+            oracle.rel_l2(s.cpu(), rs), "oracle fed the oracle's own alpha of the gate, all heads")
+
     if "--long" in sys.argv:
         w = synth.WORKLOADS["long_1m"]
         inp = synth.make_dense(w["B"], w["T"], w["H"], w["D"], w["D"], seed=w["seed"],

@@ -131,3 +131,61 @@ def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 4, 1, 64)
     with pytest.raises(ValueError):
         kda.prefill_chunked(q, q, q, q, torch.zeros(1, 4, 1))
+
+
+def _gated(kind, gate=FAKE, a_log=None, g_min=0.0, null_desc=False, entry="chunked", **over):
+    lib = kda.load()
+    g = _lib._Gate(kind, gate, a_log, g_min)
+    gp = None if null_desc else ctypes.byref(g)
+    a = dict(qd=BF16, chunk=64, Dk=128)
+    a.update(over)
+    if entry == "chunked":
+        return lib.kda_prefill_chunked_gated(FAKE, FAKE, FAKE, a["qd"], gp, FAKE, None, None,
+                                             FAKE, F32, 1, 128, 2, a["Dk"], 128, a["chunk"],
+                                             None, 0, None)
+    if entry == "varlen":
+        return lib.kda_prefill_varlen_gated(FAKE, FAKE, FAKE, a["qd"], gp, FAKE, FAKE, 1, 128,
+                                            None, None, FAKE, F32, 2, a["Dk"], 128, a["chunk"],
+                                            None, 0, None)
+    return lib.kda_decode_step_gated(FAKE, FAKE, FAKE, a["qd"], gp, FAKE, FAKE, FAKE, F32, 4, 2,
+                                     a["Dk"], 128, None)
+
+
+ALPHA, LOG, BOUNDED, SCALAR, NONE = (_lib.GATES[n] for n in
+                                     ("alpha", "log", "bounded", "scalar", "none"))
+
+
+@pytest.mark.parametrize("entry", ["chunked", "varlen", "decode"])
+@pytest.mark.parametrize("args,expect", [
+    (dict(kind=ALPHA, null_desc=True), INVALID),          # no descriptor
+    (dict(kind=9), INVALID),                              # unknown kind
+    (dict(kind=-1), INVALID),
+    (dict(kind=LOG, gate=None), INVALID),                 # tensor missing
+    (dict(kind=SCALAR, gate=None), INVALID),
+    (dict(kind=BOUNDED, a_log=None, g_min=-5.0), INVALID),
+    (dict(kind=BOUNDED, a_log=FAKE + 2, g_min=-5.0), INVALID),
+    (dict(kind=BOUNDED, a_log=FAKE, g_min=-5.5), INVALID),  # bound outside [-5, 0)
+    (dict(kind=BOUNDED, a_log=FAKE, g_min=0.0), INVALID),
+    (dict(kind=BOUNDED, a_log=FAKE, g_min=float("nan")), INVALID),
+    (dict(kind=ALPHA, gate=FAKE + 2), INVALID),           # not even 4-byte aligned
+    # accepted descriptors, stopped by an unsupported shape before any launch
+    (dict(kind=NONE, gate=None, Dk=96), UNSUPPORTED),
+    (dict(kind=SCALAR, gate=FAKE + 4, Dk=96), UNSUPPORTED),
+    (dict(kind=BOUNDED, a_log=FAKE + 4, g_min=-5.0, Dk=96), UNSUPPORTED),
+    (dict(kind=BOUNDED, a_log=FAKE, g_min=-0.5, Dk=96), UNSUPPORTED),
+])
+def test_gate_validation(entry, args, expect):
+    assert _gated(entry=entry, **args) == expect
+    assert len(kda.load().kda_last_error_message()) > 0
+
+
+def test_gate_alignment_per_kind():
+    """bf16 prefill reads a per-channel gate with 16-byte loads; a scalar gate and
+    the decode step need only 4-byte alignment."""
+    for kind in (ALPHA, LOG):
+        assert _gated(kind=kind, gate=FAKE + 8) == INVALID
+        assert _gated(kind=kind, gate=FAKE + 8, entry="varlen") == INVALID
+        assert _gated(kind=kind, gate=FAKE + 8, entry="decode", Dk=96) == UNSUPPORTED
+        assert _gated(kind=kind, gate=FAKE + 8, qd=F32, Dk=96) == UNSUPPORTED
+    assert _gated(kind=BOUNDED, gate=FAKE + 8, a_log=FAKE, g_min=-5.0) == INVALID
+    assert _gated(kind=SCALAR, gate=FAKE + 4, chunk=32) == UNSUPPORTED

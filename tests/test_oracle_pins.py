@@ -313,3 +313,68 @@ def test_bad_arguments_rejected():
         oracle.recurrent(q, k, v[:, :3], a, b)
     with pytest.raises(ValueError):
         oracle.recurrent(q, k, v, a, b, cu_seqlens=[0, 3, 2, 4])
+
+
+def test_bounded_gate_closed_forms():
+    """K3's bounded gate g = g_min Sigmoid(e^{A_h} z), alpha = e^g ("Kimi K3 的 KDA"
+    section 6; "Kimi K3模型架构详解" section 3.4): Sigmoid(0) = 1/2 gives
+    alpha = e^{g_min/2}; the logit limits give e^{g_min} and 1; e^{A_h} rescales
+    the logit of head h only; alpha stays in (e^{g_min}, 1), so a 16-token tile
+    decays by at most e^{16 g_min} = e^{-80} > 1e-35 at g_min = -5."""
+    H, Dk = 3, 4
+    z = np.zeros((2, H, Dk))
+    a = oracle.gate_alpha("bounded", z, z.shape, a_log=np.array([0.0, 1.0, -2.0]))
+    assert np.allclose(a, np.exp(-2.5), rtol=0, atol=1e-15)
+    a = oracle.gate_alpha("bounded", z, z.shape, a_log=np.zeros(H), g_min=-3.0)
+    assert np.allclose(a, np.exp(-1.5), rtol=0, atol=1e-15)
+    big = np.full((1, H, Dk), 800.0)
+    assert np.allclose(oracle.gate_alpha("bounded", big, big.shape, a_log=np.zeros(H)),
+                       np.exp(-5.0), rtol=1e-15, atol=0)
+    assert np.all(oracle.gate_alpha("bounded", -big, big.shape, a_log=np.zeros(H)) == 1.0)
+    # head 1 has scale e^{ln 2} = 2: its alpha at z equals head 0's at 2 z
+    rng = np.random.default_rng(3)
+    zz = rng.standard_normal((5, 2, Dk))
+    a = oracle.gate_alpha("bounded", zz, zz.shape, a_log=np.array([0.0, np.log(2.0)]))
+    z2 = zz.copy(); z2[:, 0] = 2.0 * zz[:, 1]
+    b = oracle.gate_alpha("bounded", z2, z2.shape, a_log=np.zeros(2))
+    assert np.allclose(a[:, 1], b[:, 0], rtol=1e-14, atol=0)
+    # one value by hand: z = 1, A = 0: Sigmoid(1) = e / (1 + e)
+    one = np.ones((1, 1, 1))
+    ref = np.exp(-5.0 * np.e / (1.0 + np.e))
+    assert abs(oracle.gate_alpha("bounded", one, one.shape, a_log=np.zeros(1))[0, 0, 0] - ref) \
+        < 1e-16
+    # range and the 16-token tile bound
+    zz = rng.standard_normal((4000, 1, 8)) * 30.0
+    a = oracle.gate_alpha("bounded", zz, zz.shape, a_log=np.zeros(1))
+    assert np.all(a >= np.exp(-5.0)) and np.all(a <= 1.0)
+    assert np.exp(-5.0) ** 16 > 1e-35
+
+
+def test_log_scalar_and_none_gates():
+    """The log-space gate is log alpha; the scalar gate puts one alpha on every key
+    channel; no gate is alpha = 1 ("Kimi Delta Attention 完全拆解", sections "KDA 的核心"
+    and "Gated DeltaNet 仍只有一个遗忘旋钮").  With a scalar gate the decay commutes
+    with the erase, alpha (I - b k k^T) S = (I - b k k^T)(alpha S), so decaying
+    before or after the erase gives the same result -- which fails if the per-token
+    value were spread over the wrong axis or differed across channels."""
+    rng = np.random.default_rng(11)
+    B, T, H, Dk, Dv = 1, 24, 2, 8, 5
+    a = rng.uniform(0.2, 1.0, (B, T, H, Dk))
+    assert np.allclose(oracle.gate_alpha("log", np.log(a), a.shape), a, rtol=1e-15, atol=0)
+    assert np.all(oracle.gate_alpha("none", None, a.shape) == 1.0)
+    sc = rng.uniform(0.2, 1.0, (B, T, H))
+    sa = oracle.gate_alpha("scalar", sc, a.shape)
+    assert np.all(sa == sc[..., None])
+    q, k, v, _, b = _rand(rng, B, T, H, Dk, Dv)
+    s0 = rng.standard_normal((B, H, Dk, Dv))
+    o1, S1 = oracle.recurrent(q, k, v, sa, b, initial_state=s0)
+    o2, S2 = oracle.recurrent(q, k, v, sa, b, initial_state=s0, mode="erase_then_decay")
+    assert np.max(np.abs(S1 - S2)) < 1e-12 and np.max(np.abs(o1 - o2)) < 1e-12
+    # ... and a per-channel gate does not commute (the order the pages fix matters)
+    o3, _ = oracle.recurrent(q, k, v, a, b, initial_state=s0)
+    o4, _ = oracle.recurrent(q, k, v, a, b, initial_state=s0, mode="erase_then_decay")
+    assert np.max(np.abs(o3 - o4)) > 1e-3
+    with pytest.raises(ValueError):
+        oracle.gate_alpha("scalar", sc[:, :, :1], a.shape)
+    with pytest.raises(ValueError):
+        oracle.gate_alpha("softplus", a, a.shape)
