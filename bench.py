@@ -80,8 +80,8 @@ DECODE_SOURCES = ["kimi_delta_attention_amd/csrc/kda_decode.hip",
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=50)
     args = ap.parse_args()
@@ -217,9 +217,9 @@ def main():
                                                  PREFILL_SOURCES),
                      "traffic_unit": "HBM bytes per kda_prefill_chunked call (rocprofv3 "
                                      "FETCH_SIZE + WRITE_SIZE of its kernels, copy-calibrated)",
-                     "kernel": ("kda_prefill_chunked, two-pass: prefill_prep_kernel<128, 128> "
+                     "kernel": ("kda_prefill_chunked, two-pass: prefill_prep_kernel<128, 128, alpha gate> "
                                 "+ prefill_state_kernel<128, 128>" if two_pass else
-                                "kda_prefill_chunked, fused: prefill_bf16_kernel<128, fp32 out>"),
+                                "kda_prefill_chunked, fused: prefill_bf16_kernel<128, fp32 out, alpha gate>"),
                      "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_ms": avg_launch_ms,
                      "mfma_frac_pages_flops": tflops / BF16_PEAK_TFLOPS},

@@ -72,36 +72,12 @@ __device__ __forceinline__ float gate_bounded(float z, float scale, float g_min)
 // about 1 ulp each): e^x = 2^(x log2 e).  For the arguments a gate produces
 // (|x| <= 5 log2 e in the outer exponential of the bounded gate) the rounding of
 // x log2 e adds under 1e-6 relative error to alpha.  The bf16 prefill kernels
-// use these (both schedules the same ones); a logit of -inf still gives alpha 1.
+// use these (both schedules, through gate_finish_blocks); a logit of -inf still
+// gives alpha 1.
 constexpr float kLog2e = 1.44269504088896341f;
 __device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 __device__ __forceinline__ float gate_bounded_hw(float z, float scale, float g_min) {
   return exp_hw(g_min * __builtin_amdgcn_rcpf(1.f + exp_hw(-scale * z)));
-}
-
-// alpha of key channels c..c+3 (c a multiple of 4, 16-byte aligned rows), the
-// bf16 first pass's form (hardware exponentials, like gate_finish_blocks)
-__device__ __forceinline__ floatx4 gate_alpha4(const Gate& G, size_t row, int Dk, int c, int h) {
-  switch (G.kind) {
-    case GATE_LOG: {
-      const floatx4 x = *reinterpret_cast<const floatx4*>(G.g + row * Dk + c);
-      return floatx4{exp_hw(x[0]), exp_hw(x[1]), exp_hw(x[2]), exp_hw(x[3])};
-    }
-    case GATE_BOUNDED: {
-      const floatx4 x = *reinterpret_cast<const floatx4*>(G.g + row * Dk + c);
-      const float sc = expf(G.a_log[h]);
-      return floatx4{gate_bounded_hw(x[0], sc, G.g_min), gate_bounded_hw(x[1], sc, G.g_min),
-                     gate_bounded_hw(x[2], sc, G.g_min), gate_bounded_hw(x[3], sc, G.g_min)};
-    }
-    case GATE_SCALAR: {
-      const float a = G.g[row];
-      return floatx4{a, a, a, a};
-    }
-    case GATE_NONE:
-      return floatx4{1.f, 1.f, 1.f, 1.f};
-    default:
-      return *reinterpret_cast<const floatx4*>(G.g + row * Dk + c);
-  }
 }
 
 // alpha of one key channel c
@@ -141,36 +117,26 @@ __device__ __forceinline__ void gate_alpha_rows(const Gate& G, size_t row, int D
   }
 }
 
-// Gate values of the key channels c0 + 32 kb + 16 hf + {0..3} (kb < NB, hf < 2)
-// of one row (c0 a multiple of 4, 16-byte aligned rows), as stored, for a gate
-// kind fixed at compile time: a prefetch issues the loads only, and
-// gate_finish_blocks turns them into alpha where they are used.  A row with !ok
-// reads nothing and gets the stored value whose alpha is 1 (1 for alpha, 0 for
-// log alpha, a logit of -inf for the bounded gate).
-template <int KIND, int NB>
-__device__ __forceinline__ void gate_load_blocks(const Gate& G, bool ok, size_t row, int Dk,
-                                                 int c0, floatx4 (&a)[NB][2]) {
-  if constexpr (KIND == GATE_SCALAR || KIND == GATE_NONE) {
-    float x = 1.f;
-    if constexpr (KIND == GATE_SCALAR) x = ok ? G.g[row] : 1.f;
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) a[kb][hf] = floatx4{x, x, x, x};
+// Gate values of the key channels c..c+3 of one row (c a multiple of 4, 16-byte
+// aligned rows), as stored, for a gate kind fixed at compile time: a prefetch
+// issues the loads only, and gate_finish_blocks turns them into alpha where they
+// are used.  A row with !ok reads nothing and gets the stored value whose alpha
+// is 1 (1 for alpha, 0 for log alpha, a logit of -inf for the bounded gate).
+template <int KIND>
+__device__ __forceinline__ floatx4 gate_load4(const Gate& G, bool ok, size_t row, int Dk, int c) {
+  if constexpr (KIND == GATE_SCALAR) {
+    const float x = ok ? G.g[row] : 1.f;
+    return floatx4{x, x, x, x};
+  } else if constexpr (KIND == GATE_NONE) {
+    return floatx4{1.f, 1.f, 1.f, 1.f};
   } else {
     constexpr float f = KIND == GATE_LOG ? 0.f : KIND == GATE_BOUNDED ? -INFINITY : 1.f;
-    const float* g = G.g + row * Dk + c0;
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        a[kb][hf] = ok ? *reinterpret_cast<const floatx4*>(g + 32 * kb + 16 * hf)
-                       : floatx4{f, f, f, f};
+    return ok ? *reinterpret_cast<const floatx4*>(G.g + row * Dk + c) : floatx4{f, f, f, f};
   }
 }
 
-// alpha from the values gate_load_blocks gave, in place; `sc` = exp(A_h) of the
-// row's head for the bounded gate
+// alpha from the values gate_load4 gave, [NB][2] blocks in place; `sc` =
+// exp(A_h) of the row's head for the bounded gate
 template <int KIND, int NB>
 __device__ __forceinline__ void gate_finish_blocks(const Gate& G, float sc, floatx4 (&a)[NB][2]) {
   if constexpr (KIND == GATE_LOG || KIND == GATE_BOUNDED) {

@@ -216,10 +216,6 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       in.b = okc ? beta[thc] : 0.f;
       return;
     }
-    if (part == 2) {
-      gate_load_blocks<KIND, NKH>(gate, okc, thc, DK, 32 * NKH * hh + 4 * g, in.a);
-      return;
-    }
 #pragma unroll
     for (int kk = 0; kk < NKH; ++kk)
 #pragma unroll
@@ -229,6 +225,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
                                           : uint2v{0u, 0u};
         if (part == 1) in.q[kk][hf] = okc ? *reinterpret_cast<const uint2v*>(q + thc * DK + c)
                                           : uint2v{0u, 0u};
+        if (part == 2) in.a[kk][hf] = gate_load4<KIND>(gate, okc, thc, DK, c);
       }
   };
   Desc cur = Desc{start, (int)(len < CH ? len : CH), h, 0};

@@ -86,7 +86,7 @@ struct PrepPlan {
 // half separately and adds them later
 __device__ __forceinline__ float scaled_sum(float b, float x, float y) { return b * x + b * y; }
 
-template <int DK, int DV>
+template <int DK, int DV, int KIND>
 __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     Gate gate, const float* __restrict__ beta,
@@ -166,6 +166,7 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     const int r = 16 * ((w4 + item) & 3) + (ln & 15);
     const bool okc = r < d.nv;
     const size_t thc = (size_t)(d.tok0 + r) * H + d.hd;
+    floatx4 a4[NKB][2];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -173,10 +174,13 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
         const int c = 32 * kb + 16 * hf + 4 * gl;
         kin[kb][hf] = okc ? *reinterpret_cast<const uint2v*>(k + thc * DK + c) : uint2v{0u, 0u};
         qin[kb][hf] = okc ? *reinterpret_cast<const uint2v*>(q + thc * DK + c) : uint2v{0u, 0u};
-        const floatx4 a4 = okc ? gate_alpha4(gate, thc, DK, c, d.hd) : floatx4{1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Pv[kb][4 * hf + i] = a4[i];
+        a4[kb][hf] = gate_load4<KIND>(gate, okc, thc, DK, c);
       }
+    gate_finish_blocks<KIND, NKB>(gate, KIND == GATE_BOUNDED ? expf(gate.a_log[d.hd]) : 1.f, a4);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Pv[kb][i] = a4[kb][i >> 2][i & 3];
     bt = okc ? beta[thc] : 0.f;
   };
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -535,11 +539,11 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
   }
 }
 
-template <int DK, int DV>
-hipError_t launch_t(const PrefillArgs& a, unsigned char* img, const int32_t* chunk_off,
+template <int DK, int DV, int KIND>
+hipError_t launch_k(const PrefillArgs& a, unsigned char* img, const int32_t* chunk_off,
                     long long tok_lo, long long tok_hi, int cap, int grid) {
   using L = PrepPlan<DK, DV>;
-  auto kern = prefill_prep_kernel<DK, DV>;
+  auto kern = prefill_prep_kernel<DK, DV, KIND>;
   static bool attr_set = false;  // per instantiation; idempotent if raced
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::total);
@@ -550,6 +554,21 @@ hipError_t launch_t(const PrefillArgs& a, unsigned char* img, const int32_t* chu
                      (const bf16*)a.k, (const bf16*)a.v, a.gate, a.beta, a.cu_seqlens, a.n_seq, a.T, a.H,
                      img, chunk_off, tok_lo, tok_hi, cap);
   return hipGetLastError();
+}
+
+// one instantiation per gate kind, as for the fused kernel
+template <int DK, int DV>
+hipError_t launch_t(const PrefillArgs& a, unsigned char* img, const int32_t* chunk_off,
+                    long long tok_lo, long long tok_hi, int cap, int grid) {
+  switch (a.gate.kind) {
+    case GATE_LOG: return launch_k<DK, DV, GATE_LOG>(a, img, chunk_off, tok_lo, tok_hi, cap, grid);
+    case GATE_BOUNDED:
+      return launch_k<DK, DV, GATE_BOUNDED>(a, img, chunk_off, tok_lo, tok_hi, cap, grid);
+    case GATE_SCALAR:
+      return launch_k<DK, DV, GATE_SCALAR>(a, img, chunk_off, tok_lo, tok_hi, cap, grid);
+    case GATE_NONE: return launch_k<DK, DV, GATE_NONE>(a, img, chunk_off, tok_lo, tok_hi, cap, grid);
+    default: return launch_k<DK, DV, GATE_ALPHA>(a, img, chunk_off, tok_lo, tok_hi, cap, grid);
+  }
 }
 
 }  // namespace
