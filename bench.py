@@ -7,9 +7,10 @@ the shape (two-pass: a first pass over all (chunk, head) items, then the
 state pass; one kda_prefill_chunked call, two kernel launches, workspace
 allocated once outside the timed region).  The line also carries the fused
 single-kernel schedule's time on the same step, the decode step's state
-bandwidth (64 sessions x 96 heads x 128x128 fp32 state, updated in place), the
-step's roofline position, and the fp64 CPU oracle timed on this host on the
-same prefill workload.
+bandwidth (64 sessions x 96 heads x 128x128 fp32 state, updated in place), a
+speculative-decoding round on the same sessions (verify 8 draft tokens, commit
+them), the step's roofline position, and the fp64 CPU oracle timed on this host
+on the same prefill workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 """
@@ -181,6 +182,44 @@ def main():
     print(f"bench: decode {dec_ms * 1e3:.1f} us/step, state {dec_state_gbs:.0f} GB/s",
           file=sys.stderr, flush=True)
 
+    # speculative round on the decode workload: verify NS draft tokens per session
+    # (state read only), then commit all of them (state read and written once)
+    NS = 8
+    sp = synth.make_dense(wd["B"], NS, wd["H"], wd["D"], wd["D"], seed=wd["seed"] + 100,
+                          state_std=wd["state_std"], device=d)
+    osp = torch.empty(wd["B"], NS, wd["H"], wd["D"], dtype=torch.float32, device=d)
+    nacc = torch.full((wd["B"],), NS, dtype=torch.int32, device=d)
+
+    def verify():
+        kda.decode_verify(sp.q, sp.k, sp.v, sp.alpha, sp.beta, sp.state, o=osp)
+
+    def commit():
+        kda.decode_commit(sp.k, sp.v, sp.alpha, sp.beta, nacc, sp.state)
+
+    def timed(f, reps):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ver_ms = timed(verify, args.decode_steps)
+    com_ms = timed(commit, args.decode_steps)
+    rnd_ms = timed(lambda: (verify(), commit()), args.decode_steps)
+    tok_in = NS * wd["B"] * wd["H"]  # token-heads per round
+    dd = wd["D"]
+    spec_bytes = (3 * sbytes // 2                               # state: read, read, write
+                  + tok_in * (2 * dd * 3 + 4 * dd + 4 + 4 * dd)  # verify: q k v, alpha, beta, o
+                  + tok_in * (2 * dd * 2 + 4 * dd + 4))          # commit: k v, alpha, beta
+    print(f"bench: spec round N={NS}: verify {ver_ms * 1e3:.1f} us + commit {com_ms * 1e3:.1f} us"
+          f" = {rnd_ms * 1e3:.1f} us ({NS * dec_ms / rnd_ms:.2f}x {NS} decode steps)",
+          file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu:
         import oracle
@@ -231,8 +270,17 @@ def main():
                    "roofline": {"bound": "hbm", "achieved": dec_total_gbs, "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": dec_total_gbs / HBM_PEAK_GBS,
                                 "traffic": measured_traffic(
-                                    "decode_step_kernel__decode_b64__hbm_counters.txt",
+                                    "decode_kernel_step__decode_b64__hbm_counters.txt",
                                     DECODE_SOURCES)}},
+        "spec_decode": {"workload": f"decode_b64, {NS} draft tokens per session, all accepted",
+                        "N": NS, "verify_us": ver_ms * 1e3, "commit_us": com_ms * 1e3,
+                        "us_per_round": rnd_ms * 1e3,
+                        "tokens_per_s": NS * wd["B"] / (rnd_ms / 1e3),
+                        "vs_single_steps": NS * dec_ms / rnd_ms,
+                        "algorithmic_bytes_per_round": spec_bytes,
+                        "roofline": {"bound": "hbm", "achieved": spec_bytes / (rnd_ms / 1e3) / 1e9,
+                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": spec_bytes / (rnd_ms / 1e3) / 1e9 / HBM_PEAK_GBS}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

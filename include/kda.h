@@ -18,9 +18,9 @@
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller, dense and
  *    row-major in the shapes given, aligned to their element size; state
- *    pointers (initial_state, final_state, state) and, for the bf16 prefill
- *    entry points, q, k, v and alpha 16-byte aligned; a prefill workspace
- *    256-byte aligned.  The library never allocates device memory and keeps
+ *    pointers (initial_state, final_state, state), the decode entry points'
+ *    q, k, v and per-channel gate, and, for the bf16 prefill entry points, q,
+ *    k, v and alpha 16-byte aligned; a prefill workspace 256-byte aligned.  The library never allocates device memory and keeps
  *    no state besides cached device properties.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Calls enqueue work asynchronously on it; a kernel fault surfaces at the
@@ -195,6 +195,7 @@ kda_status kda_prefill_varlen(const void* q, const void* k, const void* v, kda_d
  *   alpha  [B, H, Dk] fp32;       beta [B, H] fp32
  *   state  [B, H, Dk, Dv] fp32, updated IN PLACE
  *   o      [B, H, Dv] o_dtype
+ * q, k, v, alpha and state 16-byte aligned.
  */
 kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
                            const float* alpha, const float* beta, float* state,
@@ -229,6 +230,46 @@ kda_status kda_decode_step_gated(const void* q, const void* k, const void* v,
                                  kda_dtype qkv_dtype, const kda_gate* gate, const float* beta,
                                  float* state, void* o, kda_dtype o_dtype, int B, int H, int Dk,
                                  int Dv, void* stream);
+
+/*
+ * kda_decode_verify, kda_decode_commit -- speculative decoding with replay.
+ * The state is updated in place, so tokens a verifier rejects cannot be taken
+ * back once stepped; following "Kimi K3 的 KDA" (section 9, the inference
+ * kernel; section 11.1, the decode / spec-decode regime), no state copy is
+ * kept per draft position: the caller keeps the draft tokens' inputs, verify
+ * computes their outputs without touching the state, and commit replays the
+ * accepted ones into it.
+ *
+ * kda_decode_verify: for each of B sessions, N tokens (1 <= N <= 16) stepped
+ * in order from `state`; o[b, t] is the output of token t after tokens
+ * 0..t.  `state` is READ ONLY.
+ *   q, k   [B, N, H, Dk] qkv_dtype;  v [B, N, H, Dv] qkv_dtype
+ *   gate   kda_gate over [B, N, H, Dk] ([B, N, H] for KDA_GATE_SCALAR)
+ *   beta   [B, N, H] fp32
+ *   state  [B, H, Dk, Dv] fp32, not written
+ *   o      [B, N, H, Dv] o_dtype
+ *
+ * kda_decode_commit: for each session b, tokens 0..n_accept[b]-1 of the same
+ * k, v, gate and beta tensors replayed into `state` (IN PLACE), with exactly
+ * the arithmetic of kda_decode_step: the result is bitwise the state that
+ * n_accept[b] decode steps would leave, and verify's outputs are bitwise the
+ * steps' outputs.
+ *   n_accept  DEVICE int32 [B], read on the device and clamped to [0, N];
+ *             a session with 0 is left untouched
+ *
+ * Both: q, k, v, state and a per-channel gate 16-byte aligned, beta and
+ * n_accept 4-byte aligned, o element-aligned; Dk, Dv in {64, 128}.  B == 0 or
+ * N == 0 is a no-op; N > 16 returns KDA_ERR_UNSUPPORTED.  The three decode
+ * calls run one kernel (in three modes) and one per-token routine.
+ */
+kda_status kda_decode_verify(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                             const kda_gate* gate, const float* beta, const float* state,
+                             void* o, kda_dtype o_dtype, int B, int N, int H, int Dk, int Dv,
+                             void* stream);
+
+kda_status kda_decode_commit(const void* k, const void* v, kda_dtype qkv_dtype,
+                             const kda_gate* gate, const float* beta, const int32_t* n_accept,
+                             float* state, int B, int N, int H, int Dk, int Dv, void* stream);
 
 /*
  * kda_prefill_workspace_size -- workspace bytes that enable the two-pass

@@ -5,8 +5,8 @@ The operator runs in hand-written HIP kernels behind the C ABI of
 Importing it does not load the library; the first call does, and raises if the
 library has not been built.
 """
-from ._lib import (KdaError, decode_step, load, prefill_chunked, prefill_varlen,  # noqa: F401
-                   workspace_size)
+from ._lib import (MAX_DRAFT, KdaError, decode_commit, decode_step,  # noqa: F401
+                   decode_verify, load, prefill_chunked, prefill_varlen, workspace_size)
 
-__all__ = ["prefill_chunked", "prefill_varlen", "decode_step", "workspace_size", "load",
-           "KdaError"]
+__all__ = ["prefill_chunked", "prefill_varlen", "decode_step", "decode_verify", "decode_commit",
+           "workspace_size", "load", "KdaError", "MAX_DRAFT"]

@@ -20,6 +20,7 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
 
 EXPORTED = ("kda_prefill_chunked", "kda_prefill_varlen", "kda_decode_step",
             "kda_prefill_chunked_gated", "kda_prefill_varlen_gated", "kda_decode_step_gated",
+            "kda_decode_verify", "kda_decode_commit",
             "kda_prefill_workspace_size", "kda_prefill_varlen_workspace_size",
             "kda_prefill_two_pass_preferred", "kda_status_string", "kda_last_error_message")
 
@@ -68,6 +69,10 @@ def load() -> ctypes.CDLL:
     lib.kda_prefill_varlen_gated.restype = I
     lib.kda_decode_step_gated.argtypes = [P, P, P, I, G, P, P, P, I, I, I, I, I, P]
     lib.kda_decode_step_gated.restype = I
+    lib.kda_decode_verify.argtypes = [P, P, P, I, G, P, P, P, I, I, I, I, I, I, P]
+    lib.kda_decode_verify.restype = I
+    lib.kda_decode_commit.argtypes = [P, P, I, G, P, P, P, I, I, I, I, I, P]
+    lib.kda_decode_commit.restype = I
     lib.kda_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.kda_prefill_workspace_size.restype = Z
     lib.kda_prefill_varlen_workspace_size.argtypes = [I, I, I, I, I, I]
@@ -284,3 +289,58 @@ def decode_step(q, k, v, alpha, beta, state, out_dtype=torch.float32,
         _ptr(q), _ptr(k), _ptr(v), _dt(q), ctypes.byref(g), _ptr(beta), _ptr(state), _ptr(o),
         _dt(o), B, H, Dk, Dv, _stream(dev)))
     return o
+
+
+MAX_DRAFT = 16  # tokens per session of one verify / commit call
+
+
+def _multi_inputs(k, v, alpha, beta, gate, a_log, g_min, q=None):
+    B, N, H, Dk = k.shape
+    Dv = v.shape[-1]
+    dev = k.device
+    for t, n in ((k, "k"), (v, "v")) + (((q, "q"),) if q is not None else ()):
+        _need(t, n, k.dtype, dev)
+    if (q is not None and q.shape != k.shape) or v.shape != (B, N, H, Dv):
+        raise ValueError("inconsistent shapes")
+    g = _gate(gate, alpha, a_log, g_min, (B, N), H, Dk, dev)
+    _need(beta, "beta", torch.float32, dev)
+    if beta.shape != (B, N, H):
+        raise ValueError("beta must be [B, N, H]")
+    return B, N, H, Dk, Dv, dev, g
+
+
+def decode_verify(q, k, v, alpha, beta, state, out_dtype=torch.float32,
+                  o: torch.Tensor | None = None, gate: str = "alpha",
+                  a_log: torch.Tensor | None = None, g_min: float = -5.0):
+    """Speculative-decoding verify: N draft tokens per session stepped from
+    `state` (read only).  q, k, alpha [B,N,H,Dk]; v [B,N,H,Dv]; beta [B,N,H];
+    state [B,H,Dk,Dv] fp32; gate arguments as for prefill_chunked.  Returns
+    o [B,N,H,Dv], token t's output after tokens 0..t."""
+    B, N, H, Dk, Dv, dev, g = _multi_inputs(k, v, alpha, beta, gate, a_log, g_min, q=q)
+    _need(state, "state", torch.float32, dev)
+    if state.shape != (B, H, Dk, Dv):
+        raise ValueError("state must be [B, H, Dk, Dv]")
+    if o is None:
+        o = torch.empty(B, N, H, Dv, dtype=out_dtype, device=dev)
+    else:
+        _need(o, "o", None, dev)
+    _check(load().kda_decode_verify(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), ctypes.byref(g), _ptr(beta), _ptr(state), _ptr(o),
+        _dt(o), B, N, H, Dk, Dv, _stream(dev)))
+    return o
+
+
+def decode_commit(k, v, alpha, beta, n_accept, state, gate: str = "alpha",
+                  a_log: torch.Tensor | None = None, g_min: float = -5.0):
+    """Speculative-decoding commit: replays tokens 0..n_accept[b]-1 of the same
+    draft inputs into `state` in place (bitwise what that many decode_step calls
+    leave).  n_accept: int32 [B] device tensor, clamped to [0, N] on the device."""
+    B, N, H, Dk, Dv, dev, g = _multi_inputs(k, v, alpha, beta, gate, a_log, g_min)
+    _need(state, "state", torch.float32, dev)
+    _need(n_accept, "n_accept", torch.int32, dev)
+    if state.shape != (B, H, Dk, Dv) or n_accept.shape != (B,):
+        raise ValueError("state must be [B, H, Dk, Dv] and n_accept [B]")
+    _check(load().kda_decode_commit(
+        _ptr(k), _ptr(v), _dt(k), ctypes.byref(g), _ptr(beta), _ptr(n_accept), _ptr(state),
+        B, N, H, Dk, Dv, _stream(dev)))
+    return state

@@ -219,10 +219,11 @@ kda_status kda_decode_step_gated(const void* q, const void* k, const void* v, kd
   kda_status s = check_common(q, k, v, qkv_dtype, beta, o, o_dtype, H, Dk, Dv);
   if (s != KDA_OK) return s;
   kda::Gate g;
-  s = check_gate(gate, false, &g);
+  s = check_gate(gate, true, &g);
   if (s != KDA_OK) return s;
   if (!state) return fail(KDA_ERR_INVALID_ARGUMENT, "state must be non-null");
-  if (!aligned16(state)) return fail(KDA_ERR_INVALID_ARGUMENT, "state must be 16-byte aligned");
+  if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v and state must be 16-byte aligned");
   if (!((Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128)))
     return fail(KDA_ERR_UNSUPPORTED, "Dk and Dv must be 64 or 128 (got %d, %d)", Dk, Dv);
   if ((long long)B * H > 0x7fffffffLL) return fail(KDA_ERR_INVALID_ARGUMENT, "B*H too large");
@@ -239,6 +240,70 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
   const kda_gate g = {KDA_GATE_ALPHA, alpha, nullptr, 0.f};
   return kda_decode_step_gated(q, k, v, qkv_dtype, &g, beta, state, o, o_dtype, B, H, Dk, Dv,
                                stream);
+}
+
+// Shape and pointer checks shared by verify and commit (q and o are checked by
+// the caller where they exist).
+static kda_status multi_common(const void* k, const void* v, kda_dtype qkv_dtype,
+                               const kda_gate* gate, const float* beta, const float* state,
+                               int B, int N, int H, int Dk, int Dv, kda::Gate* g) {
+  if (!k || !v || !beta || !state)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "k, v, beta and state must be non-null");
+  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "bad qkv_dtype");
+  if (H <= 0 || Dk <= 0 || Dv <= 0)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "H, Dk and Dv must be positive");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(state) || ((uintptr_t)beta & 3u))
+    return fail(KDA_ERR_INVALID_ARGUMENT,
+                "k, v and state must be 16-byte aligned, beta 4-byte aligned");
+  kda_status s = check_gate(gate, true, g);
+  if (s != KDA_OK) return s;
+  if (!((Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128)))
+    return fail(KDA_ERR_UNSUPPORTED, "Dk and Dv must be 64 or 128 (got %d, %d)", Dk, Dv);
+  if (N > kda::kMaxDraft)
+    return fail(KDA_ERR_UNSUPPORTED, "at most %d tokens per session (got %d)", kda::kMaxDraft, N);
+  if ((long long)B * H > 0x7fffffffLL) return fail(KDA_ERR_INVALID_ARGUMENT, "B*H too large");
+  return KDA_OK;
+}
+
+kda_status kda_decode_verify(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                             const kda_gate* gate, const float* beta, const float* state,
+                             void* o, kda_dtype o_dtype, int B, int N, int H, int Dk, int Dv,
+                             void* stream) {
+  if (B < 0 || N < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B and N must be >= 0");
+  if (B == 0 || N == 0) return ok();
+  if (!q || !o) return fail(KDA_ERR_INVALID_ARGUMENT, "q and o must be non-null");
+  if (o_dtype != KDA_F32 && o_dtype != KDA_BF16)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "bad o_dtype");
+  if (!aligned16(q) || ((uintptr_t)o & (o_dtype == KDA_BF16 ? 1u : 3u)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "q must be 16-byte aligned, o element-aligned");
+  kda::Gate g;
+  kda_status s = multi_common(k, v, qkv_dtype, gate, beta, state, B, N, H, Dk, Dv, &g);
+  if (s != KDA_OK) return s;
+  kda::DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.gate = g; a.beta = beta; a.state = const_cast<float*>(state);
+  a.o = o; a.qkv_bf16 = qkv_dtype == KDA_BF16; a.o_bf16 = o_dtype == KDA_BF16;
+  a.B = B; a.H = H; a.Dk = Dk; a.Dv = Dv; a.stream = stream;
+  a.mode = kda::DECODE_VERIFY; a.N = N;
+  return hip_status(kda::launch_decode(a));
+}
+
+kda_status kda_decode_commit(const void* k, const void* v, kda_dtype qkv_dtype,
+                             const kda_gate* gate, const float* beta, const int32_t* n_accept,
+                             float* state, int B, int N, int H, int Dk, int Dv, void* stream) {
+  if (B < 0 || N < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B and N must be >= 0");
+  if (B == 0 || N == 0) return ok();
+  if (!n_accept || ((uintptr_t)n_accept & 3u))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "n_accept must be non-null and 4-byte aligned");
+  kda::Gate g;
+  kda_status s = multi_common(k, v, qkv_dtype, gate, beta, state, B, N, H, Dk, Dv, &g);
+  if (s != KDA_OK) return s;
+  kda::DecodeArgs a;
+  a.q = nullptr; a.k = k; a.v = v; a.gate = g; a.beta = beta; a.state = state; a.o = nullptr;
+  a.qkv_bf16 = qkv_dtype == KDA_BF16; a.o_bf16 = false;
+  a.B = B; a.H = H; a.Dk = Dk; a.Dv = Dv; a.stream = stream;
+  a.mode = kda::DECODE_COMMIT; a.N = N; a.n_accept = n_accept;
+  return hip_status(kda::launch_decode(a));
 }
 
 }  // extern "C"

@@ -91,32 +91,6 @@ __device__ __forceinline__ float gate_alpha1(const Gate& G, size_t row, int Dk, 
   }
 }
 
-// alpha of the N key channels c0, c0 + STRIDE, ... of one row, for a gate kind
-// fixed at compile time (one straight-line loop per kind)
-template <int KIND, int N, int STRIDE>
-__device__ __forceinline__ void gate_alpha_rows(const Gate& G, size_t row, int Dk, int c0, int h,
-                                                float (&a)[N]) {
-  const float* g = G.g + row * Dk + c0;
-  if constexpr (KIND == GATE_LOG) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) a[i] = expf(g[STRIDE * i]);
-  } else if constexpr (KIND == GATE_BOUNDED) {
-    const float sc = expf(G.a_log[h]);
-#pragma unroll
-    for (int i = 0; i < N; ++i) a[i] = gate_bounded(g[STRIDE * i], sc, G.g_min);
-  } else if constexpr (KIND == GATE_SCALAR) {
-    const float x = G.g[row];
-#pragma unroll
-    for (int i = 0; i < N; ++i) a[i] = x;
-  } else if constexpr (KIND == GATE_NONE) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) a[i] = 1.f;
-  } else {
-#pragma unroll
-    for (int i = 0; i < N; ++i) a[i] = g[STRIDE * i];
-  }
-}
-
 // Gate values of the key channels c..c+3 of one row (c a multiple of 4, 16-byte
 // aligned rows), as stored, for a gate kind fixed at compile time: a prefetch
 // issues the loads only, and gate_finish_blocks turns them into alpha where they

@@ -1,4 +1,6 @@
-// kda_decode.hip -- one-token KDA step for B sessions x H heads (gfx950).
+// kda_decode.hip -- decode kernels for B sessions x H heads (gfx950): the
+// one-token step, and the multi-token verify / commit pair of speculative
+// decoding.
 //
 // Fused recurrent form ("Kimi Delta Attention 完全拆解", section "一次 KDA 前向究竟
 // 发生了什么": decay, the decayed state's answer for k, the corrected write along
@@ -14,113 +16,316 @@
 // column groups of a set of rows, so every global access is a 16-byte vector
 // and a wave touches whole 64..128-byte row segments; the state write uses
 // non-temporal stores.  The column sums over
-// the key axis are finished with cross-lane xor shuffles inside the wave (no
-// LDS, no barrier).
+// the key axis are finished inside the wave with DPP row rotations and the
+// permlane swaps (no LDS, no barrier).
+//
+// Speculative decoding ("Kimi K3 的 KDA" sections 9 and 11.1): the state is
+// updated in place, so a rejected draft token cannot simply be dropped.  Verify
+// runs N draft tokens per session from the state kept in registers and writes
+// their outputs, but not the state; commit replays the first n_accept[b] of
+// those tokens from their cached inputs (k, v, gate, beta) and writes the
+// state once.  A round moves three state tiles (read, read, write) where N
+// single steps move 2N, and rejected tokens cost nothing to undo.  Both stage
+// the session's N tokens in LDS once (alpha formed there), with the key-side
+// vectors permuted so each lane reads its rows as contiguous 16-byte words.
 #include "kda_common.h"
 #include "kda_internal.h"
 
+// Every product and sum is rounded on its own (no fused multiply-add
+// contraction): the one-token step and the multi-token kernels evaluate the
+// same per-token expressions in different code shapes, and uncontracted they
+// agree bitwise (N single steps = verify + commit of N tokens).
+#pragma clang fp contract(off)
+
 namespace kda {
 
-template <typename TIn>
-__device__ __forceinline__ float ld_in(const TIn* p, size_t i);
-template <>
-__device__ __forceinline__ float ld_in<float>(const float* p, size_t i) { return p[i]; }
-template <>
-__device__ __forceinline__ float ld_in<bf16>(const bf16* p, size_t i) { return (float)p[i]; }
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-template <int DK, int DV, typename TIn, typename TOut, int KIND>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+// four consecutive elements as fp32 (8- or 16-byte aligned)
+template <typename TIn>
+__device__ __forceinline__ floatx4 ld4(const TIn* p);
+template <>
+__device__ __forceinline__ floatx4 ld4<float>(const float* p) {
+  return *reinterpret_cast<const floatx4*>(p);
+}
+template <>
+__device__ __forceinline__ floatx4 ld4<bf16>(const bf16* p) {
+  const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+  return floatx4{__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u),
+                 __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u)};
+}
+
+// Lane geometry of a Dk x Dv tile on 4 waves: wave w owns CW value columns;
+// LPR lanes share a row set, a lane holds float4 columns of the NP rows
+// ro + RPP i.
+template <int DK, int DV>
+struct Geo {
+  static constexpr int CW = DV / 4;
+  static constexpr int LPR = CW / 4;
+  static constexpr int RPP = 64 / LPR;
+  static constexpr int NP = DK / RPP;
+  static_assert(NP * RPP == DK, "row split");
+};
+
+// Sum of x over the lanes of the wave that share lane % LPR (LPR = 4 or 8: the
+// lanes holding the same value columns), in every such lane, without LDS: a DPP
+// row rotation by 8 (and by 4) pairs the lanes inside a 16-lane row, and the
+// gfx950 permlane16 / permlane32 swaps bring the other row / half-wave next to
+// it (swapping a register with itself leaves x and its partner's x in the two
+// results, so their sum is x + x[lane ^ 16] or x + x[lane ^ 32]).  Every lane
+// adds the same pairs, so all of them hold bitwise the same sum.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LPR == 4 || LPR == 8, "lane groups of 4 or 8");
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+  if constexpr (LPR == 4)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
+  const unsigned xb = __float_as_uint(x);
+  const auto h = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
+  x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  const unsigned yb = __float_as_uint(x);
+  const auto w = __builtin_amdgcn_permlane32_swap(yb, yb, false, false);
+  return __uint_as_float(w[0]) + __uint_as_float(w[1]);
+}
+
+// q.k over the rows a lane holds (x, y), finished across the lane group
+template <int NP, int LPR>
+__device__ __forceinline__ float dot_rows(const float (&x)[NP], const float (&y)[NP]) {
+  float d = 0.f;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) d = __builtin_fmaf(x[i], y[i], d);
+  return group_sum<LPR>(d);
+}
+
+// One token on the state rows a lane holds (kr = k, ak = alpha k, aq = alpha q,
+// al = alpha at those rows; qk = q.k; vv = v at the lane's 4 columns).  The
+// decayed state's sums come from the stored state and the alpha-scaled vectors,
+// (Diag(alpha) S)^T k = S^T (alpha k), so the decay folds into the update:
+//     u = beta (v - S^T (alpha k)),  o = S^T (alpha q) + (q.k) u,
+//     S' = Diag(alpha) S + k u^T   (a multiply and an fma per element)
+// s is replaced by S'; returns o for the lane's 4 columns.  Explicit fmas only,
+// so every kernel that calls this rounds identically.
+template <int NP, int LPR>
+__device__ __forceinline__ floatx4 token_step(floatx4 (&s)[NP], const float (&kr)[NP],
+                                              const float (&ak)[NP], const float (&aq)[NP],
+                                              const float (&al)[NP], float qk, float b,
+                                              floatx4 vv) {
+  floatx4 old = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NP; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      old[j] = __builtin_fmaf(s[i][j], ak[i], old[j]);  // S^T (alpha k), this lane's rows
+      p[j] = __builtin_fmaf(s[i][j], aq[i], p[j]);      // S^T (alpha q)
+    }
+  // finish the sums over the lanes that share these columns
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    old[j] = group_sum<LPR>(old[j]);
+    p[j] = group_sum<LPR>(p[j]);
+  }
+  floatx4 u, o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u[j] = b * (vv[j] - old[j]);
+    o[j] = __builtin_fmaf(qk, u[j], p[j]);
+  }
+  // decay in place, then the rank-one write accumulated into the same register
+#pragma unroll
+  for (int i = 0; i < NP; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[i][j] = __builtin_fmaf(kr[i], u[j], s[i][j] * al[i]);
+  return o;
+}
+
+// alpha of key channels c..c+3 of one token row, correctly rounded library
+// exponentials as in the one-token step (same values bit for bit)
+template <int KIND>
+__device__ __forceinline__ floatx4 alpha4_exact(const Gate& G, size_t row, int Dk, int c,
+                                                float sc) {
+  floatx4 x = gate_load4<KIND>(G, true, row, Dk, c);
+  if constexpr (KIND == GATE_LOG) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = expf(x[e]);
+  } else if constexpr (KIND == GATE_BOUNDED) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = gate_bounded(x[e], sc, G.g_min);
+  }
+  return x;
+}
+
+// Per-token LDS record, fp32: k, alpha k, alpha and (with outputs) q, alpha q,
+// each permuted to [ro][i] (row ro + RPP i at ro * NP + i); v; beta; q.k.
+template <int DK, int DV, bool VERIFY>
+struct Rec {
+  static constexpr int K = 0;
+  static constexpr int AK = DK;
+  static constexpr int AL = 2 * DK;
+  static constexpr int Q = 3 * DK;                // verify only
+  static constexpr int AQ = 4 * DK;               // verify only
+  static constexpr int V = VERIFY ? 5 * DK : 3 * DK;
+  static constexpr int Bt = V + DV;
+  static constexpr int QK = Bt + 1;               // verify only
+  static constexpr int stride = Bt + 4;           // floats, keeps 16-byte alignment
+};
+
+template <int NP>
+__device__ __forceinline__ void ld_rows(const float* p, float (&x)[NP]) {
+#pragma unroll
+  for (int i = 0; i < NP; i += 4) {
+    const floatx4 t = *reinterpret_cast<const floatx4*>(p + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[i + e] = t[e];
+  }
+}
+
+// One kernel for the three decode calls, by MODE:
+//   DECODE_STEP    one token (N = 1): output written, state written in place
+//   DECODE_VERIFY  tokens 0..N-1: outputs written, state untouched
+//   DECODE_COMMIT  tokens 0..n_accept[b]-1 (clamped to [0, N]) replayed into the
+//                  state, written in place; no outputs
+// All of them stage the tokens' inputs in LDS (one coalesced pass, alpha and the
+// alpha-scaled vectors formed once) and step the state held in registers with
+// token_step, so the three calls agree bitwise.
+template <int DK, int DV, typename TIn, typename TOut, int KIND, int MODE>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     Gate gate, const float* __restrict__ beta, float* __restrict__ state, TOut* __restrict__ o,
-    int H) {
-  constexpr int CW = DV / 4;       // value columns per wave
-  constexpr int LPR = CW / 4;      // lanes sharing one row (float4 each)
-  constexpr int RPP = 64 / LPR;    // rows covered per pass
-  constexpr int NP = DK / RPP;     // passes (rows per lane)
-  static_assert(NP * RPP == DK, "row split");
+    const int32_t* __restrict__ n_accept, int N, int H) {
+  constexpr bool VERIFY = MODE != DECODE_COMMIT;  // outputs (and q) needed
+  constexpr bool WRITE = MODE != DECODE_VERIFY;   // state written back
+  using G = Geo<DK, DV>;
+  using R = Rec<DK, DV, VERIFY>;
+  constexpr int NP = G::NP, LPR = G::LPR, RPP = G::RPP;
+  extern __shared__ __align__(16) float rec[];
 
-  const int tile = blockIdx.x;     // (session, head) flattened
-  const int w = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+  const int tile = blockIdx.x;  // (session, head) flattened
+  const int sb = tile / H, h = tile - sb * H;
+  int n = N;
+  if constexpr (MODE == DECODE_COMMIT) {
+    const int na = n_accept[sb];
+    n = na < 0 ? 0 : (na > N ? N : na);
+    if (n == 0) return;  // nothing accepted: the state stays as it is
+  }
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
   const int cg = lane % LPR;
   const int ro = lane / LPR;
-  const int col = w * CW + 4 * cg;
+  const int col = w * G::CW + 4 * cg;
 
   float* S = state + (size_t)tile * DK * DV;
-  const TIn* qt = q + (size_t)tile * DK;
-  const TIn* kt = k + (size_t)tile * DK;
-
   floatx4 s[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i)
     s[i] = *reinterpret_cast<const floatx4*>(S + (size_t)(ro + RPP * i) * DV + col);
 
-  float kr[NP], qr[NP], al[NP];
-  if constexpr (KIND == GATE_BOUNDED) {
-    // the LPR lanes that hold the same rows each evaluate NP / LPR of the gates
-    // (two exponentials each) and read the others' across the group
-    constexpr int PER = NP / LPR;
-    static_assert(PER * LPR == NP, "rows per lane split");
-    float mine[PER];
-    const float sc = expf(gate.a_log[tile % H]);
+  // stage the n tokens' inputs (alpha and the alpha-scaled vectors formed once)
+  const float sc = KIND == GATE_BOUNDED ? expf(gate.a_log[h]) : 1.f;
+  for (int idx = tid; idx < n * (DK / 4); idx += 256) {
+    const int t = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+    const size_t row = ((size_t)sb * N + t) * H + h;
+    const floatx4 k4 = ld4<TIn>(k + row * DK + c);
+    const floatx4 a4 = alpha4_exact<KIND>(gate, row, DK, c, sc);
+    floatx4 q4 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (VERIFY) q4 = ld4<TIn>(q + row * DK + c);
+    float* rt = rec + t * R::stride;
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
-      mine[j] = gate_bounded(gate.g[(size_t)tile * DK + ro + RPP * (PER * cg + j)], sc,
-                             gate.g_min);
-    const int base = lane - cg;
-#pragma unroll
-    for (int i = 0; i < NP; ++i) al[i] = __shfl(mine[i % PER], base + i / PER, 64);
-  } else {
-    gate_alpha_rows<KIND, NP, RPP>(gate, tile, DK, ro, 0, al);
-  }
-  floatx4 old = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
-  float qk = 0.f;
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int r = ro + RPP * i;
-    const float a = al[i];
-    kr[i] = ld_in(kt, r);
-    qr[i] = ld_in(qt, r);
-    s[i] *= a;                     // Sbar = Diag(alpha) S
-    old += s[i] * kr[i];           // Sbar^T k (partial over this lane's rows)
-    p += s[i] * qr[i];             // Sbar^T q
-    qk += kr[i] * qr[i];
-  }
-  // finish the sums over the lanes that share these columns
-#pragma unroll
-  for (int m = LPR; m < 64; m <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      old[j] += __shfl_xor(old[j], m);
-      p[j] += __shfl_xor(p[j], m);
+    for (int e = 0; e < 4; ++e) {
+      const int pos = ((c + e) % RPP) * NP + (c + e) / RPP;
+      rt[R::K + pos] = k4[e];
+      rt[R::AK + pos] = a4[e] * k4[e];
+      rt[R::AL + pos] = a4[e];
+      if constexpr (VERIFY) {
+        rt[R::Q + pos] = q4[e];
+        rt[R::AQ + pos] = a4[e] * q4[e];
+      }
     }
-    qk += __shfl_xor(qk, m);
   }
-  const float b = beta[tile];
-  floatx4 u;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) u[j] = b * (ld_in(v + (size_t)tile * DV, col + j) - old[j]);
-
-  // streaming (non-temporal) stores: the state is written once and not re-read
-  // by this launch; on gfx950 this write path sustains close to HBM peak where
-  // ordinary stores of the same pattern stall on the cache write-back path
-#pragma unroll
-  for (int i = 0; i < NP; ++i)
-    __builtin_nontemporal_store(s[i] + kr[i] * u,
-                                reinterpret_cast<floatx4*>(S + (size_t)(ro + RPP * i) * DV + col));
-
-  if (ro == 0) {
-    TOut* ot = o + (size_t)tile * DV + col;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ot[j] = (TOut)(p[j] + qk * u[j]);
+  for (int idx = tid; idx < n * (DV / 4); idx += 256) {
+    const int t = idx / (DV / 4), c = 4 * (idx % (DV / 4));
+    const size_t row = ((size_t)sb * N + t) * H + h;
+    *reinterpret_cast<floatx4*>(rec + t * R::stride + R::V + c) = ld4<TIn>(v + row * DV + c);
   }
+  if (tid < n) rec[tid * R::stride + R::Bt] = beta[((size_t)sb * N + tid) * H + h];
+  __syncthreads();
+  if constexpr (MODE == DECODE_VERIFY) {
+    // q.k of each token (the loop below computes it in place for a single step)
+    for (int t = w; t < n; t += 4) {
+      float kr[NP], qr[NP];
+      ld_rows<NP>(rec + t * R::stride + R::K + ro * NP, kr);
+      ld_rows<NP>(rec + t * R::stride + R::Q + ro * NP, qr);
+      const float qk = dot_rows<NP, LPR>(kr, qr);
+      if (lane == 0) rec[t * R::stride + R::QK] = qk;
+    }
+    __syncthreads();
+  }
+
+  for (int t = 0; t < n; ++t) {
+    const float* rt = rec + t * R::stride;
+    float kr[NP], ak[NP], aq[NP], al[NP];
+    ld_rows<NP>(rt + R::K + ro * NP, kr);
+    ld_rows<NP>(rt + R::AK + ro * NP, ak);
+    ld_rows<NP>(rt + R::AL + ro * NP, al);
+    float qk = 0.f;
+    if constexpr (MODE == DECODE_VERIFY) {
+      ld_rows<NP>(rt + R::AQ + ro * NP, aq);
+      qk = rt[R::QK];
+    } else if constexpr (MODE == DECODE_STEP) {
+      float qr[NP];
+      ld_rows<NP>(rt + R::AQ + ro * NP, aq);
+      ld_rows<NP>(rt + R::Q + ro * NP, qr);
+      qk = dot_rows<NP, LPR>(kr, qr);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NP; ++i) aq[i] = 0.f;
+    }
+    const floatx4 vv = *reinterpret_cast<const floatx4*>(rt + R::V + col);
+    const floatx4 ov = token_step<NP, LPR>(s, kr, ak, aq, al, qk, rt[R::Bt], vv);
+    if constexpr (VERIFY) {
+      if (ro == 0) {
+        TOut* ot = o + (((size_t)sb * N + t) * H + h) * DV + col;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ot[j] = (TOut)ov[j];
+      }
+    }
+  }
+  if constexpr (WRITE) {
+    // streaming (non-temporal) stores: the state is written once and not re-read
+    // by this launch; on gfx950 this write path sustains close to HBM peak where
+    // ordinary stores of the same pattern stall on the cache write-back path
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      __builtin_nontemporal_store(s[i],
+                                  reinterpret_cast<floatx4*>(S + (size_t)(ro + RPP * i) * DV + col));
+  }
+}
+
+template <int DK, int DV, bool VERIFY>
+constexpr int multi_lds_bytes(int N) {
+  return (int)sizeof(float) * Rec<DK, DV, VERIFY>::stride * N;
 }
 
 template <int DK, int DV, typename TIn, typename TOut, int KIND>
 static hipError_t launch_decode_k(const DecodeArgs& a) {
-  hipLaunchKernelGGL((decode_step_kernel<DK, DV, TIn, TOut, KIND>), dim3(a.B * a.H), dim3(256), 0,
-                     (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                     a.gate, a.beta, a.state, (TOut*)a.o, a.H);
+  const dim3 grid(a.B * a.H);
+  if (a.mode == DECODE_STEP) {
+    hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, TOut, KIND, DECODE_STEP>), grid, dim3(256),
+                       (multi_lds_bytes<DK, DV, true>(1)), (hipStream_t)a.stream,
+                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.gate, a.beta, a.state,
+                       (TOut*)a.o, (const int32_t*)nullptr, 1, a.H);
+  } else if (a.mode == DECODE_VERIFY) {
+    hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, TOut, KIND, DECODE_VERIFY>), grid, dim3(256),
+                       (multi_lds_bytes<DK, DV, true>(a.N)), (hipStream_t)a.stream,
+                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.gate, a.beta, a.state,
+                       (TOut*)a.o, (const int32_t*)nullptr, a.N, a.H);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, float, KIND, DECODE_COMMIT>), grid, dim3(256),
+                       (multi_lds_bytes<DK, DV, false>(a.N)), (hipStream_t)a.stream,
+                       (const TIn*)nullptr, (const TIn*)a.k, (const TIn*)a.v, a.gate, a.beta,
+                       a.state, (float*)nullptr, a.n_accept, a.N, a.H);
+  }
   return hipGetLastError();
 }
 

@@ -8,6 +8,9 @@
 
 namespace kda {
 
+enum DecodeMode { DECODE_STEP = 0, DECODE_VERIFY = 1, DECODE_COMMIT = 2 };
+constexpr int kMaxDraft = 16;  // tokens per session of one verify / commit call
+
 struct DecodeArgs {
   const void *q, *k, *v;
   Gate gate;
@@ -17,6 +20,9 @@ struct DecodeArgs {
   bool qkv_bf16, o_bf16;
   int B, H, Dk, Dv;
   void* stream;
+  int mode = DECODE_STEP;
+  int N = 1;                          // tokens per session (verify, commit)
+  const int32_t* n_accept = nullptr;  // commit: accepted tokens per session
 };
 
 struct PrefillArgs {

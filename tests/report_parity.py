@@ -99,6 +99,29 @@ def main():
         row(f"gate '{kind}' (B1 H8 T4096 d128)", 2e-3, oracle.rel_l2(o.cpu(), ro),
             oracle.rel_l2(s.cpu(), rs), "oracle fed the oracle's own alpha of the gate, all heads")
 
+    # speculative round: verify 8 draft tokens per session, commit a seeded prefix
+    B, N, H, D = 64, 8, 96, 128
+    inp = synth.make_dense(B, N, H, D, D, seed=1006, device=d)
+    z, a_log = synth.make_gate("bounded", (B, N), H, D, seed=1007, device=d)
+    st = inp.state.clone()
+    o = kda.decode_verify(inp.q, inp.k, inp.v, z, inp.beta, st, gate="bounded", a_log=a_log)
+    n_acc = torch.randint(0, N + 1, (B,), generator=torch.Generator().manual_seed(1008),
+                          dtype=torch.int32)
+    kda.decode_commit(inp.k, inp.v, z, inp.beta, n_acc.to(d), st, gate="bounded", a_log=a_log)
+    torch.cuda.synchronize()
+    alpha = oracle.gate_alpha("bounded", z.cpu().numpy(), inp.q.shape, a_log=a_log.cpu().numpy())
+    hq, hk, hv, hb = (x.cpu() for x in (inp.q, inp.k, inp.v, inp.beta))
+    ro, _ = oracle.recurrent(hq, hk, hv, alpha, hb, initial_state=inp.state.cpu())
+    lens = [int(x) for x in n_acc]
+    sel = lambda x: torch.cat([torch.as_tensor(x)[b, :lens[b]] for b in range(B)])[None]  # noqa: E731
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    _, rs = oracle.recurrent(sel(hq), sel(hk), sel(hv), sel(alpha), sel(hb), cu_seqlens=cu,
+                             initial_state=inp.state.cpu())
+    row("spec round (B64 H96 d128, 8 drafts, bounded gate)", 2e-3, oracle.rel_l2(o.cpu(), ro),
+        oracle.rel_l2(st.cpu(), rs), "oracle: verify outputs, committed states (seeded prefixes)")
+
     if "--long" in sys.argv:
         w = synth.WORKLOADS["long_1m"]
         inp = synth.make_dense(w["B"], w["T"], w["H"], w["D"], w["D"], seed=w["seed"],

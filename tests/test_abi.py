@@ -122,6 +122,8 @@ def test_varlen_and_decode_validation():
                                128, None) == UNSUPPORTED
     assert lib.kda_decode_step(FAKE + 1, FAKE, FAKE, BF16, FAKE, FAKE, FAKE, FAKE, F32, 4, 2, 128,
                                128, None) == INVALID
+    assert lib.kda_decode_step(FAKE, FAKE + 8, FAKE, BF16, FAKE, FAKE, FAKE, FAKE, F32, 4, 2, 128,
+                               128, None) == INVALID  # 16-byte alignment
     assert lib.kda_decode_step(None, None, None, BF16, None, None, None, None, F32, 0, 2, 128,
                                128, None) == OK
 
@@ -180,12 +182,48 @@ def test_gate_validation(entry, args, expect):
 
 
 def test_gate_alignment_per_kind():
-    """bf16 prefill reads a per-channel gate with 16-byte loads; a scalar gate and
-    the decode step need only 4-byte alignment."""
+    """bf16 prefill and the decode calls read a per-channel gate with 16-byte
+    loads; a scalar gate, and the fp32 prefill, need only 4-byte alignment."""
     for kind in (ALPHA, LOG):
         assert _gated(kind=kind, gate=FAKE + 8) == INVALID
         assert _gated(kind=kind, gate=FAKE + 8, entry="varlen") == INVALID
-        assert _gated(kind=kind, gate=FAKE + 8, entry="decode", Dk=96) == UNSUPPORTED
+        assert _gated(kind=kind, gate=FAKE + 8, entry="decode") == INVALID
         assert _gated(kind=kind, gate=FAKE + 8, qd=F32, Dk=96) == UNSUPPORTED
+    assert _gated(kind=SCALAR, gate=FAKE + 4, entry="decode", Dk=96) == UNSUPPORTED
     assert _gated(kind=BOUNDED, gate=FAKE + 8, a_log=FAKE, g_min=-5.0) == INVALID
     assert _gated(kind=SCALAR, gate=FAKE + 4, chunk=32) == UNSUPPORTED
+
+
+def test_verify_and_commit_validation():
+    lib = kda.load()
+    g = _lib._Gate(ALPHA, FAKE, None, 0.0)
+    gp = ctypes.byref(g)
+
+    def verify(**o):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, qd=BF16, beta=FAKE, st=FAKE, o=FAKE, od=F32, B=2, N=4,
+                 H=2, Dk=128, Dv=128, gp=gp)
+        a.update(o)
+        return lib.kda_decode_verify(a["q"], a["k"], a["v"], a["qd"], a["gp"], a["beta"],
+                                     a["st"], a["o"], a["od"], a["B"], a["N"], a["H"], a["Dk"],
+                                     a["Dv"], None)
+
+    def commit(**o):
+        a = dict(k=FAKE, v=FAKE, qd=BF16, beta=FAKE, n=FAKE, st=FAKE, B=2, N=4, H=2, Dk=128,
+                 Dv=128, gp=gp)
+        a.update(o)
+        return lib.kda_decode_commit(a["k"], a["v"], a["qd"], a["gp"], a["beta"], a["n"],
+                                     a["st"], a["B"], a["N"], a["H"], a["Dk"], a["Dv"], None)
+
+    for f in (verify, commit):
+        assert f(B=0) == OK and f(N=0) == OK                # nothing to do
+        assert f(N=-1) == INVALID and f(B=-1) == INVALID
+        assert f(k=None) == INVALID and f(st=None) == INVALID
+        assert f(v=FAKE + 8) == INVALID                      # 16-byte alignment
+        assert f(st=FAKE + 8) == INVALID
+        assert f(gp=None) == INVALID
+        assert f(qd=5) == INVALID
+        assert f(N=17) == UNSUPPORTED                        # at most 16 tokens
+        assert f(Dk=96) == UNSUPPORTED
+    assert verify(q=None) == INVALID and verify(o=None) == INVALID
+    assert verify(q=FAKE + 8) == INVALID
+    assert commit(n=None) == INVALID and commit(n=FAKE + 2) == INVALID
