@@ -301,3 +301,39 @@ def test_two_pass_windows():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
     assert rel(o2.cpu(), o_ref) <= TOL_BF16 and rel(s2.cpu(), s_ref) <= TOL_BF16
+
+
+def test_two_pass_on_caller_stream_and_in_a_graph():
+    """The two-pass schedule (two launches per 4096-token window) on a
+    non-default caller stream, and captured in a graph replayed several times
+    with eager work between the replays, gives bitwise the eager result."""
+    d = dev()
+    inp = synth.make_dense(1, 5000, 3, 128, 128, seed=511, state_std=0.02, device=d)
+    ref_o, ref_s = _run(inp, d, schedule="fused")
+    ws = torch.empty(kda.workspace_size(1, 5000, 3, 128, 128), dtype=torch.uint8, device=d)
+    o = torch.empty_like(ref_o)
+    fs = torch.empty_like(ref_s)
+
+    def call():
+        kda.prefill_chunked(inp.q, inp.k, inp.v, inp.alpha, inp.beta, initial_state=inp.state,
+                            final_state=fs, o=o, schedule="two_pass", workspace=ws)
+
+    side = torch.cuda.Stream(device=d)
+    side.wait_stream(torch.cuda.current_stream(d))
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            call()
+    torch.cuda.current_stream(d).wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(fs, ref_s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(3):
+        o.zero_()
+        fs.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(fs, ref_s)
+        _run(inp, d, schedule="fused")  # eager work between replays
