@@ -51,10 +51,10 @@ using namespace frag;
 
 constexpr int NTH_S = 512;
 
-template <int DK>
+template <int DK, int BV>
 struct StatePlan {
   static constexpr int ldS = DK + 8, ldP = CH + 8;
-  // o staging of each output wave: 16 rows x 64 values fp32, row stride 80
+  // o staging of each output wave: 16 rows x BV values fp32, row stride BV + 16
   // floats (16-lane groups of the 16-byte accesses hit distinct banks)
   static constexpr int ldO = BV + 16;
   static constexpr int ST = BV * ldS * 2 * 2, PT = BV * ldP * 2 * 2, OS = 4 * 16 * ldO * 4;
@@ -112,12 +112,13 @@ __device__ __forceinline__ void store4<bf16>(__amdgpu_buffer_rsrc_t rs, int off,
 // derives for the loop then hold on every iteration).
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int DK, int DV, typename TOut>
+template <int DK, int DV, int BV, typename TOut>
 __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     const unsigned char* __restrict__ img, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ cu_seqlens, const float* s_init, float* carry,
     TOut* __restrict__ o, int n_seq, int T, int H, long long tok_lo, long long tok_hi, int cap) {
-  using L = StatePlan<DK>;
+  static_assert(BV == 32 || BV == 64, "value slice of 32 or 64 columns");
+  using L = StatePlan<DK, BV>;
   using IM = Images<DK, DV>;
   constexpr int NKB = DK / 32;
   constexpr int NKH = NKB / 2;                   // 32-channel blocks per channel half
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
   const int vt0 = vcol0 / 16;  // first U tile of the slice
   // state tiles of this wave
   const int srt = DK == 128 ? 2 * w + role : w;  // 16-row tile
-  const int sv0 = DK == 128 ? 0 : 2 * role;      // first value tile (within the slice)
+  const int sv0 = DK == 128 ? 0 : KVT * role;    // first value tile (within the slice)
 
   floatx4 Sacc[KVT];
   {
@@ -389,8 +390,9 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
         }
       // o of the tile through this wave's LDS staging area: a quad transpose
       // gives each lane four consecutive values of row 4g + (tr & 3), stored
-      // as one 16-byte word; read back, each store instruction covers four
-      // whole rows of the slice.  The descriptor spans the chunk's nv rows.
+      // as one 16-byte word; read back, each store instruction covers whole
+      // rows of the slice (64 / (BV / 4) of them).  The descriptor spans the
+      // chunk's nv rows.
       {
         float* os = OS + w * 16 * ldO;
         const int b = tr & 3;
@@ -402,11 +404,14 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             o + ((size_t)tok0 * H + h) * DV + vcol0, 0, (int)((size_t)nv * rowel * sizeof(TOut)),
             0x00020000);
+        constexpr int LPO = BV / 4;    // lanes per o row
+        constexpr int RPI = 64 / LPO;  // rows per store instruction
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int row = 4 * q4 + (lane_x >> 4);
-          const floatx4 y = *reinterpret_cast<const floatx4*>(os + row * ldO + 4 * (lane_x & 15));
-          store4<TOut>(rs, (int)(((size_t)(16 * w + row) * rowel + 4 * (lane_x & 15)) * sizeof(TOut)), y);
+        for (int q4 = 0; q4 < 16 / RPI; ++q4) {
+          const int row = RPI * q4 + lane_x / LPO;
+          const int cq = 4 * (lane_x % LPO);
+          const floatx4 y = *reinterpret_cast<const floatx4*>(os + row * ldO + cq);
+          store4<TOut>(rs, (int)(((size_t)(16 * w + row) * rowel + cq) * sizeof(TOut)), y);
         }
       }
     };
@@ -472,11 +477,17 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restr
   }
 }
 
+// value slice of one state-pass workgroup: 64 columns.  32 (twice the
+// workgroups, every frame fetched by four instead of two) is slower: the pass
+// is bound by frame fetches per compute unit, not by idle compute units.
+constexpr int BV_STATE = 64;
+
 template <int DK, int DV, typename TOut>
 hipError_t launch_state_t(const PrefillArgs& a, const unsigned char* img, const int32_t* chunk_off,
                           float* carry, long long tok_lo, long long tok_hi, int cap) {
-  using L = StatePlan<DK>;
-  auto kern = prefill_state_kernel<DK, DV, TOut>;
+  constexpr int BV = BV_STATE;
+  using L = StatePlan<DK, BV>;
+  auto kern = prefill_state_kernel<DK, DV, BV, TOut>;
   static bool attr_set = false;  // per instantiation; idempotent if raced
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
