@@ -17,11 +17,19 @@ Two independent formulations live here:
   "Kimi Delta Attention 完全拆解", section "KDA 为什么比一般 DPLR 更容易做成快 Kernel")
   and applies S <- M S + beta k v^T.  It is for tiny inputs only.
 
+Around the recurrence: :func:`gate_alpha` (the decay from each gate
+parametrization) and the layer's prologue and epilogue -- :func:`short_conv`,
+:func:`silu`, :func:`l2norm`, :func:`prologue` (q, k, v from the projections'
+outputs, with the conv state) and :func:`rmsnorm_gate` (per-head RMSNorm and
+sigmoid output gate).
+
 Parity status: pinned (see the CPU tests) by linear-attention brute force, the
 exact-overwrite property, the beta = 0 closed form, the erase-free two-token
 expansion, the gradient-step derivation, the state-size arithmetic, the
-chunk form and two-segment composition; the general random case has no printed
-values on the pages.
+chunk form and two-segment composition; the gates by closed forms and the
+scalar-gate commutation; the prologue / epilogue by numpy's convolution, shift
+kernels, the state hand-over and closed forms.  The general random case has no
+printed values on the pages.
 """
 from __future__ import annotations
 
@@ -201,6 +209,72 @@ def gate_alpha(kind: str, gate, shape, a_log=None, g_min: float = -5.0) -> np.nd
     if a.shape != shape:
         raise ValueError(f"gate {kind!r} gives shape {a.shape}, expected {shape}")
     return np.ascontiguousarray(a)
+
+
+# ---------------------------------------------------------------------------
+# The steps on either side of the recurrence in a KDA layer ("Kimi Delta
+# Attention 完全拆解", section "一次 KDA 前向究竟发生了什么", formulas for q, k, v and
+# the output; "从线性注意力到 KDA", the bullet list of the layer's inputs and the
+# section on the per-head output norm and gate).  The projections themselves are
+# not part of the operator: their outputs are the inputs here.
+
+def short_conv(x, w, state=None):
+    """Depthwise causal convolution with kernel size 4 along the token axis.
+
+    ``x`` [B, T, C] (C = heads x head dim, each channel on its own), ``w`` [C, 4]
+    with tap 3 weighting the current token and tap j the token 3 - j before it;
+    ``state`` [B, 3, C] holds the 3 inputs before the first token, oldest first
+    (None: zeros).  Returns (y [B, T, C], the new state: the last 3 inputs of
+    the concatenation of state and x)."""
+    x = _f64(x)
+    w = _f64(w)
+    B, T, C = x.shape
+    prev = np.zeros((B, 3, C)) if state is None else _f64(state)
+    xx = np.concatenate([prev, x], axis=1)
+    y = np.zeros((B, T, C))
+    for j in range(4):
+        y += w[:, j] * xx[:, j:j + T]
+    return y, xx[:, -3:].copy()
+
+
+def silu(x):
+    """Swish / SiLU: x * Sigmoid(x)."""
+    x = _f64(x)
+    return x * _sigmoid(x)
+
+
+def l2norm(x, eps: float = 1e-6):
+    """x / sqrt(sum of squares over the last axis + eps)."""
+    x = _f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def prologue(xq, xk, xv, wq, wk, wv, state=None, eps: float = 1e-6):
+    """q, k = L2Norm(Swish(ShortConv(x_q / x_k))), v = Swish(ShortConv(x_v)).
+
+    ``xq, xk`` [B, T, H, Dk], ``xv`` [B, T, H, Dv] (the projections' outputs);
+    ``wq, wk`` [H, Dk, 4], ``wv`` [H, Dv, 4]; ``state`` [B, 3, H, 2 Dk + Dv]: the
+    last 3 inputs of q | k | v before the first token (None: zeros).  Returns
+    (q, k, v, new state)."""
+    xq, xk, xv = _f64(xq), _f64(xk), _f64(xv)
+    B, T, H, Dk = xq.shape
+    Dv = xv.shape[-1]
+    st = None if state is None else _f64(state).reshape(B, 3, H, 2 * Dk + Dv)
+    outs, news = [], []
+    for x, w, lo, D in ((xq, wq, 0, Dk), (xk, wk, Dk, Dk), (xv, wv, 2 * Dk, Dv)):
+        s_in = None if st is None else st[:, :, :, lo:lo + D].reshape(B, 3, H * D)
+        y, s_out = short_conv(x.reshape(B, T, H * D), _f64(w).reshape(H * D, 4), s_in)
+        outs.append(silu(y).reshape(B, T, H, D))
+        news.append(s_out.reshape(B, 3, H, D))
+    q, k, v = outs
+    return l2norm(q, eps), l2norm(k, eps), v, np.concatenate(news, axis=-1)
+
+
+def rmsnorm_gate(o, g, w, eps: float = 1e-5):
+    """Per-head output: RMSNorm over the head's Dv channels with weight ``w`` [Dv],
+    then the sigmoid output gate, o * rsqrt(mean(o^2) + eps) * w * Sigmoid(g)."""
+    o, g, w = _f64(o), _f64(g), _f64(w)
+    return o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps) * w * _sigmoid(g)
 
 
 def rel_l2(x, ref) -> float:

@@ -378,3 +378,92 @@ def test_log_scalar_and_none_gates():
         oracle.gate_alpha("scalar", sc[:, :, :1], a.shape)
     with pytest.raises(ValueError):
         oracle.gate_alpha("softplus", a, a.shape)
+
+
+def test_short_conv_pins():
+    """Depthwise causal convolution, kernel 4 ("从线性注意力到 KDA", the ShortConv
+    bullet; "Kimi Delta Attention 完全拆解", section "一次 KDA 前向究竟发生了什么"):
+    each channel against numpy's full convolution, a one-hot kernel is a shift
+    (tap 3 the current token, tap 0 three tokens back, reaching into the state),
+    and a sequence cut in two with the state handed over equals the whole."""
+    rng = np.random.default_rng(21)
+    B, T, C = 2, 11, 5
+    x = rng.standard_normal((B, T, C))
+    w = rng.standard_normal((C, 4))
+    y, st = oracle.short_conv(x, w)
+    for b in range(B):
+        for c in range(C):
+            full = np.convolve(x[b, :, c], w[c, ::-1])[:T]
+            assert np.allclose(y[b, :, c], full, rtol=0, atol=1e-13)
+    assert np.array_equal(st, x[:, -3:])
+    s0 = rng.standard_normal((B, 3, C))
+    e3 = np.zeros((C, 4)); e3[:, 3] = 1.0
+    assert np.array_equal(oracle.short_conv(x, e3, s0)[0], x)
+    e0 = np.zeros((C, 4)); e0[:, 0] = 1.0
+    y0, _ = oracle.short_conv(x, e0, s0)
+    assert np.array_equal(y0[:, :3], s0) and np.array_equal(y0[:, 3:], x[:, :-3])
+    ya, sa = oracle.short_conv(x[:, :4], w, s0)
+    yb, sb = oracle.short_conv(x[:, 4:], w, sa)
+    yw, sw = oracle.short_conv(x, w, s0)
+    assert np.allclose(np.concatenate([ya, yb], axis=1), yw, rtol=0, atol=1e-14)
+    assert np.array_equal(sb, sw)
+    # a cut shorter than the kernel: the state carries old inputs forward
+    yc, sc = oracle.short_conv(x[:, :1], w, s0)
+    assert np.array_equal(sc, np.concatenate([s0[:, 1:], x[:, :1]], axis=1))
+
+
+def test_silu_l2norm_rmsnorm_gate_pins():
+    """Swish(x) - Swish(-x) = x and Swish(0) = 0; L2Norm gives unit rows (eps = 0)
+    and ignores scale; RMSNorm of a constant row c gives sign(c) w, the gate
+    Sigmoid(0) halves it, and with w = 1 and an open gate the output has RMS 1
+    ("从线性注意力到 KDA", the output norm and gate section)."""
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((4, 9)) * 3
+    assert np.allclose(oracle.silu(x) - oracle.silu(-x), x, rtol=0, atol=1e-14)
+    assert oracle.silu(np.zeros(1))[0] == 0.0
+    assert abs(oracle.silu(np.array([1.0]))[0] - 1.0 / (1.0 + np.exp(-1.0))) < 1e-16
+    n = oracle.l2norm(x, eps=0.0)
+    assert np.allclose(np.linalg.norm(n, axis=-1), 1.0, rtol=0, atol=1e-14)
+    assert np.allclose(oracle.l2norm(7.5 * x, eps=0.0), n, rtol=0, atol=1e-14)
+    assert np.all(oracle.l2norm(np.zeros((1, 4))) == 0.0)
+    w = rng.uniform(0.5, 1.5, 9)
+    c = np.full((2, 9), -2.5)
+    big = np.full((2, 9), 50.0)
+    assert np.allclose(oracle.rmsnorm_gate(c, big, w, eps=0.0), -w, rtol=0, atol=1e-14)
+    assert np.allclose(oracle.rmsnorm_gate(c, np.zeros((2, 9)), w, eps=0.0), -0.5 * w,
+                       rtol=0, atol=1e-14)
+    y = oracle.rmsnorm_gate(x, np.full(x.shape, 60.0), np.ones(9), eps=0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=0, atol=1e-14)
+
+
+def test_prologue_state_layout_and_handover():
+    """The prologue's state holds the last 3 inputs of q | k | v per head; a
+    prefill cut in two with the state handed over equals the whole, and each
+    tensor reads its own channel range of the state (a plausible slip -- q and k
+    swapped, or heads interleaved -- changes the first tokens)."""
+    rng = np.random.default_rng(23)
+    B, T, H, Dk, Dv = 2, 7, 3, 4, 5
+    xq, xk = rng.standard_normal((2, B, T, H, Dk))
+    xv = rng.standard_normal((B, T, H, Dv))
+    wq, wk = rng.standard_normal((2, H, Dk, 4))
+    wv = rng.standard_normal((H, Dv, 4))
+    s0 = rng.standard_normal((B, 3, H, 2 * Dk + Dv))
+    q, k, v, s = oracle.prologue(xq, xk, xv, wq, wk, wv, s0)
+    assert np.array_equal(s[:, :, :, :Dk], xq[:, -3:]) and np.array_equal(s[:, :, :, Dk:2 * Dk], xk[:, -3:])
+    assert np.array_equal(s[:, :, :, 2 * Dk:], xv[:, -3:])
+    q1, k1, v1, s1 = oracle.prologue(xq[:, :2], xk[:, :2], xv[:, :2], wq, wk, wv, s0)
+    q2, k2, v2, s2 = oracle.prologue(xq[:, 2:], xk[:, 2:], xv[:, 2:], wq, wk, wv, s1)
+    for a, b1, b2 in ((q, q1, q2), (k, k1, k2), (v, v1, v2)):
+        assert np.allclose(a, np.concatenate([b1, b2], axis=1), rtol=0, atol=1e-14)
+    assert np.array_equal(s, s2)
+    # token 0 of head 1, channel 0 of k by hand: taps over (state k rows, x_k)
+    h, c = 1, 0
+    pre = (wk[h, c, 0] * s0[0, 0, h, Dk + c] + wk[h, c, 1] * s0[0, 1, h, Dk + c]
+           + wk[h, c, 2] * s0[0, 2, h, Dk + c] + wk[h, c, 3] * xk[0, 0, h, c])
+    row = []
+    for cc in range(Dk):
+        p = (wk[h, cc, 0] * s0[0, 0, h, Dk + cc] + wk[h, cc, 1] * s0[0, 1, h, Dk + cc]
+             + wk[h, cc, 2] * s0[0, 2, h, Dk + cc] + wk[h, cc, 3] * xk[0, 0, h, cc])
+        row.append(p / (1.0 + np.exp(-p)))
+    row = np.array(row)
+    assert abs(k[0, 0, h, c] - (pre / (1 + np.exp(-pre))) / np.sqrt(np.sum(row ** 2) + 1e-6)) < 1e-13
