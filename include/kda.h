@@ -272,6 +272,55 @@ kda_status kda_decode_commit(const void* k, const void* v, kda_dtype qkv_dtype,
                              float* state, int B, int N, int H, int Dk, int Dv, void* stream);
 
 /*
+ * The layer's steps on either side of the recurrence ("Kimi Delta Attention
+ * 完全拆解", section "一次 KDA 前向究竟发生了什么", the formulas for q, k, v and the
+ * layer output; "从线性注意力到 KDA", the ShortConv / L2Norm bullets and the
+ * per-head output norm and gate):
+ *   prologue  q, k = L2Norm(Swish(ShortConv(x_q / x_k))), v = Swish(ShortConv(x_v))
+ *   epilogue  y = RMSNorm(o) * w * Sigmoid(g), per head over its Dv channels
+ * x_q, x_k, x_v and g are the outputs of the layer's projections (not part of
+ * this library).  ShortConv is depthwise and causal with kernel size 4: per
+ * channel, y_t = w[0] x_{t-3} + w[1] x_{t-2} + w[2] x_{t-1} + w[3] x_t, no bias.
+ * Its state is the last 3 inputs of q | k | v of every head, the only state of
+ * the layer besides S: conv state [sessions, 3, H, 2 Dk + Dv] fp32, oldest row
+ * first.  L2Norm: x / sqrt(sum x^2 + eps).  RMSNorm: o / sqrt(mean o^2 + eps).
+ */
+typedef struct {
+    const float* w_q;  /* [H, Dk, 4] taps (tap 3 weights the current token) */
+    const float* w_k;  /* [H, Dk, 4] */
+    const float* w_v;  /* [H, Dv, 4] */
+    float eps;         /* L2Norm epsilon, finite and > 0 (e.g. 1e-6) */
+} kda_conv;
+
+/*
+ * kda_prologue -- the prologue over a prefill, dense (cu_seqlens NULL: N
+ * sequences of T tokens, tensors [N, T, H, .]) or packed (cu_seqlens DEVICE
+ * int32 [N + 1], T = total tokens, tensors [1, T, H, .]).
+ *   xq, xk [.., H, Dk], xv [.., H, Dv]  dtype;  q, k, v outputs of the same
+ *                      shapes and dtype (rounded once), not aliasing the inputs
+ *   conv_state_in      [N, 3, H, 2 Dk + Dv] fp32 or NULL (zeros): the inputs
+ *                      before each sequence's first token
+ *   conv_state_out     same shape or NULL (not written): the last 3 inputs of
+ *                      each sequence (an empty sequence's is copied through);
+ *                      must not alias conv_state_in
+ * All tensors 16-byte aligned; Dk, Dv in {64, 128}.
+ */
+kda_status kda_prologue(const void* xq, const void* xk, const void* xv, kda_dtype dtype,
+                        const kda_conv* conv, const float* conv_state_in,
+                        float* conv_state_out, const int32_t* cu_seqlens, int N, int T,
+                        int H, int Dk, int Dv, void* q, void* k, void* v, void* stream);
+
+/*
+ * kda_epilogue -- y = RMSNorm(o) * w * Sigmoid(g) for `tokens` x H rows of Dv.
+ *   o [tokens, H, Dv] o_dtype;  g [tokens, H, Dv] g_dtype;  w [Dv] fp32
+ *   y [tokens, H, Dv] y_dtype (may alias o when the dtypes match)
+ * eps finite and > 0 (e.g. 1e-5); all tensors 16-byte aligned; Dv in {64, 128}.
+ */
+kda_status kda_epilogue(const void* o, kda_dtype o_dtype, const void* g, kda_dtype g_dtype,
+                        const float* w, float eps, void* y, kda_dtype y_dtype,
+                        long long tokens, int H, int Dv, void* stream);
+
+/*
  * kda_prefill_workspace_size -- workspace bytes that enable the two-pass
  * schedule of kda_prefill_chunked for these sizes, independent of T (the state
  * is fixed-size, "Kimi K3 混合线性注意力": the per-session state does not grow

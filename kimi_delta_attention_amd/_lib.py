@@ -20,7 +20,7 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
 
 EXPORTED = ("kda_prefill_chunked", "kda_prefill_varlen", "kda_decode_step",
             "kda_prefill_chunked_gated", "kda_prefill_varlen_gated", "kda_decode_step_gated",
-            "kda_decode_verify", "kda_decode_commit",
+            "kda_decode_verify", "kda_decode_commit", "kda_prologue", "kda_epilogue",
             "kda_prefill_workspace_size", "kda_prefill_varlen_workspace_size",
             "kda_prefill_two_pass_preferred", "kda_status_string", "kda_last_error_message")
 
@@ -28,6 +28,11 @@ SCHEDULES = ("auto", "fused", "two_pass")
 
 # kda_gate_kind: how the decay tensor passed as `alpha` is read (include/kda.h)
 GATES = {"alpha": 0, "log": 1, "bounded": 2, "scalar": 3, "none": 4}
+
+
+class _Conv(ctypes.Structure):
+    _fields_ = [("w_q", ctypes.c_void_p), ("w_k", ctypes.c_void_p), ("w_v", ctypes.c_void_p),
+                ("eps", ctypes.c_float)]
 
 
 class _Gate(ctypes.Structure):
@@ -73,6 +78,11 @@ def load() -> ctypes.CDLL:
     lib.kda_decode_verify.restype = I
     lib.kda_decode_commit.argtypes = [P, P, I, G, P, P, P, I, I, I, I, I, P]
     lib.kda_decode_commit.restype = I
+    C = ctypes.POINTER(_Conv)
+    lib.kda_prologue.argtypes = [P, P, P, I, C, P, P, P, I, I, I, I, I, P, P, P, P]
+    lib.kda_prologue.restype = I
+    lib.kda_epilogue.argtypes = [P, I, P, I, P, ctypes.c_float, P, I, ctypes.c_longlong, I, I, P]
+    lib.kda_epilogue.restype = I
     lib.kda_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.kda_prefill_workspace_size.restype = Z
     lib.kda_prefill_varlen_workspace_size.argtypes = [I, I, I, I, I, I]
@@ -344,3 +354,71 @@ def decode_commit(k, v, alpha, beta, n_accept, state, gate: str = "alpha",
         _ptr(k), _ptr(v), _dt(k), ctypes.byref(g), _ptr(beta), _ptr(n_accept), _ptr(state),
         B, N, H, Dk, Dv, _stream(dev)))
     return state
+
+
+def _conv(wq, wk, wv, eps, H, Dk, Dv, dev):
+    for t, n, D in ((wq, "w_q", Dk), (wk, "w_k", Dk), (wv, "w_v", Dv)):
+        _need(t, n, torch.float32, dev)
+        if tuple(t.shape) != (H, D, 4):
+            raise ValueError(f"{n} must be [H, {D}, 4]")
+    return _Conv(wq.data_ptr(), wk.data_ptr(), wv.data_ptr(), float(eps))
+
+
+def prologue(xq, xk, xv, wq, wk, wv, conv_state=None, cu_seqlens=None, eps: float = 1e-6,
+             conv_state_out: bool | torch.Tensor = True):
+    """The layer's prologue over a prefill: q, k = L2Norm(Swish(ShortConv(x))),
+    v = Swish(ShortConv(x_v)).  xq, xk [B,T,H,Dk], xv [B,T,H,Dv] (packed: B = 1
+    with cu_seqlens int32 [N+1]); taps wq, wk [H,Dk,4], wv [H,Dv,4] fp32;
+    conv_state [N,3,H,2Dk+Dv] fp32 or None (zeros).  Returns (q, k, v,
+    conv_state_out or None)."""
+    B, T, H, Dk = xq.shape
+    Dv = xv.shape[-1]
+    dev = xq.device
+    for t, n in ((xq, "x_q"), (xk, "x_k"), (xv, "x_v")):
+        _need(t, n, xq.dtype, dev)
+    if xk.shape != xq.shape or xv.shape != (B, T, H, Dv):
+        raise ValueError("inconsistent shapes")
+    c = _conv(wq, wk, wv, eps, H, Dk, Dv, dev)
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("packed inputs have B == 1")
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    sw = (N, 3, H, 2 * Dk + Dv)
+    if conv_state is not None:
+        _need(conv_state, "conv_state", torch.float32, dev)
+        if tuple(conv_state.shape) != sw:
+            raise ValueError(f"conv_state must be {sw}")
+    if isinstance(conv_state_out, torch.Tensor):
+        so = conv_state_out
+        _need(so, "conv_state_out", torch.float32, dev)
+    elif conv_state_out:
+        so = torch.empty(sw, dtype=torch.float32, device=dev)
+    else:
+        so = None
+    q, k, v = torch.empty_like(xq), torch.empty_like(xk), torch.empty_like(xv)
+    _check(load().kda_prologue(
+        _ptr(xq), _ptr(xk), _ptr(xv), _dt(xq), ctypes.byref(c), _ptr(conv_state), _ptr(so),
+        _ptr(cu_seqlens), N, T, H, Dk, Dv, _ptr(q), _ptr(k), _ptr(v), _stream(dev)))
+    return q, k, v, so
+
+
+def epilogue(o, g, w, eps: float = 1e-5, out_dtype=None, y: torch.Tensor | None = None):
+    """y = RMSNorm(o) * w * Sigmoid(g) per head: o, g [..., H, Dv]; w [Dv] fp32."""
+    dev = o.device
+    _need(o, "o", None, dev)
+    _need(g, "g", None, dev)
+    _need(w, "w", torch.float32, dev)
+    if g.shape != o.shape or o.dim() < 2 or tuple(w.shape) != (o.shape[-1],):
+        raise ValueError("o and g must match, w must be [Dv]")
+    H, Dv = o.shape[-2], o.shape[-1]
+    tokens = o.numel() // (H * Dv)
+    if y is None:
+        y = torch.empty(o.shape, dtype=out_dtype or o.dtype, device=dev)
+    else:
+        _need(y, "y", None, dev)
+    _check(load().kda_epilogue(_ptr(o), _dt(o), _ptr(g), _dt(g), _ptr(w), float(eps), _ptr(y),
+                               _dt(y), tokens, H, Dv, _stream(dev)))
+    return y

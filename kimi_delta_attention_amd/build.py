@@ -8,7 +8,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_prep.hip",
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_layer.hip", "kda_prefill.hip",
+           "kda_prefill_prep.hip",
            "kda_prefill_state.hip", "kda_prefill_f32.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 

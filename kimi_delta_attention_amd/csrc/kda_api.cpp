@@ -242,6 +242,77 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
                                stream);
 }
 
+static bool dtype_ok(kda_dtype d) { return d == KDA_F32 || d == KDA_BF16; }
+static bool eps_ok(float e) { return e > 0.f && e < 3.0e38f; }
+
+static kda_status check_conv(const kda_conv* c, kda::ConvArgs* out) {
+  if (!c) return fail(KDA_ERR_INVALID_ARGUMENT, "conv descriptor must be non-null");
+  if (!c->w_q || !c->w_k || !c->w_v)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "conv taps w_q, w_k, w_v must be non-null");
+  if (((uintptr_t)c->w_q | (uintptr_t)c->w_k | (uintptr_t)c->w_v) & 3u)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "conv taps must be 4-byte aligned");
+  if (!eps_ok(c->eps)) return fail(KDA_ERR_INVALID_ARGUMENT, "L2Norm eps must be finite and > 0");
+  out->w[0] = c->w_q; out->w[1] = c->w_k; out->w[2] = c->w_v; out->eps = c->eps;
+  return KDA_OK;
+}
+
+kda_status kda_prologue(const void* xq, const void* xk, const void* xv, kda_dtype dtype,
+                        const kda_conv* conv, const float* conv_state_in,
+                        float* conv_state_out, const int32_t* cu_seqlens, int N, int T,
+                        int H, int Dk, int Dv, void* q, void* k, void* v, void* stream) {
+  if (N < 0 || T < 0 || H <= 0) return fail(KDA_ERR_INVALID_ARGUMENT, "need N, T >= 0 and H > 0");
+  if (N == 0) return ok();
+  if (!dtype_ok(dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "bad dtype");
+  kda::ConvArgs ca;
+  kda_status s = check_conv(conv, &ca);
+  if (s != KDA_OK) return s;
+  if (!((Dk == 64 || Dk == 128) && (Dv == 64 || Dv == 128)))
+    return fail(KDA_ERR_UNSUPPORTED, "Dk and Dv must be 64 or 128 (got %d, %d)", Dk, Dv);
+  const long long total = cu_seqlens ? (long long)T : (long long)N * T;
+  if (total > 0) {
+    if (!xq || !xk || !xv || !q || !k || !v)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "x_q, x_k, x_v, q, k and v must be non-null");
+    if (!aligned16(xq) || !aligned16(xk) || !aligned16(xv) || !aligned16(q) || !aligned16(k) ||
+        !aligned16(v))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "token tensors must be 16-byte aligned");
+    if (q == xq || k == xk || v == xv || q == xk || k == xq)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "outputs must not alias the inputs");
+  }
+  if ((conv_state_in && !aligned16(conv_state_in)) || (conv_state_out && !aligned16(conv_state_out)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "conv states must be 16-byte aligned");
+  if (conv_state_out && conv_state_out == conv_state_in)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "conv_state_out must not alias conv_state_in");
+  if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
+  kda::PrologueArgs a;
+  a.xq = xq; a.xk = xk; a.xv = xv; a.bf16 = dtype == KDA_BF16; a.conv = ca;
+  a.st_in = conv_state_in; a.st_out = conv_state_out; a.cu_seqlens = cu_seqlens; a.n_seq = N;
+  a.Tseq = T; a.total = total; a.H = H; a.Dk = Dk; a.Dv = Dv; a.q = q; a.k = k; a.v = v;
+  a.stream = stream;
+  return hip_status(kda::launch_prologue(a));
+}
+
+kda_status kda_epilogue(const void* o, kda_dtype o_dtype, const void* g, kda_dtype g_dtype,
+                        const float* w, float eps, void* y, kda_dtype y_dtype,
+                        long long tokens, int H, int Dv, void* stream) {
+  if (tokens < 0 || H <= 0) return fail(KDA_ERR_INVALID_ARGUMENT, "need tokens >= 0 and H > 0");
+  if (!dtype_ok(o_dtype) || !dtype_ok(g_dtype) || !dtype_ok(y_dtype))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "bad dtype");
+  if (!eps_ok(eps)) return fail(KDA_ERR_INVALID_ARGUMENT, "RMSNorm eps must be finite and > 0");
+  if (Dv != 64 && Dv != 128) return fail(KDA_ERR_UNSUPPORTED, "Dv must be 64 or 128 (got %d)", Dv);
+  if (tokens == 0) return ok();
+  if (!o || !g || !w || !y) return fail(KDA_ERR_INVALID_ARGUMENT, "o, g, w and y must be non-null");
+  if (!aligned16(o) || !aligned16(g) || !aligned16(y) || ((uintptr_t)w & 3u))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "o, g, y must be 16-byte aligned, w 4-byte");
+  if (y == o && y_dtype != o_dtype)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "y may alias o only with the same dtype");
+  kda::EpilogueArgs a;
+  a.o = o; a.o_bf16 = o_dtype == KDA_BF16; a.g = g; a.g_bf16 = g_dtype == KDA_BF16; a.w = w;
+  a.eps = eps; a.y = y; a.y_bf16 = y_dtype == KDA_BF16; a.rows = tokens; a.H = H; a.Dv = Dv;
+  a.stream = stream;
+  return hip_status(kda::launch_epilogue(a));
+}
+
 // Shape and pointer checks shared by verify and commit (q and o are checked by
 // the caller where they exist).
 static kda_status multi_common(const void* k, const void* v, kda_dtype qkv_dtype,

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "kda_common.h"
+#include "kda_layer.h"
 
 namespace kda {
 
@@ -45,6 +46,37 @@ struct PrefillArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
+
+// The layer's prologue and epilogue as standalone passes (kda_layer.hip).
+struct PrologueArgs {
+  const void *xq, *xk, *xv;        // [tokens, H, D] the projections' outputs
+  bool bf16;                       // token tensors bf16 (else fp32)
+  ConvArgs conv;
+  const float* st_in;              // [n_seq, 3, H, 2 Dk + Dv] or null (zeros)
+  float* st_out;                   // same shape or null; not aliasing st_in
+  const int32_t* cu_seqlens;       // packed: [n_seq + 1]; dense: null
+  int n_seq;
+  long long Tseq;                  // dense: tokens per sequence
+  long long total;                 // tokens in all
+  int H, Dk, Dv;
+  void *q, *k, *v;                 // outputs, the token dtype
+  void* stream;
+};
+struct EpilogueArgs {
+  const void* o;                   // [rows, H, Dv]
+  bool o_bf16;
+  const void* g;                   // [rows, H, Dv]
+  bool g_bf16;
+  const float* w;                  // [Dv]
+  float eps;
+  void* y;                         // [rows, H, Dv]
+  bool y_bf16;
+  long long rows;                  // tokens
+  int H, Dv;
+  void* stream;
+};
+hipError_t launch_prologue(const PrologueArgs& a);
+hipError_t launch_epilogue(const EpilogueArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);      // dispatch (kda_prefill.hip)
 hipError_t launch_prefill_f32(const PrefillArgs& a);  // fp32 inputs (kda_prefill_f32.hip)
 bool prefill_supported(bool qkv_bf16, int Dk, int Dv);

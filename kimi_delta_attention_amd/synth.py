@@ -17,6 +17,10 @@ Distributions (the workload recipe):
   stress input (mean alpha about 0.97); ``alpha_one=True`` gives alpha = 1.
 * beta = sigmoid(N(0, 1)) in fp64, stored fp32.
 * initial state ~ N(0, state_std^2) fp32 when requested.
+* layer inputs (``make_layer``): the projections' outputs x_q, x_k, x_v and the
+  output-gate logits g ~ N(0, 1) in the token dtype; conv taps ~ N(0, 0.5^2)
+  fp32 [H, D, 4]; a conv state ~ N(0, 1) fp32 [N, 3, H, 2 Dk + Dv]; the RMSNorm
+  weight ~ U(0.5, 1.5) fp32 [Dv].
 * decay in another gate parametrization (``make_gate``): 'log' stores
   -softplus(z + shift) (the same decays, in log space); 'bounded' stores the
   logits z ~ N(0, 1) with a per-head log scale A ~ U(-1, 1); 'scalar' stores
@@ -159,6 +163,33 @@ def make_gate(kind: str, lead: tuple, H: int, Dk: int, *, seed: int, shift: floa
         a_log = torch.rand(H, generator=g, device=device, dtype=torch.float64) * 2.0 - 1.0
         return z.to(torch.float32), a_log.to(torch.float32)
     raise ValueError(f"unknown gate kind {kind!r}")
+
+
+@dataclass
+class LayerInputs:
+    xq: torch.Tensor          # [B, T, H, Dk]
+    xk: torch.Tensor          # [B, T, H, Dk]
+    xv: torch.Tensor          # [B, T, H, Dv]
+    g: torch.Tensor           # [B, T, H, Dv] output-gate logits
+    wq: torch.Tensor          # [H, Dk, 4]
+    wk: torch.Tensor          # [H, Dk, 4]
+    wv: torch.Tensor          # [H, Dv, 4]
+    conv_state: torch.Tensor  # [N, 3, H, 2 Dk + Dv]
+    norm_w: torch.Tensor      # [Dv]
+
+
+def make_layer(B: int, T: int, H: int, Dk: int, Dv: int, *, seed: int, n_state: int | None = None,
+               dtype=torch.bfloat16, device="cpu") -> LayerInputs:
+    """Seeded inputs of the layer's prologue and epilogue (see the module docstring)."""
+    g = _gen(device, seed * 1_000_037 + 29)
+    rn = lambda *sh: torch.randn(*sh, generator=g, device=device, dtype=torch.float64)  # noqa: E731
+    N = B if n_state is None else n_state
+    return LayerInputs(
+        rn(B, T, H, Dk).to(dtype), rn(B, T, H, Dk).to(dtype), rn(B, T, H, Dv).to(dtype),
+        rn(B, T, H, Dv).to(dtype),
+        (0.5 * rn(H, Dk, 4)).float(), (0.5 * rn(H, Dk, 4)).float(), (0.5 * rn(H, Dv, 4)).float(),
+        rn(N, 3, H, 2 * Dk + Dv).float(),
+        (torch.rand(Dv, generator=g, device=device, dtype=torch.float64) + 0.5).float())
 
 
 # The workloads, named by what they are.

@@ -7,8 +7,10 @@ import oracle
 
 TOL_F32 = 1e-5    # fp32 inputs, fp32 output
 TOL_BF16 = 2e-3   # bf16 q/k/v, fp32 alpha/beta/state/accumulation, fp32 output
-# bf16 output: one extra RNE rounding of o (relative error <= 2^-9 per element)
-TOL_BF16_OUT = TOL_BF16 + 2.0 ** -9
+# bf16 output: one extra RNE rounding of o.  bf16 keeps 8 significant bits, so
+# a rounding to nearest is off by at most 2^-8 relative per element (and so in
+# relative L2)
+TOL_BF16_OUT = TOL_BF16 + 2.0 ** -8
 
 
 def dev():

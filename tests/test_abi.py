@@ -227,3 +227,45 @@ def test_verify_and_commit_validation():
     assert verify(q=None) == INVALID and verify(o=None) == INVALID
     assert verify(q=FAKE + 8) == INVALID
     assert commit(n=None) == INVALID and commit(n=FAKE + 2) == INVALID
+
+
+def test_prologue_epilogue_validation():
+    lib = kda.load()
+    c = _lib._Conv(FAKE, FAKE, FAKE, 1e-6)
+    cp = ctypes.byref(c)
+
+    def pro(**o):
+        a = dict(xq=FAKE, xk=FAKE + 0x100, xv=FAKE + 0x200, dt=BF16, cp=cp, si=None, so=None,
+                 cu=None, N=2, T=8, H=2, Dk=128, Dv=128, q=FAKE + 0x300, k=FAKE + 0x400,
+                 v=FAKE + 0x500)
+        a.update(o)
+        return lib.kda_prologue(a["xq"], a["xk"], a["xv"], a["dt"], a["cp"], a["si"], a["so"],
+                                a["cu"], a["N"], a["T"], a["H"], a["Dk"], a["Dv"], a["q"],
+                                a["k"], a["v"], None)
+
+    assert pro(N=0) == OK
+    assert pro(cp=None) == INVALID
+    assert pro(xq=None) == INVALID and pro(v=None) == INVALID
+    assert pro(xk=FAKE + 8) == INVALID                      # 16-byte alignment
+    assert pro(q=FAKE) == INVALID                           # output aliases x_q
+    assert pro(si=FAKE + 0x600, so=FAKE + 0x600) == INVALID  # states alias
+    assert pro(dt=9) == INVALID and pro(H=0) == INVALID
+    assert pro(Dk=96) == UNSUPPORTED
+    bad = _lib._Conv(FAKE, None, FAKE, 1e-6)
+    assert pro(cp=ctypes.byref(bad)) == INVALID
+    zero_eps = _lib._Conv(FAKE, FAKE, FAKE, 0.0)
+    assert pro(cp=ctypes.byref(zero_eps)) == INVALID
+
+    def epi(**o):
+        a = dict(o=FAKE, od=F32, g=FAKE + 0x100, gd=BF16, w=FAKE + 0x200, eps=1e-5,
+                 y=FAKE + 0x300, yd=BF16, tokens=4, H=2, Dv=128)
+        a.update(o)
+        return lib.kda_epilogue(a["o"], a["od"], a["g"], a["gd"], a["w"], a["eps"], a["y"],
+                                a["yd"], a["tokens"], a["H"], a["Dv"], None)
+
+    assert epi(tokens=0) == OK
+    assert epi(g=None) == INVALID and epi(w=None) == INVALID
+    assert epi(eps=0.0) == INVALID and epi(eps=float("nan")) == INVALID
+    assert epi(y=FAKE) == INVALID                           # aliases o with another dtype
+    assert epi(o=FAKE + 4) == INVALID
+    assert epi(Dv=96) == UNSUPPORTED

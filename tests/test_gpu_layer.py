@@ -1,0 +1,135 @@
+"""The layer's prologue (ShortConv + Swish + L2Norm with the conv state) and
+epilogue (per-head RMSNorm and sigmoid output gate) on the GPU against the fp64
+oracle, and a whole layer's prefill composed of prologue, recurrence and
+epilogue against the oracle's chain of the same steps."""
+import numpy as np
+import pytest
+import torch
+
+import kimi_delta_attention_amd as kda
+import oracle
+from kimi_delta_attention_amd import synth
+from tests._common import TOL_BF16, TOL_F32, dev, rel
+
+pytestmark = pytest.mark.gpu
+
+# one rounding to nearest of the output to bf16 (8 significant bits: relative
+# error <= 2^-8 per element) on top of fp32 arithmetic
+TOL_ROUND = 2.0 ** -8 + 1e-5
+
+
+def _f(x):
+    return x.float().cpu()
+
+
+def _oracle_pro(L, state, lo=None, hi=None):
+    sl = slice(lo, hi)
+    return oracle.prologue(_f(L.xq[:, sl]), _f(L.xk[:, sl]), _f(L.xv[:, sl]), L.wq, L.wk, L.wv,
+                           state=None if state is None else state.cpu())
+
+
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("with_state", [True, False])
+def test_prologue_dense(Dk, Dv, dtype, with_state):
+    d = dev()
+    L = synth.make_layer(2, 150, 3, Dk, Dv, seed=1100 + Dk + Dv, dtype=dtype, device=d)
+    st = L.conv_state if with_state else None
+    q, k, v, so = kda.prologue(L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, conv_state=st)
+    torch.cuda.synchronize()
+    rq, rk, rv, rs = _oracle_pro(L, st)
+    tol = TOL_ROUND if dtype == torch.bfloat16 else TOL_F32
+    for a, r in ((q, rq), (k, rk), (v, rv)):
+        assert rel(a.float().cpu(), r) <= tol
+    assert np.array_equal(so.cpu().numpy(), rs.astype(np.float32))  # inputs, copied exactly
+
+
+def test_prologue_packed_boundaries():
+    """Packed sequences that are empty, shorter than the kernel, cross the
+    kernel's 64-token blocks or share one: each equals the oracle on its own, and
+    each sequence's conv state (an empty one's copied through) is exact."""
+    d = dev()
+    lengths = [0, 1, 2, 70, 3, 0, 130, 64, 5]
+    H, D = 2, 128
+    tot = sum(lengths)
+    L = synth.make_layer(1, tot, H, D, D, seed=1120, n_state=len(lengths), device=d)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device=d)
+    q, k, v, so = kda.prologue(L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, conv_state=L.conv_state,
+                               cu_seqlens=cu)
+    torch.cuda.synchronize()
+    c = cu.cpu().numpy()
+    for i, n in enumerate(lengths):
+        st_i = L.conv_state[i:i + 1]
+        if n == 0:
+            assert torch.equal(so[i], L.conv_state[i])
+            continue
+        rq, rk, rv, rs = oracle.prologue(_f(L.xq[:, c[i]:c[i + 1]]), _f(L.xk[:, c[i]:c[i + 1]]),
+                                         _f(L.xv[:, c[i]:c[i + 1]]), L.wq, L.wk, L.wv,
+                                         state=st_i.cpu())
+        for a, r in ((q, rq), (k, rk), (v, rv)):
+            assert rel(a[:, c[i]:c[i + 1]].float().cpu(), r) <= TOL_ROUND, i
+        assert np.array_equal(so[i:i + 1].cpu().numpy(), rs.astype(np.float32)), i
+
+
+def test_prologue_handover_bitwise():
+    """A prefill cut in two, the conv state handed from the first call to the
+    second, gives bitwise the outputs and final state of one call."""
+    d = dev()
+    L = synth.make_layer(2, 200, 3, 128, 128, seed=1130, device=d)
+    q, k, v, so = kda.prologue(L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, conv_state=L.conv_state)
+    parts = []
+    st = L.conv_state
+    for lo, hi in ((0, 77), (77, 200)):
+        sub = [x[:, lo:hi].contiguous() for x in (L.xq, L.xk, L.xv)]
+        qa, ka, va, st = kda.prologue(*sub, L.wq, L.wk, L.wv, conv_state=st)
+        parts.append((qa, ka, va))
+    torch.cuda.synchronize()
+    for j, full in enumerate((q, k, v)):
+        assert torch.equal(torch.cat([p[j] for p in parts], dim=1), full)
+    assert torch.equal(st, so)
+
+
+@pytest.mark.parametrize("Dv", [128, 64])
+@pytest.mark.parametrize("odt,gdt,ydt", [(torch.float32, torch.bfloat16, torch.bfloat16),
+                                         (torch.float32, torch.float32, torch.float32),
+                                         (torch.bfloat16, torch.bfloat16, torch.float32)])
+def test_epilogue(Dv, odt, gdt, ydt):
+    d = dev()
+    L = synth.make_layer(2, 50, 3, 128, Dv, seed=1140 + Dv, dtype=gdt, device=d)
+    o = (torch.randn(2, 50, 3, Dv, generator=torch.Generator(device=d).manual_seed(7),
+                     device=d) * 0.3).to(odt)
+    y = kda.epilogue(o, L.g, L.norm_w, out_dtype=ydt)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm_gate(_f(o), _f(L.g), L.norm_w.cpu())
+    assert rel(y.float().cpu(), ref) <= (TOL_ROUND if ydt == torch.bfloat16 else TOL_F32)
+    if odt == ydt:  # in place over o
+        o2 = o.clone()
+        kda.epilogue(o2, L.g, L.norm_w, y=o2)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, y)
+
+
+@pytest.mark.parametrize("schedule", ["fused", "two_pass"])
+def test_layer_prefill_composed(schedule):
+    """x -> prologue -> prefill (K3's bounded gate) -> epilogue against the
+    oracle's prologue -> recurrence -> RMSNorm and gate (B=1, T=300, H=4, d=128)."""
+    d = dev()
+    B, T, H, D = 1, 300, 4, 128
+    L = synth.make_layer(B, T, H, D, D, seed=1150, device=d)
+    z, a_log = synth.make_gate("bounded", (B, T), H, D, seed=1151, device=d)
+    beta = torch.sigmoid(torch.randn(B, T, H, generator=torch.Generator(device=d).manual_seed(3),
+                                     device=d))
+    s0 = synth.make_state(B, H, D, D, seed=1152, device=d)
+    q, k, v, cso = kda.prologue(L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, conv_state=L.conv_state)
+    o, s = kda.prefill_chunked(q, k, v, z, beta, initial_state=s0, schedule=schedule,
+                               gate="bounded", a_log=a_log)
+    y = kda.epilogue(o, L.g, L.norm_w, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rq, rk, rv, rcs = _oracle_pro(L, L.conv_state)
+    alpha = oracle.gate_alpha("bounded", z.cpu().numpy(), (B, T, H, D), a_log=a_log.cpu().numpy())
+    ro, rs = oracle.recurrent(rq, rk, rv, alpha, beta.cpu(), initial_state=s0.cpu())
+    ry = oracle.rmsnorm_gate(ro, _f(L.g), L.norm_w.cpu())
+    # q, k, v enter the recurrence rounded to bf16, as the chunked kernels take them
+    assert rel(y.cpu(), ry) <= TOL_BF16 + TOL_ROUND
+    assert rel(s.cpu(), rs) <= TOL_BF16 + TOL_ROUND
+    assert np.array_equal(cso.cpu().numpy(), rcs.astype(np.float32))
