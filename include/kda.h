@@ -321,6 +321,41 @@ kda_status kda_epilogue(const void* o, kda_dtype o_dtype, const void* g, kda_dty
                         long long tokens, int H, int Dv, void* stream);
 
 /*
+ * kda_decode_layer -- the whole recurrent layer step in one kernel, as K3's
+ * inference kernel fuses it ("Kimi K3 的 KDA" section 9: short conv, input
+ * norm, gate, recurrence and output norm): the prologue from the projections'
+ * outputs and the conv state, the decode call of `mode`, the epilogue.
+ *   KDA_DECODE_STEP    N must be 1: y written; state and conv_state advanced
+ *   KDA_DECODE_VERIFY  y of the N tokens; state and conv_state only read
+ *   KDA_DECODE_COMMIT  the first n_accept[b] tokens replayed from their cached
+ *                      projections: state and conv_state advanced; no y
+ *   xq, xk [B, N, H, Dk], xv [B, N, H, Dv]  x_dtype (xq is needed by commit too:
+ *                      the conv state of q advances)
+ *   conv, conv_state   as for kda_prologue, conv_state [B, 3, H, 2 Dk + Dv]
+ *   gate, beta         as for kda_decode_verify ([B, N, H, Dk] / [B, N, H])
+ *   state              [B, H, Dk, Dv] fp32
+ *   out                output gate: g [B, N, H, Dv] x_dtype, w [Dv], eps
+ *   y                  [B, N, H, Dv] y_dtype (not for commit)
+ * With the standalone kda_prologue before and kda_epilogue after the plain call
+ * (its o in fp32), the results are bitwise the same.  Alignment and limits as
+ * for kda_decode_verify.
+ */
+typedef enum { KDA_DECODE_STEP = 0, KDA_DECODE_VERIFY = 1, KDA_DECODE_COMMIT = 2 } kda_decode_mode;
+
+typedef struct {
+    const void* g;     /* [B, N, H, Dv] output-gate logits, the token dtype */
+    const float* w;    /* [Dv] RMSNorm weight */
+    float eps;         /* finite and > 0 (e.g. 1e-5) */
+} kda_out_gate;
+
+kda_status kda_decode_layer(kda_decode_mode mode, const void* xq, const void* xk, const void* xv,
+                            kda_dtype x_dtype, const kda_conv* conv, float* conv_state,
+                            const kda_gate* gate, const float* beta, float* state,
+                            const kda_out_gate* out, void* y, kda_dtype y_dtype,
+                            const int32_t* n_accept, int B, int N, int H, int Dk, int Dv,
+                            void* stream);
+
+/*
  * kda_prefill_workspace_size -- workspace bytes that enable the two-pass
  * schedule of kda_prefill_chunked for these sizes, independent of T (the state
  * is fixed-size, "Kimi K3 混合线性注意力": the per-session state does not grow

@@ -6,8 +6,8 @@ Importing it does not load the library; the first call does, and raises if the
 library has not been built.
 """
 from ._lib import (MAX_DRAFT, KdaError, decode_commit, decode_step,  # noqa: F401
-                   decode_verify, epilogue, load, prefill_chunked, prefill_varlen, prologue,
+                   decode_layer, decode_verify, epilogue, load, prefill_chunked, prefill_varlen, prologue,
                    workspace_size)
 
 __all__ = ["prefill_chunked", "prefill_varlen", "decode_step", "decode_verify", "decode_commit",
-           "prologue", "epilogue", "workspace_size", "load", "KdaError", "MAX_DRAFT"]
+           "decode_layer", "prologue", "epilogue", "workspace_size", "load", "KdaError", "MAX_DRAFT"]

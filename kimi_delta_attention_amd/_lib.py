@@ -21,6 +21,7 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
 EXPORTED = ("kda_prefill_chunked", "kda_prefill_varlen", "kda_decode_step",
             "kda_prefill_chunked_gated", "kda_prefill_varlen_gated", "kda_decode_step_gated",
             "kda_decode_verify", "kda_decode_commit", "kda_prologue", "kda_epilogue",
+            "kda_decode_layer",
             "kda_prefill_workspace_size", "kda_prefill_varlen_workspace_size",
             "kda_prefill_two_pass_preferred", "kda_status_string", "kda_last_error_message")
 
@@ -33,6 +34,13 @@ GATES = {"alpha": 0, "log": 1, "bounded": 2, "scalar": 3, "none": 4}
 class _Conv(ctypes.Structure):
     _fields_ = [("w_q", ctypes.c_void_p), ("w_k", ctypes.c_void_p), ("w_v", ctypes.c_void_p),
                 ("eps", ctypes.c_float)]
+
+
+class _OutGate(ctypes.Structure):
+    _fields_ = [("g", ctypes.c_void_p), ("w", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
+DECODE_MODES = {"step": 0, "verify": 1, "commit": 2}
 
 
 class _Gate(ctypes.Structure):
@@ -83,6 +91,9 @@ def load() -> ctypes.CDLL:
     lib.kda_prologue.restype = I
     lib.kda_epilogue.argtypes = [P, I, P, I, P, ctypes.c_float, P, I, ctypes.c_longlong, I, I, P]
     lib.kda_epilogue.restype = I
+    lib.kda_decode_layer.argtypes = [I, P, P, P, I, C, P, G, P, P, ctypes.POINTER(_OutGate), P, I,
+                                     P, I, I, I, I, I, P]
+    lib.kda_decode_layer.restype = I
     lib.kda_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.kda_prefill_workspace_size.restype = Z
     lib.kda_prefill_varlen_workspace_size.argtypes = [I, I, I, I, I, I]
@@ -421,4 +432,46 @@ def epilogue(o, g, w, eps: float = 1e-5, out_dtype=None, y: torch.Tensor | None 
         _need(y, "y", None, dev)
     _check(load().kda_epilogue(_ptr(o), _dt(o), _ptr(g), _dt(g), _ptr(w), float(eps), _ptr(y),
                                _dt(y), tokens, H, Dv, _stream(dev)))
+    return y
+
+
+
+def decode_layer(mode: str, xq, xk, xv, wq, wk, wv, conv_state, alpha, beta, state, g=None,
+                 norm_w=None, n_accept=None, gate: str = "alpha",
+                 a_log: torch.Tensor | None = None, g_min: float = -5.0, conv_eps: float = 1e-6,
+                 norm_eps: float = 1e-5, out_dtype=torch.float32, y: torch.Tensor | None = None):
+    """The fused recurrent layer step: prologue (conv taps wq, wk [H,Dk,4], wv
+    [H,Dv,4], conv_state [B,3,H,2Dk+Dv]), the decode call of `mode` ('step' with
+    N = 1, 'verify', 'commit' with n_accept), epilogue (g [B,N,H,Dv], norm_w
+    [Dv]).  xq, xk [B,N,H,Dk], xv [B,N,H,Dv] are the projections' outputs.
+    Returns y [B,N,H,Dv] (None for commit); state and conv_state are updated in
+    place by step and commit."""
+    if mode not in DECODE_MODES:
+        raise ValueError(f"mode must be one of {tuple(DECODE_MODES)}")
+    B, N, H, Dk, Dv, dev, gd = _multi_inputs(xk, xv, alpha, beta, gate, a_log, g_min, q=xq)
+    c = _conv(wq, wk, wv, conv_eps, H, Dk, Dv, dev)
+    _need(conv_state, "conv_state", torch.float32, dev)
+    _need(state, "state", torch.float32, dev)
+    if tuple(conv_state.shape) != (B, 3, H, 2 * Dk + Dv) or state.shape != (B, H, Dk, Dv):
+        raise ValueError("conv_state must be [B, 3, H, 2Dk+Dv] and state [B, H, Dk, Dv]")
+    og = _OutGate(None, None, float(norm_eps))
+    if mode == "commit":
+        _need(n_accept, "n_accept", torch.int32, dev)
+        if n_accept.shape != (B,):
+            raise ValueError("n_accept must be [B]")
+        y = None
+    else:
+        _need(g, "g", xq.dtype, dev)
+        _need(norm_w, "norm_w", torch.float32, dev)
+        if g.shape != (B, N, H, Dv) or tuple(norm_w.shape) != (Dv,):
+            raise ValueError("g must be [B, N, H, Dv] and norm_w [Dv]")
+        og = _OutGate(g.data_ptr(), norm_w.data_ptr(), float(norm_eps))
+        if y is None:
+            y = torch.empty(B, N, H, Dv, dtype=out_dtype, device=dev)
+        else:
+            _need(y, "y", None, dev)
+    _check(load().kda_decode_layer(
+        DECODE_MODES[mode], _ptr(xq), _ptr(xk), _ptr(xv), _dt(xq), ctypes.byref(c),
+        _ptr(conv_state), ctypes.byref(gd), _ptr(beta), _ptr(state), ctypes.byref(og), _ptr(y),
+        _dt(y) if y is not None else KDA_F32, _ptr(n_accept), B, N, H, Dk, Dv, _stream(dev)))
     return y

@@ -27,14 +27,26 @@ def build(verbose: bool = False) -> str:
     objs = []
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
+    cmds = []
     for src in SOURCES:
         obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmds.append([HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    # the sources compile independently: run them side by side (bounded by the
+    # host's cores and the job limit the environment sets)
+    jobs = max(1, min(len(cmds), os.cpu_count() or 1, int(os.environ.get("MAX_JOBS", "16"))))
+    running = []
+    for cmd in cmds:
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.check_call(cmd)
-        objs.append(obj)
+        running.append(subprocess.Popen(cmd))
+        if len(running) >= jobs:
+            if running.pop(0).wait() != 0:
+                raise subprocess.CalledProcessError(1, "hipcc")
+    for pr in running:
+        if pr.wait() != 0:
+            raise subprocess.CalledProcessError(1, "hipcc")
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:

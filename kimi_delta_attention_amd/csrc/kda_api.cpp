@@ -377,4 +377,50 @@ kda_status kda_decode_commit(const void* k, const void* v, kda_dtype qkv_dtype,
   return hip_status(kda::launch_decode(a));
 }
 
+kda_status kda_decode_layer(kda_decode_mode mode, const void* xq, const void* xk, const void* xv,
+                            kda_dtype x_dtype, const kda_conv* conv, float* conv_state,
+                            const kda_gate* gate, const float* beta, float* state,
+                            const kda_out_gate* out, void* y, kda_dtype y_dtype,
+                            const int32_t* n_accept, int B, int N, int H, int Dk, int Dv,
+                            void* stream) {
+  if (mode != KDA_DECODE_STEP && mode != KDA_DECODE_VERIFY && mode != KDA_DECODE_COMMIT)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "unknown decode mode %d", (int)mode);
+  if (B < 0 || N < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B and N must be >= 0");
+  if (mode == KDA_DECODE_STEP && N != 1 && B > 0)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "a step takes N == 1 token per session");
+  if (B == 0 || N == 0) return ok();
+  kda::Gate g;
+  kda_status s = multi_common(xk, xv, x_dtype, gate, beta, state, B, N, H, Dk, Dv, &g);
+  if (s != KDA_OK) return s;
+  kda::ConvArgs ca;
+  if ((s = check_conv(conv, &ca)) != KDA_OK) return s;
+  if (!xq || !aligned16(xq)) return fail(KDA_ERR_INVALID_ARGUMENT, "x_q must be non-null and 16-byte aligned");
+  if (!conv_state || !aligned16(conv_state))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "conv_state must be non-null and 16-byte aligned");
+  kda::OutGateArgs og = {nullptr, nullptr, 1.f};
+  if (mode != KDA_DECODE_COMMIT) {
+    if (!out || !out->g || !out->w || !y)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "the output gate (g, w) and y must be non-null");
+    if (!aligned16(out->g) || ((uintptr_t)out->w & 3u) || !aligned16(y))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "g and y must be 16-byte aligned, w 4-byte");
+    if (!eps_ok(out->eps)) return fail(KDA_ERR_INVALID_ARGUMENT, "RMSNorm eps must be finite and > 0");
+    if (!dtype_ok(y_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "bad y_dtype");
+    og.g = out->g; og.w = out->w; og.eps = out->eps;
+  } else if (!n_accept || ((uintptr_t)n_accept & 3u)) {
+    return fail(KDA_ERR_INVALID_ARGUMENT, "n_accept must be non-null and 4-byte aligned");
+  }
+  kda::DecodeArgs a;
+  a.q = nullptr; a.k = nullptr; a.v = nullptr; a.gate = g; a.beta = beta; a.state = state;
+  a.o = mode == KDA_DECODE_COMMIT ? nullptr : y;
+  a.qkv_bf16 = x_dtype == KDA_BF16; a.o_bf16 = mode != KDA_DECODE_COMMIT && y_dtype == KDA_BF16;
+  a.B = B; a.H = H; a.Dk = Dk; a.Dv = Dv; a.stream = stream;
+  a.mode = mode == KDA_DECODE_STEP ? kda::DECODE_STEP
+         : mode == KDA_DECODE_VERIFY ? kda::DECODE_VERIFY : kda::DECODE_COMMIT;
+  a.N = N; a.n_accept = n_accept;
+  a.layer = true;
+  a.io.xq = xq; a.io.xk = xk; a.io.xv = xv; a.io.conv = ca; a.io.conv_state = conv_state;
+  a.io.out = og;
+  return hip_status(kda::launch_decode(a));
+}
+
 }  // extern "C"

@@ -30,6 +30,7 @@
 // vectors permuted so each lane reads its rows as contiguous 16-byte words.
 #include "kda_common.h"
 #include "kda_internal.h"
+#include "kda_layer.h"
 
 // Every product and sum is rounded on its own (no fused multiply-add
 // contraction): the one-token step and the multi-token kernels evaluate the
@@ -179,6 +180,40 @@ __device__ __forceinline__ void ld_rows(const float* p, float (&x)[NP]) {
   }
 }
 
+// Prologue of token t's row of one tensor for the fused layer, from the raw
+// rows staged in LDS (xr: [3 + n][2 Dk + Dv], the conv state's three rows and
+// then the tokens') and the head's taps of the tensor staged in LDS ([D][4]),
+// rounded to the token dtype as the standalone prologue stores it, into the
+// token's record: k (with alpha k), q (with alpha q) or v.
+template <typename TIn, int CPL, bool NORM, int NP, int RPP>
+__device__ __forceinline__ void layer_row(const float* xr, const float* taps, float eps, int t,
+                                          int off, int SW, int lane, float* dst, float* adst,
+                                          const float* al) {
+  float hist[3][CPL], xc[CPL], w[CPL][4], y[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int ch = CPL * lane + c;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[c][j] = taps[ch * 4 + j];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) hist[j][c] = xr[(t + j) * SW + off + ch];
+    xc[c] = xr[(t + 3) * SW + off + ch];
+  }
+  prologue_row<CPL, NORM>(hist, xc, w, eps, y);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int ch = CPL * lane + c;
+    const float yr = (float)(TIn)y[c];
+    if (adst) {  // key-side vectors: permuted record rows, alpha-scaled copy
+      const int pos = (ch % RPP) * NP + ch / RPP;
+      dst[pos] = yr;
+      adst[pos] = al[pos] * yr;
+    } else {
+      dst[ch] = yr;
+    }
+  }
+}
+
 // One kernel for the three decode calls, by MODE:
 //   DECODE_STEP    one token (N = 1): output written, state written in place
 //   DECODE_VERIFY  tokens 0..N-1: outputs written, state untouched
@@ -187,12 +222,17 @@ __device__ __forceinline__ void ld_rows(const float* p, float (&x)[NP]) {
 // All of them stage the tokens' inputs in LDS (one coalesced pass, alpha and the
 // alpha-scaled vectors formed once) and step the state held in registers with
 // token_step, so the three calls agree bitwise.
-template <int DK, int DV, typename TIn, typename TOut, int KIND, int MODE>
+// LAYER: the whole recurrent layer step of "Kimi K3 的 KDA" section 9 in one
+// kernel -- q, k, v come from the projections' outputs through the prologue
+// (the conv state read, and advanced by step and commit), and the outputs leave
+// through the epilogue (RMSNorm and gate) as y; with the standalone prologue and
+// epilogue around the plain call the results are bitwise the same.
+template <int DK, int DV, typename TIn, typename TOut, int KIND, int MODE, bool LAYER>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     Gate gate, const float* __restrict__ beta, float* __restrict__ state, TOut* __restrict__ o,
-    const int32_t* __restrict__ n_accept, int N, int H) {
+    const int32_t* __restrict__ n_accept, int N, int H, LayerIO io) {
   constexpr bool VERIFY = MODE != DECODE_COMMIT;  // outputs (and q) needed
   constexpr bool WRITE = MODE != DECODE_VERIFY;   // state written back
   using G = Geo<DK, DV>;
@@ -217,39 +257,129 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
 
   float* S = state + (size_t)tile * DK * DV;
   floatx4 s[NP];
+  auto load_state = [&]() {
 #pragma unroll
-  for (int i = 0; i < NP; ++i)
-    s[i] = *reinterpret_cast<const floatx4*>(S + (size_t)(ro + RPP * i) * DV + col);
+    for (int i = 0; i < NP; ++i)
+      s[i] = *reinterpret_cast<const floatx4*>(S + (size_t)(ro + RPP * i) * DV + col);
+  };
+  // the plain calls fetch the state first; the layer issues its (smaller)
+  // staging loads first, so that the prologue rows -- which wait for them,
+  // and with them for every load issued earlier -- run while the state is
+  // still arriving
+  if constexpr (!LAYER) load_state();
+
+  constexpr int SW = 2 * DK + DV;                  // conv-state row: q | k | v
+  // LAYER: the raw rows [3 + n][SW] (conv state, then the tokens' projections),
+  // the gate logits [n][Dv] and the head's conv taps [SW][4]; the raw rows'
+  // space later holds o [n][Dv]
+  float* xr = rec + R::stride * N;
+  float* gs = xr + (N + 3) * SW;
+  float* tp = gs + N * DV;
+  constexpr int CPLV = DV / 64;
+  float wn[CPLV];  // RMSNorm weight of the lane's channels (layer epilogue)
+  if constexpr (LAYER) {
+    for (int idx = tid; idx < SW; idx += 256) {
+      const int ten = idx < DK ? 0 : idx < 2 * DK ? 1 : 2;
+      const int ch = idx - (ten == 0 ? 0 : ten == 1 ? DK : 2 * DK);
+      const int D = ten == 2 ? DV : DK;
+      *reinterpret_cast<floatx4*>(tp + 4 * idx) =
+          *reinterpret_cast<const floatx4*>(io.conv.w[ten] + ((size_t)h * D + ch) * 4);
+    }
+    if constexpr (VERIFY) {
+#pragma unroll
+      for (int c = 0; c < CPLV; ++c) wn[c] = io.out.w[CPLV * lane + c];
+    }
+    const float* cs = io.conv_state + ((size_t)sb * 3 * H + h) * SW;
+    for (int idx = tid; idx < 3 * (SW / 4); idx += 256) {
+      const int j = idx / (SW / 4), c = 4 * (idx % (SW / 4));
+      *reinterpret_cast<floatx4*>(xr + j * SW + c) =
+          *reinterpret_cast<const floatx4*>(cs + (size_t)j * H * SW + c);
+    }
+    for (int idx = tid; idx < n * (SW / 4); idx += 256) {
+      const int t = idx / (SW / 4), c = 4 * (idx % (SW / 4));
+      const size_t row = ((size_t)sb * N + t) * H + h;
+      floatx4 x4;
+      if (c < DK) x4 = ld4<TIn>((const TIn*)io.xq + row * DK + c);
+      else if (c < 2 * DK) x4 = ld4<TIn>((const TIn*)io.xk + row * DK + c - DK);
+      else x4 = ld4<TIn>((const TIn*)io.xv + row * DV + c - 2 * DK);
+      *reinterpret_cast<floatx4*>(xr + (3 + t) * SW + c) = x4;
+    }
+    if constexpr (VERIFY) {
+      for (int idx = tid; idx < n * (DV / 4); idx += 256) {
+        const int t = idx / (DV / 4), c = 4 * (idx % (DV / 4));
+        const size_t row = ((size_t)sb * N + t) * H + h;
+        *reinterpret_cast<floatx4*>(gs + t * DV + c) = ld4<TIn>((const TIn*)io.out.g + row * DV + c);
+      }
+    }
+  }
 
   // stage the n tokens' inputs (alpha and the alpha-scaled vectors formed once)
   const float sc = KIND == GATE_BOUNDED ? expf(gate.a_log[h]) : 1.f;
   for (int idx = tid; idx < n * (DK / 4); idx += 256) {
     const int t = idx / (DK / 4), c = 4 * (idx % (DK / 4));
     const size_t row = ((size_t)sb * N + t) * H + h;
-    const floatx4 k4 = ld4<TIn>(k + row * DK + c);
     const floatx4 a4 = alpha4_exact<KIND>(gate, row, DK, c, sc);
-    floatx4 q4 = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (VERIFY) q4 = ld4<TIn>(q + row * DK + c);
     float* rt = rec + t * R::stride;
+    if constexpr (LAYER) {  // k and q come from the prologue rows below
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int pos = ((c + e) % RPP) * NP + (c + e) / RPP;
-      rt[R::K + pos] = k4[e];
-      rt[R::AK + pos] = a4[e] * k4[e];
-      rt[R::AL + pos] = a4[e];
-      if constexpr (VERIFY) {
-        rt[R::Q + pos] = q4[e];
-        rt[R::AQ + pos] = a4[e] * q4[e];
+      for (int e = 0; e < 4; ++e) rt[R::AL + ((c + e) % RPP) * NP + (c + e) / RPP] = a4[e];
+    } else {
+      const floatx4 k4 = ld4<TIn>(k + row * DK + c);
+      floatx4 q4 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (VERIFY) q4 = ld4<TIn>(q + row * DK + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pos = ((c + e) % RPP) * NP + (c + e) / RPP;
+        rt[R::K + pos] = k4[e];
+        rt[R::AK + pos] = a4[e] * k4[e];
+        rt[R::AL + pos] = a4[e];
+        if constexpr (VERIFY) {
+          rt[R::Q + pos] = q4[e];
+          rt[R::AQ + pos] = a4[e] * q4[e];
+        }
       }
     }
   }
-  for (int idx = tid; idx < n * (DV / 4); idx += 256) {
-    const int t = idx / (DV / 4), c = 4 * (idx % (DV / 4));
-    const size_t row = ((size_t)sb * N + t) * H + h;
-    *reinterpret_cast<floatx4*>(rec + t * R::stride + R::V + c) = ld4<TIn>(v + row * DV + c);
+  if constexpr (!LAYER) {
+    for (int idx = tid; idx < n * (DV / 4); idx += 256) {
+      const int t = idx / (DV / 4), c = 4 * (idx % (DV / 4));
+      const size_t row = ((size_t)sb * N + t) * H + h;
+      *reinterpret_cast<floatx4*>(rec + t * R::stride + R::V + c) = ld4<TIn>(v + row * DV + c);
+    }
   }
   if (tid < n) rec[tid * R::stride + R::Bt] = beta[((size_t)sb * N + tid) * H + h];
+  if constexpr (LAYER) load_state();
   __syncthreads();
+  if constexpr (LAYER) {
+    // prologue rows into the records, one wave per (token, tensor); commit
+    // needs no q
+    for (int r = w; r < 3 * n; r += 4) {
+      const int t = r / 3, ten = r - 3 * (r / 3);
+      float* rt = rec + t * R::stride;
+      if (ten == 0) {
+        if constexpr (VERIFY)
+          layer_row<TIn, DK / 64, true, NP, RPP>(xr, tp, io.conv.eps, t, 0, SW, lane, rt + R::Q,
+                                                 rt + R::AQ, rt + R::AL);
+      } else if (ten == 1) {
+        layer_row<TIn, DK / 64, true, NP, RPP>(xr, tp + 4 * DK, io.conv.eps, t, DK, SW, lane,
+                                               rt + R::K, rt + R::AK, rt + R::AL);
+      } else {
+        layer_row<TIn, DV / 64, false, NP, RPP>(xr, tp + 8 * DK, io.conv.eps, t, 2 * DK, SW,
+                                                lane, rt + R::V, nullptr, nullptr);
+      }
+    }
+    if constexpr (MODE != DECODE_VERIFY) {
+      // the conv state advances past the n tokens: its new rows are the last
+      // three of the raw rows
+      float* cs = io.conv_state + ((size_t)sb * 3 * H + h) * SW;
+      for (int idx = tid; idx < 3 * (SW / 4); idx += 256) {
+        const int j = idx / (SW / 4), c = 4 * (idx % (SW / 4));
+        *reinterpret_cast<floatx4*>(cs + (size_t)j * H * SW + c) =
+            *reinterpret_cast<const floatx4*>(xr + (n + j) * SW + c);
+      }
+    }
+    __syncthreads();
+  }
   if constexpr (MODE == DECODE_VERIFY) {
     // q.k of each token (the loop below computes it in place for a single step)
     for (int t = w; t < n; t += 4) {
@@ -285,10 +415,31 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
     const floatx4 ov = token_step<NP, LPR>(s, kr, ak, aq, al, qk, rt[R::Bt], vv);
     if constexpr (VERIFY) {
       if (ro == 0) {
-        TOut* ot = o + (((size_t)sb * N + t) * H + h) * DV + col;
+        if constexpr (LAYER) {
+          // to the epilogue, through LDS (the raw rows are consumed)
+          *reinterpret_cast<floatx4*>(xr + t * DV + col) = ov;
+        } else {
+          TOut* ot = o + (((size_t)sb * N + t) * H + h) * DV + col;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ot[j] = (TOut)ov[j];
+          for (int j = 0; j < 4; ++j) ot[j] = (TOut)ov[j];
+        }
       }
+    }
+  }
+  if constexpr (LAYER && VERIFY) {
+    // epilogue rows, one wave per token: y = RMSNorm(o) w Sigmoid(g)
+    __syncthreads();
+    constexpr int CPL = CPLV;
+    for (int t = w; t < n; t += 4) {
+      float ov[CPL], gv[CPL], y[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        ov[c] = xr[t * DV + CPL * lane + c];
+        gv[c] = gs[t * DV + CPL * lane + c];
+      }
+      const size_t row = (((size_t)sb * N + t) * H + h) * DV;
+      epilogue_row<CPL>(ov, gv, wn, io.out.eps, y);
+      row_store<TOut, CPL>(o + row, lane, y);
     }
   }
   if constexpr (WRITE) {
@@ -302,31 +453,65 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
   }
 }
 
+// LDS of one workgroup: N token records; with the layer, the raw rows
+// [3 + N][2 Dk + Dv], the gate logits [N][Dv] and the conv taps [2 Dk + Dv][4]
 template <int DK, int DV, bool VERIFY>
-constexpr int multi_lds_bytes(int N) {
-  return (int)sizeof(float) * Rec<DK, DV, VERIFY>::stride * N;
+constexpr int multi_lds_bytes(int N, bool layer = false) {
+  return (int)sizeof(float) * (Rec<DK, DV, VERIFY>::stride * N +
+                               (layer ? (N + 7) * (2 * DK + DV) + N * DV : 0));
+}
+
+// the largest LDS a mode's instantiation may ask for (N up to kMaxDraft),
+// granted once per instantiation before its first launch
+template <typename K>
+static hipError_t allow_lds(K kern, int bytes, bool& done) {
+  if (done || bytes <= 65536) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     bytes);
+  if (e == hipSuccess) done = true;
+  return e;
+}
+
+template <int DK, int DV, typename TIn, typename TOut, int KIND, bool LAYER>
+static hipError_t launch_decode_l(const DecodeArgs& a) {
+  const dim3 grid(a.B * a.H);
+  static bool lds_v = false, lds_c = false;  // per instantiation; idempotent if raced
+  if (a.mode == DECODE_VERIFY) {
+    if (hipError_t e = allow_lds(decode_kernel<DK, DV, TIn, TOut, KIND, DECODE_VERIFY, LAYER>,
+                                 multi_lds_bytes<DK, DV, true>(kMaxDraft, LAYER), lds_v);
+        e != hipSuccess)
+      return e;
+  } else if (a.mode == DECODE_COMMIT) {
+    if (hipError_t e = allow_lds(decode_kernel<DK, DV, TIn, float, KIND, DECODE_COMMIT, LAYER>,
+                                 multi_lds_bytes<DK, DV, false>(kMaxDraft, LAYER), lds_c);
+        e != hipSuccess)
+      return e;
+  }
+  if (a.mode == DECODE_STEP) {
+    hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, TOut, KIND, DECODE_STEP, LAYER>), grid,
+                       dim3(256), (multi_lds_bytes<DK, DV, true>(1, LAYER)), (hipStream_t)a.stream,
+                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.gate, a.beta, a.state,
+                       (TOut*)a.o, (const int32_t*)nullptr, 1, a.H, a.io);
+  } else if (a.mode == DECODE_VERIFY) {
+    hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, TOut, KIND, DECODE_VERIFY, LAYER>), grid,
+                       dim3(256), (multi_lds_bytes<DK, DV, true>(a.N, LAYER)),
+                       (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
+                       a.gate, a.beta, a.state, (TOut*)a.o, (const int32_t*)nullptr, a.N, a.H,
+                       a.io);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, float, KIND, DECODE_COMMIT, LAYER>), grid,
+                       dim3(256), (multi_lds_bytes<DK, DV, false>(a.N, LAYER)),
+                       (hipStream_t)a.stream, (const TIn*)nullptr, (const TIn*)a.k,
+                       (const TIn*)a.v, a.gate, a.beta, a.state, (float*)nullptr, a.n_accept, a.N,
+                       a.H, a.io);
+  }
+  return hipGetLastError();
 }
 
 template <int DK, int DV, typename TIn, typename TOut, int KIND>
 static hipError_t launch_decode_k(const DecodeArgs& a) {
-  const dim3 grid(a.B * a.H);
-  if (a.mode == DECODE_STEP) {
-    hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, TOut, KIND, DECODE_STEP>), grid, dim3(256),
-                       (multi_lds_bytes<DK, DV, true>(1)), (hipStream_t)a.stream,
-                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.gate, a.beta, a.state,
-                       (TOut*)a.o, (const int32_t*)nullptr, 1, a.H);
-  } else if (a.mode == DECODE_VERIFY) {
-    hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, TOut, KIND, DECODE_VERIFY>), grid, dim3(256),
-                       (multi_lds_bytes<DK, DV, true>(a.N)), (hipStream_t)a.stream,
-                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.gate, a.beta, a.state,
-                       (TOut*)a.o, (const int32_t*)nullptr, a.N, a.H);
-  } else {
-    hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, float, KIND, DECODE_COMMIT>), grid, dim3(256),
-                       (multi_lds_bytes<DK, DV, false>(a.N)), (hipStream_t)a.stream,
-                       (const TIn*)nullptr, (const TIn*)a.k, (const TIn*)a.v, a.gate, a.beta,
-                       a.state, (float*)nullptr, a.n_accept, a.N, a.H);
-  }
-  return hipGetLastError();
+  return a.layer ? launch_decode_l<DK, DV, TIn, TOut, KIND, true>(a)
+                 : launch_decode_l<DK, DV, TIn, TOut, KIND, false>(a);
 }
 
 // one instantiation per gate kind: the per-row decay is a straight-line loop

@@ -24,6 +24,8 @@ struct DecodeArgs {
   int mode = DECODE_STEP;
   int N = 1;                          // tokens per session (verify, commit)
   const int32_t* n_accept = nullptr;  // commit: accepted tokens per session
+  bool layer = false;                 // the fused layer step (io below; o receives y)
+  LayerIO io{};
 };
 
 struct PrefillArgs {

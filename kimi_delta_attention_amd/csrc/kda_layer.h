@@ -13,8 +13,11 @@
 //     y = o / sqrt(mean o^2 + eps) * w * Sigmoid(g)   over the head's Dv channels
 //
 // A row of D channels is handled by one wave: lane l holds channels 2l, 2l + 1
-// (D = 128) or channel l (D = 64); row sums use one fixed xor butterfly, so
-// every lane holds bitwise the same sum.
+// (D = 128) or channel l (D = 64).  Row sums pair lanes with DPP row rotations
+// by 8, 4, 2 and 1 and then the permlane16 / permlane32 swaps: each step adds
+// the same pairs in every lane, so every lane holds bitwise the same sum.
+// Transcendentals use the hardware units (exp2, reciprocal, reciprocal square
+// root, each about 1 ulp): Swish(a) = a / (1 + 2^(-a log2 e)).
 #pragma once
 
 #include "kda_common.h"
@@ -32,13 +35,40 @@ struct OutGateArgs {
   float eps;
 };
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
-  return x;
+// The fused layer decode step's extra operands: the projections' outputs of the
+// call's tokens ([B, N, H, D], the token dtype), the conv taps and state
+// ([B, 3, H, 2 Dk + Dv] fp32), and the output gate.
+struct LayerIO {
+  const void *xq, *xk, *xv;
+  ConvArgs conv;
+  float* conv_state;
+  OutGateArgs out;
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 
-__device__ __forceinline__ float swish(float a) { return a / (1.f + expf(-a)); }
+__device__ __forceinline__ float wave_sum(float x) {
+  x = dpp_add<0x128>(x);  // row_ror:8
+  x = dpp_add<0x124>(x);  // row_ror:4
+  x = dpp_add<0x122>(x);  // row_ror:2
+  x = dpp_add<0x121>(x);  // row_ror:1
+  const unsigned xb = __float_as_uint(x);
+  const auto h = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
+  x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  const unsigned yb = __float_as_uint(x);
+  const auto w = __builtin_amdgcn_permlane32_swap(yb, yb, false, false);
+  return __uint_as_float(w[0]) + __uint_as_float(w[1]);
+}
+
+// Sigmoid(a) = 1 / (1 + 2^(-a log2 e)) on the hardware units
+__device__ __forceinline__ float sigmoid_hw(float a) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-a * 1.44269504088896341f));
+}
+
+__device__ __forceinline__ float swish(float a) { return a * sigmoid_hw(a); }
 
 template <typename T>
 __device__ __forceinline__ float to_f(T x) { return (float)x; }
@@ -72,7 +102,7 @@ __device__ __forceinline__ void prologue_row(const float (&h)[3][CPL], const flo
     ss = __builtin_fmaf(y[c], y[c], ss);
   }
   if constexpr (NORM) {
-    const float r = 1.f / sqrtf(wave_sum(ss) + eps);
+    const float r = __builtin_amdgcn_rsqf(wave_sum(ss) + eps);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) y[c] *= r;
   }
@@ -86,9 +116,9 @@ __device__ __forceinline__ void epilogue_row(const float (&o)[CPL], const float 
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) ss = __builtin_fmaf(o[c], o[c], ss);
-  const float r = 1.f / sqrtf(wave_sum(ss) * (1.f / (64 * CPL)) + eps);
+  const float r = __builtin_amdgcn_rsqf(wave_sum(ss) * (1.f / (64 * CPL)) + eps);
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) y[c] = o[c] * r * w[c] / (1.f + expf(-g[c]));
+  for (int c = 0; c < CPL; ++c) y[c] = o[c] * r * w[c] * sigmoid_hw(g[c]);
 }
 
 }  // namespace kda

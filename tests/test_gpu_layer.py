@@ -133,3 +133,116 @@ def test_layer_prefill_composed(schedule):
     assert rel(y.cpu(), ry) <= TOL_BF16 + TOL_ROUND
     assert rel(s.cpu(), rs) <= TOL_BF16 + TOL_ROUND
     assert np.array_equal(cso.cpu().numpy(), rcs.astype(np.float32))
+
+
+def _layer_case(B, N, H, Dk, Dv, seed, kind, dtype, d):
+    L = synth.make_layer(B, N, H, Dk, Dv, seed=seed, dtype=dtype, device=d)
+    if kind == "alpha":
+        gate, a_log = synth.make_dense(B, N, H, Dk, Dv, seed=seed, device=d).alpha, None
+    else:
+        gate, a_log = synth.make_gate(kind, (B, N), H, Dk, seed=seed + 1, device=d)
+    beta = torch.sigmoid(torch.randn(B, N, H, generator=torch.Generator(device=d).manual_seed(seed),
+                                     device=d))
+    s0 = synth.make_state(B, H, Dk, Dv, seed=seed + 2, device=d)
+    return L, gate, a_log, beta, s0
+
+
+@pytest.mark.parametrize("kind", ["alpha", "bounded"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 128)])
+def test_decode_layer_step_equals_composed(kind, dtype, Dk, Dv):
+    """One fused layer step is bitwise the standalone prologue, the decode step
+    (fp32 o) and the standalone epilogue, conv state and state included."""
+    d = dev()
+    B, H = 3, 4
+    L, gate, a_log, beta, s0 = _layer_case(B, 1, H, Dk, Dv, 1200 + Dk, kind, dtype, d)
+    cs, st = L.conv_state.clone(), s0.clone()
+    y = kda.decode_layer("step", L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, cs, gate, beta, st, L.g,
+                         L.norm_w, gate=kind, a_log=a_log, out_dtype=dtype)
+    q, k, v, cso = kda.prologue(L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, conv_state=L.conv_state)
+    st2 = s0.clone()
+    o = kda.decode_step(q[:, 0], k[:, 0], v[:, 0], gate[:, 0].contiguous(), beta[:, 0].contiguous(),
+                        st2, gate=kind, a_log=a_log)
+    y2 = kda.epilogue(o, L.g[:, 0].contiguous(), L.norm_w, out_dtype=dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:, 0], y2) and torch.equal(st, st2) and torch.equal(cs, cso)
+
+
+@pytest.mark.parametrize("kind", ["alpha", "bounded", "scalar"])
+def test_decode_layer_spec_round_equals_composed(kind):
+    """Fused verify: bitwise the composed verify, conv state and state untouched.
+    Fused commit of seeded prefixes: the state bitwise the plain commit of the
+    prologue's k, v; the conv state exactly the oracle's after each prefix."""
+    d = dev()
+    B, N, H, D = 4, 6, 3, 128
+    L, gate, a_log, beta, s0 = _layer_case(B, N, H, D, D, 1220, kind, torch.bfloat16, d)
+    cs, st = L.conv_state.clone(), s0.clone()
+    y = kda.decode_layer("verify", L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, cs, gate, beta, st, L.g,
+                         L.norm_w, gate=kind, a_log=a_log)
+    q, k, v, _ = kda.prologue(L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, conv_state=L.conv_state)
+    o = kda.decode_verify(q, k, v, gate, beta, s0, gate=kind, a_log=a_log)
+    y2 = kda.epilogue(o, L.g, L.norm_w, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    assert torch.equal(cs, L.conv_state) and torch.equal(st, s0)
+    n_acc = torch.tensor([N, 0, 2, 5], dtype=torch.int32, device=d)
+    kda.decode_layer("commit", L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, cs, gate, beta, st,
+                     n_accept=n_acc, gate=kind, a_log=a_log)
+    st2 = s0.clone()
+    kda.decode_commit(k, v, gate, beta, n_acc, st2, gate=kind, a_log=a_log)
+    torch.cuda.synchronize()
+    assert torch.equal(st, st2)
+    for b, n in enumerate(n_acc.tolist()):
+        if n == 0:
+            assert torch.equal(cs[b], L.conv_state[b])
+            continue
+        *_, rs = oracle.prologue(_f(L.xq[b:b + 1, :n]), _f(L.xk[b:b + 1, :n]),
+                                 _f(L.xv[b:b + 1, :n]), L.wq, L.wk, L.wv,
+                                 state=L.conv_state[b:b + 1].cpu())
+        assert np.array_equal(cs[b:b + 1].cpu().numpy(), rs.astype(np.float32)), b
+
+
+def test_decode_layer_steps_against_oracle():
+    """Seven fused layer steps from given conv and recurrent states against the
+    oracle's prologue, recurrence and epilogue over the seven tokens."""
+    d = dev()
+    B, T, H, D = 2, 7, 4, 128
+    L, gate, a_log, beta, s0 = _layer_case(B, T, H, D, D, 1240, "bounded", torch.bfloat16, d)
+    cs, st = L.conv_state.clone(), s0.clone()
+    ys = []
+    for t in range(T):
+        sl = lambda x: x[:, t:t + 1].contiguous()  # noqa: E731
+        ys.append(kda.decode_layer("step", sl(L.xq), sl(L.xk), sl(L.xv), L.wq, L.wk, L.wv, cs,
+                                   sl(gate), sl(beta), st, sl(L.g), L.norm_w, gate="bounded",
+                                   a_log=a_log))
+    torch.cuda.synchronize()
+    y = torch.cat(ys, dim=1)
+    rq, rk, rv, rcs = oracle.prologue(_f(L.xq), _f(L.xk), _f(L.xv), L.wq, L.wk, L.wv,
+                                      state=L.conv_state.cpu())
+    alpha = oracle.gate_alpha("bounded", gate.cpu().numpy(), (B, T, H, D), a_log=a_log.cpu().numpy())
+    ro, rs = oracle.recurrent(rq, rk, rv, alpha, beta.cpu(), initial_state=s0.cpu())
+    ry = oracle.rmsnorm_gate(ro, _f(L.g), L.norm_w.cpu())
+    assert rel(y.cpu(), ry) <= TOL_BF16 + TOL_ROUND
+    assert rel(st.cpu(), rs) <= TOL_BF16 + TOL_ROUND
+    assert np.array_equal(cs.cpu().numpy(), rcs.astype(np.float32))
+
+
+def test_decode_layer_max_draft():
+    """16 draft tokens (the largest LDS footprint of the fused layer): verify and
+    commit bitwise the composed calls."""
+    d = dev()
+    B, N, H, D = 2, 16, 2, 128
+    L, gate, a_log, beta, s0 = _layer_case(B, N, H, D, D, 1260, "alpha", torch.bfloat16, d)
+    cs, st = L.conv_state.clone(), s0.clone()
+    y = kda.decode_layer("verify", L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, cs, gate, beta, st, L.g,
+                         L.norm_w)
+    q, k, v, cso = kda.prologue(L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, conv_state=L.conv_state)
+    y2 = kda.epilogue(kda.decode_verify(q, k, v, gate, beta, s0), L.g, L.norm_w,
+                      out_dtype=torch.float32)
+    n_acc = torch.full((B,), N, dtype=torch.int32, device=d)
+    kda.decode_layer("commit", L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, cs, gate, beta, st,
+                     n_accept=n_acc)
+    st2 = s0.clone()
+    kda.decode_commit(k, v, gate, beta, n_acc, st2)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(st, st2) and torch.equal(cs, cso)
