@@ -220,6 +220,36 @@ def main():
           f" = {rnd_ms * 1e3:.1f} us ({NS * dec_ms / rnd_ms:.2f}x {NS} decode steps)",
           file=sys.stderr, flush=True)
 
+    # the layer around the recurrence: the fused layer decode step (prologue +
+    # step + epilogue in one kernel) against the three calls, and the standalone
+    # prologue / epilogue over the prefill layer
+    lay = synth.make_layer(wd["B"], 1, wd["H"], wd["D"], wd["D"], seed=wd["seed"] + 200,
+                           device=d)
+    lst, lcs = dec.state.clone(), lay.conv_state.clone()
+    ly = torch.empty(wd["B"], 1, wd["H"], wd["D"], dtype=torch.bfloat16, device=d)
+    layer_ms = timed(lambda: kda.decode_layer("step", lay.xq, lay.xk, lay.xv, lay.wq, lay.wk,
+                                              lay.wv, lcs, dec.alpha, dec.beta, lst, lay.g,
+                                              lay.norm_w, y=ly), args.decode_steps)
+    lcs2 = torch.empty_like(lcs)
+    g1 = lay.g[:, 0].contiguous()
+    ly1 = torch.empty(wd["B"], wd["H"], wd["D"], dtype=torch.bfloat16, device=d)
+
+    def composed():
+        q1, k1, v1, _ = kda.prologue(lay.xq, lay.xk, lay.xv, lay.wq, lay.wk, lay.wv,
+                                     conv_state=lcs, conv_state_out=lcs2)
+        o1 = kda.decode_step(q1[:, 0], k1[:, 0], v1[:, 0], da, db, lst, o=od)
+        kda.epilogue(o1, g1, lay.norm_w, y=ly1)
+
+    comp_ms = timed(composed, args.decode_steps)
+    pl = synth.make_layer(B, T, H, D, D, seed=w["seed"] + 300, device=d)
+    pro_ms = timed(lambda: kda.prologue(pl.xq, pl.xk, pl.xv, pl.wq, pl.wk, pl.wv,
+                                        conv_state=pl.conv_state), 10)
+    py = torch.empty(B, T, H, D, dtype=torch.bfloat16, device=d)
+    epi_ms = timed(lambda: kda.epilogue(o, pl.g, pl.norm_w, y=py), 10)
+    print(f"bench: layer decode step {layer_ms * 1e3:.1f} us fused vs {comp_ms * 1e3:.1f} us "
+          f"composed; prefill prologue {pro_ms * 1e3:.1f} us, epilogue {epi_ms * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu:
         import oracle
@@ -281,6 +311,12 @@ def main():
                         "roofline": {"bound": "hbm", "achieved": spec_bytes / (rnd_ms / 1e3) / 1e9,
                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                      "frac": spec_bytes / (rnd_ms / 1e3) / 1e9 / HBM_PEAK_GBS}},
+        "layer": {"decode_step_fused_us": layer_ms * 1e3, "decode_step_composed_us": comp_ms * 1e3,
+                  "decode_workload": "decode_b64: prologue (ShortConv 4 + Swish + L2Norm, conv "
+                                     "state), step, RMSNorm x sigmoid gate; bf16 y",
+                  "prefill_prologue_us": pro_ms * 1e3, "prefill_epilogue_us": epi_ms * 1e3,
+                  "prefill_workload": "k3_prefill_8k, standalone kernels (bf16 x, q/k/v, y; "
+                                      "fp32 o)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
