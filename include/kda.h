@@ -234,8 +234,9 @@ kda_status kda_decode_step_gated(const void* q, const void* k, const void* v,
 /*
  * kda_decode_verify, kda_decode_commit -- speculative decoding with replay.
  * The state is updated in place, so tokens a verifier rejects cannot be taken
- * back once stepped; following "Kimi K3 的 KDA" (section 9, the inference
- * kernel; section 11.1, the decode / spec-decode regime), no state copy is
+ * back once stepped; following "Kimi K3模型架构详解" (section 9.2, the inference
+ * kernel; section 10.1, rollback by replay; section 11.1, the decode /
+ * spec-decode regime), no state copy is
  * kept per draft position: the caller keeps the draft tokens' inputs, verify
  * computes their outputs without touching the state, and commit replays the
  * accepted ones into it.
@@ -322,7 +323,7 @@ kda_status kda_epilogue(const void* o, kda_dtype o_dtype, const void* g, kda_dty
 
 /*
  * kda_decode_layer -- the whole recurrent layer step in one kernel, as K3's
- * inference kernel fuses it ("Kimi K3 的 KDA" section 9: short conv, input
+ * inference kernel fuses it ("Kimi K3模型架构详解" section 9.2: short conv, input
  * norm, gate, recurrence and output norm): the prologue from the projections'
  * outputs and the conv state, the decode call of `mode`, the epilogue.
  *   KDA_DECODE_STEP    N must be 1: y written; state and conv_state advanced

@@ -19,7 +19,7 @@
 // the key axis are finished inside the wave with DPP row rotations and the
 // permlane swaps (no LDS, no barrier).
 //
-// Speculative decoding ("Kimi K3 的 KDA" sections 9 and 11.1): the state is
+// Speculative decoding ("Kimi K3模型架构详解" sections 9.2, 10.1 and 11.1): the state is
 // updated in place, so a rejected draft token cannot simply be dropped.  Verify
 // runs N draft tokens per session from the state kept in registers and writes
 // their outputs, but not the state; commit replays the first n_accept[b] of
@@ -222,7 +222,7 @@ __device__ __forceinline__ void layer_row(const float* xr, const float* taps, fl
 // All of them stage the tokens' inputs in LDS (one coalesced pass, alpha and the
 // alpha-scaled vectors formed once) and step the state held in registers with
 // token_step, so the three calls agree bitwise.
-// LAYER: the whole recurrent layer step of "Kimi K3 的 KDA" section 9 in one
+// LAYER: the whole recurrent layer step of "Kimi K3模型架构详解" section 9.2 in one
 // kernel -- q, k, v come from the projections' outputs through the prologue
 // (the conv state read, and advanced by step and commit), and the outputs leave
 // through the epilogue (RMSNorm and gate) as y; with the standalone prologue and

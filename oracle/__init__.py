@@ -17,6 +17,8 @@ Two independent formulations live here:
   "Kimi Delta Attention 完全拆解", section "KDA 为什么比一般 DPLR 更容易做成快 Kernel")
   and applies S <- M S + beta k v^T.  It is for tiny inputs only.
 
+Segment summaries: :func:`affine_summary` and :func:`compose_summaries`.
+
 Around the recurrence: :func:`gate_alpha` (the decay from each gate
 parametrization) and the layer's prologue and epilogue -- :func:`short_conv`,
 :func:`silu`, :func:`l2norm`, :func:`prologue` (q, k, v from the projections'
@@ -27,7 +29,9 @@ Parity status: pinned (see the CPU tests) by linear-attention brute force, the
 exact-overwrite property, the beta = 0 closed form, the erase-free two-token
 expansion, the gradient-step derivation, the state-size arithmetic, the
 chunk form and two-segment composition; the gates by closed forms and the
-scalar-gate commutation; the prologue / epilogue by numpy's convolution, shift
+scalar-gate commutation; the segment summaries by the recurrence itself
+(applied to a state) and their composition; the prologue / epilogue by
+numpy's convolution, shift
 kernels, the state hand-over and closed forms.  The general random case has no
 printed values on the pages.
 """
@@ -158,6 +162,34 @@ def recurrent_matrix(q, k, v, alpha, beta, initial_state=None):
                 o[b, t, h] = S.T @ q[b, t, h]
             sf[b, h] = S
     return o, sf
+
+
+def affine_summary(k, v, alpha, beta):
+    """The affine map of one segment of tokens on the state, S_end = M S_start + b
+    (the segment summary that lets segments of one sequence be processed in
+    parallel and composed afterwards: "Kimi K3模型架构详解" section 3.6, the summaries
+    (M, b) and their associative composition).
+
+    ``k, alpha`` [T, Dk], ``v`` [T, Dv], ``beta`` [T] for one (sequence, head).
+    Built from each token's explicit transition A_t = Diag(alpha_t) -
+    (beta_t k_t)(k_t * alpha_t)^T: M = A_T ... A_1 and b_t = A_t b_{t-1} +
+    beta_t k_t v_t^T.  Returns (M [Dk, Dk], b [Dk, Dv]) in fp64."""
+    k, v, alpha, beta = (_f64(x) for x in (k, v, alpha, beta))
+    T, Dk = k.shape
+    M = np.eye(Dk)
+    b = np.zeros((Dk, v.shape[1]))
+    for t in range(T):
+        A = np.diag(alpha[t]) - np.outer(beta[t] * k[t], k[t] * alpha[t])
+        M = A @ M
+        b = A @ b + beta[t] * np.outer(k[t], v[t])
+    return M, b
+
+
+def compose_summaries(first, second):
+    """The summary of a segment followed by another: (M2 M1, M2 b1 + b2)."""
+    M1, b1 = first
+    M2, b2 = second
+    return M2 @ M1, M2 @ b1 + b2
 
 
 GATES = ("alpha", "log", "bounded", "scalar", "none")

@@ -467,3 +467,29 @@ def test_prologue_state_layout_and_handover():
         row.append(p / (1.0 + np.exp(-p)))
     row = np.array(row)
     assert abs(k[0, 0, h, c] - (pre / (1 + np.exp(-pre))) / np.sqrt(np.sum(row ** 2) + 1e-6)) < 1e-13
+
+
+def test_affine_summary_pins():
+    """The recurrence is affine in the entry state, so a segment of tokens acts as
+    S -> M S + b ("Kimi K3模型架构详解" section 3.6): applied to any entry state the
+    summary equals the token loop (a different formulation: the C recurrence),
+    summaries compose associatively, the empty segment is (I, 0), and with
+    beta = 0 the map is the pure decay Diag(prod alpha)."""
+    rng = np.random.default_rng(31)
+    T, Dk, Dv = 20, 6, 5
+    q, k, v, a, b = _rand(rng, 1, T, 1, Dk, Dv)
+    M, bb = oracle.affine_summary(k[0, :, 0], v[0, :, 0], a[0, :, 0], b[0, :, 0])
+    for _ in range(3):
+        s0 = rng.standard_normal((1, 1, Dk, Dv))
+        _, S = oracle.recurrent(q, k, v, a, b, initial_state=s0)
+        assert np.max(np.abs(M @ s0[0, 0] + bb - S[0, 0])) < 1e-12
+    cut = 7
+    first = oracle.affine_summary(k[0, :cut, 0], v[0, :cut, 0], a[0, :cut, 0], b[0, :cut, 0])
+    second = oracle.affine_summary(k[0, cut:, 0], v[0, cut:, 0], a[0, cut:, 0], b[0, cut:, 0])
+    Mc, bc = oracle.compose_summaries(first, second)
+    assert np.max(np.abs(Mc - M)) < 1e-12 and np.max(np.abs(bc - bb)) < 1e-12
+    M0, b0 = oracle.affine_summary(k[0, :0, 0], v[0, :0, 0], a[0, :0, 0], b[0, :0, 0])
+    assert np.array_equal(M0, np.eye(Dk)) and np.array_equal(b0, np.zeros((Dk, Dv)))
+    Mz, bz = oracle.affine_summary(k[0, :, 0], v[0, :, 0], a[0, :, 0], np.zeros(T))
+    assert np.allclose(Mz, np.diag(np.prod(a[0, :, 0], axis=0)), rtol=0, atol=1e-15)
+    assert np.all(bz == 0.0)
