@@ -389,6 +389,62 @@ size_t kda_prefill_varlen_workspace_size(int N, int total_tokens, int H, int Dk,
 int kda_prefill_two_pass_preferred(kda_dtype qkv_dtype, int n_seq, int total_tokens, int H, int Dk,
                                    int Dv);
 
+/*
+ * kda_prefill_segmented -- the two-pass prefill with the recurrence of each
+ * window cut along the chunk axis, for calls with few (sequence, head) pairs
+ * (few heads per device), where one workgroup per (sequence, head, 64 values)
+ * walking a window's 64 chunks in order leaves most compute units idle.  A
+ * segment of consecutive chunks acts on its entry state as the affine map
+ * S -> M S + b, and maps compose associatively, (M2, b2) o (M1, b1) =
+ * (M2 M1, M2 b1 + b2) ("Kimi K3模型架构详解", section 3.6, the segment summary
+ * of context parallelism, here between segments of one device instead of
+ * ranks).  Per window: a summary kernel carries [M | b] from [I | 0] through
+ * each segment but the last (all segments at once), a combine kernel chains
+ * the summaries into each segment's entry state (the split-bf16 MFMA product
+ * of the state pass, in fp32), and the state pass runs all segments at once
+ * from their entry states.  Each sequence uses min(n_segments, its chunks in
+ * the window) segments; with one segment it runs exactly the two-pass schedule.
+ *
+ *   cu_seqlens    NULL: n_seq dense sequences of T tokens, tensors as for
+ *                 kda_prefill_chunked with B = n_seq; else DEVICE int32
+ *                 [n_seq + 1] delimiting packed sequences, T = total_tokens,
+ *                 tensors as for kda_prefill_varlen with N = n_seq
+ *   n_segments    in [1, 16] (kda_prefill_segments_preferred suggests one)
+ *   workspace     required: at least kda_prefill_segmented_workspace_size(
+ *                 n_seq, H, Dk, Dv, chunk, n_segments) bytes, 256-byte aligned
+ * bf16 q, k, v only (KDA_ERR_UNSUPPORTED otherwise); other arguments as for
+ * kda_prefill_chunked_gated.  Equal to the token recurrence up to rounding;
+ * deterministic, but with n_segments > 1 not bitwise equal to the other
+ * schedules (the products are associated differently), and a packed
+ * sequence's segment boundaries depend on where its windows fall.
+ */
+kda_status kda_prefill_segmented(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                                 const kda_gate* gate, const float* beta,
+                                 const int32_t* cu_seqlens, int n_seq, int T,
+                                 const float* initial_state, float* final_state, void* o,
+                                 kda_dtype o_dtype, int H, int Dk, int Dv, int chunk,
+                                 int n_segments, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * kda_prefill_segmented_workspace_size -- the two-pass workspace plus the
+ * segments' entry states (n_segments * n_seq * H * Dk * Dv fp32) and summaries
+ * ((n_segments - 1) * n_seq * H * Dk * (Dk + Dv) fp32); 0 for unsupported head
+ * dims, (size_t)-1 for invalid sizes or n_segments outside [1, 16].
+ */
+size_t kda_prefill_segmented_workspace_size(int n_seq, int H, int Dk, int Dv, int chunk,
+                                            int n_segments);
+
+/*
+ * kda_prefill_segments_preferred -- a segment count expected to be fastest on
+ * the current device (1: do not segment): the largest whose summary pass,
+ * (n_segments - 1) * n_seq * H * (Dk + Dv) / 64 workgroups, fits one per
+ * compute unit, at most 8, and at least 4 chunks per segment; 1 where the
+ * two-pass schedule itself is not preferred or the inputs are not bf16.
+ */
+int kda_prefill_segments_preferred(kda_dtype qkv_dtype, int n_seq, int total_tokens, int H, int Dk,
+                                   int Dv);
+
 /* Static string naming a status code. */
 const char* kda_status_string(kda_status s);
 

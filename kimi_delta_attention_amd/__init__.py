@@ -5,9 +5,12 @@ The operator runs in hand-written HIP kernels behind the C ABI of
 Importing it does not load the library; the first call does, and raises if the
 library has not been built.
 """
-from ._lib import (MAX_DRAFT, KdaError, decode_commit, decode_step,  # noqa: F401
-                   decode_layer, decode_verify, epilogue, load, prefill_chunked, prefill_varlen, prologue,
+from ._lib import (MAX_DRAFT, MAX_SEGMENTS, KdaError, decode_commit, decode_step,  # noqa: F401
+                   decode_layer, decode_verify, epilogue, load, prefill_chunked, prefill_segmented,
+                   prefill_varlen, prologue, segmented_workspace_size, segments_preferred,
                    workspace_size)
 
-__all__ = ["prefill_chunked", "prefill_varlen", "decode_step", "decode_verify", "decode_commit",
-           "decode_layer", "prologue", "epilogue", "workspace_size", "load", "KdaError", "MAX_DRAFT"]
+__all__ = ["prefill_chunked", "prefill_varlen", "prefill_segmented", "decode_step",
+           "decode_verify", "decode_commit", "decode_layer", "prologue", "epilogue",
+           "workspace_size", "segmented_workspace_size", "segments_preferred", "load", "KdaError",
+           "MAX_DRAFT", "MAX_SEGMENTS"]

@@ -21,7 +21,8 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
 EXPORTED = ("kda_prefill_chunked", "kda_prefill_varlen", "kda_decode_step",
             "kda_prefill_chunked_gated", "kda_prefill_varlen_gated", "kda_decode_step_gated",
             "kda_decode_verify", "kda_decode_commit", "kda_prologue", "kda_epilogue",
-            "kda_decode_layer",
+            "kda_decode_layer", "kda_prefill_segmented",
+            "kda_prefill_segmented_workspace_size", "kda_prefill_segments_preferred",
             "kda_prefill_workspace_size", "kda_prefill_varlen_workspace_size",
             "kda_prefill_two_pass_preferred", "kda_status_string", "kda_last_error_message")
 
@@ -94,6 +95,13 @@ def load() -> ctypes.CDLL:
     lib.kda_decode_layer.argtypes = [I, P, P, P, I, C, P, G, P, P, ctypes.POINTER(_OutGate), P, I,
                                      P, I, I, I, I, I, P]
     lib.kda_decode_layer.restype = I
+    lib.kda_prefill_segmented.argtypes = [P, P, P, I, G, P, P, I, I, P, P, P, I, I, I, I, I, I,
+                                          P, Z, P]
+    lib.kda_prefill_segmented.restype = I
+    lib.kda_prefill_segmented_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.kda_prefill_segmented_workspace_size.restype = Z
+    lib.kda_prefill_segments_preferred.argtypes = [I, I, I, I, I, I]
+    lib.kda_prefill_segments_preferred.restype = I
     lib.kda_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.kda_prefill_workspace_size.restype = Z
     lib.kda_prefill_varlen_workspace_size.argtypes = [I, I, I, I, I, I]
@@ -285,6 +293,73 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None,
         _ptr(q), _ptr(k), _ptr(v), _dt(q), ctypes.byref(g), _ptr(beta), _ptr(cu_seqlens), N, NT,
         _ptr(initial_state), _ptr(fs), _ptr(o), _dt(o), H, Dk, Dv, 64, _ptr(ws),
         0 if ws is None else ws.numel(), _stream(dev)))
+    return o, fs
+
+
+MAX_SEGMENTS = 16
+
+
+def segmented_workspace_size(n_seq: int, H: int, Dk: int, Dv: int, n_segments: int) -> int:
+    return int(load().kda_prefill_segmented_workspace_size(n_seq, H, Dk, Dv, 64, n_segments))
+
+
+def segments_preferred(dtype, n_seq: int, tokens: int, H: int, Dk: int, Dv: int) -> int:
+    return int(load().kda_prefill_segments_preferred(_DT[dtype], n_seq, tokens, H, Dk, Dv))
+
+
+def prefill_segmented(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
+                      n_segments: int | None = None, out_dtype=torch.float32,
+                      final_state: bool | torch.Tensor = True, o: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, gate: str = "alpha",
+                      a_log: torch.Tensor | None = None, g_min: float = -5.0):
+    """Two-pass prefill with each window's chunks of a sequence split into up to
+    n_segments segments that run side by side (None: the library's choice).
+    Dense (cu_seqlens None): tensors as for prefill_chunked; packed: as for
+    prefill_varlen.  bf16 q, k, v.  Returns (o, final_state)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(beta, "beta", torch.float32, dev)
+    if k.shape != q.shape or v.shape != (B, T, H, Dv) or beta.shape != (B, T, H):
+        raise ValueError("inconsistent shapes")
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("packed inputs have B == 1")
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        n_seq, tokens = cu_seqlens.numel() - 1, T
+    else:
+        n_seq, tokens = B, B * T
+    g = _gate(gate, alpha, a_log, g_min, (B, T), H, Dk, dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev)
+        if initial_state.shape != (n_seq, H, Dk, Dv):
+            raise ValueError("initial_state must be [n_seq, H, Dk, Dv]")
+    if o is None:
+        o = torch.empty(B, T, H, Dv, dtype=out_dtype, device=dev)
+    else:
+        _need(o, "o", None, dev)
+    if isinstance(final_state, torch.Tensor):
+        fs = final_state
+        _need(fs, "final_state", torch.float32, dev)
+    elif final_state:
+        fs = torch.empty(n_seq, H, Dk, Dv, dtype=torch.float32, device=dev)
+    else:
+        fs = None
+    if n_segments is None:
+        n_segments = segments_preferred(q.dtype, n_seq, tokens, H, Dk, Dv)
+    need = segmented_workspace_size(n_seq, H, Dk, Dv, n_segments)
+    if need == (1 << 64) - 1:
+        raise ValueError(f"n_segments must lie in [1, {MAX_SEGMENTS}]")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, dev)
+    _check(load().kda_prefill_segmented(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), ctypes.byref(g), _ptr(beta), _ptr(cu_seqlens), n_seq,
+        T if cu_seqlens is None else tokens, _ptr(initial_state), _ptr(fs), _ptr(o), _dt(o), H, Dk,
+        Dv, 64, n_segments, _ptr(workspace), workspace.numel(), _stream(dev)))
     return o, fs
 
 

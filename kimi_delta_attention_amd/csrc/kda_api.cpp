@@ -113,12 +113,27 @@ int kda_prefill_two_pass_preferred(kda_dtype qkv_dtype, int n_seq, int total_tok
   return kda::prefill_two_pass_preferred(n_seq, total_tokens, H, Dk, Dv) ? 1 : 0;
 }
 
+size_t kda_prefill_segmented_workspace_size(int n_seq, int H, int Dk, int Dv, int chunk,
+                                            int n_segments) {
+  if (n_seq < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || chunk != 64 || n_segments < 1 ||
+      n_segments > kda::kMaxSegments)
+    return (size_t)-1;
+  return kda::prefill_segmented_bytes(n_seq, H, Dk, Dv, n_segments);
+}
+
+int kda_prefill_segments_preferred(kda_dtype qkv_dtype, int n_seq, int total_tokens, int H, int Dk,
+                                   int Dv) {
+  if (qkv_dtype != KDA_BF16) return 1;
+  return kda::prefill_segments_preferred(n_seq, total_tokens, H, Dk, Dv);
+}
+
 static kda_status prefill_common(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
                                  const kda_gate* gate, const float* beta,
                                  const int32_t* cu_seqlens, int n_seq, int T,
                                  const float* initial_state, float* final_state, void* o,
                                  kda_dtype o_dtype, int H, int Dk, int Dv, int chunk,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 int nseg = 1) {
   if (n_seq < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative batch or length");
   if (n_seq == 0) return ok();
   kda::Gate g = {KDA_GATE_NONE, nullptr, nullptr, 0.f};
@@ -150,6 +165,17 @@ static kda_status prefill_common(const void* q, const void* k, const void* v, kd
   if (T == 0 && !cu_seqlens && !final_state) return ok();
   if (workspace && ((uintptr_t)workspace & 255u))
     return fail(KDA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (nseg > 1) {
+    if (qkv_dtype != KDA_BF16)
+      return fail(KDA_ERR_UNSUPPORTED, "the segmented schedule needs bf16 q, k, v");
+    const size_t need = kda::prefill_segmented_bytes(n_seq, H, Dk, Dv, nseg);
+    if (!workspace || workspace_bytes < need)
+      return fail(KDA_ERR_INVALID_ARGUMENT,
+                  "the segmented schedule needs a workspace of %zu bytes (got %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if ((long long)nseg * n_seq * H * ((Dk + Dv) / 64) > 0x7fffffffLL)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "too many (segment, sequence, head) work items");
+  }
   kda::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.gate = g; a.beta = beta;
   a.initial_state = initial_state; a.final_state = final_state; a.o = o;
@@ -157,7 +183,37 @@ static kda_status prefill_common(const void* q, const void* k, const void* v, kd
   a.cu_seqlens = cu_seqlens; a.n_seq = n_seq; a.T = T; a.H = H; a.Dk = Dk; a.Dv = Dv;
   a.workspace = workspace; a.workspace_bytes = workspace ? workspace_bytes : 0;
   a.stream = stream;
+  a.nseg = nseg;
   return hip_status(kda::launch_prefill(a));
+}
+
+kda_status kda_prefill_segmented(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                                 const kda_gate* gate, const float* beta,
+                                 const int32_t* cu_seqlens, int n_seq, int T,
+                                 const float* initial_state, float* final_state, void* o,
+                                 kda_dtype o_dtype, int H, int Dk, int Dv, int chunk,
+                                 int n_segments, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (n_seq < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "n_seq and T must be >= 0");
+  if (n_segments < 1 || n_segments > kda::kMaxSegments)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "n_segments must lie in [1, %d] (got %d)",
+                kda::kMaxSegments, n_segments);
+  if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
+  if (n_seq > 0 && qkv_dtype != KDA_BF16)
+    return fail(KDA_ERR_UNSUPPORTED, "the segmented schedule needs bf16 q, k, v");
+  if (n_seq > 0) {
+    const size_t need = kda::prefill_segmented_bytes(n_seq, H, Dk, Dv, n_segments);
+    if (need == 0 && kda::prefill_supported(true, Dk, Dv) && H > 0)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "sizes too large for the segmented schedule");
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(KDA_ERR_INVALID_ARGUMENT,
+                  "the segmented schedule needs a workspace of %zu bytes (got %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+  }
+  return prefill_common(q, k, v, qkv_dtype, gate, beta, cu_seqlens, n_seq, T, initial_state,
+                        final_state, o, o_dtype, H, Dk, Dv, chunk, workspace, workspace_bytes,
+                        stream, n_segments);
 }
 
 kda_status kda_prefill_chunked_gated(const void* q, const void* k, const void* v,

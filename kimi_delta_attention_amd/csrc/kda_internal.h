@@ -45,6 +45,10 @@ struct PrefillArgs {
   void* workspace;
   size_t workspace_bytes;
   void* stream;
+  // Segments per window and sequence of the two-pass state recurrence (1: one
+  // workgroup walks all of a window's chunks); above 1 the workspace must hold
+  // prefill_segmented_bytes(...).
+  int nseg = 1;
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
@@ -88,14 +92,26 @@ bool prefill_supported(bool qkv_bf16, int Dk, int Dv);
 // beat the fused kernel on the current device (`tokens`: packed total).
 size_t prefill_two_pass_bytes(int n_seq, int H, int Dk, int Dv);
 bool prefill_two_pass_preferred(int n_seq, long long tokens, int H, int Dk, int Dv);
+constexpr int kMaxSegments = 16;  // segments per window and sequence
+size_t prefill_segmented_bytes(int n_seq, int H, int Dk, int Dv, int nseg);
+int prefill_segments_preferred(int n_seq, long long tokens, int H, int Dk, int Dv);
 // (kda_prefill_state.hip) operand-image bytes per (chunk, head); the state
 // pass over one window of packed tokens [tok_lo, tok_hi) (state read from the
 // initial state for a sequence's first chunk, else from `carry`, and written
 // to `carry`); the chunk table of packed sequences (clamped to `cap` chunks).
 size_t prefill_image_bytes(int Dk, int Dv);
+// Segments of a window processed side by side (nseg > 1): the summaries
+// [nseg - 1][n_seq][H][Dk][Dk + Dv] and the entry states [nseg][n_seq][H][Dk][Dv]
+// (entry 0 a copy of the state entering the window, so that no workgroup reads
+// the carried state that another one writes) live in the caller's workspace.
+struct SegmentArgs {
+  int nseg = 1;
+  float* seg_in = nullptr;
+  float* summ = nullptr;
+};
 hipError_t launch_prefill_state(const PrefillArgs& a, const unsigned char* img,
                                 const int32_t* chunk_off, float* carry, long long tok_lo,
-                                long long tok_hi, int cap);
+                                long long tok_hi, int cap, const SegmentArgs& sg = SegmentArgs{});
 hipError_t launch_chunk_table(const int32_t* cu_seqlens, int n_seq, int cap, int32_t* chunk_off,
                               void* stream);
 // (kda_prefill_prep.hip) the first pass over one window: operand images of the

@@ -766,6 +766,21 @@ size_t prefill_two_pass_bytes(int n_seq, int H, int Dk, int Dv) {
          (size_t)items * prefill_image_bytes(Dk, Dv);
 }
 
+// The segmented schedule adds, after the two-pass workspace, the segments'
+// entry states [nseg][n_seq][H][Dk][Dv] and the summaries [M | b]
+// [nseg - 1][n_seq][H][Dk][Dk + Dv], fp32.
+size_t seg_in_bytes(int n_seq, int H, int Dk, int Dv, int nseg) {
+  return ((size_t)nseg * n_seq * H * Dk * Dv * 4 + 255) / 256 * 256;
+}
+
+size_t prefill_segmented_bytes(int n_seq, int H, int Dk, int Dv, int nseg) {
+  const size_t base = prefill_two_pass_bytes(n_seq, H, Dk, Dv);
+  if (base == 0 || nseg < 1 || nseg > kMaxSegments) return 0;
+  if (nseg == 1) return base;
+  return base + seg_in_bytes(n_seq, H, Dk, Dv, nseg) +
+         (size_t)(nseg - 1) * n_seq * H * Dk * (Dk + Dv) * 4;
+}
+
 size_t device_mem() {
   static size_t mem[64] = {0};
   int dev = 0;
@@ -794,12 +809,39 @@ bool prefill_two_pass_preferred(int n_seq, long long tokens, int H, int Dk, int 
   return need > 0 && need <= cap;
 }
 
+int prefill_segments_preferred(int n_seq, long long tokens, int H, int Dk, int Dv) {
+  if (!prefill_two_pass_preferred(n_seq, tokens, H, Dk, Dv)) return 1;
+  // The state pass runs n_seq * H * Dv / 64 workgroups per window, each walking
+  // up to 64 chunks in order; with few of them most compute units idle.
+  // Segments multiply the workgroups: the summary pass runs (nseg - 1) * grid *
+  // (Dk + Dv) / Dv of them (one per compute unit fits), the state pass nseg *
+  // grid.  The largest nseg whose summary pass fits the device in one round was
+  // the fastest on MI355X at 12, 24, 48 and 96 heads (within 2%), and only
+  // while a sequence has at least 4 chunks per segment in a window.
+  const long long grid = (long long)n_seq * H * (Dv / BV);
+  long long ns = 1 + (long long)device_cus() * Dv / (grid * (Dk + Dv));
+  const long long per_seq = tokens / n_seq / CH;  // chunks per sequence
+  const long long win = per_seq < WIN_CHUNKS ? per_seq : WIN_CHUNKS;
+  if (ns > win / 4) ns = win / 4;
+  if (ns > 8) ns = 8;
+  return ns < 2 ? 1 : (int)ns;
+}
+
 hipError_t launch_prefill(const PrefillArgs& a) {
   if (!a.qkv_bf16) return launch_prefill_f32(a);
   const bool varlen = a.cu_seqlens != nullptr;
   // packed tokens in all (dense: n_seq sequences of T tokens back to back)
   const long long total = varlen ? (long long)a.T : (long long)a.n_seq * a.T;
   const size_t need = prefill_two_pass_bytes(a.n_seq, a.H, a.Dk, a.Dv);
+  SegmentArgs sg;
+  if (a.nseg > 1) {  // the caller checked the workspace size
+    if (a.workspace_bytes < prefill_segmented_bytes(a.n_seq, a.H, a.Dk, a.Dv, a.nseg))
+      return hipErrorInvalidValue;
+    sg.nseg = a.nseg;
+    sg.seg_in = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + need);
+    sg.summ = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + need +
+                                       seg_in_bytes(a.n_seq, a.H, a.Dk, a.Dv, a.nseg));
+  }
   if (need == 0 || !a.workspace || a.workspace_bytes < need || total == 0) {
     if (a.Dk == 128) return a.o_bf16 ? launch_fused<128, bf16>(a) : launch_fused<128, float>(a);
     return a.o_bf16 ? launch_fused<64, bf16>(a) : launch_fused<64, float>(a);
@@ -824,7 +866,7 @@ hipError_t launch_prefill(const PrefillArgs& a) {
   for (long long t0 = 0; t0 < total; t0 += win) {
     hipError_t e = launch_prefill_prep(a, img, chunk_off, t0, t0 + win, cap, grid);
     if (e != hipSuccess) return e;
-    e = launch_prefill_state(a, img, chunk_off, carry, t0, t0 + win, cap);
+    e = launch_prefill_state(a, img, chunk_off, carry, t0, t0 + win, cap, sg);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

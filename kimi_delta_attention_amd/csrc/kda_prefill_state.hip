@@ -112,12 +112,65 @@ __device__ __forceinline__ void store4<bf16>(__amdgpu_buffer_rsrc_t rs, int off,
 // derives for the loop then hold on every iteration).
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int DK, int DV, int BV, typename TOut>
+// The chunks of one sequence that start in the window [tok_lo, tok_hi): chunk
+// c of the sequence (c_lo <= c < c_hi) has item slot ci0 + c - ci_lo (below cap).
+struct SeqWindow {
+  long long start, len;
+  int ci0, ci_lo, nch_seq, c_lo, c_hi;
+};
+__device__ __forceinline__ SeqWindow seq_window(const int32_t* cu_seqlens, const int32_t* chunk_off,
+                                                int n_seq, int T, int seq, long long tok_lo,
+                                                long long tok_hi, int cap) {
+  SeqWindow sw;
+  if (cu_seqlens) {
+    sw.start = cu_seqlens[seq];
+    sw.len = (long long)cu_seqlens[seq + 1] - sw.start;
+    sw.ci0 = chunk_off[seq];
+    sw.nch_seq = chunk_off[seq + 1] - sw.ci0;  // ceil(len / 64) for monotone offsets
+  } else {
+    sw.start = (long long)seq * T;
+    sw.len = T;
+    sw.nch_seq = (T + CH - 1) / CH;
+    sw.ci0 = seq * sw.nch_seq;
+  }
+  if (sw.len > (long long)sw.nch_seq * CH) sw.len = (long long)sw.nch_seq * CH;
+  sw.ci_lo = chunks_before(tok_lo, cu_seqlens, chunk_off, n_seq, T);
+  auto first_from = [&](long long tok) {
+    long long c = (tok - sw.start + CH - 1) / CH;
+    if (c < 0) c = 0;
+    return (int)(c < sw.nch_seq ? c : sw.nch_seq);
+  };
+  sw.c_lo = first_from(tok_lo);
+  sw.c_hi = first_from(tok_hi);
+  if (sw.c_lo < sw.ci_lo - sw.ci0) sw.c_lo = sw.ci_lo - sw.ci0;            // reached only for
+  if (sw.c_hi > cap + sw.ci_lo - sw.ci0) sw.c_hi = cap + sw.ci_lo - sw.ci0;  // non-monotone cu_seqlens
+  return sw;
+}
+
+// Segments of a sequence's chunks in a window: nseg, but no more than its
+// chunk count (so that no segment is empty), and 1 when it has none.
+__device__ __forceinline__ int seg_count(int nseg, int c_lo, int c_hi) {
+  const int n = c_hi - c_lo;
+  return n <= 1 ? 1 : (nseg < n ? nseg : n);
+}
+
+// SUMMARY: instead of the state, the workgroup carries a 64-column slice of
+// [M | b] (Dk + Dv columns, from [I | 0]) through its segment of the window's
+// chunks -- the segment's affine map S -> M S + b ("Kimi K3模型架构详解"
+// section 3.6): the M columns see U = 0, no output is formed, and the result
+// goes to `summ`.  With nseg > 1 the window's chunks of a sequence are cut
+// into ns = seg_count(nseg, ..) segments of consecutive chunks; when ns > 1,
+// the normal workgroup of segment s enters from seg_in[s] (the combine
+// kernel's entry states) and only the last segment writes the carried state.
+// With ns = 1, segment 0 runs exactly as the unsegmented pass.
+template <int DK, int DV, int BV, typename TOut, bool SUMMARY>
 __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     const unsigned char* __restrict__ img, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ cu_seqlens, const float* s_init, float* carry,
-    TOut* __restrict__ o, int n_seq, int T, int H, long long tok_lo, long long tok_hi, int cap) {
+    TOut* __restrict__ o, int n_seq, int T, int H, long long tok_lo, long long tok_hi, int cap,
+    int nseg, const float* __restrict__ seg_in, float* __restrict__ summ) {
   static_assert(BV == 32 || BV == 64, "value slice of 32 or 64 columns");
+  constexpr int SWC = SUMMARY ? DK + DV : DV;  // columns the workgroups carry
   using L = StatePlan<DK, BV>;
   using IM = Images<DK, DV>;
   constexpr int NKB = DK / 32;
@@ -138,42 +191,31 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
   const int w = w8 & 3;      // token tile
   const int lane = tid & 63;
 
-  constexpr int nsl = DV / BV;
-  const int total = n_seq * H * nsl;
+  constexpr int nsl = SWC / BV;
+  const int nsg = SUMMARY ? nseg - 1 : nseg;  // segments with a workgroup each
+  const int total = nsg * n_seq * H * nsl;
   int wid = blockIdx.x;
   if ((total & 7) == 0) wid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
   const int sl = wid % nsl;
   const int h = (wid / nsl) % H;
-  const int seq = wid / (nsl * H);
-  long long start, len;
-  int ci0, nch_seq;  // global index of the sequence's first chunk, its chunk count
-  if (cu_seqlens) {
-    start = cu_seqlens[seq];
-    len = (long long)cu_seqlens[seq + 1] - start;
-    ci0 = chunk_off[seq];
-    nch_seq = chunk_off[seq + 1] - ci0;  // ceil(len / 64) for monotone offsets
-  } else {
-    start = (long long)seq * T;
-    len = T;
-    nch_seq = (T + CH - 1) / CH;
-    ci0 = seq * nch_seq;
-  }
-  if (len > (long long)nch_seq * CH) len = (long long)nch_seq * CH;
-  // this window's chunks of the sequence, [c_lo, c_hi); item slot of chunk c
-  // is ci0 + c - ci_lo, below cap
-  const int ci_lo = chunks_before(tok_lo, cu_seqlens, chunk_off, n_seq, T);
-  auto first_from = [&](long long tok) {
-    long long c = (tok - start + CH - 1) / CH;
-    if (c < 0) c = 0;
-    return (int)(c < nch_seq ? c : nch_seq);
-  };
-  int c_lo = first_from(tok_lo), c_hi = first_from(tok_hi);
-  if (c_lo < ci_lo - ci0) c_lo = ci_lo - ci0;          // reached only for
-  if (c_hi > cap + ci_lo - ci0) c_hi = cap + ci_lo - ci0;  // non-monotone cu_seqlens
+  const int seq = (wid / (nsl * H)) % n_seq;
+  const int seg = wid / (nsl * H * n_seq);
+  const SeqWindow sw = seq_window(cu_seqlens, chunk_off, n_seq, T, seq, tok_lo, tok_hi, cap);
+  const long long start = sw.start, len = sw.len;
+  const int ci0 = sw.ci0, ci_lo = sw.ci_lo, nch_seq = sw.nch_seq;
+  const bool window_first = sw.c_lo == 0;  // the window starts the sequence
+  const int ns = seg_count(nseg, sw.c_lo, sw.c_hi);
+  // a summary only for segments before the last
+  if (seg >= (SUMMARY ? ns - 1 : ns)) return;
+  // this workgroup's segment of the window's chunks
+  const int n_ch = sw.c_hi > sw.c_lo ? sw.c_hi - sw.c_lo : 0;
+  const int c_lo = sw.c_lo + n_ch * seg / ns, c_hi = sw.c_lo + n_ch * (seg + 1) / ns;
   // an empty sequence hands its initial state through in the first window
   if (!(c_lo < c_hi || (nch_seq == 0 && tok_lo == 0))) return;
   const int vcol0 = sl * BV;
-  const int vt0 = vcol0 / 16;  // first U tile of the slice
+  // the U tiles of the slice: b's columns map to v's; M's columns see U = 0
+  const bool u_zero = SUMMARY && vcol0 < DK;
+  const int vt0 = (SUMMARY ? (u_zero ? 0 : vcol0 - DK) : vcol0) / 16;
   // state tiles of this wave
   const int srt = DK == 128 ? 2 * w + role : w;  // 16-row tile
   const int sv0 = DK == 128 ? 0 : KVT * role;    // first value tile (within the slice)
@@ -181,14 +223,19 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
   floatx4 Sacc[KVT];
   {
     const int tr = lane & 15, g = lane >> 4;
-    const float* src = c_lo == 0 ? s_init : carry;
+    const float* src = ns > 1 ? seg_in + (size_t)seg * n_seq * H * DK * DV
+                              : window_first ? s_init : carry;
     const float* si = src ? src + ((size_t)seq * H + h) * DK * DV : nullptr;
 #pragma unroll
     for (int j = 0; j < KVT; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * srt + 4 * g + i;
-        Sacc[j][i] = si ? si[(size_t)row * DV + vcol0 + 16 * (sv0 + j) + tr] : 0.f;
+        const int col = vcol0 + 16 * (sv0 + j) + tr;
+        if constexpr (SUMMARY)
+          Sacc[j][i] = col == row ? 1.f : 0.f;  // [I | 0]
+        else
+          Sacc[j][i] = si ? si[(size_t)row * DV + col] : 0.f;
       }
   }
 
@@ -232,7 +279,9 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       const unsigned char* b = item_base(c);
       op.gc = *reinterpret_cast<const floatx4*>(b + IM::g_off + 4 * (16 * srt + 4 * (lane >> 4)));
 #pragma unroll
-      for (int j = 0; j < NVT; ++j) op.u[j] = *frame_ptr<floatx4>(b, IM::u_frame(w, vt0 + j), lane);
+      for (int j = 0; j < NVT; ++j)
+        op.u[j] = u_zero ? floatx4{0.f, 0.f, 0.f, 0.f}
+                         : *frame_ptr<floatx4>(b, IM::u_frame(w, vt0 + j), lane);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         op.kh[kb] = *frame_ptr<bf16x8>(b, IM::k_frame(srt, kb, 0), lane);
@@ -313,6 +362,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     // (Gamma*Q) and Mqk frames (fetched during the (Gamma*Q) S of the chunk
     // before) and the state-update operands (fetched during its update)
     auto fetch_w = [&](int c, Ops& op) {
+      if constexpr (SUMMARY) return;  // no output: only the state update
       const unsigned char* b = item_base(c);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) op.qf[kb] = *frame_ptr<bf16x8>(b, IM::q_frame(w, kb), lane);
@@ -346,25 +396,27 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       __syncthreads();
       fetch_w(next_of(c), nx);
       // ---- (Gamma*Q) S over both channel halves (separate chains, low half first)
-      floatx4 a0[NVT], a1[NVT];
-#pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) {
-        a0[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        a1[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      floatx4 ov[NVT];
+      if constexpr (!SUMMARY) {
+        floatx4 a0[NVT], a1[NVT];
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt) {
-          const bf16x8 bh = frag_ld(ST, ldS, 16 * vt + tr, 32 * kb, g);
-          const bf16x8 bl = frag_ld(ST + loS, ldS, 16 * vt + tr, 32 * kb, g);
-          floatx4& acc = kb < NKH ? a0[vt] : a1[vt];
-          acc = mfma_bf16(op.qf[kb], bh, acc);
-          acc = mfma_bf16(op.qf[kb], bl, acc);
+          a0[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
+          a1[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
-      floatx4 ov[NVT];
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) ov[vt] = a0[vt] + a1[vt];
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int vt = 0; vt < NVT; ++vt) {
+            const bf16x8 bh = frag_ld(ST, ldS, 16 * vt + tr, 32 * kb, g);
+            const bf16x8 bl = frag_ld(ST + loS, ldS, 16 * vt + tr, 32 * kb, g);
+            floatx4& acc = kb < NKH ? a0[vt] : a1[vt];
+            acc = mfma_bf16(op.qf[kb], bh, acc);
+            acc = mfma_bf16(op.qf[kb], bl, acc);
+          }
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) ov[vt] = a0[vt] + a1[vt];
+      }
       __syncthreads();
       fetch_r(next_of(c), nx);
       // ---- O += Mqk P and the state update of this wave's tiles, from the
@@ -384,7 +436,8 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
         for (int vt = 0; vt < NVT; ++vt) {
           const bf16x8 bh = frag_ld(PT, ldP, 16 * vt + tr, 32 * kb, g);
           const bf16x8 bl = frag_ld(PT + loP, ldP, 16 * vt + tr, 32 * kb, g);
-          ov[vt] = mma_ab(kb ? mh1 : op.mh[0], kb ? ml1 : op.ml[0], bh, bl, ov[vt]);
+          if constexpr (!SUMMARY)
+            ov[vt] = mma_ab(kb ? mh1 : op.mh[0], kb ? ml1 : op.ml[0], bh, bl, ov[vt]);
           if (vt >= OSV && vt < OSV + KVT)
             Sacc[vt - OSV] = mma_ab(op.kh[kb], op.kl[kb], bh, bl, Sacc[vt - OSV]);
         }
@@ -393,7 +446,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       // as one 16-byte word; read back, each store instruction covers whole
       // rows of the slice (64 / (BV / 4) of them).  The descriptor spans the
       // chunk's nv rows.
-      {
+      if constexpr (!SUMMARY) {
         float* os = OS + w * 16 * ldO;
         const int b = tr & 3;
 #pragma unroll
@@ -428,16 +481,95 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     }
   }
 
-  {
+  if (SUMMARY || seg == ns - 1) {
     const int tr = lane & 15, g = lane >> 4;
-    float* sf = carry + ((size_t)seq * H + h) * DK * DV;
+    float* sf = SUMMARY ? summ + (((size_t)seg * n_seq + seq) * H + h) * DK * SWC
+                        : carry + ((size_t)seq * H + h) * DK * DV;
 #pragma unroll
     for (int j = 0; j < KVT; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * srt + 4 * g + i;
-        sf[(size_t)row * DV + vcol0 + 16 * (sv0 + j) + tr] = Sacc[j][i];
+        sf[(size_t)row * SWC + vcol0 + 16 * (sv0 + j) + tr] = Sacc[j][i];
       }
+  }
+}
+
+// Entry states of the segments of one window, for a sequence with ns > 1
+// segments: E_0 is the state entering the window (the initial state in the
+// sequence's first window, else the carried one) and E_{s+1} = M_s E_s + b_s,
+// the composition of the segment maps ("Kimi K3模型架构详解" section 3.6).
+// One workgroup of 8 waves per (sequence, head, 64-column slice of the state).
+// The slice of E_s sits in LDS as the split (high, low bf16) B operand,
+// [column][row]; rows of M_s arrive from memory as split A fragments; each
+// product is the three-term split-bf16 MFMA product of the state pass, added
+// to b_s in fp32.  Wave w owns row tile w % (Dk / 16) and Dk / 32 of the four
+// column tiles.
+template <int DK, int DV>
+__global__ __launch_bounds__(512) void segment_combine_kernel(
+    const float* __restrict__ summ, float* __restrict__ seg_in,
+    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ chunk_off,
+    const float* s_init, const float* carry, int n_seq, int T, int H, long long tok_lo,
+    long long tok_hi, int cap, int nseg) {
+  constexpr int SC = 64, SWC = DK + DV, ld = DK + 8;
+  constexpr int NRT = DK / 16, CTW = NRT / 2;  // row tiles; column tiles per wave
+  __shared__ __align__(16) bf16 EB[2 * SC * ld];
+  constexpr int nsl = DV / SC;
+  const int sl = blockIdx.x % nsl, h = (blockIdx.x / nsl) % H, seq = blockIdx.x / (nsl * H);
+  const SeqWindow sw = seq_window(cu_seqlens, chunk_off, n_seq, T, seq, tok_lo, tok_hi, cap);
+  const int ns = seg_count(nseg, sw.c_lo, sw.c_hi);
+  if (ns <= 1) return;  // the state pass enters from the state itself
+  const float* src = sw.c_lo == 0 ? s_init : carry;
+  const float* si = src ? src + ((size_t)seq * H + h) * DK * DV : nullptr;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, tr = lane & 15, g = lane >> 4;
+  const int rt = w % NRT, ct0 = (w / NRT) * CTW;
+  const int col0 = sl * SC;
+  const size_t head = ((size_t)seq * H + h) * DK * DV;
+  const size_t seg_stride = (size_t)n_seq * H * DK * DV;
+  floatx4 acc[CTW];
+#pragma unroll
+  for (int j = 0; j < CTW; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t e = (size_t)(16 * rt + 4 * g + i) * DV + col0 + 16 * (ct0 + j) + tr;
+      acc[j][i] = si ? si[e] : 0.f;
+      seg_in[head + e] = acc[j][i];
+    }
+  for (int s = 0; s + 1 < ns; ++s) {
+#pragma unroll
+    for (int j = 0; j < CTW; ++j) {
+      float x4[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+      st_split4(EB + (16 * (ct0 + j) + tr) * ld + 16 * rt + 4 * g, SC * ld, x4);
+    }
+    __syncthreads();
+    const float* ms = summ + (((size_t)s * n_seq + seq) * H + h) * DK * SWC;
+#pragma unroll
+    for (int j = 0; j < CTW; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[j][i] = ms[(size_t)(16 * rt + 4 * g + i) * SWC + DK + col0 + 16 * (ct0 + j) + tr];
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      const float* mr = ms + (size_t)(16 * rt + tr) * SWC + 32 * kb + 8 * g;
+      const floatx4 m0 = *reinterpret_cast<const floatx4*>(mr);
+      const floatx4 m1 = *reinterpret_cast<const floatx4*>(mr + 4);
+      const float x8[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
+      bf16x8 ah, al;
+      split8(x8, ah, al);
+#pragma unroll
+      for (int j = 0; j < CTW; ++j) {
+        const bf16x8 bh = frag_ld(EB, ld, 16 * (ct0 + j) + tr, 32 * kb, g);
+        const bf16x8 bl = frag_ld(EB + SC * ld, ld, 16 * (ct0 + j) + tr, 32 * kb, g);
+        acc[j] = mma_ab(ah, al, bh, bl, acc[j]);
+      }
+    }
+    __syncthreads();  // E_s read by every wave before it is replaced
+    float* out = seg_in + (size_t)(s + 1) * seg_stride + head;
+#pragma unroll
+    for (int j = 0; j < CTW; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        out[(size_t)(16 * rt + 4 * g + i) * DV + col0 + 16 * (ct0 + j) + tr] = acc[j][i];
   }
 }
 
@@ -482,12 +614,13 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restr
 // is bound by frame fetches per compute unit, not by idle compute units.
 constexpr int BV_STATE = 64;
 
-template <int DK, int DV, typename TOut>
+template <int DK, int DV, typename TOut, bool SUMMARY>
 hipError_t launch_state_t(const PrefillArgs& a, const unsigned char* img, const int32_t* chunk_off,
-                          float* carry, long long tok_lo, long long tok_hi, int cap) {
+                          float* carry, long long tok_lo, long long tok_hi, int cap,
+                          const SegmentArgs& sg) {
   constexpr int BV = BV_STATE;
   using L = StatePlan<DK, BV>;
-  auto kern = prefill_state_kernel<DK, DV, BV, TOut>;
+  auto kern = prefill_state_kernel<DK, DV, BV, TOut, SUMMARY>;
   static bool attr_set = false;  // per instantiation; idempotent if raced
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -495,31 +628,65 @@ hipError_t launch_state_t(const PrefillArgs& a, const unsigned char* img, const 
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int grid = a.n_seq * a.H * (DV / BV);
+  const int cols = SUMMARY ? DK + DV : DV;
+  const int grid = (SUMMARY ? sg.nseg - 1 : sg.nseg) * a.n_seq * a.H * (cols / BV);
+  if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH_S), L::total, (hipStream_t)a.stream, img, chunk_off,
                      a.cu_seqlens, a.initial_state, carry, (TOut*)a.o, a.n_seq, a.T, a.H, tok_lo,
-                     tok_hi, cap);
+                     tok_hi, cap, sg.nseg, sg.seg_in, sg.summ);
   return hipGetLastError();
 }
 
 template <int DK, int DV>
 hipError_t launch_state_d(const PrefillArgs& a, const unsigned char* img, const int32_t* chunk_off,
-                          float* carry, long long tok_lo, long long tok_hi, int cap) {
-  return a.o_bf16 ? launch_state_t<DK, DV, bf16>(a, img, chunk_off, carry, tok_lo, tok_hi, cap)
-                  : launch_state_t<DK, DV, float>(a, img, chunk_off, carry, tok_lo, tok_hi, cap);
+                          float* carry, long long tok_lo, long long tok_hi, int cap,
+                          const SegmentArgs& sg, bool summary) {
+  if (summary)  // no output: one instantiation
+    return launch_state_t<DK, DV, float, true>(a, img, chunk_off, carry, tok_lo, tok_hi, cap, sg);
+  return a.o_bf16
+             ? launch_state_t<DK, DV, bf16, false>(a, img, chunk_off, carry, tok_lo, tok_hi, cap, sg)
+             : launch_state_t<DK, DV, float, false>(a, img, chunk_off, carry, tok_lo, tok_hi, cap, sg);
+}
+
+template <int DK, int DV>
+hipError_t launch_combine_t(const PrefillArgs& a, const int32_t* chunk_off, float* carry,
+                            long long tok_lo, long long tok_hi, int cap, const SegmentArgs& sg) {
+  const int grid = a.n_seq * a.H * (DV / 64);
+  hipLaunchKernelGGL((segment_combine_kernel<DK, DV>), dim3(grid), dim3(512), 0,
+                     (hipStream_t)a.stream, sg.summ, sg.seg_in, a.cu_seqlens, chunk_off,
+                     a.initial_state, carry, a.n_seq, a.T, a.H, tok_lo, tok_hi, cap, sg.nseg);
+  return hipGetLastError();
+}
+
+hipError_t state_dispatch(const PrefillArgs& a, const unsigned char* img, const int32_t* chunk_off,
+                          float* carry, long long tok_lo, long long tok_hi, int cap,
+                          const SegmentArgs& sg, bool summary) {
+  if (a.Dk == 128)
+    return a.Dv == 128 ? launch_state_d<128, 128>(a, img, chunk_off, carry, tok_lo, tok_hi, cap, sg, summary)
+                       : launch_state_d<128, 64>(a, img, chunk_off, carry, tok_lo, tok_hi, cap, sg, summary);
+  return a.Dv == 128 ? launch_state_d<64, 128>(a, img, chunk_off, carry, tok_lo, tok_hi, cap, sg, summary)
+                     : launch_state_d<64, 64>(a, img, chunk_off, carry, tok_lo, tok_hi, cap, sg, summary);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_state(const PrefillArgs& a, const unsigned char* img,
                                 const int32_t* chunk_off, float* carry, long long tok_lo,
-                                long long tok_hi, int cap) {
-  if (a.Dk == 128) {
-    return a.Dv == 128 ? launch_state_d<128, 128>(a, img, chunk_off, carry, tok_lo, tok_hi, cap)
-                       : launch_state_d<128, 64>(a, img, chunk_off, carry, tok_lo, tok_hi, cap);
+                                long long tok_hi, int cap, const SegmentArgs& sg) {
+  if (sg.nseg > 1) {
+    if (hipError_t e = state_dispatch(a, img, chunk_off, carry, tok_lo, tok_hi, cap, sg, true);
+        e != hipSuccess)
+      return e;
+    hipError_t e;
+    if (a.Dk == 128)
+      e = a.Dv == 128 ? launch_combine_t<128, 128>(a, chunk_off, carry, tok_lo, tok_hi, cap, sg)
+                      : launch_combine_t<128, 64>(a, chunk_off, carry, tok_lo, tok_hi, cap, sg);
+    else
+      e = a.Dv == 128 ? launch_combine_t<64, 128>(a, chunk_off, carry, tok_lo, tok_hi, cap, sg)
+                      : launch_combine_t<64, 64>(a, chunk_off, carry, tok_lo, tok_hi, cap, sg);
+    if (e != hipSuccess) return e;
   }
-  return a.Dv == 128 ? launch_state_d<64, 128>(a, img, chunk_off, carry, tok_lo, tok_hi, cap)
-                     : launch_state_d<64, 64>(a, img, chunk_off, carry, tok_lo, tok_hi, cap);
+  return state_dispatch(a, img, chunk_off, carry, tok_lo, tok_hi, cap, sg, false);
 }
 
 hipError_t launch_chunk_table(const int32_t* cu_seqlens, int n_seq, int cap, int32_t* chunk_off,

@@ -204,4 +204,8 @@ WORKLOADS = {
                       shift=1.0, state_std=0.02, seed=1004),
     "long_1m": dict(B=1, T=1_048_576, H=96, D=128, qkv_dtype=torch.bfloat16, shift=1.0,
                     state_std=0.02, seed=1005),
+    # one device's share of the 8K layer when its 96 heads are split over 8
+    # devices (heads are independent, so each holds 12 whole heads)
+    "k3_prefill_8k_h12": dict(B=1, T=8192, H=12, D=128, qkv_dtype=torch.bfloat16, shift=1.0,
+                              state_std=0.02, seed=1008),
 }

@@ -74,6 +74,72 @@ def test_two_pass_preference():
     assert lib.kda_prefill_two_pass_preferred(F32, 1, 8192, 2, 64, 64) == 0
 
 
+def test_segmented_workspace_and_preference():
+    """The segmented schedule adds the segments' entry states (n_segments
+    states per (sequence, head)) and the summaries [M | b] (n_segments - 1 of
+    them, Dk x (Dk + Dv) each) to the two-pass workspace; one segment needs
+    nothing more."""
+    lib = kda.load()
+    up = lambda x: -(-x // 256) * 256
+    for dk, dv in ((128, 128), (64, 128), (128, 64), (64, 64)):
+        for n, H in ((1, 12), (3, 2)):
+            base = kda.workspace_size(n, 256, H, dk, dv)
+            assert kda.segmented_workspace_size(n, H, dk, dv, 1) == base
+            for ns in (2, 8, 16):
+                want = base + up(ns * n * H * dk * dv * 4) + (ns - 1) * n * H * dk * (dk + dv) * 4
+                assert kda.segmented_workspace_size(n, H, dk, dv, ns) == want
+    bad = ctypes.c_size_t(-1).value
+    assert kda.segmented_workspace_size(1, 12, 128, 128, 0) == bad
+    assert kda.segmented_workspace_size(1, 12, 128, 128, 17) == bad
+    assert lib.kda_prefill_segmented_workspace_size(1, 12, 128, 128, 32, 4) == bad
+    assert kda.segmented_workspace_size(1, 12, 96, 128, 4) == 0
+    # few (sequence, head) pairs and long sequences: segments, at most 8; many
+    # heads, short sequences or fp32 inputs: none (these figures assume 256
+    # compute units, the count taken when no device is visible)
+    pref = lambda *a: lib.kda_prefill_segments_preferred(*a)
+    if not __import__("torch").cuda.is_available():
+        assert pref(BF16, 1, 8192, 12, 128, 128) == 6
+        assert pref(BF16, 1, 8192, 24, 128, 128) == 3
+        assert pref(BF16, 1, 8192, 48, 128, 128) == 2
+        assert pref(BF16, 1, 8192, 4, 128, 128) == 8   # capped
+        assert pref(BF16, 1, 8192, 12, 64, 128) == 8   # smaller summaries
+    assert pref(BF16, 1, 8192, 96, 128, 128) == 1
+    assert pref(BF16, 1, 448, 12, 128, 128) == 1  # 7 chunks: under 4 per segment
+    assert pref(BF16, 1, 512, 12, 128, 128) == 2  # 8 chunks: two segments of 4
+    assert pref(F32, 1, 8192, 12, 64, 64) == 1
+    assert 1 <= pref(BF16, 2, 2 * 8192, 12, 128, 128) <= 8
+
+
+def _segmented(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, qd=BF16, cu=None, n=1, T=4096, s0=None, s1=None, o=FAKE,
+             od=F32, H=2, Dk=128, Dv=128, chunk=64, ns=4, ws=FAKE, wsb=1 << 40)
+    a.update(over)
+    g = _lib._Gate(0, FAKE, None, 0.0)
+    return kda.load().kda_prefill_segmented(
+        a["q"], a["k"], a["v"], a["qd"], ctypes.byref(g), FAKE, a["cu"], a["n"], a["T"], a["s0"],
+        a["s1"], a["o"], a["od"], a["H"], a["Dk"], a["Dv"], a["chunk"], a["ns"], a["ws"], a["wsb"],
+        None)
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(ns=0), INVALID),
+    (dict(ns=17), INVALID),
+    (dict(ws=None, wsb=0), INVALID),
+    (dict(wsb=1024), INVALID),
+    (dict(ws=FAKE + 64), INVALID),
+    (dict(qd=F32, Dk=64), UNSUPPORTED),
+    (dict(Dk=96), UNSUPPORTED),
+    (dict(chunk=32), UNSUPPORTED),
+    (dict(cu=FAKE + 2), INVALID),
+    (dict(n=-1), INVALID),
+    (dict(n=0, q=None, k=None, v=None, o=None, ws=None, wsb=0), OK),
+])
+def test_segmented_validation(over, expect):
+    assert _segmented(**over) == expect
+    if expect != OK:
+        assert len(kda.load().kda_last_error_message()) > 0
+
+
 def _prefill(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, qd=BF16, alpha=FAKE, beta=FAKE, s0=None, s1=None, o=FAKE,
              od=F32, B=1, T=128, H=2, Dk=128, Dv=128, chunk=64, ws=None, wsb=0)
