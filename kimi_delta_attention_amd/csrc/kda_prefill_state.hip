@@ -499,21 +499,26 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
 // segments: E_0 is the state entering the window (the initial state in the
 // sequence's first window, else the carried one) and E_{s+1} = M_s E_s + b_s,
 // the composition of the segment maps ("Kimi K3模型架构详解" section 3.6).
-// One workgroup of 8 waves per (sequence, head, 64-column slice of the state).
-// The slice of E_s sits in LDS as the split (high, low bf16) B operand,
-// [column][row]; rows of M_s arrive from memory as split A fragments; each
-// product is the three-term split-bf16 MFMA product of the state pass, added
-// to b_s in fp32.  Wave w owns row tile w % (Dk / 16) and Dk / 32 of the four
-// column tiles.
+// One workgroup of 8 waves per (sequence, head, 32-column slice of the state);
+// wave w owns row tile w % (Dk / 16) and Dk / 64 of the two column tiles.  The
+// slice of E_s sits in LDS as the split (high, low bf16) B operand,
+// [column][row], in one of two buffers (one barrier per step); rows of M_s are
+// the split A fragments; each product is the three-term split-bf16 MFMA
+// product of the state pass, added to b_s in fp32.  A step's M_s rows and b_s
+// are fetched three steps ahead: one step's work is shorter than a memory
+// access.  A step costs about 3 us on MI355X (the chain of barrier, LDS reads,
+// MFMAs and LDS writes of few waves), so the combine grows with the segment
+// count; more independent MFMA chains per step did not shorten it.
 template <int DK, int DV>
 __global__ __launch_bounds__(512) void segment_combine_kernel(
     const float* __restrict__ summ, float* __restrict__ seg_in,
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ chunk_off,
     const float* s_init, const float* carry, int n_seq, int T, int H, long long tok_lo,
     long long tok_hi, int cap, int nseg) {
-  constexpr int SC = 64, SWC = DK + DV, ld = DK + 8;
-  constexpr int NRT = DK / 16, CTW = NRT / 2;  // row tiles; column tiles per wave
-  __shared__ __align__(16) bf16 EB[2 * SC * ld];
+  constexpr int SC = 32, SWC = DK + DV, ld = DK + 8, NKB = DK / 32;
+  constexpr int NRT = DK / 16, CTW = NRT / 4;  // row tiles; column tiles per wave
+  constexpr int BUF = 2 * SC * ld;             // one buffer: high parts, then low parts
+  __shared__ __align__(16) bf16 EB[2 * BUF];
   constexpr int nsl = DV / SC;
   const int sl = blockIdx.x % nsl, h = (blockIdx.x / nsl) % H, seq = blockIdx.x / (nsl * H);
   const SeqWindow sw = seq_window(cu_seqlens, chunk_off, n_seq, T, seq, tok_lo, tok_hi, cap);
@@ -526,50 +531,90 @@ __global__ __launch_bounds__(512) void segment_combine_kernel(
   const int col0 = sl * SC;
   const size_t head = ((size_t)seq * H + h) * DK * DV;
   const size_t seg_stride = (size_t)n_seq * H * DK * DV;
-  floatx4 acc[CTW];
-#pragma unroll
-  for (int j = 0; j < CTW; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t e = (size_t)(16 * rt + 4 * g + i) * DV + col0 + 16 * (ct0 + j) + tr;
-      acc[j][i] = si ? si[e] : 0.f;
-      seg_in[head + e] = acc[j][i];
-    }
-  for (int s = 0; s + 1 < ns; ++s) {
-#pragma unroll
-    for (int j = 0; j < CTW; ++j) {
-      float x4[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
-      st_split4(EB + (16 * (ct0 + j) + tr) * ld + 16 * rt + 4 * g, SC * ld, x4);
-    }
-    __syncthreads();
+  struct Step {
+    floatx4 m[NKB][2];  // M_s row 16 rt + tr, columns 32 kb + 8 g ..
+    floatx4 b[CTW];     // b_s rows 16 rt + 4 g + i, this lane's column of tile j
+  };
+  auto fetch = [&](int s, Step& st) {
     const float* ms = summ + (((size_t)s * n_seq + seq) * H + h) * DK * SWC;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const float* mr = ms + (size_t)(16 * rt + tr) * SWC + 32 * kb + 8 * g;
+      st.m[kb][0] = *reinterpret_cast<const floatx4*>(mr);
+      st.m[kb][1] = *reinterpret_cast<const floatx4*>(mr + 4);
+    }
 #pragma unroll
     for (int j = 0; j < CTW; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        acc[j][i] = ms[(size_t)(16 * rt + 4 * g + i) * SWC + DK + col0 + 16 * (ct0 + j) + tr];
+        st.b[j][i] = ms[(size_t)(16 * rt + 4 * g + i) * SWC + DK + col0 + 16 * (ct0 + j) + tr];
+  };
+  floatx4 acc[CTW];
+  auto put = [&](bf16* E) {
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) {
-      const float* mr = ms + (size_t)(16 * rt + tr) * SWC + 32 * kb + 8 * g;
-      const floatx4 m0 = *reinterpret_cast<const floatx4*>(mr);
-      const floatx4 m1 = *reinterpret_cast<const floatx4*>(mr + 4);
-      const float x8[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
+    for (int j = 0; j < CTW; ++j) {
+      float x4[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+      st_split4(E + (16 * (ct0 + j) + tr) * ld + 16 * rt + 4 * g, SC * ld, x4);
+    }
+  };
+  // a ring of three steps' operands, fetched three steps ahead (the chain is
+  // unrolled over its at most kMaxSegments - 1 steps, so every ring index is a
+  // constant)
+  constexpr int RING = 3;
+  Step ring[RING];
+#pragma unroll
+  for (int s = 0; s < RING; ++s)
+    if (s + 1 < ns) fetch(s, ring[s]);
+  if (si) {
+#pragma unroll
+    for (int j = 0; j < CTW; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[j][i] = si[(size_t)(16 * rt + 4 * g + i) * DV + col0 + 16 * (ct0 + j) + tr];
+  } else {
+#pragma unroll
+    for (int j = 0; j < CTW; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int j = 0; j < CTW; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      seg_in[head + (size_t)(16 * rt + 4 * g + i) * DV + col0 + 16 * (ct0 + j) + tr] = acc[j][i];
+  put(EB);
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < kMaxSegments - 1; ++s) {
+    if (s + 1 >= ns) break;
+    Step& cur = ring[s % RING];
+    const bf16* E = EB + (s & 1) * BUF;
+#pragma unroll
+    for (int j = 0; j < CTW; ++j) acc[j] = cur.b[j];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const float x8[8] = {cur.m[kb][0][0], cur.m[kb][0][1], cur.m[kb][0][2], cur.m[kb][0][3],
+                           cur.m[kb][1][0], cur.m[kb][1][1], cur.m[kb][1][2], cur.m[kb][1][3]};
       bf16x8 ah, al;
       split8(x8, ah, al);
 #pragma unroll
       for (int j = 0; j < CTW; ++j) {
-        const bf16x8 bh = frag_ld(EB, ld, 16 * (ct0 + j) + tr, 32 * kb, g);
-        const bf16x8 bl = frag_ld(EB + SC * ld, ld, 16 * (ct0 + j) + tr, 32 * kb, g);
+        const bf16x8 bh = frag_ld(E, ld, 16 * (ct0 + j) + tr, 32 * kb, g);
+        const bf16x8 bl = frag_ld(E + SC * ld, ld, 16 * (ct0 + j) + tr, 32 * kb, g);
         acc[j] = mma_ab(ah, al, bh, bl, acc[j]);
       }
     }
-    __syncthreads();  // E_s read by every wave before it is replaced
+    // the ring slot just used takes the step RING ahead
+    if (s + RING + 1 < ns) fetch(s + RING, cur);
     float* out = seg_in + (size_t)(s + 1) * seg_stride + head;
 #pragma unroll
     for (int j = 0; j < CTW; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         out[(size_t)(16 * rt + 4 * g + i) * DV + col0 + 16 * (ct0 + j) + tr] = acc[j][i];
+    if (s + 2 < ns) {
+      // the other buffer was last read in the step before, ahead of its barrier
+      put(EB + ((s + 1) & 1) * BUF);
+      __syncthreads();
+    }
   }
 }
 
@@ -651,7 +696,7 @@ hipError_t launch_state_d(const PrefillArgs& a, const unsigned char* img, const 
 template <int DK, int DV>
 hipError_t launch_combine_t(const PrefillArgs& a, const int32_t* chunk_off, float* carry,
                             long long tok_lo, long long tok_hi, int cap, const SegmentArgs& sg) {
-  const int grid = a.n_seq * a.H * (DV / 64);
+  const int grid = a.n_seq * a.H * (DV / 32);
   hipLaunchKernelGGL((segment_combine_kernel<DK, DV>), dim3(grid), dim3(512), 0,
                      (hipStream_t)a.stream, sg.summ, sg.seg_in, a.cu_seqlens, chunk_off,
                      a.initial_state, carry, a.n_seq, a.T, a.H, tok_lo, tok_hi, cap, sg.nseg);
