@@ -251,6 +251,30 @@ def main():
           f"composed; prefill prologue {pro_ms * 1e3:.1f} us, epilogue {epi_ms * 1e3:.1f} us",
           file=sys.stderr, flush=True)
 
+    # one device's share of the layer under an 8-way head split (12 heads): the
+    # segmented two-pass schedule against the unsegmented one and the fused kernel
+    wh = synth.WORKLOADS["k3_prefill_8k_h12"]
+    hin = synth.make_dense(wh["B"], wh["T"], wh["H"], wh["D"], wh["D"], seed=wh["seed"],
+                           state_std=wh["state_std"], device=d)
+    hB, hT, hH, hD = wh["B"], wh["T"], wh["H"], wh["D"]
+    nseg = kda.segments_preferred(torch.bfloat16, hB, hB * hT, hH, hD, hD)
+    hws = torch.empty(kda.segmented_workspace_size(hB, hH, hD, hD, nseg), dtype=torch.uint8,
+                      device=d)
+    ho = torch.empty(hB, hT, hH, hD, dtype=torch.float32, device=d)
+    hfs = torch.empty(hB, hH, hD, hD, dtype=torch.float32, device=d)
+    hg = (hin.q, hin.k, hin.v, hin.alpha, hin.beta)
+    seg_ms = timed(lambda: kda.prefill_segmented(*hg, initial_state=hin.state, n_segments=nseg,
+                                                 final_state=hfs, o=ho, workspace=hws),
+                   args.steps)
+    h2p_ms = timed(lambda: kda.prefill_chunked(*hg, initial_state=hin.state, final_state=hfs,
+                                               o=ho, schedule="two_pass", workspace=hws),
+                   args.steps)
+    hfu_ms = timed(lambda: kda.prefill_chunked(*hg, initial_state=hin.state, final_state=hfs,
+                                               o=ho, schedule="fused"), args.steps)
+    hbytes = prefill_bytes(hB, hT, hH, hD, hD)
+    print(f"bench: 12-head share: segmented ({nseg}) {seg_ms:.3f} ms, two-pass {h2p_ms:.3f} ms, "
+          f"fused {hfu_ms:.3f} ms", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu:
         import oracle
@@ -318,6 +342,12 @@ def main():
                   "prefill_prologue_us": pro_ms * 1e3, "prefill_epilogue_us": epi_ms * 1e3,
                   "prefill_workload": "k3_prefill_8k, standalone kernels (bf16 x, q/k/v, y; "
                                       "fp32 o)"},
+        "prefill_one_device_share": {
+            "workload": "k3_prefill_8k_h12: the 8K layer's 12 heads per device under an 8-way "
+                        "head split (B=1, T=8192, d=128)",
+            "segments": nseg, "segmented_ms": seg_ms, "two_pass_ms": h2p_ms, "fused_ms": hfu_ms,
+            "tokens_per_s": hB * hT / (seg_ms / 1e3),
+            "algorithmic_gbs": hbytes / (seg_ms / 1e3) / 1e9},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -57,6 +57,17 @@ def main():
     eo, es = replay(inp, o, s)
     row("k3_prefill_8k", 2e-3, eo, es, "GPU decode replay, all 96 heads")
 
+    w = synth.WORKLOADS["k3_prefill_8k_h12"]
+    inp = synth.make_dense(w["B"], w["T"], w["H"], w["D"], w["D"], seed=w["seed"],
+                           state_std=w["state_std"], device=d)
+    ns = kda.segments_preferred(torch.bfloat16, w["B"], w["B"] * w["T"], w["H"], w["D"], w["D"])
+    o, s = kda.prefill_segmented(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
+                                 initial_state=inp.state, n_segments=ns)
+    torch.cuda.synchronize()
+    ro, rs = oracle_heads(inp, list(range(12)))
+    row(f"k3_prefill_8k_h12 segmented x{ns} (B1 H12 T8192 d128)", 2e-3,
+        oracle.rel_l2(o.cpu(), ro), oracle.rel_l2(s.cpu(), rs), "oracle, all 12 heads")
+
     w = synth.WORKLOADS["decode_b64"]
     inp = synth.make_dense(w["B"], 1, w["H"], w["D"], w["D"], seed=w["seed"], state_std=0.02)
     st = inp.state.to(d)
