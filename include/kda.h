@@ -50,7 +50,7 @@
  * matrix) and a short state-dependent remainder ("Kimi Delta Attention 完全拆解",
  * section "chunk 内并行、chunk 间递推").  Fused: one kernel, one workgroup per
  * (sequence, head, 64-wide value slice) walks its chunks and does both.
- * Two-pass: the packed token axis is cut into windows of 4096 tokens; for each
+ * Two-pass: the packed token axis is cut into windows of 8192 tokens; for each
  * window a first kernel does the state-independent work of the chunks starting
  * in it, once per (chunk, head) over the whole device, and leaves per-chunk
  * operands in the caller's workspace, and a second kernel runs the recurrence
@@ -58,7 +58,7 @@
  * schedule runs when the call passes a workspace of at least
  * kda_prefill_workspace_size / kda_prefill_varlen_workspace_size bytes (a
  * non-zero value); otherwise the fused kernel runs.  Like the state, the
- * workspace does not grow with the sequence length (about 8.2 MiB per head for
+ * workspace does not grow with the sequence length (about 16.3 MiB per head for
  * one sequence at Dk = Dv = 128); its contents on return are unspecified.
  * kda_prefill_two_pass_preferred says which schedule is expected to be faster
  * on the current device.
@@ -361,7 +361,7 @@ kda_status kda_decode_layer(kda_decode_mode mode, const void* xq, const void* xk
  * schedule of kda_prefill_chunked for these sizes, independent of T (the state
  * is fixed-size, "Kimi K3 混合线性注意力": the per-session state does not grow
  * with length): a chunk table of B + 1 int32, one carried state per
- * (sequence, head) and the operand blocks of one window, (64 + B) * H of them
+ * (sequence, head) and the operand blocks of one window, (128 + B) * H of them
  * (131,584 B each at Dk = Dv = 128).  0 when the schedule does not exist for
  * the shape (head dims outside {64, 128}, or B <= 0).  (size_t)-1 for invalid
  * sizes.  Only bf16 inputs use it.

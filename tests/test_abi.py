@@ -46,7 +46,7 @@ def test_status_strings():
 
 def test_workspace_sizes():
     """Two-pass workspace: a chunk table (B + 1 int32), one carried fp32 state per
-    (sequence, head), and the operand blocks of one 4096-token window, (64 + B) * H
+    (sequence, head), and the operand blocks of one 8192-token window, (128 + B) * H
     of them; each block holds the frames of W, (Gamma*Q), Mqk, Ktil^T and U plus
     Gamma_C, rounded to 256 B.  Like the state, it does not depend on T."""
     frames = {(128, 128): 4 * 4 * 2 + 4 * 4 + 16 + 8 * 4 + 4 * 8,
@@ -55,7 +55,7 @@ def test_workspace_sizes():
     for (dk, dv), f in frames.items():
         blk = up(f * 1024 + dk * 4)
         for B, H in ((1, 1), (1, 96), (3, 2), (16, 96)):
-            want = up((B + 1) * 4) + up(B * H * dk * dv * 4) + (64 + B) * H * blk
+            want = up((B + 1) * 4) + up(B * H * dk * dv * 4) + (128 + B) * H * blk
             sizes = {kda.workspace_size(B, T, H, dk, dv) for T in (1, 256, 8192, 1 << 20)}
             assert sizes == {want}
             assert {_lib.varlen_workspace_size(B, tot, H, dk, dv) for tot in (B, 129161, 1 << 30)} \

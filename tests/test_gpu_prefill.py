@@ -270,12 +270,12 @@ def test_two_pass_workspace_reuse_and_capacity():
 
 
 def test_two_pass_windows():
-    """Several 4096-token windows: dense sequences longer than a window, packed
+    """Several 8192-token windows: dense sequences longer than a window, packed
     sequences that start, end or lie entirely inside later windows (and empty
     ones among them), state handed over in place or not returned at all.  The
     two-pass result equals the fused kernel bitwise and the oracle within 2e-3."""
     d = dev()
-    inp = synth.make_dense(2, 5000, 2, 128, 128, seed=501, state_std=0.02)
+    inp = synth.make_dense(2, 9000, 2, 128, 128, seed=501, state_std=0.02)
     o_ref, s_ref = oracle.recurrent(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
                                     initial_state=inp.state)
     o1, s1 = _run(inp, d, schedule="fused")
@@ -291,7 +291,7 @@ def test_two_pass_windows():
                                    schedule="two_pass")
     torch.cuda.synchronize()
     assert none is None and torch.equal(st, s1) and torch.equal(o3, o1) and torch.equal(o4, o1)
-    lengths = [3000, 0, 2500, 64, 4096, 1, 0, 5000, 130]
+    lengths = [6000, 0, 2500, 64, 8192, 1, 0, 9000, 130]
     vin = _varlen_case(lengths, 2, 64, seed=73, d=d)
     cu = vin.cu_seqlens.cpu().numpy()
     o_ref, s_ref = oracle.recurrent(vin.q.cpu(), vin.k.cpu(), vin.v.cpu(), vin.alpha.cpu(),
@@ -304,13 +304,13 @@ def test_two_pass_windows():
 
 
 def test_two_pass_on_caller_stream_and_in_a_graph():
-    """The two-pass schedule (two launches per 4096-token window) on a
+    """The two-pass schedule (two launches per 8192-token window) on a
     non-default caller stream, and captured in a graph replayed several times
     with eager work between the replays, gives bitwise the eager result."""
     d = dev()
-    inp = synth.make_dense(1, 5000, 3, 128, 128, seed=511, state_std=0.02, device=d)
+    inp = synth.make_dense(1, 10000, 3, 128, 128, seed=511, state_std=0.02, device=d)
     ref_o, ref_s = _run(inp, d, schedule="fused")
-    ws = torch.empty(kda.workspace_size(1, 5000, 3, 128, 128), dtype=torch.uint8, device=d)
+    ws = torch.empty(kda.workspace_size(1, 10000, 3, 128, 128), dtype=torch.uint8, device=d)
     o = torch.empty_like(ref_o)
     fs = torch.empty_like(ref_s)
 

@@ -80,10 +80,10 @@ def test_gates(kind):
 
 
 def test_windows_in_place_and_bf16_output():
-    """Three 4096-token windows (the carried state enters each window's
+    """Three 8192-token windows (the carried state enters each window's
     combine), the final state written over the initial one, bf16 output."""
     d = dev()
-    inp = synth.make_dense(1, 2 * 4096 + 1500, 2, 128, 128, seed=1230, state_std=0.02)
+    inp = synth.make_dense(1, 2 * 8192 + 1500, 2, 128, 128, seed=1230, state_std=0.02)
     o_ref, s_ref = oracle.recurrent(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
                                     initial_state=inp.state)
     st = inp.state.to(d).clone()
@@ -105,7 +105,7 @@ def test_packed_sequences():
     """Empty, one-token, sub-chunk, window-crossing and multi-window sequences
     packed together; segments are cut per sequence and window."""
     d = dev()
-    lengths = [3000, 0, 2500, 64, 4096, 1, 0, 5000, 130, 700]
+    lengths = [6000, 0, 2500, 64, 8192, 1, 0, 9000, 130, 700]
     inp = synth.make_varlen(lengths, 2, 128, 128, seed=1240, device=d)
     cu = inp.cu_seqlens.cpu().numpy()
     o_ref, s_ref = oracle.recurrent(inp.q.cpu(), inp.k.cpu(), inp.v.cpu(), inp.alpha.cpu(),
@@ -158,3 +158,39 @@ def test_k3_8k_twelve_heads():
     o_ref, s_ref = oracle_heads(inp, heads)
     assert rel(o[:, :, heads].cpu(), o_ref) <= TOL_BF16
     assert rel(s[:, heads].cpu(), s_ref) <= TOL_BF16
+
+
+def test_in_a_graph():
+    """Two windows of summary, combine and state passes captured in a graph and
+    replayed several times, with eager work between the replays: every replay
+    gives bitwise the eager result."""
+    d = dev()
+    inp = synth.make_dense(1, 8192 + 3000, 2, 128, 128, seed=1260, state_std=0.02, device=d)
+    g = (inp.q, inp.k, inp.v, inp.alpha, inp.beta)
+    ws = torch.empty(kda.segmented_workspace_size(1, 2, 128, 128, 5), dtype=torch.uint8, device=d)
+    ref_o, ref_s = kda.prefill_segmented(*g, initial_state=inp.state, n_segments=5, workspace=ws)
+    o = torch.empty_like(ref_o)
+    fs = torch.empty_like(ref_s)
+
+    def call():
+        kda.prefill_segmented(*g, initial_state=inp.state, final_state=fs, o=o, n_segments=5,
+                              workspace=ws)
+
+    side = torch.cuda.Stream(device=d)
+    side.wait_stream(torch.cuda.current_stream(d))
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream(d).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for _ in range(3):
+        o.zero_()
+        fs.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(fs, ref_s)
+        _dense(synth.make_dense(1, 700, 2, 128, 128, seed=1261, state_std=0.02), d, 3,
+               workspace=ws)  # eager work on the same workspace between replays
+        torch.cuda.synchronize()
