@@ -357,6 +357,40 @@ kda_status kda_decode_layer(kda_decode_mode mode, const void* xq, const void* xk
                             void* stream);
 
 /*
+ * kda_prefill_layer -- the recurrent layer over a prefill, from the
+ * projections' outputs to the gated output: the prologue, the two-pass
+ * (optionally segmented) recurrence and the epilogue ("Kimi Delta Attention
+ * 完全拆解", section "一次 KDA 前向究竟发生了什么"; "从线性注意力到 KDA", the
+ * ShortConv / L2Norm bullets and the output norm and gate).  The prologue runs
+ * inside the first pass as it loads each chunk, so q, k and v are never
+ * stored; the conv state is handed on after the recurrence and the epilogue
+ * turns o into y.
+ *   xq, xk [.., H, Dk], xv [.., H, Dv]  bf16 (x_dtype must be KDA_BF16)
+ *   conv, conv_state_in, conv_state_out  as for kda_prologue (taps 16-byte
+ *                      aligned; conv_state_out may be NULL)
+ *   gate, beta, cu_seqlens, n_seq, T, initial_state, final_state  as for
+ *                      kda_prefill_segmented (dense when cu_seqlens is NULL)
+ *   o                  [.., H, Dv] fp32: the recurrence's output, before the
+ *                      epilogue (caller-owned scratch or result)
+ *   out                output gate: g [.., H, Dv] bf16, w [Dv], eps
+ *   y                  [.., H, Dv] y_dtype (may alias o as fp32)
+ *   n_segments, workspace  as for kda_prefill_segmented (workspace required
+ *                      when there are tokens; 1 segment is the two-pass
+ *                      schedule)
+ * Equal to kda_prologue, the recurrence and kda_epilogue up to rounding (the
+ * L2Norm's sum of squares is associated differently; q, k, v are rounded to
+ * bf16 as the standalone prologue stores them).
+ */
+kda_status kda_prefill_layer(const void* xq, const void* xk, const void* xv, kda_dtype x_dtype,
+                             const kda_conv* conv, const float* conv_state_in,
+                             float* conv_state_out, const kda_gate* gate, const float* beta,
+                             const int32_t* cu_seqlens, int n_seq, int T,
+                             const float* initial_state, float* final_state, float* o,
+                             const kda_out_gate* out, void* y, kda_dtype y_dtype, int H, int Dk,
+                             int Dv, int chunk, int n_segments, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * kda_prefill_workspace_size -- workspace bytes that enable the two-pass
  * schedule of kda_prefill_chunked for these sizes, independent of T (the state
  * is fixed-size, "Kimi K3 混合线性注意力": the per-session state does not grow

@@ -21,7 +21,7 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED",
 EXPORTED = ("kda_prefill_chunked", "kda_prefill_varlen", "kda_decode_step",
             "kda_prefill_chunked_gated", "kda_prefill_varlen_gated", "kda_decode_step_gated",
             "kda_decode_verify", "kda_decode_commit", "kda_prologue", "kda_epilogue",
-            "kda_decode_layer", "kda_prefill_segmented",
+            "kda_decode_layer", "kda_prefill_layer", "kda_prefill_segmented",
             "kda_prefill_segmented_workspace_size", "kda_prefill_segments_preferred",
             "kda_prefill_workspace_size", "kda_prefill_varlen_workspace_size",
             "kda_prefill_two_pass_preferred", "kda_status_string", "kda_last_error_message")
@@ -97,6 +97,9 @@ def load() -> ctypes.CDLL:
     lib.kda_decode_layer.restype = I
     lib.kda_prefill_segmented.argtypes = [P, P, P, I, G, P, P, I, I, P, P, P, I, I, I, I, I, I,
                                           P, Z, P]
+    lib.kda_prefill_layer.argtypes = [P, P, P, I, C, P, P, G, P, P, I, I, P, P, P,
+                                      ctypes.POINTER(_OutGate), P, I, I, I, I, I, I, P, Z, P]
+    lib.kda_prefill_layer.restype = I
     lib.kda_prefill_segmented.restype = I
     lib.kda_prefill_segmented_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.kda_prefill_segmented_workspace_size.restype = Z
@@ -550,3 +553,83 @@ def decode_layer(mode: str, xq, xk, xv, wq, wk, wv, conv_state, alpha, beta, sta
         _ptr(conv_state), ctypes.byref(gd), _ptr(beta), _ptr(state), ctypes.byref(og), _ptr(y),
         _dt(y) if y is not None else KDA_F32, _ptr(n_accept), B, N, H, Dk, Dv, _stream(dev)))
     return y
+
+
+def prefill_layer(xq, xk, xv, wq, wk, wv, alpha, beta, g, norm_w, conv_state=None,
+                  initial_state=None, cu_seqlens=None, n_segments: int = 1,
+                  conv_eps: float = 1e-6, norm_eps: float = 1e-5, out_dtype=torch.float32,
+                  final_state: bool | torch.Tensor = True,
+                  conv_state_out: bool | torch.Tensor = True, o: torch.Tensor | None = None,
+                  y: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                  gate: str = "alpha", a_log: torch.Tensor | None = None, g_min: float = -5.0):
+    """The recurrent layer over a prefill: prologue (taps wq, wk [H,Dk,4], wv
+    [H,Dv,4]; conv_state [N,3,H,2Dk+Dv] or None) fused into the two-pass first
+    pass, the recurrence (n_segments as for prefill_segmented), the epilogue (g
+    [..,H,Dv] bf16, norm_w [Dv]).  xq, xk [B,T,H,Dk], xv [B,T,H,Dv] bf16 (packed:
+    B = 1 with cu_seqlens).  Returns (y, o, final_state, conv_state_out)."""
+    B, T, H, Dk = xq.shape
+    Dv = xv.shape[-1]
+    dev = xq.device
+    for t, n in ((xq, "x_q"), (xk, "x_k"), (xv, "x_v")):
+        _need(t, n, xq.dtype, dev)
+    if xk.shape != xq.shape or xv.shape != (B, T, H, Dv) or beta.shape != (B, T, H):
+        raise ValueError("inconsistent shapes")
+    _need(beta, "beta", torch.float32, dev)
+    c = _conv(wq, wk, wv, conv_eps, H, Dk, Dv, dev)
+    gd = _gate(gate, alpha, a_log, g_min, (B, T), H, Dk, dev)
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("packed inputs have B == 1")
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        n_seq = cu_seqlens.numel() - 1
+    else:
+        n_seq = B
+    sw = (n_seq, 3, H, 2 * Dk + Dv)
+    if conv_state is not None:
+        _need(conv_state, "conv_state", torch.float32, dev)
+        if tuple(conv_state.shape) != sw:
+            raise ValueError(f"conv_state must be {sw}")
+    if isinstance(conv_state_out, torch.Tensor):
+        so = conv_state_out
+        _need(so, "conv_state_out", torch.float32, dev)
+    elif conv_state_out:
+        so = torch.empty(sw, dtype=torch.float32, device=dev)
+    else:
+        so = None
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev)
+        if initial_state.shape != (n_seq, H, Dk, Dv):
+            raise ValueError("initial_state must be [n_seq, H, Dk, Dv]")
+    if isinstance(final_state, torch.Tensor):
+        fs = final_state
+        _need(fs, "final_state", torch.float32, dev)
+    elif final_state:
+        fs = torch.empty(n_seq, H, Dk, Dv, dtype=torch.float32, device=dev)
+    else:
+        fs = None
+    _need(g, "g", xq.dtype, dev)
+    _need(norm_w, "norm_w", torch.float32, dev)
+    if g.shape != (B, T, H, Dv) or tuple(norm_w.shape) != (Dv,):
+        raise ValueError("g must be [B, T, H, Dv] and norm_w [Dv]")
+    og = _OutGate(g.data_ptr(), norm_w.data_ptr(), float(norm_eps))
+    if o is None:
+        o = torch.empty(B, T, H, Dv, dtype=torch.float32, device=dev)
+    else:
+        _need(o, "o", torch.float32, dev)
+    if y is None:
+        y = torch.empty(B, T, H, Dv, dtype=out_dtype, device=dev)
+    else:
+        _need(y, "y", None, dev)
+    need = segmented_workspace_size(n_seq, H, Dk, Dv, n_segments)
+    if need == (1 << 64) - 1:
+        raise ValueError(f"n_segments must lie in [1, {MAX_SEGMENTS}]")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, dev)
+    _check(load().kda_prefill_layer(
+        _ptr(xq), _ptr(xk), _ptr(xv), _dt(xq), ctypes.byref(c), _ptr(conv_state), _ptr(so),
+        ctypes.byref(gd), _ptr(beta), _ptr(cu_seqlens), n_seq, T if cu_seqlens is None else T,
+        _ptr(initial_state), _ptr(fs), _ptr(o), ctypes.byref(og), _ptr(y), _dt(y), H, Dk, Dv, 64,
+        n_segments, _ptr(workspace), workspace.numel(), _stream(dev)))
+    return y, o, fs, so

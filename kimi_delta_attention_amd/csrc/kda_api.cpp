@@ -133,7 +133,7 @@ static kda_status prefill_common(const void* q, const void* k, const void* v, kd
                                  const float* initial_state, float* final_state, void* o,
                                  kda_dtype o_dtype, int H, int Dk, int Dv, int chunk,
                                  void* workspace, size_t workspace_bytes, void* stream,
-                                 int nseg = 1) {
+                                 int nseg = 1, const kda::LayerPro* pro = nullptr) {
   if (n_seq < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative batch or length");
   if (n_seq == 0) return ok();
   kda::Gate g = {KDA_GATE_NONE, nullptr, nullptr, 0.f};
@@ -184,6 +184,7 @@ static kda_status prefill_common(const void* q, const void* k, const void* v, kd
   a.workspace = workspace; a.workspace_bytes = workspace ? workspace_bytes : 0;
   a.stream = stream;
   a.nseg = nseg;
+  a.pro = pro;
   return hip_status(kda::launch_prefill(a));
 }
 
@@ -480,3 +481,63 @@ kda_status kda_decode_layer(kda_decode_mode mode, const void* xq, const void* xk
 }
 
 }  // extern "C"
+
+kda_status kda_prefill_layer(const void* xq, const void* xk, const void* xv, kda_dtype x_dtype,
+                             const kda_conv* conv, const float* conv_state_in,
+                             float* conv_state_out, const kda_gate* gate, const float* beta,
+                             const int32_t* cu_seqlens, int n_seq, int T,
+                             const float* initial_state, float* final_state, float* o,
+                             const kda_out_gate* out, void* y, kda_dtype y_dtype, int H, int Dk,
+                             int Dv, int chunk, int n_segments, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (n_seq < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "n_seq and T must be >= 0");
+  if (n_seq == 0) return ok();
+  if (x_dtype != KDA_BF16) {
+    if (!dtype_ok(x_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "bad x_dtype");
+    return fail(KDA_ERR_UNSUPPORTED, "the layer prefill takes bf16 projections");
+  }
+  if (!dtype_ok(y_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "bad y_dtype");
+  if (n_segments < 1 || n_segments > kda::kMaxSegments)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "n_segments must lie in [1, %d] (got %d)",
+                kda::kMaxSegments, n_segments);
+  kda::LayerPro pro{};
+  kda_status s = check_conv(conv, &pro.conv);
+  if (s != KDA_OK) return s;
+  if (((uintptr_t)conv->w_q | (uintptr_t)conv->w_k | (uintptr_t)conv->w_v) & 15u)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "conv taps must be 16-byte aligned");
+  if ((conv_state_in && !aligned16(conv_state_in)) || (conv_state_out && !aligned16(conv_state_out)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "conv states must be 16-byte aligned");
+  if (conv_state_out && conv_state_out == conv_state_in)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "conv_state_out must not alias conv_state_in");
+  if (!out || !out->w || !eps_ok(out->eps))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "output gate: w non-null and eps finite and > 0");
+  const bool tokens = T > 0;
+  if (tokens) {
+    if (!out->g || !y || !o)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "o, y and the output gate g must be non-null");
+    if (!aligned16(out->g) || !aligned16(y) || !aligned16(o) || ((uintptr_t)out->w & 3u))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "o, y, g must be 16-byte aligned, w 4-byte");
+    if ((void*)o == y && y_dtype != KDA_F32)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "y may alias o only as fp32");
+    if (cu_seqlens && ((uintptr_t)cu_seqlens & 3u))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
+    if (kda::prefill_supported(true, Dk, Dv) && H > 0) {
+      const size_t need = kda::prefill_segmented_bytes(n_seq, H, Dk, Dv, n_segments);
+      if (need == 0) return fail(KDA_ERR_INVALID_ARGUMENT, "sizes too large for the layer prefill");
+      if (!workspace || workspace_bytes < need)
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "the layer prefill needs a workspace of %zu bytes (got %zu)", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    }
+  }
+  pro.st_in = conv_state_in;
+  pro.st_out = conv_state_out;
+  pro.out.g = out->g;
+  pro.out.w = out->w;
+  pro.out.eps = out->eps;
+  pro.y = y;
+  pro.y_bf16 = y_dtype == KDA_BF16;
+  return prefill_common(xq, xk, xv, x_dtype, gate, beta, cu_seqlens, n_seq, T, initial_state,
+                        final_state, o, KDA_F32, H, Dk, Dv, chunk, workspace, workspace_bytes,
+                        stream, n_segments, &pro);
+}

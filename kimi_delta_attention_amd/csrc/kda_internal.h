@@ -28,6 +28,18 @@ struct DecodeArgs {
   LayerIO io{};
 };
 
+// The layer prefill: the first pass reads the projections' outputs (q, k, v
+// of PrefillArgs) and applies the prologue; after the recurrence the conv
+// state is handed on and the epilogue turns o into y.
+struct LayerPro {
+  ConvArgs conv;
+  const float* st_in;   // [n_seq, 3, H, 2 Dk + Dv] fp32 or null (zeros)
+  float* st_out;        // same shape or null; not aliasing st_in
+  OutGateArgs out;      // g [tokens, H, Dv] (bf16), w [Dv], eps
+  void* y;              // [tokens, H, Dv]
+  bool y_bf16;
+};
+
 struct PrefillArgs {
   const void *q, *k, *v;
   Gate gate;
@@ -49,6 +61,7 @@ struct PrefillArgs {
   // workgroup walks all of a window's chunks); above 1 the workspace must hold
   // prefill_segmented_bytes(...).
   int nseg = 1;
+  const LayerPro* pro = nullptr;  // the layer prefill (two-pass only)
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
@@ -83,6 +96,9 @@ struct EpilogueArgs {
 };
 hipError_t launch_prologue(const PrologueArgs& a);
 hipError_t launch_epilogue(const EpilogueArgs& a);
+// The conv state after each sequence (its last three inputs, or the state
+// handed in for a sequence shorter than three), without the prologue's rows.
+hipError_t launch_conv_state(const PrologueArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);      // dispatch (kda_prefill.hip)
 hipError_t launch_prefill_f32(const PrefillArgs& a);  // fp32 inputs (kda_prefill_f32.hip)
 bool prefill_supported(bool qkv_bf16, int Dk, int Dv);

@@ -63,6 +63,18 @@ __device__ __forceinline__ float wave_sum(float x) {
   return __uint_as_float(w[0]) + __uint_as_float(w[1]);
 }
 
+// Sum over the four 16-lane rows at the same position (lanes l, l ^ 16,
+// l ^ 32, l ^ 48): the permlane16 and permlane32 swaps, each adding the same
+// pair in both lanes, so the four lanes hold bitwise the same sum.
+__device__ __forceinline__ float rows4_sum(float x) {
+  const unsigned xb = __float_as_uint(x);
+  const auto h = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
+  x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  const unsigned yb = __float_as_uint(x);
+  const auto w = __builtin_amdgcn_permlane32_swap(yb, yb, false, false);
+  return __uint_as_float(w[0]) + __uint_as_float(w[1]);
+}
+
 // Sigmoid(a) = 1 / (1 + 2^(-a log2 e)) on the hardware units
 __device__ __forceinline__ float sigmoid_hw(float a) {
   return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-a * 1.44269504088896341f));
@@ -83,6 +95,18 @@ template <typename T, int CPL>
 __device__ __forceinline__ void row_store(T* row, int lane, const float (&x)[CPL]) {
 #pragma unroll
   for (int c = 0; c < CPL; ++c) row[CPL * lane + c] = (T)x[c];
+}
+
+// ShortConv of one channel over (h0, h1, h2, x) (oldest first; taps t[0..3],
+// t[3] on the current token), then Swish; products summed oldest tap first
+// with explicit fmas.
+__device__ __forceinline__ float conv_swish(const floatx4& t, float h0, float h1, float h2,
+                                            float x) {
+  float a = t[0] * h0;
+  a = __builtin_fmaf(t[1], h1, a);
+  a = __builtin_fmaf(t[2], h2, a);
+  a = __builtin_fmaf(t[3], x, a);
+  return swish(a);
 }
 
 // One token row of one tensor: conv over (h[0], h[1], h[2], x), Swish, and for

@@ -132,6 +132,38 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     st_out[s * 3 * H * SW + e] = st_in ? st_in[s * 3 * H * SW + e] : 0.f;
 }
 
+// conv state out [n_seq][3][H][SW]: element (s, j, h, c) is input end - 3 + j
+// of sequence s, from x when it lies in the sequence, else from the state
+// handed in (row index shifted by the sequence's length) or zero.
+template <typename T>
+__global__ __launch_bounds__(256) void conv_state_kernel(
+    const T* __restrict__ xq, const T* __restrict__ xk, const T* __restrict__ xv,
+    const float* __restrict__ st_in, float* __restrict__ st_out, const int32_t* __restrict__ cu,
+    int n_seq, long long Tseq, int H, int Dk, int Dv) {
+  const int SW = 2 * Dk + Dv;
+  const long long n = (long long)n_seq * 3 * H * SW;
+  for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < n;
+       idx += (long long)gridDim.x * 256) {
+    const int c = (int)(idx % SW);
+    const int h = (int)((idx / SW) % H);
+    const int j = (int)((idx / ((long long)SW * H)) % 3);
+    const long long s = idx / (3LL * SW * H);
+    const long long start = cu ? (long long)cu[s] : s * Tseq;
+    const long long end = cu ? (long long)cu[s + 1] : start + Tseq;
+    const long long p = end - 3 + j;
+    float val = 0.f;
+    if (p >= start) {
+      const T* x = c < Dk ? xq : c < 2 * Dk ? xk : xv;
+      const int cc = c < Dk ? c : c < 2 * Dk ? c - Dk : c - 2 * Dk;
+      const int D = c < 2 * Dk ? Dk : Dv;
+      val = to_f(x[((size_t)p * H + h) * D + cc]);
+    } else if (st_in) {
+      val = st_in[((s * 3 + (p - start + 3)) * H + h) * SW + c];
+    }
+    st_out[idx] = val;
+  }
+}
+
 template <typename TO, typename TG, typename TY, int CPL>
 __global__ __launch_bounds__(256) void epilogue_kernel(const TO* __restrict__ o,
                                                        const TG* __restrict__ g,
@@ -207,6 +239,24 @@ hipError_t launch_prologue(const PrologueArgs& a) {
 
 hipError_t launch_epilogue(const EpilogueArgs& a) {
   return a.o_bf16 ? launch_epi_o<bf16>(a) : launch_epi_o<float>(a);
+}
+
+hipError_t launch_conv_state(const PrologueArgs& a) {
+  if (!a.st_out || a.n_seq <= 0) return hipSuccess;
+  const long long n = (long long)a.n_seq * 3 * a.H * (2 * a.Dk + a.Dv);
+  long long grid = (n + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  if (a.bf16)
+    hipLaunchKernelGGL((conv_state_kernel<bf16>), dim3((unsigned)grid), dim3(256), 0,
+                       (hipStream_t)a.stream, (const bf16*)a.xq, (const bf16*)a.xk,
+                       (const bf16*)a.xv, a.st_in, a.st_out, a.cu_seqlens, a.n_seq, a.Tseq, a.H,
+                       a.Dk, a.Dv);
+  else
+    hipLaunchKernelGGL((conv_state_kernel<float>), dim3((unsigned)grid), dim3(256), 0,
+                       (hipStream_t)a.stream, (const float*)a.xq, (const float*)a.xk,
+                       (const float*)a.xv, a.st_in, a.st_out, a.cu_seqlens, a.n_seq, a.Tseq, a.H,
+                       a.Dk, a.Dv);
+  return hipGetLastError();
 }
 
 }  // namespace kda

@@ -832,6 +832,22 @@ int prefill_segments_preferred(int n_seq, long long tokens, int H, int Dk, int D
   return ns < 2 ? 1 : (int)ns;
 }
 
+// The layer prefill after the recurrence: the conv state handed on, and the
+// epilogue over o.
+hipError_t layer_tail(const PrefillArgs& a, long long total) {
+  const LayerPro& p = *a.pro;
+  PrologueArgs c{};
+  c.xq = a.q; c.xk = a.k; c.xv = a.v; c.bf16 = a.qkv_bf16;
+  c.st_in = p.st_in; c.st_out = p.st_out; c.cu_seqlens = a.cu_seqlens; c.n_seq = a.n_seq;
+  c.Tseq = a.T; c.total = total; c.H = a.H; c.Dk = a.Dk; c.Dv = a.Dv; c.stream = a.stream;
+  if (hipError_t e = launch_conv_state(c); e != hipSuccess) return e;
+  EpilogueArgs ep{};
+  ep.o = a.o; ep.o_bf16 = a.o_bf16; ep.g = p.out.g; ep.g_bf16 = a.qkv_bf16; ep.w = p.out.w;
+  ep.eps = p.out.eps; ep.y = p.y; ep.y_bf16 = p.y_bf16; ep.rows = total; ep.H = a.H;
+  ep.Dv = a.Dv; ep.stream = a.stream;
+  return launch_epilogue(ep);
+}
+
 hipError_t launch_prefill(const PrefillArgs& a) {
   if (!a.qkv_bf16) return launch_prefill_f32(a);
   const bool varlen = a.cu_seqlens != nullptr;
@@ -848,8 +864,13 @@ hipError_t launch_prefill(const PrefillArgs& a) {
                                        seg_in_bytes(a.n_seq, a.H, a.Dk, a.Dv, a.nseg));
   }
   if (need == 0 || !a.workspace || a.workspace_bytes < need || total == 0) {
-    if (a.Dk == 128) return a.o_bf16 ? launch_fused<128, bf16>(a) : launch_fused<128, float>(a);
-    return a.o_bf16 ? launch_fused<64, bf16>(a) : launch_fused<64, float>(a);
+    // the layer prefill's prologue lives in the two-pass first pass: without
+    // tokens only the states are handed through
+    if (a.pro && total > 0) return hipErrorInvalidValue;
+    hipError_t e = a.Dk == 128 ? (a.o_bf16 ? launch_fused<128, bf16>(a) : launch_fused<128, float>(a))
+                               : (a.o_bf16 ? launch_fused<64, bf16>(a) : launch_fused<64, float>(a));
+    if (e == hipSuccess && a.pro) e = layer_tail(a, total);
+    return e;
   }
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
   int32_t* chunk_off = varlen ? reinterpret_cast<int32_t*>(ws) : nullptr;
@@ -874,6 +895,7 @@ hipError_t launch_prefill(const PrefillArgs& a) {
     e = launch_prefill_state(a, img, chunk_off, carry, t0, t0 + win, cap, sg);
     if (e != hipSuccess) return e;
   }
+  if (a.pro) return layer_tail(a, total);
   return hipSuccess;
 }
 

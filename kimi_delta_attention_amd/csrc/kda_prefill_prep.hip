@@ -75,23 +75,44 @@ struct PrepPlan {
   static constexpr int oKT = 0;
   static constexpr int m1 = 3 * TILE > oTF + F32T ? 3 * TILE : oTF + F32T;
   static constexpr int R = m1 > 2 * TILE ? m1 : 2 * TILE;
+  static constexpr int oR0 = 0;
   static constexpr int oGK = R, oES = oGK + TILE, oGC = oES + 4 * DK * 4, oBS = oGC + DK * 4,
                        total = oBS + CH * 4;
   static_assert(total <= 81920, "two workgroups per compute unit");
+  // With the layer prologue: the conv taps of the item's head ([2 Dk + Dv][4]
+  // fp32) after the plan; the chunk's raw inputs XR ([64][SWP + 8] bf16) in R
+  // and the three inputs before the chunk HIST ([3][SWP] fp32) in GK, both
+  // between the barriers that end phase 1 and start phase 2.
+  static constexpr int SWP = 2 * DK + DV, ldX = SWP + 8;
+  static constexpr int oTP = total, totalP = oTP + SWP * 16;
+  static_assert(totalP <= 81920, "two workgroups per compute unit with the prologue");
+  static_assert(CH * ldX * 2 <= R && 3 * SWP * 4 <= TILE, "prologue staging");
   static_assert(oTB + TBsz <= oTF && oMQ + F32T <= oTF, "TF is read while TB, VS are written");
   static_assert((oQLh | oQLl | oMQ | oTF | oVS | oGK | oES | oGC | oBS) % 16 == 0, "alignment");
+};
+
+// The layer prologue in front of the first pass ("Kimi Delta Attention
+// 完全拆解", section "一次 KDA 前向究竟发生了什么"): q, k = L2Norm(Swish(ShortConv
+// (x))), v = Swish(ShortConv(x)), computed from the projections' outputs as
+// the chunk is loaded, so that q, k and v never reach memory.  The raw rows
+// go through LDS for the convolution's three previous inputs (the rows before
+// the chunk from the sequence's previous chunk or its conv state); the
+// results are rounded to bf16, as the standalone prologue stores them.
+struct ProArgs {
+  ConvArgs conv;
+  const float* st_in;  // [n_seq, 3, H, 2 Dk + Dv] fp32 or null (zeros)
 };
 
 // b x + b y with both products rounded: the fused kernel scales each channel
 // half separately and adds them later
 __device__ __forceinline__ float scaled_sum(float b, float x, float y) { return b * x + b * y; }
 
-template <int DK, int DV, int KIND>
+template <int DK, int DV, int KIND, bool PRO>
 __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     Gate gate, const float* __restrict__ beta,
     const int32_t* __restrict__ cu_seqlens, int n_seq, int T, int H, unsigned char* __restrict__ img,
-    const int32_t* __restrict__ chunk_off, long long tok_lo, long long tok_hi, int cap) {
+    const int32_t* __restrict__ chunk_off, long long tok_lo, long long tok_hi, int cap, ProArgs pa) {
   using L = PrepPlan<DK, DV>;
   using IM = Images<DK, DV>;
   constexpr int NKB = DK / 32;   // 32-channel blocks
@@ -116,6 +137,10 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
   float* ES = reinterpret_cast<float*>(smem + L::oES);  // [4][DK] tile decays
   float* GC = reinterpret_cast<float*>(smem + L::oGC);  // [DK] chunk decay
   float* BS = reinterpret_cast<float*>(smem + L::oBS);  // [64] beta
+  float* TP = reinterpret_cast<float*>(smem + L::oTP);  // prologue taps [SWP][4]
+  bf16* XR = reinterpret_cast<bf16*>(smem + L::oR0);    // prologue raw rows [64][ldX]
+  float* HI = reinterpret_cast<float*>(smem + L::oGK);  // prologue HIST [3][SWP]
+  constexpr int SWP = L::SWP, ldX = L::ldX;
 
   const int w4 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -127,8 +152,8 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
 
   // One item: chunk ci of head hd; its first token and valid tokens.
   struct Item {
-    long long tok0;
-    int nv, hd;
+    long long tok0, start;  // first token of the chunk, of its sequence
+    int nv, hd, seq;
   };
   auto locate = [&](int item) {
     const int ci = ci_lo + item / H;
@@ -145,13 +170,16 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
       st = cu_seqlens[lo];
       ln = (long long)cu_seqlens[lo + 1] - st;
       cc = (long long)(ci - chunk_off[lo]) * CH;
+      d.seq = lo;
     } else {
       const int nch = (T + CH - 1) / CH;
       const int sq = ci / nch;
       st = (long long)sq * T;
       ln = T;
       cc = (long long)(ci - sq * nch) * CH;
+      d.seq = sq;
     }
+    d.start = st;
     d.tok0 = st + cc;
     d.nv = (int)(ln - cc < CH ? ln - cc : CH);
     return d;
@@ -188,6 +216,8 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     // recomputed per item rather than held (or spilled) across the loop.
     int lane_x = threadIdx.x & 63;
     __asm__ volatile("" : "+v"(lane_x));
+    int tid_x = threadIdx.x;  // the same for the workgroup-wide prologue staging
+    __asm__ volatile("" : "+v"(tid_x));
     const Item cur = locate(item);
     load_in(item, cur, lane_x);
     const long long tok0 = cur.tok0;
@@ -207,6 +237,144 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
       vin[j] = okc ? *reinterpret_cast<const uint4v*>(v + thc * DV + (DV / 4) * g + 8 * j)
                    : uint4v{0u, 0u, 0u, 0u};
 
+    // prologue: the three inputs before the chunk (fp32), and the head's taps
+    // to LDS (their last readers, in the item before, are behind its barriers)
+    constexpr int HPT = (3 * SWP + NTH_P - 1) / NTH_P;
+    float hpre[HPT];
+    if constexpr (PRO) {
+      auto split_c = [&](int c, int& ten, int& cc, int& D) {
+        ten = c < DK ? 0 : c < 2 * DK ? 1 : 2;
+        cc = c - (ten == 0 ? 0 : ten == 1 ? DK : 2 * DK);
+        D = ten < 2 ? DK : DV;
+      };
+#pragma unroll
+      for (int i = 0; i < HPT; ++i) {
+        const int idx = tid_x + NTH_P * i;
+        hpre[i] = 0.f;
+        if (idx < 3 * SWP) {
+          const int j = idx / SWP, c = idx % SWP;
+          int ten, cc, D;
+          split_c(c, ten, cc, D);
+          const long long p = tok0 - 3 + j;
+          const bf16* xt = ten == 0 ? q : ten == 1 ? k : v;
+          if (p >= cur.start)
+            hpre[i] = (float)xt[((size_t)p * H + hd) * D + cc];
+          else if (pa.st_in)
+            hpre[i] = pa.st_in[(((size_t)cur.seq * 3 + (int)(p - cur.start + 3)) * H + hd) * SWP + c];
+        }
+      }
+      for (int c = tid_x; c < SWP; c += NTH_P) {
+        int ten, cc, D;
+        split_c(c, ten, cc, D);
+        *reinterpret_cast<floatx4*>(TP + 4 * c) =
+            *reinterpret_cast<const floatx4*>(pa.conv.w[ten] + ((size_t)hd * D + cc) * 4);
+      }
+    }
+
+    // ---- prologue (layer prefill): conv over the three previous inputs,
+    // Swish, L2Norm of q and k; the results replace the raw rows in kin, qin
+    // and vin.  It runs first in the item, with the raw rows read back from
+    // LDS, so that little else is live; phase 1's barrier ends its LDS reads
+    // before phase 2 reuses the region.
+    if constexpr (PRO) {
+      __syncthreads();  // the item before is done with R and GK
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int c = 32 * kb + 16 * hf + 4 * g;
+          *reinterpret_cast<uint2v*>(XR + r * ldX + c) = qin[kb][hf];
+          *reinterpret_cast<uint2v*>(XR + r * ldX + DK + c) = kin[kb][hf];
+        }
+#pragma unroll
+      for (int j = 0; j < NVL; ++j)
+        *reinterpret_cast<uint4v*>(XR + r * ldX + 2 * DK + (DV / 4) * g + 8 * j) = vin[j];
+#pragma unroll
+      for (int i = 0; i < HPT; ++i) {
+        const int idx = tid_x + NTH_P * i;
+        if (idx < 3 * SWP) HI[idx] = hpre[i];
+      }
+      __syncthreads();
+      // input m rows before this lane's token, channels c0 .. c0 + N - 1 of
+      // the concatenated [q | k | v] row (N = 4 or 8)
+      // (both rows are read at valid addresses and one is selected: a branch
+      // here costs far more registers than the extra LDS read)
+      auto hist4 = [&](int m, int c0, float* out) {
+        const bool in = r - m >= 0;
+        const uint2v u = *reinterpret_cast<const uint2v*>(XR + (in ? r - m : 0) * ldX + c0);
+        const floatx4 f = *reinterpret_cast<const floatx4*>(HI + (in ? 0 : 3 + r - m) * SWP + c0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = in ? bfv(u[e >> 1], e & 1) : f[e];
+      };
+      auto pack4 = [&](const float* y) {
+        uint2v u;
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          u[e] = (unsigned)__builtin_bit_cast(unsigned short, (bf16)y[2 * e]) |
+                 ((unsigned)__builtin_bit_cast(unsigned short, (bf16)y[2 * e + 1]) << 16);
+        return u;
+      };
+      // q and k: 32 channels per lane, the row's 128 over the four lanes of
+      // this token (one per 16-lane row); the fp32 values are scaled once the
+      // sum of squares is known, then rounded to bf16
+      auto group = [&](int c, float* y) {
+        const uint2v xr = *reinterpret_cast<const uint2v*>(XR + r * ldX + c);
+        float h1[4], h2[4], h3[4];
+        hist4(1, c, h1);
+        hist4(2, c, h2);
+        hist4(3, c, h3);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const floatx4 t = *reinterpret_cast<const floatx4*>(TP + 4 * (c + e));
+          y[e] = conv_swish(t, h3[e], h2[e], h1[e], bfv(xr[e >> 1], e & 1));
+        }
+      };
+      auto qk = [&](uint2v (&xin)[NKB][2], int off) {
+        float y[NKB][2][4];
+        float ss = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            group(off + 32 * kb + 16 * hf + 4 * g, y[kb][hf]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(y[kb][hf][e], y[kb][hf][e], ss);
+          }
+        const float rn = __builtin_amdgcn_rsqf(rows4_sum(ss) + pa.conv.eps);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            float z[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[e] = okc ? y[kb][hf][e] * rn : 0.f;  // padding: 0
+            xin[kb][hf] = pack4(z);
+          }
+      };
+      qk(qin, 0);
+      qk(kin, DK);
+#pragma unroll
+      for (int j = 0; j < NVL; ++j) {
+        const int c = 2 * DK + (DV / 4) * g + 8 * j;
+        float z[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          float h1[4], h2[4], h3[4];
+          hist4(1, c + 4 * hh, h1);
+          hist4(2, c + 4 * hh, h2);
+          hist4(3, c + 4 * hh, h3);
+          const uint2v xr = *reinterpret_cast<const uint2v*>(XR + r * ldX + c + 4 * hh);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const floatx4 t = *reinterpret_cast<const floatx4*>(TP + 4 * (c + 4 * hh + e));
+            z[4 * hh + e] = okc ? conv_swish(t, h3[e], h2[e], h1[e], bfv(xr[e >> 1], e & 1)) : 0.f;
+          }
+        }
+        const uint2v lo = pack4(z), hi = pack4(z + 4);
+        vin[j] = uint4v{lo[0], lo[1], hi[0], hi[1]};
+      }
+    }
+
     // ---- 1. within-tile decay products P (inclusive scan over the 16 tokens)
 #pragma unroll
     for (int kb = 0; kb < NKB; kb += 2) row_scan_mul<16>(&Pv[kb][0]);
@@ -220,6 +388,7 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     }
     if (g == 0) BS[r] = bt;
     __syncthreads();
+
 
     // ---- 2. operands of this lane's token, per 32-channel block
     bf16x8 kth[NKB], ktl[NKB];  // Ktil (split), kept until phase 6
@@ -539,21 +708,31 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
   }
 }
 
-template <int DK, int DV, int KIND>
-hipError_t launch_k(const PrefillArgs& a, unsigned char* img, const int32_t* chunk_off,
-                    long long tok_lo, long long tok_hi, int cap, int grid) {
+template <int DK, int DV, int KIND, bool PRO>
+hipError_t launch_kp(const PrefillArgs& a, unsigned char* img, const int32_t* chunk_off,
+                     long long tok_lo, long long tok_hi, int cap, int grid) {
   using L = PrepPlan<DK, DV>;
-  auto kern = prefill_prep_kernel<DK, DV, KIND>;
+  constexpr int lds = PRO ? L::totalP : L::total;
+  auto kern = prefill_prep_kernel<DK, DV, KIND, PRO>;
   static bool attr_set = false;  // per instantiation; idempotent if raced
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::total);
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH_P), L::total, (hipStream_t)a.stream, (const bf16*)a.q,
+  ProArgs pa{};
+  if (PRO) pa = ProArgs{a.pro->conv, a.pro->st_in};
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH_P), lds, (hipStream_t)a.stream, (const bf16*)a.q,
                      (const bf16*)a.k, (const bf16*)a.v, a.gate, a.beta, a.cu_seqlens, a.n_seq, a.T, a.H,
-                     img, chunk_off, tok_lo, tok_hi, cap);
+                     img, chunk_off, tok_lo, tok_hi, cap, pa);
   return hipGetLastError();
+}
+
+template <int DK, int DV, int KIND>
+hipError_t launch_k(const PrefillArgs& a, unsigned char* img, const int32_t* chunk_off,
+                    long long tok_lo, long long tok_hi, int cap, int grid) {
+  return a.pro ? launch_kp<DK, DV, KIND, true>(a, img, chunk_off, tok_lo, tok_hi, cap, grid)
+               : launch_kp<DK, DV, KIND, false>(a, img, chunk_off, tok_lo, tok_hi, cap, grid);
 }
 
 // one instantiation per gate kind, as for the fused kernel

@@ -140,6 +140,38 @@ def test_segmented_validation(over, expect):
         assert len(kda.load().kda_last_error_message()) > 0
 
 
+def _layer(**over):
+    a = dict(x=FAKE, xd=BF16, taps=FAKE, st=None, so=None, ns=1, T=256, o=FAKE, y=FAKE, yd=F32,
+             g=FAKE, w=FAKE, eps=1e-5, ws=FAKE, wsb=1 << 40, H=2, Dk=128, Dv=128, chunk=64)
+    a.update(over)
+    c = _lib._Conv(a["taps"], a["taps"], a["taps"], 1e-6)
+    gt = _lib._Gate(0, FAKE, None, 0.0)
+    og = _lib._OutGate(a["g"], a["w"], a["eps"])
+    return kda.load().kda_prefill_layer(
+        a["x"], a["x"], a["x"], a["xd"], ctypes.byref(c), a["st"], a["so"], ctypes.byref(gt),
+        FAKE, None, 1, a["T"], None, None, a["o"], ctypes.byref(og), a["y"], a["yd"], a["H"],
+        a["Dk"], a["Dv"], a["chunk"], a["ns"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(xd=F32), UNSUPPORTED),
+    (dict(taps=FAKE + 4), INVALID),       # taps need 16-byte alignment here
+    (dict(st=FAKE, so=FAKE), INVALID),    # conv state out aliasing in
+    (dict(eps=0.0), INVALID),
+    (dict(g=None), INVALID),
+    (dict(y=FAKE + 8), INVALID),
+    (dict(yd=BF16, y=FAKE), INVALID),     # y aliasing o needs fp32
+    (dict(ws=None, wsb=0), INVALID),
+    (dict(wsb=4096), INVALID),
+    (dict(ns=0), INVALID),
+    (dict(Dk=96), UNSUPPORTED),
+    (dict(chunk=32), UNSUPPORTED),
+])
+def test_layer_prefill_validation(over, expect):
+    assert _layer(**over) == expect
+    assert len(kda.load().kda_last_error_message()) > 0
+
+
 def _prefill(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, qd=BF16, alpha=FAKE, beta=FAKE, s0=None, s1=None, o=FAKE,
              od=F32, B=1, T=128, H=2, Dk=128, Dv=128, chunk=64, ws=None, wsb=0)
