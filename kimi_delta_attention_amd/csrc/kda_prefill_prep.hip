@@ -79,14 +79,15 @@ struct PrepPlan {
   static constexpr int oGK = R, oES = oGK + TILE, oGC = oES + 4 * DK * 4, oBS = oGC + DK * 4,
                        total = oBS + CH * 4;
   static_assert(total <= 81920, "two workgroups per compute unit");
-  // With the layer prologue: the conv taps of the item's head ([2 Dk + Dv][4]
-  // fp32) after the plan; the chunk's raw inputs XR ([64][SWP + 8] bf16) in R
-  // and the three inputs before the chunk HIST ([3][SWP] fp32) in GK, both
-  // between the barriers that end phase 1 and start phase 2.
+  // With the layer prologue, at the start of an item: the chunk's raw inputs
+  // XR ([64][SWP + 8] bf16, then the results) in R, and in GK the three
+  // inputs before the chunk ([3][SWP] fp32) and the partial sums of squares
+  // of the L2Norm ([4][64] fp32).
   static constexpr int SWP = 2 * DK + DV, ldX = SWP + 8;
+  // and the item's conv taps ([SWP][4] fp32) after the plan
   static constexpr int oTP = total, totalP = oTP + SWP * 16;
   static_assert(totalP <= 81920, "two workgroups per compute unit with the prologue");
-  static_assert(CH * ldX * 2 <= R && 3 * SWP * 4 <= TILE, "prologue staging");
+  static_assert(CH * ldX * 2 <= R && (3 * SWP + 4 * CH) * 4 <= TILE, "prologue staging");
   static_assert(oTB + TBsz <= oTF && oMQ + F32T <= oTF, "TF is read while TB, VS are written");
   static_assert((oQLh | oQLl | oMQ | oTF | oVS | oGK | oES | oGC | oBS) % 16 == 0, "alignment");
 };
@@ -137,9 +138,9 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
   float* ES = reinterpret_cast<float*>(smem + L::oES);  // [4][DK] tile decays
   float* GC = reinterpret_cast<float*>(smem + L::oGC);  // [DK] chunk decay
   float* BS = reinterpret_cast<float*>(smem + L::oBS);  // [64] beta
-  float* TP = reinterpret_cast<float*>(smem + L::oTP);  // prologue taps [SWP][4]
   bf16* XR = reinterpret_cast<bf16*>(smem + L::oR0);    // prologue raw rows [64][ldX]
   float* HI = reinterpret_cast<float*>(smem + L::oGK);  // prologue HIST [3][SWP]
+  float* TP = reinterpret_cast<float*>(smem + L::oTP);  // prologue taps [SWP][4]
   constexpr int SWP = L::SWP, ldX = L::ldX;
 
   const int w4 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -237,24 +238,19 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
       vin[j] = okc ? *reinterpret_cast<const uint4v*>(v + thc * DV + (DV / 4) * g + 8 * j)
                    : uint4v{0u, 0u, 0u, 0u};
 
-    // prologue: the three inputs before the chunk (fp32), and the head's taps
-    // to LDS (their last readers, in the item before, are behind its barriers)
+    // prologue: the three inputs before the chunk (fp32)
     constexpr int HPT = (3 * SWP + NTH_P - 1) / NTH_P;
     float hpre[HPT];
     if constexpr (PRO) {
-      auto split_c = [&](int c, int& ten, int& cc, int& D) {
-        ten = c < DK ? 0 : c < 2 * DK ? 1 : 2;
-        cc = c - (ten == 0 ? 0 : ten == 1 ? DK : 2 * DK);
-        D = ten < 2 ? DK : DV;
-      };
 #pragma unroll
       for (int i = 0; i < HPT; ++i) {
         const int idx = tid_x + NTH_P * i;
         hpre[i] = 0.f;
         if (idx < 3 * SWP) {
           const int j = idx / SWP, c = idx % SWP;
-          int ten, cc, D;
-          split_c(c, ten, cc, D);
+          const int ten = c < DK ? 0 : c < 2 * DK ? 1 : 2;
+          const int cc = c - (ten == 0 ? 0 : ten == 1 ? DK : 2 * DK);
+          const int D = ten < 2 ? DK : DV;
           const long long p = tok0 - 3 + j;
           const bf16* xt = ten == 0 ? q : ten == 1 ? k : v;
           if (p >= cur.start)
@@ -263,19 +259,28 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
             hpre[i] = pa.st_in[(((size_t)cur.seq * 3 + (int)(p - cur.start + 3)) * H + hd) * SWP + c];
         }
       }
+      // the head's taps to LDS (their readers in the item before are behind
+      // its barriers): read as broadcasts, they cost no memory wait per group
       for (int c = tid_x; c < SWP; c += NTH_P) {
-        int ten, cc, D;
-        split_c(c, ten, cc, D);
+        const int ten = c < DK ? 0 : c < 2 * DK ? 1 : 2;
+        const int cc = c - (ten == 0 ? 0 : ten == 1 ? DK : 2 * DK);
+        const int D = ten < 2 ? DK : DV;
         *reinterpret_cast<floatx4*>(TP + 4 * c) =
             *reinterpret_cast<const floatx4*>(pa.conv.w[ten] + ((size_t)hd * D + cc) * 4);
       }
     }
 
-    // ---- prologue (layer prefill): conv over the three previous inputs,
-    // Swish, L2Norm of q and k; the results replace the raw rows in kin, qin
-    // and vin.  It runs first in the item, with the raw rows read back from
-    // LDS, so that little else is live; phase 1's barrier ends its LDS reads
-    // before phase 2 reuses the region.
+    // ---- prologue (layer prefill): ShortConv over the three previous
+    // inputs, Swish, and the L2Norm of q and k.  The raw rows go to LDS; then
+    // lane l of every wave takes token l of the chunk over a range of
+    // channels (waves 0 / 1: the two halves of q, waves 2 / 3: the halves of
+    // k, each wave a quarter of v), so that the taps are the same in every
+    // lane and the previous inputs come from the lanes below (a wave-wide
+    // DPP shift by one lane; lane 0 takes the input before the chunk).  The
+    // two halves of a row's sum of squares meet through LDS; the results,
+    // rounded to bf16, replace the raw values in LDS and are read back in the
+    // operand layout.  Phase 1's barrier ends these LDS reads before phase 2
+    // reuses the region.
     if constexpr (PRO) {
       __syncthreads();  // the item before is done with R and GK
 #pragma unroll
@@ -295,84 +300,88 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
         if (idx < 3 * SWP) HI[idx] = hpre[i];
       }
       __syncthreads();
-      // input m rows before this lane's token, channels c0 .. c0 + N - 1 of
-      // the concatenated [q | k | v] row (N = 4 or 8)
-      // (both rows are read at valid addresses and one is selected: a branch
-      // here costs far more registers than the extra LDS read)
-      auto hist4 = [&](int m, int c0, float* out) {
-        const bool in = r - m >= 0;
-        const uint2v u = *reinterpret_cast<const uint2v*>(XR + (in ? r - m : 0) * ldX + c0);
-        const floatx4 f = *reinterpret_cast<const floatx4*>(HI + (in ? 0 : 3 + r - m) * SWP + c0);
+      const int row = lane_x;             // token of the chunk
+      const bool okr = row < nv;
+      float* SS = HI + 3 * SWP;           // [4 waves][64 rows] partial sums of squares
+      // one group of 8 channels c0.. of the [q | k | v] row for this lane's
+      // token: ShortConv + Swish into y
+      auto group8 = [&](int c0, float* y) {
+        const uint4v u = *reinterpret_cast<const uint4v*>(XR + row * ldX + c0);
+        const floatx4 o0 = *reinterpret_cast<const floatx4*>(HI + 0 * SWP + c0);
+        const floatx4 o1 = *reinterpret_cast<const floatx4*>(HI + 0 * SWP + c0 + 4);
+        const floatx4 p0 = *reinterpret_cast<const floatx4*>(HI + 1 * SWP + c0);
+        const floatx4 p1 = *reinterpret_cast<const floatx4*>(HI + 1 * SWP + c0 + 4);
+        const floatx4 q0 = *reinterpret_cast<const floatx4*>(HI + 2 * SWP + c0);
+        const floatx4 q1 = *reinterpret_cast<const floatx4*>(HI + 2 * SWP + c0 + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out[e] = in ? bfv(u[e >> 1], e & 1) : f[e];
-      };
-      auto pack4 = [&](const float* y) {
-        uint2v u;
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          u[e] = (unsigned)__builtin_bit_cast(unsigned short, (bf16)y[2 * e]) |
-                 ((unsigned)__builtin_bit_cast(unsigned short, (bf16)y[2 * e + 1]) << 16);
-        return u;
-      };
-      // q and k: 32 channels per lane, the row's 128 over the four lanes of
-      // this token (one per 16-lane row); the fp32 values are scaled once the
-      // sum of squares is known, then rounded to bf16
-      auto group = [&](int c, float* y) {
-        const uint2v xr = *reinterpret_cast<const uint2v*>(XR + r * ldX + c);
-        float h1[4], h2[4], h3[4];
-        hist4(1, c, h1);
-        hist4(2, c, h2);
-        hist4(3, c, h3);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const floatx4 t = *reinterpret_cast<const floatx4*>(TP + 4 * (c + e));
-          y[e] = conv_swish(t, h3[e], h2[e], h1[e], bfv(xr[e >> 1], e & 1));
+        for (int e = 0; e < 8; ++e) {
+          const float x = bfv(u[e >> 1], e & 1);
+          // inputs 1, 2, 3 tokens back: lane l - 1's, or before the chunk
+          const float h1 = __int_as_float(__builtin_amdgcn_update_dpp(
+              __float_as_int(e < 4 ? q0[e] : q1[e - 4]), __float_as_int(x), 0x138, 0xf, 0xf, false));
+          const float h2 = __int_as_float(__builtin_amdgcn_update_dpp(
+              __float_as_int(e < 4 ? p0[e] : p1[e - 4]), __float_as_int(h1), 0x138, 0xf, 0xf, false));
+          const float h3 = __int_as_float(__builtin_amdgcn_update_dpp(
+              __float_as_int(e < 4 ? o0[e] : o1[e - 4]), __float_as_int(h2), 0x138, 0xf, 0xf, false));
+          const floatx4 t = *reinterpret_cast<const floatx4*>(TP + 4 * (c0 + e));
+          y[e] = conv_swish(t, h3, h2, h1, x);
         }
       };
-      auto qk = [&](uint2v (&xin)[NKB][2], int off) {
-        float y[NKB][2][4];
+      auto store8 = [&](int c0, const float* z) {
+        uint4v u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          u[e] = (unsigned)__builtin_bit_cast(unsigned short, (bf16)(okr ? z[2 * e] : 0.f)) |
+                 ((unsigned)__builtin_bit_cast(unsigned short, (bf16)(okr ? z[2 * e + 1] : 0.f)) << 16);
+        *reinterpret_cast<uint4v*>(XR + row * ldX + c0) = u;
+      };
+      // q or k half of this wave
+      {
+        const int ten = w4 >> 1, half = w4 & 1;
+        const int cc0 = half * (DK / 2);
+        const int off = ten * DK + cc0;
         float ss = 0.f;
+        for (int gi = 0; gi < DK / 16; ++gi) {
+          float y[8];
+          group8(off + 8 * gi, y);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            group(off + 32 * kb + 16 * hf + 4 * g, y[kb][hf]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ss = __builtin_fmaf(y[kb][hf][e], y[kb][hf][e], ss);
-          }
-        const float rn = __builtin_amdgcn_rsqf(rows4_sum(ss) + pa.conv.eps);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            float z[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) z[e] = okc ? y[kb][hf][e] * rn : 0.f;  // padding: 0
-            xin[kb][hf] = pack4(z);
-          }
-      };
-      qk(qin, 0);
-      qk(kin, DK);
-#pragma unroll
-      for (int j = 0; j < NVL; ++j) {
-        const int c = 2 * DK + (DV / 4) * g + 8 * j;
-        float z[8];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          float h1[4], h2[4], h3[4];
-          hist4(1, c + 4 * hh, h1);
-          hist4(2, c + 4 * hh, h2);
-          hist4(3, c + 4 * hh, h3);
-          const uint2v xr = *reinterpret_cast<const uint2v*>(XR + r * ldX + c + 4 * hh);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const floatx4 t = *reinterpret_cast<const floatx4*>(TP + 4 * (c + 4 * hh + e));
-            z[4 * hh + e] = okc ? conv_swish(t, h3[e], h2[e], h1[e], bfv(xr[e >> 1], e & 1)) : 0.f;
-          }
+          for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(y[e], y[e], ss);
         }
-        const uint2v lo = pack4(z), hi = pack4(z + 4);
-        vin[j] = uint4v{lo[0], lo[1], hi[0], hi[1]};
+        SS[w4 * 64 + row] = ss;
+        __syncthreads();
+        // the two halves in a fixed order, so both waves form the same norm
+        const float tot = SS[(w4 & 2) * 64 + row] + SS[((w4 & 2) + 1) * 64 + row];
+        const float rn = __builtin_amdgcn_rsqf(tot + pa.conv.eps);
+        for (int gi = 0; gi < DK / 16; ++gi) {
+          float y[8];
+          group8(off + 8 * gi, y);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] *= rn;
+          store8(off + 8 * gi, y);
+        }
       }
+      // v quarter of this wave
+      {
+        const int cc0 = w4 * (DV / 4);
+        for (int gi = 0; gi < DV / 32; ++gi) {
+          float y[8];
+          group8(2 * DK + cc0 + 8 * gi, y);
+          store8(2 * DK + cc0 + 8 * gi, y);
+        }
+      }
+      __syncthreads();
+      // the results in the operand layout
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int c = 32 * kb + 16 * hf + 4 * g;
+          qin[kb][hf] = *reinterpret_cast<const uint2v*>(XR + r * ldX + c);
+          kin[kb][hf] = *reinterpret_cast<const uint2v*>(XR + r * ldX + DK + c);
+        }
+#pragma unroll
+      for (int j = 0; j < NVL; ++j)
+        vin[j] = *reinterpret_cast<const uint4v*>(XR + r * ldX + 2 * DK + (DV / 4) * g + 8 * j);
     }
 
     // ---- 1. within-tile decay products P (inclusive scan over the 16 tokens)
