@@ -247,8 +247,27 @@ def main():
                                         conv_state=pl.conv_state), 10)
     py = torch.empty(B, T, H, D, dtype=torch.bfloat16, device=d)
     epi_ms = timed(lambda: kda.epilogue(o, pl.g, pl.norm_w, y=py), 10)
+    # the whole layer over the prefill in one call (prologue inside the first
+    # pass), against the standalone prologue, recurrence and epilogue composed
+    pcs = torch.empty_like(pl.conv_state)
+    lo_ = torch.empty(B, T, H, D, dtype=torch.float32, device=d)
+    lay_ms = timed(lambda: kda.prefill_layer(pl.xq, pl.xk, pl.xv, pl.wq, pl.wk, pl.wv, inp.alpha,
+                                             inp.beta, pl.g, pl.norm_w, conv_state=pl.conv_state,
+                                             initial_state=inp.state, final_state=fs,
+                                             conv_state_out=pcs, o=lo_, y=py, workspace=ws),
+                   10)
+
+    def layer_composed():
+        q3, k3, v3, _ = kda.prologue(pl.xq, pl.xk, pl.xv, pl.wq, pl.wk, pl.wv,
+                                     conv_state=pl.conv_state, conv_state_out=pcs)
+        kda.prefill_chunked(q3, k3, v3, inp.alpha, inp.beta, initial_state=inp.state,
+                            final_state=fs, o=lo_, schedule=schedule, workspace=ws)
+        kda.epilogue(lo_, pl.g, pl.norm_w, y=py)
+
+    lay_comp_ms = timed(layer_composed, 10)
     print(f"bench: layer decode step {layer_ms * 1e3:.1f} us fused vs {comp_ms * 1e3:.1f} us "
-          f"composed; prefill prologue {pro_ms * 1e3:.1f} us, epilogue {epi_ms * 1e3:.1f} us",
+          f"composed; prefill prologue {pro_ms * 1e3:.1f} us, epilogue {epi_ms * 1e3:.1f} us; "
+          f"layer prefill {lay_ms:.3f} ms in one call vs {lay_comp_ms:.3f} ms composed",
           file=sys.stderr, flush=True)
 
     # one device's share of the layer under an 8-way head split (12 heads): the
@@ -340,6 +359,7 @@ def main():
                   "decode_workload": "decode_b64: prologue (ShortConv 4 + Swish + L2Norm, conv "
                                      "state), step, RMSNorm x sigmoid gate; bf16 y",
                   "prefill_prologue_us": pro_ms * 1e3, "prefill_epilogue_us": epi_ms * 1e3,
+                  "prefill_layer_ms": lay_ms, "prefill_layer_composed_ms": lay_comp_ms,
                   "prefill_workload": "k3_prefill_8k, standalone kernels (bf16 x, q/k/v, y; "
                                       "fp32 o)"},
         "prefill_one_device_share": {
