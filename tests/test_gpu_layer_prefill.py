@@ -128,3 +128,32 @@ def test_empty_call_hands_states_through():
                                     L.norm_w, conv_state=L.conv_state, initial_state=s0)
     torch.cuda.synchronize()
     assert torch.equal(s, s0) and torch.equal(cs, L.conv_state)
+
+
+def test_k3_8k_layer_sampled_heads():
+    """The 8K layer (B=1, T=8192, H=96, d=128) in one call, as the bench times
+    it: the oracle chain on 4 heads spread over the head axis (all tokens), the
+    composed calls on all heads."""
+    d = dev()
+    B, T, H, D = 1, 8192, 96, 128
+    L = synth.make_layer(B, T, H, D, D, seed=1360, device=d)
+    r = synth.make_dense(B, T, H, D, D, seed=1361, state_std=0.02, device=d)
+    y, o, s, cs = kda.prefill_layer(L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, r.alpha, r.beta, L.g,
+                                    L.norm_w, conv_state=L.conv_state, initial_state=r.state)
+    q, k, v, _ = kda.prologue(L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, conv_state=L.conv_state)
+    o2, s2 = kda.prefill_chunked(q, k, v, r.alpha, r.beta, initial_state=r.state,
+                                 schedule="two_pass")
+    y2 = kda.epilogue(o2, L.g, L.norm_w, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert rel(y.cpu(), y2.cpu()) <= TOL_BF16 and rel(s.cpu(), s2.cpu()) <= TOL_BF16
+    heads = [3, 30, 61, 94]
+    sel = lambda x: _f(x[:, :, heads])  # noqa: E731
+    st = L.conv_state[:, :, heads].cpu()
+    rq, rk, rv, rcs = oracle.prologue(sel(L.xq), sel(L.xk), sel(L.xv), L.wq[heads].cpu(),
+                                      L.wk[heads].cpu(), L.wv[heads].cpu(), state=st)
+    ro, rs = oracle.recurrent(rq, rk, rv, r.alpha[:, :, heads].cpu().numpy(),
+                              r.beta[:, :, heads].cpu(), initial_state=r.state[:, heads].cpu())
+    ry = oracle.rmsnorm_gate(ro, sel(L.g), L.norm_w.cpu())
+    assert rel(y[:, :, heads].cpu(), ry) <= TOL_LAYER
+    assert rel(s[:, heads].cpu(), rs) <= TOL_LAYER
+    assert np.array_equal(cs[:, :, heads].cpu().numpy(), rcs.astype(np.float32))
