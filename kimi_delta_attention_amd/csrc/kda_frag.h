@@ -111,6 +111,16 @@ __device__ __forceinline__ void split4_pack(const float* x, uint2v& hi, uint2v& 
   lo = uint2v{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
 }
 
+// a (rounded once) times b = bh + bl: the A operand W of W S when the gate
+// decays (its single rounding then stays within the error budget; the B side,
+// the state, does not)
+__device__ __forceinline__ floatx4 mma_a1(const bf16x8& a, const bf16x8& bh, const bf16x8& bl,
+                                          floatx4 c) {
+  c = mfma_bf16(a, bh, c);
+  c = mfma_bf16(a, bl, c);
+  return c;
+}
+
 __device__ __forceinline__ floatx4 mma_ab(const bf16x8& ah, const bf16x8& al, const bf16x8& bh,
                                           const bf16x8& bl, floatx4 c) {
   c = mfma_bf16(ah, bh, c);
@@ -119,6 +129,18 @@ __device__ __forceinline__ floatx4 mma_ab(const bf16x8& ah, const bf16x8& al, co
   return c;
 }
 
+// W S with W rounded once (decaying gates) or split (no decay: the state never
+// forgets, so the rounding of W would accumulate), the same products in the
+// same order in both schedules
+template <bool WS>
+__device__ __forceinline__ floatx4 mma_w(const bf16x8& wh, const bf16x8& wl, const bf16x8& bh,
+                                         const bf16x8& bl, floatx4 c) {
+  if constexpr (WS) return mma_ab(wh, wl, bh, bl, c);
+  return mma_a1(wh, bh, bl, c);
+}
+template <int KIND>
+constexpr bool w_split() { return KIND == GATE_NONE; }
+
 // Per-chunk operand images written by the first pass of the two-pass prefill
 // and read by the state pass.  Every image is a sequence of 1 KiB frames; a
 // frame is one 16-byte register fragment per lane (lane l at byte 16 l), so a
@@ -126,7 +148,9 @@ __device__ __forceinline__ floatx4 mma_ab(const bf16x8& ah, const bf16x8& al, co
 // Frames (w = token tile of the chunk, kb = 32-wide k block):
 //   W  [w][kb < DK/32][hi, lo]   A operand of W S (row = token, k = channel
 //                                position 32kb + 8g + 4h + i <-> channel
-//                                32kb + 16h + 4g + i)
+//                                32kb + 16h + 4g + i); the low part only for
+//                                the gate without decay (w_split): with decay,
+//                                W rounded once is within the error budget
 //   Q  [w][kb < DK/32]           A operand of (Gamma*Q) S, same positions
 //   M  [w][kb < 2][hi, lo]       A operand of Mqk P (k = token position)
 //   K  [rt < DK/16][kb < 2][hi, lo]  A operand of Ktil^T P for state rows

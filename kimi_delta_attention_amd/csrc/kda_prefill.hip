@@ -606,7 +606,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
           const bf16x8 bl = frag_ld(ST + loS, ldS, vh0 + 16 * c + tr, 32 * kb, g);
           floatx4& aw = kb < NKH ? accW[c] : accW2[c];
           floatx4& ao = kb < NKH ? accO[c] : accO2[c];
-          aw = mma_ab(wh[kb], wl[kb], bh, bl, aw);
+          aw = mma_w<w_split<KIND>()>(wh[kb], wl[kb], bh, bl, aw);
           ao = mfma_bf16(aq, bh, ao);
           ao = mfma_bf16(aq, bl, ao);
         }

@@ -671,7 +671,7 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
           }
         }
         put_frame(im, IM::w_frame(w, kp, 0), lane_x, wh);
-        put_frame(im, IM::w_frame(w, kp, 1), lane_x, wl);
+        if constexpr (w_split<KIND>()) put_frame(im, IM::w_frame(w, kp, 1), lane_x, wl);
       }
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt) {

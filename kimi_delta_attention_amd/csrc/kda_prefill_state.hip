@@ -163,7 +163,7 @@ __device__ __forceinline__ int seg_count(int nseg, int c_lo, int c_hi) {
 // the normal workgroup of segment s enters from seg_in[s] (the combine
 // kernel's entry states) and only the last segment writes the carried state.
 // With ns = 1, segment 0 runs exactly as the unsegmented pass.
-template <int DK, int DV, int BV, typename TOut, bool SUMMARY>
+template <int DK, int DV, int BV, typename TOut, bool SUMMARY, bool WS>
 __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     const unsigned char* __restrict__ img, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ cu_seqlens, const float* s_init, float* carry,
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         op.wh[kb] = *frame_ptr<bf16x8>(b, IM::w_frame(w, kb, 0), lane);
-        op.wl[kb] = *frame_ptr<bf16x8>(b, IM::w_frame(w, kb, 1), lane);
+        if constexpr (WS) op.wl[kb] = *frame_ptr<bf16x8>(b, IM::w_frame(w, kb, 1), lane);
       }
     };
     auto fetch_r = [&](int c, Ops& op) {
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
           const bf16x8 bh = frag_ld(ST, ldS, 16 * vt + tr, 32 * kb, g);
           const bf16x8 bl = frag_ld(ST + loS, ldS, 16 * vt + tr, 32 * kb, g);
           floatx4& acc = kb < NKH ? a0[vt] : a1[vt];
-          acc = mma_ab(op.wh[kb], op.wl[kb], bh, bl, acc);
+          acc = mma_w<WS>(op.wh[kb], op.wl[kb], bh, bl, acc);
         }
       const int pos = 32 * (w >> 1) + 8 * g + 4 * (w & 1);
 #pragma unroll
@@ -659,13 +659,13 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restr
 // is bound by frame fetches per compute unit, not by idle compute units.
 constexpr int BV_STATE = 64;
 
-template <int DK, int DV, typename TOut, bool SUMMARY>
-hipError_t launch_state_t(const PrefillArgs& a, const unsigned char* img, const int32_t* chunk_off,
+template <int DK, int DV, typename TOut, bool SUMMARY, bool WS>
+hipError_t launch_state_w(const PrefillArgs& a, const unsigned char* img, const int32_t* chunk_off,
                           float* carry, long long tok_lo, long long tok_hi, int cap,
                           const SegmentArgs& sg) {
   constexpr int BV = BV_STATE;
   using L = StatePlan<DK, BV>;
-  auto kern = prefill_state_kernel<DK, DV, BV, TOut, SUMMARY>;
+  auto kern = prefill_state_kernel<DK, DV, BV, TOut, SUMMARY, WS>;
   static bool attr_set = false;  // per instantiation; idempotent if raced
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -680,6 +680,16 @@ hipError_t launch_state_t(const PrefillArgs& a, const unsigned char* img, const 
                      a.cu_seqlens, a.initial_state, carry, (TOut*)a.o, a.n_seq, a.T, a.H, tok_lo,
                      tok_hi, cap, sg.nseg, sg.seg_in, sg.summ);
   return hipGetLastError();
+}
+
+// W split in the images only for the gate without decay
+template <int DK, int DV, typename TOut, bool SUMMARY>
+hipError_t launch_state_t(const PrefillArgs& a, const unsigned char* img, const int32_t* chunk_off,
+                          float* carry, long long tok_lo, long long tok_hi, int cap,
+                          const SegmentArgs& sg) {
+  return a.gate.kind == GATE_NONE
+             ? launch_state_w<DK, DV, TOut, SUMMARY, true>(a, img, chunk_off, carry, tok_lo, tok_hi, cap, sg)
+             : launch_state_w<DK, DV, TOut, SUMMARY, false>(a, img, chunk_off, carry, tok_lo, tok_hi, cap, sg);
 }
 
 template <int DK, int DV>
