@@ -203,7 +203,7 @@ kda_status kda_prefill_segmented(const void* q, const void* k, const void* v, kd
     return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
   if (n_seq > 0 && qkv_dtype != KDA_BF16)
     return fail(KDA_ERR_UNSUPPORTED, "the segmented schedule needs bf16 q, k, v");
-  if (n_seq > 0) {
+  if (n_seq > 0 && (T > 0 || cu_seqlens)) {  // without tokens only the states are handed on
     const size_t need = kda::prefill_segmented_bytes(n_seq, H, Dk, Dv, n_segments);
     if (need == 0 && kda::prefill_supported(true, Dk, Dv) && H > 0)
       return fail(KDA_ERR_INVALID_ARGUMENT, "sizes too large for the segmented schedule");

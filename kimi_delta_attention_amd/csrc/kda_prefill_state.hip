@@ -421,10 +421,10 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       fetch_r(next_of(c), nx);
       // ---- O += Mqk P and the state update of this wave's tiles, from the
       // same P fragments (the Mqk block after the tile enters as zeros)
-      bf16x8 mh1 = op.mh[1], ml1 = op.ml[1];
-      if (w < 2) {
-        mh1 = bf16x8{};
-        ml1 = bf16x8{};
+      bf16x8 mh1{}, ml1{};  // (no output in the summary mode: its frames are not fetched)
+      if (!SUMMARY && w >= 2) {
+        mh1 = op.mh[1];
+        ml1 = op.ml[1];
       }
 #pragma unroll
       for (int j = 0; j < KVT; ++j)

@@ -133,6 +133,7 @@ def _segmented(**over):
     (dict(cu=FAKE + 2), INVALID),
     (dict(n=-1), INVALID),
     (dict(n=0, q=None, k=None, v=None, o=None, ws=None, wsb=0), OK),
+    (dict(T=0, ws=None, wsb=0), OK),  # no tokens and no final state: nothing to do
 ])
 def test_segmented_validation(over, expect):
     assert _segmented(**over) == expect
