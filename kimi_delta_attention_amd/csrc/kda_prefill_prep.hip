@@ -197,20 +197,44 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     const size_t thc = (size_t)(d.tok0 + r) * H + d.hd;
     floatx4 a4[NKB][2];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
+      // k and q in 16 bytes per lane: row gl of the wave reads channels
+      // 8 (gl >> 1) + 16 (gl & 1) .. + 8 of the block, so a token's 32
+      // channels come in one 64-byte piece (order_in puts them in place)
+      const int c8 = 32 * kb + 8 * (gl >> 1) + 16 * (gl & 1);
+      const uint4v z4{0u, 0u, 0u, 0u};
+      const uint4v k8 = okc ? *reinterpret_cast<const uint4v*>(k + thc * DK + c8) : z4;
+      const uint4v q8 = okc ? *reinterpret_cast<const uint4v*>(q + thc * DK + c8) : z4;
+      kin[kb][0] = uint2v{k8[0], k8[1]};
+      kin[kb][1] = uint2v{k8[2], k8[3]};
+      qin[kb][0] = uint2v{q8[0], q8[1]};
+      qin[kb][1] = uint2v{q8[2], q8[3]};
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int c = 32 * kb + 16 * hf + 4 * gl;
-        kin[kb][hf] = okc ? *reinterpret_cast<const uint2v*>(k + thc * DK + c) : uint2v{0u, 0u};
-        qin[kb][hf] = okc ? *reinterpret_cast<const uint2v*>(q + thc * DK + c) : uint2v{0u, 0u};
-        a4[kb][hf] = gate_load4<KIND>(gate, okc, thc, DK, c);
-      }
+      for (int hf = 0; hf < 2; ++hf) a4[kb][hf] = gate_load4<KIND>(gate, okc, thc, DK, 32 * kb + 16 * hf + 4 * gl);
+    }
     gate_finish_blocks<KIND, NKB>(gate, KIND == GATE_BOUNDED ? expf(gate.a_log[d.hd]) : 1.f, a4);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 8; ++i) Pv[kb][i] = a4[kb][i >> 2][i & 3];
     bt = okc ? beta[thc] : 0.f;
+  };
+  // A permlane16 swap of the middle halves of the loaded pieces between rows
+  // 0 / 1 and 2 / 3 leaves each lane its 4-channel groups 4 gl and 16 + 4 gl.
+  // Done after every load of the item has been issued: its wait for the k and
+  // q loads then holds back no other load.
+  auto order_in = [&]() {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const auto sk = __builtin_amdgcn_permlane16_swap(kin[kb][0][a], kin[kb][1][a], false, false);
+        const auto sq = __builtin_amdgcn_permlane16_swap(qin[kb][0][a], qin[kb][1][a], false, false);
+        kin[kb][0][a] = sk[0];
+        kin[kb][1][a] = sk[1];
+        qin[kb][0][a] = sq[0];
+        qin[kb][1][a] = sq[1];
+      }
   };
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     // Lane index behind an empty asm, so that the per-lane addresses are
@@ -231,12 +255,18 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     const bool okc = r < nv;
     const size_t thc = (size_t)(tok0 + r) * H + hd;
 
-    // v of this lane's token (DV / 4 values), staged in phase 5
+    // v of the wave's token tile, staged in phase 5: load j covers whole rows
+    // (DV / 8 lanes of 16 bytes per row, rows 16 w + VRJ j + lane / (DV / 8)),
+    // so that each row is read in one coalesced piece
+    constexpr int VLR = DV / 8, VRJ = 64 / VLR;
+    const int vrow = 16 * w + lane_x / VLR, vcol = 8 * (lane_x % VLR);
     uint4v vin[NVL];
 #pragma unroll
-    for (int j = 0; j < NVL; ++j)
-      vin[j] = okc ? *reinterpret_cast<const uint4v*>(v + thc * DV + (DV / 4) * g + 8 * j)
-                   : uint4v{0u, 0u, 0u, 0u};
+    for (int j = 0; j < NVL; ++j) {
+      const int rv = vrow + VRJ * j;
+      vin[j] = rv < nv ? *reinterpret_cast<const uint4v*>(v + ((size_t)(tok0 + rv) * H + hd) * DV + vcol)
+                       : uint4v{0u, 0u, 0u, 0u};
+    }
 
     // prologue: the three inputs before the chunk (fp32)
     constexpr int HPT = (3 * SWP + NTH_P - 1) / NTH_P;
@@ -270,6 +300,8 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
       }
     }
 
+    order_in();
+
     // ---- prologue (layer prefill): ShortConv over the three previous
     // inputs, Swish, and the L2Norm of q and k.  The raw rows go to LDS; then
     // lane l of every wave takes token l of the chunk over a range of
@@ -293,7 +325,7 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
         }
 #pragma unroll
       for (int j = 0; j < NVL; ++j)
-        *reinterpret_cast<uint4v*>(XR + r * ldX + 2 * DK + (DV / 4) * g + 8 * j) = vin[j];
+        *reinterpret_cast<uint4v*>(XR + (vrow + VRJ * j) * ldX + 2 * DK + vcol) = vin[j];
 #pragma unroll
       for (int i = 0; i < HPT; ++i) {
         const int idx = tid_x + NTH_P * i;
@@ -381,7 +413,7 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
         }
 #pragma unroll
       for (int j = 0; j < NVL; ++j)
-        vin[j] = *reinterpret_cast<const uint4v*>(XR + r * ldX + 2 * DK + (DV / 4) * g + 8 * j);
+        vin[j] = *reinterpret_cast<const uint4v*>(XR + (vrow + VRJ * j) * ldX + 2 * DK + vcol);
     }
 
     // ---- 1. within-tile decay products P (inclusive scan over the 16 tokens)
@@ -638,7 +670,7 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     }
 #pragma unroll
     for (int j = 0; j < NVL; ++j)
-      *reinterpret_cast<uint4v*>(VS + r * ldV + (DV / 4) * g + 8 * j) = vin[j];
+      *reinterpret_cast<uint4v*>(VS + (vrow + VRJ * j) * ldV + vcol) = vin[j];
     __syncthreads();
     {
       bf16x8 tbh[2], tbl[2];
