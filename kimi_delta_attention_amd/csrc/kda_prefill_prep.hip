@@ -300,7 +300,7 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
       }
     }
 
-    order_in();
+    if constexpr (!PRO) order_in();  // the prologue reads the rows back in place
 
     // ---- prologue (layer prefill): ShortConv over the three previous
     // inputs, Swish, and the L2Norm of q and k.  The raw rows go to LDS; then
@@ -316,13 +316,13 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     if constexpr (PRO) {
       __syncthreads();  // the item before is done with R and GK
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int c = 32 * kb + 16 * hf + 4 * g;
-          *reinterpret_cast<uint2v*>(XR + r * ldX + c) = qin[kb][hf];
-          *reinterpret_cast<uint2v*>(XR + r * ldX + DK + c) = kin[kb][hf];
-        }
+      for (int kb = 0; kb < NKB; ++kb) {  // the pieces as loaded (8 channels from c8)
+        const int c8 = 32 * kb + 8 * (g >> 1) + 16 * (g & 1);
+        *reinterpret_cast<uint4v*>(XR + r * ldX + c8) =
+            uint4v{qin[kb][0][0], qin[kb][0][1], qin[kb][1][0], qin[kb][1][1]};
+        *reinterpret_cast<uint4v*>(XR + r * ldX + DK + c8) =
+            uint4v{kin[kb][0][0], kin[kb][0][1], kin[kb][1][0], kin[kb][1][1]};
+      }
 #pragma unroll
       for (int j = 0; j < NVL; ++j)
         *reinterpret_cast<uint4v*>(XR + (vrow + VRJ * j) * ldX + 2 * DK + vcol) = vin[j];
