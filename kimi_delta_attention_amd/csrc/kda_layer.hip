@@ -19,6 +19,7 @@ namespace {
 
 constexpr int TB = 64;         // tokens per prologue wave
 constexpr int ROWS_EPI = 8;    // rows per epilogue wave
+constexpr int PF_ROWS = 8;     // prologue rows in flight per wave
 
 // The sequence holding packed token t: the last s with cu[s] <= t (t below
 // cu[n_seq]; such an s has cu[s + 1] > t, so it is not empty).
@@ -65,6 +66,41 @@ __device__ void prologue_rows(const T* __restrict__ x, T* __restrict__ y,
     }
   };
   init_hist(t0);
+  if (t1 - t0 == TB && t1 < end) {
+    // A whole block inside one sequence that does not hold its last token
+    // (no sequence change, no state row): PF_ROWS rows in flight per wave.
+    // Slot i of the ring holds row tb + i of the group tb and is refilled
+    // with row tb + i + PF_ROWS once read; the group is unrolled and every
+    // step issues exactly one load and one store, so the slots are fixed
+    // registers and a row is waited for only when it is used (a row past the
+    // block re-reads its last row).
+    T ring[PF_ROWS][CPL];  // as loaded: converted when used, so only the use waits
+#pragma unroll
+    for (int i = 0; i < PF_ROWS; ++i)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) ring[i][c] = x[((size_t)(t0 + i) * H + h) * D + CPL * lane + c];
+    for (int gi = 0; gi < TB / PF_ROWS; ++gi) {
+#pragma unroll
+      for (int i = 0; i < PF_ROWS; ++i) {
+        const long long t = t0 + PF_ROWS * gi + i;
+        const long long tn = t + PF_ROWS < t1 ? t + PF_ROWS : t1 - 1;
+        float xr[CPL], out[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) xr[c] = to_f(ring[i][c]);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) ring[i][c] = x[((size_t)tn * H + h) * D + CPL * lane + c];
+        prologue_row<CPL, NORM>(hist, xr, w, eps, out);
+        row_store<T, CPL>(y + ((size_t)t * H + h) * D, lane, out);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          hist[0][c] = hist[1][c];
+          hist[1][c] = hist[2][c];
+          hist[2][c] = xr[c];
+        }
+      }
+    }
+    return;
+  }
   for (long long t = t0; t < t1; ++t) {
     if (t >= end) {  // next non-empty sequence
       do {
