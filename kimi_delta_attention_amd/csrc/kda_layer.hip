@@ -20,6 +20,7 @@ namespace {
 constexpr int TB = 64;         // tokens per prologue wave
 constexpr int ROWS_EPI = 8;    // rows per epilogue wave
 constexpr int PF_ROWS = 8;     // prologue rows in flight per wave
+static_assert(TB % PF_ROWS == 0, "whole groups of rows per block");
 
 // The sequence holding packed token t: the last s with cu[s] <= t (t below
 // cu[n_seq]; such an s has cu[s + 1] > t, so it is not empty).
@@ -69,8 +70,9 @@ __device__ void prologue_rows(const T* __restrict__ x, T* __restrict__ y,
   if (t1 - t0 == TB && t1 < end) {
     // A whole block inside one sequence that does not hold its last token
     // (no sequence change, no state row): PF_ROWS rows in flight per wave.
-    // Slot i of the ring holds row tb + i of the group tb and is refilled
-    // with row tb + i + PF_ROWS once read; the group is unrolled and every
+    // Slot i of the ring holds row t0 + PF_ROWS gi + i of group gi and is
+    // refilled with the same slot's row of group gi + 1 once read; the group
+    // is unrolled and every
     // step issues exactly one load and one store, so the slots are fixed
     // registers and a row is waited for only when it is used (a row past the
     // block re-reads its last row).
