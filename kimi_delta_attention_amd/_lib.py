@@ -152,6 +152,31 @@ def _need(t: torch.Tensor, name: str, dtype=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _out(t: torch.Tensor, name: str, shape: tuple, dtypes: tuple, device):
+    """A caller-supplied output: a contiguous device tensor on `device` of exactly
+    `shape` and one of `dtypes` (the kernels write it through a raw pointer)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    _need(t, name, None, device)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be one of {dtypes}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+_FLOAT_OUT = (torch.float32, torch.bfloat16)
+_F32 = (torch.float32,)
+
+
+def _final_state(final_state, shape, dev):
+    if isinstance(final_state, torch.Tensor):
+        return _out(final_state, "final_state", shape, _F32, dev)
+    if final_state:
+        return torch.empty(shape, dtype=torch.float32, device=dev)
+    return None
+
+
 def _gate(kind: str, alpha, a_log, g_min: float, lead: tuple, H: int, Dk: int, dev):
     """Checks the decay tensor against its gate kind and returns the kda_gate
     descriptor.  Per-channel kinds take [*lead, H, Dk], 'scalar' [*lead, H],
@@ -241,14 +266,8 @@ def prefill_chunked(q, k, v, alpha, beta, initial_state=None, out_dtype=torch.fl
     if o is None:
         o = torch.empty(B, T, H, Dv, dtype=out_dtype, device=dev)
     else:
-        _need(o, "o", None, dev)
-    if isinstance(final_state, torch.Tensor):
-        fs = final_state
-        _need(fs, "final_state", torch.float32, dev)
-    elif final_state:
-        fs = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev)
-    else:
-        fs = None
+        _out(o, "o", (B, T, H, Dv), _FLOAT_OUT, dev)
+    fs = _final_state(final_state, (B, H, Dk, Dv), dev)
     ws = _workspace(schedule, workspace, q.dtype, B, B * T,
                     (workspace_size(B, T, H, Dk, Dv), B, H, Dk, Dv), dev)
     _check(load().kda_prefill_chunked_gated(
@@ -274,9 +293,13 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None,
         raise ValueError("packed inputs have B == 1")
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, q.dtype, dev)
+    if k.shape != q.shape or v.shape != (1, NT, H, Dv) or beta.shape != (1, NT, H):
+        raise ValueError("inconsistent shapes")
     g = _gate(gate, alpha, a_log, g_min, (1, NT), H, Dk, dev)
     _need(beta, "beta", torch.float32, dev)
     _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be [N + 1]")
     N = cu_seqlens.numel() - 1
     if initial_state is not None:
         _need(initial_state, "initial_state", torch.float32, dev)
@@ -284,12 +307,9 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None,
             raise ValueError("initial_state must be [N, H, Dk, Dv]")
     if o is None:
         o = torch.empty(1, NT, H, Dv, dtype=out_dtype, device=dev)
-    if isinstance(final_state, torch.Tensor):
-        fs = final_state
-    elif final_state:
-        fs = torch.empty(N, H, Dk, Dv, dtype=torch.float32, device=dev)
     else:
-        fs = None
+        _out(o, "o", (1, NT, H, Dv), _FLOAT_OUT, dev)
+    fs = _final_state(final_state, (N, H, Dk, Dv), dev)
     ws = _workspace(schedule, workspace, q.dtype, N, NT,
                     (varlen_workspace_size(N, NT, H, Dk, Dv), N, H, Dk, Dv), dev)
     _check(load().kda_prefill_varlen_gated(
@@ -342,14 +362,8 @@ def prefill_segmented(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
     if o is None:
         o = torch.empty(B, T, H, Dv, dtype=out_dtype, device=dev)
     else:
-        _need(o, "o", None, dev)
-    if isinstance(final_state, torch.Tensor):
-        fs = final_state
-        _need(fs, "final_state", torch.float32, dev)
-    elif final_state:
-        fs = torch.empty(n_seq, H, Dk, Dv, dtype=torch.float32, device=dev)
-    else:
-        fs = None
+        _out(o, "o", (B, T, H, Dv), _FLOAT_OUT, dev)
+    fs = _final_state(final_state, (n_seq, H, Dk, Dv), dev)
     if n_segments is None:
         n_segments = segments_preferred(q.dtype, n_seq, tokens, H, Dk, Dv)
     need = segmented_workspace_size(n_seq, H, Dk, Dv, n_segments)
@@ -359,6 +373,8 @@ def prefill_segmented(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _need(workspace, "workspace", torch.uint8, dev)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
     _check(load().kda_prefill_segmented(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), ctypes.byref(g), _ptr(beta), _ptr(cu_seqlens), n_seq,
         T if cu_seqlens is None else tokens, _ptr(initial_state), _ptr(fs), _ptr(o), _dt(o), H, Dk,
@@ -384,6 +400,8 @@ def decode_step(q, k, v, alpha, beta, state, out_dtype=torch.float32,
         raise ValueError("inconsistent shapes")
     if o is None:
         o = torch.empty(B, H, Dv, dtype=out_dtype, device=dev)
+    else:
+        _out(o, "o", (B, H, Dv), _FLOAT_OUT, dev)
     _check(load().kda_decode_step_gated(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), ctypes.byref(g), _ptr(beta), _ptr(state), _ptr(o),
         _dt(o), B, H, Dk, Dv, _stream(dev)))
@@ -422,7 +440,7 @@ def decode_verify(q, k, v, alpha, beta, state, out_dtype=torch.float32,
     if o is None:
         o = torch.empty(B, N, H, Dv, dtype=out_dtype, device=dev)
     else:
-        _need(o, "o", None, dev)
+        _out(o, "o", (B, N, H, Dv), _FLOAT_OUT, dev)
     _check(load().kda_decode_verify(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), ctypes.byref(g), _ptr(beta), _ptr(state), _ptr(o),
         _dt(o), B, N, H, Dk, Dv, _stream(dev)))
@@ -481,8 +499,7 @@ def prologue(xq, xk, xv, wq, wk, wv, conv_state=None, cu_seqlens=None, eps: floa
         if tuple(conv_state.shape) != sw:
             raise ValueError(f"conv_state must be {sw}")
     if isinstance(conv_state_out, torch.Tensor):
-        so = conv_state_out
-        _need(so, "conv_state_out", torch.float32, dev)
+        so = _out(conv_state_out, "conv_state_out", sw, _F32, dev)
     elif conv_state_out:
         so = torch.empty(sw, dtype=torch.float32, device=dev)
     else:
@@ -507,7 +524,7 @@ def epilogue(o, g, w, eps: float = 1e-5, out_dtype=None, y: torch.Tensor | None 
     if y is None:
         y = torch.empty(o.shape, dtype=out_dtype or o.dtype, device=dev)
     else:
-        _need(y, "y", None, dev)
+        _out(y, "y", tuple(o.shape), _FLOAT_OUT, dev)
     _check(load().kda_epilogue(_ptr(o), _dt(o), _ptr(g), _dt(g), _ptr(w), float(eps), _ptr(y),
                                _dt(y), tokens, H, Dv, _stream(dev)))
     return y
@@ -547,7 +564,7 @@ def decode_layer(mode: str, xq, xk, xv, wq, wk, wv, conv_state, alpha, beta, sta
         if y is None:
             y = torch.empty(B, N, H, Dv, dtype=out_dtype, device=dev)
         else:
-            _need(y, "y", None, dev)
+            _out(y, "y", (B, N, H, Dv), _FLOAT_OUT, dev)
     _check(load().kda_decode_layer(
         DECODE_MODES[mode], _ptr(xq), _ptr(xk), _ptr(xv), _dt(xq), ctypes.byref(c),
         _ptr(conv_state), ctypes.byref(gd), _ptr(beta), _ptr(state), ctypes.byref(og), _ptr(y),
@@ -590,8 +607,7 @@ def prefill_layer(xq, xk, xv, wq, wk, wv, alpha, beta, g, norm_w, conv_state=Non
         if tuple(conv_state.shape) != sw:
             raise ValueError(f"conv_state must be {sw}")
     if isinstance(conv_state_out, torch.Tensor):
-        so = conv_state_out
-        _need(so, "conv_state_out", torch.float32, dev)
+        so = _out(conv_state_out, "conv_state_out", sw, _F32, dev)
     elif conv_state_out:
         so = torch.empty(sw, dtype=torch.float32, device=dev)
     else:
@@ -600,13 +616,7 @@ def prefill_layer(xq, xk, xv, wq, wk, wv, alpha, beta, g, norm_w, conv_state=Non
         _need(initial_state, "initial_state", torch.float32, dev)
         if initial_state.shape != (n_seq, H, Dk, Dv):
             raise ValueError("initial_state must be [n_seq, H, Dk, Dv]")
-    if isinstance(final_state, torch.Tensor):
-        fs = final_state
-        _need(fs, "final_state", torch.float32, dev)
-    elif final_state:
-        fs = torch.empty(n_seq, H, Dk, Dv, dtype=torch.float32, device=dev)
-    else:
-        fs = None
+    fs = _final_state(final_state, (n_seq, H, Dk, Dv), dev)
     _need(g, "g", xq.dtype, dev)
     _need(norm_w, "norm_w", torch.float32, dev)
     if g.shape != (B, T, H, Dv) or tuple(norm_w.shape) != (Dv,):
@@ -615,11 +625,11 @@ def prefill_layer(xq, xk, xv, wq, wk, wv, alpha, beta, g, norm_w, conv_state=Non
     if o is None:
         o = torch.empty(B, T, H, Dv, dtype=torch.float32, device=dev)
     else:
-        _need(o, "o", torch.float32, dev)
+        _out(o, "o", (B, T, H, Dv), _F32, dev)
     if y is None:
         y = torch.empty(B, T, H, Dv, dtype=out_dtype, device=dev)
     else:
-        _need(y, "y", None, dev)
+        _out(y, "y", (B, T, H, Dv), _FLOAT_OUT, dev)
     need = segmented_workspace_size(n_seq, H, Dk, Dv, n_segments)
     if need == (1 << 64) - 1:
         raise ValueError(f"n_segments must lie in [1, {MAX_SEGMENTS}]")
@@ -627,6 +637,8 @@ def prefill_layer(xq, xk, xv, wq, wk, wv, alpha, beta, g, norm_w, conv_state=Non
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _need(workspace, "workspace", torch.uint8, dev)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
     _check(load().kda_prefill_layer(
         _ptr(xq), _ptr(xk), _ptr(xv), _dt(xq), ctypes.byref(c), _ptr(conv_state), _ptr(so),
         ctypes.byref(gd), _ptr(beta), _ptr(cu_seqlens), n_seq, T if cu_seqlens is None else T,

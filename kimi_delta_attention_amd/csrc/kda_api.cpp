@@ -30,6 +30,39 @@ kda_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A byte range of a caller's tensor; overlap checks between the outputs an
+// entry point writes and the tensors it reads (an empty or absent range
+// overlaps nothing).
+struct Range {
+  const void* p;
+  size_t n;
+};
+bool overlaps(Range a, Range b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a.p), y = reinterpret_cast<uintptr_t>(b.p);
+  return x < y + b.n && y < x + a.n;
+}
+// The first output of `outs` that overlaps an input of `ins`, as "out / in"
+// names, or nullptr.
+template <size_t NO, size_t NI>
+bool any_overlap(const Range (&outs)[NO], const char* const (&on)[NO], const Range (&ins)[NI],
+                 const char* const (&in)[NI], const char** a, const char** b) {
+  for (size_t i = 0; i < NO; ++i)
+    for (size_t j = 0; j < NI; ++j)
+      if (overlaps(outs[i], ins[j])) {
+        *a = on[i];
+        *b = in[j];
+        return true;
+      }
+  return false;
+}
+size_t esize(kda_dtype d) { return d == KDA_BF16 ? 2 : 4; }
+// bytes of a gate tensor over `rows` (token, head) rows
+size_t gate_bytes(const kda_gate* g, size_t rows, int Dk) {
+  if (!g || g->kind == KDA_GATE_NONE) return 0;
+  return g->kind == KDA_GATE_SCALAR ? rows * 4 : rows * (size_t)Dk * 4;
+}
+
 kda_status check_common(const void* q, const void* k, const void* v, kda_dtype qkv,
                         const float* beta, const void* o, kda_dtype od, int H, int Dk, int Dv) {
   if (!q || !k || !v || !beta || !o)
@@ -163,6 +196,26 @@ static kda_status prefill_common(const void* q, const void* k, const void* v, kd
   if ((long long)n_seq * H * (Dv / 64) > 0x7fffffffLL)
     return fail(KDA_ERR_INVALID_ARGUMENT, "too many (sequence, head) work items");
   if (T == 0 && !cu_seqlens && !final_state) return ok();
+  {
+    // outputs against inputs (final_state may be initial_state itself: in place)
+    const size_t tok = cu_seqlens ? (size_t)T : (size_t)n_seq * T;
+    const size_t rows = tok * H, st = (size_t)n_seq * H * Dk * Dv * 4;
+    const size_t xe = pro ? 2 : esize(qkv_dtype);
+    const Range ins[] = {{q, rows * Dk * xe}, {k, rows * Dk * xe}, {v, rows * Dv * xe},
+                         {beta, rows * 4}, {gate ? gate->gate : nullptr, gate_bytes(gate, rows, Dk)},
+                         {cu_seqlens, cu_seqlens ? (size_t)(n_seq + 1) * 4 : 0},
+                         {initial_state == final_state ? nullptr : initial_state, st},
+                         {workspace, workspace ? workspace_bytes : 0}};
+    const char* const in[] = {"q", "k", "v", "beta", "the gate tensor", "cu_seqlens",
+                              "initial_state", "workspace"};
+    const Range outs[] = {{o, rows * Dv * esize(o_dtype)}, {final_state, st}};
+    const char* const on[] = {"o", "final_state"};
+    const char *a = nullptr, *b = nullptr;
+    if (any_overlap(outs, on, ins, in, &a, &b))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s must not overlap %s", a, b);
+    if (overlaps(outs[0], outs[1]))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "o must not overlap final_state");
+  }
   if (workspace && ((uintptr_t)workspace & 255u))
     return fail(KDA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   if (nseg > 1) {
@@ -332,8 +385,24 @@ kda_status kda_prologue(const void* xq, const void* xk, const void* xv, kda_dtyp
     if (!aligned16(xq) || !aligned16(xk) || !aligned16(xv) || !aligned16(q) || !aligned16(k) ||
         !aligned16(v))
       return fail(KDA_ERR_INVALID_ARGUMENT, "token tensors must be 16-byte aligned");
-    if (q == xq || k == xk || v == xv || q == xk || k == xq)
-      return fail(KDA_ERR_INVALID_ARGUMENT, "outputs must not alias the inputs");
+    const size_t e = esize(dtype), rows = (size_t)total * H;
+    const size_t sw = (size_t)N * 3 * H * (2 * Dk + Dv) * 4;
+    const Range ins[] = {{xq, rows * Dk * e}, {xk, rows * Dk * e}, {xv, rows * Dv * e},
+                         {conv->w_q, (size_t)H * Dk * 16}, {conv->w_k, (size_t)H * Dk * 16},
+                         {conv->w_v, (size_t)H * Dv * 16}, {conv_state_in, conv_state_in ? sw : 0},
+                         {cu_seqlens, cu_seqlens ? (size_t)(N + 1) * 4 : 0}};
+    const char* const in[] = {"x_q", "x_k", "x_v", "w_q", "w_k", "w_v", "conv_state_in",
+                              "cu_seqlens"};
+    const Range outs[] = {{q, rows * Dk * e}, {k, rows * Dk * e}, {v, rows * Dv * e},
+                          {conv_state_out, conv_state_out ? sw : 0}};
+    const char* const on[] = {"q", "k", "v", "conv_state_out"};
+    const char *a = nullptr, *b = nullptr;
+    if (any_overlap(outs, on, ins, in, &a, &b))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s must not overlap %s", a, b);
+    for (int i = 0; i < 4; ++i)
+      for (int j = i + 1; j < 4; ++j)
+        if (overlaps(outs[i], outs[j]))
+          return fail(KDA_ERR_INVALID_ARGUMENT, "%s must not overlap %s", on[i], on[j]);
   }
   if ((conv_state_in && !aligned16(conv_state_in)) || (conv_state_out && !aligned16(conv_state_out)))
     return fail(KDA_ERR_INVALID_ARGUMENT, "conv states must be 16-byte aligned");
@@ -480,8 +549,6 @@ kda_status kda_decode_layer(kda_decode_mode mode, const void* xq, const void* xk
   return hip_status(kda::launch_decode(a));
 }
 
-}  // extern "C"
-
 kda_status kda_prefill_layer(const void* xq, const void* xk, const void* xv, kda_dtype x_dtype,
                              const kda_conv* conv, const float* conv_state_in,
                              float* conv_state_out, const kda_gate* gate, const float* beta,
@@ -530,6 +597,29 @@ kda_status kda_prefill_layer(const void* xq, const void* xk, const void* xv, kda
                     workspace ? workspace_bytes : (size_t)0);
     }
   }
+  if (tokens) {
+    const size_t tok = cu_seqlens ? (size_t)T : (size_t)n_seq * T;
+    const size_t rows = tok * H, sw = (size_t)n_seq * 3 * H * (2 * Dk + Dv) * 4;
+    const Range ins[] = {{xq, rows * Dk * 2}, {xk, rows * Dk * 2}, {xv, rows * Dv * 2},
+                         {out->g, rows * Dv * 2}, {beta, rows * 4},
+                         {gate ? gate->gate : nullptr, gate_bytes(gate, rows, Dk)},
+                         {conv->w_q, (size_t)H * Dk * 16}, {conv->w_k, (size_t)H * Dk * 16},
+                         {conv->w_v, (size_t)H * Dv * 16}, {conv_state_in, conv_state_in ? sw : 0},
+                         {cu_seqlens, cu_seqlens ? (size_t)(n_seq + 1) * 4 : 0}};
+    const char* const in[] = {"x_q", "x_k", "x_v", "g", "beta", "the gate tensor", "w_q", "w_k",
+                              "w_v", "conv_state_in", "cu_seqlens"};
+    // y may be o itself (fp32), checked above; otherwise the three are apart
+    const Range outs[] = {{o, rows * Dv * 4}, {(void*)y == (void*)o ? nullptr : y, rows * Dv * esize(y_dtype)},
+                          {conv_state_out, conv_state_out ? sw : 0}};
+    const char* const on[] = {"o", "y", "conv_state_out"};
+    const char *a = nullptr, *b = nullptr;
+    if (any_overlap(outs, on, ins, in, &a, &b))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s must not overlap %s", a, b);
+    for (int i = 0; i < 3; ++i)
+      for (int j = i + 1; j < 3; ++j)
+        if (overlaps(outs[i], outs[j]))
+          return fail(KDA_ERR_INVALID_ARGUMENT, "%s must not overlap %s", on[i], on[j]);
+  }
   pro.st_in = conv_state_in;
   pro.st_out = conv_state_out;
   pro.out.g = out->g;
@@ -541,3 +631,5 @@ kda_status kda_prefill_layer(const void* xq, const void* xk, const void* xv, kda
                         final_state, o, KDA_F32, H, Dk, Dv, chunk, workspace, workspace_bytes,
                         stream, n_segments, &pro);
 }
+
+}  // extern "C"

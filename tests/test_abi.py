@@ -17,6 +17,9 @@ HEADER = os.path.join(ROOT, "include", "kda.h")
 F32, BF16 = 0, 1
 OK, INVALID, UNSUPPORTED = 0, 1, 2
 FAKE = 0x10000  # an aligned non-null address; never dereferenced by these calls
+# distinct fake tensors, 4 GiB apart: the entry points reject an output that
+# overlaps an input, so every argument gets an address range of its own
+AT = [FAKE + (i << 32) for i in range(1, 40)]
 
 
 def _declared():
@@ -111,12 +114,12 @@ def test_segmented_workspace_and_preference():
 
 
 def _segmented(**over):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, qd=BF16, cu=None, n=1, T=4096, s0=None, s1=None, o=FAKE,
-             od=F32, H=2, Dk=128, Dv=128, chunk=64, ns=4, ws=FAKE, wsb=1 << 40)
+    a = dict(q=AT[0], k=AT[1], v=AT[2], qd=BF16, cu=None, n=1, T=4096, s0=None, s1=None, o=AT[3],
+             od=F32, H=2, Dk=128, Dv=128, chunk=64, ns=4, ws=AT[4], wsb=1 << 31)
     a.update(over)
-    g = _lib._Gate(0, FAKE, None, 0.0)
+    g = _lib._Gate(0, AT[5], None, 0.0)
     return kda.load().kda_prefill_segmented(
-        a["q"], a["k"], a["v"], a["qd"], ctypes.byref(g), FAKE, a["cu"], a["n"], a["T"], a["s0"],
+        a["q"], a["k"], a["v"], a["qd"], ctypes.byref(g), AT[6], a["cu"], a["n"], a["T"], a["s0"],
         a["s1"], a["o"], a["od"], a["H"], a["Dk"], a["Dv"], a["chunk"], a["ns"], a["ws"], a["wsb"],
         None)
 
@@ -126,11 +129,14 @@ def _segmented(**over):
     (dict(ns=17), INVALID),
     (dict(ws=None, wsb=0), INVALID),
     (dict(wsb=1024), INVALID),
-    (dict(ws=FAKE + 64), INVALID),
+    (dict(ws=AT[4] + 64), INVALID),
     (dict(qd=F32, Dk=64), UNSUPPORTED),
     (dict(Dk=96), UNSUPPORTED),
     (dict(chunk=32), UNSUPPORTED),
-    (dict(cu=FAKE + 2), INVALID),
+    (dict(cu=AT[7] + 2), INVALID),
+    (dict(o=AT[0] + 1024), INVALID),      # o overlaps q
+    (dict(s0=AT[8], s1=AT[8] + 256), INVALID),  # final state overlaps the initial one
+    (dict(s0=AT[8], s1=AT[8], T=0, ws=None, wsb=0, n=0), OK),  # in place is allowed
     (dict(n=-1), INVALID),
     (dict(n=0, q=None, k=None, v=None, o=None, ws=None, wsb=0), OK),
     (dict(T=0, ws=None, wsb=0), OK),  # no tokens and no final state: nothing to do
@@ -142,26 +148,33 @@ def test_segmented_validation(over, expect):
 
 
 def _layer(**over):
-    a = dict(x=FAKE, xd=BF16, taps=FAKE, st=None, so=None, ns=1, T=256, o=FAKE, y=FAKE, yd=F32,
-             g=FAKE, w=FAKE, eps=1e-5, ws=FAKE, wsb=1 << 40, H=2, Dk=128, Dv=128, chunk=64)
+    a = dict(xq=AT[0], xk=AT[1], xv=AT[2], xd=BF16, taps=AT[3], st=None, so=None, ns=1, T=256,
+             o=AT[4], y=AT[4], yd=F32, g=AT[5], w=AT[6], eps=1e-5, ws=AT[7], wsb=1 << 31, H=2,
+             Dk=128, Dv=128, chunk=64, beta=AT[8])
     a.update(over)
-    c = _lib._Conv(a["taps"], a["taps"], a["taps"], 1e-6)
-    gt = _lib._Gate(0, FAKE, None, 0.0)
+    c = _lib._Conv(a["taps"], a["taps"] + (1 << 20), a["taps"] + (2 << 20), 1e-6)
+    gt = _lib._Gate(0, AT[9], None, 0.0)
     og = _lib._OutGate(a["g"], a["w"], a["eps"])
     return kda.load().kda_prefill_layer(
-        a["x"], a["x"], a["x"], a["xd"], ctypes.byref(c), a["st"], a["so"], ctypes.byref(gt),
-        FAKE, None, 1, a["T"], None, None, a["o"], ctypes.byref(og), a["y"], a["yd"], a["H"],
+        a["xq"], a["xk"], a["xv"], a["xd"], ctypes.byref(c), a["st"], a["so"], ctypes.byref(gt),
+        a["beta"], None, 1, a["T"], None, None, a["o"], ctypes.byref(og), a["y"], a["yd"], a["H"],
         a["Dk"], a["Dv"], a["chunk"], a["ns"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("over,expect", [
     (dict(xd=F32), UNSUPPORTED),
-    (dict(taps=FAKE + 4), INVALID),       # taps need 16-byte alignment here
-    (dict(st=FAKE, so=FAKE), INVALID),    # conv state out aliasing in
+    (dict(taps=AT[3] + 4), INVALID),      # taps need 16-byte alignment here
+    (dict(st=AT[10], so=AT[10]), INVALID),  # conv state out aliasing in
+    (dict(st=AT[10], so=AT[10] + 64), INVALID),  # ... or overlapping it
     (dict(eps=0.0), INVALID),
     (dict(g=None), INVALID),
-    (dict(y=FAKE + 8), INVALID),
-    (dict(yd=BF16, y=FAKE), INVALID),     # y aliasing o needs fp32
+    (dict(y=AT[11] + 8), INVALID),
+    (dict(yd=BF16), INVALID),             # y aliasing o needs fp32
+    (dict(o=AT[0]), INVALID),             # o is the x_q buffer
+    (dict(o=AT[2] + 4096), INVALID),      # o overlaps x_v
+    (dict(y=AT[11], yd=BF16, g=AT[11] + 256), INVALID),  # y overlaps g
+    (dict(y=AT[4] + 256), INVALID),       # y overlaps o without being it
+    (dict(so=AT[10], st=None, xk=AT[10] + 128), INVALID),  # conv state out overlaps x_k
     (dict(ws=None, wsb=0), INVALID),
     (dict(wsb=4096), INVALID),
     (dict(ns=0), INVALID),
@@ -174,8 +187,8 @@ def test_layer_prefill_validation(over, expect):
 
 
 def _prefill(**over):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, qd=BF16, alpha=FAKE, beta=FAKE, s0=None, s1=None, o=FAKE,
-             od=F32, B=1, T=128, H=2, Dk=128, Dv=128, chunk=64, ws=None, wsb=0)
+    a = dict(q=AT[0], k=AT[1], v=AT[2], qd=BF16, alpha=AT[3], beta=AT[4], s0=None, s1=None,
+             o=AT[5], od=F32, B=1, T=128, H=2, Dk=128, Dv=128, chunk=64, ws=None, wsb=0)
     a.update(over)
     lib = kda.load()
     return lib.kda_prefill_chunked(a["q"], a["k"], a["v"], a["qd"], a["alpha"], a["beta"],
@@ -186,10 +199,14 @@ def _prefill(**over):
 @pytest.mark.parametrize("over,expect", [
     (dict(q=None), INVALID),
     (dict(beta=None), INVALID),
-    (dict(o=FAKE + 2), INVALID),
-    (dict(q=FAKE + 1), INVALID),
-    (dict(alpha=FAKE + 8), INVALID),
-    (dict(s0=FAKE + 8), INVALID),
+    (dict(o=AT[5] + 2), INVALID),
+    (dict(q=AT[0] + 1), INVALID),
+    (dict(alpha=AT[3] + 8), INVALID),
+    (dict(s0=AT[6] + 8), INVALID),
+    (dict(o=AT[1] + 512), INVALID),       # o overlaps k
+    (dict(o=AT[4]), INVALID),             # o is beta
+    (dict(s1=AT[3] + 1024), INVALID),     # final state overlaps alpha
+    (dict(s1=AT[5] + 4096), INVALID),     # final state overlaps o
     (dict(H=0), INVALID),
     (dict(T=-1), INVALID),
     (dict(qd=7), INVALID),
@@ -198,7 +215,8 @@ def _prefill(**over):
     (dict(Dv=256), UNSUPPORTED),
     (dict(qd=F32, Dk=128), UNSUPPORTED),
     (dict(B=0), OK),
-    (dict(ws=FAKE + 64, wsb=1 << 30), INVALID),
+    (dict(ws=AT[7] + 64, wsb=1 << 30), INVALID),
+    (dict(ws=AT[5] - 4096, wsb=1 << 20), INVALID),  # workspace overlaps o
 ])
 def test_prefill_argument_validation(over, expect):
     assert _prefill(**over) == expect
@@ -209,8 +227,11 @@ def test_prefill_argument_validation(over, expect):
 def test_varlen_and_decode_validation():
     lib = kda.load()
     # varlen: missing cu_seqlens
-    assert lib.kda_prefill_varlen(FAKE, FAKE, FAKE, BF16, FAKE, FAKE, None, 4, 100, None, None,
-                                  FAKE, F32, 2, 128, 128, 64, None, 0, None) == INVALID
+    assert lib.kda_prefill_varlen(AT[0], AT[1], AT[2], BF16, AT[3], AT[4], None, 4, 100, None,
+                                  None, AT[5], F32, 2, 128, 128, 64, None, 0, None) == INVALID
+    # varlen: o overlapping cu_seqlens
+    assert lib.kda_prefill_varlen(AT[0], AT[1], AT[2], BF16, AT[3], AT[4], AT[5], 4, 100, None,
+                                  None, AT[5], F32, 2, 128, 128, 64, None, 0, None) == INVALID
     # varlen: N == 0 is a no-op
     assert lib.kda_prefill_varlen(None, None, None, BF16, None, None, None, 0, 0, None, None,
                                   None, F32, 2, 128, 128, 64, None, 0, None) == OK
@@ -241,13 +262,13 @@ def _gated(kind, gate=FAKE, a_log=None, g_min=0.0, null_desc=False, entry="chunk
     a = dict(qd=BF16, chunk=64, Dk=128)
     a.update(over)
     if entry == "chunked":
-        return lib.kda_prefill_chunked_gated(FAKE, FAKE, FAKE, a["qd"], gp, FAKE, None, None,
-                                             FAKE, F32, 1, 128, 2, a["Dk"], 128, a["chunk"],
-                                             None, 0, None)
+        return lib.kda_prefill_chunked_gated(AT[20], AT[21], AT[22], a["qd"], gp, AT[23], None,
+                                             None, AT[24], F32, 1, 128, 2, a["Dk"], 128,
+                                             a["chunk"], None, 0, None)
     if entry == "varlen":
-        return lib.kda_prefill_varlen_gated(FAKE, FAKE, FAKE, a["qd"], gp, FAKE, FAKE, 1, 128,
-                                            None, None, FAKE, F32, 2, a["Dk"], 128, a["chunk"],
-                                            None, 0, None)
+        return lib.kda_prefill_varlen_gated(AT[20], AT[21], AT[22], a["qd"], gp, AT[23], AT[25],
+                                            1, 128, None, None, AT[24], F32, 2, a["Dk"], 128,
+                                            a["chunk"], None, 0, None)
     return lib.kda_decode_step_gated(FAKE, FAKE, FAKE, a["qd"], gp, FAKE, FAKE, FAKE, F32, 4, 2,
                                      a["Dk"], 128, None)
 
@@ -348,6 +369,17 @@ def test_prologue_epilogue_validation():
     assert pro(xk=FAKE + 8) == INVALID                      # 16-byte alignment
     assert pro(q=FAKE) == INVALID                           # output aliases x_q
     assert pro(si=FAKE + 0x600, so=FAKE + 0x600) == INVALID  # states alias
+    far = lambda i: FAKE + (i << 32)  # noqa: E731
+    sep = dict(xq=far(1), xk=far(2), xv=far(3), q=far(4), k=far(5), v=far(6))
+    for o, i in (("v", "xq"), ("v", "xk"), ("q", "xv"), ("k", "xv"), ("q", "xk"), ("k", "xq")):
+        over = dict(sep)
+        over[o] = sep[i] + 256  # overlapping, not equal
+        assert pro(**over) == INVALID, (o, i)
+    assert pro(**dict(sep, q=far(5) + 16)) == INVALID       # two outputs overlap
+    assert pro(**dict(sep, so=far(7), si=None, xv=far(7) + 64)) == INVALID
+    c2 = _lib._Conv(far(8), far(8) + (1 << 20), far(8) + (2 << 20), 1e-6)
+    assert pro(**dict(sep, cp=ctypes.byref(c2), so=far(8) + 2048)) == INVALID  # taps
+    assert pro(**dict(sep, cp=ctypes.byref(c2), Dk=96)) == UNSUPPORTED  # no overlap
     assert pro(dt=9) == INVALID and pro(H=0) == INVALID
     assert pro(Dk=96) == UNSUPPORTED
     bad = _lib._Conv(FAKE, None, FAKE, 1e-6)

@@ -8,13 +8,13 @@ import torch
 import kimi_delta_attention_amd as kda
 import oracle
 from kimi_delta_attention_amd import synth
-from tests._common import TOL_BF16, dev, rel
+from tests._common import TOL_BF16, close, dev, rounded
 
 pytestmark = pytest.mark.gpu
 
-# q, k, v enter the recurrence rounded to bf16 (one rounding, 2^-8 relative per
-# element) on top of the recurrence's own bar
-TOL_LAYER = TOL_BF16 + 2.0 ** -8
+# the oracle's chain rounds q, k, v to bf16 where the prologue stores them, so
+# the layer is held to the recurrence's own bar (fp32 y and o)
+TOL_LAYER = TOL_BF16
 
 
 def _f(x):
@@ -35,6 +35,7 @@ def _oracle_chain(L, alpha, beta, s0, cu=None):
     if cu is None:
         rq, rk, rv, rcs = oracle.prologue(_f(L.xq), _f(L.xk), _f(L.xv), L.wq, L.wk, L.wv,
                                           state=L.conv_state.cpu())
+        rq, rk, rv = (rounded(x, torch.bfloat16) for x in (rq, rk, rv))
         ro, rs = oracle.recurrent(rq, rk, rv, alpha.cpu().numpy(), beta.cpu(),
                                   initial_state=s0.cpu())
     else:
@@ -49,7 +50,8 @@ def _oracle_chain(L, alpha, beta, s0, cu=None):
                                           _f(L.xv[:, lo:hi]), L.wq, L.wk, L.wv, state=st)
             parts.append((q, k, v))
             states.append(cs)
-        rq, rk, rv = (np.concatenate([p[j] for p in parts], axis=1) for j in range(3))
+        rq, rk, rv = (rounded(np.concatenate([p[j] for p in parts], axis=1), torch.bfloat16)
+                      for j in range(3))
         rcs = np.concatenate(states, axis=0)
         ro, rs = oracle.recurrent(rq, rk, rv, alpha.cpu().numpy(), beta.cpu(), cu_seqlens=cu,
                                   initial_state=s0.cpu())
@@ -66,9 +68,9 @@ def test_dense_against_oracle_and_composed(Dk, Dv):
                                     L.norm_w, conv_state=L.conv_state, initial_state=s0)
     torch.cuda.synchronize()
     ry, ro, rs, rcs = _oracle_chain(L, alpha, beta, s0)
-    assert rel(y.cpu(), ry) <= TOL_LAYER
-    assert rel(o.cpu(), ro) <= TOL_LAYER
-    assert rel(s.cpu(), rs) <= TOL_LAYER
+    close(y, ry, TOL_LAYER, "tokens")
+    close(o, ro, TOL_LAYER, "tokens")
+    close(s, rs, TOL_LAYER, "state")
     assert np.array_equal(cs.cpu().numpy(), rcs.astype(np.float32))  # inputs, copied exactly
     # the standalone calls composed: the same up to the L2Norm's summation order
     q, k, v, cs2 = kda.prologue(L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, conv_state=L.conv_state)
@@ -76,7 +78,8 @@ def test_dense_against_oracle_and_composed(Dk, Dv):
     y2 = kda.epilogue(o2, L.g, L.norm_w, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(cs, cs2)
-    assert rel(y.cpu(), y2.cpu()) <= TOL_BF16 and rel(s.cpu(), s2.cpu()) <= TOL_BF16
+    close(y, y2, TOL_BF16, "tokens")
+    close(s, s2, TOL_BF16, "state")
 
 
 @pytest.mark.parametrize("n_segments", [1, 4])
@@ -95,8 +98,8 @@ def test_packed_sequences_and_windows(n_segments):
                                     cu_seqlens=cu, n_segments=n_segments)
     torch.cuda.synchronize()
     ry, ro, rs, rcs = _oracle_chain(L, alpha, beta, s0, cu=cu.cpu().numpy())
-    assert rel(y.cpu(), ry) <= TOL_LAYER
-    assert rel(s.cpu(), rs) <= TOL_LAYER
+    close(y, ry, TOL_LAYER, "tokens", cu=cu)
+    close(s, rs, TOL_LAYER, "state")
     assert np.array_equal(cs.cpu().numpy(), rcs.astype(np.float32))
     assert torch.equal(cs[1], L.conv_state[1]) and torch.equal(s[1], s0[1])
 
@@ -114,11 +117,12 @@ def test_bounded_gate_segments_bf16_output_no_conv_state():
     torch.cuda.synchronize()
     assert cs is None and y.dtype == torch.bfloat16
     rq, rk, rv, _ = oracle.prologue(_f(L.xq), _f(L.xk), _f(L.xv), L.wq, L.wk, L.wv)
+    rq, rk, rv = (rounded(x, torch.bfloat16) for x in (rq, rk, rv))
     alpha = oracle.gate_alpha("bounded", z.cpu().numpy(), (B, T, H, D), a_log=a_log.cpu().numpy())
     ro, rs = oracle.recurrent(rq, rk, rv, alpha, beta.cpu(), initial_state=s0.cpu())
     ry = oracle.rmsnorm_gate(ro, _f(L.g), L.norm_w.cpu())
-    assert rel(y.float().cpu(), ry) <= TOL_LAYER + 2.0 ** -8
-    assert rel(s.cpu(), rs) <= TOL_LAYER
+    close(y.float(), ry, TOL_LAYER + 2.0 ** -8, "tokens")
+    close(s, rs, TOL_LAYER, "state")
 
 
 def test_empty_call_hands_states_through():
@@ -130,10 +134,9 @@ def test_empty_call_hands_states_through():
     assert torch.equal(s, s0) and torch.equal(cs, L.conv_state)
 
 
-def test_k3_8k_layer_sampled_heads():
+def test_k3_8k_layer_all_heads():
     """The 8K layer (B=1, T=8192, H=96, d=128) in one call, as the bench times
-    it: the oracle chain on 4 heads spread over the head axis (all tokens), the
-    composed calls on all heads."""
+    it: the oracle chain on every head and token, and the composed calls."""
     d = dev()
     B, T, H, D = 1, 8192, 96, 128
     L = synth.make_layer(B, T, H, D, D, seed=1360, device=d)
@@ -145,15 +148,17 @@ def test_k3_8k_layer_sampled_heads():
                                  schedule="two_pass")
     y2 = kda.epilogue(o2, L.g, L.norm_w, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert rel(y.cpu(), y2.cpu()) <= TOL_BF16 and rel(s.cpu(), s2.cpu()) <= TOL_BF16
-    heads = [3, 30, 61, 94]
+    close(y, y2, TOL_BF16, "tokens")
+    close(s, s2, TOL_BF16, "state")
+    heads = list(range(H))
     sel = lambda x: _f(x[:, :, heads])  # noqa: E731
     st = L.conv_state[:, :, heads].cpu()
     rq, rk, rv, rcs = oracle.prologue(sel(L.xq), sel(L.xk), sel(L.xv), L.wq[heads].cpu(),
                                       L.wk[heads].cpu(), L.wv[heads].cpu(), state=st)
+    rq, rk, rv = (rounded(x, torch.bfloat16) for x in (rq, rk, rv))
     ro, rs = oracle.recurrent(rq, rk, rv, r.alpha[:, :, heads].cpu().numpy(),
                               r.beta[:, :, heads].cpu(), initial_state=r.state[:, heads].cpu())
     ry = oracle.rmsnorm_gate(ro, sel(L.g), L.norm_w.cpu())
-    assert rel(y[:, :, heads].cpu(), ry) <= TOL_LAYER
-    assert rel(s[:, heads].cpu(), rs) <= TOL_LAYER
+    close(y[:, :, heads], ry, TOL_LAYER, "tokens")
+    close(s[:, heads], rs, TOL_LAYER, "state")
     assert np.array_equal(cs[:, :, heads].cpu().numpy(), rcs.astype(np.float32))

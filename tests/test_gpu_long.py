@@ -13,7 +13,7 @@ import torch
 import kimi_delta_attention_amd as kda
 import oracle
 from kimi_delta_attention_amd import synth
-from tests._common import TOL_BF16, dev, oracle_heads, rel
+from tests._common import TOL_BF16, close, dev, oracle_heads
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -43,19 +43,18 @@ def test_long_1m():
     t1 = time.time()
     o_ref, s_ref = oracle_heads(inp, heads)
     _log(f"oracle on heads {heads} in {time.time() - t1:.1f}s")
-    e_o = rel(o[:, :, heads].cpu(), o_ref)
-    e_s = rel(s[:, heads].cpu(), s_ref)
-    _log(f"oracle rel-L2 o={e_o:.3e} S={e_s:.3e}")
+    e_o, b_o = close(o[:, :, heads], o_ref, TOL_BF16, "tokens")
+    e_s, b_s = close(s[:, heads], s_ref, TOL_BF16, "state")
+    _log(f"oracle rel-L2 o={e_o:.3e} (worst head {b_o:.3e}) S={e_s:.3e} (worst head {b_s:.3e})")
     del o_ref, s_ref
-    assert e_o <= TOL_BF16 and e_s <= TOL_BF16
 
     # all heads: GPU decode replay, compared block by block
     T = inp.q.shape[1]
     state = inp.state.clone()
     blk = 4096
     orep = torch.empty(blk, w["H"], w["D"], dtype=torch.float32, device=d)
-    num = torch.zeros((), dtype=torch.float64, device=d)
-    den = torch.zeros((), dtype=torch.float64, device=d)
+    num = torch.zeros(w["H"], dtype=torch.float64, device=d)  # per head
+    den = torch.zeros(w["H"], dtype=torch.float64, device=d)
     t2 = time.time()
     for b0 in range(0, T, blk):
         for t in range(b0, min(T, b0 + blk)):
@@ -63,11 +62,13 @@ def test_long_1m():
                             inp.beta[:, t], state, o=orep[t - b0:t - b0 + 1])
         n = min(T, b0 + blk) - b0
         ref = o[0, b0:b0 + n].double()
-        num += (orep[:n].double() - ref).square().sum()
-        den += ref.square().sum()
+        num += (orep[:n].double() - ref).square().sum(dim=(0, 2))
+        den += ref.square().sum(dim=(0, 2))
         if (b0 // blk) % 32 == 0:
             _log(f"replay {b0 + n}/{T} tokens, {time.time() - t2:.0f}s")
-    e_rep = (num / den).sqrt().item()
-    e_rep_s = rel(s.cpu(), state.cpu())
-    _log(f"replay rel-L2 o={e_rep:.3e} S={e_rep_s:.3e}")
-    assert e_rep <= TOL_BF16 and e_rep_s <= TOL_BF16
+    e_rep = (num.sum() / den.sum()).sqrt().item()
+    b_rep = (num / den).sqrt().max().item()  # worst head
+    e_rep_s, b_rep_s = close(s, state, TOL_BF16, "state")
+    _log(f"replay rel-L2 o={e_rep:.3e} (worst head {b_rep:.3e}) S={e_rep_s:.3e} "
+         f"(worst head {b_rep_s:.3e})")
+    assert e_rep <= TOL_BF16 and b_rep <= TOL_BF16
