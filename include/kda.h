@@ -32,11 +32,12 @@
  *  - Supported shapes: Dk, Dv in {64, 128}; chunk == 64.  q/k/v dtype KDA_BF16
  *    or KDA_F32 (all three the same); alpha, beta and the state are fp32; the
  *    output o is KDA_F32 or KDA_BF16.
- *  - Documented, not checked: alpha in (0, 1] and, for the chunked paths, the
- *    per-channel product of alpha over any 16-token tile aligned to a 64-token
- *    chunk boundary is at least 1e-35 (true whenever log alpha >= -5 per token,
- *    the bounded gate of "Kimi K3 的 KDA" section 6 / "Kimi K3模型架构详解" section
- *    3.4); finite beta; monotone cu_seqlens; o does not alias any input.
+ *  - Documented, not checked: alpha in (0, 1] (any value in it, however fast
+ *    the decay: a 16-token tile whose decay product leaves the range of the
+ *    chunked kernels' factored form is computed by exact running products
+ *    instead); finite beta; monotone cu_seqlens.  Checked: no output's byte
+ *    range overlaps an input's (except final_state == initial_state, in place,
+ *    and y == o where documented).
  *  - Results are deterministic (no floating-point atomics): the same call on
  *    the same inputs gives bitwise-identical results, and a sequence of a
  *    packed batch gives bitwise the result it gives when run alone.  Both

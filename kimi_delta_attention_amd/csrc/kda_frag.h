@@ -4,6 +4,7 @@
 // pass 1 writes and the state pass reads.
 #pragma once
 #include "kda_common.h"
+#include "kda_layer.h"
 
 namespace kda {
 namespace frag {
@@ -77,6 +78,102 @@ __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
 __device__ __forceinline__ float bfv(unsigned int packed, int half) {
   return __builtin_bit_cast(float, half ? (packed & 0xffff0000u) : (packed << 16));
 }
+
+// Exclusive suffix product over the 16 lanes of each DPP row, for N values per
+// lane: lane i ends with x_{i+1} * ... * x_15 (1 for lane 15).  A shift by one
+// lane (lane 15 takes 1), then steps of v_mul_f32_dpp with row_shl:D and
+// bound_ctrl off, which leave lanes i >= 16 - D unwritten.  Every factor is a
+// product of decays <= 1, so nothing can overflow.
+template <int N>
+__device__ __forceinline__ void row_rscan_excl(float* x) {
+  static_assert(N == 8, "suffix scan width");
+#pragma unroll
+  for (int e = 0; e < N; ++e)
+    x[e] = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x[e]),
+                                                      0x101, 0xf, 0xf, false));  // row_shl:1
+#define KDA_RSCAN_STEP(D, i) "v_mul_f32_dpp %" #i ", %" #i ", %" #i " row_shl:" #D " row_mask:0xf bank_mask:0xf\n"
+#define KDA_RSCAN8(D) KDA_RSCAN_STEP(D, 0) KDA_RSCAN_STEP(D, 1) KDA_RSCAN_STEP(D, 2) KDA_RSCAN_STEP(D, 3) \
+  KDA_RSCAN_STEP(D, 4) KDA_RSCAN_STEP(D, 5) KDA_RSCAN_STEP(D, 6) KDA_RSCAN_STEP(D, 7)
+  __asm__("s_nop 1\n" KDA_RSCAN8(1) KDA_RSCAN8(2) KDA_RSCAN8(4) KDA_RSCAN8(8)
+          : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+            "+v"(x[7]));
+#undef KDA_RSCAN8
+#undef KDA_RSCAN_STEP
+}
+
+// The diagonal 16-token tile of A and Mqk uses the factored decay
+// (k_j / P_j) . (q_r P_r): exact as long as 1 / P_j stays in fp32 range.  A tile
+// whose whole-tile decay E (its smallest P) falls below kTileMin in any key
+// channel is computed instead by tile_exact_sums, and its other factors that
+// divide by P (E / P_j for Ktil and the key side of later tiles) become the
+// exclusive suffix products of the tile's decays.  K3's lower-bounded gate
+// (log alpha >= -5 per token, "Kimi K3 的 KDA" section 6, "Kimi K3模型架构详解"
+// section 3.4) never goes below it: e^(-80) > 2^(-116), so such tiles take the
+// factored path, bitwise as before.
+constexpr float kTileMin = 0x1p-116f;
+
+// 1 in every lane if any of the tile's Dk whole-tile decays (E, a [Dk] row in
+// LDS) is below kTileMin: a wave-uniform decision.
+template <int DK>
+__device__ __forceinline__ bool tile_flagged(const float* E, int lane) {
+  bool low = false;
+#pragma unroll
+  for (int c = 0; c < DK; c += 64) low = low || E[c + lane] < kTileMin;
+  return __builtin_amdgcn_ballot_w64(low) != 0;
+}
+
+// Exact decayed dot products inside one 16-token tile (the fallback of the
+// factored diagonal tile).  This lane holds query token r = tr of the tile and,
+// for NB 32-channel blocks, the 8 channels 32 kb + 16 h + 4 g + i (h, i < 2, 4):
+// their decays al[b][4 h + i] and k, q packed two bf16 per word (kp, qp, as
+// loaded).  For key token j of the tile,
+//     R_c(r, j) = alpha_{j+1,c} ... alpha_{r,c}   (1 for j = r),
+//     a(j) = sum_c k_rc k_jc R_c(r, j),   m(j) = sum_c q_rc k_jc R_c(r, j),
+// summed over these blocks' channels of all four lane rows; R is a running
+// product restarted after j (a 16-lane DPP scan), so no factor exceeds 1.
+// Returns in A[i], M[i] the sums for j = 4 g + i, the accumulator layout of a
+// 16 x 16 tile product with rows j and columns r (entries with j > r are not
+// meaningful; the callers mask them).  Fixed order of every sum, so the two
+// schedules that call it agree bitwise.
+template <int NB>
+__device__ __forceinline__ void tile_exact_sums(const float (*al)[8], const uint2v (*kp)[2],
+                                                const uint2v (*qp)[2], int tr, int g,
+                                                float (&A)[4], float (&M)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    A[i] = 0.f;
+    M[i] = 0.f;
+  }
+  const int row0 = 4 * 16 * g;  // ds_bpermute byte address of lane 16 g
+  for (int j = 0; j < 16; ++j) {
+    float pa = 0.f, pm = 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = tr > j ? al[b][e] : 1.f;
+      row_scan_mul<8>(x);
+      unsigned kj[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        kj[u] = (unsigned)__builtin_amdgcn_ds_bpermute(row0 + 4 * j, (int)kp[b][u >> 1][u & 1]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = x[e] * bfv(kj[e >> 1], e & 1);
+        pa = __builtin_fmaf(bfv(kp[b][e >> 2][(e & 3) >> 1], e & 1), t, pa);
+        pm = __builtin_fmaf(bfv(qp[b][e >> 2][(e & 3) >> 1], e & 1), t, pm);
+      }
+    }
+    pa = rows4_sum(pa);
+    pm = rows4_sum(pm);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      A[i] = j == 4 * g + i ? pa : A[i];
+      M[i] = j == 4 * g + i ? pm : M[i];
+    }
+  }
+}
+
 
 __device__ __forceinline__ void st_bf16x4(bf16* p, const float* x) {
   // 4 values -> one 8-byte LDS store

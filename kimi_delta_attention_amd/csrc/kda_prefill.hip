@@ -280,6 +280,30 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     if (g == 0 && hh == 0) BS[r] = bt;
     __syncthreads();
 
+    // A tile whose decay product leaves the range of the factored form takes
+    // the exact path (the first pass does the same, in the same order): the
+    // diagonal tile's A and Mqk sums of this wave's channel half by running
+    // products, and suffix products in place of E / P below.  The decays are
+    // loaded again (the scan overwrote them, and the next chunk's are in flight).
+    const bool exact = tile_flagged<DK>(ES + w * DK, lane_x);
+    auto alpha_of = [&](int kb, float* al) {
+      floatx4 a4[1][2];
+      const bool okc = r < nv;
+      const size_t thc = (size_t)(tok0 + r) * H + h;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) a4[0][hf] = gate_load4<KIND>(gate, okc, thc, DK, 32 * kb + 16 * hf + 4 * g);
+      gate_finish_blocks<KIND, 1>(gate, gsc, a4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) al[e] = a4[0][e >> 2][e & 3];
+    };
+    float dA[4] = {}, dM[4] = {};
+    if (exact) {
+      float al[NKH][8];
+#pragma unroll
+      for (int kk = 0; kk < NKH; ++kk) alpha_of(NKH * hh + kk, al[kk]);
+      tile_exact_sums<NKH>(al, in.k, in.q, tr, g, dA, dM);
+    }
+
     // ---- operands for this wave's channels.  Registers: KL = k*P and QL = q*P
     // (split), the B operands of A^T and Mqk^T; Ktil (split) until it is stored.
     // LDS: RT rows of this tile for row tiles mm >= w, GK = k*Gamma (bf16,
@@ -315,8 +339,12 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) post[e] *= tmp[e];
       }
-      float y[8], gk[8], kt[8], rd[8], re[8];
+      float y[8], gk[8], kt[8], rd[8], re[8], sfx[8];
       bf16x8 qt8;
+      if (exact) {  // decay from after this token to the tile's end, as a product
+        alpha_of(kb, sfx);
+        row_rscan_excl<8>(sfx);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         kl[kk][e] = (bf16)(kk8[e] * Pv[kk][e]);
@@ -325,9 +353,10 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
         qt8[e] = (bf16)(qq[e] * gam);
         gk[e] = kk8[e] * gam;
         const float ip = __builtin_amdgcn_rcpf(Pv[kk][e]);
-        kt[e] = kk8[e] * ((Ew[e] * ip) * post[e]);
-        rd[e] = kk8[e] * ip;
-        re[e] = kk8[e] * (Ew[e] * ip);
+        const float ew = exact ? sfx[e] : Ew[e] * ip;
+        kt[e] = kk8[e] * (ew * post[e]);
+        rd[e] = kk8[e] * ip;  // (not used in an exact tile)
+        re[e] = kk8[e] * ew;
       }
       split8(y, qlh[kk], qll[kk]);
       split8(kt, kth[kk], ktl[kk]);
@@ -387,6 +416,10 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
         const bf16x8 al = frag_ld(RT + loR, ldR, row, 32 * kb, g);
         accA[n] = mfma_bf16(ah, kl[kk], accA[n]);
         accM[n] = mma_ab(ah, al, qlh[kk], qll[kk], accM[n]);
+      }
+      if (n == w && exact) {  // the diagonal tile from the exact sums
+        accA[n] = floatx4{dA[0], dA[1], dA[2], dA[3]};
+        accM[n] = floatx4{dM[0], dM[1], dM[2], dM[3]};
       }
     }
     __syncthreads();  // RT reads done; the partials overwrite it

@@ -30,6 +30,7 @@
 // split-bf16 operand machinery; bf16 inputs use the kernel in kda_prefill.hip.)
 #include "kda_common.h"
 #include "kda_internal.h"
+#include "kda_layer.h"
 
 namespace kda {
 namespace f32path {
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(NTH) void prefill_f32_kernel(
     // ---- load: k, q, alpha for this thread's (tile, channel) segments;
     // P = running product of alpha from the tile start.
     TIn kf[NSEG][16], qf[NSEG][16];  // exact input values (bf16 stays bf16)
-    float Pf[NSEG][16];
+    float Pf[NSEG][16], af[NSEG][16];
 #pragma unroll
     for (int s = 0; s < NSEG; ++s) {
       const int m = tid / DK + s * TPC;
@@ -215,6 +216,7 @@ __global__ __launch_bounds__(NTH) void prefill_f32_kernel(
         const float a = ok ? gate_alpha1(gate, (size_t)(tok0 + r) * H + h, DK, ch, h) : 1.f;
         run = (j == 0) ? a : run * a;
         Pf[s][j] = run;
+        af[s][j] = a;
       }
       ESd[m * DK + ch] = run;
     }
@@ -250,23 +252,32 @@ __global__ __launch_bounds__(NTH) void prefill_f32_kernel(
       pre[s] = p;
       post[s] = po;
       Em[s] = Et[m];
+      // decay from after token j to the end of tile m, a product of decays
+      // (no division by P, so nothing overflows however fast the decay)
+      float sf[16];
+      {
+        float run = 1.f;
+#pragma unroll
+        for (int j = 15; j >= 0; --j) {
+          sf[j] = run;
+          run *= af[s][j];
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int r = 16 * m + j;
-        const float ip = 1.f / Pf[s][j];
         const float kv = (float)kf[s][j];
         Ld::store_hi(KL, r * ldK + ch, kv * Pf[s][j]);
         Ld::store(QL, r * ldK + ch, loQL, (float)qf[s][j] * Pf[s][j]);
-        // right operand rows for row tiles mm >= m
-        const float kd = kv * ip;                         // diagonal tile
-        float ke = kv * (Em[s] * ip);                     // decayed to the end of tile m
+        // right operand rows for row tiles mm > m (the diagonal tile is summed
+        // exactly below)
+        float ke = kv * sf[j];                            // decayed to the end of tile m
 #pragma unroll
         for (int mm = 0; mm < 4; ++mm) {
-          if (mm < m) continue;
+          if (mm <= m) continue;
           const int base = 8 * mm * (mm + 1);            // 16 * mm(mm+1)/2
-          const float val = (mm == m) ? kd : ke;
-          Ld::store(RT, (base + r) * ldK + ch, loRT, val);
-          if (mm > m) ke *= Et[mm];
+          Ld::store(RT, (base + r) * ldK + ch, loRT, ke);
+          ke *= Et[mm];
         }
       }
     }
@@ -280,7 +291,7 @@ __global__ __launch_bounds__(NTH) void prefill_f32_kernel(
       accM[p] = floatx4{0.f, 0.f, 0.f, 0.f};
       int mm, n;
       pair_of(w, p, mm, n);
-      if (n < 0) continue;
+      if (n < 0 || n == mm) continue;  // diagonal tiles: exact sums below
       const int base = 8 * mm * (mm + 1);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -302,11 +313,44 @@ __global__ __launch_bounds__(NTH) void prefill_f32_kernel(
         for (int i = 0; i < 4; ++i) Ld::store(MQ, (16 * mm + 4 * g4 + i) * ldC + 16 * nn + l16, loMQ, 0.f);
         continue;
       }
+      if (n == mm) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mm + 4 * g4 + i, j = 16 * n + l16;
         AF[r * ldA + j] = (j < r) ? BS[r] * accA[p][i] : 0.f;
         Ld::store(MQ, r * ldC + j, loMQ, (j <= r) ? accM[p][i] : 0.f);
+      }
+    }
+    // ---- the diagonal tile of wave w's token tile, exactly: for tokens
+    // j <= r of the tile, sum_c k_rc k_jc R and sum_c q_rc k_jc R with
+    // R = alpha_{j+1} ... alpha_r of channel c, a running product (every factor
+    // <= 1); lane c holds channel c of the tile (Dk = 64: one channel a lane)
+    // and the wave sums over the channels.
+    static_assert(NSEG == 1 && TPC == 4, "one (tile, channel) segment per thread");
+    {
+      const int m = w;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float kr = (float)kf[0][r], qr = (float)qf[0][r];
+        float ca[16], cm[16];
+        float R = 1.f;
+#pragma unroll
+        for (int j = r; j >= 0; --j) {
+          const float t = (float)kf[0][j] * R;
+          ca[j] = kr * t;
+          cm[j] = qr * t;
+          R *= af[0][j];
+        }
+        float av = 0.f, mv = 0.f;
+#pragma unroll
+        for (int j = 0; j <= r; ++j) {
+          const float sa = wave_sum(ca[j]), sm = wave_sum(cm[j]);
+          av = lane == j ? sa : av;
+          mv = lane == 16 + j ? sm : mv;
+        }
+        const int rr = 16 * m + r;
+        if (lane < 16) AF[rr * ldA + 16 * m + lane] = lane < r ? BS[rr] * av : 0.f;
+        else if (lane < 32) Ld::store(MQ, rr * ldC + 16 * m + lane - 16, loMQ, lane - 16 <= r ? mv : 0.f);
       }
     }
     __syncthreads();
@@ -402,7 +446,10 @@ __global__ __launch_bounds__(NTH) void prefill_f32_kernel(
       for (int j = 0; j < 16; ++j) {
         const int r = 16 * m + j;
         Ld::store_hi(QT, r * ldK + ch, (float)qf[s][j] * (pre[s] * Pf[s][j]));
-        Ld::store(KT, ch * ldC + r, loKT, (float)kf[s][j] * ((Em[s] / Pf[s][j]) * post[s]));
+        float sfx = 1.f;  // decay from after token j to the end of tile m
+#pragma unroll
+        for (int i = j + 1; i < 16; ++i) sfx *= af[s][i];
+        Ld::store(KT, ch * ldC + r, loKT, (float)kf[s][j] * (sfx * post[s]));
       }
     }
 #pragma unroll

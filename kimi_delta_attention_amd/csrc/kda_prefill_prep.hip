@@ -430,6 +430,41 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     if (g == 0) BS[r] = bt;
     __syncthreads();
 
+    // A tile whose decay product leaves the range of the factored form takes
+    // the exact path: the diagonal tile's A and Mqk by running products (per
+    // channel half, as the fused kernel's waves form them; parked in this
+    // item's U frames, which phase 5 writes later, so that nothing extra stays
+    // in registers through phase 2), and, after phase 2, suffix products in
+    // place of E / P.  The decays are loaded again (the scan overwrote them).
+    const bool exact = tile_flagged<DK>(ES + w * DK, lane_x);
+    const float gsc = KIND == GATE_BOUNDED ? expf(gate.a_log[hd]) : 1.f;
+    auto alpha_of = [&](int kb, float* al) {
+      floatx4 a4[1][2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) a4[0][hf] = gate_load4<KIND>(gate, okc, thc, DK, 32 * kb + 16 * hf + 4 * g);
+      gate_finish_blocks<KIND, 1>(gate, gsc, a4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) al[e] = a4[0][e >> 2][e & 3];
+    };
+    if (exact) {
+      float dA[2][4], dM[2][4];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float al[NKH][8];
+#pragma unroll
+        for (int kk = 0; kk < NKH; ++kk) alpha_of(NKH * hh + kk, al[kk]);
+        tile_exact_sums<NKH>(al, kin + NKH * hh, qin + NKH * hh, tr, g, dA[hh], dM[hh]);
+      }
+      floatx4 ra, rm;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * w + 4 * g + i;
+        ra[i] = (j < r) ? scaled_sum(bt, dA[0][i], dA[1][i]) : 0.f;
+        rm[i] = (j <= r) ? dM[0][i] + dM[1][i] : 0.f;
+      }
+      *frame_ptr<floatx4>(im, IM::u_frame(w, 0), lane_x) = ra;
+      *frame_ptr<floatx4>(im, IM::u_frame(w, 1), lane_x) = rm;
+    }
 
     // ---- 2. operands of this lane's token, per 32-channel block
     bf16x8 kth[NKB], ktl[NKB];  // Ktil (split), kept until phase 6
@@ -473,9 +508,10 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
         qt8[e] = (bf16)(qq[e] * gam);
         gk[e] = kk8[e] * gam;
         const float ip = __builtin_amdgcn_rcpf(Pv[kb][e]);
-        kt[e] = kk8[e] * ((Ew[e] * ip) * post[e]);
+        const float ew = Ew[e] * ip;  // (an exact tile replaces it below)
+        kt[e] = kk8[e] * (ew * post[e]);
         vd[kb][e] = kk8[e] * ip;
-        vn[kb][e] = kk8[e] * (Ew[e] * ip);
+        vn[kb][e] = kk8[e] * ew;
       }
       bf16x8 yh, yl;
       split8(y, yh, yl);
@@ -494,6 +530,34 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
         for (int hf = 0; hf < 2; ++hf)
           *reinterpret_cast<floatx4*>(GC + 32 * kb + 16 * hf + 4 * g) =
               floatx4{gc[4 * hf], gc[4 * hf + 1], gc[4 * hf + 2], gc[4 * hf + 3]};
+      }
+    }
+    if (exact) {
+      // E / P_j of an exact tile as the product of the decays after token j
+      // (no factor above 1): Ktil and the key side of the later tiles again
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        float sfx[8], post[8], kk8[8], kt[8];
+        alpha_of(kb, sfx);
+        row_rscan_excl<8>(sfx);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          post[e] = 1.f;
+          kk8[e] = bfv(kin[kb][e >> 2][(e & 3) >> 1], e & 1);
+        }
+        for (int i = w + 1; i < 4; ++i)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const floatx4 e4 = *reinterpret_cast<const floatx4*>(ES + i * DK + 32 * kb + 16 * hf + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) post[4 * hf + e] *= e4[e];
+          }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kt[e] = kk8[e] * (sfx[e] * post[e]);
+          vn[kb][e] = kk8[e] * sfx[e];
+        }
+        split8(kt, kth[kb], ktl[kb]);
       }
     }
     __syncthreads();
@@ -551,6 +615,10 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
           const int j = 16 * n + 4 * g + i;
           rA[m][i] = (j < rq) ? scaled_sum(br, a0[i], a1[i]) : 0.f;
           rM[m][i] = (j <= rq) ? m0[i] + m1[i] : 0.f;
+        }
+        if (m == n && exact) {  // the diagonal tile from the exact sums
+          rA[m] = *frame_ptr<floatx4>(im, IM::u_frame(w, 0), lane_x);
+          rM[m] = *frame_ptr<floatx4>(im, IM::u_frame(w, 1), lane_x);
         }
       }
     }

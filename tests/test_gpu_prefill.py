@@ -345,3 +345,94 @@ def test_two_pass_on_caller_stream_and_in_a_graph():
         torch.cuda.synchronize()
         assert torch.equal(o, ref_o) and torch.equal(fs, ref_s)
         _run(inp, d, schedule="fused")  # eager work between replays
+
+
+def _fast_decay(B, T, H, D, seed, qkv_dtype=torch.bfloat16, channel=None):
+    """-log alpha ~ N(6, 0.5^2) per token and channel (a 16-token tile decays by
+    about e^-96, past fp32's range), or only in one channel with the workloads'
+    gate elsewhere: inside (0, 1] but beyond what the factored diagonal tile
+    can hold, so every such tile takes the exact path."""
+    inp = synth.make_dense(B, T, H, D, D, seed=seed, qkv_dtype=qkv_dtype, state_std=0.02)
+    g = torch.Generator().manual_seed(seed + 1)
+    fast = torch.exp(-(6.0 + 0.5 * torch.randn(inp.alpha.shape, generator=g,
+                                                 dtype=torch.float64))).float()
+    if channel is None:
+        inp.alpha = fast
+    else:
+        inp.alpha[..., channel] = fast[..., channel]
+    return inp
+
+
+@pytest.mark.parametrize("channel", [None, 5])
+def test_fast_decay_takes_the_exact_tile_path(channel):
+    """Both schedules against the oracle per (sequence, head), bitwise against
+    each other, and against the GPU decode step replayed token by token."""
+    d = dev()
+    inp = _fast_decay(1, 1000, 3, 128, seed=810 + (channel or 0), channel=channel)
+    o_ref, s_ref = oracle.recurrent(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
+                                    initial_state=inp.state)
+    res = {}
+    for sch in SCHEDULES:
+        o, s = _run(inp, d, schedule=sch)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o).all() and torch.isfinite(s).all(), sch
+        close(o, o_ref, TOL_BF16, "tokens")
+        close(s, s_ref, TOL_BF16, "state")
+        res[sch] = (o, s)
+    assert torch.equal(res["fused"][0], res["two_pass"][0])
+    assert torch.equal(res["fused"][1], res["two_pass"][1])
+    q, k, v, a, b = (x.to(d) for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta))
+    state = inp.state.to(d)
+    orep = torch.empty_like(res["two_pass"][0])
+    for t in range(q.shape[1]):
+        kda.decode_step(q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(),
+                        a[:, t].contiguous(), b[:, t].contiguous(), state, o=orep[:, t])
+    torch.cuda.synchronize()
+    close(res["two_pass"][0], orep, TOL_BF16, "tokens")
+    close(res["two_pass"][1], state, TOL_BF16, "state")
+
+
+def test_fast_decay_segmented_packed_and_fp32():
+    """The exact tile path under the segmented schedule on packed sequences,
+    and in the fp32-input kernel (tolerance 1e-5)."""
+    d = dev()
+    lengths = [300, 1, 0, 130, 64]
+    inp = synth.make_varlen(lengths, 2, 128, 128, seed=820)
+    g = torch.Generator().manual_seed(821)
+    inp.alpha = torch.exp(-(6.0 + 0.5 * torch.randn(inp.alpha.shape, generator=g,
+                                                      dtype=torch.float64))).float()
+    cu = inp.cu_seqlens.numpy()
+    o_ref, s_ref = oracle.recurrent(inp.q, inp.k, inp.v, inp.alpha, inp.beta, cu_seqlens=cu,
+                                    initial_state=inp.state)
+    o, s = kda.prefill_segmented(*(x.to(d) for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta)),
+                                 initial_state=inp.state.to(d), cu_seqlens=inp.cu_seqlens.to(d),
+                                 n_segments=3)
+    torch.cuda.synchronize()
+    close(o, o_ref, TOL_BF16, "tokens", cu=cu)
+    close(s, s_ref, TOL_BF16, "state")
+    f = _fast_decay(1, 200, 2, 64, seed=830, qkv_dtype=torch.float32)
+    o_ref, s_ref = oracle.recurrent(f.q, f.k, f.v, f.alpha, f.beta, initial_state=f.state)
+    o, s = _run(f, d)
+    torch.cuda.synchronize()
+    close(o, o_ref, TOL_F32, "tokens")
+    close(s, s_ref, TOL_F32, "state")
+
+
+def test_bounded_gate_at_its_floor_keeps_the_factored_path():
+    """K3's bounded gate at g = g_min = -5 for every token (logits far in the
+    saturated range): each 16-token tile decays by e^-80, just inside the
+    factored form's range, so no tile is flagged and the result matches."""
+    d = dev()
+    inp = synth.make_dense(1, 500, 2, 128, 128, seed=840, state_std=0.02)
+    z = torch.full(inp.alpha.shape, 60.0)
+    a_log = torch.zeros(2)
+    alpha = oracle.gate_alpha("bounded", z.numpy(), z.shape, a_log=a_log.numpy())
+    o_ref, s_ref = oracle.recurrent(inp.q, inp.k, inp.v, alpha, inp.beta,
+                                    initial_state=inp.state)
+    for sch in SCHEDULES:
+        o, s = kda.prefill_chunked(*(x.to(d) for x in (inp.q, inp.k, inp.v)), z.to(d),
+                                   inp.beta.to(d), initial_state=inp.state.to(d), schedule=sch,
+                                   gate="bounded", a_log=a_log.to(d))
+        torch.cuda.synchronize()
+        close(o, o_ref, TOL_BF16, "tokens")
+        close(s, s_ref, TOL_BF16, "state")
