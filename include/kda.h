@@ -160,6 +160,28 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_prefill_chunked_noalloc -- kda_prefill_chunked for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The same arguments without a workspace;
+ * bf16 inputs run the two-pass schedule with its workspace in a device array
+ * of the library (128 MiB, one per device, held until the process ends; its
+ * address is looked up on the first call on a device), so the results are
+ * bitwise those of kda_prefill_chunked with a workspace.  fp32 inputs need no
+ * workspace.  Calls neither hipMalloc nor hipFree.
+ *   Sizes whose kda_prefill_workspace_size exceeds 128 MiB (at Dk = Dv = 128:
+ *   more than 7 heads of one sequence) return KDA_ERR_INVALID_ARGUMENT.
+ *   Every call on a device shares that device's array: calls that overlap on
+ *   one device (other streams, other threads) race and must be serialised by
+ *   the caller.  Nothing in the array needs clearing between calls.
+ */
+kda_status kda_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
+                                       kda_dtype qkv_dtype, const float* alpha, const float* beta,
+                                       const float* initial_state, float* final_state,
+                                       void* o, kda_dtype o_dtype,
+                                       int B, int T, int H, int Dk, int Dv, int chunk,
+                                       void* stream);
+
+/*
  * kda_prefill_varlen -- packed variable-length prefill.  N sequences are
  * concatenated along the token axis (B = 1); sequence i occupies tokens
  * cu_seqlens[i] .. cu_seqlens[i+1]-1, has its own initial state and final state,

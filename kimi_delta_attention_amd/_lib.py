@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_F32, KDA_BF16 = 0, 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_HIP"}
 
-EXPORTED = ("kda_prefill_chunked", "kda_prefill_varlen", "kda_decode_step",
+EXPORTED = ("kda_prefill_chunked", "kda_prefill_chunked_noalloc", "kda_prefill_varlen",
+            "kda_decode_step",
             "kda_prefill_chunked_gated", "kda_prefill_varlen_gated", "kda_decode_step_gated",
             "kda_decode_verify", "kda_decode_commit", "kda_prologue", "kda_epilogue",
             "kda_decode_layer", "kda_prefill_layer", "kda_prefill_segmented",
@@ -70,6 +71,8 @@ def load() -> ctypes.CDLL:
     P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.kda_prefill_chunked.argtypes = [P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P]
     lib.kda_prefill_chunked.restype = I
+    lib.kda_prefill_chunked_noalloc.argtypes = [P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.kda_prefill_chunked_noalloc.restype = I
     lib.kda_prefill_varlen.argtypes = [P, P, P, I, P, P, P, I, I, P, P, P, I, I, I, I, I, P, Z, P]
     lib.kda_prefill_varlen.restype = I
     lib.kda_decode_step.argtypes = [P, P, P, I, P, P, P, P, I, I, I, I, I, P]
@@ -274,6 +277,38 @@ def prefill_chunked(q, k, v, alpha, beta, initial_state=None, out_dtype=torch.fl
         _ptr(q), _ptr(k), _ptr(v), _dt(q), ctypes.byref(g), _ptr(beta), _ptr(initial_state),
         _ptr(fs), _ptr(o), _dt(o), B, T, H, Dk, Dv, 64, _ptr(ws),
         0 if ws is None else ws.numel(), _stream(dev)))
+    return o, fs
+
+
+def prefill_chunked_noalloc(q, k, v, alpha, beta, initial_state=None,
+                            final_state: bool | torch.Tensor = True,
+                            o: torch.Tensor | None = None, out_dtype=torch.float32):
+    """kda_prefill_chunked_noalloc: the dense prefill with its workspace in the
+    library's device array (nothing allocated by the library; with `o` and a
+    `final_state` tensor given, nothing allocated here either).  Tensors as for
+    prefill_chunked.  Returns (o, final_state)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    _need(alpha, "alpha", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    if k.shape != q.shape or alpha.shape != q.shape or v.shape != (B, T, H, Dv) \
+            or beta.shape != (B, T, H):
+        raise ValueError("inconsistent shapes")
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev)
+        if initial_state.shape != (B, H, Dk, Dv):
+            raise ValueError("initial_state must be [B, H, Dk, Dv]")
+    if o is None:
+        o = torch.empty(B, T, H, Dv, dtype=out_dtype, device=dev)
+    else:
+        _out(o, "o", (B, T, H, Dv), _FLOAT_OUT, dev)
+    fs = _final_state(final_state, (B, H, Dk, Dv), dev)
+    _check(load().kda_prefill_chunked_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(alpha), _ptr(beta), _ptr(initial_state),
+        _ptr(fs), _ptr(o), _dt(o), B, T, H, Dk, Dv, 64, _stream(dev)))
     return o, fs
 
 

@@ -10,7 +10,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_layer.hip", "kda_prefill.hip",
            "kda_prefill_prep.hip",
-           "kda_prefill_state.hip", "kda_prefill_f32.hip"]
+           "kda_prefill_state.hip", "kda_prefill_f32.hip", "kda_noalloc.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

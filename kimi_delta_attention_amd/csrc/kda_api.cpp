@@ -293,6 +293,35 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_
                                    stream);
 }
 
+kda_status kda_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
+                                       kda_dtype qkv_dtype, const float* alpha, const float* beta,
+                                       const float* initial_state, float* final_state, void* o,
+                                       kda_dtype o_dtype, int B, int T, int H, int Dk, int Dv,
+                                       int chunk, void* stream) {
+  if (B < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B and T must be >= 0");
+  if (B == 0) return ok();
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (qkv_dtype == KDA_BF16 && T > 0) {  // the two-pass schedule and its workspace
+    if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk must be 64 (got %d)", chunk);
+    if (H <= 0 || Dk <= 0 || Dv <= 0)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "H, Dk and Dv must be positive");
+    const size_t need = kda::prefill_two_pass_bytes(B, H, Dk, Dv);
+    if (need == 0)
+      return fail(KDA_ERR_UNSUPPORTED, "unsupported head dims Dk=%d Dv=%d", Dk, Dv);
+    if (need > kda::kNoAllocScratchBytes)
+      return fail(KDA_ERR_INVALID_ARGUMENT,
+                  "B=%d, H=%d, Dk=%d, Dv=%d need %zu bytes of workspace, more than the %zu "
+                  "bytes of device scratch this entry point has",
+                  B, H, Dk, Dv, need, kda::kNoAllocScratchBytes);
+    if (hipError_t e = kda::noalloc_scratch(&ws); e != hipSuccess) return hip_status(e);
+    ws_bytes = kda::kNoAllocScratchBytes;
+  }
+  const kda_gate g = {KDA_GATE_ALPHA, alpha, nullptr, 0.f};
+  return prefill_common(q, k, v, qkv_dtype, &g, beta, nullptr, B, T, initial_state, final_state,
+                        o, o_dtype, H, Dk, Dv, chunk, ws, ws_bytes, stream);
+}
+
 kda_status kda_prefill_varlen_gated(const void* q, const void* k, const void* v,
                                     kda_dtype qkv_dtype, const kda_gate* gate, const float* beta,
                                     const int32_t* cu_seqlens, int N, int total_tokens,

@@ -100,6 +100,10 @@ hipError_t launch_epilogue(const EpilogueArgs& a);
 // handed in for a sequence shorter than three), without the prologue's rows.
 hipError_t launch_conv_state(const PrologueArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);      // dispatch (kda_prefill.hip)
+// (kda_noalloc.hip) the device scratch of the entry point that allocates
+// nothing: 128 MiB per device, its address on the current device
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_prefill_f32(const PrefillArgs& a);  // fp32 inputs (kda_prefill_f32.hip)
 bool prefill_supported(bool qkv_bf16, int Dk, int Dv);
 
