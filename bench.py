@@ -12,7 +12,11 @@ speculative-decoding round on the same sessions (verify 8 draft tokens, commit
 them), the step's roofline position, and the fp64 CPU oracle timed on this host
 on the same prefill workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+Also timed: the packed workload (16 sequences of seeded lengths in [1024, 16384],
+one kda_prefill_varlen call) and the 1,048,576-token prefill (one call, inputs
+generated on the device), each with its roofline position.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-long]
 """
 from __future__ import annotations
 
@@ -86,6 +90,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the 1,048,576-token prefill leg (its inputs take ~180 GB)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
@@ -197,8 +203,8 @@ def main():
     def commit():
         kda.decode_commit(sp.k, sp.v, sp.alpha, sp.beta, nacc, sp.state)
 
-    def timed(f, reps):
-        for _ in range(3):
+    def timed(f, reps, warm=3):
+        for _ in range(warm):
             f()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -294,19 +300,94 @@ def main():
     print(f"bench: 12-head share: segmented ({nseg}) {seg_ms:.3f} ms, two-pass {h2p_ms:.3f} ms, "
           f"fused {hfu_ms:.3f} ms", file=sys.stderr, flush=True)
 
+    # the packed workload: 16 sequences of seeded lengths in [1024, 16384], one
+    # kda_prefill_varlen call (two-pass, workspace allocated once)
+    wv = synth.WORKLOADS["varlen_16"]
+    vlen = synth.varlen_lengths(wv["N"], wv["lo"], wv["hi"], seed=wv["seed"])
+    vin = synth.make_varlen(vlen, wv["H"], wv["D"], wv["D"], seed=wv["seed"], device=d)
+    vtok, vH, vD, vN = sum(vlen), wv["H"], wv["D"], wv["N"]
+    vo = torch.empty(1, vtok, vH, vD, dtype=torch.float32, device=d)
+    vfs = torch.empty(vN, vH, vD, vD, dtype=torch.float32, device=d)
+    vws = torch.empty(kda._lib.varlen_workspace_size(vN, vtok, vH, vD, vD), dtype=torch.uint8,
+                      device=d)
+    var_ms = timed(lambda: kda.prefill_varlen(vin.q, vin.k, vin.v, vin.alpha, vin.beta,
+                                              vin.cu_seqlens, initial_state=vin.state,
+                                              final_state=vfs, o=vo, schedule="two_pass",
+                                              workspace=vws), max(3, args.steps // 5), warm=2)
+    # per token-head as prefill_bytes, plus an initial and a final state per sequence
+    var_bytes = vtok * vH * (2 * vD * 3 + 4 * vD + 4 + 4 * vD) + 2 * vN * vH * vD * vD * 4
+    print(f"bench: varlen_16 ({vtok} tokens) {var_ms:.3f} ms, "
+          f"{var_bytes / (var_ms / 1e3) / 1e9:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
+    varlen = {"workload": f"varlen_16: {vN} packed sequences, lengths seeded in [1024, 16384] "
+                          f"({vtok} tokens), H={vH}, d={vD}, one kda_prefill_varlen call",
+              "tokens": vtok, "ms_per_call": var_ms, "tokens_per_s": vtok / (var_ms / 1e3),
+              "roofline": {"bound": "hbm", "achieved": var_bytes / (var_ms / 1e3) / 1e9,
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": var_bytes / (var_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                           "algorithmic_bytes_per_call": var_bytes,
+                           "floor_ms": var_bytes / (HBM_PEAK_GBS * 1e9) * 1e3}}
+    del vin, vo, vfs, vws
+
     cpu = None
     if not args.no_cpu:
         import oracle
         nth = oracle.default_threads()
         print(f"bench: cpu oracle on the full prefill workload, {nth} threads", file=sys.stderr,
               flush=True)
-        host = [x.cpu() for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.state)]
-        tc = time.perf_counter()
-        oracle.recurrent(*host[:5], initial_state=host[5], nthreads=nth)
-        ct = time.perf_counter() - tc
+        # inputs upcast to fp64 before the clock starts: the timed region is the
+        # oracle's token loop alone; best of three passes
+        host = [x.cpu().double().numpy() for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta,
+                                                    inp.state)]
+        runs = []
+        for _ in range(3):
+            tc = time.perf_counter()
+            oracle.recurrent(*host[:5], initial_state=host[5], nthreads=nth)
+            runs.append(time.perf_counter() - tc)
+        ct = min(runs)
         cpu = {"value": B * T / ct, "unit": "tokens/s", "cores": nth, "kind": "oracle",
-               "sample": f"the whole workload (B={B}, T={T}, H={H}, d={D}), one pass, "
-                         f"fp64 token loop, {ct:.2f} s"}
+               "sample": f"the whole workload (B={B}, T={T}, H={H}, d={D}): fp64 token loop over "
+                         f"inputs already in fp64, best of 3 passes, {ct:.2f} s"}
+        del host
+
+    # the long-context workload: 1,048,576 tokens x 96 heads in one call (inputs
+    # generated on the device, about 176 GB; 128 windows of 8192 tokens)
+    long1m = None
+    if not args.no_long:
+        del inp, o, fs, ws, calib, calib2, dec, st, od, sp, osp, lay, lst, lcs, ly, ly1, lcs2, pl, \
+            py, lo_, pcs, hin, hws, ho, hfs
+        torch.cuda.empty_cache()
+        wl = synth.WORKLOADS["long_1m"]
+        free, _ = torch.cuda.mem_get_info(d)
+        if free > 200e9:
+            tg = time.perf_counter()
+            lin = synth.make_dense(wl["B"], wl["T"], wl["H"], wl["D"], wl["D"], seed=wl["seed"],
+                                   state_std=wl["state_std"], device=d)
+            torch.cuda.synchronize()
+            print(f"bench: long_1m inputs generated in {time.perf_counter() - tg:.1f} s",
+                  file=sys.stderr, flush=True)
+            lT, lH, lD = wl["T"], wl["H"], wl["D"]
+            lo = torch.empty(1, lT, lH, lD, dtype=torch.float32, device=d)
+            lfs = torch.empty(1, lH, lD, lD, dtype=torch.float32, device=d)
+            lws = torch.empty(kda.workspace_size(1, lT, lH, lD, lD), dtype=torch.uint8, device=d)
+            long_ms = timed(lambda: kda.prefill_chunked(lin.q, lin.k, lin.v, lin.alpha, lin.beta,
+                                                        initial_state=lin.state, final_state=lfs,
+                                                        o=lo, schedule="two_pass", workspace=lws),
+                            3, warm=1)
+            lbytes = prefill_bytes(1, lT, lH, lD, lD)
+            print(f"bench: long_1m {long_ms:.2f} ms, {lbytes / (long_ms / 1e3) / 1e9:.0f} GB/s "
+                  "algorithmic", file=sys.stderr, flush=True)
+            long1m = {"workload": "long_1m: B=1, T=1,048,576, H=96, d=128, one "
+                                  "kda_prefill_chunked call (two-pass, 128 windows)",
+                      "ms_per_call": long_ms, "tokens_per_s": lT / (long_ms / 1e3),
+                      "roofline": {"bound": "hbm", "achieved": lbytes / (long_ms / 1e3) / 1e9,
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": lbytes / (long_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                   "algorithmic_bytes_per_call": lbytes,
+                                   "floor_ms": lbytes / (HBM_PEAK_GBS * 1e9) * 1e3}}
+            del lin, lo, lfs, lws
+            torch.cuda.empty_cache()
+        else:
+            long1m = {"skipped": f"needs ~200 GB of device memory, {free / 1e9:.0f} GB free"}
 
     line = {
         "metric": "KDA prefill tokens/s (H=96,d=128) + decode-step state GB/s vs HBM peak",
@@ -368,6 +449,8 @@ def main():
             "segments": nseg, "segmented_ms": seg_ms, "two_pass_ms": h2p_ms, "fused_ms": hfu_ms,
             "tokens_per_s": hB * hT / (seg_ms / 1e3),
             "algorithmic_gbs": hbytes / (seg_ms / 1e3) / 1e9},
+        "prefill_varlen_16": varlen,
+        "prefill_long_1m": long1m,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

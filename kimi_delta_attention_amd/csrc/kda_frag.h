@@ -226,17 +226,31 @@ __device__ __forceinline__ floatx4 mma_ab(const bf16x8& ah, const bf16x8& al, co
   return c;
 }
 
-// W S with W rounded once (decaying gates) or split (no decay: the state never
-// forgets, so the rounding of W would accumulate), the same products in the
-// same order in both schedules
-template <bool WS>
-__device__ __forceinline__ floatx4 mma_w(const bf16x8& wh, const bf16x8& wl, const bf16x8& bh,
-                                         const bf16x8& bl, floatx4 c) {
-  if constexpr (WS) return mma_ab(wh, wl, bh, bl, c);
-  return mma_a1(wh, bh, bl, c);
+// W S with W rounded once, or split where the rounding would build up: the
+// products of mma_ab in the same order, the third (W's low part) only for a
+// split chunk, so both schedules give bitwise the same results.
+__device__ __forceinline__ floatx4 mma_w(bool split, const bf16x8& wh, const bf16x8& wl,
+                                         const bf16x8& bh, const bf16x8& bl, floatx4 c) {
+  c = mma_a1(wh, bh, bl, c);
+  if (split) c = mfma_bf16(wl, bh, c);
+  return c;
 }
-template <int KIND>
-constexpr bool w_split() { return KIND == GATE_NONE; }
+
+// The rounding of W (W S's left side) once to bf16 enters the state through
+// Ktil^T P and decays with it: where every key channel keeps less than half of
+// its state over the chunk (Gamma_C < 1/2), the error of a chunk is at most
+// doubled by the chunks after it, but where some channel keeps more (slow
+// decay, alpha = 1, the gate without decay) it accumulates over the sequence.
+// Such chunks keep W split (hi + lo).  A wave-uniform decision from the
+// chunk's Dk decays Gamma_C (a [Dk] row in LDS).
+constexpr float kKeepSplitW = 0.5f;
+template <int DK>
+__device__ __forceinline__ bool w_split_chunk(const float* GC, int lane) {
+  bool keep = false;
+#pragma unroll
+  for (int c = 0; c < DK; c += 64) keep = keep || GC[c + lane] >= kKeepSplitW;
+  return __builtin_amdgcn_ballot_w64(keep) != 0;
+}
 
 // Per-chunk operand images written by the first pass of the two-pass prefill
 // and read by the state pass.  Every image is a sequence of 1 KiB frames; a
@@ -245,16 +259,16 @@ constexpr bool w_split() { return KIND == GATE_NONE; }
 // Frames (w = token tile of the chunk, kb = 32-wide k block):
 //   W  [w][kb < DK/32][hi, lo]   A operand of W S (row = token, k = channel
 //                                position 32kb + 8g + 4h + i <-> channel
-//                                32kb + 16h + 4g + i); the low part only for
-//                                the gate without decay (w_split): with decay,
-//                                W rounded once is within the error budget
+//                                32kb + 16h + 4g + i); the low part written
+//                                only for a chunk that keeps W split
+//                                (w_split_chunk)
 //   Q  [w][kb < DK/32]           A operand of (Gamma*Q) S, same positions
 //   M  [w][kb < 2][hi, lo]       A operand of Mqk P (k = token position)
 //   K  [rt < DK/16][kb < 2][hi, lo]  A operand of Ktil^T P for state rows
 //                                16rt..16rt+15 (k = token position)
 //   U  [w][vt < DV/16]           U tile (tokens 16w.., values 16vt..) in the
 //                                accumulator layout, fp32
-// followed by Gamma_C (DK floats).
+// followed by Gamma_C (DK floats) and a flag word (non-zero: W is split).
 template <int DK, int DV>
 struct Images {
   static constexpr int NKB = DK / 32, NCHT = DK / 16, NVT = DV / 16;
@@ -265,7 +279,8 @@ struct Images {
   static constexpr int U = K + NCHT * 2 * 2;
   static constexpr int frames = U + 4 * NVT;
   static constexpr size_t g_off = (size_t)frames * 1024;
-  static constexpr size_t bytes = (g_off + DK * 4 + 255) / 256 * 256;
+  static constexpr size_t f_off = g_off + DK * 4;
+  static constexpr size_t bytes = (f_off + 4 + 255) / 256 * 256;
   static __device__ __forceinline__ int w_frame(int w, int kb, int part) { return W + (w * NKB + kb) * 2 + part; }
   static __device__ __forceinline__ int q_frame(int w, int kb) { return Q + w * NKB + kb; }
   static __device__ __forceinline__ int m_frame(int w, int kb, int part) { return M + (w * 2 + kb) * 2 + part; }

@@ -622,6 +622,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     // channel half, added at the end (the order the state pass uses)
     floatx4 accO[NCH];
     {
+      const bool wsplit = w_split_chunk<DK>(GC, lane_x);
       floatx4 accW[NCH], accW2[NCH], accO2[NCH];
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
@@ -639,7 +640,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
           const bf16x8 bl = frag_ld(ST + loS, ldS, vh0 + 16 * c + tr, 32 * kb, g);
           floatx4& aw = kb < NKH ? accW[c] : accW2[c];
           floatx4& ao = kb < NKH ? accO[c] : accO2[c];
-          aw = mma_w<w_split<KIND>()>(wh[kb], wl[kb], bh, bl, aw);
+          aw = mma_w(wsplit, wh[kb], wl[kb], bh, bl, aw);
           ao = mfma_bf16(aq, bh, ao);
           ao = mfma_bf16(aq, bl, ao);
         }

@@ -563,6 +563,9 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     __syncthreads();
     if (threadIdx.x < DK)
       __builtin_nontemporal_store(GC[threadIdx.x], reinterpret_cast<float*>(im + IM::g_off) + threadIdx.x);
+    const bool wsplit = w_split_chunk<DK>(GC, lane_x);  // W's low part kept for this chunk
+    if (threadIdx.x == 0)
+      __builtin_nontemporal_store(wsplit ? 1 : 0, reinterpret_cast<int*>(im + IM::f_off));
 
     // ---- 3. A and Mqk blocks (query tile m >= n, key tile n = w): the key
     // side k * (Gamma_r / Gamma_j restricted to the key) is this lane's
@@ -771,7 +774,7 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
           }
         }
         put_frame(im, IM::w_frame(w, kp, 0), lane_x, wh);
-        if constexpr (w_split<KIND>()) put_frame(im, IM::w_frame(w, kp, 1), lane_x, wl);
+        if (wsplit) put_frame(im, IM::w_frame(w, kp, 1), lane_x, wl);
       }
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt) {

@@ -163,7 +163,7 @@ __device__ __forceinline__ int seg_count(int nseg, int c_lo, int c_hi) {
 // the normal workgroup of segment s enters from seg_in[s] (the combine
 // kernel's entry states) and only the last segment writes the carried state.
 // With ns = 1, segment 0 runs exactly as the unsegmented pass.
-template <int DK, int DV, int BV, typename TOut, bool SUMMARY, bool WS>
+template <int DK, int DV, int BV, typename TOut, bool SUMMARY>
 __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     const unsigned char* __restrict__ img, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ cu_seqlens, const float* s_init, float* carry,
@@ -194,8 +194,18 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
   constexpr int nsl = SWC / BV;
   const int nsg = SUMMARY ? nseg - 1 : nseg;  // segments with a workgroup each
   const int total = nsg * n_seq * H * nsl;
+  // Workgroups are dealt round-robin over the 8 XCDs.  The nsl slices of one
+  // (segment, sequence, head) stay on one XCD (they fetch the same operand
+  // frames, so all but the first hit that XCD's L2), and consecutive
+  // (segment, sequence, head) pairs go to different XCDs: a window of a packed
+  // batch often holds chunks of only one or two sequences, whose pairs are
+  // consecutive, and they should spread over the whole device.
   int wid = blockIdx.x;
-  if ((total & 7) == 0) wid = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int npair = total / nsl;
+  if ((npair & 7) == 0) {
+    const int x = blockIdx.x & 7, r = blockIdx.x >> 3;
+    wid = ((r / nsl) * 8 + x) * nsl + r % nsl;
+  }
   const int sl = wid % nsl;
   const int h = (wid / nsl) % H;
   const int seq = (wid / (nsl * H)) % n_seq;
@@ -264,19 +274,28 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       floatx4 u[NVT];
       bf16x8 kh[2], kl[2];
       floatx4 gc;
+      int ws;       // this chunk keeps W split (its low frames were fetched)
+      int ws_next;  // the next chunk's flag, read one chunk ahead of its W frames
     };
-    // the operands of W S (fetched during the W S of the chunk before) and
-    // the rest (fetched during its state update)
-    auto fetch_w = [&](int c, Ops& op) {
+    // the chunk's W split flag (written by the first pass)
+    auto flag_of = [&](int c) -> int {
+      return *reinterpret_cast<const int*>(item_base(c) + IM::f_off);
+    };
+    // the operands of W S (fetched during the W S of the chunk before; W's low
+    // frames only for a split chunk) and the rest (fetched during its state
+    // update, with the flag of the chunk after)
+    auto fetch_w = [&](int c, int ws, Ops& op) {
       const unsigned char* b = item_base(c);
+      op.ws = ws;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         op.wh[kb] = *frame_ptr<bf16x8>(b, IM::w_frame(w, kb, 0), lane);
-        if constexpr (WS) op.wl[kb] = *frame_ptr<bf16x8>(b, IM::w_frame(w, kb, 1), lane);
+        if (ws) op.wl[kb] = *frame_ptr<bf16x8>(b, IM::w_frame(w, kb, 1), lane);
       }
     };
     auto fetch_r = [&](int c, Ops& op) {
       const unsigned char* b = item_base(c);
+      op.ws_next = flag_of(next_of(c));
       op.gc = *reinterpret_cast<const floatx4*>(b + IM::g_off + 4 * (16 * srt + 4 * (lane >> 4)));
 #pragma unroll
       for (int j = 0; j < NVT; ++j)
@@ -295,7 +314,9 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       const int g = lane_x >> 4;
       put_state(g, tr);
       __syncthreads();
-      fetch_w(next_of(c), nx);
+      const int ws_next = __builtin_amdgcn_readfirstlane(op.ws_next);
+      fetch_w(next_of(c), ws_next, nx);
+      const bool ws = op.ws != 0;
       // ---- W S over both channel halves (separate chains, low half first)
       // and P = U - W S, to LDS as [value][token position]: token
       // 32kb + 16h + 4g + i sits at position 32kb + 8g + 4h + i (the order of
@@ -313,7 +334,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
           const bf16x8 bh = frag_ld(ST, ldS, 16 * vt + tr, 32 * kb, g);
           const bf16x8 bl = frag_ld(ST + loS, ldS, 16 * vt + tr, 32 * kb, g);
           floatx4& acc = kb < NKH ? a0[vt] : a1[vt];
-          acc = mma_w<WS>(op.wh[kb], op.wl[kb], bh, bl, acc);
+          acc = mma_w(ws, op.wh[kb], op.wl[kb], bh, bl, acc);
         }
       const int pos = 32 * (w >> 1) + 8 * g + 4 * (w & 1);
 #pragma unroll
@@ -341,7 +362,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     };
     if (c_lo < c_hi) {
       Ops X, Y;
-      fetch_w(c_lo, X);
+      fetch_w(c_lo, __builtin_amdgcn_readfirstlane(flag_of(c_lo)), X);
       fetch_r(c_lo, X);
       wait_vm0();
       for (int c = c_lo; c < c_hi; c += 2) {
@@ -659,13 +680,13 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t* __restr
 // is bound by frame fetches per compute unit, not by idle compute units.
 constexpr int BV_STATE = 64;
 
-template <int DK, int DV, typename TOut, bool SUMMARY, bool WS>
-hipError_t launch_state_w(const PrefillArgs& a, const unsigned char* img, const int32_t* chunk_off,
+template <int DK, int DV, typename TOut, bool SUMMARY>
+hipError_t launch_state_t(const PrefillArgs& a, const unsigned char* img, const int32_t* chunk_off,
                           float* carry, long long tok_lo, long long tok_hi, int cap,
                           const SegmentArgs& sg) {
   constexpr int BV = BV_STATE;
   using L = StatePlan<DK, BV>;
-  auto kern = prefill_state_kernel<DK, DV, BV, TOut, SUMMARY, WS>;
+  auto kern = prefill_state_kernel<DK, DV, BV, TOut, SUMMARY>;
   static bool attr_set = false;  // per instantiation; idempotent if raced
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -680,16 +701,6 @@ hipError_t launch_state_w(const PrefillArgs& a, const unsigned char* img, const 
                      a.cu_seqlens, a.initial_state, carry, (TOut*)a.o, a.n_seq, a.T, a.H, tok_lo,
                      tok_hi, cap, sg.nseg, sg.seg_in, sg.summ);
   return hipGetLastError();
-}
-
-// W split in the images only for the gate without decay
-template <int DK, int DV, typename TOut, bool SUMMARY>
-hipError_t launch_state_t(const PrefillArgs& a, const unsigned char* img, const int32_t* chunk_off,
-                          float* carry, long long tok_lo, long long tok_hi, int cap,
-                          const SegmentArgs& sg) {
-  return a.gate.kind == GATE_NONE
-             ? launch_state_w<DK, DV, TOut, SUMMARY, true>(a, img, chunk_off, carry, tok_lo, tok_hi, cap, sg)
-             : launch_state_w<DK, DV, TOut, SUMMARY, false>(a, img, chunk_off, carry, tok_lo, tok_hi, cap, sg);
 }
 
 template <int DK, int DV>

@@ -51,12 +51,13 @@ def test_workspace_sizes():
     """Two-pass workspace: a chunk table (B + 1 int32), one carried fp32 state per
     (sequence, head), and the operand blocks of one 8192-token window, (128 + B) * H
     of them; each block holds the frames of W, (Gamma*Q), Mqk, Ktil^T and U plus
-    Gamma_C, rounded to 256 B.  Like the state, it does not depend on T."""
+    Gamma_C and the chunk's W-split flag, rounded to 256 B.  Like the state, it
+    does not depend on T."""
     frames = {(128, 128): 4 * 4 * 2 + 4 * 4 + 16 + 8 * 4 + 4 * 8,
               (64, 64): 4 * 2 * 2 + 4 * 2 + 16 + 4 * 4 + 4 * 4}
     up = lambda x: -(-x // 256) * 256
     for (dk, dv), f in frames.items():
-        blk = up(f * 1024 + dk * 4)
+        blk = up(f * 1024 + dk * 4 + 4)
         for B, H in ((1, 1), (1, 96), (3, 2), (16, 96)):
             want = up((B + 1) * 4) + up(B * H * dk * dv * 4) + (128 + B) * H * blk
             sizes = {kda.workspace_size(B, T, H, dk, dv) for T in (1, 256, 8192, 1 << 20)}
