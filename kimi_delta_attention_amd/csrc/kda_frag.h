@@ -266,9 +266,15 @@ __device__ __forceinline__ bool w_split_chunk(const float* GC, int lane) {
 //   M  [w][kb < 2][hi, lo]       A operand of Mqk P (k = token position)
 //   K  [rt < DK/16][kb < 2][hi, lo]  A operand of Ktil^T P for state rows
 //                                16rt..16rt+15 (k = token position)
-//   U  [w][vt < DV/16]           U tile (tokens 16w.., values 16vt..) in the
-//                                accumulator layout, fp32
+//   T  [w][kb < 2][hi, lo]       A operand of U = T Diag(b) V (row = token r,
+//                                k = token j in order); the frames of key
+//                                blocks after the tile are zero and not written
+//   V  [64 tokens][DV] bf16      the chunk's v rows, written only by the layer
+//                                prefill (its v exists only inside the first
+//                                pass); otherwise the state pass reads v itself
 // followed by Gamma_C (DK floats) and a flag word (non-zero: W is split).
+// U is not stored: the state pass forms it from T Diag(b) and v (12 KiB of
+// T frames against 32 KiB of fp32 U at Dv = 128, and v is read once).
 template <int DK, int DV>
 struct Images {
   static constexpr int NKB = DK / 32, NCHT = DK / 16, NVT = DV / 16;
@@ -276,8 +282,10 @@ struct Images {
   static constexpr int Q = W + 4 * NKB * 2;
   static constexpr int M = Q + 4 * NKB;
   static constexpr int K = M + 4 * 2 * 2;
-  static constexpr int U = K + NCHT * 2 * 2;
-  static constexpr int frames = U + 4 * NVT;
+  static constexpr int TB = K + NCHT * 2 * 2;
+  static constexpr int V = TB + 4 * 2 * 2;
+  static constexpr int frames = V + DV / 8;  // 64 rows of DV bf16
+  static constexpr size_t v_off = (size_t)V * 1024;
   static constexpr size_t g_off = (size_t)frames * 1024;
   static constexpr size_t f_off = g_off + DK * 4;
   static constexpr size_t bytes = (f_off + 4 + 255) / 256 * 256;
@@ -285,7 +293,7 @@ struct Images {
   static __device__ __forceinline__ int q_frame(int w, int kb) { return Q + w * NKB + kb; }
   static __device__ __forceinline__ int m_frame(int w, int kb, int part) { return M + (w * 2 + kb) * 2 + part; }
   static __device__ __forceinline__ int k_frame(int rt, int kb, int part) { return K + (rt * 2 + kb) * 2 + part; }
-  static __device__ __forceinline__ int u_frame(int w, int vt) { return U + w * NVT + vt; }
+  static __device__ __forceinline__ int tb_frame(int w, int kb, int part) { return TB + (w * 2 + kb) * 2 + part; }
 };
 
 // 16-byte fragment of frame f of an image at `base`, lane `lane`.

@@ -59,7 +59,7 @@ constexpr int NTH_P = 256;  // four waves, one per token tile
 //   A, Mqk   (3-4):  AF (b A), MQ (Mqk)                           [token][token] fp32
 //   solve    (4):    TF (T; its unused upper blocks hold the diagonal solve's
 //                    N^2 / N^4 scratch)
-//   T b, V   (5):    TB (T Diag(b), split), VS (V)
+//   T b      (5):    TB (T Diag(b), split); VS (V) is no longer staged
 //   Ktil     (6):    KT (split)                                   [token][channel]
 // GK (Gamma*K, [token][channel]) lives from phase 2 to 5; ES / GC / BS are small.
 template <int DK, int DV>
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
   constexpr int NCHT = DK / 16;  // 16-channel tiles
   constexpr int NVT = DV / 16;   // 16-value tiles
   constexpr int NVL = DV / 32;   // 16-byte v loads per lane
-  constexpr int ldK = L::ldK, ldA = L::ldA, ldT = L::ldT, ldV = L::ldV;
+  constexpr int ldK = L::ldK, ldA = L::ldA, ldT = L::ldT;
   constexpr int loK = CH * ldK, loT = CH * ldT;
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -132,7 +132,6 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
   float* MQ = reinterpret_cast<float*>(smem + L::oMQ);
   float* TF = reinterpret_cast<float*>(smem + L::oTF);
   bf16* TB = reinterpret_cast<bf16*>(smem + L::oTB);
-  bf16* VS = reinterpret_cast<bf16*>(smem + L::oVS);
   bf16* KT = reinterpret_cast<bf16*>(smem + L::oKT);
   bf16* GK = reinterpret_cast<bf16*>(smem + L::oGK);
   float* ES = reinterpret_cast<float*>(smem + L::oES);  // [4][DK] tile decays
@@ -255,17 +254,21 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     const bool okc = r < nv;
     const size_t thc = (size_t)(tok0 + r) * H + hd;
 
-    // v of the wave's token tile, staged in phase 5: load j covers whole rows
-    // (DV / 8 lanes of 16 bytes per row, rows 16 w + VRJ j + lane / (DV / 8)),
-    // so that each row is read in one coalesced piece
+    // (layer prologue) the raw v rows of the wave's token tile: load j covers
+    // whole rows (DV / 8 lanes of 16 bytes per row, rows 16 w + VRJ j +
+    // lane / (DV / 8)), so that each row is read in one coalesced piece.  The
+    // prologue's v goes into the operand block for the state pass; without the
+    // prologue the state pass reads v itself.
     constexpr int VLR = DV / 8, VRJ = 64 / VLR;
     const int vrow = 16 * w + lane_x / VLR, vcol = 8 * (lane_x % VLR);
     uint4v vin[NVL];
+    if constexpr (PRO) {
 #pragma unroll
-    for (int j = 0; j < NVL; ++j) {
-      const int rv = vrow + VRJ * j;
-      vin[j] = rv < nv ? *reinterpret_cast<const uint4v*>(v + ((size_t)(tok0 + rv) * H + hd) * DV + vcol)
-                       : uint4v{0u, 0u, 0u, 0u};
+      for (int j = 0; j < NVL; ++j) {
+        const int rv = vrow + VRJ * j;
+        vin[j] = rv < nv ? *reinterpret_cast<const uint4v*>(v + ((size_t)(tok0 + rv) * H + hd) * DV + vcol)
+                         : uint4v{0u, 0u, 0u, 0u};
+      }
     }
 
     // prologue: the three inputs before the chunk (fp32)
@@ -433,8 +436,8 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     // A tile whose decay product leaves the range of the factored form takes
     // the exact path: the diagonal tile's A and Mqk by running products (per
     // channel half, as the fused kernel's waves form them; parked in this
-    // item's U frames, which phase 5 writes later, so that nothing extra stays
-    // in registers through phase 2), and, after phase 2, suffix products in
+    // wave's first T frames, which phase 5 writes later, so that nothing extra
+    // stays in registers through phase 2), and, after phase 2, suffix products in
     // place of E / P.  The decays are loaded again (the scan overwrote them).
     const bool exact = tile_flagged<DK>(ES + w * DK, lane_x);
     const float gsc = KIND == GATE_BOUNDED ? expf(gate.a_log[hd]) : 1.f;
@@ -462,8 +465,8 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
         ra[i] = (j < r) ? scaled_sum(bt, dA[0][i], dA[1][i]) : 0.f;
         rm[i] = (j <= r) ? dM[0][i] + dM[1][i] : 0.f;
       }
-      *frame_ptr<floatx4>(im, IM::u_frame(w, 0), lane_x) = ra;
-      *frame_ptr<floatx4>(im, IM::u_frame(w, 1), lane_x) = rm;
+      *frame_ptr<floatx4>(im, IM::tb_frame(w, 0, 0), lane_x) = ra;
+      *frame_ptr<floatx4>(im, IM::tb_frame(w, 0, 1), lane_x) = rm;
     }
 
     // ---- 2. operands of this lane's token, per 32-channel block
@@ -620,8 +623,8 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
           rM[m][i] = (j <= rq) ? m0[i] + m1[i] : 0.f;
         }
         if (m == n && exact) {  // the diagonal tile from the exact sums
-          rA[m] = *frame_ptr<floatx4>(im, IM::u_frame(w, 0), lane_x);
-          rM[m] = *frame_ptr<floatx4>(im, IM::u_frame(w, 1), lane_x);
+          rA[m] = *frame_ptr<floatx4>(im, IM::tb_frame(w, 0, 0), lane_x);
+          rM[m] = *frame_ptr<floatx4>(im, IM::tb_frame(w, 0, 1), lane_x);
         }
       }
     }
@@ -725,9 +728,9 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
       }
     }
 
-    // ---- 5. TB = T Diag(beta) (split, [r][j]) and V ([token][value]); then
-    // W^T = (Gamma*K)^T (T Diag b)^T for this tile's tokens, all channels, as
-    // the split operand image of W S, and U = T Diag(b) V, all values
+    // ---- 5. TB = T Diag(beta) (split, [r][j]); then W^T = (Gamma*K)^T
+    // (T Diag b)^T for this tile's tokens, all channels, as the operand image
+    // of W S, and T Diag(b) as the operand image of U
 #pragma unroll
     for (int it = 0; it < CH * CH / 4 / NTH_P; ++it) {
       const int idx = 64 * w4 + lane_x + NTH_P * it;
@@ -739,9 +742,12 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
       for (int e = 0; e < 4; ++e) x4[e] = (j0 + e <= rr) ? t4[e] * b4[e] : 0.f;
       st_split4(TB + rr * ldT + j0, loT, x4);
     }
+    if constexpr (PRO) {  // the prologue's v rows (zero past the chunk's end)
 #pragma unroll
-    for (int j = 0; j < NVL; ++j)
-      *reinterpret_cast<uint4v*>(VS + (vrow + VRJ * j) * ldV + vcol) = vin[j];
+      for (int j = 0; j < NVL; ++j)
+        __builtin_nontemporal_store(
+            vin[j], reinterpret_cast<uint4v*>(im + IM::v_off + ((size_t)(vrow + VRJ * j) * DV + vcol) * 2));
+    }
     __syncthreads();
     {
       bf16x8 tbh[2], tbl[2];
@@ -776,20 +782,16 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
         put_frame(im, IM::w_frame(w, kp, 0), lane_x, wh);
         if (wsplit) put_frame(im, IM::w_frame(w, kp, 1), lane_x, wl);
       }
+      // T Diag(b) as the A operand of U = T Diag(b) V, which the state pass
+      // forms (the frames of key blocks after the tile are zero, not stored)
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          if (kb > (w >> 1)) continue;
-          const bf16x8 b = frag_tr(VS, ldV, 16 * vt, 32 * kb + 8 * g, 32 * kb + 8 * g + 4, tr);
-          acc = mfma_bf16(tbh[kb], b, acc);
-          acc = mfma_bf16(tbl[kb], b, acc);
-        }
-        put_frame(im, IM::u_frame(w, vt), lane_x, acc);
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb > (w >> 1)) continue;
+        put_frame(im, IM::tb_frame(w, kb, 0), lane_x, tbh[kb]);
+        put_frame(im, IM::tb_frame(w, kb, 1), lane_x, tbl[kb]);
       }
     }
-    __syncthreads();  // TB / VS / GK reads done; KT overwrites the region
+    __syncthreads();  // TB / GK reads done; KT overwrites the region
 
     // ---- 6. Ktil ([token][channel], split) into the A operand images of
     // Ktil^T P, 16 state rows per frame

@@ -57,10 +57,14 @@ struct StatePlan {
   // o staging of each output wave: 16 rows x BV values fp32, row stride BV + 16
   // floats (16-lane groups of the 16-byte accesses hit distinct banks)
   static constexpr int ldO = BV + 16;
-  static constexpr int ST = BV * ldS * 2 * 2, PT = BV * ldP * 2 * 2, OS = 4 * 16 * ldO * 4;
-  static constexpr int oST = 0, oPT = ST, oOS = ST + PT, total = ST + PT + OS;
+  // v rows of a chunk, [token][value] bf16, two buffers (the chunk after the
+  // current one is staged while U of the current one is formed)
+  static constexpr int ldV = BV + 8;
+  static constexpr int ST = BV * ldS * 2 * 2, PT = BV * ldP * 2 * 2, OS = 4 * 16 * ldO * 4,
+                       VS = CH * ldV * 2;
+  static constexpr int oST = 0, oPT = ST, oOS = ST + PT, oVS = oOS + OS, total = oVS + 2 * VS;
   static_assert(total <= 163840, "LDS budget");
-  static_assert(oOS % 16 == 0, "alignment");
+  static_assert(oOS % 16 == 0 && oVS % 16 == 0 && VS % 16 == 0, "alignment");
 };
 
 // Lane quad transpose: lane b of each group of four lanes holds x[i] = element
@@ -167,8 +171,9 @@ template <int DK, int DV, int BV, typename TOut, bool SUMMARY>
 __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     const unsigned char* __restrict__ img, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ cu_seqlens, const float* s_init, float* carry,
-    TOut* __restrict__ o, int n_seq, int T, int H, long long tok_lo, long long tok_hi, int cap,
-    int nseg, const float* __restrict__ seg_in, float* __restrict__ summ) {
+    TOut* __restrict__ o, const bf16* __restrict__ v, int n_seq, int T, int H, long long tok_lo,
+    long long tok_hi, int cap, int nseg, const float* __restrict__ seg_in,
+    float* __restrict__ summ) {
   static_assert(BV == 32 || BV == 64, "value slice of 32 or 64 columns");
   constexpr int SWC = SUMMARY ? DK + DV : DV;  // columns the workgroups carry
   using L = StatePlan<DK, BV>;
@@ -177,13 +182,14 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
   constexpr int NKH = NKB / 2;                   // 32-channel blocks per channel half
   constexpr int NVT = BV / 16;                   // value tiles of the slice
   constexpr int KVT = DK == 128 ? NVT : NVT / 2;  // value tiles of this wave's state rows
-  constexpr int ldS = L::ldS, ldP = L::ldP, ldO = L::ldO;
+  constexpr int ldS = L::ldS, ldP = L::ldP, ldO = L::ldO, ldV = L::ldV;
   constexpr int loS = BV * ldS, loP = BV * ldP;
 
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* ST = reinterpret_cast<bf16*>(smem + L::oST);
   bf16* PT = reinterpret_cast<bf16*>(smem + L::oPT);
   float* OS = reinterpret_cast<float*>(smem + L::oOS);
+  bf16* VS0 = reinterpret_cast<bf16*>(smem + L::oVS);  // v rows, buffers 0 and 1
 
   const int tid = threadIdx.x;
   const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -269,11 +275,14 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
 
   if (role == 0) {
     // ---- chain waves
+    static_assert(BV == 64, "v rows staged by the 256 chain threads, 32 bytes each");
     struct Ops {
       bf16x8 wh[NKB], wl[NKB];
-      floatx4 u[NVT];
+      bf16x8 th[2], tl[2];   // T Diag(b) of the tile's rows (A operand of U)
+      floatx4 u[NVT];        // U of the tile, formed during the chunk before
       bf16x8 kh[2], kl[2];
       floatx4 gc;
+      uint4v vr[2];          // this thread's v rows of the chunk after
       int ws;       // this chunk keeps W split (its low frames were fetched)
       int ws_next;  // the next chunk's flag, read one chunk ahead of its W frames
     };
@@ -281,9 +290,9 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     auto flag_of = [&](int c) -> int {
       return *reinterpret_cast<const int*>(item_base(c) + IM::f_off);
     };
-    // the operands of W S (fetched during the W S of the chunk before; W's low
-    // frames only for a split chunk) and the rest (fetched during its state
-    // update, with the flag of the chunk after)
+    // the operands of W S and of U (fetched during the W S of the chunk before;
+    // W's low frames only for a split chunk) and the rest (fetched during its
+    // state update, with the flag of the chunk after)
     auto fetch_w = [&](int c, int ws, Ops& op) {
       const unsigned char* b = item_base(c);
       op.ws = ws;
@@ -292,20 +301,73 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
         op.wh[kb] = *frame_ptr<bf16x8>(b, IM::w_frame(w, kb, 0), lane);
         if (ws) op.wl[kb] = *frame_ptr<bf16x8>(b, IM::w_frame(w, kb, 1), lane);
       }
+      if (!u_zero) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          // key block 1 of tiles 0 and 1 lies after the tile: its frames are
+          // not stored and its products are not formed
+          const int kbt = kb > (w >> 1) ? 0 : kb;
+          op.th[kb] = *frame_ptr<bf16x8>(b, IM::tb_frame(w, kbt, 0), lane);
+          op.tl[kb] = *frame_ptr<bf16x8>(b, IM::tb_frame(w, kbt, 1), lane);
+        }
+      }
+    };
+    // v rows of chunk c for this thread: row tid / 4, columns 16 (tid % 4) and
+    // + 8 of the slice (zero past the chunk's end); from v, or from the
+    // operand block where the first pass formed v (the layer prologue)
+    const int vrow = tid >> 2, vcol = 16 * (tid & 3);
+    auto load_v = [&](int c, uint4v (&vr)[2]) {
+      if (u_zero) return;
+      const long long c0 = (long long)c * CH;
+      const int nvc = (int)(len - c0 < CH ? len - c0 : CH);
+      const int col = 16 * vt0 + vcol;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (vrow >= nvc) {
+          vr[j] = uint4v{0u, 0u, 0u, 0u};
+        } else if (v) {
+          vr[j] = *reinterpret_cast<const uint4v*>(v + ((size_t)(start + c0 + vrow) * H + h) * DV +
+                                                   col + 8 * j);
+        } else {
+          vr[j] = *reinterpret_cast<const uint4v*>(item_base(c) + IM::v_off +
+                                                   ((size_t)vrow * DV + col + 8 * j) * 2);
+        }
+      }
+    };
+    auto put_v = [&](int c, const uint4v (&vr)[2]) {
+      if (u_zero) return;
+      bf16* VS = VS0 + (c & 1) * (CH * ldV);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) *reinterpret_cast<uint4v*>(VS + vrow * ldV + vcol + 8 * j) = vr[j];
+    };
+    // U = T Diag(b) V of the tile, every value of the slice (the first pass's
+    // products, in its order); zero for M's columns of a summary
+    auto form_u = [&](int c, Ops& op) {
+      const int tr = lane & 15, g = lane >> 4;
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) op.u[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (u_zero) return;
+      const bf16* VS = VS0 + (c & 1) * (CH * ldV);
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if (kb > (w >> 1)) continue;
+          const bf16x8 bv = frag_tr(VS, ldV, 16 * vt, 32 * kb + 8 * g, 32 * kb + 8 * g + 4, tr);
+          op.u[vt] = mfma_bf16(op.th[kb], bv, op.u[vt]);
+          op.u[vt] = mfma_bf16(op.tl[kb], bv, op.u[vt]);
+        }
     };
     auto fetch_r = [&](int c, Ops& op) {
       const unsigned char* b = item_base(c);
       op.ws_next = flag_of(next_of(c));
       op.gc = *reinterpret_cast<const floatx4*>(b + IM::g_off + 4 * (16 * srt + 4 * (lane >> 4)));
 #pragma unroll
-      for (int j = 0; j < NVT; ++j)
-        op.u[j] = u_zero ? floatx4{0.f, 0.f, 0.f, 0.f}
-                         : *frame_ptr<floatx4>(b, IM::u_frame(w, vt0 + j), lane);
-#pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         op.kh[kb] = *frame_ptr<bf16x8>(b, IM::k_frame(srt, kb, 0), lane);
         op.kl[kb] = *frame_ptr<bf16x8>(b, IM::k_frame(srt, kb, 1), lane);
       }
+      load_v(next_of(c), op.vr);
     };
     auto chunk = [&](int c, const Ops& op, Ops& nx) {
       int lane_x = lane;
@@ -313,6 +375,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       const int tr = lane_x & 15;
       const int g = lane_x >> 4;
       put_state(g, tr);
+      put_v(next_of(c), op.vr);  // read after the barrier below, by the U of the next chunk
       __syncthreads();
       const int ws_next = __builtin_amdgcn_readfirstlane(op.ws_next);
       fetch_w(next_of(c), ws_next, nx);
@@ -339,10 +402,10 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       const int pos = 32 * (w >> 1) + 8 * g + 4 * (w & 1);
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt) {
-        const floatx4 ws = a0[vt] + a1[vt];
+        const floatx4 wsv = a0[vt] + a1[vt];
         float pv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[i] = op.u[vt][i] - ws[i];
+        for (int i = 0; i < 4; ++i) pv[i] = op.u[vt][i] - wsv[i];
         st_split4(PT + (16 * vt + tr) * ldP + pos, loP, pv);
       }
       __syncthreads();
@@ -359,10 +422,17 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
           Sacc[j] = mma_ab(op.kh[kb], op.kl[kb], bh, bl, Sacc[j]);
         }
       }
+      // ---- U of the next chunk (its v rows were staged before the first
+      // barrier of this chunk), off the state's dependency chain
+      form_u(next_of(c), nx);
     };
     if (c_lo < c_hi) {
       Ops X, Y;
       fetch_w(c_lo, __builtin_amdgcn_readfirstlane(flag_of(c_lo)), X);
+      load_v(c_lo, X.vr);
+      put_v(c_lo, X.vr);
+      __syncthreads();  // (matched by the output waves)
+      form_u(c_lo, X);
       fetch_r(c_lo, X);
       wait_vm0();
       for (int c = c_lo; c < c_hi; c += 2) {
@@ -493,6 +563,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       Ops X, Y;
       fetch_w(c_lo, X);
       fetch_r(c_lo, X);
+      __syncthreads();  // the chain waves' staging of the first chunk's v rows
       wait_vm0();
       for (int c = c_lo; c < c_hi; c += 2) {
         chunk(c, X, Y);
@@ -697,9 +768,12 @@ hipError_t launch_state_t(const PrefillArgs& a, const unsigned char* img, const 
   const int cols = SUMMARY ? DK + DV : DV;
   const int grid = (SUMMARY ? sg.nseg - 1 : sg.nseg) * a.n_seq * a.H * (cols / BV);
   if (grid <= 0) return hipSuccess;
+  // the layer prefill's v exists only in the operand blocks (the first pass's
+  // prologue formed it); otherwise the state pass reads the caller's v
+  const bf16* v = a.pro ? nullptr : static_cast<const bf16*>(a.v);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH_S), L::total, (hipStream_t)a.stream, img, chunk_off,
-                     a.cu_seqlens, a.initial_state, carry, (TOut*)a.o, a.n_seq, a.T, a.H, tok_lo,
-                     tok_hi, cap, sg.nseg, sg.seg_in, sg.summ);
+                     a.cu_seqlens, a.initial_state, carry, (TOut*)a.o, v, a.n_seq, a.T, a.H,
+                     tok_lo, tok_hi, cap, sg.nseg, sg.seg_in, sg.summ);
   return hipGetLastError();
 }
 
