@@ -34,6 +34,8 @@
 // twice in a workgroup.  The fused kernel computes the same products with the
 // same accumulation order (the two channel halves as separate chains, low half
 // first), so both schedules give bitwise the same results.
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_frag.h"
 #include "kda_internal.h"
@@ -53,10 +55,15 @@ constexpr int NTH_S = 512;
 
 template <int DK, int BV>
 struct StatePlan {
-  static constexpr int ldS = DK + 8, ldP = CH + 8;
-  // o staging of each output wave: 16 rows x BV values fp32, row stride BV + 16
-  // floats (16-lane groups of the 16-byte accesses hit distinct banks)
-  static constexpr int ldO = BV + 16;
+  // Row strides of 8 (mod 16) dwords, and in ST and PT the 16-byte chunks of
+  // a row swapped in pairs on rows with bit 2 set (chunk c at c ^ ((row >> 2)
+  // & 1)): measured on gfx950, the 16-byte operand reads (row = lane % 16,
+  // chunk = lane / 16) and 16-byte writes then take no bank conflicts, where a
+  // stride of 4 (mod 8) dwords doubles the reads.  The 8-byte writes of the
+  // split halves keep a 2-way conflict.
+  static constexpr int ldS = DK + 16, ldP = CH + 16;
+  // o staging of each output wave: 16 rows x BV values fp32
+  static constexpr int ldO = BV + 8;
   // v rows of a chunk, [token][value] bf16, two buffers (the chunk after the
   // current one is staged while U of the current one is formed)
   static constexpr int ldV = BV + 8;
@@ -260,9 +267,10 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
   };
   // the state as the B operand of W S and (Gamma*Q) S: [value][channel
   // position], position 32kb + 8g + 4h + i holds channel 32kb + 16h + 4g + i
-  auto put_state = [&](int g, int tr) {
+  // (gs: the lane's chunk g after the swizzle of its row 16 j + tr)
+  auto put_state = [&](int gs, int tr) {
     const int c0r = 16 * srt;
-    const int pos = 32 * (c0r >> 5) + 8 * g + 4 * ((c0r >> 4) & 1);
+    const int pos = 32 * (c0r >> 5) + 8 * gs + 4 * ((c0r >> 4) & 1);
 #pragma unroll
     for (int j = 0; j < KVT; ++j) {
       float x4[4] = {Sacc[j][0], Sacc[j][1], Sacc[j][2], Sacc[j][3]};
@@ -274,7 +282,10 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
   auto next_of = [&](int c) { return c + 1 < c_hi ? c + 1 : c; };
 
   if (role == 0) {
-    // ---- chain waves
+    // ---- chain waves: they carry the state's dependency chain, so they take
+    // the issue priority over the output wave of their SIMD (whose work has
+    // slack until the chunk's barriers)
+    __builtin_amdgcn_s_setprio(2);
     static_assert(BV == 64, "v rows staged by the 256 chain threads, 32 bytes each");
     struct Ops {
       bf16x8 wh[NKB], wl[NKB];
@@ -348,15 +359,22 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       for (int vt = 0; vt < NVT; ++vt) op.u[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
       if (u_zero) return;
       const bf16* VS = VS0 + (c & 1) * (CH * ldV);
+      // one loop per number of key blocks (1 for tiles 0, 1; 2 for tiles 2,
+      // 3), so that no branch cuts it (see W S)
+      auto u_loop = [&](auto nkb) {
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt)
+        for (int vt = 0; vt < NVT; ++vt)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          if (kb > (w >> 1)) continue;
-          const bf16x8 bv = frag_tr(VS, ldV, 16 * vt, 32 * kb + 8 * g, 32 * kb + 8 * g + 4, tr);
-          op.u[vt] = mfma_bf16(op.th[kb], bv, op.u[vt]);
-          op.u[vt] = mfma_bf16(op.tl[kb], bv, op.u[vt]);
-        }
+          for (int kb = 0; kb < decltype(nkb)::value; ++kb) {
+            const bf16x8 bv = frag_tr(VS, ldV, 16 * vt, 32 * kb + 8 * g, 32 * kb + 8 * g + 4, tr);
+            op.u[vt] = mfma_bf16(op.th[kb], bv, op.u[vt]);
+            op.u[vt] = mfma_bf16(op.tl[kb], bv, op.u[vt]);
+          }
+      };
+      if (w >> 1)
+        u_loop(std::integral_constant<int, 2>{});
+      else
+        u_loop(std::integral_constant<int, 1>{});
     };
     auto fetch_r = [&](int c, Ops& op) {
       const unsigned char* b = item_base(c);
@@ -374,7 +392,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       __asm__ volatile("" : "+v"(lane_x));
       const int tr = lane_x & 15;
       const int g = lane_x >> 4;
-      put_state(g, tr);
+      const int gs = g ^ ((tr >> 2) & 1);  // swizzled chunk of ST / PT rows
       put_v(next_of(c), op.vr);  // read after the barrier below, by the U of the next chunk
       __syncthreads();
       const int ws_next = __builtin_amdgcn_readfirstlane(op.ws_next);
@@ -390,16 +408,25 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
         a0[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
         a1[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
+      // one loop per value of the (wave-uniform) split flag: a branch inside
+      // the loop would cut it into blocks that each wait for their own LDS
+      // reads, with no read issued ahead of the products
+      auto ws_loop = [&](auto split) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int vt = 0; vt < NVT; ++vt) {
-          const bf16x8 bh = frag_ld(ST, ldS, 16 * vt + tr, 32 * kb, g);
-          const bf16x8 bl = frag_ld(ST + loS, ldS, 16 * vt + tr, 32 * kb, g);
-          floatx4& acc = kb < NKH ? a0[vt] : a1[vt];
-          acc = mma_w(ws, op.wh[kb], op.wl[kb], bh, bl, acc);
-        }
-      const int pos = 32 * (w >> 1) + 8 * g + 4 * (w & 1);
+          for (int vt = 0; vt < NVT; ++vt) {
+            const bf16x8 bh = frag_ld(ST, ldS, 16 * vt + tr, 32 * kb, gs);
+            const bf16x8 bl = frag_ld(ST + loS, ldS, 16 * vt + tr, 32 * kb, gs);
+            floatx4& acc = kb < NKH ? a0[vt] : a1[vt];
+            acc = mma_w(decltype(split)::value, op.wh[kb], op.wl[kb], bh, bl, acc);
+          }
+      };
+      if (ws)
+        ws_loop(std::true_type{});
+      else
+        ws_loop(std::false_type{});
+      const int pos = 32 * (w >> 1) + 8 * gs + 4 * (w & 1);
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt) {
         const floatx4 wsv = a0[vt] + a1[vt];
@@ -417,13 +444,16 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
         for (int i = 0; i < 4; ++i) Sacc[j][i] *= op.gc[i];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 bh = frag_ld(PT, ldP, 16 * (sv0 + j) + tr, 32 * kb, g);
-          const bf16x8 bl = frag_ld(PT + loP, ldP, 16 * (sv0 + j) + tr, 32 * kb, g);
+          const bf16x8 bh = frag_ld(PT, ldP, 16 * (sv0 + j) + tr, 32 * kb, gs);
+          const bf16x8 bl = frag_ld(PT + loP, ldP, 16 * (sv0 + j) + tr, 32 * kb, gs);
           Sacc[j] = mma_ab(op.kh[kb], op.kl[kb], bh, bl, Sacc[j]);
         }
       }
-      // ---- U of the next chunk (its v rows were staged before the first
-      // barrier of this chunk), off the state's dependency chain
+      // the updated state as the next chunk's operand (ST is not read after
+      // the second barrier), then U of the next chunk (its v rows were staged
+      // before the first barrier of this chunk), off the state's dependency
+      // chain
+      put_state(gs, tr);
       form_u(next_of(c), nx);
     };
     if (c_lo < c_hi) {
@@ -431,6 +461,10 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       fetch_w(c_lo, __builtin_amdgcn_readfirstlane(flag_of(c_lo)), X);
       load_v(c_lo, X.vr);
       put_v(c_lo, X.vr);
+      {
+        const int tr = lane & 15, g = lane >> 4;
+        put_state(g ^ ((tr >> 2) & 1), tr);  // the entry state as the first chunk's operand
+      }
       __syncthreads();  // (matched by the output waves)
       form_u(c_lo, X);
       fetch_r(c_lo, X);
@@ -476,68 +510,15 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
         op.kl[kb] = *frame_ptr<bf16x8>(b, IM::k_frame(srt, kb, 1), lane);
       }
     };
-    auto chunk = [&](int c, const Ops& op, Ops& nx) {
-      int lane_x = lane;
-      __asm__ volatile("" : "+v"(lane_x));
-      const int tr = lane_x & 15;
-      const int g = lane_x >> 4;
-      const long long tok0 = start + (long long)c * CH;
-      const int nv = (int)(len - (long long)c * CH < CH ? len - (long long)c * CH : CH);
-      put_state(g, tr);
-      __syncthreads();
-      fetch_w(next_of(c), nx);
-      // ---- (Gamma*Q) S over both channel halves (separate chains, low half first)
-      floatx4 ov[NVT];
+    // o of chunk c through this wave's LDS staging area: a quad transpose
+    // gives each lane four consecutive values of row 4g + (tr & 3), stored as
+    // one 16-byte word; read back, each store instruction covers whole rows of
+    // the slice (64 / (BV / 4) of them).  The descriptor spans the chunk's nv
+    // rows.
+    auto store_o = [&](int c, const floatx4 (&ov)[NVT], int tr, int g, int lane_x) {
       if constexpr (!SUMMARY) {
-        floatx4 a0[NVT], a1[NVT];
-#pragma unroll
-        for (int vt = 0; vt < NVT; ++vt) {
-          a0[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
-          a1[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int vt = 0; vt < NVT; ++vt) {
-            const bf16x8 bh = frag_ld(ST, ldS, 16 * vt + tr, 32 * kb, g);
-            const bf16x8 bl = frag_ld(ST + loS, ldS, 16 * vt + tr, 32 * kb, g);
-            floatx4& acc = kb < NKH ? a0[vt] : a1[vt];
-            acc = mfma_bf16(op.qf[kb], bh, acc);
-            acc = mfma_bf16(op.qf[kb], bl, acc);
-          }
-#pragma unroll
-        for (int vt = 0; vt < NVT; ++vt) ov[vt] = a0[vt] + a1[vt];
-      }
-      __syncthreads();
-      fetch_r(next_of(c), nx);
-      // ---- O += Mqk P and the state update of this wave's tiles, from the
-      // same P fragments (the Mqk block after the tile enters as zeros)
-      bf16x8 mh1{}, ml1{};  // (no output in the summary mode: its frames are not fetched)
-      if (!SUMMARY && w >= 2) {
-        mh1 = op.mh[1];
-        ml1 = op.ml[1];
-      }
-#pragma unroll
-      for (int j = 0; j < KVT; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Sacc[j][i] *= op.gc[i];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int vt = 0; vt < NVT; ++vt) {
-          const bf16x8 bh = frag_ld(PT, ldP, 16 * vt + tr, 32 * kb, g);
-          const bf16x8 bl = frag_ld(PT + loP, ldP, 16 * vt + tr, 32 * kb, g);
-          if constexpr (!SUMMARY)
-            ov[vt] = mma_ab(kb ? mh1 : op.mh[0], kb ? ml1 : op.ml[0], bh, bl, ov[vt]);
-          if (vt >= OSV && vt < OSV + KVT)
-            Sacc[vt - OSV] = mma_ab(op.kh[kb], op.kl[kb], bh, bl, Sacc[vt - OSV]);
-        }
-      // o of the tile through this wave's LDS staging area: a quad transpose
-      // gives each lane four consecutive values of row 4g + (tr & 3), stored
-      // as one 16-byte word; read back, each store instruction covers whole
-      // rows of the slice (64 / (BV / 4) of them).  The descriptor spans the
-      // chunk's nv rows.
-      if constexpr (!SUMMARY) {
+        const long long tok0 = start + (long long)c * CH;
+        const int nv = (int)(len - (long long)c * CH < CH ? len - (long long)c * CH : CH);
         float* os = OS + w * 16 * ldO;
         const int b = tr & 3;
 #pragma unroll
@@ -559,16 +540,91 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
         }
       }
     };
+    // One chunk.  The o of the chunk before is stored during this chunk's
+    // (Gamma*Q) S, where the output waves wait for the chain's W S anyway, and
+    // the updated state goes to LDS right after the update: neither holds up
+    // the next chunk's first barrier.
+    floatx4 ovp[NVT];  // o of the chunk before
+    auto chunk = [&](int c, const Ops& op, Ops& nx) {
+      int lane_x = lane;
+      __asm__ volatile("" : "+v"(lane_x));
+      const int tr = lane_x & 15;
+      const int g = lane_x >> 4;
+      const int gs = g ^ ((tr >> 2) & 1);
+      __syncthreads();
+      fetch_w(next_of(c), nx);
+      // ---- (Gamma*Q) S over both channel halves (separate chains, low half first)
+      floatx4 ov[NVT];
+      if constexpr (!SUMMARY) {
+        floatx4 a0[NVT], a1[NVT];
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) {
+          a0[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
+          a1[vt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int vt = 0; vt < NVT; ++vt) {
+            const bf16x8 bh = frag_ld(ST, ldS, 16 * vt + tr, 32 * kb, gs);
+            const bf16x8 bl = frag_ld(ST + loS, ldS, 16 * vt + tr, 32 * kb, gs);
+            floatx4& acc = kb < NKH ? a0[vt] : a1[vt];
+            acc = mfma_bf16(op.qf[kb], bh, acc);
+            acc = mfma_bf16(op.qf[kb], bl, acc);
+          }
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) ov[vt] = a0[vt] + a1[vt];
+        if (c > c_lo) store_o(c - 1, ovp, tr, g, lane_x);
+      }
+      __syncthreads();
+      fetch_r(next_of(c), nx);
+      // ---- O += Mqk P and the state update of this wave's tiles, from the
+      // same P fragments (the Mqk block after the tile enters as zeros)
+      bf16x8 mh1{}, ml1{};  // (no output in the summary mode: its frames are not fetched)
+      if (!SUMMARY && w >= 2) {
+        mh1 = op.mh[1];
+        ml1 = op.ml[1];
+      }
+#pragma unroll
+      for (int j = 0; j < KVT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Sacc[j][i] *= op.gc[i];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) {
+          const bf16x8 bh = frag_ld(PT, ldP, 16 * vt + tr, 32 * kb, gs);
+          const bf16x8 bl = frag_ld(PT + loP, ldP, 16 * vt + tr, 32 * kb, gs);
+          if constexpr (!SUMMARY)
+            ov[vt] = mma_ab(kb ? mh1 : op.mh[0], kb ? ml1 : op.ml[0], bh, bl, ov[vt]);
+          if (vt >= OSV && vt < OSV + KVT)
+            Sacc[vt - OSV] = mma_ab(op.kh[kb], op.kl[kb], bh, bl, Sacc[vt - OSV]);
+        }
+      put_state(gs, tr);  // ST is not read after the second barrier
+      if constexpr (!SUMMARY) {
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) ovp[vt] = ov[vt];
+      }
+    };
     if (c_lo < c_hi) {
       Ops X, Y;
       fetch_w(c_lo, X);
       fetch_r(c_lo, X);
+      {
+        const int tr = lane & 15, g = lane >> 4;
+        put_state(g ^ ((tr >> 2) & 1), tr);
+      }
       __syncthreads();  // the chain waves' staging of the first chunk's v rows
       wait_vm0();
       for (int c = c_lo; c < c_hi; c += 2) {
         chunk(c, X, Y);
         if (c + 1 >= c_hi) break;
         chunk(c + 1, Y, X);
+      }
+      {
+        int lane_x = lane;
+        __asm__ volatile("" : "+v"(lane_x));
+        store_o(c_hi - 1, ovp, lane_x & 15, lane_x >> 4, lane_x);
       }
     }
   }
