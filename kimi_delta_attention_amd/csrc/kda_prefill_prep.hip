@@ -184,40 +184,78 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     d.nv = (int)(ln - cc < CH ? ln - cc : CH);
     return d;
   };
-  // k, q, alpha of this lane's token and channels, and beta; token tile
-  // (w4 + item) & 3
-  uint2v kin[NKB][2], qin[NKB][2];
-  float Pv[NKB][8];
+  // k, q, gate values (as stored) of this lane's token and channels, and beta;
+  // token tile (w4 + item) & 3.  Loads only, straight into the registers that
+  // hold them until the item starts (order_in and finish_in use them there),
+  // so that a prefetch waits for nothing: buffer loads through descriptors
+  // that span the chunk's nv tokens read zero past them, with no select.
+  uint4v kr[NKB], qr[NKB];  // raw 16-byte pieces (order_in)
+  floatx4 ain[NKB][2];      // gate values as stored (finish_in)
   float bt = 0.f;
+  auto rsrc = [](const void* base, long long bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+  };
   auto load_in = [&](int item, const Item& d, int ln) {
     const int gl = ln >> 4;
     const int r = 16 * ((w4 + item) & 3) + (ln & 15);
-    const bool okc = r < d.nv;
-    const size_t thc = (size_t)(d.tok0 + r) * H + d.hd;
-    floatx4 a4[NKB][2];
+    const size_t row0 = (size_t)d.tok0 * H + d.hd;  // (first token, head)
+    const long long rows = (long long)d.nv * H;    // rows the chunk's tokens span
+    const int ro = r * H;                           // this lane's row after row0
+    const auto rk = rsrc(k + row0 * DK, rows * DK * 2);
+    const auto rq = rsrc(q + row0 * DK, rows * DK * 2);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       // k and q in 16 bytes per lane: row gl of the wave reads channels
       // 8 (gl >> 1) + 16 (gl & 1) .. + 8 of the block, so a token's 32
       // channels come in one 64-byte piece (order_in puts them in place)
       const int c8 = 32 * kb + 8 * (gl >> 1) + 16 * (gl & 1);
-      const uint4v z4{0u, 0u, 0u, 0u};
-      const uint4v k8 = okc ? *reinterpret_cast<const uint4v*>(k + thc * DK + c8) : z4;
-      const uint4v q8 = okc ? *reinterpret_cast<const uint4v*>(q + thc * DK + c8) : z4;
-      kin[kb][0] = uint2v{k8[0], k8[1]};
-      kin[kb][1] = uint2v{k8[2], k8[3]};
-      qin[kb][0] = uint2v{q8[0], q8[1]};
-      qin[kb][1] = uint2v{q8[2], q8[3]};
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) a4[kb][hf] = gate_load4<KIND>(gate, okc, thc, DK, 32 * kb + 16 * hf + 4 * gl);
+      kr[kb] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(rk, (ro * DK + c8) * 2, 0, 0));
+      qr[kb] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(rq, (ro * DK + c8) * 2, 0, 0));
     }
-    gate_finish_blocks<KIND, NKB>(gate, KIND == GATE_BOUNDED ? expf(gate.a_log[d.hd]) : 1.f, a4);
+    if constexpr (KIND == GATE_SCALAR) {
+      const auto rg = rsrc(gate.g + row0, rows * 4);
+      ain[0][0][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, ro * 4, 0, 0));
+    } else if constexpr (KIND != GATE_NONE) {
+      const auto rg = rsrc(gate.g + row0 * DK, rows * DK * 4);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          ain[kb][hf] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        rg, (ro * DK + 32 * kb + 16 * hf + 4 * gl) * 4, 0, 0));
+    }
+    bt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(beta + row0, rows * 4), ro * 4, 0, 0));
+  };
+  // alpha of this lane's token and channels (rows past the chunk's end: the
+  // gate value whose alpha is 1)
+  float Pv[NKB][8];
+  auto finish_in = [&](int hd, bool okc) {
+    if constexpr (KIND == GATE_SCALAR) {
+      const float x = okc ? ain[0][0][0] : 1.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) ain[kb][hf] = floatx4{x, x, x, x};
+    } else if constexpr (KIND == GATE_NONE) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) ain[kb][hf] = floatx4{1.f, 1.f, 1.f, 1.f};
+    } else {
+      constexpr float f = KIND == GATE_LOG ? 0.f : KIND == GATE_BOUNDED ? -INFINITY : 1.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          if (!okc) ain[kb][hf] = floatx4{f, f, f, f};
+    }
+    gate_finish_blocks<KIND, NKB>(gate, KIND == GATE_BOUNDED ? expf(gate.a_log[hd]) : 1.f, ain);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) Pv[kb][i] = a4[kb][i >> 2][i & 3];
-    bt = okc ? beta[thc] : 0.f;
+      for (int i = 0; i < 8; ++i) Pv[kb][i] = ain[kb][i >> 2][i & 3];
   };
+  uint2v kin[NKB][2], qin[NKB][2];  // k, q of the operand layout (order_in)
   // A permlane16 swap of the middle halves of the loaded pieces between rows
   // 0 / 1 and 2 / 3 leaves each lane its 4-channel groups 4 gl and 16 + 4 gl.
   // Done after every load of the item has been issued: its wait for the k and
@@ -227,14 +265,25 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
-        const auto sk = __builtin_amdgcn_permlane16_swap(kin[kb][0][a], kin[kb][1][a], false, false);
-        const auto sq = __builtin_amdgcn_permlane16_swap(qin[kb][0][a], qin[kb][1][a], false, false);
+        const auto sk = __builtin_amdgcn_permlane16_swap(kr[kb][a], kr[kb][2 + a], false, false);
+        const auto sq = __builtin_amdgcn_permlane16_swap(qr[kb][a], qr[kb][2 + a], false, false);
         kin[kb][0][a] = sk[0];
         kin[kb][1][a] = sk[1];
         qin[kb][0][a] = sq[0];
         qin[kb][1][a] = sq[1];
       }
   };
+  // The inputs of an item are loaded while the item before runs its phases
+  // 4 to 6 (they are dead after its phase 3): otherwise every item waits for
+  // its own loads, and all workgroups read at the same time.  (With the layer
+  // prologue the registers do not allow it: its items load at their start.)
+  Item pre{};
+  if constexpr (!PRO) {
+    if ((int)blockIdx.x < n_items) {
+      pre = locate(blockIdx.x);
+      load_in(blockIdx.x, pre, threadIdx.x & 63);
+    }
+  }
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     // Lane index behind an empty asm, so that the per-lane addresses are
     // recomputed per item rather than held (or spilled) across the loop.
@@ -242,8 +291,8 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     __asm__ volatile("" : "+v"(lane_x));
     int tid_x = threadIdx.x;  // the same for the workgroup-wide prologue staging
     __asm__ volatile("" : "+v"(tid_x));
-    const Item cur = locate(item);
-    load_in(item, cur, lane_x);
+    const Item cur = PRO ? locate(item) : pre;
+    if constexpr (PRO) load_in(item, cur, lane_x);
     const long long tok0 = cur.tok0;
     const int nv = cur.nv, hd = cur.hd;
     unsigned char* im = img + (size_t)item * IM::bytes;
@@ -304,6 +353,7 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     }
 
     if constexpr (!PRO) order_in();  // the prologue reads the rows back in place
+    finish_in(hd, okc);
 
     // ---- prologue (layer prefill): ShortConv over the three previous
     // inputs, Swish, and the L2Norm of q and k.  The raw rows go to LDS; then
@@ -321,10 +371,8 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {  // the pieces as loaded (8 channels from c8)
         const int c8 = 32 * kb + 8 * (g >> 1) + 16 * (g & 1);
-        *reinterpret_cast<uint4v*>(XR + r * ldX + c8) =
-            uint4v{qin[kb][0][0], qin[kb][0][1], qin[kb][1][0], qin[kb][1][1]};
-        *reinterpret_cast<uint4v*>(XR + r * ldX + DK + c8) =
-            uint4v{kin[kb][0][0], kin[kb][0][1], kin[kb][1][0], kin[kb][1][1]};
+        *reinterpret_cast<uint4v*>(XR + r * ldX + c8) = qr[kb];
+        *reinterpret_cast<uint4v*>(XR + r * ldX + DK + c8) = kr[kb];
       }
 #pragma unroll
       for (int j = 0; j < NVL; ++j)
@@ -639,6 +687,13 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
       }
     }
     __syncthreads();
+    if constexpr (!PRO) {  // the next item's inputs (see above)
+      const int nxt = item + (int)gridDim.x;
+      if (nxt < n_items) {
+        pre = locate(nxt);
+        load_in(nxt, pre, lane_x);
+      }
+    }
 
     // ---- 4. Mqk image of this tile's queries (token k-slots in the swizzled
     // order), then T = (I + A)^{-1}, blockwise over 16x16 tiles on fp32 MFMA
