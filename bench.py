@@ -73,6 +73,28 @@ def measured_traffic(summary: str, sources: list[str]):
     return float(kv["traffic_bytes_per_launch"].split()[0])
 
 
+def measured_mfma(summary: str, sources: list[str]):
+    """Matrix-core counters of a committed rocprofv3 summary: busy fraction per
+    kernel and hardware FLOPs per call, or None when the sources changed."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    kv, busy = {}, {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+            if key.strip().endswith("] busy_frac"):
+                busy[key.strip()[1:key.index("]")]] = float(val.split()[0])
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if kv.get("source_sha256") != h.hexdigest():
+        return None
+    return {"busy_frac": busy, "hw_flops_per_call": float(kv["hw_flops_per_call"].split()[0])}
+
+
 PREFILL_SOURCES = ["kimi_delta_attention_amd/csrc/kda_prefill.hip",
                    "kimi_delta_attention_amd/csrc/kda_prefill_prep.hip",
                    "kimi_delta_attention_amd/csrc/kda_prefill_state.hip",
@@ -389,6 +411,8 @@ def main():
         else:
             long1m = {"skipped": f"needs ~200 GB of device memory, {free / 1e9:.0f} GB free"}
 
+    traffic = measured_traffic(f"prefill_{schedule}__k3_prefill_8k__hbm_counters.txt", PREFILL_SOURCES)
+    mf = measured_mfma(f"prefill_{schedule}__k3_prefill_8k__mfma_counters.txt", PREFILL_SOURCES)
     line = {
         "metric": "KDA prefill tokens/s (H=96,d=128) + decode-step state GB/s vs HBM peak",
         "value": tokens_s,
@@ -407,8 +431,7 @@ def main():
                    "schedule": schedule},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(f"prefill_{schedule}__k3_prefill_8k__hbm_counters.txt",
-                                                 PREFILL_SOURCES),
+                     "traffic": traffic,
                      "traffic_unit": "HBM bytes per kda_prefill_chunked call (rocprofv3 "
                                      "FETCH_SIZE + WRITE_SIZE of its kernels, copy-calibrated)",
                      "kernel": ("kda_prefill_chunked, two-pass: prefill_prep_kernel<128, 128, alpha gate> "
@@ -416,7 +439,13 @@ def main():
                                 "kda_prefill_chunked, fused: prefill_bf16_kernel<128, fp32 out, alpha gate>"),
                      "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_ms": avg_launch_ms,
-                     "mfma_frac_pages_flops": tflops / BF16_PEAK_TFLOPS},
+                     "traffic_gbps": (traffic / (avg_launch_ms / 1e3) / 1e9) if traffic else None,
+                     "mfma_frac_pages_flops": tflops / BF16_PEAK_TFLOPS,
+                     "mfma_counters": ({"busy_frac": mf["busy_frac"],
+                                        "hw_tflops": mf["hw_flops_per_call"] / (avg_launch_ms / 1e3) / 1e12,
+                                        "hw_frac_bf16_peak": mf["hw_flops_per_call"] / (avg_launch_ms / 1e3)
+                                                             / 1e12 / BF16_PEAK_TFLOPS}
+                                       if mf else None)},
         "prefill_other_schedule": ({"schedule": other, "ms_per_step": other_ms,
                                     "tokens_per_s": B * T / (other_ms / 1e3)} if other else None),
         "decode": {"workload": "decode_b64", "B": wd["B"], "H": wd["H"], "d": wd["D"],
