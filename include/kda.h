@@ -408,7 +408,11 @@ kda_status kda_decode_layer(kda_decode_mode mode, const void* xq, const void* xk
  *                      schedule)
  * Equal to kda_prologue, the recurrence and kda_epilogue up to rounding (the
  * L2Norm's sum of squares is associated differently; q, k, v are rounded to
- * bf16 as the standalone prologue stores them).
+ * bf16 as the standalone prologue stores them).  The one call trades time for
+ * memory: it needs no q, k, v buffers (3 x tokens x H x Dk bf16 values), but
+ * where they fit, kda_prologue + kda_prefill_chunked (two-pass) + kda_epilogue
+ * run faster (on MI355X, for 8192 tokens and 96 heads of 128 channels, about
+ * 1.27 ms against 1.42 ms).
  */
 kda_status kda_prefill_layer(const void* xq, const void* xk, const void* xv, kda_dtype x_dtype,
                              const kda_conv* conv, const float* conv_state_in,
