@@ -31,13 +31,12 @@
  *    launch returns KDA_ERR_HIP.  No exception or abort crosses the ABI.
  *  - Supported shapes: Dk, Dv in {64, 128}; chunk == 64.  q/k/v dtype KDA_BF16
  *    or KDA_F32 (all three the same); alpha, beta and the state are fp32; the
- *    output o is KDA_F32 or KDA_BF16.  One exception: the chunked prefill
- *    entry points (kda_prefill_chunked, _varlen, their _gated forms and
- *    kda_prefill_chunked_noalloc) take KDA_F32 q/k/v only with Dk == 64 (Dv 64
- *    or 128); KDA_F32 with Dk == 128 returns KDA_ERR_UNSUPPORTED there.  The
- *    decode and speculative entry points take every listed shape in either
- *    dtype; the layer prefill and the segmented schedule take bf16 only (as
- *    stated with them).
+ *    output o is KDA_F32 or KDA_BF16.  The prefill entry points compute fp32
+ *    q/k/v in fp32 arithmetic: with Dk == 64 in the chunk form, with Dk == 128
+ *    as the token recurrence (one workgroup per sequence and head stepping
+ *    its tokens; the same function, slower); fp32 q, k, v and a per-channel
+ *    gate 16-byte aligned at Dk == 128.  The layer prefill and the segmented
+ *    schedule take bf16 only (as stated with them).
  *  - Documented, not checked: alpha in (0, 1] (any value in it, however fast
  *    the decay: a 16-token tile whose decay product leaves the range of the
  *    chunked kernels' factored form is computed by exact running products

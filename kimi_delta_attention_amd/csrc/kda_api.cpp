@@ -170,28 +170,26 @@ static kda_status prefill_common(const void* q, const void* k, const void* v, kd
   if (n_seq < 0 || T < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "negative batch or length");
   if (n_seq == 0) return ok();
   kda::Gate g = {KDA_GATE_NONE, nullptr, nullptr, 0.f};
+  const bool vec16 = qkv_dtype == KDA_BF16 || Dk == 128;  // 16-byte input loads
   if (T > 0 || cu_seqlens) {
     kda_status s = check_common(q, k, v, qkv_dtype, beta, o, o_dtype, H, Dk, Dv);
     if (s != KDA_OK) return s;
-    s = check_gate(gate, qkv_dtype == KDA_BF16, &g);
+    s = check_gate(gate, vec16, &g);
     if (s != KDA_OK) return s;
   } else if (H <= 0 || Dk <= 0 || Dv <= 0) {
     // T == 0: no token tensor is read; the kernel only hands the state through
     return fail(KDA_ERR_INVALID_ARGUMENT, "H, Dk and Dv must be positive");
   }
   if (chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk must be 64 (got %d)", chunk);
-  // the bf16 kernels read q, k, v (and a per-channel gate, checked above) with
-  // 8- and 16-byte vector loads
-  if (qkv_dtype == KDA_BF16 && (T > 0 || cu_seqlens) &&
-      (!aligned16(q) || !aligned16(k) || !aligned16(v)))
-    return fail(KDA_ERR_INVALID_ARGUMENT, "bf16 prefill needs 16-byte aligned q, k, v and alpha");
+  // the bf16 kernels and the fp32 token recurrence (Dk = 128) read q, k, v
+  // (and a per-channel gate, checked above) with 8- and 16-byte vector loads
+  if (vec16 && (T > 0 || cu_seqlens) && (!aligned16(q) || !aligned16(k) || !aligned16(v)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "this prefill needs 16-byte aligned q, k, v and alpha");
   if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
     return fail(KDA_ERR_INVALID_ARGUMENT, "state pointers must be 16-byte aligned");
   if (!kda::prefill_supported(qkv_dtype == KDA_BF16, Dk, Dv))
     return fail(KDA_ERR_UNSUPPORTED,
-                "unsupported head dims Dk=%d Dv=%d for %s inputs (bf16: Dk,Dv in {64,128}; "
-                "fp32: Dk=64, Dv in {64,128})",
-                Dk, Dv, qkv_dtype == KDA_BF16 ? "bf16" : "fp32");
+                "unsupported head dims Dk=%d Dv=%d (Dk, Dv in {64, 128})", Dk, Dv);
   // token offsets are 64-bit in the kernels; the head / row counts must fit int32
   if ((long long)n_seq * H * (Dv / 64) > 0x7fffffffLL)
     return fail(KDA_ERR_INVALID_ARGUMENT, "too many (sequence, head) work items");

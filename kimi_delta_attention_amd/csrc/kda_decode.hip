@@ -453,6 +453,104 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
   }
 }
 
+// The prefill as the token recurrence, for fp32 q, k, v where the chunked
+// fp32 kernel's LDS plan does not fit (Dk = 128): one workgroup per
+// (sequence, head) holds the state tile in registers, as the decode kernel
+// does, and steps the sequence's tokens in blocks of NBLK staged in LDS
+// (records as for verify), writing o per token and the state once at the end
+// ("Kimi Delta Attention 完全拆解", section "一次 KDA 前向究竟发生了什么": the
+// recurrent form, which the chunk form equals up to rounding).  Empty
+// sequences hand their state through.
+constexpr int NBLK = 16;
+template <int DK, int DV, typename TIn, typename TOut, int KIND>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void recurrent_prefill_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v, Gate gate,
+    const float* __restrict__ beta, const float* s_init, float* s_final, TOut* __restrict__ o,
+    const int32_t* __restrict__ cu_seqlens, int n_seq, int T, int H) {
+  using G = Geo<DK, DV>;
+  using R = Rec<DK, DV, true>;
+  constexpr int NP = G::NP, LPR = G::LPR, RPP = G::RPP;
+  extern __shared__ __align__(16) float rec[];
+  const int tile = blockIdx.x;  // (sequence, head)
+  const int seq = tile / H, h = tile - seq * H;
+  long long start, len;
+  if (cu_seqlens) {
+    start = cu_seqlens[seq];
+    len = (long long)cu_seqlens[seq + 1] - start;
+  } else {
+    start = (long long)seq * T;
+    len = T;
+  }
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int cg = lane % LPR, ro = lane / LPR, col = w * G::CW + 4 * cg;
+  floatx4 s[NP];
+  {
+    const float* S = s_init ? s_init + (size_t)tile * DK * DV : nullptr;
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      s[i] = S ? *reinterpret_cast<const floatx4*>(S + (size_t)(ro + RPP * i) * DV + col)
+               : floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sc = KIND == GATE_BOUNDED ? expf(gate.a_log[h]) : 1.f;
+  for (long long t0 = 0; t0 < len; t0 += NBLK) {
+    const int n = (int)(len - t0 < NBLK ? len - t0 : NBLK);
+    __syncthreads();  // the block before is done with the records
+    for (int idx = tid; idx < n * (DK / 4); idx += 256) {
+      const int t = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+      const size_t row = (size_t)(start + t0 + t) * H + h;
+      const floatx4 a4 = alpha4_exact<KIND>(gate, row, DK, c, sc);
+      const floatx4 k4 = ld4<TIn>(k + row * DK + c);
+      const floatx4 q4 = ld4<TIn>(q + row * DK + c);
+      float* rt = rec + t * R::stride;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pos = ((c + e) % RPP) * NP + (c + e) / RPP;
+        rt[R::K + pos] = k4[e];
+        rt[R::AK + pos] = a4[e] * k4[e];
+        rt[R::AL + pos] = a4[e];
+        rt[R::Q + pos] = q4[e];
+        rt[R::AQ + pos] = a4[e] * q4[e];
+      }
+    }
+    for (int idx = tid; idx < n * (DV / 4); idx += 256) {
+      const int t = idx / (DV / 4), c = 4 * (idx % (DV / 4));
+      const size_t row = (size_t)(start + t0 + t) * H + h;
+      *reinterpret_cast<floatx4*>(rec + t * R::stride + R::V + c) = ld4<TIn>(v + row * DV + c);
+    }
+    if (tid < n) rec[tid * R::stride + R::Bt] = beta[(size_t)(start + t0 + tid) * H + h];
+    __syncthreads();
+    for (int t = w; t < n; t += 4) {  // q.k of each token
+      float kr[NP], qr[NP];
+      ld_rows<NP>(rec + t * R::stride + R::K + ro * NP, kr);
+      ld_rows<NP>(rec + t * R::stride + R::Q + ro * NP, qr);
+      const float qk = dot_rows<NP, LPR>(kr, qr);
+      if (lane == 0) rec[t * R::stride + R::QK] = qk;
+    }
+    __syncthreads();
+    for (int t = 0; t < n; ++t) {
+      const float* rt = rec + t * R::stride;
+      float kr[NP], ak[NP], aq[NP], al[NP];
+      ld_rows<NP>(rt + R::K + ro * NP, kr);
+      ld_rows<NP>(rt + R::AK + ro * NP, ak);
+      ld_rows<NP>(rt + R::AL + ro * NP, al);
+      ld_rows<NP>(rt + R::AQ + ro * NP, aq);
+      const floatx4 vv = *reinterpret_cast<const floatx4*>(rt + R::V + col);
+      const floatx4 ov = token_step<NP, LPR>(s, kr, ak, aq, al, rt[R::QK], rt[R::Bt], vv);
+      if (ro == 0) {
+        TOut* ot = o + ((size_t)(start + t0 + t) * H + h) * DV + col;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ot[j] = (TOut)ov[j];
+      }
+    }
+  }
+  if (s_final) {
+    float* S = s_final + (size_t)tile * DK * DV;
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4*>(S + (size_t)(ro + RPP * i) * DV + col));
+  }
+}
+
 // LDS of one workgroup: N token records; with the layer, the raw rows
 // [3 + N][2 Dk + Dv], the gate logits [N][Dv] and the conv taps [2 Dk + Dv][4]
 template <int DK, int DV, bool VERIFY>
@@ -539,6 +637,33 @@ hipError_t launch_decode(const DecodeArgs& a) {
   if (a.Dk == 128 && a.Dv == 64) return launch_decode_d<128, 64>(a);
   if (a.Dk == 64 && a.Dv == 128) return launch_decode_d<64, 128>(a);
   return launch_decode_d<64, 64>(a);
+}
+
+template <int DK, int DV, typename TOut, int KIND>
+static hipError_t launch_rec_k(const PrefillArgs& a) {
+  const int grid = a.n_seq * a.H;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((recurrent_prefill_kernel<DK, DV, float, TOut, KIND>), dim3(grid), dim3(256),
+                     ((int)sizeof(float) * Rec<DK, DV, true>::stride * NBLK), (hipStream_t)a.stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, a.gate, a.beta,
+                     a.initial_state, a.final_state, (TOut*)a.o, a.cu_seqlens, a.n_seq, a.T, a.H);
+  return hipGetLastError();
+}
+template <int DK, int DV, typename TOut>
+static hipError_t launch_rec_t(const PrefillArgs& a) {
+  switch (a.gate.kind) {
+    case GATE_LOG: return launch_rec_k<DK, DV, TOut, GATE_LOG>(a);
+    case GATE_BOUNDED: return launch_rec_k<DK, DV, TOut, GATE_BOUNDED>(a);
+    case GATE_SCALAR: return launch_rec_k<DK, DV, TOut, GATE_SCALAR>(a);
+    case GATE_NONE: return launch_rec_k<DK, DV, TOut, GATE_NONE>(a);
+    default: return launch_rec_k<DK, DV, TOut, GATE_ALPHA>(a);
+  }
+}
+
+// fp32 q, k, v with Dk = 128 (the fp32 chunked kernel serves Dk = 64)
+hipError_t launch_prefill_recurrent(const PrefillArgs& a) {
+  if (a.Dv == 128) return a.o_bf16 ? launch_rec_t<128, 128, bf16>(a) : launch_rec_t<128, 128, float>(a);
+  return a.o_bf16 ? launch_rec_t<128, 64, bf16>(a) : launch_rec_t<128, 64, float>(a);
 }
 
 }  // namespace kda

@@ -104,7 +104,8 @@ hipError_t launch_prefill(const PrefillArgs& a);      // dispatch (kda_prefill.h
 // nothing: 128 MiB per device, its address on the current device
 constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
 hipError_t noalloc_scratch(void** ptr);
-hipError_t launch_prefill_f32(const PrefillArgs& a);  // fp32 inputs (kda_prefill_f32.hip)
+hipError_t launch_prefill_f32(const PrefillArgs& a);  // fp32 inputs, Dk = 64 (kda_prefill_f32.hip)
+hipError_t launch_prefill_recurrent(const PrefillArgs& a);  // fp32 inputs, Dk = 128 (kda_decode.hip)
 bool prefill_supported(bool qkv_bf16, int Dk, int Dv);
 
 // Two-pass bf16 prefill.  Workspace bytes it needs (0 if unavailable for the

@@ -789,7 +789,8 @@ size_t carry_bytes(int n_seq, int H, int Dk, int Dv) {
 bool prefill_supported(bool qkv_bf16, int Dk, int Dv) {
   if (!(Dv == 64 || Dv == 128)) return false;
   if (qkv_bf16) return Dk == 64 || Dk == 128;
-  return Dk == 64;  // fp32 inputs: the fp32-MFMA kernel, Dk = 64
+  return Dk == 64 || Dk == 128;  // fp32 inputs: the fp32-MFMA chunk kernel (Dk = 64) or the
+                                // token recurrence (Dk = 128)
 }
 
 // Workspace of the two-pass schedule: the chunk table (packed calls), a state
@@ -883,7 +884,7 @@ hipError_t layer_tail(const PrefillArgs& a, long long total) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {
-  if (!a.qkv_bf16) return launch_prefill_f32(a);
+  if (!a.qkv_bf16) return a.Dk == 64 ? launch_prefill_f32(a) : launch_prefill_recurrent(a);
   const bool varlen = a.cu_seqlens != nullptr;
   // packed tokens in all (dense: n_seq sequences of T tokens back to back)
   const long long total = varlen ? (long long)a.T : (long long)a.n_seq * a.T;

@@ -216,7 +216,7 @@ def _prefill(**over):
     (dict(chunk=32), UNSUPPORTED),
     (dict(Dk=96), UNSUPPORTED),
     (dict(Dv=256), UNSUPPORTED),
-    (dict(qd=F32, Dk=128), UNSUPPORTED),
+    (dict(qd=F32, Dk=128, q=AT[0] + 4), INVALID),  # fp32 at Dk 128: 16-byte loads
     (dict(B=0), OK),
     (dict(ws=AT[7] + 64, wsb=1 << 30), INVALID),
     (dict(ws=AT[5] - 4096, wsb=1 << 20), INVALID),  # workspace overlaps o

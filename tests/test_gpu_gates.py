@@ -62,10 +62,12 @@ def test_prefill_gates_bf16(kind, B, T, H, Dk, Dv):
 
 
 @pytest.mark.parametrize("kind", KINDS)
-def test_prefill_gates_fp32(kind):
-    """fp32 inputs (the fp32 prefill kernel): tolerance 1e-5."""
+@pytest.mark.parametrize("Dk", [64, 128])
+def test_prefill_gates_fp32(kind, Dk):
+    """fp32 inputs (the fp32 chunk kernel at Dk 64, the token recurrence at
+    Dk 128): tolerance 1e-5."""
     d = dev()
-    inp, gate, a_log, alpha = _case(1, 150, 2, 64, 128, kind, seed=610,
+    inp, gate, a_log, alpha = _case(1, 150, 2, Dk, 128, kind, seed=610 + Dk,
                                     qkv_dtype=torch.float32)
     o_ref, s_ref = oracle.recurrent(inp.q, inp.k, inp.v, alpha, inp.beta,
                                     initial_state=inp.state)

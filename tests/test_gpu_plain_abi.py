@@ -39,6 +39,7 @@ def _ok(status):
     (2, 64 * 3 + 17, 2, 128, 128, torch.bfloat16),
     (1, 150, 3, 64, 128, torch.bfloat16),
     (2, 64 * 2 + 5, 2, 64, 64, torch.float32),
+    (2, 64 * 2 + 5, 2, 128, 128, torch.float32),
 ])
 @pytest.mark.parametrize("two_pass", [False, True])
 def test_prefill_chunked(B, T, H, Dk, Dv, qkv, two_pass):

@@ -77,6 +77,40 @@ def test_fp32_inputs_dv128_and_bf16_output():
     close(o.float(), o_ref, TOL_BF16_OUT, "tokens")
 
 
+@pytest.mark.parametrize("Dv", [128, 64])
+def test_fp32_inputs_dk128_token_recurrence(Dv):
+    """fp32 q, k, v at Dk = 128 (the token recurrence): dense with a ragged
+    tail, in-place state, bf16 output, and packed with empty and one-token
+    sequences; fp32 tolerance."""
+    d = dev()
+    inp = synth.make_dense(2, 64 * 3 + 9, 3, 128, Dv, seed=35 + Dv, qkv_dtype=torch.float32,
+                           state_std=0.02)
+    o_ref, s_ref = oracle.recurrent(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
+                                    initial_state=inp.state)
+    o, s = _run(inp, d)
+    torch.cuda.synchronize()
+    close(o, o_ref, TOL_F32, "tokens")
+    close(s, s_ref, TOL_F32, "state")
+    st = inp.state.to(d)  # in place
+    kda.prefill_chunked(to(inp.q, d), to(inp.k, d), to(inp.v, d), to(inp.alpha, d),
+                        to(inp.beta, d), initial_state=st, final_state=st)
+    o16, _ = _run(inp, d, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    close(st, s_ref, TOL_F32, "state")
+    close(o16.float(), o_ref, TOL_BF16_OUT, "tokens")
+    lengths = [40, 0, 1, 129]
+    pk = synth.make_varlen(lengths, 2, 128, Dv, seed=36, qkv_dtype=torch.float32, device=d)
+    o, s = kda.prefill_varlen(pk.q, pk.k, pk.v, pk.alpha, pk.beta, pk.cu_seqlens,
+                              initial_state=pk.state)
+    torch.cuda.synchronize()
+    cu = pk.cu_seqlens.cpu().numpy()
+    o_ref, s_ref = oracle.recurrent(pk.q.cpu(), pk.k.cpu(), pk.v.cpu(), pk.alpha.cpu(),
+                                    pk.beta.cpu(), cu_seqlens=cu, initial_state=pk.state.cpu())
+    close(o, o_ref, TOL_F32, "tokens", cu=cu)
+    close(s, s_ref, TOL_F32, "state")
+    assert torch.equal(s[1], pk.state[1])
+
+
 @pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("kind", ["slow_decay", "alpha_one", "bounded_gate"])
 def test_decay_regimes(kind, schedule):
