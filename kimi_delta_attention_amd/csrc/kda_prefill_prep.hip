@@ -274,8 +274,9 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
       }
   };
   // The inputs of an item are loaded while the item before runs its phases
-  // 4 to 6 (they are dead after its phase 3): otherwise every item waits for
-  // its own loads, and all workgroups read at the same time.  (With the layer
+  // 4 to 6 (they are dead after its phase 3; issued after phase 4's Mqk
+  // stores, which would otherwise queue behind them): otherwise every item
+  // waits for its own loads, and all workgroups read at the same time.  (With the layer
   // prologue the registers do not allow it: its items load at their start.)
   Item pre{};
   if constexpr (!PRO) {
@@ -687,13 +688,6 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
       }
     }
     __syncthreads();
-    if constexpr (!PRO) {  // the next item's inputs (see above)
-      const int nxt = item + (int)gridDim.x;
-      if (nxt < n_items) {
-        pre = locate(nxt);
-        load_in(nxt, pre, lane_x);
-      }
-    }
 
     // ---- 4. Mqk image of this tile's queries (token k-slots in the swizzled
     // order), then T = (I + A)^{-1}, blockwise over 16x16 tiles on fp32 MFMA
@@ -719,6 +713,13 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
         if (kb > (w >> 1)) continue;
         put_frame(im, IM::m_frame(w, kb, 0), lane_x, mqh[kb]);
         put_frame(im, IM::m_frame(w, kb, 1), lane_x, mql[kb]);
+      }
+    }
+    if constexpr (!PRO) {  // the next item's inputs (see above)
+      const int nxt = item + (int)gridDim.x;
+      if (nxt < n_items) {
+        pre = locate(nxt);
+        load_in(nxt, pre, lane_x);
       }
     }
     {
