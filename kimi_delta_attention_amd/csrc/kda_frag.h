@@ -263,6 +263,9 @@ __device__ __forceinline__ bool w_split_chunk(const float* GC, int lane) {
 //                                only for a chunk that keeps W split
 //                                (w_split_chunk)
 //   Q  [w][kb < DK/32]           A operand of (Gamma*Q) S, same positions
+//   QL [kb < DK/32]              low halves of tile 0's Gamma*Q (the tile whose
+//                                read-out of the entry state is the least
+//                                decayed keeps Gamma*Q split)
 //   M  [w][kb < 2][hi, lo]       A operand of Mqk P (k = token position)
 //   K  [rt < DK/16][kb < 2][hi, lo]  A operand of Ktil^T P for state rows
 //                                16rt..16rt+15 (k = token position)
@@ -280,7 +283,10 @@ struct Images {
   static constexpr int NKB = DK / 32, NCHT = DK / 16, NVT = DV / 16;
   static constexpr int W = 0;
   static constexpr int Q = W + 4 * NKB * 2;
-  static constexpr int M = Q + 4 * NKB;
+  // Gamma*Q: the high halves of every tile, then the low halves of tile 0
+  // (the tile whose read-out of the entry state is the least decayed)
+  static constexpr int QL = Q + 4 * NKB;
+  static constexpr int M = QL + NKB;
   static constexpr int K = M + 4 * 2 * 2;
   static constexpr int TB = K + NCHT * 2 * 2;
   static constexpr int V = TB + 4 * 2 * 2;
@@ -291,6 +297,7 @@ struct Images {
   static constexpr size_t bytes = (f_off + 4 + 255) / 256 * 256;
   static __device__ __forceinline__ int w_frame(int w, int kb, int part) { return W + (w * NKB + kb) * 2 + part; }
   static __device__ __forceinline__ int q_frame(int w, int kb) { return Q + w * NKB + kb; }
+  static __device__ __forceinline__ int ql_frame(int kb) { return QL + kb; }
   static __device__ __forceinline__ int m_frame(int w, int kb, int part) { return M + (w * 2 + kb) * 2 + part; }
   static __device__ __forceinline__ int k_frame(int rt, int kb, int part) { return K + (rt * 2 + kb) * 2 + part; }
   static __device__ __forceinline__ int tb_frame(int w, int kb, int part) { return TB + (w * 2 + kb) * 2 + part; }

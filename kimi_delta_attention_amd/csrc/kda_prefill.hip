@@ -91,13 +91,14 @@ struct Plan {
   static constexpr int m1 = RT > 5 * AF ? RT : 5 * AF;
   static constexpr int m2 = endB > endC ? endB : endC;
   static constexpr int R0 = m1 > m2 ? m1 : m2;
-  static constexpr int GK = CH * ldG * 2, QT = CH * ldQ * 2;
-  static constexpr int oGK = R0, oQT = oGK + GK, oES = oQT + QT, oGC = oES + 4 * DK * 4,
+  static constexpr int GK = CH * ldG * 2, QT = CH * ldQ * 2, QTL = 16 * ldQ * 2;
+  static constexpr int oGK = R0, oQT = oGK + GK, oQTL = oQT + QT, oES = oQTL + QTL,
+                       oGC = oES + 4 * DK * 4,
                        oBS = oGC + DK * 4, total = oBS + CH * 4;
   static_assert(total <= 163840, "LDS budget (160 KiB)");
   static_assert(4 * 2048 <= AF, "T-solve scratch fits in the MQ0 region");
   static_assert(oTB >= oTF + AF, "TB is built from TF and must not overlap it");
-  static_assert((oGK | oQT | oES | oGC | oBS | oTF | oTB | oVS | oPT | oKT | oAF2 | oMQ1) % 16 == 0,
+  static_assert((oGK | oQT | oQTL | oES | oGC | oBS | oTF | oTB | oVS | oPT | oKT | oAF2 | oMQ1) % 16 == 0,
                 "alignment");
 };
 
@@ -135,6 +136,7 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
   bf16* KT = reinterpret_cast<bf16*>(smem + L::oKT);
   bf16* GK = reinterpret_cast<bf16*>(smem + L::oGK);
   bf16* QT = reinterpret_cast<bf16*>(smem + L::oQT);
+  bf16* QTL = reinterpret_cast<bf16*>(smem + L::oQTL);  // low halves of tile 0's rows
   float* ES = reinterpret_cast<float*>(smem + L::oES);  // [4][DK] tile decays
   float* GC = reinterpret_cast<float*>(smem + L::oGC);  // [DK] chunk decay
   float* BS = reinterpret_cast<float*>(smem + L::oBS);  // [64] beta
@@ -362,6 +364,10 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       split8(kt, kth[kk], ktl[kk]);
       // (Gamma*Q) at operand positions 32kb + 8g.. of token r
       *reinterpret_cast<bf16x8*>(QT + r * ldQ + 32 * kb + 8 * g) = qt8;
+      // tile 0 keeps Gamma*Q split (its read-out of the entry state is the
+      // least decayed); there Gamma = P, so Gamma*Q is q P and its low half
+      // is qll
+      if (w == 0) *reinterpret_cast<bf16x8*>(QTL + r * ldQ + 32 * kb + 8 * g) = qll[kk];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
         st_bf16x4(GK + r * ldG + 32 * kb + 16 * hf + 4 * g, gk + 4 * hf);
@@ -663,6 +669,17 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     }
     __syncthreads();
 
+    // ---- tile 0 keeps Gamma*Q split: its low halves times the state's high
+    // halves (as the two-pass state pass adds them, before Mqk P)
+    if (w == 0) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 aql = frag_ld(QTL, ldQ, r, 32 * kb, g);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          accO[c] = mfma_bf16(aql, frag_ld(ST, ldS, vh0 + 16 * c + tr, 32 * kb, g), accO[c]);
+      }
+    }
     // ---- O += Mqk P; store o
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {

@@ -491,6 +491,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       const unsigned char* b = item_base(c);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) op.qf[kb] = *frame_ptr<bf16x8>(b, IM::q_frame(w, kb), lane);
+
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         // key block 1 of tiles 0 and 1 lies after the tile: its frames are
@@ -545,6 +546,18 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     // the updated state goes to LDS right after the update: neither holds up
     // the next chunk's first barrier.
     floatx4 ovp[NVT];  // o of the chunk before
+    // tile 0's low halves of Gamma*Q (wave 0 only): one buffer, refilled for
+    // the next chunk right after its use, a chunk ahead of the next use
+    bf16x8 qlb[NKB];
+    auto fetch_ql = [&](int c) {
+      if constexpr (!SUMMARY) {
+        if (w == 0) {
+          const unsigned char* b = item_base(c);
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) qlb[kb] = *frame_ptr<bf16x8>(b, IM::ql_frame(kb), lane);
+        }
+      }
+    };
     auto chunk = [&](int c, const Ops& op, Ops& nx) {
       int lane_x = lane;
       __asm__ volatile("" : "+v"(lane_x));
@@ -575,6 +588,17 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt) ov[vt] = a0[vt] + a1[vt];
         if (c > c_lo) store_o(c - 1, ovp, tr, g, lane_x);
+        // tile 0 keeps Gamma*Q split: its low halves times the state's high
+        // halves join o before the second barrier (after it the chain waves
+        // overwrite ST with the updated state)
+        if (w == 0) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt)
+              ov[vt] = mfma_bf16(qlb[kb], frag_ld(ST, ldS, 16 * vt + tr, 32 * kb, gs), ov[vt]);
+          fetch_ql(next_of(c));
+        }
       }
       __syncthreads();
       fetch_r(next_of(c), nx);
@@ -610,6 +634,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       Ops X, Y;
       fetch_w(c_lo, X);
       fetch_r(c_lo, X);
+      fetch_ql(c_lo);
       {
         const int tr = lane & 15, g = lane >> 4;
         put_state(g ^ ((tr >> 2) & 1), tr);

@@ -53,10 +53,10 @@ def test_workspace_sizes():
     of them; each block holds the frames of W, (Gamma*Q), Mqk, Ktil^T, T Diag(b)
     and the chunk's v rows, plus Gamma_C and the chunk's W-split flag, rounded
     to 256 B.  Like the state, it does not depend on T."""
-    # frames: W (hi, lo), Gamma*Q, Mqk (hi, lo), Ktil^T (hi, lo), T Diag(b) (hi, lo),
-    # then the chunk's 64 v rows (Dv / 8 frames of 1 KiB)
-    frames = {(128, 128): 4 * 4 * 2 + 4 * 4 + 16 + 8 * 4 + 16 + 16,
-              (64, 64): 4 * 2 * 2 + 4 * 2 + 16 + 4 * 4 + 16 + 8}
+    # frames: W (hi, lo), Gamma*Q (hi; lo of tile 0), Mqk (hi, lo), Ktil^T (hi, lo),
+    # T Diag(b) (hi, lo), then the chunk's 64 v rows (Dv / 8 frames of 1 KiB)
+    frames = {(128, 128): 4 * 4 * 2 + 4 * 4 + 4 + 16 + 8 * 4 + 16 + 16,
+              (64, 64): 4 * 2 * 2 + 4 * 2 + 2 + 16 + 4 * 4 + 16 + 8}
     up = lambda x: -(-x // 256) * 256
     for (dk, dv), f in frames.items():
         blk = up(f * 1024 + dk * 4 + 4)
