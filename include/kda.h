@@ -279,17 +279,21 @@ kda_status kda_decode_step_gated(const void* q, const void* k, const void* v,
  *   o      [B, N, H, Dv] o_dtype
  *
  * kda_decode_commit: for each session b, tokens 0..n_accept[b]-1 of the same
- * k, v, gate and beta tensors replayed into `state` (IN PLACE), with exactly
- * the arithmetic of kda_decode_step: the result is bitwise the state that
- * n_accept[b] decode steps would leave, and verify's outputs are bitwise the
- * steps' outputs.
+ * k, v, gate and beta tensors folded into `state` (IN PLACE).
  *   n_accept  DEVICE int32 [B], read on the device and clamped to [0, N];
  *             a session with 0 is left untouched
  *
+ * Arithmetic: below 8 drafts for verify and below 12 for commit, the tokens
+ * are stepped with exactly the arithmetic of kda_decode_step, so verify's
+ * outputs are bitwise the steps' outputs and commit leaves bitwise the state
+ * that n_accept[b] steps would leave.  From 8 (verify) and 12 (commit) drafts
+ * on, the drafts are one chunk of the chunk form ("Kimi Delta Attention 完全拆解",
+ * section "chunk 内并行、chunk 间递推"), evaluated in fp32 on the matrix cores:
+ * equal to the steps up to fp32 rounding (about 1e-6 relative), not bitwise.
+ *
  * Both: q, k, v, state and a per-channel gate 16-byte aligned, beta and
  * n_accept 4-byte aligned, o element-aligned; Dk, Dv in {64, 128}.  B == 0 or
- * N == 0 is a no-op; N > 16 returns KDA_ERR_UNSUPPORTED.  The three decode
- * calls run one kernel (in three modes) and one per-token routine.
+ * N == 0 is a no-op; N > 16 returns KDA_ERR_UNSUPPORTED.
  */
 kda_status kda_decode_verify(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
                              const kda_gate* gate, const float* beta, const float* state,
@@ -365,9 +369,11 @@ kda_status kda_epilogue(const void* o, kda_dtype o_dtype, const void* g, kda_dty
  *   state              [B, H, Dk, Dv] fp32
  *   out                output gate: g [B, N, H, Dv] x_dtype, w [Dv], eps
  *   y                  [B, N, H, Dv] y_dtype (not for commit)
- * With the standalone kda_prologue before and kda_epilogue after the plain call
- * (its o in fp32), the results are bitwise the same.  Alignment and limits as
- * for kda_decode_verify.
+ * The fused calls always step the tokens: with the standalone kda_prologue
+ * before and kda_epilogue after the plain call (its o in fp32), the results
+ * are bitwise the same wherever the plain call steps the tokens too (a step,
+ * and verify / commit below 8 / 12 drafts), else equal up to fp32 rounding.
+ * Alignment and limits as for kda_decode_verify.
  */
 typedef enum { KDA_DECODE_STEP = 0, KDA_DECODE_VERIFY = 1, KDA_DECODE_COMMIT = 2 } kda_decode_mode;
 

@@ -29,6 +29,7 @@
 // the session's N tokens in LDS once (alpha formed there), with the key-side
 // vectors permuted so each lane reads its rows as contiguous 16-byte words.
 #include "kda_common.h"
+#include "kda_frag.h"
 #include "kda_internal.h"
 #include "kda_layer.h"
 
@@ -551,6 +552,390 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void r
   }
 }
 
+// ---- Speculative verify / commit as one chunk -------------------------------
+// The n <= 16 draft tokens of a session are one chunk of the chunk form ("Kimi
+// Delta Attention 完全拆解", section "chunk 内并行、chunk 间递推"; the prefill's
+// algebra with the chunk starting at the first draft), evaluated in fp32 on the
+// fp32 matrix cores (v_mfma_f32_16x16x4_f32).  With Gamma_t = alpha_1 ... alpha_t
+// per key channel (from the first draft token) and S the state read:
+//   A_tj   = beta_t sum_c k_tc k_jc Gamma_tc / Gamma_jc  (j < t),  T = (I + A)^{-1}
+//   P      = T Diag(beta) (V - (Gamma*K) S)       (the corrected writes u_t)
+//   verify: o = (Gamma*Q) S + Mqk P,   Mqk_tj = sum_c q_tc k_jc Gamma_tc / Gamma_jc  (j <= t)
+//   commit: S' = Diag(Gamma_n) S + Ktil^T P,   Ktil_j = (Gamma_n / Gamma_j) k_j
+// The state tile is read once (and written once by commit) and the work on it is
+// two products (three for verify's o) on the matrix cores, where the token loop
+// spends four VALU operations per state element and token.  The results agree
+// with the token loop up to fp32 rounding, not bitwise.
+//
+// Mapping: one workgroup (4 waves) per (session, head).  Wave w owns the value
+// columns [w CW, (w + 1) CW); lane (g = l / 16, tr = l % 16) holds, for each
+// k-step s of 4 key channels, S[4s + g][w CW + E tr + e] (e < E = CW / 16) -- the
+// B operand of the fp32 MFMA with the tile's columns taken E apart -- loaded as
+// E consecutive floats, so a row segment of the wave's columns is one
+// contiguous 64..128-byte access.  The token-side operands (Gamma*K, k / Gamma,
+// Gamma*Q) sit in LDS as [token][channel]; A and Mqk are summed over the key
+// channels by the four waves in parts; T is formed by every wave for itself
+// (N^16 = 0 for the strictly lower 16 x 16 A: (I + N)^{-1} = (I - N)(I + N^2)
+// (I + N^4)(I + N^8)).  Ktil^T for commit is stored with its rows permuted so
+// that the product's accumulator rows are the state rows each lane holds.
+// The decay ratios are factored as (Gamma_t k_t) . (k_j / Gamma_j) while every
+// channel's Gamma_n stays at or above kTileMin; otherwise A and Mqk come from
+// running products of the decays between the two tokens (exact, slower).
+template <int DK, int DV, bool COMMIT>
+struct SpecGeo {
+  static constexpr int CW = DV / 4;   // value columns per wave
+  static constexpr int E = CW / 16;   // columns per lane (1 or 2)
+  static constexpr int KS = DK / 4;   // k-steps over the key channels
+  static constexpr int KW = KS / 4;   // k-steps per wave of the A / Mqk sums
+  static constexpr int ld = DK + 4;   // [16][DK] token arrays (conflict-free reads)
+  static constexpr int ldT = 20;      // the 16 x 16 scratch
+  static constexpr int ldKt = 16;     // commit's Ktil^T [DK][16]
+  static constexpr int oK = 0;              // k, then Gamma*k
+  static constexpr int oA = oK + 16 * ld;   // alpha, then k / Gamma
+  static constexpr int oQ = oA + 16 * ld;   // verify: q, then Gamma*q; commit: Ktil^T
+  static constexpr int szQ = COMMIT ? DK * ldKt : 16 * ld;
+  static constexpr int oB = oQ + szQ;       // beta [16]
+  static constexpr int oG = oB + 16;        // commit: Gamma_n [DK]
+  static constexpr int oF = oG + DK;        // exact-path flags, one per scanning wave
+  static constexpr int oP = oF + 4;         // partial A / Mqk sums [4][2][256]
+  static constexpr int oW = oP + 4 * 2 * 256;  // per-wave 16 x 16 scratch [4][16 * ldT]
+  static constexpr int total = oW + 4 * 16 * ldT;
+  static_assert(oP % 4 == 0 && oW % 4 == 0 && oQ % 4 == 0, "16-byte LDS rows");
+};
+
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// M X for a 16 x 16 M whose row this lane read as a = M[tr][4g .. 4g + 3] and
+// X in the accumulator layout (lane holds X[4g + i][tr]): MFMA i takes k-slot g
+// as k = 4g + i.  The result is in the accumulator layout.
+__device__ __forceinline__ floatx4 mm16(const floatx4& a, const floatx4& x) {
+  floatx4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y = mfma4(a[i], x[i], y);
+  return y;
+}
+__device__ __forceinline__ void lds_sync() { __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int E>
+struct SpecVec;
+template <>
+struct SpecVec<1> {
+  typedef float F;
+  static __device__ __forceinline__ void ld(const float* p, float (&x)[1]) { x[0] = *p; }
+  static __device__ __forceinline__ void st(float* p, const float (&x)[1]) {
+    __builtin_nontemporal_store(x[0], p);
+  }
+};
+template <>
+struct SpecVec<2> {
+  typedef float F __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ void ld(const float* p, float (&x)[2]) {
+    const F t = *reinterpret_cast<const F*>(p);
+    x[0] = t[0];
+    x[1] = t[1];
+  }
+  static __device__ __forceinline__ void st(float* p, const float (&x)[2]) {
+    __builtin_nontemporal_store(F{x[0], x[1]}, reinterpret_cast<F*>(p));
+  }
+};
+template <typename T, int E>
+__device__ __forceinline__ void ld_elems(const T* p, float (&x)[E]) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = (float)p[e];
+}
+template <typename T, int E>
+__device__ __forceinline__ void st_elems(T* p, const float (&x)[E]) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) p[e] = (T)x[e];
+}
+
+template <int DK, int DV, typename TIn, typename TOut, int KIND, bool COMMIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || sizeof(TIn) == 4 ? 3 : 4))) void spec_chunk_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v, Gate gate,
+    const float* __restrict__ beta, float* __restrict__ state, TOut* __restrict__ o,
+    const int32_t* __restrict__ n_accept, int N, int H) {
+  using G = SpecGeo<DK, DV, COMMIT>;
+  constexpr int CW = G::CW, E = G::E, KS = G::KS, ld = G::ld, ldT = G::ldT, ldKt = G::ldKt;
+  __shared__ __align__(16) float sm[G::total];
+  float* sK = sm + G::oK;
+  float* sA = sm + G::oA;
+  float* sQ = sm + G::oQ;
+  float* sB = sm + G::oB;
+  float* part = sm + G::oP;
+
+  const int tile = blockIdx.x;  // (session, head) flattened
+  const int sb = tile / H, h = tile - sb * H;
+  int n = N;
+  if constexpr (COMMIT) {
+    const int na = n_accept[sb];
+    n = na < 0 ? 0 : (na > N ? N : na);
+    if (n == 0) return;  // nothing accepted: the state stays as it is
+  }
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tr = lane & 15, g = lane >> 4;
+  const int col0 = w * CW + E * tr;  // this lane's first value column
+
+  // The tokens' inputs are issued first and the state tile after them: loads
+  // complete in order, so the token work below waits only for its own loads
+  // while the state is still arriving.  Rows n..15 are alpha = 1, k = q = 0,
+  // beta = 0.
+  constexpr int SIT = 16 * (DK / 4) / 256;  // staging items per thread
+  floatx4 ga[SIT], k4[SIT], q4[SIT];
+#pragma unroll
+  for (int it = 0; it < SIT; ++it) {
+    const int idx = tid + 256 * it, t = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+    const bool ok = t < n;
+    const size_t row = ((size_t)sb * N + (ok ? t : 0)) * H + h;
+    ga[it] = gate_load4<KIND>(gate, ok, row, DK, c);
+    k4[it] = ok ? ld4<TIn>(k + row * DK + c) : floatx4{0.f, 0.f, 0.f, 0.f};
+    q4[it] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (!COMMIT) q4[it] = ok ? ld4<TIn>(q + row * DK + c) : q4[it];
+  }
+  const float bt = tid < n ? beta[((size_t)sb * N + tid) * H + h] : 0.f;
+  float vv[4][E];  // v of rows 4g + i at this lane's columns
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 4 * g + i;
+#pragma unroll
+    for (int e = 0; e < E; ++e) vv[i][e] = 0.f;
+    if (t < n) ld_elems<TIn, E>(v + (((size_t)sb * N + t) * H + h) * DV + col0, vv[i]);
+  }
+  // the state tile: k-step s holds row 4s + g
+  float* S = state + (size_t)tile * DK * DV;
+  float sr[KS][E];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) SpecVec<E>::ld(S + (size_t)(4 * s + g) * DV + col0, sr[s]);
+
+  const float scl = KIND == GATE_BOUNDED ? expf(gate.a_log[h]) : 1.f;
+#pragma unroll
+  for (int it = 0; it < SIT; ++it) {
+    const int idx = tid + 256 * it, t = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+    floatx4 a4 = ga[it];
+    if constexpr (KIND == GATE_LOG) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a4[e] = expf(a4[e]);
+    } else if constexpr (KIND == GATE_BOUNDED) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a4[e] = gate_bounded(a4[e], scl, gate.g_min);
+    }
+    *reinterpret_cast<floatx4*>(sA + t * ld + c) = a4;
+    *reinterpret_cast<floatx4*>(sK + t * ld + c) = k4[it];
+    if constexpr (!COMMIT) *reinterpret_cast<floatx4*>(sQ + t * ld + c) = q4[it];
+  }
+  if (tid < 16) sB[tid] = bt;
+  __syncthreads();
+
+  // per key channel: Gamma_t by a running product; Gamma*k, k / Gamma (and
+  // Gamma*q) in place; commit: Ktil by a suffix product (no division), and
+  // Gamma_n (each block of four tokens read ahead of its products)
+  if (tid < DK) {
+    const int c = tid;
+    if constexpr (COMMIT) {
+      const int p = (c & ~15) + 4 * (c & 3) + ((c & 15) >> 2);  // Ktil^T row of channel c
+      float sfx = 1.f;
+#pragma unroll
+      for (int t0 = 12; t0 >= 0; t0 -= 4) {
+        float al[4], kc[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          al[u] = sA[(t0 + u) * ld + c];
+          kc[u] = sK[(t0 + u) * ld + c];
+        }
+#pragma unroll
+        for (int u = 3; u >= 0; --u) {
+          sQ[p * ldKt + t0 + u] = sfx * kc[u];
+          sfx *= al[u];
+        }
+      }
+    }
+    float gm = 1.f;
+#pragma unroll
+    for (int t0 = 0; t0 < 16; t0 += 4) {
+      float al[4], kc[4], qc[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        al[u] = sA[(t0 + u) * ld + c];
+        kc[u] = sK[(t0 + u) * ld + c];
+        if constexpr (!COMMIT) qc[u] = sQ[(t0 + u) * ld + c];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = t0 + u;
+        gm *= al[u];
+        sK[t * ld + c] = gm * kc[u];
+        // k / Gamma: read only while every channel stays in the factored range
+        sA[t * ld + c] = kc[u] * __builtin_amdgcn_rcpf(gm);
+        if constexpr (!COMMIT) sQ[t * ld + c] = gm * qc[u];
+      }
+    }
+    if constexpr (COMMIT) sm[G::oG + c] = gm;
+    const bool low = __builtin_amdgcn_ballot_w64(gm < frag::kTileMin) != 0;
+    if (lane == 0) sm[G::oF + w] = low ? 1.f : 0.f;
+  }
+  __syncthreads();
+  bool exact = sm[G::oF] != 0.f;
+  if constexpr (DK == 128) exact = exact || sm[G::oF + 1] != 0.f;
+
+  // ---- A (unscaled) and Mqk: rows t, columns j, parts over the key channels
+  if (!exact) {
+    floatx4 pa = {0.f, 0.f, 0.f, 0.f}, pm = pa;
+#pragma unroll
+    for (int s = w * G::KW; s < (w + 1) * G::KW; ++s) {
+      const int c = 4 * s + g;
+      const float kg = sA[tr * ld + c];
+      pa = mfma4(sK[tr * ld + c], kg, pa);
+      if constexpr (!COMMIT) pm = mfma4(sQ[tr * ld + c], kg, pm);
+    }
+    *reinterpret_cast<floatx4*>(part + (2 * w) * 256 + 4 * lane) = pa;
+    *reinterpret_cast<floatx4*>(part + (2 * w + 1) * 256 + 4 * lane) = pm;
+  } else {
+    // thread (t, j): the decays between the two tokens as a running product
+    const int t = tid >> 4, j = tid & 15;
+    float a = 0.f, m = 0.f;
+    if (j <= t && t < n) {
+      const size_t rt = ((size_t)sb * N + t) * H + h, rj = ((size_t)sb * N + j) * H + h;
+      for (int c = 0; c < DK; c += 4) {
+        floatx4 r = {1.f, 1.f, 1.f, 1.f};
+        for (int u = j + 1; u <= t; ++u) {
+          const floatx4 a4 = alpha4_exact<KIND>(gate, ((size_t)sb * N + u) * H + h, DK, c, scl);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[e] = r[e] * a4[e];
+        }
+        const floatx4 kt = ld4<TIn>(k + rt * DK + c), kj = ld4<TIn>(k + rj * DK + c);
+        floatx4 qt = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (!COMMIT) qt = ld4<TIn>(q + rt * DK + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float kr = kj[e] * r[e];
+          a = a + kt[e] * kr;
+          m = m + qt[e] * kr;
+        }
+      }
+    }
+    // (t, j) sits at lane 16 (t / 4) + j, entry t % 4 of the accumulator layout
+    const int pos = 4 * (16 * (t >> 2) + j) + (t & 3);
+    part[pos] = a;
+    part[256 + pos] = m;
+    for (int idx = tid; idx < 3 * 2 * 256; idx += 256) part[2 * 256 + idx] = 0.f;
+  }
+  __syncthreads();
+  floatx4 am = {0.f, 0.f, 0.f, 0.f}, mm = am;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    am += *reinterpret_cast<const floatx4*>(part + (2 * u) * 256 + 4 * lane);
+    if constexpr (!COMMIT) mm += *reinterpret_cast<const floatx4*>(part + (2 * u + 1) * 256 + 4 * lane);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 4 * g + i;
+    am[i] = tr < t ? sB[t] * am[i] : 0.f;
+    mm[i] = tr <= t ? mm[i] : 0.f;
+  }
+
+  // ---- T Diag(beta) (and Mqk) as row reads of this wave's scratch
+  float* buf = sm + G::oW + w * 16 * ldT;
+  auto put = [&](const floatx4& x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) buf[(4 * g + i) * ldT + tr] = x[i];
+    lds_sync();
+  };
+  auto row = [&]() -> floatx4 {
+    const floatx4 r = *reinterpret_cast<const floatx4*>(buf + tr * ldT + 4 * g);
+    lds_sync();
+    return r;
+  };
+  put(am);
+  const floatx4 aN = row();
+  const floatx4 n2 = mm16(aN, am);
+  put(n2);
+  const floatx4 a2 = row();
+  const floatx4 n4 = mm16(a2, n2);
+  put(n4);
+  const floatx4 a4r = row();
+  floatx4 X = mm16(a4r, n4);  // N^8
+#pragma unroll
+  for (int i = 0; i < 4; ++i) X[i] += (4 * g + i == tr) ? 1.f : 0.f;
+  X += mm16(a4r, X);
+  X += mm16(a2, X);
+  X -= mm16(aN, X);
+  const float bj = sB[tr];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) X[i] = X[i] * bj;
+  put(X);
+  const floatx4 aT = row();
+  floatx4 aM = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (!COMMIT) {
+    put(mm);
+    aM = row();
+  }
+
+  // ---- (Gamma*K) S and (Gamma*Q) S on this wave's columns
+  floatx4 R[E], Y[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    R[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+    Y[e] = R[e];
+  }
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const float gk = sK[tr * ld + 4 * s + g];
+#pragma unroll
+    for (int e = 0; e < E; ++e) R[e] = mfma4(gk, sr[s][e], R[e]);
+    if constexpr (!COMMIT) {
+      const float gq = sQ[tr * ld + 4 * s + g];
+#pragma unroll
+      for (int e = 0; e < E; ++e) Y[e] = mfma4(gq, sr[s][e], Y[e]);
+    }
+  }
+
+  // ---- P = T Diag(beta) (V - (Gamma*K) S): rows t = 4g + i, columns col0 + e
+  floatx4 P[E];
+  {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      floatx4 d;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i] = vv[i][e] - R[e][i];
+      P[e] = mm16(aT, d);
+    }
+  }
+
+  if constexpr (!COMMIT) {
+    float ov[4][E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const floatx4 x = Y[e] + mm16(aM, P[e]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[i][e] = x[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * g + i;
+      if (t < n) st_elems<TOut, E>(o + (((size_t)sb * N + t) * H + h) * DV + col0, ov[i]);
+    }
+  } else {
+    // S' = Diag(Gamma_n) S + Ktil^T P: row tile rt of the permuted Ktil^T gives
+    // accumulator row 4g + i = state row 16 rt + 4i + g = k-step 4 rt + i
+    const float* gn = sm + G::oG;
+#pragma unroll
+    for (int rt = 0; rt < DK / 16; ++rt) {
+      const floatx4 ak = *reinterpret_cast<const floatx4*>(sQ + (16 * rt + tr) * ldKt + 4 * g);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const floatx4 acc = mm16(ak, P[e]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 4 * rt + i;
+          sr[s][e] = gn[4 * s + g] * sr[s][e] + acc[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) SpecVec<E>::st(S + (size_t)(4 * s + g) * DV + col0, sr[s]);
+  }
+}
+
 // LDS of one workgroup: N token records; with the layer, the raw rows
 // [3 + N][2 Dk + Dv], the gate logits [N][Dv] and the conv taps [2 Dk + Dv][4]
 template <int DK, int DV, bool VERIFY>
@@ -570,9 +955,38 @@ static hipError_t allow_lds(K kern, int bytes, bool& done) {
   return e;
 }
 
+// Verify and commit of at least this many draft tokens run as one chunk
+// (spec_chunk_kernel); fewer, and the layer's fused calls, step the tokens.
+// The token loop's cost grows with N and the chunk form's hardly does; on
+// MI355X at 64 sessions x 96 heads x 128 x 128 they cross near 7 tokens for
+// verify (8: 138 against 157 us) and near 12 for commit (16: 180 against
+// 197 us; 8: 162 against 156 us).
+constexpr int kSpecVerifyChunkMin = 8;
+constexpr int kSpecCommitChunkMin = 12;
+
+template <int DK, int DV, typename TIn, typename TOut, int KIND>
+static hipError_t launch_spec_chunk(const DecodeArgs& a) {
+  const dim3 grid(a.B * a.H);
+  if (a.mode == DECODE_VERIFY) {
+    hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, TOut, KIND, false>), grid, dim3(256), 0,
+                       (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
+                       a.gate, a.beta, a.state, (TOut*)a.o, (const int32_t*)nullptr, a.N, a.H);
+  } else {
+    hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, float, KIND, true>), grid, dim3(256), 0,
+                       (hipStream_t)a.stream, (const TIn*)nullptr, (const TIn*)a.k, (const TIn*)a.v,
+                       a.gate, a.beta, a.state, (float*)nullptr, a.n_accept, a.N, a.H);
+  }
+  return hipGetLastError();
+}
+
 template <int DK, int DV, typename TIn, typename TOut, int KIND, bool LAYER>
 static hipError_t launch_decode_l(const DecodeArgs& a) {
   const dim3 grid(a.B * a.H);
+  if constexpr (!LAYER) {
+    if ((a.mode == DECODE_VERIFY && a.N >= kSpecVerifyChunkMin) ||
+        (a.mode == DECODE_COMMIT && a.N >= kSpecCommitChunkMin))
+      return launch_spec_chunk<DK, DV, TIn, TOut, KIND>(a);
+  }
   static bool lds_v = false, lds_c = false;  // per instantiation; idempotent if raced
   if (a.mode == DECODE_VERIFY) {
     if (hipError_t e = allow_lds(decode_kernel<DK, DV, TIn, TOut, KIND, DECODE_VERIFY, LAYER>,

@@ -172,9 +172,11 @@ def test_decode_layer_step_equals_composed(kind, dtype, Dk, Dv):
 
 @pytest.mark.parametrize("kind", ["alpha", "bounded", "scalar"])
 def test_decode_layer_spec_round_equals_composed(kind):
-    """Fused verify: bitwise the composed verify, conv state and state untouched.
-    Fused commit of seeded prefixes: the state bitwise the plain commit of the
-    prologue's k, v; the conv state exactly the oracle's after each prefix."""
+    """Fused verify against the composed verify (within fp32 rounding: the fused
+    layer always steps the tokens, the plain calls take the chunk form from
+    eight drafts on), conv state and state untouched.  Fused commit of seeded
+    prefixes: the state against the plain commit of the prologue's k, v,
+    likewise; the conv state exactly the oracle's after each prefix."""
     d = dev()
     B, N, H, D = 4, 6, 3, 128
     L, gate, a_log, beta, s0 = _layer_case(B, N, H, D, D, 1220, kind, torch.bfloat16, d)
@@ -185,7 +187,7 @@ def test_decode_layer_spec_round_equals_composed(kind):
     o = kda.decode_verify(q, k, v, gate, beta, s0, gate=kind, a_log=a_log)
     y2 = kda.epilogue(o, L.g, L.norm_w, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert torch.equal(y, y2)
+    close(y, y2, TOL_F32, "steps")
     assert torch.equal(cs, L.conv_state) and torch.equal(st, s0)
     n_acc = torch.tensor([N, 0, 2, 5], dtype=torch.int32, device=d)
     kda.decode_layer("commit", L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, cs, gate, beta, st,
@@ -193,7 +195,7 @@ def test_decode_layer_spec_round_equals_composed(kind):
     st2 = s0.clone()
     kda.decode_commit(k, v, gate, beta, n_acc, st2, gate=kind, a_log=a_log)
     torch.cuda.synchronize()
-    assert torch.equal(st, st2)
+    close(st, st2, TOL_F32, "state")
     for b, n in enumerate(n_acc.tolist()):
         if n == 0:
             assert torch.equal(cs[b], L.conv_state[b])
@@ -232,7 +234,8 @@ def test_decode_layer_steps_against_oracle():
 
 def test_decode_layer_max_draft():
     """16 draft tokens (the largest LDS footprint of the fused layer): verify and
-    commit bitwise the composed calls."""
+    commit against the composed calls (within fp32 rounding: the plain calls
+    take the chunk form), the conv state bitwise."""
     d = dev()
     B, N, H, D = 2, 16, 2, 128
     L, gate, a_log, beta, s0 = _layer_case(B, N, H, D, D, 1260, "alpha", torch.bfloat16, d)
@@ -248,4 +251,6 @@ def test_decode_layer_max_draft():
     st2 = s0.clone()
     kda.decode_commit(k, v, gate, beta, n_acc, st2)
     torch.cuda.synchronize()
-    assert torch.equal(y, y2) and torch.equal(st, st2) and torch.equal(cs, cso)
+    close(y, y2, TOL_F32, "steps")
+    close(st, st2, TOL_F32, "state")
+    assert torch.equal(cs, cso)
