@@ -263,9 +263,10 @@ __device__ __forceinline__ bool w_split_chunk(const float* GC, int lane) {
 //                                only for a chunk that keeps W split
 //                                (w_split_chunk)
 //   Q  [w][kb < DK/32]           A operand of (Gamma*Q) S, same positions
-//   QL [kb < DK/32]              low halves of tile 0's Gamma*Q (the tile whose
-//                                read-out of the entry state is the least
-//                                decayed keeps Gamma*Q split)
+//   QL [kb < DK/32]              low halves of tile 0's Gamma*Q, written and
+//                                read only in a sequence's first chunk (there
+//                                the read-out of the entry state is the least
+//                                decayed and keeps Gamma*Q split)
 //   M  [w][kb < 2][hi, lo]       A operand of Mqk P (k = token position)
 //   K  [rt < DK/16][kb < 2][hi, lo]  A operand of Ktil^T P for state rows
 //                                16rt..16rt+15 (k = token position)
@@ -284,7 +285,7 @@ struct Images {
   static constexpr int W = 0;
   static constexpr int Q = W + 4 * NKB * 2;
   // Gamma*Q: the high halves of every tile, then the low halves of tile 0
-  // (the tile whose read-out of the entry state is the least decayed)
+  // (used in a sequence's first chunk only)
   static constexpr int QL = Q + 4 * NKB;
   static constexpr int M = QL + NKB;
   static constexpr int K = M + 4 * 2 * 2;

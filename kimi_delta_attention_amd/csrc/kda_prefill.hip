@@ -364,10 +364,12 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
       split8(kt, kth[kk], ktl[kk]);
       // (Gamma*Q) at operand positions 32kb + 8g.. of token r
       *reinterpret_cast<bf16x8*>(QT + r * ldQ + 32 * kb + 8 * g) = qt8;
-      // tile 0 keeps Gamma*Q split (its read-out of the entry state is the
-      // least decayed); there Gamma = P, so Gamma*Q is q P and its low half
-      // is qll
-      if (w == 0) *reinterpret_cast<bf16x8*>(QTL + r * ldQ + 32 * kb + 8 * g) = qll[kk];
+      // tile 0 of a sequence's first chunk keeps Gamma*Q split (its read-out
+      // of the entry state is the least decayed, and a short sequence is
+      // nothing else); there Gamma = P, so Gamma*Q is q P and its low half is
+      // qll
+      if (w == 0 && cur.c0 == 0)
+        *reinterpret_cast<bf16x8*>(QTL + r * ldQ + 32 * kb + 8 * g) = qll[kk];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
         st_bf16x4(GK + r * ldG + 32 * kb + 16 * hf + 4 * g, gk + 4 * hf);
@@ -669,9 +671,10 @@ __global__ __launch_bounds__(NTH) void prefill_bf16_kernel(
     }
     __syncthreads();
 
-    // ---- tile 0 keeps Gamma*Q split: its low halves times the state's high
-    // halves (as the two-pass state pass adds them, before Mqk P)
-    if (w == 0) {
+    // ---- tile 0 of the first chunk keeps Gamma*Q split: its low halves times
+    // the state's high halves (as the two-pass state pass adds them, before
+    // Mqk P)
+    if (w == 0 && cur.c0 == 0) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const bf16x8 aql = frag_ld(QTL, ldQ, r, 32 * kb, g);

@@ -293,6 +293,7 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     int tid_x = threadIdx.x;  // the same for the workgroup-wide prologue staging
     __asm__ volatile("" : "+v"(tid_x));
     const Item cur = PRO ? locate(item) : pre;
+    const bool first = cur.tok0 == cur.start;  // the sequence's first chunk
     if constexpr (PRO) load_in(item, cur, lane_x);
     const long long tok0 = cur.tok0;
     const int nv = cur.nv, hd = cur.hd;
@@ -572,10 +573,10 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
       *reinterpret_cast<bf16x8*>(QLh + r * ldK + 32 * kb + 8 * g) = yh;
       *reinterpret_cast<bf16x8*>(QLl + r * ldK + 32 * kb + 8 * g) = yl;
       put_frame(im, IM::q_frame(w, kb), lane_x, qt8);
-      // tile 0 keeps Gamma*Q split (its read-out of the entry state is the
-      // least decayed); there Gamma = P, so Gamma*Q is q P and its low half
-      // is yl
-      if (w == 0) put_frame(im, IM::ql_frame(kb), lane_x, yl);
+      // tile 0 of a sequence's first chunk keeps Gamma*Q split (its read-out
+      // of the entry state is the least decayed, and a short sequence is
+      // nothing else); there Gamma = P, so Gamma*Q is q P and its low half is yl
+      if (w == 0 && first) put_frame(im, IM::ql_frame(kb), lane_x, yl);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) st_bf16x4(GK + r * ldK + 32 * kb + 16 * hf + 4 * g, gk + 4 * hf);
       if (w == 0 && tr == 0) {

@@ -546,8 +546,8 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
     // the updated state goes to LDS right after the update: neither holds up
     // the next chunk's first barrier.
     floatx4 ovp[NVT];  // o of the chunk before
-    // tile 0's low halves of Gamma*Q (wave 0 only): one buffer, refilled for
-    // the next chunk right after its use, a chunk ahead of the next use
+    // the low halves of Gamma*Q of tile 0 of the sequence's first chunk (wave
+    // 0 only), fetched with the first chunk's other operands
     bf16x8 qlb[NKB];
     auto fetch_ql = [&](int c) {
       if constexpr (!SUMMARY) {
@@ -588,16 +588,16 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt) ov[vt] = a0[vt] + a1[vt];
         if (c > c_lo) store_o(c - 1, ovp, tr, g, lane_x);
-        // tile 0 keeps Gamma*Q split: its low halves times the state's high
-        // halves join o before the second barrier (after it the chain waves
-        // overwrite ST with the updated state)
-        if (w == 0) {
+        // tile 0 of the sequence's first chunk keeps Gamma*Q split: its low
+        // halves times the state's high halves join o before the second
+        // barrier (after it the chain waves overwrite ST with the updated
+        // state)
+        if (w == 0 && c == 0) {
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int vt = 0; vt < NVT; ++vt)
               ov[vt] = mfma_bf16(qlb[kb], frag_ld(ST, ldS, 16 * vt + tr, 32 * kb, gs), ov[vt]);
-          fetch_ql(next_of(c));
         }
       }
       __syncthreads();
@@ -634,7 +634,7 @@ __global__ __launch_bounds__(NTH_S) void prefill_state_kernel(
       Ops X, Y;
       fetch_w(c_lo, X);
       fetch_r(c_lo, X);
-      fetch_ql(c_lo);
+      if (c_lo == 0) fetch_ql(c_lo);
       {
         const int tr = lane & 15, g = lane >> 4;
         put_state(g ^ ((tr >> 2) & 1), tr);
