@@ -283,10 +283,10 @@ kda_status kda_decode_step_gated(const void* q, const void* k, const void* v,
  *   n_accept  DEVICE int32 [B], read on the device and clamped to [0, N];
  *             a session with 0 is left untouched
  *
- * Arithmetic: below 8 drafts for verify and below 12 for commit, the tokens
+ * Arithmetic: below 6 drafts for verify and below 12 for commit, the tokens
  * are stepped with exactly the arithmetic of kda_decode_step, so verify's
  * outputs are bitwise the steps' outputs and commit leaves bitwise the state
- * that n_accept[b] steps would leave.  From 8 (verify) and 12 (commit) drafts
+ * that n_accept[b] steps would leave.  From 6 (verify) and 12 (commit) drafts
  * on, the drafts are one chunk of the chunk form ("Kimi Delta Attention 完全拆解",
  * section "chunk 内并行、chunk 间递推"), evaluated in fp32 on the matrix cores:
  * equal to the steps up to fp32 rounding (about 1e-6 relative), not bitwise.
@@ -372,7 +372,7 @@ kda_status kda_epilogue(const void* o, kda_dtype o_dtype, const void* g, kda_dty
  * The fused calls always step the tokens: with the standalone kda_prologue
  * before and kda_epilogue after the plain call (its o in fp32), the results
  * are bitwise the same wherever the plain call steps the tokens too (a step,
- * and verify / commit below 8 / 12 drafts), else equal up to fp32 rounding.
+ * and verify / commit below 6 / 12 drafts), else equal up to fp32 rounding.
  * Alignment and limits as for kda_decode_verify.
  */
 typedef enum { KDA_DECODE_STEP = 0, KDA_DECODE_VERIFY = 1, KDA_DECODE_COMMIT = 2 } kda_decode_mode;

@@ -650,7 +650,13 @@ __device__ __forceinline__ void st_elems(T* p, const float (&x)[E]) {
   for (int e = 0; e < E; ++e) p[e] = (T)x[e];
 }
 
-template <int DK, int DV, typename TIn, typename TOut, int KIND, bool COMMIT>
+// FORM: SPEC_VERIFY, SPEC_VERIFY8 (at most 8 drafts: Gamma*K and Gamma*Q
+// stacked into one 16-row operand, so one pass of products with the state
+// gives both), SPEC_COMMIT.
+enum SpecForm { SPEC_VERIFY = 0, SPEC_VERIFY8 = 1, SPEC_COMMIT = 2 };
+
+template <int DK, int DV, typename TIn, typename TOut, int KIND, int FORM,
+          bool COMMIT = FORM == SPEC_COMMIT, bool STACK = FORM == SPEC_VERIFY8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || sizeof(TIn) == 4 ? 3 : 4))) void spec_chunk_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v, Gate gate,
     const float* __restrict__ beta, float* __restrict__ state, TOut* __restrict__ o,
@@ -865,7 +871,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || s
   put(X);
   const floatx4 aT = row();
   floatx4 aM = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (!COMMIT) {
+  if constexpr (STACK) {
+    // Mqk shifted down by 8 rows: its product with P lands on the rows that
+    // hold (Gamma*Q) S below
+#pragma unroll
+    for (int i = 0; i < 4; ++i) buf[((4 * g + i + 8) & 15) * ldT + tr] = g < 2 ? mm[i] : 0.f;
+    lds_sync();
+    aM = row();
+  } else if constexpr (!COMMIT) {
     put(mm);
     aM = row();
   }
@@ -879,10 +892,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || s
   }
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    const float gk = sK[tr * ld + 4 * s + g];
+    // stacked: rows 0..7 take Gamma*K, rows 8..15 Gamma*Q of tokens 0..7
+    const float gk = STACK && tr >= 8 ? sQ[(tr - 8) * ld + 4 * s + g] : sK[tr * ld + 4 * s + g];
 #pragma unroll
     for (int e = 0; e < E; ++e) R[e] = mfma4(gk, sr[s][e], R[e]);
-    if constexpr (!COMMIT) {
+    if constexpr (!COMMIT && !STACK) {
       const float gq = sQ[tr * ld + 4 * s + g];
 #pragma unroll
       for (int e = 0; e < E; ++e) Y[e] = mfma4(gq, sr[s][e], Y[e]);
@@ -896,7 +910,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || s
     for (int e = 0; e < E; ++e) {
       floatx4 d;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = vv[i][e] - R[e][i];
+      for (int i = 0; i < 4; ++i) d[i] = STACK && g >= 2 ? 0.f : vv[i][e] - R[e][i];
       P[e] = mm16(aT, d);
     }
   }
@@ -905,14 +919,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || s
     float ov[4][E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const floatx4 x = Y[e] + mm16(aM, P[e]);
+      const floatx4 x = (STACK ? R[e] : Y[e]) + mm16(aM, P[e]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) ov[i][e] = x[i];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = 4 * g + i;
-      if (t < n) st_elems<TOut, E>(o + (((size_t)sb * N + t) * H + h) * DV + col0, ov[i]);
+      const int t = STACK ? 4 * (g - 2) + i : 4 * g + i;
+      if ((!STACK || g >= 2) && t < n)
+        st_elems<TOut, E>(o + (((size_t)sb * N + t) * H + h) * DV + col0, ov[i]);
     }
   } else {
     // S' = Diag(Gamma_n) S + Ktil^T P: row tile rt of the permuted Ktil^T gives
@@ -958,21 +973,25 @@ static hipError_t allow_lds(K kern, int bytes, bool& done) {
 // Verify and commit of at least this many draft tokens run as one chunk
 // (spec_chunk_kernel); fewer, and the layer's fused calls, step the tokens.
 // The token loop's cost grows with N and the chunk form's hardly does; on
-// MI355X at 64 sessions x 96 heads x 128 x 128 they cross near 7 tokens for
-// verify (8: 138 against 157 us) and near 12 for commit (16: 180 against
-// 197 us; 8: 162 against 156 us).
-constexpr int kSpecVerifyChunkMin = 8;
+// MI355X at 64 sessions x 96 heads x 128 x 128 they cross near 5 tokens for
+// verify (stacked form, 6: 115 against about 120 us; 8: 115 against 147 us)
+// and near 12 for commit (16: 178 against 201 us; 8: 162 against 153 us).
+constexpr int kSpecVerifyChunkMin = 6;
 constexpr int kSpecCommitChunkMin = 12;
 
 template <int DK, int DV, typename TIn, typename TOut, int KIND>
 static hipError_t launch_spec_chunk(const DecodeArgs& a) {
   const dim3 grid(a.B * a.H);
-  if (a.mode == DECODE_VERIFY) {
-    hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, TOut, KIND, false>), grid, dim3(256), 0,
+  if (a.mode == DECODE_VERIFY && a.N <= 8) {
+    hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY8>), grid, dim3(256), 0,
+                       (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
+                       a.gate, a.beta, a.state, (TOut*)a.o, (const int32_t*)nullptr, a.N, a.H);
+  } else if (a.mode == DECODE_VERIFY) {
+    hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY>), grid, dim3(256), 0,
                        (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
                        a.gate, a.beta, a.state, (TOut*)a.o, (const int32_t*)nullptr, a.N, a.H);
   } else {
-    hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, float, KIND, true>), grid, dim3(256), 0,
+    hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, float, KIND, SPEC_COMMIT>), grid, dim3(256), 0,
                        (hipStream_t)a.stream, (const TIn*)nullptr, (const TIn*)a.k, (const TIn*)a.v,
                        a.gate, a.beta, a.state, (float*)nullptr, a.n_accept, a.N, a.H);
   }

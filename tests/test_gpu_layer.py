@@ -174,7 +174,7 @@ def test_decode_layer_step_equals_composed(kind, dtype, Dk, Dv):
 def test_decode_layer_spec_round_equals_composed(kind):
     """Fused verify against the composed verify (within fp32 rounding: the fused
     layer always steps the tokens, the plain calls take the chunk form from
-    eight drafts on), conv state and state untouched.  Fused commit of seeded
+    six drafts on), conv state and state untouched.  Fused commit of seeded
     prefixes: the state against the plain commit of the prologue's k, v,
     likewise; the conv state exactly the oracle's after each prefix."""
     d = dev()

@@ -54,9 +54,10 @@ def _oracle_commit(inp, alpha, n_acc):
 
 @pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
 @pytest.mark.parametrize("qkv", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("N", [7, 12])
+@pytest.mark.parametrize("N", [5, 8, 12])
 def test_verify_and_commit_against_oracle(Dk, Dv, qkv, N):
-    """Seven drafts step the tokens; twelve take the chunk form for both calls."""
+    """Five drafts step the tokens; eight take the chunk form for verify (its
+    stacked form of up to eight drafts), twelve for both calls."""
     d = dev()
     B, H = 3, 4
     inp, gate, a_log, alpha = _case(B, N, H, Dk, Dv, seed=900 + Dk + Dv + N, qkv=qkv)
