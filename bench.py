@@ -102,6 +102,7 @@ PREFILL_SOURCES = ["kimi_delta_attention_amd/csrc/kda_prefill.hip",
                    "kimi_delta_attention_amd/csrc/kda_common.h"]
 DECODE_SOURCES = ["kimi_delta_attention_amd/csrc/kda_decode.hip",
                   "kimi_delta_attention_amd/csrc/kda_common.h",
+                  "kimi_delta_attention_amd/csrc/kda_frag.h",
                   "kimi_delta_attention_amd/csrc/kda_layer.h"]
 
 
