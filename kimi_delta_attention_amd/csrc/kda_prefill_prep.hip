@@ -301,6 +301,13 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     const int tr = lane_x & 15;
     const int g = lane_x >> 4;
     const int w = (w4 + item) & 3;  // token tile of this wave
+    // issue priority by the tile's share of the item's work (tile 0 takes four
+    // of the ten A / Mqk blocks, tile 3 one): on a SIMD shared with the other
+    // workgroup's wave, the wave the next barrier waits for goes first
+    if (w == 0) __builtin_amdgcn_s_setprio(3);
+    else if (w == 1) __builtin_amdgcn_s_setprio(2);
+    else if (w == 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     const int r = 16 * w + tr;      // this lane's token within the chunk
     const bool okc = r < nv;
     const size_t thc = (size_t)(tok0 + r) * H + hd;
