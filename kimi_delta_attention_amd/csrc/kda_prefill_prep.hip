@@ -303,11 +303,18 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
     const int w = (w4 + item) & 3;  // token tile of this wave
     // issue priority by the tile's share of the item's work (tile 0 takes four
     // of the ten A / Mqk blocks, tile 3 one): on a SIMD shared with the other
-    // workgroup's wave, the wave the next barrier waits for goes first
-    if (w == 0) __builtin_amdgcn_s_setprio(3);
-    else if (w == 1) __builtin_amdgcn_s_setprio(2);
-    else if (w == 2) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
+    // workgroup's wave, the wave the next barrier waits for goes first.  The
+    // layer prologue deals its work by wave, not by tile, so with it the
+    // priorities are level until the prologue is done (set by tile from its
+    // start, they made that pass 10 % slower).
+    if constexpr (!PRO) {
+      if (w == 0) __builtin_amdgcn_s_setprio(3);
+      else if (w == 1) __builtin_amdgcn_s_setprio(2);
+      else if (w == 2) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    } else {
+      __builtin_amdgcn_s_setprio(0);
+    }
     const int r = 16 * w + tr;      // this lane's token within the chunk
     const bool okc = r < nv;
     const size_t thc = (size_t)(tok0 + r) * H + hd;
@@ -476,6 +483,12 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
         vin[j] = *reinterpret_cast<const uint4v*>(XR + (vrow + VRJ * j) * ldX + 2 * DK + vcol);
     }
 
+    if constexpr (PRO) {  // the prologue is done: priority by tile (see above)
+      if (w == 0) __builtin_amdgcn_s_setprio(3);
+      else if (w == 1) __builtin_amdgcn_s_setprio(2);
+      else if (w == 2) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     // ---- 1. within-tile decay products P (inclusive scan over the 16 tokens)
 #pragma unroll
     for (int kb = 0; kb < NKB; kb += 2) row_scan_mul<16>(&Pv[kb][0]);
