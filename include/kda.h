@@ -373,6 +373,9 @@ kda_status kda_epilogue(const void* o, kda_dtype o_dtype, const void* g, kda_dty
  * before and kda_epilogue after the plain call (its o in fp32), the results
  * are bitwise the same wherever the plain call steps the tokens too (a step,
  * and verify / commit below 6 / 12 drafts), else equal up to fp32 rounding.
+ * Time for memory: the fused call needs no intermediate q, k, v or o, but
+ * from about 8 drafts (verify) and 16 (commit) the three calls are faster on
+ * MI355X, the plain call taking the chunk form there.
  * Alignment and limits as for kda_decode_verify.
  */
 typedef enum { KDA_DECODE_STEP = 0, KDA_DECODE_VERIFY = 1, KDA_DECODE_COMMIT = 2 } kda_decode_mode;
