@@ -369,13 +369,15 @@ kda_status kda_epilogue(const void* o, kda_dtype o_dtype, const void* g, kda_dty
  *   state              [B, H, Dk, Dv] fp32
  *   out                output gate: g [B, N, H, Dv] x_dtype, w [Dv], eps
  *   y                  [B, N, H, Dv] y_dtype (not for commit)
- * The fused calls always step the tokens: with the standalone kda_prologue
- * before and kda_epilogue after the plain call (its o in fp32), the results
- * are bitwise the same wherever the plain call steps the tokens too (a step,
- * and verify / commit below 6 / 12 drafts), else equal up to fp32 rounding.
+ * The fused verify takes the plain verify's form (the token loop below 6
+ * drafts, the chunk form from there on); the fused step and commit step the
+ * tokens.  With the standalone kda_prologue before and kda_epilogue after the
+ * plain call (its o in fp32), step and verify results are bitwise the same,
+ * and commit's too below 12 drafts (the plain commit's chunk form from there
+ * on), else equal up to fp32 rounding.
  * Time for memory: the fused call needs no intermediate q, k, v or o, but
- * from about 8 drafts (verify) and 16 (commit) the three calls are faster on
- * MI355X, the plain call taking the chunk form there.
+ * from about 6 drafts (verify) and 12 (commit) the three calls are faster on
+ * MI355X.
  * Alignment and limits as for kda_decode_verify.
  */
 typedef enum { KDA_DECODE_STEP = 0, KDA_DECODE_VERIFY = 1, KDA_DECODE_COMMIT = 2 } kda_decode_mode;

@@ -655,12 +655,20 @@ __device__ __forceinline__ void st_elems(T* p, const float (&x)[E]) {
 // gives both), SPEC_COMMIT.
 enum SpecForm { SPEC_VERIFY = 0, SPEC_VERIFY8 = 1, SPEC_COMMIT = 2 };
 
-template <int DK, int DV, typename TIn, typename TOut, int KIND, int FORM,
+// LAYER (verify only): the fused layer's verify in the chunk form -- q, k, v
+// from the projections' outputs through the prologue rows (conv state, taps
+// and raw rows staged in the dynamic LDS, as the token loop's layer mode does),
+// o through the epilogue rows into y; with the standalone prologue and
+// epilogue around the plain call the results are bitwise the same.  The
+// staging leaves room for two workgroups per CU, so this form takes the
+// registers of two waves per SIMD.
+template <int DK, int DV, typename TIn, typename TOut, int KIND, int FORM, bool LAYER = false,
           bool COMMIT = FORM == SPEC_COMMIT, bool STACK = FORM == SPEC_VERIFY8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || sizeof(TIn) == 4 ? 3 : 4))) void spec_chunk_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER ? 2 : COMMIT || sizeof(TIn) == 4 ? 3 : 4))) void spec_chunk_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v, Gate gate,
     const float* __restrict__ beta, float* __restrict__ state, TOut* __restrict__ o,
-    const int32_t* __restrict__ n_accept, int N, int H) {
+    const int32_t* __restrict__ n_accept, int N, int H, LayerIO io) {
+  static_assert(!(LAYER && COMMIT), "the layer's commit steps the tokens");
   using G = SpecGeo<DK, DV, COMMIT>;
   constexpr int CW = G::CW, E = G::E, KS = G::KS, ld = G::ld, ldT = G::ldT, ldKt = G::ldKt;
   __shared__ __align__(16) float sm[G::total];
@@ -682,6 +690,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || s
   const int tr = lane & 15, g = lane >> 4;
   const int col0 = w * CW + E * tr;  // this lane's first value column
 
+  // the layer's staging (dynamic LDS): raw rows [3 + N][2 Dk + Dv] (the conv
+  // state's three rows, then the tokens'; after the prologue, copies of the
+  // tokens' k [n][Dk] and q [n][Dk] for the exact path, and then o [n][Dv]
+  // for the epilogue) and the head's taps [2 Dk + Dv][4]; the prologue's v
+  // rows [n][Dv] pass through the partial sums' space
+  constexpr int SW = 2 * DK + DV, CPLV = DV / 64;
+  static_assert(16 * DV <= 4 * 2 * 256, "v rows in the partial sums' space");
+  extern __shared__ __align__(16) float dyn[];
+  float* xr = dyn;
+  float* tp = xr + (3 + N) * SW;
+  float* sV = part;
+  if constexpr (LAYER) {
+    for (int idx = tid; idx < SW; idx += 256) {
+      const int ten = idx < DK ? 0 : idx < 2 * DK ? 1 : 2;
+      const int ch = idx - (ten == 0 ? 0 : ten == 1 ? DK : 2 * DK);
+      const int D = ten == 2 ? DV : DK;
+      *reinterpret_cast<floatx4*>(tp + 4 * idx) =
+          *reinterpret_cast<const floatx4*>(io.conv.w[ten] + ((size_t)h * D + ch) * 4);
+    }
+    const float* cs = io.conv_state + ((size_t)sb * 3 * H + h) * SW;
+    for (int idx = tid; idx < 3 * (SW / 4); idx += 256) {
+      const int j = idx / (SW / 4), c = 4 * (idx % (SW / 4));
+      *reinterpret_cast<floatx4*>(xr + j * SW + c) =
+          *reinterpret_cast<const floatx4*>(cs + (size_t)j * H * SW + c);
+    }
+    for (int idx = tid; idx < n * (SW / 4); idx += 256) {
+      const int t = idx / (SW / 4), c = 4 * (idx % (SW / 4));
+      const size_t row = ((size_t)sb * N + t) * H + h;
+      floatx4 x4;
+      if (c < DK) x4 = ld4<TIn>((const TIn*)io.xq + row * DK + c);
+      else if (c < 2 * DK) x4 = ld4<TIn>((const TIn*)io.xk + row * DK + c - DK);
+      else x4 = ld4<TIn>((const TIn*)io.xv + row * DV + c - 2 * DK);
+      *reinterpret_cast<floatx4*>(xr + (3 + t) * SW + c) = x4;
+    }
+  }
+
   // The tokens' inputs are issued first and the state tile after them: loads
   // complete in order, so the token work below waits only for its own loads
   // while the state is still arriving.  Rows n..15 are alpha = 1, k = q = 0,
@@ -694,9 +738,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || s
     const bool ok = t < n;
     const size_t row = ((size_t)sb * N + (ok ? t : 0)) * H + h;
     ga[it] = gate_load4<KIND>(gate, ok, row, DK, c);
-    k4[it] = ok ? ld4<TIn>(k + row * DK + c) : floatx4{0.f, 0.f, 0.f, 0.f};
-    q4[it] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (!COMMIT) q4[it] = ok ? ld4<TIn>(q + row * DK + c) : q4[it];
+    k4[it] = floatx4{0.f, 0.f, 0.f, 0.f};
+    q4[it] = k4[it];
+    if constexpr (!LAYER) {  // (the layer's k and q come from the prologue rows)
+      k4[it] = ok ? ld4<TIn>(k + row * DK + c) : k4[it];
+      if constexpr (!COMMIT) q4[it] = ok ? ld4<TIn>(q + row * DK + c) : q4[it];
+    }
   }
   const float bt = tid < n ? beta[((size_t)sb * N + tid) * H + h] : 0.f;
   float vv[4][E];  // v of rows 4g + i at this lane's columns
@@ -705,7 +752,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || s
     const int t = 4 * g + i;
 #pragma unroll
     for (int e = 0; e < E; ++e) vv[i][e] = 0.f;
-    if (t < n) ld_elems<TIn, E>(v + (((size_t)sb * N + t) * H + h) * DV + col0, vv[i]);
+    if (!LAYER && t < n) ld_elems<TIn, E>(v + (((size_t)sb * N + t) * H + h) * DV + col0, vv[i]);
   }
   // the state tile: k-step s holds row 4s + g
   float* S = state + (size_t)tile * DK * DV;
@@ -731,6 +778,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || s
   }
   if (tid < 16) sB[tid] = bt;
   __syncthreads();
+  if constexpr (LAYER) {
+    // prologue rows into the token arrays, one wave per (token, tensor)
+    for (int r = w; r < 3 * n; r += 4) {
+      const int t = r / 3, ten = r - 3 * (r / 3);
+      if (ten == 0)
+        layer_row<TIn, DK / 64, true, 1, 1>(xr, tp, io.conv.eps, t, 0, SW, lane, sQ + t * ld,
+                                           nullptr, nullptr);
+      else if (ten == 1)
+        layer_row<TIn, DK / 64, true, 1, 1>(xr, tp + 4 * DK, io.conv.eps, t, DK, SW, lane,
+                                           sK + t * ld, nullptr, nullptr);
+      else
+        layer_row<TIn, DV / 64, false, 1, 1>(xr, tp + 8 * DK, io.conv.eps, t, 2 * DK, SW, lane,
+                                            sV + t * DV, nullptr, nullptr);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * g + i;
+#pragma unroll
+      for (int e = 0; e < E; ++e) vv[i][e] = t < n ? sV[t * DV + col0 + e] : 0.f;
+    }
+  }
 
   // per key channel: Gamma_t by a running product; Gamma*k, k / Gamma (and
   // Gamma*q) in place; commit: Ktil by a suffix product (no division), and
@@ -768,6 +837,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || s
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int t = t0 + u;
+        if (LAYER && t < n) {  // the prologue's k and q, kept for the exact path
+          xr[t * DK + c] = kc[u];
+          xr[(n + t) * DK + c] = qc[u];
+        }
         gm *= al[u];
         sK[t * ld + c] = gm * kc[u];
         // k / Gamma: read only while every channel stays in the factored range
@@ -801,6 +874,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || s
     float a = 0.f, m = 0.f;
     if (j <= t && t < n) {
       const size_t rt = ((size_t)sb * N + t) * H + h, rj = ((size_t)sb * N + j) * H + h;
+#pragma unroll 1
       for (int c = 0; c < DK; c += 4) {
         floatx4 r = {1.f, 1.f, 1.f, 1.f};
         for (int u = j + 1; u <= t; ++u) {
@@ -808,9 +882,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || s
 #pragma unroll
           for (int e = 0; e < 4; ++e) r[e] = r[e] * a4[e];
         }
-        const floatx4 kt = ld4<TIn>(k + rt * DK + c), kj = ld4<TIn>(k + rj * DK + c);
-        floatx4 qt = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (!COMMIT) qt = ld4<TIn>(q + rt * DK + c);
+        floatx4 kt, kj, qt = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (LAYER) {
+          kt = *reinterpret_cast<const floatx4*>(xr + t * DK + c);
+          kj = *reinterpret_cast<const floatx4*>(xr + j * DK + c);
+          qt = *reinterpret_cast<const floatx4*>(xr + (n + t) * DK + c);
+        } else {
+          kt = ld4<TIn>(k + rt * DK + c);
+          kj = ld4<TIn>(k + rj * DK + c);
+          if constexpr (!COMMIT) qt = ld4<TIn>(q + rt * DK + c);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float kr = kj[e] * r[e];
@@ -926,8 +1007,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || s
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = STACK ? 4 * (g - 2) + i : 4 * g + i;
-      if ((!STACK || g >= 2) && t < n)
-        st_elems<TOut, E>(o + (((size_t)sb * N + t) * H + h) * DV + col0, ov[i]);
+      if ((!STACK || g >= 2) && t < n) {
+        if constexpr (LAYER) {  // to the epilogue, through LDS (the raw rows are consumed)
+#pragma unroll
+          for (int e = 0; e < E; ++e) xr[t * DV + col0 + e] = ov[i][e];
+        } else {
+          st_elems<TOut, E>(o + (((size_t)sb * N + t) * H + h) * DV + col0, ov[i]);
+        }
+      }
+    }
+    if constexpr (LAYER) {
+      // epilogue rows, one wave per token (t = w + 4 r): y = RMSNorm(o) w Sigmoid(g)
+      float wn[CPLV], gv[4][CPLV];
+      ld_elems<float, CPLV>(io.out.w + CPLV * lane, wn);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = w + 4 * r;
+        if (t < n) ld_elems<TIn, CPLV>((const TIn*)io.out.g + (((size_t)sb * N + t) * H + h) * DV + CPLV * lane, gv[r]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = w + 4 * r;
+        if (t < n) {
+          float ovr[CPLV], y[CPLV];
+#pragma unroll
+          for (int c = 0; c < CPLV; ++c) ovr[c] = xr[t * DV + CPLV * lane + c];
+          epilogue_row<CPLV>(ovr, gv[r], wn, io.out.eps, y);
+          row_store<TOut, CPLV>(o + (((size_t)sb * N + t) * H + h) * DV, lane, y);
+        }
+      }
     }
   } else {
     // S' = Diag(Gamma_n) S + Ktil^T P: row tile rt of the permuted Ktil^T gives
@@ -962,8 +1071,8 @@ constexpr int multi_lds_bytes(int N, bool layer = false) {
 // the largest LDS a mode's instantiation may ask for (N up to kMaxDraft),
 // granted once per instantiation before its first launch
 template <typename K>
-static hipError_t allow_lds(K kern, int bytes, bool& done) {
-  if (done || bytes <= 65536) return hipSuccess;
+static hipError_t allow_lds(K kern, int bytes, bool& done, int below = 65536) {
+  if (done || bytes <= below) return hipSuccess;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      bytes);
   if (e == hipSuccess) done = true;
@@ -971,7 +1080,8 @@ static hipError_t allow_lds(K kern, int bytes, bool& done) {
 }
 
 // Verify and commit of at least this many draft tokens run as one chunk
-// (spec_chunk_kernel); fewer, and the layer's fused calls, step the tokens.
+// (spec_chunk_kernel), the fused layer's verify too; fewer, and the layer's
+// commit, step the tokens.
 // The token loop's cost grows with N and the chunk form's hardly does; on
 // MI355X at 64 sessions x 96 heads x 128 x 128 they cross near 5 tokens for
 // verify (stacked form, 6: 115 against about 120 us; 8: 115 against 147 us)
@@ -979,21 +1089,40 @@ static hipError_t allow_lds(K kern, int bytes, bool& done) {
 constexpr int kSpecVerifyChunkMin = 6;
 constexpr int kSpecCommitChunkMin = 12;
 
-template <int DK, int DV, typename TIn, typename TOut, int KIND>
+// the layer's verify: raw rows [3 + N][2 Dk + Dv] and taps [2 Dk + Dv][4]
+template <int DK, int DV>
+constexpr int spec_layer_lds_bytes(int N) {
+  return (int)sizeof(float) * (N + 7) * (2 * DK + DV);
+}
+
+template <int DK, int DV, typename TIn, typename TOut, int KIND, bool LAYER>
 static hipError_t launch_spec_chunk(const DecodeArgs& a) {
   const dim3 grid(a.B * a.H);
+  const int lds = LAYER ? spec_layer_lds_bytes<DK, DV>(a.N) : 0;
+  if constexpr (LAYER) {  // static and dynamic LDS together pass 64 KiB
+    static bool d8 = false, d16 = false;  // per instantiation; idempotent if raced
+    const int mx = spec_layer_lds_bytes<DK, DV>(kMaxDraft);
+    hipError_t e =
+        a.N <= 8 ? allow_lds(spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY8, true>, mx, d8, 0)
+                 : allow_lds(spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY, true>, mx, d16, 0);
+    if (e != hipSuccess) return e;
+  }
   if (a.mode == DECODE_VERIFY && a.N <= 8) {
-    hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY8>), grid, dim3(256), 0,
-                       (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                       a.gate, a.beta, a.state, (TOut*)a.o, (const int32_t*)nullptr, a.N, a.H);
+    hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY8, LAYER>), grid,
+                       dim3(256), lds, (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k,
+                       (const TIn*)a.v, a.gate, a.beta, a.state, (TOut*)a.o,
+                       (const int32_t*)nullptr, a.N, a.H, a.io);
   } else if (a.mode == DECODE_VERIFY) {
-    hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY>), grid, dim3(256), 0,
-                       (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v,
-                       a.gate, a.beta, a.state, (TOut*)a.o, (const int32_t*)nullptr, a.N, a.H);
-  } else {
+    hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY, LAYER>), grid,
+                       dim3(256), lds, (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k,
+                       (const TIn*)a.v, a.gate, a.beta, a.state, (TOut*)a.o,
+                       (const int32_t*)nullptr, a.N, a.H, a.io);
+  } else if constexpr (!LAYER) {
     hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, float, KIND, SPEC_COMMIT>), grid, dim3(256), 0,
                        (hipStream_t)a.stream, (const TIn*)nullptr, (const TIn*)a.k, (const TIn*)a.v,
-                       a.gate, a.beta, a.state, (float*)nullptr, a.n_accept, a.N, a.H);
+                       a.gate, a.beta, a.state, (float*)nullptr, a.n_accept, a.N, a.H, a.io);
+  } else {
+    return hipErrorInvalidValue;  // (the layer's commit steps the tokens)
   }
   return hipGetLastError();
 }
@@ -1001,11 +1130,10 @@ static hipError_t launch_spec_chunk(const DecodeArgs& a) {
 template <int DK, int DV, typename TIn, typename TOut, int KIND, bool LAYER>
 static hipError_t launch_decode_l(const DecodeArgs& a) {
   const dim3 grid(a.B * a.H);
-  if constexpr (!LAYER) {
-    if ((a.mode == DECODE_VERIFY && a.N >= kSpecVerifyChunkMin) ||
-        (a.mode == DECODE_COMMIT && a.N >= kSpecCommitChunkMin))
-      return launch_spec_chunk<DK, DV, TIn, TOut, KIND>(a);
-  }
+  if (a.mode == DECODE_VERIFY && a.N >= kSpecVerifyChunkMin)
+    return launch_spec_chunk<DK, DV, TIn, TOut, KIND, LAYER>(a);
+  if (!LAYER && a.mode == DECODE_COMMIT && a.N >= kSpecCommitChunkMin)
+    return launch_spec_chunk<DK, DV, TIn, TOut, KIND, LAYER>(a);
   static bool lds_v = false, lds_c = false;  // per instantiation; idempotent if raced
   if (a.mode == DECODE_VERIFY) {
     if (hipError_t e = allow_lds(decode_kernel<DK, DV, TIn, TOut, KIND, DECODE_VERIFY, LAYER>,

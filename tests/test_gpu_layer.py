@@ -172,11 +172,11 @@ def test_decode_layer_step_equals_composed(kind, dtype, Dk, Dv):
 
 @pytest.mark.parametrize("kind", ["alpha", "bounded", "scalar"])
 def test_decode_layer_spec_round_equals_composed(kind):
-    """Fused verify against the composed verify (within fp32 rounding: the fused
-    layer always steps the tokens, the plain calls take the chunk form from
-    six drafts on), conv state and state untouched.  Fused commit of seeded
-    prefixes: the state against the plain commit of the prologue's k, v,
-    likewise; the conv state exactly the oracle's after each prefix."""
+    """Fused verify bitwise the composed verify (both take the chunk form at six
+    drafts), conv state and state untouched.  Fused commit of seeded prefixes:
+    the state against the plain commit of the prologue's k, v (within fp32
+    rounding: the fused commit steps the tokens); the conv state exactly the
+    oracle's after each prefix."""
     d = dev()
     B, N, H, D = 4, 6, 3, 128
     L, gate, a_log, beta, s0 = _layer_case(B, N, H, D, D, 1220, kind, torch.bfloat16, d)
@@ -187,7 +187,7 @@ def test_decode_layer_spec_round_equals_composed(kind):
     o = kda.decode_verify(q, k, v, gate, beta, s0, gate=kind, a_log=a_log)
     y2 = kda.epilogue(o, L.g, L.norm_w, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    close(y, y2, TOL_F32, "steps")
+    assert torch.equal(y, y2)
     assert torch.equal(cs, L.conv_state) and torch.equal(st, s0)
     n_acc = torch.tensor([N, 0, 2, 5], dtype=torch.int32, device=d)
     kda.decode_layer("commit", L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, cs, gate, beta, st,
@@ -233,9 +233,10 @@ def test_decode_layer_steps_against_oracle():
 
 
 def test_decode_layer_max_draft():
-    """16 draft tokens (the largest LDS footprint of the fused layer): verify and
-    commit against the composed calls (within fp32 rounding: the plain calls
-    take the chunk form), the conv state bitwise."""
+    """16 draft tokens (the largest LDS footprint of the fused layer): verify
+    bitwise the composed calls, commit within fp32 rounding of them (the plain
+    commit takes the chunk form, the fused one steps the tokens), the conv
+    state bitwise."""
     d = dev()
     B, N, H, D = 2, 16, 2, 128
     L, gate, a_log, beta, s0 = _layer_case(B, N, H, D, D, 1260, "alpha", torch.bfloat16, d)
@@ -251,6 +252,41 @@ def test_decode_layer_max_draft():
     st2 = s0.clone()
     kda.decode_commit(k, v, gate, beta, n_acc, st2)
     torch.cuda.synchronize()
-    close(y, y2, TOL_F32, "steps")
+    assert torch.equal(y, y2)
     close(st, st2, TOL_F32, "state")
     assert torch.equal(cs, cso)
+
+
+@pytest.mark.parametrize("N", [4, 7, 12])
+@pytest.mark.parametrize("dtype,Dk,Dv", [(torch.bfloat16, 128, 128), (torch.float32, 64, 64),
+                                         (torch.bfloat16, 64, 128)])
+@pytest.mark.parametrize("decay", ["normal", "fast"])
+def test_decode_layer_verify_forms(N, dtype, Dk, Dv, decay):
+    """Fused verify in each form (4 drafts: the token loop; 7: the chunk form
+    with K and Q stacked; 12: the chunk form) bitwise the composed calls, and
+    against the oracle's prologue, recurrence and epilogue.  With -log alpha ~
+    N(6, 0.5^2) the decay over the drafts leaves the factored range, so the
+    chunk form's decay ratios come from running products of the prologue's k."""
+    d = dev()
+    B, H = 3, 2
+    seed = 1280 + N + Dk + (7 if decay == "fast" else 0)
+    L, gate, a_log, beta, s0 = _layer_case(B, N, H, Dk, Dv, seed, "alpha", dtype, d)
+    if decay == "fast":
+        z = torch.randn(gate.shape, generator=torch.Generator().manual_seed(seed))
+        gate = torch.exp(-(6.0 + 0.5 * z)).float().to(d)
+    cs, st = L.conv_state.clone(), s0.clone()
+    y = kda.decode_layer("verify", L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, cs, gate, beta, st, L.g,
+                         L.norm_w, out_dtype=torch.float32)
+    q, k, v, _ = kda.prologue(L.xq, L.xk, L.xv, L.wq, L.wk, L.wv, conv_state=L.conv_state)
+    y2 = kda.epilogue(kda.decode_verify(q, k, v, gate, beta, s0), L.g, L.norm_w,
+                      out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all()
+    assert torch.equal(y, y2)
+    assert torch.equal(cs, L.conv_state) and torch.equal(st, s0)
+    rq, rk, rv, _ = oracle.prologue(_f(L.xq), _f(L.xk), _f(L.xv), L.wq, L.wk, L.wv,
+                                    state=L.conv_state.cpu())
+    rq, rk, rv = (rounded(x, dtype) for x in (rq, rk, rv))
+    ro, _ = oracle.recurrent(rq, rk, rv, gate.cpu().double(), beta.cpu(), initial_state=s0.cpu())
+    ry = oracle.rmsnorm_gate(ro, _f(L.g), L.norm_w.cpu())
+    close(y, ry, TOL_BF16, "tokens")
