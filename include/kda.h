@@ -375,9 +375,9 @@ kda_status kda_epilogue(const void* o, kda_dtype o_dtype, const void* g, kda_dty
  * plain call (its o in fp32), step and verify results are bitwise the same,
  * and commit's too below 12 drafts (the plain commit's chunk form from there
  * on), else equal up to fp32 rounding.
- * Time for memory: the fused call needs no intermediate q, k, v or o, but
- * from about 6 drafts (verify) and 12 (commit) the three calls are faster on
- * MI355X.
+ * Time for memory: the fused call needs no intermediate q, k, v or o; on
+ * MI355X the fused verify is faster than the three calls at every draft
+ * count, the fused commit up to about 8 drafts.
  * Alignment and limits as for kda_decode_verify.
  */
 typedef enum { KDA_DECODE_STEP = 0, KDA_DECODE_VERIFY = 1, KDA_DECODE_COMMIT = 2 } kda_decode_mode;

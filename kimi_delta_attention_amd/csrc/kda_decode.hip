@@ -215,6 +215,71 @@ __device__ __forceinline__ void layer_row(const float* xr, const float* taps, fl
   }
 }
 
+// The fused layer's prologue rows of tokens t0 .. t0 + cnt - 1 (cnt <= 4) of
+// one tensor, straight from memory.  pro_load fetches the head's taps and the
+// cnt + 3 raw rows of the lane's channels (raw row r < 3 is conv-state row r,
+// fp32, row stride csr; row r >= 3 is token r - 3 of x, row stride xr);
+// pro_rows slides the conv window over them -- the arithmetic of layer_row --
+// and writes each row, rounded to the token dtype as the standalone prologue
+// stores it, to dst + t * ldd.  Split so that a wave issues the loads of all
+// its blocks ahead of its other loads.  The loads take no branches (a load
+// under a branch is waited for inside it): rows outside the tokens re-read a
+// token row in range and are not used, and where the block may be the first
+// (MAYBE_FIRST) the conv-state rows are read too and chosen when t0 = 0.
+template <int CPL>
+struct ProBlock {
+  float w[CPL][4], raw[7][CPL];
+};
+template <typename TIn, int CPL, bool MAYBE_FIRST, int CPLM>
+__device__ __forceinline__ void pro_load(ProBlock<CPLM>& b, const float* cs, const TIn* x,
+                                         size_t xr, int csr, const float* taps, int t0, int n,
+                                         int lane) {
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const floatx4 t4 = *reinterpret_cast<const floatx4*>(taps + (CPL * lane + c) * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b.w[c][j] = t4[j];
+  }
+#pragma unroll
+  for (int r = 0; r < 7; ++r) {
+    const int tk = max(0, min(t0 + r - 3, n - 1));
+    float x4[CPL];
+    row_load<TIn, CPL>(x + (size_t)tk * xr, lane, x4);
+    if (MAYBE_FIRST && r < 3) {
+      float c4[CPL];
+      row_load<float, CPL>(cs + (size_t)r * csr, lane, c4);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) x4[c] = t0 == 0 ? c4[c] : x4[c];
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) b.raw[r][c] = x4[c];
+  }
+}
+template <typename TIn, int CPL, bool NORM, int CPLM>
+__device__ __forceinline__ void pro_rows(const ProBlock<CPLM>& b, float eps, int t0, int cnt,
+                                         int lane, float* dst, int ldd) {
+  float w[CPL][4];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[c][j] = b.w[c][j];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < cnt) {
+      float hist[3][CPL], xc[CPL], y[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) hist[j][c] = b.raw[i + j][c];
+        xc[c] = b.raw[i + 3][c];
+      }
+      prologue_row<CPL, NORM>(hist, xc, w, eps, y);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) dst[(t0 + i) * ldd + CPL * lane + c] = (float)(TIn)y[c];
+    }
+  }
+}
+
 // One kernel for the three decode calls, by MODE:
 //   DECODE_STEP    one token (N = 1): output written, state written in place
 //   DECODE_VERIFY  tokens 0..N-1: outputs written, state untouched
@@ -656,15 +721,14 @@ __device__ __forceinline__ void st_elems(T* p, const float (&x)[E]) {
 enum SpecForm { SPEC_VERIFY = 0, SPEC_VERIFY8 = 1, SPEC_COMMIT = 2 };
 
 // LAYER (verify only): the fused layer's verify in the chunk form -- q, k, v
-// from the projections' outputs through the prologue rows (conv state, taps
-// and raw rows staged in the dynamic LDS, as the token loop's layer mode does),
-// o through the epilogue rows into y; with the standalone prologue and
-// epilogue around the plain call the results are bitwise the same.  The
-// staging leaves room for two workgroups per CU, so this form takes the
-// registers of two waves per SIMD.
+// from the projections' outputs through the prologue rows (each wave reads the
+// raw rows of its block of tokens straight from the conv state and the
+// projections), o through the epilogue rows into y; with the standalone
+// prologue and epilogue around the plain call the results are bitwise the
+// same.  For 2-byte tokens the LDS leaves room for three workgroups per CU.
 template <int DK, int DV, typename TIn, typename TOut, int KIND, int FORM, bool LAYER = false,
           bool COMMIT = FORM == SPEC_COMMIT, bool STACK = FORM == SPEC_VERIFY8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER ? 2 : COMMIT || sizeof(TIn) == 4 ? 3 : 4))) void spec_chunk_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || LAYER || sizeof(TIn) == 4 ? 3 : 4))) void spec_chunk_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v, Gate gate,
     const float* __restrict__ beta, float* __restrict__ state, TOut* __restrict__ o,
     const int32_t* __restrict__ n_accept, int N, int H, LayerIO io) {
@@ -690,41 +754,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER ? 2 :
   const int tr = lane & 15, g = lane >> 4;
   const int col0 = w * CW + E * tr;  // this lane's first value column
 
-  // the layer's staging (dynamic LDS): raw rows [3 + N][2 Dk + Dv] (the conv
-  // state's three rows, then the tokens'; after the prologue, copies of the
-  // tokens' k [n][Dk] and q [n][Dk] for the exact path, and then o [n][Dv]
-  // for the epilogue) and the head's taps [2 Dk + Dv][4]; the prologue's v
-  // rows [n][Dv] pass through the partial sums' space
-  constexpr int SW = 2 * DK + DV, CPLV = DV / 64;
-  static_assert(16 * DV <= 4 * 2 * 256, "v rows in the partial sums' space");
+  // the layer's dynamic LDS: the prologue's v rows [N][Dv] (then o [N][Dv] for
+  // the epilogue) and, for 4-byte tokens, the exact path's copies of the
+  // prologue's k and q [2][N][Dk]; 2-byte tokens keep those copies in the
+  // partial sums' space (free until the sums are written)
+  constexpr int SW = 2 * DK + DV, CPLK = DK / 64, CPLV = DV / 64;
+  static_assert(sizeof(TIn) == 4 || 2 * 16 * DK * sizeof(TIn) <= 4 * 2 * 256 * sizeof(float),
+                "k and q copies in the partial sums' space");
   extern __shared__ __align__(16) float dyn[];
-  float* xr = dyn;
-  float* tp = xr + (3 + N) * SW;
-  float* sV = part;
-  if constexpr (LAYER) {
-    for (int idx = tid; idx < SW; idx += 256) {
-      const int ten = idx < DK ? 0 : idx < 2 * DK ? 1 : 2;
-      const int ch = idx - (ten == 0 ? 0 : ten == 1 ? DK : 2 * DK);
-      const int D = ten == 2 ? DV : DK;
-      *reinterpret_cast<floatx4*>(tp + 4 * idx) =
-          *reinterpret_cast<const floatx4*>(io.conv.w[ten] + ((size_t)h * D + ch) * 4);
-    }
-    const float* cs = io.conv_state + ((size_t)sb * 3 * H + h) * SW;
-    for (int idx = tid; idx < 3 * (SW / 4); idx += 256) {
-      const int j = idx / (SW / 4), c = 4 * (idx % (SW / 4));
-      *reinterpret_cast<floatx4*>(xr + j * SW + c) =
-          *reinterpret_cast<const floatx4*>(cs + (size_t)j * H * SW + c);
-    }
-    for (int idx = tid; idx < n * (SW / 4); idx += 256) {
-      const int t = idx / (SW / 4), c = 4 * (idx % (SW / 4));
-      const size_t row = ((size_t)sb * N + t) * H + h;
-      floatx4 x4;
-      if (c < DK) x4 = ld4<TIn>((const TIn*)io.xq + row * DK + c);
-      else if (c < 2 * DK) x4 = ld4<TIn>((const TIn*)io.xk + row * DK + c - DK);
-      else x4 = ld4<TIn>((const TIn*)io.xv + row * DV + c - 2 * DK);
-      *reinterpret_cast<floatx4*>(xr + (3 + t) * SW + c) = x4;
-    }
-  }
+  float* sV = dyn;
+  TIn* cpy = sizeof(TIn) == 2 ? reinterpret_cast<TIn*>(part) : reinterpret_cast<TIn*>(dyn + N * DV);
 
   // The tokens' inputs are issued first and the state tile after them: loads
   // complete in order, so the token work below waits only for its own loads
@@ -754,45 +793,86 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER ? 2 :
     for (int e = 0; e < E; ++e) vv[i][e] = 0.f;
     if (!LAYER && t < n) ld_elems<TIn, E>(v + (((size_t)sb * N + t) * H + h) * DV + col0, vv[i]);
   }
+  // the layer's prologue: one wave per (block of 4 tokens, tensor), job
+  // jb = 3 block + tensor, at most three per wave (jobs w, w + 4, w + 8), so
+  // that the first blocks are jobs 0..2; their loads go out ahead of the
+  // state's (a wave's slot past the last job loads the rows of job 0 and
+  // computes nothing)
+  static_assert(kMaxDraft <= 16, "three prologue blocks per wave");
+  constexpr int CPLM = CPLK > CPLV ? CPLK : CPLV;
+  ProBlock<CPLM> pb[3];
+  const int nb = (n + 3) >> 2;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const float* cs = io.conv_state + ((size_t)sb * 3 * H + h) * SW;
+  const size_t xs = (size_t)sb * N * H + h;  // row of (token 0, head h)
+  if constexpr (LAYER) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int jb = wu + 4 * i < 3 * nb ? wu + 4 * i : 0;
+      const int ten = jb % 3, t0 = 4 * (jb / 3);
+      const TIn* x = (const TIn*)(ten == 0 ? io.xq : ten == 1 ? io.xk : io.xv);
+      const float* tp = ten == 0 ? io.conv.w[0] : ten == 1 ? io.conv.w[1] : io.conv.w[2];
+      if constexpr (DK == DV) {
+        if (i == 0)
+          pro_load<TIn, CPLK, true>(pb[i], cs + ten * DK, x + xs * DK, (size_t)H * DK, H * SW,
+                                    tp + (size_t)h * DK * 4, t0, n, lane);
+        else
+          pro_load<TIn, CPLK, false>(pb[i], cs, x + xs * DK, (size_t)H * DK, H * SW,
+                                     tp + (size_t)h * DK * 4, t0, n, lane);
+      } else if (ten == 2) {  // (Dk != Dv: the loads under the branch wait there)
+        pro_load<TIn, CPLV, true>(pb[i], cs + 2 * DK, x + xs * DV, (size_t)H * DV, H * SW,
+                                  tp + (size_t)h * DV * 4, t0, n, lane);
+      } else {
+        pro_load<TIn, CPLK, true>(pb[i], cs + ten * DK, x + xs * DK, (size_t)H * DK, H * SW,
+                                  tp + (size_t)h * DK * 4, t0, n, lane);
+      }
+    }
+  }
+  // alpha, and the zero rows of k and q, into the token arrays (the layer does
+  // this ahead of the state loads, which frees the gate's registers there)
+#define KDA_SPEC_STAGE()                                                                    \
+  {                                                                                         \
+    const float sc = KIND == GATE_BOUNDED ? expf(gate.a_log[h]) : 1.f;                      \
+    _Pragma("unroll") for (int it = 0; it < SIT; ++it) {                                    \
+      const int idx = tid + 256 * it, t = idx / (DK / 4), c = 4 * (idx % (DK / 4));        \
+      floatx4 a4 = ga[it];                                                                  \
+      if constexpr (KIND == GATE_LOG) {                                                     \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) a4[e] = expf(a4[e]);                  \
+      } else if constexpr (KIND == GATE_BOUNDED) {                                          \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) a4[e] =                               \
+            gate_bounded(a4[e], sc, gate.g_min);                                            \
+      }                                                                                     \
+      *reinterpret_cast<floatx4*>(sA + t * ld + c) = a4;                                    \
+      if (!LAYER || t >= n) { /* the layer's rows below n are the prologue's */             \
+        *reinterpret_cast<floatx4*>(sK + t * ld + c) = k4[it];                              \
+        if constexpr (!COMMIT) *reinterpret_cast<floatx4*>(sQ + t * ld + c) = q4[it];       \
+      }                                                                                     \
+    }                                                                                       \
+    if (tid < 16) sB[tid] = bt;                                                             \
+  }
+  if constexpr (LAYER) KDA_SPEC_STAGE()
   // the state tile: k-step s holds row 4s + g
   float* S = state + (size_t)tile * DK * DV;
   float sr[KS][E];
 #pragma unroll
   for (int s = 0; s < KS; ++s) SpecVec<E>::ld(S + (size_t)(4 * s + g) * DV + col0, sr[s]);
+  if constexpr (LAYER) {
+    // the prologue rows into the token arrays (rows n..15 stay zero)
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int jb = wu + 4 * i, ten = jb % 3, t0 = 4 * (jb / 3), cnt = min(4, n - t0);
+      if (jb >= 3 * nb) continue;
+      if (ten == 0) pro_rows<TIn, CPLK, true>(pb[i], io.conv.eps, t0, cnt, lane, sQ, ld);
+      else if (ten == 1) pro_rows<TIn, CPLK, true>(pb[i], io.conv.eps, t0, cnt, lane, sK, ld);
+      else pro_rows<TIn, CPLV, false>(pb[i], io.conv.eps, t0, cnt, lane, sV, DV);
+    }
+  }
 
   const float scl = KIND == GATE_BOUNDED ? expf(gate.a_log[h]) : 1.f;
-#pragma unroll
-  for (int it = 0; it < SIT; ++it) {
-    const int idx = tid + 256 * it, t = idx / (DK / 4), c = 4 * (idx % (DK / 4));
-    floatx4 a4 = ga[it];
-    if constexpr (KIND == GATE_LOG) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) a4[e] = expf(a4[e]);
-    } else if constexpr (KIND == GATE_BOUNDED) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) a4[e] = gate_bounded(a4[e], scl, gate.g_min);
-    }
-    *reinterpret_cast<floatx4*>(sA + t * ld + c) = a4;
-    *reinterpret_cast<floatx4*>(sK + t * ld + c) = k4[it];
-    if constexpr (!COMMIT) *reinterpret_cast<floatx4*>(sQ + t * ld + c) = q4[it];
-  }
-  if (tid < 16) sB[tid] = bt;
+  if constexpr (!LAYER) KDA_SPEC_STAGE()
+#undef KDA_SPEC_STAGE
   __syncthreads();
   if constexpr (LAYER) {
-    // prologue rows into the token arrays, one wave per (token, tensor)
-    for (int r = w; r < 3 * n; r += 4) {
-      const int t = r / 3, ten = r - 3 * (r / 3);
-      if (ten == 0)
-        layer_row<TIn, DK / 64, true, 1, 1>(xr, tp, io.conv.eps, t, 0, SW, lane, sQ + t * ld,
-                                           nullptr, nullptr);
-      else if (ten == 1)
-        layer_row<TIn, DK / 64, true, 1, 1>(xr, tp + 4 * DK, io.conv.eps, t, DK, SW, lane,
-                                           sK + t * ld, nullptr, nullptr);
-      else
-        layer_row<TIn, DV / 64, false, 1, 1>(xr, tp + 8 * DK, io.conv.eps, t, 2 * DK, SW, lane,
-                                            sV + t * DV, nullptr, nullptr);
-    }
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 4 * g + i;
@@ -837,9 +917,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER ? 2 :
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int t = t0 + u;
-        if (LAYER && t < n) {  // the prologue's k and q, kept for the exact path
-          xr[t * DK + c] = kc[u];
-          xr[(n + t) * DK + c] = qc[u];
+        if (LAYER && t < n) {  // the prologue's k and q (token-dtype values), for the exact path
+          cpy[t * DK + c] = (TIn)kc[u];
+          cpy[(n + t) * DK + c] = (TIn)qc[u];
         }
         gm *= al[u];
         sK[t * ld + c] = gm * kc[u];
@@ -884,9 +964,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER ? 2 :
         }
         floatx4 kt, kj, qt = {0.f, 0.f, 0.f, 0.f};
         if constexpr (LAYER) {
-          kt = *reinterpret_cast<const floatx4*>(xr + t * DK + c);
-          kj = *reinterpret_cast<const floatx4*>(xr + j * DK + c);
-          qt = *reinterpret_cast<const floatx4*>(xr + (n + t) * DK + c);
+          kt = ld4<TIn>(cpy + t * DK + c);
+          kj = ld4<TIn>(cpy + j * DK + c);
+          qt = ld4<TIn>(cpy + (n + t) * DK + c);
         } else {
           kt = ld4<TIn>(k + rt * DK + c);
           kj = ld4<TIn>(k + rj * DK + c);
@@ -900,6 +980,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER ? 2 :
         }
       }
     }
+    if constexpr (LAYER) __syncthreads();  // (the copies may sit in the sums' space)
     // (t, j) sits at lane 16 (t / 4) + j, entry t % 4 of the accumulator layout
     const int pos = 4 * (16 * (t >> 2) + j) + (t & 3);
     part[pos] = a;
@@ -964,6 +1045,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER ? 2 :
     aM = row();
   }
 
+  // the epilogue's weight and gate logits (tokens w + 4 r), ahead of the products
+  float wn[CPLV], gv[4][CPLV];
+  if constexpr (LAYER) {
+    ld_elems<float, CPLV>(io.out.w + CPLV * lane, wn);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = w + 4 * r;
+      if (t < n)
+        ld_elems<TIn, CPLV>((const TIn*)io.out.g + (((size_t)sb * N + t) * H + h) * DV + CPLV * lane,
+                            gv[r]);
+    }
+  }
+
   // ---- (Gamma*K) S and (Gamma*Q) S on this wave's columns
   floatx4 R[E], Y[E];
 #pragma unroll
@@ -1008,9 +1102,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER ? 2 :
     for (int i = 0; i < 4; ++i) {
       const int t = STACK ? 4 * (g - 2) + i : 4 * g + i;
       if ((!STACK || g >= 2) && t < n) {
-        if constexpr (LAYER) {  // to the epilogue, through LDS (the raw rows are consumed)
+        if constexpr (LAYER) {  // to the epilogue, through LDS (the v rows are consumed)
 #pragma unroll
-          for (int e = 0; e < E; ++e) xr[t * DV + col0 + e] = ov[i][e];
+          for (int e = 0; e < E; ++e) sV[t * DV + col0 + e] = ov[i][e];
         } else {
           st_elems<TOut, E>(o + (((size_t)sb * N + t) * H + h) * DV + col0, ov[i]);
         }
@@ -1018,13 +1112,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER ? 2 :
     }
     if constexpr (LAYER) {
       // epilogue rows, one wave per token (t = w + 4 r): y = RMSNorm(o) w Sigmoid(g)
-      float wn[CPLV], gv[4][CPLV];
-      ld_elems<float, CPLV>(io.out.w + CPLV * lane, wn);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = w + 4 * r;
-        if (t < n) ld_elems<TIn, CPLV>((const TIn*)io.out.g + (((size_t)sb * N + t) * H + h) * DV + CPLV * lane, gv[r]);
-      }
       __syncthreads();
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1032,7 +1119,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER ? 2 :
         if (t < n) {
           float ovr[CPLV], y[CPLV];
 #pragma unroll
-          for (int c = 0; c < CPLV; ++c) ovr[c] = xr[t * DV + CPLV * lane + c];
+          for (int c = 0; c < CPLV; ++c) ovr[c] = sV[t * DV + CPLV * lane + c];
           epilogue_row<CPLV>(ovr, gv[r], wn, io.out.eps, y);
           row_store<TOut, CPLV>(o + (((size_t)sb * N + t) * H + h) * DV, lane, y);
         }
@@ -1089,19 +1176,20 @@ static hipError_t allow_lds(K kern, int bytes, bool& done, int below = 65536) {
 constexpr int kSpecVerifyChunkMin = 6;
 constexpr int kSpecCommitChunkMin = 12;
 
-// the layer's verify: raw rows [3 + N][2 Dk + Dv] and taps [2 Dk + Dv][4]
-template <int DK, int DV>
+// the layer's verify: v (then o) rows [N][Dv]; for 4-byte tokens also the
+// copies of k and q [2][N][Dk]
+template <int DK, int DV, typename TIn>
 constexpr int spec_layer_lds_bytes(int N) {
-  return (int)sizeof(float) * (N + 7) * (2 * DK + DV);
+  return (int)sizeof(float) * N * (DV + (sizeof(TIn) == 4 ? 2 * DK : 0));
 }
 
 template <int DK, int DV, typename TIn, typename TOut, int KIND, bool LAYER>
 static hipError_t launch_spec_chunk(const DecodeArgs& a) {
   const dim3 grid(a.B * a.H);
-  const int lds = LAYER ? spec_layer_lds_bytes<DK, DV>(a.N) : 0;
+  const int lds = LAYER ? spec_layer_lds_bytes<DK, DV, TIn>(a.N) : 0;
   if constexpr (LAYER) {  // static and dynamic LDS together pass 64 KiB
     static bool d8 = false, d16 = false;  // per instantiation; idempotent if raced
-    const int mx = spec_layer_lds_bytes<DK, DV>(kMaxDraft);
+    const int mx = spec_layer_lds_bytes<DK, DV, TIn>(kMaxDraft);
     hipError_t e =
         a.N <= 8 ? allow_lds(spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY8, true>, mx, d8, 0)
                  : allow_lds(spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY, true>, mx, d16, 0);
