@@ -369,15 +369,12 @@ kda_status kda_epilogue(const void* o, kda_dtype o_dtype, const void* g, kda_dty
  *   state              [B, H, Dk, Dv] fp32
  *   out                output gate: g [B, N, H, Dv] x_dtype, w [Dv], eps
  *   y                  [B, N, H, Dv] y_dtype (not for commit)
- * The fused verify takes the plain verify's form (the token loop below 6
- * drafts, the chunk form from there on); the fused step and commit step the
- * tokens.  With the standalone kda_prologue before and kda_epilogue after the
- * plain call (its o in fp32), step and verify results are bitwise the same,
- * and commit's too below 12 drafts (the plain commit's chunk form from there
- * on), else equal up to fp32 rounding.
+ * The fused verify and commit take the plain calls' forms (the token loop
+ * below 6 / 12 drafts, the chunk form from there on): with the standalone
+ * kda_prologue before and kda_epilogue after the plain call (its o in fp32),
+ * the results are bitwise the same, conv state included.
  * Time for memory: the fused call needs no intermediate q, k, v or o; on
- * MI355X the fused verify is faster than the three calls at every draft
- * count, the fused commit up to about 8 drafts.
+ * MI355X it is faster than the three calls at every draft count.
  * Alignment and limits as for kda_decode_verify.
  */
 typedef enum { KDA_DECODE_STEP = 0, KDA_DECODE_VERIFY = 1, KDA_DECODE_COMMIT = 2 } kda_decode_mode;

@@ -720,19 +720,20 @@ __device__ __forceinline__ void st_elems(T* p, const float (&x)[E]) {
 // gives both), SPEC_COMMIT.
 enum SpecForm { SPEC_VERIFY = 0, SPEC_VERIFY8 = 1, SPEC_COMMIT = 2 };
 
-// LAYER (verify only): the fused layer's verify in the chunk form -- q, k, v
-// from the projections' outputs through the prologue rows (each wave reads the
-// raw rows of its block of tokens straight from the conv state and the
-// projections), o through the epilogue rows into y; with the standalone
+// LAYER: the fused layer's verify and commit in the chunk form -- q, k, v
+// (commit: k, v) from the projections' outputs through the prologue rows (each
+// wave reads the raw rows of its blocks of tokens straight from the conv state
+// and the projections); verify's o through the epilogue rows into y; commit
+// advances the conv state past the accepted tokens.  With the standalone
 // prologue and epilogue around the plain call the results are bitwise the
-// same.  For 2-byte tokens the LDS leaves room for three workgroups per CU.
+// same.  The LDS leaves room for three workgroups per CU with 2-byte tokens,
+// two with 4-byte ones (which then take the registers of two waves per SIMD).
 template <int DK, int DV, typename TIn, typename TOut, int KIND, int FORM, bool LAYER = false,
           bool COMMIT = FORM == SPEC_COMMIT, bool STACK = FORM == SPEC_VERIFY8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || LAYER || sizeof(TIn) == 4 ? 3 : 4))) void spec_chunk_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER && sizeof(TIn) == 4 ? 2 : COMMIT || LAYER || sizeof(TIn) == 4 ? 3 : 4))) void spec_chunk_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v, Gate gate,
     const float* __restrict__ beta, float* __restrict__ state, TOut* __restrict__ o,
     const int32_t* __restrict__ n_accept, int N, int H, LayerIO io) {
-  static_assert(!(LAYER && COMMIT), "the layer's commit steps the tokens");
   using G = SpecGeo<DK, DV, COMMIT>;
   constexpr int CW = G::CW, E = G::E, KS = G::KS, ld = G::ld, ldT = G::ldT, ldKt = G::ldKt;
   __shared__ __align__(16) float sm[G::total];
@@ -794,22 +795,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || L
     if (!LAYER && t < n) ld_elems<TIn, E>(v + (((size_t)sb * N + t) * H + h) * DV + col0, vv[i]);
   }
   // the layer's prologue: one wave per (block of 4 tokens, tensor), job
-  // jb = 3 block + tensor, at most three per wave (jobs w, w + 4, w + 8), so
-  // that the first blocks are jobs 0..2; their loads go out ahead of the
-  // state's (a wave's slot past the last job loads the rows of job 0 and
-  // computes nothing)
+  // jb = NT block + tensor over the NT tensors the call needs (commit: k and
+  // v), at most three per wave (jobs w, w + 4, w + 8), so that the first
+  // blocks are jobs 0..NT-1; their loads go out ahead of the state's (a wave's
+  // slot past the last job loads the rows of job 0 and computes nothing)
   static_assert(kMaxDraft <= 16, "three prologue blocks per wave");
-  constexpr int CPLM = CPLK > CPLV ? CPLK : CPLV;
+  constexpr int CPLM = CPLK > CPLV ? CPLK : CPLV, NT = COMMIT ? 2 : 3;
   ProBlock<CPLM> pb[3];
   const int nb = (n + 3) >> 2;
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  const float* cs = io.conv_state + ((size_t)sb * 3 * H + h) * SW;
+  float* cs = io.conv_state + ((size_t)sb * 3 * H + h) * SW;
   const size_t xs = (size_t)sb * N * H + h;  // row of (token 0, head h)
+  // commit: the conv state's new rows, raw rows n .. n + 2 of (its three rows,
+  // then the tokens'), read here and written once every wave is past its
+  // prologue rows (the reads of the old rows are then done); each source row
+  // is read from both places in range and chosen, without branches
+  constexpr int CIT = (3 * SW / 4 + 255) / 256;
+  floatx4 cn[CIT];
+  if constexpr (LAYER && COMMIT) {
+#pragma unroll
+    for (int it = 0; it < CIT; ++it) {
+      const int idx = min(tid + 256 * it, 3 * SW / 4 - 1);
+      const int j = idx / (SW / 4), c = 4 * (idx % (SW / 4)), r = n + j;
+      const int tk = max(r - 3, 0), ten = c < DK ? 0 : c < 2 * DK ? 1 : 2;
+      const int cc = c - (ten == 0 ? 0 : ten == 1 ? DK : 2 * DK), D = ten == 2 ? DV : DK;
+      const TIn* x = (const TIn*)(ten == 0 ? io.xq : ten == 1 ? io.xk : io.xv);
+      const floatx4 fx = ld4<TIn>(x + (xs + (size_t)tk * H) * D + cc);
+      const floatx4 fc = *reinterpret_cast<const floatx4*>(cs + (size_t)min(r, 2) * H * SW + c);
+      cn[it] = r < 3 ? fc : fx;
+    }
+  }
   if constexpr (LAYER) {
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      const int jb = wu + 4 * i < 3 * nb ? wu + 4 * i : 0;
-      const int ten = jb % 3, t0 = 4 * (jb / 3);
+      const int jb = wu + 4 * i < NT * nb ? wu + 4 * i : 0;
+      const int ten = (3 - NT) + jb % NT, t0 = 4 * (jb / NT);
       const TIn* x = (const TIn*)(ten == 0 ? io.xq : ten == 1 ? io.xk : io.xv);
       const float* tp = ten == 0 ? io.conv.w[0] : ten == 1 ? io.conv.w[1] : io.conv.w[2];
       if constexpr (DK == DV) {
@@ -860,8 +880,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || L
     // the prologue rows into the token arrays (rows n..15 stay zero)
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      const int jb = wu + 4 * i, ten = jb % 3, t0 = 4 * (jb / 3), cnt = min(4, n - t0);
-      if (jb >= 3 * nb) continue;
+      const int jb = wu + 4 * i, ten = (3 - NT) + jb % NT, t0 = 4 * (jb / NT);
+      const int cnt = min(4, n - t0);
+      if (jb >= NT * nb) continue;
       if (ten == 0) pro_rows<TIn, CPLK, true>(pb[i], io.conv.eps, t0, cnt, lane, sQ, ld);
       else if (ten == 1) pro_rows<TIn, CPLK, true>(pb[i], io.conv.eps, t0, cnt, lane, sK, ld);
       else pro_rows<TIn, CPLV, false>(pb[i], io.conv.eps, t0, cnt, lane, sV, DV);
@@ -878,6 +899,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || L
       const int t = 4 * g + i;
 #pragma unroll
       for (int e = 0; e < E; ++e) vv[i][e] = t < n ? sV[t * DV + col0 + e] : 0.f;
+    }
+    if constexpr (COMMIT) {  // the conv state advances past the n tokens
+#pragma unroll
+      for (int it = 0; it < CIT; ++it) {
+        const int idx = tid + 256 * it;
+        if (idx < 3 * SW / 4)
+          *reinterpret_cast<floatx4*>(cs + (size_t)(idx / (SW / 4)) * H * SW + 4 * (idx % (SW / 4))) =
+              cn[it];
+      }
     }
   }
 
@@ -919,7 +949,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || L
         const int t = t0 + u;
         if (LAYER && t < n) {  // the prologue's k and q (token-dtype values), for the exact path
           cpy[t * DK + c] = (TIn)kc[u];
-          cpy[(n + t) * DK + c] = (TIn)qc[u];
+          if constexpr (!COMMIT) cpy[(n + t) * DK + c] = (TIn)qc[u];
         }
         gm *= al[u];
         sK[t * ld + c] = gm * kc[u];
@@ -966,7 +996,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(COMMIT || L
         if constexpr (LAYER) {
           kt = ld4<TIn>(cpy + t * DK + c);
           kj = ld4<TIn>(cpy + j * DK + c);
-          qt = ld4<TIn>(cpy + (n + t) * DK + c);
+          if constexpr (!COMMIT) qt = ld4<TIn>(cpy + (n + t) * DK + c);
         } else {
           kt = ld4<TIn>(k + rt * DK + c);
           kj = ld4<TIn>(k + rj * DK + c);
@@ -1167,8 +1197,7 @@ static hipError_t allow_lds(K kern, int bytes, bool& done, int below = 65536) {
 }
 
 // Verify and commit of at least this many draft tokens run as one chunk
-// (spec_chunk_kernel), the fused layer's verify too; fewer, and the layer's
-// commit, step the tokens.
+// (spec_chunk_kernel), the fused layer's calls too; fewer step the tokens.
 // The token loop's cost grows with N and the chunk form's hardly does; on
 // MI355X at 64 sessions x 96 heads x 128 x 128 they cross near 5 tokens for
 // verify (stacked form, 6: 115 against about 120 us; 8: 115 against 147 us)
@@ -1176,7 +1205,7 @@ static hipError_t allow_lds(K kern, int bytes, bool& done, int below = 65536) {
 constexpr int kSpecVerifyChunkMin = 6;
 constexpr int kSpecCommitChunkMin = 12;
 
-// the layer's verify: v (then o) rows [N][Dv]; for 4-byte tokens also the
+// the layer's calls: v (then o) rows [N][Dv]; for 4-byte tokens also the
 // copies of k and q [2][N][Dk]
 template <int DK, int DV, typename TIn>
 constexpr int spec_layer_lds_bytes(int N) {
@@ -1186,31 +1215,38 @@ constexpr int spec_layer_lds_bytes(int N) {
 template <int DK, int DV, typename TIn, typename TOut, int KIND, bool LAYER>
 static hipError_t launch_spec_chunk(const DecodeArgs& a) {
   const dim3 grid(a.B * a.H);
+  // with the layer, static and dynamic LDS together pass 64 KiB: the larger
+  // size is granted once per instantiation (idempotent if raced)
   const int lds = LAYER ? spec_layer_lds_bytes<DK, DV, TIn>(a.N) : 0;
-  if constexpr (LAYER) {  // static and dynamic LDS together pass 64 KiB
-    static bool d8 = false, d16 = false;  // per instantiation; idempotent if raced
-    const int mx = spec_layer_lds_bytes<DK, DV, TIn>(kMaxDraft);
-    hipError_t e =
-        a.N <= 8 ? allow_lds(spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY8, true>, mx, d8, 0)
-                 : allow_lds(spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY, true>, mx, d16, 0);
-    if (e != hipSuccess) return e;
-  }
+  const int mx = LAYER ? spec_layer_lds_bytes<DK, DV, TIn>(kMaxDraft) : 0;
+  static bool lds8 = false, lds16 = false, ldsc = false;
   if (a.mode == DECODE_VERIFY && a.N <= 8) {
+    if (hipError_t e = allow_lds(spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY8, LAYER>,
+                                 mx, lds8, 0);
+        e != hipSuccess)
+      return e;
     hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY8, LAYER>), grid,
                        dim3(256), lds, (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k,
                        (const TIn*)a.v, a.gate, a.beta, a.state, (TOut*)a.o,
                        (const int32_t*)nullptr, a.N, a.H, a.io);
   } else if (a.mode == DECODE_VERIFY) {
+    if (hipError_t e = allow_lds(spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY, LAYER>,
+                                 mx, lds16, 0);
+        e != hipSuccess)
+      return e;
     hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, TOut, KIND, SPEC_VERIFY, LAYER>), grid,
                        dim3(256), lds, (hipStream_t)a.stream, (const TIn*)a.q, (const TIn*)a.k,
                        (const TIn*)a.v, a.gate, a.beta, a.state, (TOut*)a.o,
                        (const int32_t*)nullptr, a.N, a.H, a.io);
-  } else if constexpr (!LAYER) {
-    hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, float, KIND, SPEC_COMMIT>), grid, dim3(256), 0,
-                       (hipStream_t)a.stream, (const TIn*)nullptr, (const TIn*)a.k, (const TIn*)a.v,
-                       a.gate, a.beta, a.state, (float*)nullptr, a.n_accept, a.N, a.H, a.io);
   } else {
-    return hipErrorInvalidValue;  // (the layer's commit steps the tokens)
+    if (hipError_t e = allow_lds(spec_chunk_kernel<DK, DV, TIn, float, KIND, SPEC_COMMIT, LAYER>,
+                                 mx, ldsc, 0);
+        e != hipSuccess)
+      return e;
+    hipLaunchKernelGGL((spec_chunk_kernel<DK, DV, TIn, float, KIND, SPEC_COMMIT, LAYER>), grid,
+                       dim3(256), lds, (hipStream_t)a.stream, (const TIn*)nullptr,
+                       (const TIn*)a.k, (const TIn*)a.v, a.gate, a.beta, a.state,
+                       (float*)nullptr, a.n_accept, a.N, a.H, a.io);
   }
   return hipGetLastError();
 }
@@ -1220,7 +1256,7 @@ static hipError_t launch_decode_l(const DecodeArgs& a) {
   const dim3 grid(a.B * a.H);
   if (a.mode == DECODE_VERIFY && a.N >= kSpecVerifyChunkMin)
     return launch_spec_chunk<DK, DV, TIn, TOut, KIND, LAYER>(a);
-  if (!LAYER && a.mode == DECODE_COMMIT && a.N >= kSpecCommitChunkMin)
+  if (a.mode == DECODE_COMMIT && a.N >= kSpecCommitChunkMin)
     return launch_spec_chunk<DK, DV, TIn, TOut, KIND, LAYER>(a);
   static bool lds_v = false, lds_c = false;  // per instantiation; idempotent if raced
   if (a.mode == DECODE_VERIFY) {
