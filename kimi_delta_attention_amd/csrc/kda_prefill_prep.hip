@@ -336,35 +336,46 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
       }
     }
 
-    // prologue: the three inputs before the chunk (fp32)
-    constexpr int HPT = (3 * SWP + NTH_P - 1) / NTH_P;
-    float hpre[HPT];
+    // prologue: the three inputs before the chunk (fp32).  Each is read from
+    // both places without a branch (a load under a branch is waited for
+    // inside it, which held every item's start for five serial loads): the
+    // token row when it lies in the sequence (else the sequence's first row,
+    // not used) and the conv-state row through a buffer descriptor that reads
+    // zero where there is no conv state; the choice is made where they are
+    // stored, after the barrier below.
+    constexpr int HPT = (3 * SWP + NTH_P - 1) / NTH_P, TPT = (SWP + NTH_P - 1) / NTH_P;
+    bf16 hx[HPT];
+    float hs[HPT];
+    floatx4 tpv[TPT];
     if constexpr (PRO) {
+      const auto rs = rsrc(pa.st_in ? (const void*)(pa.st_in + (size_t)cur.seq * 3 * H * SWP)
+                                    : (const void*)q,
+                           pa.st_in ? 3LL * H * SWP * 4 : 0);
 #pragma unroll
       for (int i = 0; i < HPT; ++i) {
-        const int idx = tid_x + NTH_P * i;
-        hpre[i] = 0.f;
-        if (idx < 3 * SWP) {
-          const int j = idx / SWP, c = idx % SWP;
-          const int ten = c < DK ? 0 : c < 2 * DK ? 1 : 2;
-          const int cc = c - (ten == 0 ? 0 : ten == 1 ? DK : 2 * DK);
-          const int D = ten < 2 ? DK : DV;
-          const long long p = tok0 - 3 + j;
-          const bf16* xt = ten == 0 ? q : ten == 1 ? k : v;
-          if (p >= cur.start)
-            hpre[i] = (float)xt[((size_t)p * H + hd) * D + cc];
-          else if (pa.st_in)
-            hpre[i] = pa.st_in[(((size_t)cur.seq * 3 + (int)(p - cur.start + 3)) * H + hd) * SWP + c];
-        }
-      }
-      // the head's taps to LDS (their readers in the item before are behind
-      // its barriers): read as broadcasts, they cost no memory wait per group
-      for (int c = tid_x; c < SWP; c += NTH_P) {
+        const int idx = min(tid_x + NTH_P * i, 3 * SWP - 1);
+        const int j = idx / SWP, c = idx % SWP;
         const int ten = c < DK ? 0 : c < 2 * DK ? 1 : 2;
         const int cc = c - (ten == 0 ? 0 : ten == 1 ? DK : 2 * DK);
         const int D = ten < 2 ? DK : DV;
-        *reinterpret_cast<floatx4*>(TP + 4 * c) =
-            *reinterpret_cast<const floatx4*>(pa.conv.w[ten] + ((size_t)hd * D + cc) * 4);
+        const long long p = tok0 - 3 + j, pc = p >= cur.start ? p : cur.start;
+        const int jj = (int)(p - cur.start + 3) < 2 ? (int)(p - cur.start + 3) : 2;
+        const bf16* xt = ten == 0 ? q : ten == 1 ? k : v;
+        hx[i] = xt[((size_t)pc * H + hd) * D + cc];
+        hs[i] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rs, ((jj * H + hd) * SWP + c) * 4, 0, 0));
+      }
+      // the head's taps, to LDS with the rows below (read as broadcasts, they
+      // cost no memory wait per group); loaded like the inputs above, with
+      // the tensor's pointer chosen by selects rather than an indexed load
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        const int c = min(tid_x + NTH_P * i, SWP - 1);
+        const int ten = c < DK ? 0 : c < 2 * DK ? 1 : 2;
+        const int cc = c - (ten == 0 ? 0 : ten == 1 ? DK : 2 * DK);
+        const int D = ten < 2 ? DK : DV;
+        const float* wt = ten == 0 ? pa.conv.w[0] : ten == 1 ? pa.conv.w[1] : pa.conv.w[2];
+        tpv[i] = *reinterpret_cast<const floatx4*>(wt + ((size_t)hd * D + cc) * 4);
       }
     }
 
@@ -396,7 +407,12 @@ __global__ __launch_bounds__(NTH_P, 2) void prefill_prep_kernel(
 #pragma unroll
       for (int i = 0; i < HPT; ++i) {
         const int idx = tid_x + NTH_P * i;
-        if (idx < 3 * SWP) HI[idx] = hpre[i];
+        if (idx < 3 * SWP) HI[idx] = tok0 - 3 + idx / SWP >= cur.start ? (float)hx[i] : hs[i];
+      }
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        const int c = tid_x + NTH_P * i;
+        if (c < SWP) *reinterpret_cast<floatx4*>(TP + 4 * c) = tpv[i];
       }
       __syncthreads();
       const int row = lane_x;             // token of the chunk
