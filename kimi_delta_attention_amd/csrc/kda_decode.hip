@@ -343,53 +343,122 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
   float* tp = gs + N * DV;
   constexpr int CPLV = DV / 64;
   float wn[CPLV];  // RMSNorm weight of the lane's channels (layer epilogue)
+  const float sc = KIND == GATE_BOUNDED ? expf(gate.a_log[h]) : 1.f;
   if constexpr (LAYER) {
-    for (int idx = tid; idx < SW; idx += 256) {
+    // Every staging load is issued first, at clamped indices and without
+    // branches (a load under a branch or inside a loop is waited for there,
+    // which would put each group of them on the workgroup's chain), then the
+    // state's, then the stores.  Unrolled for up to MAXN tokens, the most this
+    // mode takes before the chunk form; loops take any beyond.
+    constexpr int MAXN = MODE == DECODE_STEP ? 1 : MODE == DECODE_VERIFY ? 5 : 11;
+    constexpr int TPT = (SW + 255) / 256, CRT = (3 * SW / 4 + 255) / 256;
+    constexpr int XRT = (MAXN * SW / 4 + 255) / 256, ALT = (MAXN * DK / 4 + 255) / 256;
+    constexpr int GST = VERIFY ? (MAXN * DV / 4 + 255) / 256 : 1;
+    const float* cs = io.conv_state + ((size_t)sb * 3 * H + h) * SW;
+    const size_t row0 = (size_t)sb * N * H + h;  // (token 0, head h)
+    auto tap_src = [&](int idx) {
       const int ten = idx < DK ? 0 : idx < 2 * DK ? 1 : 2;
-      const int ch = idx - (ten == 0 ? 0 : ten == 1 ? DK : 2 * DK);
-      const int D = ten == 2 ? DV : DK;
-      *reinterpret_cast<floatx4*>(tp + 4 * idx) =
-          *reinterpret_cast<const floatx4*>(io.conv.w[ten] + ((size_t)h * D + ch) * 4);
-    }
+      const int ch = idx - (ten == 0 ? 0 : ten == 1 ? DK : 2 * DK), D = ten == 2 ? DV : DK;
+      const float* wt = ten == 0 ? io.conv.w[0] : ten == 1 ? io.conv.w[1] : io.conv.w[2];
+      return wt + ((size_t)h * D + ch) * 4;
+    };
+    auto x_src = [&](int idx) {  // raw row item idx of the tokens: 4 values
+      const int t = idx / (SW / 4), c = 4 * (idx % (SW / 4));
+      const size_t row = row0 + (size_t)t * H;
+      return c < DK ? ld4<TIn>((const TIn*)io.xq + row * DK + c)
+                    : c < 2 * DK ? ld4<TIn>((const TIn*)io.xk + row * DK + c - DK)
+                                 : ld4<TIn>((const TIn*)io.xv + row * DV + c - 2 * DK);
+    };
+    floatx4 tv[TPT], cv[CRT], xv[XRT], gv[GST], av[ALT];
+#pragma unroll
+    for (int i = 0; i < TPT; ++i)
+      tv[i] = *reinterpret_cast<const floatx4*>(tap_src(min(tid + 256 * i, SW - 1)));
     if constexpr (VERIFY) {
 #pragma unroll
       for (int c = 0; c < CPLV; ++c) wn[c] = io.out.w[CPLV * lane + c];
     }
-    const float* cs = io.conv_state + ((size_t)sb * 3 * H + h) * SW;
-    for (int idx = tid; idx < 3 * (SW / 4); idx += 256) {
-      const int j = idx / (SW / 4), c = 4 * (idx % (SW / 4));
-      *reinterpret_cast<floatx4*>(xr + j * SW + c) =
-          *reinterpret_cast<const floatx4*>(cs + (size_t)j * H * SW + c);
+#pragma unroll
+    for (int i = 0; i < CRT; ++i) {
+      const int idx = min(tid + 256 * i, 3 * (SW / 4) - 1);
+      cv[i] = *reinterpret_cast<const floatx4*>(cs + (size_t)(idx / (SW / 4)) * H * SW +
+                                                4 * (idx % (SW / 4)));
     }
-    for (int idx = tid; idx < n * (SW / 4); idx += 256) {
-      const int t = idx / (SW / 4), c = 4 * (idx % (SW / 4));
-      const size_t row = ((size_t)sb * N + t) * H + h;
-      floatx4 x4;
-      if (c < DK) x4 = ld4<TIn>((const TIn*)io.xq + row * DK + c);
-      else if (c < 2 * DK) x4 = ld4<TIn>((const TIn*)io.xk + row * DK + c - DK);
-      else x4 = ld4<TIn>((const TIn*)io.xv + row * DV + c - 2 * DK);
-      *reinterpret_cast<floatx4*>(xr + (3 + t) * SW + c) = x4;
-    }
+#pragma unroll
+    for (int i = 0; i < XRT; ++i) xv[i] = x_src(min(tid + 256 * i, n * (SW / 4) - 1));
     if constexpr (VERIFY) {
-      for (int idx = tid; idx < n * (DV / 4); idx += 256) {
-        const int t = idx / (DV / 4), c = 4 * (idx % (DV / 4));
-        const size_t row = ((size_t)sb * N + t) * H + h;
-        *reinterpret_cast<floatx4*>(gs + t * DV + c) = ld4<TIn>((const TIn*)io.out.g + row * DV + c);
+#pragma unroll
+      for (int i = 0; i < GST; ++i) {
+        const int idx = min(tid + 256 * i, n * (DV / 4) - 1);
+        gv[i] = ld4<TIn>((const TIn*)io.out.g + (row0 + (size_t)(idx / (DV / 4)) * H) * DV +
+                         4 * (idx % (DV / 4)));
       }
     }
-  }
-
-  // stage the n tokens' inputs (alpha and the alpha-scaled vectors formed once)
-  const float sc = KIND == GATE_BOUNDED ? expf(gate.a_log[h]) : 1.f;
-  for (int idx = tid; idx < n * (DK / 4); idx += 256) {
-    const int t = idx / (DK / 4), c = 4 * (idx % (DK / 4));
-    const size_t row = ((size_t)sb * N + t) * H + h;
-    const floatx4 a4 = alpha4_exact<KIND>(gate, row, DK, c, sc);
-    float* rt = rec + t * R::stride;
-    if constexpr (LAYER) {  // k and q come from the prologue rows below
+#pragma unroll
+    for (int i = 0; i < ALT; ++i) {
+      const int idx = min(tid + 256 * i, n * (DK / 4) - 1);
+      av[i] = gate_load4<KIND>(gate, true, row0 + (size_t)(idx / (DK / 4)) * H, DK,
+                               4 * (idx % (DK / 4)));
+    }
+    const float btv = beta[row0 + (size_t)min(tid, n - 1) * H];
+    load_state();
+    // the stores (alpha formed as alpha4_exact forms it)
+    auto put_alpha = [&](int idx, floatx4 a4) {
+      const int t = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+      if constexpr (KIND == GATE_LOG) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a4[e] = expf(a4[e]);
+      } else if constexpr (KIND == GATE_BOUNDED) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a4[e] = gate_bounded(a4[e], sc, gate.g_min);
+      }
+      float* rt = rec + t * R::stride;
 #pragma unroll
       for (int e = 0; e < 4; ++e) rt[R::AL + ((c + e) % RPP) * NP + (c + e) / RPP] = a4[e];
-    } else {
+    };
+#pragma unroll
+    for (int i = 0; i < TPT; ++i)
+      if (tid + 256 * i < SW) *reinterpret_cast<floatx4*>(tp + 4 * (tid + 256 * i)) = tv[i];
+#pragma unroll
+    for (int i = 0; i < CRT; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx < 3 * (SW / 4))
+        *reinterpret_cast<floatx4*>(xr + (idx / (SW / 4)) * SW + 4 * (idx % (SW / 4))) = cv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < XRT; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx < n * (SW / 4))
+        *reinterpret_cast<floatx4*>(xr + (3 + idx / (SW / 4)) * SW + 4 * (idx % (SW / 4))) = xv[i];
+    }
+    for (int idx = tid + 256 * XRT; idx < n * (SW / 4); idx += 256)
+      *reinterpret_cast<floatx4*>(xr + (3 + idx / (SW / 4)) * SW + 4 * (idx % (SW / 4))) =
+          x_src(idx);
+    if constexpr (VERIFY) {
+#pragma unroll
+      for (int i = 0; i < GST; ++i) {
+        const int idx = tid + 256 * i;
+        if (idx < n * (DV / 4))
+          *reinterpret_cast<floatx4*>(gs + (idx / (DV / 4)) * DV + 4 * (idx % (DV / 4))) = gv[i];
+      }
+      for (int idx = tid + 256 * GST; idx < n * (DV / 4); idx += 256)
+        *reinterpret_cast<floatx4*>(gs + (idx / (DV / 4)) * DV + 4 * (idx % (DV / 4))) =
+            ld4<TIn>((const TIn*)io.out.g + (row0 + (size_t)(idx / (DV / 4)) * H) * DV +
+                     4 * (idx % (DV / 4)));
+    }
+#pragma unroll
+    for (int i = 0; i < ALT; ++i)
+      if (tid + 256 * i < n * (DK / 4)) put_alpha(tid + 256 * i, av[i]);
+    for (int idx = tid + 256 * ALT; idx < n * (DK / 4); idx += 256)
+      put_alpha(idx, gate_load4<KIND>(gate, true, row0 + (size_t)(idx / (DK / 4)) * H, DK,
+                                      4 * (idx % (DK / 4))));
+    if (tid < n) rec[tid * R::stride + R::Bt] = btv;
+  } else {
+    // stage the n tokens' inputs (alpha and the alpha-scaled vectors formed once)
+    for (int idx = tid; idx < n * (DK / 4); idx += 256) {
+      const int t = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+      const size_t row = ((size_t)sb * N + t) * H + h;
+      const floatx4 a4 = alpha4_exact<KIND>(gate, row, DK, c, sc);
+      float* rt = rec + t * R::stride;
       const floatx4 k4 = ld4<TIn>(k + row * DK + c);
       floatx4 q4 = {0.f, 0.f, 0.f, 0.f};
       if constexpr (VERIFY) q4 = ld4<TIn>(q + row * DK + c);
@@ -405,16 +474,13 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
         }
       }
     }
-  }
-  if constexpr (!LAYER) {
     for (int idx = tid; idx < n * (DV / 4); idx += 256) {
       const int t = idx / (DV / 4), c = 4 * (idx % (DV / 4));
       const size_t row = ((size_t)sb * N + t) * H + h;
       *reinterpret_cast<floatx4*>(rec + t * R::stride + R::V + c) = ld4<TIn>(v + row * DV + c);
     }
+    if (tid < n) rec[tid * R::stride + R::Bt] = beta[((size_t)sb * N + tid) * H + h];
   }
-  if (tid < n) rec[tid * R::stride + R::Bt] = beta[((size_t)sb * N + tid) * H + h];
-  if constexpr (LAYER) load_state();
   __syncthreads();
   if constexpr (LAYER) {
     // prologue rows into the records, one wave per (token, tensor); commit
