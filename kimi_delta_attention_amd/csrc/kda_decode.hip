@@ -328,12 +328,9 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
     for (int i = 0; i < NP; ++i)
       s[i] = *reinterpret_cast<const floatx4*>(S + (size_t)(ro + RPP * i) * DV + col);
   };
-  // the plain calls fetch the state first; the layer issues its (smaller)
-  // staging loads first, so that the prologue rows -- which wait for them,
-  // and with them for every load issued earlier -- run while the state is
-  // still arriving
-  if constexpr (!LAYER) load_state();
-
+  // The (smaller) staging loads are issued before the state's, so that the
+  // staging -- and the layer's prologue rows -- which wait for them, and with
+  // them for every load issued earlier, run while the state is still arriving.
   constexpr int SW = 2 * DK + DV;                  // conv-state row: q | k | v
   // LAYER: the raw rows [3 + n][SW] (conv state, then the tokens' projections),
   // the gate logits [n][Dv] and the head's conv taps [SW][4]; the raw rows'
@@ -453,15 +450,37 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
                                       4 * (idx % (DK / 4))));
     if (tid < n) rec[tid * R::stride + R::Bt] = btv;
   } else {
-    // stage the n tokens' inputs (alpha and the alpha-scaled vectors formed once)
-    for (int idx = tid; idx < n * (DK / 4); idx += 256) {
+    // stage the n tokens' inputs (alpha and the alpha-scaled vectors formed
+    // once): as above, every load first, then the state's, then the stores
+    constexpr int MAXN = MODE == DECODE_STEP ? 1 : MODE == DECODE_VERIFY ? 5 : 11;
+    constexpr int KT = (MAXN * DK / 4 + 255) / 256, VT = (MAXN * DV / 4 + 255) / 256;
+    floatx4 ka[KT], qa[KT], aa[KT], va[VT];
+#pragma unroll
+    for (int i = 0; i < KT; ++i) {
+      const int idx = min(tid + 256 * i, n * (DK / 4) - 1);
+      const size_t row = ((size_t)sb * N + idx / (DK / 4)) * H + h;
+      const int c = 4 * (idx % (DK / 4));
+      ka[i] = ld4<TIn>(k + row * DK + c);
+      if constexpr (VERIFY) qa[i] = ld4<TIn>(q + row * DK + c);
+      aa[i] = gate_load4<KIND>(gate, true, row, DK, c);
+    }
+#pragma unroll
+    for (int i = 0; i < VT; ++i) {
+      const int idx = min(tid + 256 * i, n * (DV / 4) - 1);
+      va[i] = ld4<TIn>(v + (((size_t)sb * N + idx / (DV / 4)) * H + h) * DV + 4 * (idx % (DV / 4)));
+    }
+    const float btv = beta[((size_t)sb * N + min(tid, n - 1)) * H + h];
+    load_state();
+    auto put_k = [&](int idx, floatx4 a4, const floatx4& k4, const floatx4& q4) {
       const int t = idx / (DK / 4), c = 4 * (idx % (DK / 4));
-      const size_t row = ((size_t)sb * N + t) * H + h;
-      const floatx4 a4 = alpha4_exact<KIND>(gate, row, DK, c, sc);
+      if constexpr (KIND == GATE_LOG) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a4[e] = expf(a4[e]);
+      } else if constexpr (KIND == GATE_BOUNDED) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a4[e] = gate_bounded(a4[e], sc, gate.g_min);
+      }
       float* rt = rec + t * R::stride;
-      const floatx4 k4 = ld4<TIn>(k + row * DK + c);
-      floatx4 q4 = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (VERIFY) q4 = ld4<TIn>(q + row * DK + c);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int pos = ((c + e) % RPP) * NP + (c + e) / RPP;
@@ -473,13 +492,29 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
           rt[R::AQ + pos] = a4[e] * q4[e];
         }
       }
+    };
+#pragma unroll
+    for (int i = 0; i < KT; ++i)
+      if (tid + 256 * i < n * (DK / 4)) put_k(tid + 256 * i, aa[i], ka[i], qa[i]);
+    for (int idx = tid + 256 * KT; idx < n * (DK / 4); idx += 256) {
+      const size_t row = ((size_t)sb * N + idx / (DK / 4)) * H + h;
+      const int c = 4 * (idx % (DK / 4));
+      floatx4 q4 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (VERIFY) q4 = ld4<TIn>(q + row * DK + c);
+      put_k(idx, gate_load4<KIND>(gate, true, row, DK, c), ld4<TIn>(k + row * DK + c), q4);
     }
-    for (int idx = tid; idx < n * (DV / 4); idx += 256) {
+#pragma unroll
+    for (int i = 0; i < VT; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx < n * (DV / 4))
+        *reinterpret_cast<floatx4*>(rec + (idx / (DV / 4)) * R::stride + R::V + 4 * (idx % (DV / 4))) = va[i];
+    }
+    for (int idx = tid + 256 * VT; idx < n * (DV / 4); idx += 256) {
       const int t = idx / (DV / 4), c = 4 * (idx % (DV / 4));
       const size_t row = ((size_t)sb * N + t) * H + h;
       *reinterpret_cast<floatx4*>(rec + t * R::stride + R::V + c) = ld4<TIn>(v + row * DV + c);
     }
-    if (tid < n) rec[tid * R::stride + R::Bt] = beta[((size_t)sb * N + tid) * H + h];
+    if (tid < n) rec[tid * R::stride + R::Bt] = btv;
   }
   __syncthreads();
   if constexpr (LAYER) {
