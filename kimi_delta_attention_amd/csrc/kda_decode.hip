@@ -57,6 +57,27 @@ __device__ __forceinline__ floatx4 ld4<bf16>(const bf16* p) {
                  __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u)};
 }
 
+// the same four elements as loaded (ld), widened to fp32 where they are used
+// (cvt): the wait for a load goes where its first use is, so the use of a
+// load that should not hold back the loads issued after it comes after them
+template <typename TIn>
+struct Raw4;
+template <>
+struct Raw4<float> {
+  typedef floatx4 T;
+  static __device__ __forceinline__ T ld(const float* p) { return *reinterpret_cast<const T*>(p); }
+  static __device__ __forceinline__ floatx4 cvt(const T& x) { return x; }
+};
+template <>
+struct Raw4<bf16> {
+  typedef u32x2 T;
+  static __device__ __forceinline__ T ld(const bf16* p) { return *reinterpret_cast<const T*>(p); }
+  static __device__ __forceinline__ floatx4 cvt(const T& x) {
+    return floatx4{__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u),
+                   __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u)};
+  }
+};
+
 // Lane geometry of a Dk x Dv tile on 4 waves: wave w owns CW value columns;
 // LPR lanes share a row set, a lane holds float4 columns of the NP rows
 // ro + RPP i.
@@ -873,6 +894,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER && si
   // beta = 0.
   constexpr int SIT = 16 * (DK / 4) / 256;  // staging items per thread
   floatx4 ga[SIT], k4[SIT], q4[SIT];
+  typename Raw4<TIn>::T kr[SIT], qr[SIT];  // k and q as loaded (widened after the state's loads)
 #pragma unroll
   for (int it = 0; it < SIT; ++it) {
     const int idx = tid + 256 * it, t = idx / (DK / 4), c = 4 * (idx % (DK / 4));
@@ -882,8 +904,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER && si
     k4[it] = floatx4{0.f, 0.f, 0.f, 0.f};
     q4[it] = k4[it];
     if constexpr (!LAYER) {  // (the layer's k and q come from the prologue rows)
-      k4[it] = ok ? ld4<TIn>(k + row * DK + c) : k4[it];
-      if constexpr (!COMMIT) q4[it] = ok ? ld4<TIn>(q + row * DK + c) : q4[it];
+      // loaded unconditionally (row 0 stands in past the drafts) and chosen
+      // where used: a load under a branch is waited for inside it
+      kr[it] = Raw4<TIn>::ld(k + row * DK + c);
+      if constexpr (!COMMIT) qr[it] = Raw4<TIn>::ld(q + row * DK + c);
     }
   }
   const float bt = tid < n ? beta[((size_t)sb * N + tid) * H + h] : 0.f;
@@ -893,7 +917,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER && si
     const int t = 4 * g + i;
 #pragma unroll
     for (int e = 0; e < E; ++e) vv[i][e] = 0.f;
-    if (!LAYER && t < n) ld_elems<TIn, E>(v + (((size_t)sb * N + t) * H + h) * DV + col0, vv[i]);
+    if constexpr (!LAYER) {
+      float vl[E];
+      ld_elems<TIn, E>(v + (((size_t)sb * N + (t < n ? t : 0)) * H + h) * DV + col0, vl);
+#pragma unroll
+      for (int e = 0; e < E; ++e) vv[i][e] = t < n ? vl[e] : 0.f;
+    }
   }
   // the layer's prologue: one wave per (block of 4 tokens, tensor), job
   // jb = NT block + tensor over the NT tensors the call needs (commit: k and
@@ -977,6 +1006,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER && si
   float sr[KS][E];
 #pragma unroll
   for (int s = 0; s < KS; ++s) SpecVec<E>::ld(S + (size_t)(4 * s + g) * DV + col0, sr[s]);
+  // (nothing below is moved above the state's loads)
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!LAYER) {
+#pragma unroll
+    for (int it = 0; it < SIT; ++it) {
+      const bool ok = (tid + 256 * it) / (DK / 4) < n;
+      k4[it] = ok ? Raw4<TIn>::cvt(kr[it]) : k4[it];
+      if constexpr (!COMMIT) q4[it] = ok ? Raw4<TIn>::cvt(qr[it]) : q4[it];
+    }
+  }
   if constexpr (LAYER) {
     // the prologue rows into the token arrays (rows n..15 stay zero)
 #pragma unroll
