@@ -57,21 +57,31 @@ __device__ __forceinline__ floatx4 ld4<bf16>(const bf16* p) {
                  __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u)};
 }
 
-// the same four elements as loaded (ld), widened to fp32 where they are used
+// the same four elements as loaded (ld; gld through a pointer whose address
+// space the compiler cannot see), widened to fp32 where they are used
 // (cvt): the wait for a load goes where its first use is, so the use of a
 // load that should not hold back the loads issued after it comes after them
+// a load from device memory through a pointer whose address space the
+// compiler cannot see (a global load, not a flat one, which is waited for
+// with every other load in flight)
+template <typename T>
+__device__ __forceinline__ T gload(const void* p) {
+  return *(const __attribute__((address_space(1))) T*)p;
+}
 template <typename TIn>
 struct Raw4;
 template <>
 struct Raw4<float> {
   typedef floatx4 T;
   static __device__ __forceinline__ T ld(const float* p) { return *reinterpret_cast<const T*>(p); }
+  static __device__ __forceinline__ T gld(const float* p) { return gload<T>(p); }
   static __device__ __forceinline__ floatx4 cvt(const T& x) { return x; }
 };
 template <>
 struct Raw4<bf16> {
   typedef u32x2 T;
   static __device__ __forceinline__ T ld(const bf16* p) { return *reinterpret_cast<const T*>(p); }
+  static __device__ __forceinline__ T gld(const bf16* p) { return gload<T>(p); }
   static __device__ __forceinline__ floatx4 cvt(const T& x) {
     return floatx4{__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xffff0000u),
                    __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xffff0000u)};
@@ -374,23 +384,31 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
     constexpr int GST = VERIFY ? (MAXN * DV / 4 + 255) / 256 : 1;
     const float* cs = io.conv_state + ((size_t)sb * 3 * H + h) * SW;
     const size_t row0 = (size_t)sb * N * H + h;  // (token 0, head h)
+    // the per-tensor pointers held as scalars (behind empty asm), so that the
+    // per-lane choice among them stays a select and does not become a load
+    // of the pointer from the argument block, waited for before the taps'
+    const float *w0 = io.conv.w[0], *w1 = io.conv.w[1], *w2 = io.conv.w[2];
+    const TIn *pq = (const TIn*)io.xq, *pk = (const TIn*)io.xk, *pv = (const TIn*)io.xv;
+    __asm__ volatile("" : "+s"(w0), "+s"(w1), "+s"(w2));
+    __asm__ volatile("" : "+s"(pq), "+s"(pk), "+s"(pv));
     auto tap_src = [&](int idx) {
       const int ten = idx < DK ? 0 : idx < 2 * DK ? 1 : 2;
       const int ch = idx - (ten == 0 ? 0 : ten == 1 ? DK : 2 * DK), D = ten == 2 ? DV : DK;
-      const float* wt = ten == 0 ? io.conv.w[0] : ten == 1 ? io.conv.w[1] : io.conv.w[2];
+      const float* wt = ten == 0 ? w0 : ten == 1 ? w1 : w2;
       return wt + ((size_t)h * D + ch) * 4;
     };
     auto x_src = [&](int idx) {  // raw row item idx of the tokens: 4 values
       const int t = idx / (SW / 4), c = 4 * (idx % (SW / 4));
       const size_t row = row0 + (size_t)t * H;
-      return c < DK ? ld4<TIn>((const TIn*)io.xq + row * DK + c)
-                    : c < 2 * DK ? ld4<TIn>((const TIn*)io.xk + row * DK + c - DK)
-                                 : ld4<TIn>((const TIn*)io.xv + row * DV + c - 2 * DK);
+      const TIn* xp = c < DK ? pq + row * DK + c
+                             : c < 2 * DK ? pk + row * DK + c - DK : pv + row * DV + c - 2 * DK;
+      return Raw4<TIn>::gld(xp);
     };
-    floatx4 tv[TPT], cv[CRT], xv[XRT], gv[GST], av[ALT];
+    // (token-dtype values stay as loaded until their stores, after the state's loads)
+    floatx4 tv[TPT], cv[CRT], av[ALT];
+    typename Raw4<TIn>::T xv[XRT], gv[GST];
 #pragma unroll
-    for (int i = 0; i < TPT; ++i)
-      tv[i] = *reinterpret_cast<const floatx4*>(tap_src(min(tid + 256 * i, SW - 1)));
+    for (int i = 0; i < TPT; ++i) tv[i] = gload<floatx4>(tap_src(min(tid + 256 * i, SW - 1)));
     if constexpr (VERIFY) {
 #pragma unroll
       for (int c = 0; c < CPLV; ++c) wn[c] = io.out.w[CPLV * lane + c];
@@ -407,8 +425,8 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
 #pragma unroll
       for (int i = 0; i < GST; ++i) {
         const int idx = min(tid + 256 * i, n * (DV / 4) - 1);
-        gv[i] = ld4<TIn>((const TIn*)io.out.g + (row0 + (size_t)(idx / (DV / 4)) * H) * DV +
-                         4 * (idx % (DV / 4)));
+        gv[i] = Raw4<TIn>::ld((const TIn*)io.out.g + (row0 + (size_t)(idx / (DV / 4)) * H) * DV +
+                              4 * (idx % (DV / 4)));
       }
     }
 #pragma unroll
@@ -418,8 +436,16 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
                                4 * (idx % (DK / 4)));
     }
     const float btv = beta[row0 + (size_t)min(tid, n - 1) * H];
+    // (the state's loads stay after the staging loads, and the stores after them)
+    __builtin_amdgcn_sched_barrier(0);
     load_state();
-    // the stores (alpha formed as alpha4_exact forms it)
+    __builtin_amdgcn_sched_barrier(0);
+    // the stores (alpha formed as alpha4_exact forms it).  The first round
+    // stores at the same clamped indices -- the threads past an item count
+    // store the last item again, the same values to the same place -- so that
+    // its stores sit under no branch the compiler would move their loads
+    // into; later rounds (rarely partly used) keep the guard, as repeated
+    // stores to one address from a whole wave serialize
     auto put_alpha = [&](int idx, floatx4 a4) {
       const int t = idx / (DK / 4), c = 4 * (idx % (DK / 4));
       if constexpr (KIND == GATE_LOG) {
@@ -435,28 +461,31 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
     };
 #pragma unroll
     for (int i = 0; i < TPT; ++i)
-      if (tid + 256 * i < SW) *reinterpret_cast<floatx4*>(tp + 4 * (tid + 256 * i)) = tv[i];
+      if (i == 0 || tid + 256 * i < SW)
+        *reinterpret_cast<floatx4*>(tp + 4 * min(tid + 256 * i, SW - 1)) = tv[i];
 #pragma unroll
     for (int i = 0; i < CRT; ++i) {
-      const int idx = tid + 256 * i;
-      if (idx < 3 * (SW / 4))
+      const int idx = min(tid + 256 * i, 3 * (SW / 4) - 1);
+      if (i == 0 || tid + 256 * i < 3 * (SW / 4))
         *reinterpret_cast<floatx4*>(xr + (idx / (SW / 4)) * SW + 4 * (idx % (SW / 4))) = cv[i];
     }
 #pragma unroll
     for (int i = 0; i < XRT; ++i) {
-      const int idx = tid + 256 * i;
-      if (idx < n * (SW / 4))
-        *reinterpret_cast<floatx4*>(xr + (3 + idx / (SW / 4)) * SW + 4 * (idx % (SW / 4))) = xv[i];
+      const int idx = min(tid + 256 * i, n * (SW / 4) - 1);
+      if (i == 0 || tid + 256 * i < n * (SW / 4))
+        *reinterpret_cast<floatx4*>(xr + (3 + idx / (SW / 4)) * SW + 4 * (idx % (SW / 4))) =
+            Raw4<TIn>::cvt(xv[i]);
     }
     for (int idx = tid + 256 * XRT; idx < n * (SW / 4); idx += 256)
       *reinterpret_cast<floatx4*>(xr + (3 + idx / (SW / 4)) * SW + 4 * (idx % (SW / 4))) =
-          x_src(idx);
+          Raw4<TIn>::cvt(x_src(idx));
     if constexpr (VERIFY) {
 #pragma unroll
       for (int i = 0; i < GST; ++i) {
-        const int idx = tid + 256 * i;
-        if (idx < n * (DV / 4))
-          *reinterpret_cast<floatx4*>(gs + (idx / (DV / 4)) * DV + 4 * (idx % (DV / 4))) = gv[i];
+        const int idx = min(tid + 256 * i, n * (DV / 4) - 1);
+        if (i == 0 || tid + 256 * i < n * (DV / 4))
+          *reinterpret_cast<floatx4*>(gs + (idx / (DV / 4)) * DV + 4 * (idx % (DV / 4))) =
+              Raw4<TIn>::cvt(gv[i]);
       }
       for (int idx = tid + 256 * GST; idx < n * (DV / 4); idx += 256)
         *reinterpret_cast<floatx4*>(gs + (idx / (DV / 4)) * DV + 4 * (idx % (DV / 4))) =
@@ -465,7 +494,8 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
     }
 #pragma unroll
     for (int i = 0; i < ALT; ++i)
-      if (tid + 256 * i < n * (DK / 4)) put_alpha(tid + 256 * i, av[i]);
+      if (i == 0 || tid + 256 * i < n * (DK / 4))
+        put_alpha(min(tid + 256 * i, n * (DK / 4) - 1), av[i]);
     for (int idx = tid + 256 * ALT; idx < n * (DK / 4); idx += 256)
       put_alpha(idx, gate_load4<KIND>(gate, true, row0 + (size_t)(idx / (DK / 4)) * H, DK,
                                       4 * (idx % (DK / 4))));
@@ -475,23 +505,28 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
     // once): as above, every load first, then the state's, then the stores
     constexpr int MAXN = MODE == DECODE_STEP ? 1 : MODE == DECODE_VERIFY ? 5 : 11;
     constexpr int KT = (MAXN * DK / 4 + 255) / 256, VT = (MAXN * DV / 4 + 255) / 256;
-    floatx4 ka[KT], qa[KT], aa[KT], va[VT];
+    floatx4 aa[KT];
+    typename Raw4<TIn>::T ka[KT], qa[KT], va[VT];  // as loaded (widened at their stores)
 #pragma unroll
     for (int i = 0; i < KT; ++i) {
       const int idx = min(tid + 256 * i, n * (DK / 4) - 1);
       const size_t row = ((size_t)sb * N + idx / (DK / 4)) * H + h;
       const int c = 4 * (idx % (DK / 4));
-      ka[i] = ld4<TIn>(k + row * DK + c);
-      if constexpr (VERIFY) qa[i] = ld4<TIn>(q + row * DK + c);
+      ka[i] = Raw4<TIn>::ld(k + row * DK + c);
+      qa[i] = ka[i];
+      if constexpr (VERIFY) qa[i] = Raw4<TIn>::ld(q + row * DK + c);
       aa[i] = gate_load4<KIND>(gate, true, row, DK, c);
     }
 #pragma unroll
     for (int i = 0; i < VT; ++i) {
       const int idx = min(tid + 256 * i, n * (DV / 4) - 1);
-      va[i] = ld4<TIn>(v + (((size_t)sb * N + idx / (DV / 4)) * H + h) * DV + 4 * (idx % (DV / 4)));
+      va[i] = Raw4<TIn>::ld(v + (((size_t)sb * N + idx / (DV / 4)) * H + h) * DV + 4 * (idx % (DV / 4)));
     }
     const float btv = beta[((size_t)sb * N + min(tid, n - 1)) * H + h];
+    // (the state's loads stay after the staging loads, and the stores after them)
+    __builtin_amdgcn_sched_barrier(0);
     load_state();
+    __builtin_amdgcn_sched_barrier(0);
     auto put_k = [&](int idx, floatx4 a4, const floatx4& k4, const floatx4& q4) {
       const int t = idx / (DK / 4), c = 4 * (idx % (DK / 4));
       if constexpr (KIND == GATE_LOG) {
@@ -515,8 +550,10 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
       }
     };
 #pragma unroll
-    for (int i = 0; i < KT; ++i)
-      if (tid + 256 * i < n * (DK / 4)) put_k(tid + 256 * i, aa[i], ka[i], qa[i]);
+    for (int i = 0; i < KT; ++i)  // (the first round clamped, as above)
+      if (i == 0 || tid + 256 * i < n * (DK / 4))
+        put_k(min(tid + 256 * i, n * (DK / 4) - 1), aa[i], Raw4<TIn>::cvt(ka[i]),
+              Raw4<TIn>::cvt(qa[i]));
     for (int idx = tid + 256 * KT; idx < n * (DK / 4); idx += 256) {
       const size_t row = ((size_t)sb * N + idx / (DK / 4)) * H + h;
       const int c = 4 * (idx % (DK / 4));
@@ -526,9 +563,10 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
     }
 #pragma unroll
     for (int i = 0; i < VT; ++i) {
-      const int idx = tid + 256 * i;
-      if (idx < n * (DV / 4))
-        *reinterpret_cast<floatx4*>(rec + (idx / (DV / 4)) * R::stride + R::V + 4 * (idx % (DV / 4))) = va[i];
+      const int idx = min(tid + 256 * i, n * (DV / 4) - 1);
+      if (i == 0 || tid + 256 * i < n * (DV / 4))
+        *reinterpret_cast<floatx4*>(rec + (idx / (DV / 4)) * R::stride + R::V +
+                                    4 * (idx % (DV / 4))) = Raw4<TIn>::cvt(va[i]);
     }
     for (int idx = tid + 256 * VT; idx < n * (DV / 4); idx += 256) {
       const int t = idx / (DV / 4), c = 4 * (idx % (DV / 4));
