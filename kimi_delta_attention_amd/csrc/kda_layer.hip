@@ -35,7 +35,7 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int n_seq, long long t)
 }
 
 template <typename T, int CPL, bool NORM>
-__device__ void prologue_rows(const T* __restrict__ x, T* __restrict__ y,
+__device__ __forceinline__ void prologue_rows(const T* __restrict__ x, T* __restrict__ y,
                               const float* __restrict__ taps, const float* __restrict__ st_in,
                               float* __restrict__ st_out, int st_off, int SW,
                               const int32_t* __restrict__ cu, int n_seq, long long Tseq, int H,
