@@ -357,7 +357,10 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
   auto load_state = [&]() {
 #pragma unroll
     for (int i = 0; i < NP; ++i)
-      s[i] = *reinterpret_cast<const floatx4*>(S + (size_t)(ro + RPP * i) * DV + col);
+      s[i] = MODE == DECODE_VERIFY  // (see the chunk kernel's state loads)
+                 ? __builtin_nontemporal_load(
+                       reinterpret_cast<const floatx4*>(S + (size_t)(ro + RPP * i) * DV + col))
+                 : *reinterpret_cast<const floatx4*>(S + (size_t)(ro + RPP * i) * DV + col);
   };
   // The (smaller) staging loads are issued before the state's, so that the
   // staging -- and the layer's prologue rows -- which wait for them, and with
@@ -844,10 +847,16 @@ __device__ __forceinline__ void lds_sync() { __asm__ volatile("s_waitcnt lgkmcnt
 
 template <int E>
 struct SpecVec;
+// ld: plain loads; ldnt: non-temporal loads, for a state that is only read
+// (verify: 3-9 % faster on MI355X; where the state is written back as well,
+// non-temporal loads made the step and the token-loop commit 7-24 % slower)
 template <>
 struct SpecVec<1> {
   typedef float F;
   static __device__ __forceinline__ void ld(const float* p, float (&x)[1]) { x[0] = *p; }
+  static __device__ __forceinline__ void ldnt(const float* p, float (&x)[1]) {
+    x[0] = __builtin_nontemporal_load(p);
+  }
   static __device__ __forceinline__ void st(float* p, const float (&x)[1]) {
     __builtin_nontemporal_store(x[0], p);
   }
@@ -857,6 +866,11 @@ struct SpecVec<2> {
   typedef float F __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ void ld(const float* p, float (&x)[2]) {
     const F t = *reinterpret_cast<const F*>(p);
+    x[0] = t[0];
+    x[1] = t[1];
+  }
+  static __device__ __forceinline__ void ldnt(const float* p, float (&x)[2]) {
+    const F t = __builtin_nontemporal_load(reinterpret_cast<const F*>(p));
     x[0] = t[0];
     x[1] = t[1];
   }
@@ -1043,7 +1057,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER && si
   float* S = state + (size_t)tile * DK * DV;
   float sr[KS][E];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) SpecVec<E>::ld(S + (size_t)(4 * s + g) * DV + col0, sr[s]);
+  for (int s = 0; s < KS; ++s) {
+    if constexpr (COMMIT) SpecVec<E>::ld(S + (size_t)(4 * s + g) * DV + col0, sr[s]);
+    else SpecVec<E>::ldnt(S + (size_t)(4 * s + g) * DV + col0, sr[s]);
+  }
   // (nothing below is moved above the state's loads)
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (!LAYER) {
