@@ -256,7 +256,7 @@ def test_decode_layer_max_draft():
 
 @pytest.mark.parametrize("N", [4, 7, 12])
 @pytest.mark.parametrize("dtype,Dk,Dv", [(torch.bfloat16, 128, 128), (torch.float32, 64, 64),
-                                         (torch.bfloat16, 64, 128)])
+                                         (torch.bfloat16, 64, 128), (torch.float32, 128, 128)])
 @pytest.mark.parametrize("decay", ["normal", "fast"])
 def test_decode_layer_verify_forms(N, dtype, Dk, Dv, decay):
     """Fused verify in each form (4 drafts: the token loop; 7: the chunk form
@@ -291,7 +291,7 @@ def test_decode_layer_verify_forms(N, dtype, Dk, Dv, decay):
 
 @pytest.mark.parametrize("N", [4, 12, 16])
 @pytest.mark.parametrize("dtype,Dk,Dv", [(torch.bfloat16, 128, 128), (torch.float32, 64, 64),
-                                         (torch.bfloat16, 64, 128)])
+                                         (torch.bfloat16, 64, 128), (torch.float32, 128, 128)])
 @pytest.mark.parametrize("decay", ["normal", "fast"])
 def test_decode_layer_commit_forms(N, dtype, Dk, Dv, decay):
     """Fused commit in each form (4 drafts: the token loop; 12 and 16: the chunk
