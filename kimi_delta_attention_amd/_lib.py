@@ -467,7 +467,8 @@ def decode_verify(q, k, v, alpha, beta, state, out_dtype=torch.float32,
     """Speculative-decoding verify: N draft tokens per session stepped from
     `state` (read only).  q, k, alpha [B,N,H,Dk]; v [B,N,H,Dv]; beta [B,N,H];
     state [B,H,Dk,Dv] fp32; gate arguments as for prefill_chunked.  Returns
-    o [B,N,H,Dv], token t's output after tokens 0..t."""
+    o [B,N,H,Dv], token t's output after tokens 0..t (bitwise the steps' below 6
+    drafts; from 6 on the chunk form, equal up to fp32 rounding)."""
     B, N, H, Dk, Dv, dev, g = _multi_inputs(k, v, alpha, beta, gate, a_log, g_min, q=q)
     _need(state, "state", torch.float32, dev)
     if state.shape != (B, H, Dk, Dv):
@@ -486,7 +487,9 @@ def decode_commit(k, v, alpha, beta, n_accept, state, gate: str = "alpha",
                   a_log: torch.Tensor | None = None, g_min: float = -5.0):
     """Speculative-decoding commit: replays tokens 0..n_accept[b]-1 of the same
     draft inputs into `state` in place (bitwise what that many decode_step calls
-    leave).  n_accept: int32 [B] device tensor, clamped to [0, N] on the device."""
+    leave below 12 drafts; from 12 drafts on the library takes the chunk form,
+    equal up to fp32 rounding).  n_accept: int32 [B] device tensor, clamped to
+    [0, N] on the device."""
     B, N, H, Dk, Dv, dev, g = _multi_inputs(k, v, alpha, beta, gate, a_log, g_min)
     _need(state, "state", torch.float32, dev)
     _need(n_accept, "n_accept", torch.int32, dev)
@@ -575,7 +578,8 @@ def decode_layer(mode: str, xq, xk, xv, wq, wk, wv, conv_state, alpha, beta, sta
     N = 1, 'verify', 'commit' with n_accept), epilogue (g [B,N,H,Dv], norm_w
     [Dv]).  xq, xk [B,N,H,Dk], xv [B,N,H,Dv] are the projections' outputs.
     Returns y [B,N,H,Dv] (None for commit); state and conv_state are updated in
-    place by step and commit."""
+    place by step and commit.  Bitwise prologue + the plain call (fp32 o) +
+    epilogue: the fused verify and commit take the plain calls' forms."""
     if mode not in DECODE_MODES:
         raise ValueError(f"mode must be one of {tuple(DECODE_MODES)}")
     B, N, H, Dk, Dv, dev, gd = _multi_inputs(xk, xv, alpha, beta, gate, a_log, g_min, q=xq)
