@@ -389,8 +389,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
     const size_t row0 = (size_t)sb * N * H + h;  // (token 0, head h)
     // the per-tensor pointers held as scalars (behind empty asm), so that the
     // per-lane choice among them stays a select and does not become a load
-    // of the pointer from the argument block, waited for before the taps'; the
-    // asm hides their address space, so their loads go through gload
+    // of the pointer from the argument block, waited for before the taps'
     const float *w0 = io.conv.w[0], *w1 = io.conv.w[1], *w2 = io.conv.w[2];
     const TIn *pq = (const TIn*)io.xq, *pk = (const TIn*)io.xk, *pv = (const TIn*)io.xv;
     __asm__ volatile("" : "+s"(w0), "+s"(w1), "+s"(w2));
