@@ -389,7 +389,8 @@ __attribute__((amdgpu_waves_per_eu(MODE == DECODE_VERIFY ? 4 : 1))) void decode_
     const size_t row0 = (size_t)sb * N * H + h;  // (token 0, head h)
     // the per-tensor pointers held as scalars (behind empty asm), so that the
     // per-lane choice among them stays a select and does not become a load
-    // of the pointer from the argument block, waited for before the taps'
+    // of the pointer from the argument block, waited for before the taps'; the
+    // asm hides their address space, so their loads go through gload
     const float *w0 = io.conv.w[0], *w1 = io.conv.w[1], *w2 = io.conv.w[2];
     const TIn *pq = (const TIn*)io.xq, *pk = (const TIn*)io.xk, *pv = (const TIn*)io.xv;
     __asm__ volatile("" : "+s"(w0), "+s"(w1), "+s"(w2));
@@ -1270,16 +1271,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER && si
     aM = row();
   }
 
-  // the epilogue's weight and gate logits (tokens w + 4 r), ahead of the products
-  float wn[CPLV], gv[4][CPLV];
+  // the epilogue's weight and gate logits (tokens w + 4 r), ahead of the
+  // products: loaded at a clamped token (no branch, which would wait for each
+  // load in turn) and kept in the token dtype until the epilogue uses them
+  float wn[CPLV];
+  TIn gv[4][CPLV];
   if constexpr (LAYER) {
     ld_elems<float, CPLV>(io.out.w + CPLV * lane, wn);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = w + 4 * r;
-      if (t < n)
-        ld_elems<TIn, CPLV>((const TIn*)io.out.g + (((size_t)sb * N + t) * H + h) * DV + CPLV * lane,
-                            gv[r]);
+      const int t = min(w + 4 * r, n - 1);
+      const TIn* gp = (const TIn*)io.out.g + (((size_t)sb * N + t) * H + h) * DV + CPLV * lane;
+#pragma unroll
+      for (int c = 0; c < CPLV; ++c) gv[r][c] = gp[c];
     }
   }
 
@@ -1342,10 +1346,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER && si
       for (int r = 0; r < 4; ++r) {
         const int t = w + 4 * r;
         if (t < n) {
-          float ovr[CPLV], y[CPLV];
+          float ovr[CPLV], gr[CPLV], y[CPLV];
 #pragma unroll
-          for (int c = 0; c < CPLV; ++c) ovr[c] = sV[t * DV + CPLV * lane + c];
-          epilogue_row<CPLV>(ovr, gv[r], wn, io.out.eps, y);
+          for (int c = 0; c < CPLV; ++c) {
+            ovr[c] = sV[t * DV + CPLV * lane + c];
+            gr[c] = (float)gv[r][c];
+          }
+          epilogue_row<CPLV>(ovr, gr, wn, io.out.eps, y);
           row_store<TOut, CPLV>(o + (((size_t)sb * N + t) * H + h) * DV, lane, y);
         }
       }
