@@ -965,16 +965,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER && si
   }
   const float bt = tid < n ? beta[((size_t)sb * N + tid) * H + h] : 0.f;
   float vv[4][E];  // v of rows 4g + i at this lane's columns
+  TIn vr[4][E];    // ... as loaded (widened with k and q, after the state's loads)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = 4 * g + i;
 #pragma unroll
     for (int e = 0; e < E; ++e) vv[i][e] = 0.f;
     if constexpr (!LAYER) {
-      float vl[E];
-      ld_elems<TIn, E>(v + (((size_t)sb * N + (t < n ? t : 0)) * H + h) * DV + col0, vl);
+      const TIn* vp = v + (((size_t)sb * N + (t < n ? t : 0)) * H + h) * DV + col0;
 #pragma unroll
-      for (int e = 0; e < E; ++e) vv[i][e] = t < n ? vl[e] : 0.f;
+      for (int e = 0; e < E; ++e) vr[i][e] = vp[e];
     }
   }
   // the layer's prologue: one wave per (block of 4 tokens, tensor), job
@@ -1071,6 +1071,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAYER && si
       k4[it] = ok ? Raw4<TIn>::cvt(kr[it]) : k4[it];
       if constexpr (!COMMIT) q4[it] = ok ? Raw4<TIn>::cvt(qr[it]) : q4[it];
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < E; ++e) vv[i][e] = 4 * g + i < n ? (float)vr[i][e] : 0.f;
   }
   if constexpr (LAYER) {
     // the prologue rows into the token arrays (rows n..15 stay zero)
